@@ -1,0 +1,112 @@
+"""Planted mistakes in the CPU oracle must be caught by at least one pin.
+
+Each mutant replaces one oracle function (on the CPU, inside this test only)
+with a plausible wrong version; the test passes when some pin fails.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import pins
+from oracle import reference as ref
+
+
+def _caught(monkeypatch, name, fn):
+    monkeypatch.setattr(ref, name, fn)
+    failed = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(ref)
+        except AssertionError:
+            failed.append(pin.__name__)
+        except Exception as e:  # a crash also counts as detection
+            failed.append(pin.__name__ + ":" + type(e).__name__)
+    return failed
+
+
+_orig_softmax_v = ref.softmax_v
+_orig_select = ref.select_topk
+_orig_scores = ref.scores
+_orig_merge = ref.attn_merge_lse
+_orig_head_step = ref.retopk_head_step
+_orig_unit = ref.unit_query_f32
+
+
+def m_no_renormalisation(z, v):
+    o, lse = _orig_softmax_v(z, v)
+    if z.shape[0] == 0:
+        return o, lse
+    m = float(np.max(z))
+    return o * float(np.sum(np.exp(z - m))), lse
+
+
+def m_ties_to_highest(z, rows, k):
+    if z.shape[0] == 0 or k <= 0:
+        return np.zeros(0, np.int64), float("-inf")
+    order = np.lexsort((-rows, -z))
+    take = order[:min(k, z.shape[0])]
+    return np.sort(rows[take]), float(z[take[-1]])
+
+
+def m_off_by_one_k(z, rows, k):
+    return _orig_select(z, rows, k + 1)
+
+
+def m_dropped_scale(q, kc, rows, scale):
+    return _orig_scores(q, kc, rows, 1.0)
+
+
+def m_last_coordinate_dropped(q, kc, rows, scale):
+    q2 = np.array(q, dtype=np.float64).copy()
+    q2[-1] = 0.0
+    return _orig_scores(q2, kc, rows, scale)
+
+
+def m_merge_wrong_weight(o_a, lse_a, o_b, lse_b):
+    o, lse = _orig_merge(o_a, lse_a, o_b, lse_b)
+    la = np.asarray(lse_a, dtype=np.float64)
+    lb = np.asarray(lse_b, dtype=np.float64)
+    # forget to rescale the second operand
+    ga = np.where(np.isneginf(la), 0.0, np.exp(la - lse))
+    return ga[..., None] * np.asarray(o_a) + np.asarray(o_b), lse
+
+
+def m_merge_lse_max_only(o_a, lse_a, o_b, lse_b):
+    o, lse = _orig_merge(o_a, lse_a, o_b, lse_b)
+    return o, np.maximum(lse_a, lse_b)
+
+
+def m_no_recent_window(p, *a, **kw):
+    p2 = ref.RetopkParams(p.top_k, p.cache_cap, p.top_r, 0, p.tau, p.refresh)
+    return _orig_head_step(p2, *a, **kw)
+
+
+def m_topr_least_similar(p, q_hat, support, head, count, q, *a, **kw):
+    return _orig_head_step(p, -q_hat, support, head, count, q, *a, **kw) if count else \
+        _orig_head_step(p, q_hat, support, head, count, q, *a, **kw)
+
+
+def m_no_normalisation(q):
+    return np.asarray(q, dtype=np.float32)
+
+
+MUTANTS = [
+    ("softmax_v", m_no_renormalisation),
+    ("select_topk", m_ties_to_highest),
+    ("select_topk", m_off_by_one_k),
+    ("scores", m_dropped_scale),
+    ("scores", m_last_coordinate_dropped),
+    ("attn_merge_lse", m_merge_wrong_weight),
+    ("attn_merge_lse", m_merge_lse_max_only),
+    ("retopk_head_step", m_no_recent_window),
+    ("retopk_head_step", m_topr_least_similar),
+    ("unit_query_f32", m_no_normalisation),
+]
+
+
+@pytest.mark.parametrize("name,fn", MUTANTS, ids=[f.__name__ for _, f in MUTANTS])
+def test_mutant_is_caught(monkeypatch, name, fn):
+    failed = _caught(monkeypatch, name, fn)
+    assert failed, f"no pin caught mutant {fn.__name__}"
