@@ -193,8 +193,10 @@ def attn_merge_lse(o_a: np.ndarray, lse_a: np.ndarray, o_b: np.ndarray, lse_b: n
     lse = np.where(both_empty, NEG_INF, Ms + np.log(np.where(both_empty, 1.0, tot)))
     ga = np.where(both_empty, 0.0, ea / np.where(both_empty, 1.0, tot))
     gb = np.where(both_empty, 0.0, eb / np.where(both_empty, 1.0, tot))
-    o = ga[..., None] * o_a + gb[..., None] * o_b
-    return o, lse
+    # a set with weight 0 (lse = -inf) is not used at all, whatever its o holds
+    ta = np.where(ga[..., None] == 0.0, 0.0, ga[..., None] * o_a)
+    tb = np.where(gb[..., None] == 0.0, 0.0, gb[..., None] * o_b)
+    return ta + tb, lse
 
 
 # --------------------------------------------------------------------------

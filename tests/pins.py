@@ -270,6 +270,10 @@ def pin_merge_algebra(ref, seed=0):
     np.testing.assert_allclose(lm, l[0], atol=1e-15)
     om, lm = ref.attn_merge_lse(z, ninf, o[1], l[1])
     np.testing.assert_allclose(om, o[1], atol=1e-15)
+    # an empty operand is not read: its o may hold anything
+    junk = np.full((3, d), np.nan)
+    om, lm = ref.attn_merge_lse(junk, ninf, o[1], l[1])
+    np.testing.assert_allclose(om, o[1], atol=1e-15)
     # both empty
     om, lm = ref.attn_merge_lse(z, ninf, z, ninf)
     assert np.all(om == 0) and np.all(np.isneginf(lm))
