@@ -1,0 +1,215 @@
+/*
+ * stdk.h — dynamic top-K sparse decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libstdk.so. Every pointer argument is a DEVICE pointer unless its
+ * comment says "host". The caller allocates and owns every buffer (inputs,
+ * outputs, workspace, ReTopK state); the library never allocates device
+ * memory on these calls and keeps no device state between them.
+ *
+ * Conventions shared by every entry point
+ *  - Return value: STDK_OK (0) or a negative STDK_E* code. Arguments are
+ *    validated on the host before anything is enqueued, so a call that
+ *    returns STDK_EINVAL / STDK_EUNSUPPORTED / STDK_EWORKSPACE has launched
+ *    nothing. STDK_EHIP means a launch failed; stdk_last_error() (per host
+ *    thread) holds the text. No C++ exception crosses the ABI.
+ *  - Ordering: all work is enqueued on `stream` (a hipStream_t; NULL = the
+ *    legacy default stream) and nothing is synchronised inside the library.
+ *  - Determinism: identical inputs give bit-identical outputs.
+ *  - Concurrency: calls are reentrant; two calls that are in flight at the
+ *    same time must not share a workspace buffer.
+ *  - KV cache layout (stdk_layout): element (b, h_kv, row, j) lives at
+ *        base + b*stride_b + h_kv*stride_h + row*head_dim + j
+ *    (rows are contiguous, head_dim elements each). Keys and values share
+ *    one layout. Row starts must be 16-byte aligned.
+ *  - Query / output layout: q, o are [batch][n_q_heads][head_dim] fp32,
+ *    lse is [batch][n_q_heads] fp32, index outputs [batch][n_q_heads][K]
+ *    int32. Query head h reads KV head h / (n_q_heads / n_kv_heads).
+ *  - Scores use z_i = scale * (q . k_i); the caller passes scale (the usual
+ *    value is 1/sqrt(head_dim)).
+ *
+ * Sources (page title and section):
+ *  [RA]  "RetrievalAttention: Accelerating Long-Context LLM Inference via
+ *        Vector Retrieval" (review): "Approximated Attention Formulation"
+ *        (Eq. 2) and "CPU-GPU Co-Execution Architecture" (Eq. 3-5).
+ *  [RT]  "Recall Before You Rank: Similarity-Guided Top-K Reuse for
+ *        Efficient Long-Context Attention" (review): the exact Top-K cost
+ *        section and "核心方法" 1-5 with the per-step loop.
+ */
+#ifndef STDK_H
+#define STDK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define STDK_VERSION 100 /* 1.0.0 */
+
+#define STDK_OK 0
+#define STDK_EINVAL (-1)       /* a pointer, size or parameter is invalid */
+#define STDK_EUNSUPPORTED (-2) /* valid but not supported (head_dim != 128, ...) */
+#define STDK_EWORKSPACE (-3)   /* workspace missing or too small */
+#define STDK_EHIP (-4)         /* a HIP call or kernel launch failed */
+
+#define STDK_F32 0  /* KV cache stored as IEEE fp32 */
+#define STDK_BF16 1 /* KV cache stored as bfloat16 */
+
+#define STDK_MAX_RANGES 16   /* index ranges per topk_attn_decode call */
+#define STDK_MAX_GROUP 8     /* query heads per KV head */
+
+typedef struct stdk_layout {
+  int32_t batch;      /* B */
+  int32_t n_q_heads;  /* H_q */
+  int32_t n_kv_heads; /* H_kv; H_q must be a multiple, H_q / H_kv <= STDK_MAX_GROUP */
+  int32_t head_dim;   /* d; only 128 is supported */
+  int64_t max_len;    /* rows allocated per (b, h_kv) */
+  int32_t kv_dtype;   /* STDK_F32 or STDK_BF16 */
+  int32_t reserved;
+  int64_t stride_b;   /* elements between sequences (>= n_kv_heads * stride_h) */
+  int64_t stride_h;   /* elements between KV heads (>= max_len * head_dim) */
+} stdk_layout;
+
+/* ------------------------------------------------------------------------
+ * topk_attn_decode — [RA] Eq. 2 with the index set chosen as the exact top-K
+ * of the scores ([RT] exact Top-K: full QK scan, then TopK over every score).
+ *
+ * For every (b, h_q): z_i = scale * q[b][h_q] . k[b][h_kv][i] for every row i
+ * in the union of the half-open `ranges`; S = the top_k rows of largest z
+ * (ties go to the lowest row); then
+ *     m = max_S z,  s = sum_S e^{z_i - m},
+ *     o = sum_S e^{z_i - m} v_i / s,  lse = m + ln s.
+ * When top_k >= n (n = total rows in the ranges) every row is used (dense
+ * attention). n = 0 gives o = 0, lse = -inf.
+ *
+ *  ranges   host, 2*n_ranges int64: begin0, end0, begin1, end1, ... ; each
+ *           range within [0, max_len), non-empty, ascending and disjoint.
+ *           The same ranges apply to every sequence.
+ *  n_ranges 0..STDK_MAX_RANGES.
+ *  top_k    >= 1.
+ *  idx_out  [B][H_q][top_k] int32: S in ascending row order, padded with -1
+ *           when n < top_k. May be NULL.
+ *  o_out    [B][H_q][128] fp32;  lse_out [B][H_q] fp32 (natural log).
+ *  workspace / workspace_bytes: device scratch of at least
+ *           topk_attn_decode_workspace_size(lay, n, top_k) bytes, 256-byte
+ *           aligned. Its contents on entry do not matter.
+ * ---------------------------------------------------------------------- */
+int32_t topk_attn_decode(const stdk_layout* lay, const float* q, const void* k_cache,
+                         const void* v_cache, const int64_t* ranges, int32_t n_ranges,
+                         int32_t top_k, float scale, int32_t* idx_out, float* o_out,
+                         float* lse_out, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* Bytes of workspace topk_attn_decode needs for n_scan rows per (b, h_q). */
+size_t topk_attn_decode_workspace_size(const stdk_layout* lay, int64_t n_scan, int32_t top_k);
+
+/* ------------------------------------------------------------------------
+ * attn_merge_lse — [RA] Eq. 4-5: combination of two partial attention
+ * outputs over disjoint row sets a and b:
+ *     M = max(lse_a, lse_b),  lse = M + ln(e^{lse_a - M} + e^{lse_b - M}),
+ *     o = e^{lse_a - lse} o_a + e^{lse_b - lse} o_b.
+ * e^{lse_j - lse} equals the pages' gamma_j. An operand with lse = -inf
+ * contributes nothing; both -inf gives o = 0, lse = -inf.
+ *  rows     number of (o, lse) pairs (e.g. B * H_q); d = elements per o row
+ *           (1..1024). o_* are [rows][d] fp32, lse_* are [rows] fp32.
+ *  o_out / lse_out may alias o_a/lse_a or o_b/lse_b exactly.
+ * ---------------------------------------------------------------------- */
+int32_t attn_merge_lse(int64_t rows, int32_t d, const float* o_a, const float* lse_a,
+                       const float* o_b, const float* lse_b, float* o_out, float* lse_out,
+                       void* stream);
+
+/* ------------------------------------------------------------------------
+ * ReTopK ([RT] 核心方法 1-5 and the per-step loop).
+ * ---------------------------------------------------------------------- */
+typedef struct retopk_params {
+  int32_t top_k;     /* K, rows attended per step (>= 1) */
+  int32_t cache_cap; /* C, FIFO entries per query head (1..64) */
+  int32_t top_r;     /* R, cache entries recalled (1..C) */
+  int32_t recent;    /* W, newest rows always added to the candidates (>= 0) */
+  float tau;         /* similarity threshold: max cosine < tau -> exact path */
+  int32_t refresh;   /* T_r: step t with t % T_r == 0 -> exact path; 0 = never */
+  float scale;       /* score scale (1/sqrt(d)) */
+} retopk_params;
+
+/* Caller-owned per-query-head state (device memory):
+ *  q_hat   [B][H_q][C][128] fp32  unit-norm cached queries
+ *  support [B][H_q][C][K]   int32 their supports, ascending rows, -1 padded
+ *  head    [B][H_q]         int32 slot of the newest entry
+ *  count   [B][H_q]         int32 valid entries (0..C)
+ * Entry of age a (0 = newest) lives in slot (head - a) mod C, for a < count. */
+typedef struct retopk_state {
+  float* q_hat;
+  int32_t* support;
+  int32_t* head;
+  int32_t* count;
+} retopk_state;
+
+#define RETOPK_PATH_REUSE 0    /* recall + union + exact rerank */
+#define RETOPK_PATH_FALLBACK 1 /* max cosine < tau, or empty cache: exact top-K */
+#define RETOPK_PATH_REFRESH 2  /* t % T_r == 0: exact top-K */
+
+/* Fill the FIFO of every (b, h_q) with the last min(n_hist, C) (query,
+ * support) pairs of q_hist [B][H_q][n_hist][128] fp32 and sup_hist
+ * [B][H_q][n_hist][K] int32, oldest first ([RT] 核心方法 1: the cache starts
+ * from the last C prefill queries). Queries are stored normalised. n_hist = 0
+ * gives an empty cache. */
+int32_t retopk_state_init(const stdk_layout* lay, const retopk_params* p, const retopk_state* st,
+                          const float* q_hist, const int32_t* sup_hist, int32_t n_hist,
+                          void* stream);
+
+/* One decode step for every (b, h_q) ([RT] per-step loop):
+ *   q_bar = q / ||q||;  rho_c = q_bar . q_hat_c over the valid entries;
+ *   exact path if t % T_r == 0 (refresh), or count = 0, or max rho < tau;
+ *   else: recall the R entries of largest rho (ties: newest first), take the
+ *   union of their supports and rows [L_t - W, L_t) (rows outside [0, L_t)
+ *   are dropped), score those rows exactly and keep the top K;
+ *   exact path: top K over rows [0, L_t);
+ *   then o, lse = renormalised softmax . V over the K rows, and push
+ *   (q_bar, support) into slot (head + 1) mod C (count = min(count + 1, C)).
+ * The cosine, the comparison with tau and the top-R order are evaluated in
+ * fp32; scores in fp32.
+ *  L_t          rows visible this step, 1..max_len (includes the row the
+ *               caller appended for this step).
+ *  t            0-based decode step counter (for the refresh).
+ *  support_out  [B][H_q][K] int32 (ascending, -1 padded). Required.
+ *  o_out, lse_out as topk_attn_decode. Required.
+ *  path_out     [B][H_q] int32 RETOPK_PATH_*; may be NULL.
+ *  n_cand_out   [B][H_q] int32: candidate count M_t on the reuse path, L_t on
+ *               the exact path; may be NULL.
+ *  cand_out     [B][H_q][R*K + W] int32: the ascending candidate rows of the
+ *               reuse path (-1 padded; all -1 on the exact path); may be NULL.
+ *  workspace    at least retopk_workspace_size(lay, p, L_t) bytes.
+ * Limits: L_t <= 1,048,576 (the candidate bitmap lives in LDS). */
+int32_t retopk_step(const stdk_layout* lay, const retopk_params* p, const retopk_state* st,
+                    const float* q, const void* k_cache, const void* v_cache, int64_t L_t,
+                    int64_t t, int32_t* support_out, float* o_out, float* lse_out,
+                    int32_t* path_out, int32_t* n_cand_out, int32_t* cand_out, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+size_t retopk_workspace_size(const stdk_layout* lay, const retopk_params* p, int64_t max_L_t);
+
+/* ------------------------------------------------------------------------
+ * Helpers
+ * ---------------------------------------------------------------------- */
+const char* stdk_last_error(void); /* host string, valid until the next call on this thread */
+int32_t stdk_version(void);        /* STDK_VERSION */
+
+/* Kernel timing: while enabled, every kernel the library enqueues is
+ * bracketed by two hipEvents recorded on the same stream. `capacity` bounds
+ * the number of launches recorded (events are created when enabling, not on
+ * the hot path). stdk_profile_read waits for the recorded events and returns,
+ * for the kernel family `name` (e.g. "k_scan"), the summed duration in
+ * milliseconds and the launch count. Names: "k_scan", "topk_filter",
+ * "topk_select", "sparse_sv", "dense_attn", "attn_merge", "ws_clear",
+ * "retopk_select", "retopk_rerank", "retopk_push", "retopk_init". */
+int32_t stdk_profile_enable(int32_t capacity);
+int32_t stdk_profile_disable(void);
+int32_t stdk_profile_reset(void);
+int32_t stdk_profile_read(const char* name, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STDK_H */

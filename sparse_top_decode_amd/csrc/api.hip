@@ -1,0 +1,801 @@
+// Host side of libstdk: argument validation, workspace layout, kernel
+// launches and launch timing. The C entry points are declared in
+// include/stdk.h, which documents each operation and its source.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/stdk.h"
+#include "attend_kernels.h"
+#include "device.h"
+#include "retopk_kernels.h"
+#include "scan_kernels.h"
+#include "select_kernels.h"
+
+using namespace stdk;
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// errors
+// ---------------------------------------------------------------------------
+thread_local std::string g_err;
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int32_t ok() {
+  g_err.clear();
+  return STDK_OK;
+}
+
+// ---------------------------------------------------------------------------
+// launch timing
+// ---------------------------------------------------------------------------
+enum KernelId {
+  KID_SCAN, KID_FILTER, KID_SELECT, KID_SV, KID_DENSE, KID_MERGE, KID_CLEAR,
+  KID_RT_SELECT, KID_RT_RERANK, KID_RT_PUSH, KID_RT_INIT, KID_FILL, KID_COUNT
+};
+const char* const kKernelNames[KID_COUNT] = {
+    "k_scan",        "topk_filter",   "topk_select", "sparse_sv",   "dense_attn", "attn_merge", "ws_clear",
+    "retopk_select", "retopk_rerank", "retopk_push", "retopk_init", "fill_empty"};
+
+struct Profiler {
+  std::mutex mu;
+  bool on = false;
+  std::vector<hipEvent_t> ev;  // 2 per slot
+  std::vector<int> kid;
+  size_t used = 0;
+  double total_ms[KID_COUNT] = {};
+  int64_t launches[KID_COUNT] = {};
+};
+Profiler g_prof;
+
+// Returns the slot index whose first event was recorded, or -1.
+long prof_begin(int kid, hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  if (!g_prof.on || g_prof.used >= g_prof.kid.size()) return -1;
+  const size_t slot = g_prof.used++;
+  g_prof.kid[slot] = kid;
+  (void)hipEventRecord(g_prof.ev[2 * slot], s);
+  return (long)slot;
+}
+
+void prof_end(long slot, hipStream_t s) {
+  if (slot < 0) return;
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  (void)hipEventRecord(g_prof.ev[2 * slot + 1], s);
+}
+
+template <typename F>
+int32_t launch(int kid, hipStream_t s, F&& f) {
+  const long slot = prof_begin(kid, s);
+  f();
+  const hipError_t e = hipGetLastError();
+  prof_end(slot, s);
+  if (e != hipSuccess) return fail(STDK_EHIP, "%s launch failed: %s", kKernelNames[kid], hipGetErrorString(e));
+  return STDK_OK;
+}
+
+#define STDK_TRY(x)              \
+  do {                           \
+    const int32_t rc_ = (x);     \
+    if (rc_ != STDK_OK) return rc_; \
+  } while (0)
+
+// ---------------------------------------------------------------------------
+// device limits (per device, queried once)
+// ---------------------------------------------------------------------------
+struct DevInfo {
+  bool init = false;
+  int max_lds = 65536;
+};
+std::mutex g_dev_mu;
+DevInfo g_dev[64];
+
+int32_t dev_info(DevInfo** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(STDK_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(STDK_EUNSUPPORTED, "device index %d", dev);
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  DevInfo& d = g_dev[dev];
+  if (!d.init) {
+    int v = 0;
+    e = hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+    if (e != hipSuccess) return fail(STDK_EHIP, "hipDeviceGetAttribute: %s", hipGetErrorString(e));
+    d.max_lds = v;
+    const void* dyn_kernels[] = {(const void*)topk_select<true>, (const void*)retopk_select<true>};
+    for (const void* k : dyn_kernels) {
+      const int static_bytes = 12 * 1024;
+      (void)hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, std::max(0, v - static_bytes));
+    }
+    (void)hipGetLastError();
+    d.init = true;
+  }
+  *out = &d;
+  return STDK_OK;
+}
+
+// ---------------------------------------------------------------------------
+// helpers
+// ---------------------------------------------------------------------------
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t rup(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+inline size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int32_t check_layout(const stdk_layout* lay) {
+  if (!lay) return fail(STDK_EINVAL, "layout is NULL");
+  if (lay->batch < 1 || lay->n_q_heads < 1 || lay->n_kv_heads < 1)
+    return fail(STDK_EINVAL, "batch, n_q_heads and n_kv_heads must be >= 1");
+  if (lay->n_q_heads % lay->n_kv_heads != 0)
+    return fail(STDK_EUNSUPPORTED, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)", lay->n_q_heads,
+                lay->n_kv_heads);
+  const int G = lay->n_q_heads / lay->n_kv_heads;
+  if (G > STDK_MAX_GROUP) return fail(STDK_EUNSUPPORTED, "group size %d > %d", G, STDK_MAX_GROUP);
+  if (lay->head_dim != kHeadDim) return fail(STDK_EUNSUPPORTED, "head_dim %d (only 128 is supported)", lay->head_dim);
+  if (lay->kv_dtype != STDK_F32 && lay->kv_dtype != STDK_BF16)
+    return fail(STDK_EUNSUPPORTED, "kv_dtype %d", lay->kv_dtype);
+  if (lay->max_len < 1 || lay->max_len > 0x7FFFFFFFLL) return fail(STDK_EINVAL, "max_len %lld out of range", (long long)lay->max_len);
+  if (lay->stride_h < lay->max_len * kHeadDim) return fail(STDK_EINVAL, "stride_h smaller than max_len * head_dim");
+  if (lay->batch > 1 && lay->stride_b < (int64_t)lay->n_kv_heads * lay->stride_h)
+    return fail(STDK_EINVAL, "stride_b smaller than n_kv_heads * stride_h");
+  const int esz = lay->kv_dtype == STDK_BF16 ? 2 : 4;
+  if ((lay->stride_h * esz) % 16 != 0 || (lay->stride_b * esz) % 16 != 0)
+    return fail(STDK_EINVAL, "strides must keep rows 16-byte aligned");
+  return STDK_OK;
+}
+
+int32_t check_ptr(const void* p, const char* what, size_t align) {
+  if (!p) return fail(STDK_EINVAL, "%s is NULL", what);
+  if (((uintptr_t)p) % align != 0) return fail(STDK_EINVAL, "%s is not %zu-byte aligned", what, align);
+  return STDK_OK;
+}
+
+// Workspace of topk_attn_decode (and of the exact path of retopk_step).
+struct TopkWs {
+  int64_t S, groups, n, n_pad, K, nsplit, nwg_max, words;
+  size_t clear_off, clear_words;  // hist | list_cnt | done | done_grp | done_rr
+  size_t hist, list_cnt, done, done_grp, done_rr;
+  size_t scores, list, sel_row, sel_z, part, gbitmap, total;
+};
+
+constexpr int kDenseMaxWg = 32;
+
+TopkWs topk_ws(int64_t S, int64_t groups, int64_t n, int64_t K) {
+  TopkWs w{};
+  w.S = S;
+  w.groups = groups;
+  w.n = n;
+  w.n_pad = rup(std::max<int64_t>(n, 1), 64);
+  w.K = K;
+  w.nsplit = cdiv(K, kSvRows);
+  w.nwg_max = kDenseMaxWg;
+  w.words = cdiv(std::max<int64_t>(n, 1), 32);
+  size_t off = 0;
+  w.clear_off = off;
+  w.hist = off;
+  off += (size_t)S * kHistBins * 4;
+  w.list_cnt = off;
+  off += (size_t)S * 4;
+  w.done = off;
+  off += (size_t)S * 4;
+  w.done_rr = off;
+  off += (size_t)S * 4;
+  w.done_grp = off;
+  off += (size_t)groups * 4;
+  w.clear_words = (off - w.clear_off) / 4;
+  off = al256(off);
+  w.scores = off;
+  off = al256(off + (size_t)S * w.n_pad * 4);
+  w.list = off;
+  off = al256(off + (size_t)S * w.n_pad * 4);
+  w.sel_row = off;
+  off = al256(off + (size_t)S * K * 4);
+  w.sel_z = off;
+  off = al256(off + (size_t)S * K * 4);
+  w.part = off;
+  off = al256(off + (size_t)S * std::max<int64_t>(w.nsplit, w.nwg_max) * kPartStride * 4);
+  w.gbitmap = off;
+  off = al256(off + (size_t)S * w.words * 4);
+  w.total = off;
+  return w;
+}
+
+RangeTab make_tab(const int64_t* ranges, int n_ranges, int64_t* n_total) {
+  RangeTab t{};
+  t.n = n_ranges;
+  int64_t pos = 0;
+  for (int r = 0; r < n_ranges; ++r) {
+    t.row0[r] = ranges[2 * r];
+    t.pos0[r] = pos;
+    pos += ranges[2 * r + 1] - ranges[2 * r];
+  }
+  t.pos0[n_ranges] = pos;
+  if (n_ranges == 0) {
+    t.n = 1;
+    t.row0[0] = 0;
+    t.pos0[0] = 0;
+    t.pos0[1] = 0;
+  }
+  *n_total = pos;
+  return t;
+}
+
+struct Geo {
+  int B, Hq, Hkv, G;
+  int64_t S, groups;
+  int64_t sb_bytes, sh_bytes;
+  bool bf16;
+};
+
+Geo geo_of(const stdk_layout* lay) {
+  Geo g{};
+  g.B = lay->batch;
+  g.Hq = lay->n_q_heads;
+  g.Hkv = lay->n_kv_heads;
+  g.G = g.Hq / g.Hkv;
+  g.S = (int64_t)g.B * g.Hq;
+  g.groups = (int64_t)g.B * g.Hkv;
+  g.bf16 = lay->kv_dtype == STDK_BF16;
+  const int esz = g.bf16 ? 2 : 4;
+  g.sb_bytes = lay->stride_b * esz;
+  g.sh_bytes = lay->stride_h * esz;
+  return g;
+}
+
+// ---------------------------------------------------------------------------
+// kernel dispatch on (dtype, G)
+// ---------------------------------------------------------------------------
+template <typename T>
+int scan_rows_iter(int G) {
+  switch (G) {
+    case 1: return ScanShape<T, 1>::ROWS_ITER;
+    case 2: return ScanShape<T, 2>::ROWS_ITER;
+    case 3: return ScanShape<T, 3>::ROWS_ITER;
+    case 4: return ScanShape<T, 4>::ROWS_ITER;
+    case 5: return ScanShape<T, 5>::ROWS_ITER;
+    case 6: return ScanShape<T, 6>::ROWS_ITER;
+    case 7: return ScanShape<T, 7>::ROWS_ITER;
+    default: return ScanShape<T, 8>::ROWS_ITER;
+  }
+}
+
+template <typename T>
+void launch_scan_t(int G, dim3 grid, hipStream_t s, const ScanArgs& a) {
+  switch (G) {
+    case 1: hipLaunchKernelGGL((k_scan<T, 1>), grid, dim3(kScanThreads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_scan<T, 2>), grid, dim3(kScanThreads), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((k_scan<T, 3>), grid, dim3(kScanThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_scan<T, 4>), grid, dim3(kScanThreads), 0, s, a); break;
+    case 5: hipLaunchKernelGGL((k_scan<T, 5>), grid, dim3(kScanThreads), 0, s, a); break;
+    case 6: hipLaunchKernelGGL((k_scan<T, 6>), grid, dim3(kScanThreads), 0, s, a); break;
+    case 7: hipLaunchKernelGGL((k_scan<T, 7>), grid, dim3(kScanThreads), 0, s, a); break;
+    default: hipLaunchKernelGGL((k_scan<T, 8>), grid, dim3(kScanThreads), 0, s, a); break;
+  }
+}
+
+template <typename T>
+void launch_dense_t(int G, dim3 grid, hipStream_t s, const DenseArgs& a) {
+  switch (G) {
+    case 1: hipLaunchKernelGGL((dense_attn<T, 1>), grid, dim3(kDenseThreads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((dense_attn<T, 2>), grid, dim3(kDenseThreads), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((dense_attn<T, 3>), grid, dim3(kDenseThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((dense_attn<T, 4>), grid, dim3(kDenseThreads), 0, s, a); break;
+    case 5: hipLaunchKernelGGL((dense_attn<T, 5>), grid, dim3(kDenseThreads), 0, s, a); break;
+    case 6: hipLaunchKernelGGL((dense_attn<T, 6>), grid, dim3(kDenseThreads), 0, s, a); break;
+    case 7: hipLaunchKernelGGL((dense_attn<T, 7>), grid, dim3(kDenseThreads), 0, s, a); break;
+    default: hipLaunchKernelGGL((dense_attn<T, 8>), grid, dim3(kDenseThreads), 0, s, a); break;
+  }
+}
+
+int32_t run_clear(hipStream_t s, uint32_t* p, int64_t words) {
+  if (words <= 0) return STDK_OK;
+  const int64_t blocks = std::min<int64_t>(cdiv(words, 256), 1024);
+  return launch(KID_CLEAR, s, [&] { hipLaunchKernelGGL(ws_clear, dim3((unsigned)blocks), dim3(256), 0, s, p, words); });
+}
+
+// Scan + filter + select over n positions (n > K) for every segment.
+// seg_active / head_active restrict the work (ReTopK exact heads).
+int32_t run_exact_select(const Geo& g, const TopkWs& w, char* ws, const float* q, const void* k_cache,
+                         const RangeTab& tab, float scale, const int32_t* active, int32_t* idx_out,
+                         const DevInfo* di, hipStream_t s) {
+  float* scores = (float*)(ws + w.scores);
+  uint32_t* hist = (uint32_t*)(ws + w.hist);
+  int32_t* list = (int32_t*)(ws + w.list);
+  uint32_t* list_cnt = (uint32_t*)(ws + w.list_cnt);
+  // 1. scan
+  {
+    ScanArgs a{};
+    a.q = q;
+    a.k = (const char*)k_cache;
+    a.stride_b_bytes = g.sb_bytes;
+    a.stride_h_bytes = g.sh_bytes;
+    a.scores = scores;
+    a.hist = hist;
+    a.n = w.n;
+    a.n_pad = w.n_pad;
+    a.Hq = g.Hq;
+    a.Hkv = g.Hkv;
+    a.scale = scale;
+    a.head_active = active;
+    a.tab = tab;
+    const int ri = g.bf16 ? scan_rows_iter<uint16_t>(g.G) : scan_rows_iter<float>(g.G);
+    // about 4 workgroups per CU over the whole grid, whole iterations each
+    const int64_t target_blocks = 1024;
+    const int64_t per_group = std::max<int64_t>(1, target_blocks / g.groups);
+    const int64_t rpb = std::max<int64_t>(ri, rup(cdiv(w.n, per_group), ri));
+    a.rows_per_block = rpb;
+    a.blocks_per_group = (int32_t)cdiv(w.n, rpb);
+    const dim3 grid((unsigned)(g.groups * a.blocks_per_group));
+    STDK_TRY(launch(KID_SCAN, s, [&] {
+      if (g.bf16) launch_scan_t<uint16_t>(g.G, grid, s, a);
+      else launch_scan_t<float>(g.G, grid, s, a);
+    }));
+  }
+  // 2. filter
+  {
+    FilterArgs a{};
+    a.scores = scores;
+    a.hist = hist;
+    a.list = list;
+    a.list_cnt = list_cnt;
+    a.n = w.n;
+    a.n_pad = w.n_pad;
+    a.K = (int32_t)w.K;
+    a.seg_active = active;
+    a.chunk = std::max<int64_t>(4096, rup(cdiv(w.n * w.S, 1024), 1024));
+    const dim3 grid((unsigned)cdiv(w.n, a.chunk), (unsigned)w.S);
+    STDK_TRY(launch(KID_FILTER, s, [&] { hipLaunchKernelGGL(topk_filter, grid, dim3(kFilterThreads), 0, s, a); }));
+  }
+  // 3. select
+  {
+    SelectArgs a{};
+    a.scores = scores;
+    a.hist = hist;
+    a.list = list;
+    a.list_cnt = list_cnt;
+    a.n = w.n;
+    a.n_pad = w.n_pad;
+    a.K = (int32_t)w.K;
+    a.bitmap_words = (int32_t)w.words;
+    a.sel_row = (int32_t*)(ws + w.sel_row);
+    a.sel_z = (float*)(ws + w.sel_z);
+    a.idx_out = idx_out;
+    a.gbitmap = (uint32_t*)(ws + w.gbitmap);
+    a.seg_active = active;
+    a.tab = tab;
+    const size_t bm_bytes = (size_t)w.words * 4;
+    const bool lds = bm_bytes + 12 * 1024 <= (size_t)di->max_lds;
+    STDK_TRY(launch(KID_SELECT, s, [&] {
+      if (lds)
+        hipLaunchKernelGGL(topk_select<true>, dim3((unsigned)w.S), dim3(kSelectThreads), bm_bytes, s, a);
+      else
+        hipLaunchKernelGGL(topk_select<false>, dim3((unsigned)w.S), dim3(kSelectThreads), 0, s, a);
+    }));
+  }
+  return STDK_OK;
+}
+
+int32_t run_sparse_sv(const Geo& g, const TopkWs& w, char* ws, const void* v_cache, float* o_out,
+                      float* lse_out, hipStream_t s) {
+  SvArgs a{};
+  a.v = (const char*)v_cache;
+  a.stride_b_bytes = g.sb_bytes;
+  a.stride_h_bytes = g.sh_bytes;
+  a.sel_row = (const int32_t*)(ws + w.sel_row);
+  a.sel_z = (const float*)(ws + w.sel_z);
+  a.part = (float*)(ws + w.part);
+  a.done = (uint32_t*)(ws + w.done);
+  a.o_out = o_out;
+  a.lse_out = lse_out;
+  a.K = (int32_t)w.K;
+  a.nsplit = (int32_t)w.nsplit;
+  a.Hq = g.Hq;
+  a.G = g.G;
+  const dim3 grid((unsigned)w.nsplit, (unsigned)w.S);
+  return launch(KID_SV, s, [&] {
+    if (g.bf16) hipLaunchKernelGGL(sparse_sv<uint16_t>, grid, dim3(kSvThreads), 0, s, a);
+    else hipLaunchKernelGGL(sparse_sv<float>, grid, dim3(kSvThreads), 0, s, a);
+  });
+}
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+extern "C" {
+
+const char* stdk_last_error(void) { return g_err.c_str(); }
+int32_t stdk_version(void) { return STDK_VERSION; }
+
+size_t topk_attn_decode_workspace_size(const stdk_layout* lay, int64_t n_scan, int32_t top_k) {
+  if (check_layout(lay) != STDK_OK || n_scan < 0 || top_k < 1) return 0;
+  const Geo g = geo_of(lay);
+  return topk_ws(g.S, g.groups, n_scan, top_k).total;
+}
+
+int32_t topk_attn_decode(const stdk_layout* lay, const float* q, const void* k_cache, const void* v_cache,
+                         const int64_t* ranges, int32_t n_ranges, int32_t top_k, float scale, int32_t* idx_out,
+                         float* o_out, float* lse_out, void* workspace, size_t workspace_bytes, void* stream) {
+  STDK_TRY(check_layout(lay));
+  STDK_TRY(check_ptr(q, "q", 16));
+  STDK_TRY(check_ptr(k_cache, "k_cache", 16));
+  STDK_TRY(check_ptr(v_cache, "v_cache", 16));
+  STDK_TRY(check_ptr(o_out, "o_out", 4));
+  STDK_TRY(check_ptr(lse_out, "lse_out", 4));
+  if (idx_out && ((uintptr_t)idx_out) % 4) return fail(STDK_EINVAL, "idx_out is not 4-byte aligned");
+  if (top_k < 1) return fail(STDK_EINVAL, "top_k %d < 1", top_k);
+  if (n_ranges < 0 || n_ranges > STDK_MAX_RANGES) return fail(STDK_EINVAL, "n_ranges %d outside 0..%d", n_ranges, STDK_MAX_RANGES);
+  if (n_ranges > 0 && !ranges) return fail(STDK_EINVAL, "ranges is NULL");
+  if (!std::isfinite(scale)) return fail(STDK_EINVAL, "scale is not finite");
+  int64_t prev_end = 0;
+  for (int r = 0; r < n_ranges; ++r) {
+    const int64_t b = ranges[2 * r], e = ranges[2 * r + 1];
+    if (b < 0 || e > lay->max_len || e <= b) return fail(STDK_EINVAL, "range %d [%lld, %lld) invalid", r, (long long)b, (long long)e);
+    if (r > 0 && b < prev_end) return fail(STDK_EINVAL, "ranges must be ascending and disjoint");
+    prev_end = e;
+  }
+  int64_t n = 0;
+  const RangeTab tab = make_tab(ranges, n_ranges, &n);
+  const Geo g = geo_of(lay);
+  const TopkWs w = topk_ws(g.S, g.groups, n, top_k);
+  if (n > 0) {
+    STDK_TRY(check_ptr(workspace, "workspace", 256));
+    if (workspace_bytes < w.total)
+      return fail(STDK_EWORKSPACE, "workspace is %zu bytes, %zu needed", workspace_bytes, w.total);
+  }
+  hipStream_t s = (hipStream_t)stream;
+  DevInfo* di = nullptr;
+  STDK_TRY(dev_info(&di));
+  char* ws = (char*)workspace;
+
+  if (n == 0) {
+    const int64_t m = std::max<int64_t>(g.S * kHeadDim, g.S * (int64_t)top_k);
+    STDK_TRY(launch(KID_FILL, s, [&] {
+      hipLaunchKernelGGL(fill_empty, dim3((unsigned)cdiv(m, 256)), dim3(256), 0, s, o_out, lse_out, idx_out, g.S,
+                         top_k);
+    }));
+    return ok();
+  }
+  STDK_TRY(run_clear(s, (uint32_t*)(ws + w.clear_off), (int64_t)w.clear_words));
+  if (top_k >= n) {
+    DenseArgs a{};
+    a.q = q;
+    a.k = (const char*)k_cache;
+    a.v = (const char*)v_cache;
+    a.stride_b_bytes = g.sb_bytes;
+    a.stride_h_bytes = g.sh_bytes;
+    a.part = (float*)(ws + w.part);
+    a.done = (uint32_t*)(ws + w.done_grp);
+    a.o_out = o_out;
+    a.lse_out = lse_out;
+    a.idx_out = idx_out;
+    a.n = n;
+    a.Hq = g.Hq;
+    a.Hkv = g.Hkv;
+    a.K = top_k;
+    a.scale = scale;
+    a.tab = tab;
+    const int64_t nwg = std::min<int64_t>(kDenseMaxWg, cdiv(n, kDenseTile));
+    a.rows_per_wg = rup(cdiv(n, nwg), kDenseTile);
+    a.nwg = (int32_t)cdiv(n, a.rows_per_wg);
+    const dim3 grid((unsigned)a.nwg, (unsigned)g.groups);
+    STDK_TRY(launch(KID_DENSE, s, [&] {
+      if (g.bf16) launch_dense_t<uint16_t>(g.G, grid, s, a);
+      else launch_dense_t<float>(g.G, grid, s, a);
+    }));
+    return ok();
+  }
+  STDK_TRY(run_exact_select(g, w, ws, q, k_cache, tab, scale, nullptr, idx_out, di, s));
+  STDK_TRY(run_sparse_sv(g, w, ws, v_cache, o_out, lse_out, s));
+  return ok();
+}
+
+int32_t attn_merge_lse(int64_t rows, int32_t d, const float* o_a, const float* lse_a, const float* o_b,
+                       const float* lse_b, float* o_out, float* lse_out, void* stream) {
+  if (rows < 0) return fail(STDK_EINVAL, "rows %lld < 0", (long long)rows);
+  if (d < 1 || d > 1024) return fail(STDK_EINVAL, "d %d outside 1..1024", d);
+  if (rows == 0) return ok();
+  STDK_TRY(check_ptr(o_a, "o_a", 4));
+  STDK_TRY(check_ptr(lse_a, "lse_a", 4));
+  STDK_TRY(check_ptr(o_b, "o_b", 4));
+  STDK_TRY(check_ptr(lse_b, "lse_b", 4));
+  STDK_TRY(check_ptr(o_out, "o_out", 4));
+  STDK_TRY(check_ptr(lse_out, "lse_out", 4));
+  hipStream_t s = (hipStream_t)stream;
+  MergeArgs a{o_a, lse_a, o_b, lse_b, o_out, lse_out, rows, d, 0};
+  STDK_TRY(launch(KID_MERGE, s, [&] {
+    hipLaunchKernelGGL(attn_merge, dim3((unsigned)cdiv(rows, 2)), dim3(kMergeThreads), 0, s, a);
+  }));
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+// ReTopK
+// ---------------------------------------------------------------------------
+namespace {
+
+int32_t check_retopk(const stdk_layout* lay, const retopk_params* p, const retopk_state* st) {
+  STDK_TRY(check_layout(lay));
+  if (!p) return fail(STDK_EINVAL, "params is NULL");
+  if (!st) return fail(STDK_EINVAL, "state is NULL");
+  if (p->top_k < 1) return fail(STDK_EINVAL, "top_k %d < 1", p->top_k);
+  if (p->cache_cap < 1 || p->cache_cap > kMaxCache) return fail(STDK_EINVAL, "cache_cap %d outside 1..%d", p->cache_cap, kMaxCache);
+  if (p->top_r < 1 || p->top_r > p->cache_cap) return fail(STDK_EINVAL, "top_r %d outside 1..cache_cap", p->top_r);
+  if (p->recent < 0) return fail(STDK_EINVAL, "recent %d < 0", p->recent);
+  if (p->refresh < 0) return fail(STDK_EINVAL, "refresh %d < 0", p->refresh);
+  if (std::isnan(p->tau)) return fail(STDK_EINVAL, "tau is NaN");
+  if (!std::isfinite(p->scale)) return fail(STDK_EINVAL, "scale is not finite");
+  if ((int64_t)p->top_r * p->top_k + p->recent > 0x7FFFFFFFLL) return fail(STDK_EINVAL, "R*K + W too large");
+  STDK_TRY(check_ptr(st->q_hat, "state.q_hat", 16));
+  STDK_TRY(check_ptr(st->support, "state.support", 4));
+  STDK_TRY(check_ptr(st->head, "state.head", 4));
+  STDK_TRY(check_ptr(st->count, "state.count", 4));
+  return STDK_OK;
+}
+
+struct RetopkWs {
+  TopkWs t;  // exact path (scores, list, hist, sel, part, bitmap)
+  int64_t cand_cap;
+  size_t cand, n_cand, cz, qbar, path, exact, total;
+};
+
+RetopkWs retopk_ws(const Geo& g, const retopk_params* p, int64_t max_L) {
+  RetopkWs r{};
+  r.t = topk_ws(g.S, g.groups, max_L, p->top_k);
+  r.cand_cap = (int64_t)p->top_r * p->top_k + p->recent;
+  size_t off = r.t.total;
+  r.cand = off;
+  off = al256(off + (size_t)g.S * r.cand_cap * 4);
+  r.cz = off;
+  off = al256(off + (size_t)g.S * r.cand_cap * 4);
+  r.n_cand = off;
+  off = al256(off + (size_t)g.S * 4);
+  r.qbar = off;
+  off = al256(off + (size_t)g.S * kHeadDim * 4);
+  r.path = off;
+  off = al256(off + (size_t)g.S * 4);
+  r.exact = off;
+  off = al256(off + (size_t)g.S * 4);
+  r.total = off;
+  return r;
+}
+
+}  // namespace
+
+size_t retopk_workspace_size(const stdk_layout* lay, const retopk_params* p, int64_t max_L_t) {
+  if (check_layout(lay) != STDK_OK || !p || p->top_k < 1 || p->top_r < 1 || p->recent < 0 || max_L_t < 1) return 0;
+  return retopk_ws(geo_of(lay), p, max_L_t).total;
+}
+
+int32_t retopk_state_init(const stdk_layout* lay, const retopk_params* p, const retopk_state* st,
+                          const float* q_hist, const int32_t* sup_hist, int32_t n_hist, void* stream) {
+  STDK_TRY(check_retopk(lay, p, st));
+  if (n_hist < 0) return fail(STDK_EINVAL, "n_hist %d < 0", n_hist);
+  if (n_hist > 0) {
+    STDK_TRY(check_ptr(q_hist, "q_hist", 4));
+    STDK_TRY(check_ptr(sup_hist, "sup_hist", 4));
+  }
+  const Geo g = geo_of(lay);
+  hipStream_t s = (hipStream_t)stream;
+  RtInitArgs a{q_hist, sup_hist, st->q_hat, st->support, st->head, st->count, p->cache_cap, p->top_k, n_hist, 0};
+  STDK_TRY(launch(KID_RT_INIT, s, [&] { hipLaunchKernelGGL(retopk_init, dim3((unsigned)g.S), dim3(256), 0, s, a); }));
+  return ok();
+}
+
+int32_t retopk_step(const stdk_layout* lay, const retopk_params* p, const retopk_state* st, const float* q,
+                    const void* k_cache, const void* v_cache, int64_t L_t, int64_t t, int32_t* support_out,
+                    float* o_out, float* lse_out, int32_t* path_out, int32_t* n_cand_out, int32_t* cand_out,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  STDK_TRY(check_retopk(lay, p, st));
+  STDK_TRY(check_ptr(q, "q", 16));
+  STDK_TRY(check_ptr(k_cache, "k_cache", 16));
+  STDK_TRY(check_ptr(v_cache, "v_cache", 16));
+  STDK_TRY(check_ptr(support_out, "support_out", 4));
+  STDK_TRY(check_ptr(o_out, "o_out", 4));
+  STDK_TRY(check_ptr(lse_out, "lse_out", 4));
+  if (L_t < 1 || L_t > lay->max_len) return fail(STDK_EINVAL, "L_t %lld outside 1..max_len", (long long)L_t);
+  if (L_t > (1 << 20)) return fail(STDK_EUNSUPPORTED, "L_t %lld > 1048576", (long long)L_t);
+  if (t < 0) return fail(STDK_EINVAL, "t %lld < 0", (long long)t);
+  const Geo g = geo_of(lay);
+  const RetopkWs w = retopk_ws(g, p, L_t);
+  STDK_TRY(check_ptr(workspace, "workspace", 256));
+  if (workspace_bytes < w.total)
+    return fail(STDK_EWORKSPACE, "workspace is %zu bytes, %zu needed", workspace_bytes, w.total);
+  hipStream_t s = (hipStream_t)stream;
+  DevInfo* di = nullptr;
+  STDK_TRY(dev_info(&di));
+  char* ws = (char*)workspace;
+  const bool refresh_now = p->refresh > 0 && (t % p->refresh) == 0;
+  int32_t* exact = (int32_t*)(ws + w.exact);
+
+  STDK_TRY(run_clear(s, (uint32_t*)(ws + w.t.clear_off), (int64_t)w.t.clear_words));
+  // a6: selector (cosine, path, top-R, candidate union)
+  {
+    RtSelArgs a{};
+    a.q = q;
+    a.q_hat = st->q_hat;
+    a.support = st->support;
+    a.head = st->head;
+    a.count = st->count;
+    a.C = p->cache_cap;
+    a.K = p->top_k;
+    a.R = p->top_r;
+    a.W = p->recent;
+    a.tau = p->tau;
+    a.refresh_now = refresh_now ? 1 : 0;
+    a.L_t = L_t;
+    a.cand_cap = (int32_t)w.cand_cap;
+    a.bitmap_words = (int32_t)cdiv(L_t, 32);
+    a.qbar = (float*)(ws + w.qbar);
+    a.path = (int32_t*)(ws + w.path);
+    a.exact = exact;
+    a.cand = (int32_t*)(ws + w.cand);
+    a.n_cand = (int32_t*)(ws + w.n_cand);
+    a.path_out = path_out;
+    a.n_cand_out = n_cand_out;
+    a.cand_out = cand_out;
+    a.gbitmap = (uint32_t*)(ws + w.t.gbitmap);
+    const size_t bm_bytes = (size_t)a.bitmap_words * 4;
+    const bool lds = bm_bytes + 12 * 1024 <= (size_t)di->max_lds;
+    STDK_TRY(launch(KID_RT_SELECT, s, [&] {
+      if (lds) hipLaunchKernelGGL(retopk_select<true>, dim3((unsigned)g.S), dim3(kRtSelThreads), bm_bytes, s, a);
+      else hipLaunchKernelGGL(retopk_select<false>, dim3((unsigned)g.S), dim3(kRtSelThreads), 0, s, a);
+    }));
+  }
+  // exact heads: a1 + a2 over [0, L_t)
+  const int64_t rng[2] = {0, L_t};
+  int64_t n_all = 0;
+  const RangeTab tab = make_tab(rng, 1, &n_all);
+  const TopkWs& tw = w.t;  // laid out for n = L_t
+  const int32_t* active = refresh_now ? nullptr : exact;
+  if (L_t > p->top_k) {
+    STDK_TRY(run_exact_select(g, tw, ws, q, k_cache, tab, p->scale, active, support_out, di, s));
+  } else {
+    // every visible row is chosen: score them, then take all
+    ScanArgs a{};
+    a.q = q;
+    a.k = (const char*)k_cache;
+    a.stride_b_bytes = g.sb_bytes;
+    a.stride_h_bytes = g.sh_bytes;
+    a.scores = (float*)(ws + tw.scores);
+    a.hist = (uint32_t*)(ws + tw.hist);
+    a.n = L_t;
+    a.n_pad = tw.n_pad;
+    a.Hq = g.Hq;
+    a.Hkv = g.Hkv;
+    a.scale = p->scale;
+    a.head_active = active;
+    a.tab = tab;
+    const int ri = g.bf16 ? scan_rows_iter<uint16_t>(g.G) : scan_rows_iter<float>(g.G);
+    a.rows_per_block = rup(L_t, ri);
+    a.blocks_per_group = 1;
+    const dim3 grid((unsigned)g.groups);
+    STDK_TRY(launch(KID_SCAN, s, [&] {
+      if (g.bf16) launch_scan_t<uint16_t>(g.G, grid, s, a);
+      else launch_scan_t<float>(g.G, grid, s, a);
+    }));
+    SelectAllArgs b{};
+    b.scores = (const float*)(ws + tw.scores);
+    b.seg_active = active;
+    b.sel_row = (int32_t*)(ws + tw.sel_row);
+    b.sel_z = (float*)(ws + tw.sel_z);
+    b.idx_out = support_out;
+    b.n = L_t;
+    b.n_pad = tw.n_pad;
+    b.K = p->top_k;
+    b.tab = tab;
+    STDK_TRY(launch(KID_SELECT, s, [&] { hipLaunchKernelGGL(select_all, dim3((unsigned)g.S), dim3(256), 0, s, b); }));
+  }
+  // reuse heads: a7 indexed QK + rerank
+  if (!refresh_now) {
+    RtRerankArgs a{};
+    a.q = q;
+    a.k = (const char*)k_cache;
+    a.stride_b_bytes = g.sb_bytes;
+    a.stride_h_bytes = g.sh_bytes;
+    a.exact = exact;
+    a.cand = (const int32_t*)(ws + w.cand);
+    a.n_cand = (const int32_t*)(ws + w.n_cand);
+    a.cz = (float*)(ws + w.cz);
+    a.done = (uint32_t*)(ws + tw.done_rr);
+    a.sel_row = (int32_t*)(ws + tw.sel_row);
+    a.sel_z = (float*)(ws + tw.sel_z);
+    a.support_out = support_out;
+    a.cand_cap = (int32_t)w.cand_cap;
+    a.K = p->top_k;
+    a.Hq = g.Hq;
+    a.G = g.G;
+    a.nsplit = (int32_t)cdiv(w.cand_cap, kRerankRows);
+    a.scale = p->scale;
+    const dim3 grid((unsigned)a.nsplit, (unsigned)g.S);
+    STDK_TRY(launch(KID_RT_RERANK, s, [&] {
+      if (g.bf16) hipLaunchKernelGGL(retopk_rerank<uint16_t>, grid, dim3(kRerankThreads), 0, s, a);
+      else hipLaunchKernelGGL(retopk_rerank<float>, grid, dim3(kRerankThreads), 0, s, a);
+    }));
+  }
+  // a8: softmax . V over the chosen rows, then the push
+  STDK_TRY(run_sparse_sv(g, tw, ws, v_cache, o_out, lse_out, s));
+  {
+    RtPushArgs a{(const float*)(ws + w.qbar), support_out, st->q_hat, st->support, st->head, st->count,
+                 p->cache_cap, p->top_k};
+    STDK_TRY(launch(KID_RT_PUSH, s, [&] { hipLaunchKernelGGL(retopk_push, dim3((unsigned)g.S), dim3(256), 0, s, a); }));
+  }
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+// launch timing
+// ---------------------------------------------------------------------------
+int32_t stdk_profile_enable(int32_t capacity) {
+  if (capacity < 1) return fail(STDK_EINVAL, "capacity %d < 1", capacity);
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  const size_t want = (size_t)capacity * 2;
+  while (g_prof.ev.size() < want) {
+    hipEvent_t e;
+    const hipError_t err = hipEventCreate(&e);
+    if (err != hipSuccess) return fail(STDK_EHIP, "hipEventCreate: %s", hipGetErrorString(err));
+    g_prof.ev.push_back(e);
+  }
+  g_prof.kid.assign((size_t)capacity, 0);
+  g_prof.used = 0;
+  g_prof.on = true;
+  return ok();
+}
+
+int32_t stdk_profile_disable(void) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  g_prof.on = false;
+  return ok();
+}
+
+int32_t stdk_profile_reset(void) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  g_prof.used = 0;
+  for (int i = 0; i < KID_COUNT; ++i) {
+    g_prof.total_ms[i] = 0.0;
+    g_prof.launches[i] = 0;
+  }
+  return ok();
+}
+
+int32_t stdk_profile_read(const char* name, double* total_ms, int64_t* launches) {
+  if (!name || !total_ms || !launches) return fail(STDK_EINVAL, "NULL argument");
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  for (size_t i = 0; i < g_prof.used; ++i) {
+    hipError_t e = hipEventSynchronize(g_prof.ev[2 * i + 1]);
+    if (e != hipSuccess) return fail(STDK_EHIP, "hipEventSynchronize: %s", hipGetErrorString(e));
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]);
+    if (e != hipSuccess) return fail(STDK_EHIP, "hipEventElapsedTime: %s", hipGetErrorString(e));
+    g_prof.total_ms[g_prof.kid[i]] += ms;
+    g_prof.launches[g_prof.kid[i]] += 1;
+  }
+  g_prof.used = 0;
+  for (int i = 0; i < KID_COUNT; ++i) {
+    if (std::strcmp(name, kKernelNames[i]) == 0) {
+      *total_ms = g_prof.total_ms[i];
+      *launches = g_prof.launches[i];
+      return ok();
+    }
+  }
+  return fail(STDK_EINVAL, "unknown kernel name %s", name);
+}
+
+}  // extern "C"

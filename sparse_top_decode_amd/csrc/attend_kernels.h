@@ -1,0 +1,400 @@
+// Renormalised softmax . V over a row set, and the log-sum-exp combination.
+//
+// Both follow the RetrievalAttention review: Eq. 2 ("Approximated Attention
+// Formulation": softmax over the chosen subset only) written with a local
+// maximum as in "CPU-GPU Co-Execution Architecture" (o_W, o_Omega), and the
+// rescaled combination of Eq. 4-5 (gamma_j = e^{lse_j - lse}). Work is split
+// over several workgroups per head; each produces (m, s, sum e^{z-m} v) for
+// its rows and the last workgroup to finish combines them in a fixed order
+// with the same rescaling, so the result does not depend on timing.
+#pragma once
+
+#include "device.h"
+#include "scan_kernels.h"
+
+namespace stdk {
+
+constexpr int kPartStride = 132;  // m, s, pad, pad, o[128]
+
+// Combines `np` partials (m, s, o) starting at `part` into o_out[128] and
+// *lse_out. Runs on the first 128 threads of the block.
+STDK_DEV void combine_partials(const float* part, int np, float* o_out, float* lse_out) {
+  const int j = threadIdx.x;
+  if (j >= kHeadDim) return;
+  float M = -INFINITY;
+  for (int i = 0; i < np; ++i) M = fmaxf(M, part[(int64_t)i * kPartStride]);
+  float S = 0.f, O = 0.f;
+  if (M != -INFINITY) {
+    for (int i = 0; i < np; ++i) {
+      const float* p = part + (int64_t)i * kPartStride;
+      const float mi = p[0];
+      if (mi == -INFINITY) continue;
+      const float f = __expf(mi - M);
+      S = fmaf(p[1], f, S);
+      O = fmaf(p[4 + j], f, O);
+    }
+  }
+  if (S > 0.f) {
+    o_out[j] = O / S;
+    if (j == 0) *lse_out = M + __logf(S);
+  } else {
+    o_out[j] = 0.f;
+    if (j == 0) *lse_out = -INFINITY;
+  }
+}
+
+// Last-arriver election: returns true in every thread of the workgroup that
+// is the last of `expected` to arrive on `counter`, and resets the counter.
+STDK_DEV bool last_to_arrive(uint32_t* counter, uint32_t expected, int* s_flag) {
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev = atomicAdd(counter, 1u);
+    const bool last = prev == expected - 1;
+    if (last) atomicExch(counter, 0u);
+    *s_flag = last ? 1 : 0;
+  }
+  __syncthreads();
+  const bool last = *s_flag != 0;
+  if (last) __threadfence();
+  return last;
+}
+
+// ---------------------------------------------------------------------------
+// sparse_sv: gathered-row softmax . V over K chosen rows per segment.
+// ---------------------------------------------------------------------------
+struct SvArgs {
+  const char* v;           // value cache base
+  int64_t stride_b_bytes, stride_h_bytes;
+  const int32_t* sel_row;  // [S][K], -1 = unused slot
+  const float* sel_z;      // [S][K]
+  float* part;             // [S][nsplit][kPartStride]
+  uint32_t* done;          // [S] counters (start at 0, left at 0)
+  float* o_out;            // [S][128]
+  float* lse_out;          // [S]
+  int32_t K, nsplit, Hq, G;
+};
+
+constexpr int kSvThreads = 256;
+constexpr int kSvRows = 64;  // rows per workgroup
+
+template <typename T>
+__global__ __launch_bounds__(kSvThreads) void sparse_sv(SvArgs a) {
+  constexpr int EPL = KvTraits<T>::EPL, LPR = KvTraits<T>::LPR, RPL = KvTraits<T>::RPL, ROWB = KvTraits<T>::ROWB;
+  constexpr int NW = kSvThreads / 64;
+  constexpr int GROUPS = NW * RPL;  // row groups in the block
+  __shared__ int32_t rows[kSvRows];
+  __shared__ float wts[kSvRows];
+  __shared__ float red[GROUPS][kHeadDim];
+  __shared__ float s_m;
+  __shared__ int s_flag;
+  const int64_t seg = blockIdx.y;
+  const int split = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int rg = lane / LPR, c = lane % LPR;
+  const int b = (int)(seg / a.Hq), hq = (int)(seg % a.Hq), hkv = hq / a.G;
+  const int j0 = split * kSvRows;
+  const int nr = min(kSvRows, a.K - j0);
+
+  float z = -INFINITY;
+  if (tid < kSvRows) {
+    int32_t r = -1;
+    if (tid < nr) {
+      r = a.sel_row[seg * a.K + j0 + tid];
+      if (r >= 0) z = a.sel_z[seg * a.K + j0 + tid];
+    }
+    rows[tid] = r;
+  }
+  // block max over the 64 scores (held by wave 0)
+  if (w == 0) {
+    const float mx = wave_max(z);
+    if (lane == 0) s_m = mx;
+  }
+  __syncthreads();
+  const float m = s_m;
+  if (tid < kSvRows) wts[tid] = (m == -INFINITY || z == -INFINITY) ? 0.f : __expf(z - m);
+  __syncthreads();
+
+  const char* vb = a.v + (int64_t)b * a.stride_b_bytes + (int64_t)hkv * a.stride_h_bytes;
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  const int gid = w * RPL + rg;  // row group id in the block
+  for (int i = gid; i < kSvRows; i += GROUPS) {
+    const int32_t r = rows[i];
+    if (r < 0) continue;
+    const float wt = wts[i];
+    float x[EPL];
+    unpack16<T>(load16(vb + (int64_t)r * ROWB + c * 16), x);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = fmaf(wt, x[e], acc[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) red[gid][c * EPL + e] = acc[e];
+  __syncthreads();
+  float* part = a.part + (seg * a.nsplit + split) * kPartStride;
+  if (tid < kHeadDim) {
+    float o = 0.f;
+#pragma unroll
+    for (int g = 0; g < GROUPS; ++g) o += red[g][tid];
+    part[4 + tid] = o;
+  }
+  if (w == 0) {
+    const float s = wave_sum(tid < kSvRows ? wts[tid] : 0.f);
+    if (lane == 0) {
+      part[0] = m;
+      part[1] = s;
+    }
+  }
+  if (last_to_arrive(&a.done[seg], (uint32_t)a.nsplit, &s_flag))
+    combine_partials(a.part + seg * a.nsplit * kPartStride, a.nsplit, a.o_out + seg * kHeadDim, a.lse_out + seg);
+}
+
+// ---------------------------------------------------------------------------
+// dense_attn: softmax . V over every row of the ranges (K >= n), G heads per
+// KV head from one read of each K and V row. Tiles of 64 rows with a running
+// maximum; one partial per (head, workgroup).
+// ---------------------------------------------------------------------------
+struct DenseArgs {
+  const float* q;
+  const char* k;
+  const char* v;
+  int64_t stride_b_bytes, stride_h_bytes;
+  float* part;             // [S][nwg][kPartStride]
+  uint32_t* done;          // [B*Hkv]
+  float* o_out;            // [S][128]
+  float* lse_out;          // [S]
+  int32_t* idx_out;        // [S][K] or null
+  int64_t n;
+  int64_t rows_per_wg;
+  int32_t nwg, Hq, Hkv, K;
+  float scale;
+  int32_t pad_;
+  RangeTab tab;
+};
+
+constexpr int kDenseThreads = 256;
+constexpr int kDenseTile = 64;  // one row per lane of a wave in the tile reductions
+
+template <typename T, int G>
+__global__ __launch_bounds__(kDenseThreads) void dense_attn(DenseArgs a) {
+  constexpr int EPL = KvTraits<T>::EPL, LPR = KvTraits<T>::LPR, RPL = KvTraits<T>::RPL, ROWB = KvTraits<T>::ROWB;
+  constexpr int NW = kDenseThreads / 64;
+  constexpr int U = kDenseTile / (NW * RPL);  // tile rows per wave load group
+  constexpr int GROUPS = NW * RPL;
+  __shared__ float zt[G][kDenseTile];
+  __shared__ int64_t trow[kDenseTile];
+  __shared__ float tmax[G], tsum[G];
+  __shared__ float red[NW][G][kHeadDim];
+  __shared__ int s_flag;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int rg = lane / LPR, c = lane % LPR;
+  const int group = blockIdx.y;
+  const int wg = blockIdx.x;
+  const int b = group / a.Hkv, hkv = group % a.Hkv;
+  const int64_t seg0 = (int64_t)b * a.Hq + (int64_t)hkv * G;
+  float qr[G][EPL];
+  load_q_slice<T, G>(a.q, seg0, c, qr);
+  const char* kb = a.k + (int64_t)b * a.stride_b_bytes + (int64_t)hkv * a.stride_h_bytes;
+  const char* vb = a.v + (int64_t)b * a.stride_b_bytes + (int64_t)hkv * a.stride_h_bytes;
+
+  float m_run[G], s_run[G], acc[G][EPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m_run[h] = -INFINITY;
+    s_run[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+  }
+
+  const int64_t p0 = (int64_t)wg * a.rows_per_wg;
+  const int64_t p1 = min(a.n, p0 + a.rows_per_wg);
+  for (int64_t tb = p0; tb < p1; tb += kDenseTile) {
+    if (tid < kDenseTile) {
+      const int64_t p = tb + tid;
+      trow[tid] = p < p1 ? pos_to_row(a.tab, p) : -1;
+    }
+    __syncthreads();
+    // scores of the tile
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = (w * U + u) * RPL + rg;
+      const int64_t r = trow[i];
+      u32x4 kw = u32x4{0u, 0u, 0u, 0u};
+      if (r >= 0) kw = load16(kb + r * ROWB + c * 16);
+      float d[G];
+      chunk_dots<T, G>(kw, qr, d);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float s = group_sum<LPR>(d[h]);
+        if (c == h) zt[h][i] = (r >= 0) ? s * a.scale : -INFINITY;
+      }
+    }
+    __syncthreads();
+    // per-head tile maximum and new running maximum
+    for (int h = w; h < G; h += NW) {
+      const float mx = wave_max(zt[h][lane]);
+      if (lane == 0) tmax[h] = mx;
+    }
+    __syncthreads();
+    float f_old[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float mn = fmaxf(m_run[h], tmax[h]);
+      f_old[h] = (m_run[h] == -INFINITY) ? 0.f : __expf(m_run[h] - mn);
+      m_run[h] = mn;
+    }
+    // weights e^{z - m} in place, and their tile sums
+    if (tid < kDenseTile) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float zz = zt[h][tid];
+        zt[h][tid] = (zz == -INFINITY) ? 0.f : __expf(zz - m_run[h]);
+      }
+    }
+    __syncthreads();
+    for (int h = w; h < G; h += NW) {
+      const float sm = wave_sum(zt[h][lane]);
+      if (lane == 0) tsum[h] = sm;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      s_run[h] = s_run[h] * f_old[h] + tsum[h];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] *= f_old[h];
+    }
+    // value rows of the tile
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = (w * U + u) * RPL + rg;
+      const int64_t r = trow[i];
+      if (r < 0) continue;
+      float x[EPL];
+      unpack16<T>(load16(vb + r * ROWB + c * 16), x);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float wt = zt[h][i];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(wt, x[e], acc[h][e]);
+      }
+    }
+    __syncthreads();
+  }
+  // reduce the row groups of each wave, then the waves
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      float x = acc[h][e];
+      if constexpr (RPL == 4) {
+        x += __shfl_xor(x, 16, 64);
+        x += __shfl_xor(x, 32, 64);
+      } else {
+        x += __shfl_xor(x, 32, 64);
+      }
+      acc[h][e] = x;
+    }
+  if (rg == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) red[w][h][c * EPL + e] = acc[h][e];
+  }
+  __syncthreads();
+  for (int i = tid; i < G * kHeadDim; i += kDenseThreads) {
+    const int h = i / kHeadDim, j = i % kHeadDim;
+    float o = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) o += red[ww][h][j];
+    a.part[((seg0 + h) * a.nwg + wg) * kPartStride + 4 + j] = o;
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    if (tid == h) {
+      float* p = a.part + ((seg0 + h) * a.nwg + wg) * kPartStride;
+      p[0] = m_run[h];
+      p[1] = s_run[h];
+    }
+  }
+  // the row list of a dense call is every position (ascending), -1 padded
+  if (a.idx_out) {
+    for (int64_t p = p0 + tid; p < p1; p += kDenseThreads) {
+      const int32_t row = (int32_t)pos_to_row(a.tab, p);
+#pragma unroll
+      for (int h = 0; h < G; ++h) a.idx_out[(seg0 + h) * a.K + p] = row;
+    }
+    if (wg == 0)
+      for (int64_t p = a.n + tid; p < a.K; p += kDenseThreads)
+#pragma unroll
+        for (int h = 0; h < G; ++h) a.idx_out[(seg0 + h) * a.K + p] = -1;
+  }
+  if (last_to_arrive(&a.done[group], (uint32_t)a.nwg, &s_flag)) {
+    for (int h = 0; h < G; ++h) {
+      combine_partials(a.part + (seg0 + h) * a.nwg * kPartStride, a.nwg, a.o_out + (seg0 + h) * kHeadDim,
+                       a.lse_out + seg0 + h);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// attn_merge: o = e^{lse_a - lse} o_a + e^{lse_b - lse} o_b (Eq. 4-5).
+// One block row of 128 threads per (o, lse) pair; the lse values are read
+// before any thread writes so that the outputs may alias the inputs.
+// ---------------------------------------------------------------------------
+struct MergeArgs {
+  const float *o_a, *lse_a, *o_b, *lse_b;
+  float *o_out, *lse_out;
+  int64_t rows;
+  int32_t d;
+  int32_t pad_;
+};
+
+constexpr int kMergeThreads = 256;
+
+__global__ __launch_bounds__(kMergeThreads) void attn_merge(MergeArgs a) {
+  const int64_t row = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7);
+  const int t = threadIdx.x & 127;
+  float la = -INFINITY, lb = -INFINITY;
+  if (row < a.rows) {
+    la = a.lse_a[row];
+    lb = a.lse_b[row];
+  }
+  __syncthreads();
+  if (row >= a.rows) return;
+  const float M = fmaxf(la, lb);
+  float ga = 0.f, gb = 0.f, lse = -INFINITY;
+  if (M != -INFINITY) {
+    const float ea = (la == -INFINITY) ? 0.f : __expf(la - M);
+    const float eb = (lb == -INFINITY) ? 0.f : __expf(lb - M);
+    const float tot = ea + eb;
+    lse = M + __logf(tot);
+    ga = ea / tot;
+    gb = eb / tot;
+  }
+  for (int j = t; j < a.d; j += 128) {
+    const int64_t i = row * a.d + j;
+    const float xa = a.o_a[i], xb = a.o_b[i];
+    a.o_out[i] = (ga == 0.f ? 0.f : ga * xa) + (gb == 0.f ? 0.f : gb * xb);
+  }
+  if (t == 0) a.lse_out[row] = lse;
+}
+
+// ---------------------------------------------------------------------------
+// small utility kernels
+// ---------------------------------------------------------------------------
+// Zero `words` 32-bit words (counters and histograms of a call's workspace).
+__global__ __launch_bounds__(256) void ws_clear(uint32_t* p, int64_t words) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < words; i += (int64_t)gridDim.x * 256) p[i] = 0u;
+}
+
+// Empty row set: o = 0, lse = -inf, idx = -1.
+__global__ __launch_bounds__(256) void fill_empty(float* o, float* lse, int32_t* idx, int64_t S, int32_t K) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < S * kHeadDim) o[i] = 0.f;
+  if (i < S) lse[i] = -INFINITY;
+  if (idx && i < S * K) idx[i] = -1;
+}
+
+}  // namespace stdk

@@ -1,0 +1,167 @@
+// Device helpers shared by the kernels of libstdk (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define STDK_DEV __device__ __forceinline__
+
+namespace stdk {
+
+constexpr int kHeadDim = 128;
+constexpr int kMaxRanges = 16;
+constexpr int kHistBits = 11;              // first radix digit: bits 31..21 of the key
+constexpr int kHistBins = 1 << kHistBits;  // 2048
+
+// Position -> row map for the union of up to kMaxRanges half-open ranges.
+// Position p lies in range r when pos0[r] <= p < pos0[r+1]; its row is
+// row0[r] + (p - pos0[r]).
+struct RangeTab {
+  int32_t n;
+  int32_t pad_;
+  int64_t row0[kMaxRanges];
+  int64_t pos0[kMaxRanges + 1];
+};
+
+STDK_DEV int64_t pos_to_row(const RangeTab& t, int64_t p) {
+  int r = 0;
+#pragma unroll 1
+  for (int i = 1; i < t.n; ++i)
+    if (p >= t.pos0[i]) r = i;
+  return t.row0[r] + (p - t.pos0[r]);
+}
+
+// Order-preserving map fp32 -> uint32: a > b (as floats) <=> key(a) > key(b).
+// -0 is folded onto +0 so that equal floats give equal keys.
+STDK_DEV uint32_t f2key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+STDK_DEV float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+STDK_DEV float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// DPP row rotate (within each 16-lane row): lane i reads lane (i + n) mod 16.
+template <int N>
+STDK_DEV float row_ror(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of a DPP row; every lane of the row receives the same
+// bits (each step adds two values that are equal across the paired lanes).
+STDK_DEV float row16_sum(float x) {
+  x += row_ror<8>(x);
+  x += row_ror<4>(x);
+  x += row_ror<2>(x);
+  x += row_ror<1>(x);
+  return x;
+}
+
+// Sum over aligned groups of LPR lanes (16 or 32); all lanes of a group get
+// the same bits.
+template <int LPR>
+STDK_DEV float group_sum(float x) {
+  x = row16_sum(x);
+  if constexpr (LPR == 32) x += __shfl_xor(x, 16, 64);
+  return x;
+}
+
+STDK_DEV float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+
+STDK_DEV float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+// Number of set bits of `mask` below this lane.
+STDK_DEV uint32_t lane_rank(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Exclusive prefix sum over the block (NT threads, NT % 64 == 0). `tmp` is
+// LDS of at least NT/64 + 1 words. Returns the exclusive prefix; *total gets
+// the block sum. Ends with a barrier, so `tmp` may be reused afterwards.
+template <int NT>
+STDK_DEV uint32_t block_excl_scan(uint32_t v, uint32_t* tmp, uint32_t* total) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) tmp[w] = x;
+  __syncthreads();
+  if (w == 0) {
+    uint32_t t = (lane < NW) ? tmp[lane] : 0u;
+    uint32_t s = t;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      uint32_t y = __shfl_up(s, o, 64);
+      if (lane >= o) s += y;
+    }
+    if (lane < NW) tmp[lane] = s - t;
+    if (lane == NW - 1) tmp[NW] = s;
+  }
+  __syncthreads();
+  uint32_t res = x - v + tmp[w];
+  *total = tmp[NW];
+  __syncthreads();
+  return res;
+}
+
+// Radix-bin search over an LDS histogram of `nb` bins.
+// DESC: the bin b where the count of strictly higher bins is < need and the
+//       count of bins >= b reaches need (the bin holding the need-th largest).
+// ASC : the same from the low end (the bin holding the need-th smallest).
+// Result in *bin (-1 if the histogram holds fewer than `need` items) and the
+// count strictly beyond it in *beyond. Every thread must call it.
+template <int NT, bool DESC>
+STDK_DEV void find_bin(const uint32_t* hist, int nb, uint32_t need, uint32_t* tmp, int* bin,
+                       uint32_t* beyond) {
+  const int t = threadIdx.x;
+  const int per = (nb + NT - 1) / NT;
+  if (t == 0) {
+    *bin = -1;
+    *beyond = 0;
+  }
+  uint32_t local = 0;
+  for (int i = 0; i < per; ++i) {
+    int j = t * per + i;
+    if (j < nb) local += hist[DESC ? (nb - 1 - j) : j];
+  }
+  uint32_t tot;
+  uint32_t before = block_excl_scan<NT>(local, tmp, &tot);
+  if (before < need && need <= before + local) {
+    uint32_t acc = before;
+    for (int i = 0; i < per; ++i) {
+      int j = t * per + i;
+      if (j >= nb) break;
+      int b = DESC ? (nb - 1 - j) : j;
+      uint32_t h = hist[b];
+      if (acc + h >= need) {
+        *bin = b;
+        *beyond = acc;
+        break;
+      }
+      acc += h;
+    }
+  }
+  __syncthreads();
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+STDK_DEV u32x4 load16_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+STDK_DEV u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+}  // namespace stdk

@@ -1,0 +1,425 @@
+// ReTopK: query-support cache, similar-query recall, candidate union with the
+// recent window, exact rerank inside the candidates, and the cache push.
+//
+// Follows the ReTopK review "Recall Before You Rank: Similarity-Guided Top-K
+// Reuse for Efficient Long-Context Attention", sections "核心方法" 1-5 and the
+// per-step loop printed after them:
+//  1. each query head keeps a FIFO of C (unit query, support) pairs, filled
+//     from the last C prefill queries and pushed after every step on either
+//     path;
+//  2. the cosine of the current unit query with every cached one, and the R
+//     most similar entries;
+//  3. the candidate set is the union of their supports and the W newest rows
+//     (at most R*K + W rows);
+//  4. exact scores of the current query on the candidates, top K of them;
+//  5. the exact path runs instead when the best cosine is below tau or on
+//     every T_r-th step.
+// The candidate union is a bitmap of the visible rows, read back in
+// ascending order (no sort).
+#pragma once
+
+#include "attend_kernels.h"
+#include "device.h"
+#include "scan_kernels.h"
+
+namespace stdk {
+
+// Threads 0..127 each hold one query component; returns that component of
+// q / ||q||_2 (0 for a zero query). Same reduction order everywhere.
+STDK_DEV float unit_component(float x, float* tmp2) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float s = (threadIdx.x < kHeadDim) ? x * x : 0.f;
+  s = wave_sum(s);
+  if (lane == 0 && w < 2) tmp2[w] = s;
+  __syncthreads();
+  const float nrm = sqrtf(tmp2[0] + tmp2[1]);
+  __syncthreads();
+  return nrm > 0.f ? x / nrm : 0.f;
+}
+
+struct RtSelArgs {
+  const float* q;           // [S][128]
+  const float* q_hat;       // [S][C][128]
+  const int32_t* support;   // [S][C][K]
+  const int32_t* head;      // [S]
+  const int32_t* count;     // [S]
+  int32_t C, K, R, W;
+  float tau;
+  int32_t refresh_now;      // this step is a periodic refresh (host decided)
+  int64_t L_t;
+  int32_t cand_cap;         // R*K + W
+  int32_t bitmap_words;     // ceil(L_t / 32)
+  float* qbar;              // [S][128]
+  int32_t* path;            // [S]
+  int32_t* exact;           // [S]: 1 = this head takes the exact path
+  int32_t* cand;            // [S][cand_cap]
+  int32_t* n_cand;          // [S]
+  int32_t* path_out;        // [S] or null
+  int32_t* n_cand_out;      // [S] or null
+  int32_t* cand_out;        // [S][cand_cap] or null
+  uint32_t* gbitmap;        // [S][bitmap_words] when not in LDS
+};
+
+constexpr int kRtSelThreads = 256;
+constexpr int kMaxCache = 64;
+
+template <bool kLdsBitmap>
+__global__ __launch_bounds__(kRtSelThreads) void retopk_select(RtSelArgs a) {
+  extern __shared__ uint32_t dyn[];
+  __shared__ float qb[kHeadDim];
+  __shared__ float rho[kMaxCache];
+  __shared__ int picked[kMaxCache];
+  __shared__ float tmp2[2];
+  __shared__ uint32_t tmp[kRtSelThreads / 64 + 1];
+  __shared__ int s_path;
+  const int64_t seg = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int C = a.C, K = a.K;
+  const int hd = a.head[seg], cnt = a.count[seg];
+
+  // unit query (fp32)
+  const float qx = (tid < kHeadDim) ? a.q[seg * kHeadDim + tid] : 0.f;
+  const float qn = unit_component(qx, tmp2);
+  if (tid < kHeadDim) {
+    qb[tid] = qn;
+    a.qbar[seg * kHeadDim + tid] = qn;
+  }
+  __syncthreads();
+
+  // cosines with the valid entries (entry of slot s has age (head - s) mod C)
+  for (int s = w; s < C; s += kRtSelThreads / 64) {
+    const float* qh = a.q_hat + (seg * C + s) * kHeadDim;
+    const float part = qh[lane] * qb[lane] + qh[lane + 64] * qb[lane + 64];
+    const float r = wave_sum(part);
+    const int age = (hd - s + C) % C;
+    if (lane == 0) rho[s] = (age < cnt) ? r : -INFINITY;
+  }
+  __syncthreads();
+
+  if (tid == 0) {
+    float best = -INFINITY;
+    for (int s = 0; s < C; ++s) {
+      const int age = (hd - s + C) % C;
+      if (age < cnt) best = fmaxf(best, rho[s]);
+    }
+    int path;
+    if (a.refresh_now) path = 2;
+    else if (cnt == 0 || best < a.tau) path = 1;
+    else path = 0;
+    s_path = path;
+    a.path[seg] = path;
+    a.exact[seg] = path != 0;
+    if (a.path_out) a.path_out[seg] = path;
+  }
+  __syncthreads();
+  const int path = s_path;
+  if (path != 0) {
+    if (tid == 0) {
+      a.n_cand[seg] = (int32_t)a.L_t;
+      if (a.n_cand_out) a.n_cand_out[seg] = (int32_t)a.L_t;
+    }
+    if (a.cand_out)
+      for (int i = tid; i < a.cand_cap; i += kRtSelThreads) a.cand_out[seg * a.cand_cap + i] = -1;
+    return;
+  }
+
+  // top-R by (cosine descending, age ascending)
+  if (tid < C) {
+    const int age_e = (hd - tid + C) % C;
+    int pk = 0;
+    if (age_e < cnt) {
+      const float re = rho[tid];
+      int rank = 0;
+      for (int s = 0; s < C; ++s) {
+        const int age_f = (hd - s + C) % C;
+        if (age_f >= cnt || s == tid) continue;
+        const float rf = rho[s];
+        if (rf > re || (rf == re && age_f < age_e)) ++rank;
+      }
+      pk = rank < a.R;
+    }
+    picked[tid] = pk;
+  }
+  const int Wd = a.bitmap_words;
+  uint32_t* bm = kLdsBitmap ? dyn : (a.gbitmap + seg * (int64_t)Wd);
+  for (int i = tid; i < Wd; i += kRtSelThreads) bm[i] = 0u;
+  __syncthreads();
+  const int64_t L = a.L_t;
+  for (int s = 0; s < C; ++s) {
+    if (!picked[s]) continue;
+    const int32_t* sp = a.support + (seg * C + s) * (int64_t)K;
+    for (int i = tid; i < K; i += kRtSelThreads) {
+      const int32_t x = sp[i];
+      if (x >= 0 && x < L) atomicOr(&bm[x >> 5], 1u << (x & 31));
+    }
+  }
+  for (int64_t x = max((int64_t)0, L - a.W) + tid; x < L; x += kRtSelThreads)
+    atomicOr(&bm[x >> 5], 1u << (x & 31));
+  __syncthreads();
+
+  // ascending compaction
+  const int per = (Wd + kRtSelThreads - 1) / kRtSelThreads;
+  const int w0 = tid * per, w1 = min(Wd, w0 + per);
+  uint32_t c0 = 0;
+  for (int i = w0; i < w1; ++i) c0 += __popc(bm[i]);
+  uint32_t total;
+  uint32_t r = block_excl_scan<kRtSelThreads>(c0, tmp, &total);
+  int32_t* cd = a.cand + seg * a.cand_cap;
+  for (int i = w0; i < w1; ++i) {
+    uint32_t bits = bm[i];
+    while (bits) {
+      const int j = __ffs(bits) - 1;
+      bits &= bits - 1;
+      if (r < (uint32_t)a.cand_cap) cd[r] = i * 32 + j;
+      ++r;
+    }
+  }
+  if (tid == 0) {
+    const int32_t M = (int32_t)min(total, (uint32_t)a.cand_cap);
+    a.n_cand[seg] = M;
+    if (a.n_cand_out) a.n_cand_out[seg] = M;
+  }
+  if (a.cand_out) {
+    __syncthreads();
+    const int32_t M = (int32_t)min(total, (uint32_t)a.cand_cap);
+    for (int i = tid; i < a.cand_cap; i += kRtSelThreads)
+      a.cand_out[seg * a.cand_cap + i] = i < M ? cd[i] : -1;
+  }
+}
+
+// Indexed QK over the candidates of reuse-path heads (rows read in place by
+// index, no gathered copy), then, in the last workgroup of each head, the
+// exact top-K among them in candidate (= ascending row) order.
+struct RtRerankArgs {
+  const float* q;           // [S][128]
+  const char* k;
+  int64_t stride_b_bytes, stride_h_bytes;
+  const int32_t* exact;     // [S]
+  const int32_t* cand;      // [S][cand_cap]
+  const int32_t* n_cand;    // [S]
+  float* cz;                // [S][cand_cap] scores
+  uint32_t* done;           // [S]
+  int32_t* sel_row;         // [S][K]
+  float* sel_z;             // [S][K]
+  int32_t* support_out;     // [S][K]
+  int32_t cand_cap, K, Hq, G, nsplit;
+  float scale;
+};
+
+constexpr int kRerankThreads = 256;
+constexpr int kRerankRows = 128;  // candidates per workgroup
+
+template <typename T>
+__global__ __launch_bounds__(kRerankThreads) void retopk_rerank(RtRerankArgs a) {
+  constexpr int EPL = KvTraits<T>::EPL, LPR = KvTraits<T>::LPR, RPL = KvTraits<T>::RPL, ROWB = KvTraits<T>::ROWB;
+  constexpr int NW = kRerankThreads / 64;
+  constexpr int GROUPS = NW * RPL;
+  __shared__ uint32_t h[kHistBins];
+  __shared__ uint32_t tmp[kRerankThreads / 64 + 1];
+  __shared__ int s_bin, s_flag;
+  __shared__ uint32_t s_beyond;
+  const int64_t seg = blockIdx.y;
+  if (a.exact[seg]) return;
+  const int split = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int rg = lane / LPR, c = lane % LPR;
+  const int b = (int)(seg / a.Hq), hq = (int)(seg % a.Hq), hkv = hq / a.G;
+  const int M = a.n_cand[seg];
+  const int32_t* cd = a.cand + seg * a.cand_cap;
+  float* cz = a.cz + seg * a.cand_cap;
+
+  float qr[1][EPL];
+  load_q_slice<T, 1>(a.q, seg, c, qr);
+  const char* kb = a.k + (int64_t)b * a.stride_b_bytes + (int64_t)hkv * a.stride_h_bytes;
+  const int j0 = split * kRerankRows, j1 = min(M, j0 + kRerankRows);
+  for (int jb = j0; jb < j1; jb += GROUPS) {
+    const int j = jb + w * RPL + rg;
+    u32x4 kw = u32x4{0u, 0u, 0u, 0u};
+    if (j < j1) kw = load16(kb + (int64_t)cd[j] * ROWB + c * 16);
+    float d[1];
+    chunk_dots<T, 1>(kw, qr, d);
+    const float s = group_sum<LPR>(d[0]);
+    if (c == 0 && j < j1) cz[j] = s * a.scale;
+  }
+  if (!last_to_arrive(&a.done[seg], (uint32_t)a.nsplit, &s_flag)) return;
+
+  // top-K among the M candidates; ties -> lower candidate index (= lower row)
+  const int K = a.K;
+  int32_t* srow = a.sel_row + seg * K;
+  float* sz = a.sel_z + seg * K;
+  int32_t* so = a.support_out + seg * K;
+  uint32_t Tk = 0u;
+  int32_t cut = 0x7FFFFFFF;
+  if (M > K) {
+    uint32_t need = (uint32_t)K, prefix = 0;
+    const int shifts[3] = {21, 10, 0};
+    const int bits[3] = {11, 11, 10};
+#pragma unroll
+    for (int dgt = 0; dgt < 3; ++dgt) {
+      const int nb = 1 << bits[dgt];
+      for (int i = tid; i < nb; i += kRerankThreads) h[i] = 0u;
+      __syncthreads();
+      const int hs = shifts[dgt] + bits[dgt];
+      for (int j = tid; j < M; j += kRerankThreads) {
+        const uint32_t key = f2key(cz[j]);
+        if (dgt == 0 || (key >> hs) == prefix) atomicAdd(&h[(key >> shifts[dgt]) & (uint32_t)(nb - 1)], 1u);
+      }
+      __syncthreads();
+      find_bin<kRerankThreads, true>(h, nb, need, tmp, &s_bin, &s_beyond);
+      prefix = (prefix << bits[dgt]) | (uint32_t)(s_bin < 0 ? 0 : s_bin);
+      need -= s_beyond;
+      __syncthreads();
+    }
+    Tk = prefix;
+    // count ties
+    if (tid == 0) h[0] = 0u;
+    __syncthreads();
+    for (int j = tid; j < M; j += kRerankThreads)
+      if (f2key(cz[j]) == Tk) atomicAdd(&h[0], 1u);
+    __syncthreads();
+    const uint32_t ties = h[0];
+    __syncthreads();
+    if (need < ties) {
+      uint32_t pfx = 0, rem = need;
+      const int psh[3] = {20, 9, 0};
+      const int pbt[3] = {11, 11, 9};
+#pragma unroll
+      for (int dgt = 0; dgt < 3; ++dgt) {
+        const int nb = 1 << pbt[dgt];
+        for (int i = tid; i < nb; i += kRerankThreads) h[i] = 0u;
+        __syncthreads();
+        const int hs = psh[dgt] + pbt[dgt];
+        for (int j = tid; j < M; j += kRerankThreads) {
+          if (f2key(cz[j]) == Tk && (dgt == 0 || ((uint32_t)j >> hs) == pfx))
+            atomicAdd(&h[((uint32_t)j >> psh[dgt]) & (uint32_t)(nb - 1)], 1u);
+        }
+        __syncthreads();
+        find_bin<kRerankThreads, false>(h, nb, rem, tmp, &s_bin, &s_beyond);
+        pfx = (pfx << pbt[dgt]) | (uint32_t)(s_bin < 0 ? 0 : s_bin);
+        rem -= s_beyond;
+        __syncthreads();
+      }
+      cut = (int32_t)pfx;
+    }
+  }
+  // ordered compaction over candidate index
+  const int per = (M + kRerankThreads - 1) / kRerankThreads;
+  const int q0 = tid * per, q1 = min(M, q0 + per);
+  uint32_t cnt = 0;
+  for (int j = q0; j < q1; ++j) {
+    const uint32_t key = f2key(cz[j]);
+    cnt += (M <= K) || key > Tk || (key == Tk && j <= cut);
+  }
+  uint32_t total;
+  uint32_t r = block_excl_scan<kRerankThreads>(cnt, tmp, &total);
+  for (int j = q0; j < q1; ++j) {
+    const uint32_t key = f2key(cz[j]);
+    if ((M <= K) || key > Tk || (key == Tk && j <= cut)) {
+      if (r < (uint32_t)K) {
+        srow[r] = cd[j];
+        sz[r] = cz[j];
+        so[r] = cd[j];
+      }
+      ++r;
+    }
+  }
+  for (uint32_t i = total + tid; i < (uint32_t)K; i += kRerankThreads) {
+    srow[i] = -1;
+    sz[i] = -INFINITY;
+    so[i] = -1;
+  }
+}
+
+// Exact path when the visible rows do not exceed K: every row is chosen.
+struct SelectAllArgs {
+  const float* scores;        // [S][n_pad]
+  const int32_t* seg_active;  // [S] or null
+  int32_t* sel_row;
+  float* sel_z;
+  int32_t* idx_out;           // [S][K] or null
+  int64_t n, n_pad;
+  int32_t K;
+  int32_t pad_;
+  RangeTab tab;
+};
+
+__global__ __launch_bounds__(256) void select_all(SelectAllArgs a) {
+  const int64_t seg = blockIdx.x;
+  if (a.seg_active && a.seg_active[seg] == 0) return;
+  for (int64_t p = threadIdx.x; p < a.K; p += 256) {
+    int32_t row = -1;
+    float z = -INFINITY;
+    if (p < a.n) {
+      row = (int32_t)pos_to_row(a.tab, p);
+      z = a.scores[seg * a.n_pad + p];
+    }
+    a.sel_row[seg * a.K + p] = row;
+    a.sel_z[seg * a.K + p] = z;
+    if (a.idx_out) a.idx_out[seg * a.K + p] = row;
+  }
+}
+
+// Push (q_bar, support) into slot (head + 1) mod C of every head.
+struct RtPushArgs {
+  const float* qbar;          // [S][128]
+  const int32_t* support_in;  // [S][K]
+  float* q_hat;
+  int32_t* support;
+  int32_t* head;
+  int32_t* count;
+  int32_t C, K;
+};
+
+__global__ __launch_bounds__(256) void retopk_push(RtPushArgs a) {
+  const int64_t seg = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int hd = a.head[seg], cnt = a.count[seg];
+  const int slot = (hd + 1) % a.C;
+  if (tid < kHeadDim) a.q_hat[(seg * a.C + slot) * kHeadDim + tid] = a.qbar[seg * kHeadDim + tid];
+  for (int i = tid; i < a.K; i += 256)
+    a.support[(seg * a.C + slot) * (int64_t)a.K + i] = a.support_in[seg * a.K + i];
+  __syncthreads();
+  if (tid == 0) {
+    a.head[seg] = slot;
+    a.count[seg] = min(cnt + 1, a.C);
+  }
+}
+
+// Fill the FIFO from a history of (query, support) pairs, oldest first.
+struct RtInitArgs {
+  const float* q_hist;    // [S][n][128]
+  const int32_t* s_hist;  // [S][n][K]
+  float* q_hat;
+  int32_t* support;
+  int32_t* head;
+  int32_t* count;
+  int32_t C, K, n;
+  int32_t pad_;
+};
+
+__global__ __launch_bounds__(256) void retopk_init(RtInitArgs a) {
+  __shared__ float tmp2[2];
+  const int64_t seg = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int m = min(a.n, a.C);
+  for (int s = 0; s < a.C; ++s) {
+    float* dq = a.q_hat + (seg * a.C + s) * kHeadDim;
+    int32_t* ds = a.support + (seg * a.C + s) * (int64_t)a.K;
+    if (s < m) {
+      const int64_t src = (int64_t)a.n - m + s;
+      const float x = (tid < kHeadDim) ? a.q_hist[(seg * a.n + src) * kHeadDim + tid] : 0.f;
+      const float u = unit_component(x, tmp2);
+      if (tid < kHeadDim) dq[tid] = u;
+      for (int i = tid; i < a.K; i += 256) ds[i] = a.s_hist[(seg * a.n + src) * (int64_t)a.K + i];
+    } else {
+      if (tid < kHeadDim) dq[tid] = 0.f;
+      for (int i = tid; i < a.K; i += 256) ds[i] = -1;
+    }
+  }
+  if (tid == 0) {
+    a.head[seg] = m > 0 ? m - 1 : a.C - 1;
+    a.count[seg] = m;
+  }
+}
+
+}  // namespace stdk

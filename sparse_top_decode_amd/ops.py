@@ -1,0 +1,192 @@
+"""PyTorch-facing wrappers of the C ABI (include/stdk.h).
+
+Tensors only supply device pointers, shapes and the current HIP stream;
+every step of the computation runs in libstdk.so. Outputs that the caller
+does not pass are allocated with torch (plumbing, not compute).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+from . import native
+from .native import Layout, RetopkParams, RetopkState, check, load
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, shape=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def make_layout(k_cache: torch.Tensor, n_q_heads: int) -> Layout:
+    """Layout of a contiguous [B, H_kv, L_max, 128] cache (bf16 or fp32)."""
+    if k_cache.dim() != 4:
+        raise ValueError("k_cache must be [B, H_kv, L_max, head_dim]")
+    B, Hkv, L, d = k_cache.shape
+    if k_cache.dtype == torch.bfloat16:
+        dt = native.STDK_BF16
+    elif k_cache.dtype == torch.float32:
+        dt = native.STDK_F32
+    else:
+        raise ValueError(f"unsupported KV dtype {k_cache.dtype}")
+    return Layout(B, n_q_heads, Hkv, d, L, dt, 0, Hkv * L * d, L * d)
+
+
+def _ranges_arr(ranges: Sequence[Tuple[int, int]]):
+    flat = [int(x) for r in ranges for x in r]
+    arr = (ctypes.c_int64 * max(1, len(flat)))(*flat) if flat else (ctypes.c_int64 * 1)(0)
+    return arr, len(ranges)
+
+
+def topk_attn_decode_workspace_size(layout: Layout, n_scan: int, top_k: int) -> int:
+    return int(load().topk_attn_decode_workspace_size(ctypes.byref(layout), int(n_scan), int(top_k)))
+
+
+def topk_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                     ranges: Sequence[Tuple[int, int]], top_k: int, scale: Optional[float] = None,
+                     *, idx_out: Optional[torch.Tensor] = None, o_out: Optional[torch.Tensor] = None,
+                     lse_out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                     want_idx: bool = True, layout: Optional[Layout] = None):
+    """Top-K decode attention of every query head over the union of ``ranges``.
+
+    q [B, H_q, 128] fp32; caches [B, H_kv, L_max, 128] (bf16 or fp32).
+    Returns (idx [B, H_q, K] int32 or None, o [B, H_q, 128] fp32, lse [B, H_q] fp32).
+    """
+    lib = load()
+    B, Hq, d = q.shape
+    _need(q, "q", torch.float32)
+    _need(k_cache, "k_cache")
+    _need(v_cache, "v_cache", k_cache.dtype, k_cache.shape)
+    lay = layout if layout is not None else make_layout(k_cache, Hq)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    n = sum(int(e) - int(b) for b, e in ranges)
+    if o_out is None:
+        o_out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if lse_out is None:
+        lse_out = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if idx_out is None and want_idx:
+        idx_out = torch.empty((B, Hq, top_k), dtype=torch.int32, device=q.device)
+    if workspace is None:
+        nbytes = topk_attn_decode_workspace_size(lay, n, top_k)
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+    arr, nr = _ranges_arr(ranges)
+    rc = lib.topk_attn_decode(ctypes.byref(lay), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), arr, nr,
+                              int(top_k), ctypes.c_float(scale), _ptr(idx_out), o_out.data_ptr(), lse_out.data_ptr(),
+                              workspace.data_ptr(), workspace.numel(), _stream())
+    check(rc)
+    return idx_out, o_out, lse_out
+
+
+def attn_merge_lse(o_a: torch.Tensor, lse_a: torch.Tensor, o_b: torch.Tensor, lse_b: torch.Tensor,
+                   o_out: Optional[torch.Tensor] = None, lse_out: Optional[torch.Tensor] = None):
+    """Log-sum-exp combination of two partial attention outputs."""
+    lib = load()
+    d = o_a.shape[-1]
+    rows = lse_a.numel()
+    for t, nm in ((o_a, "o_a"), (o_b, "o_b")):
+        _need(t, nm, torch.float32)
+    for t, nm in ((lse_a, "lse_a"), (lse_b, "lse_b")):
+        _need(t, nm, torch.float32)
+    if o_out is None:
+        o_out = torch.empty_like(o_a)
+    if lse_out is None:
+        lse_out = torch.empty_like(lse_a)
+    rc = lib.attn_merge_lse(rows, d, o_a.data_ptr(), lse_a.data_ptr(), o_b.data_ptr(), lse_b.data_ptr(),
+                            o_out.data_ptr(), lse_out.data_ptr(), _stream())
+    check(rc)
+    return o_out, lse_out
+
+
+class Retopk:
+    """Per-query-head ReTopK state (device tensors) and its step."""
+
+    def __init__(self, k_cache: torch.Tensor, n_q_heads: int, top_k: int = 512, cache_cap: int = 32,
+                 top_r: int = 4, recent: int = 32, tau: float = 0.85, refresh: int = 128,
+                 scale: Optional[float] = None, max_len_t: Optional[int] = None):
+        load()
+        self.layout = make_layout(k_cache, n_q_heads)
+        B, Hkv, L, d = k_cache.shape
+        self.B, self.Hq, self.d = B, n_q_heads, d
+        self.params = RetopkParams(top_k, cache_cap, top_r, recent, float(tau), refresh,
+                                   float(1.0 / math.sqrt(d) if scale is None else scale))
+        dev = k_cache.device
+        self.q_hat = torch.zeros((B, n_q_heads, cache_cap, d), dtype=torch.float32, device=dev)
+        self.support = torch.full((B, n_q_heads, cache_cap, top_k), -1, dtype=torch.int32, device=dev)
+        self.head = torch.full((B, n_q_heads), cache_cap - 1, dtype=torch.int32, device=dev)
+        self.count = torch.zeros((B, n_q_heads), dtype=torch.int32, device=dev)
+        self.state = RetopkState(self.q_hat.data_ptr(), self.support.data_ptr(), self.head.data_ptr(),
+                                 self.count.data_ptr())
+        self.cand_cap = top_r * top_k + recent
+        mx = L if max_len_t is None else int(max_len_t)
+        nbytes = int(load().retopk_workspace_size(ctypes.byref(self.layout), ctypes.byref(self.params), mx))
+        self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+
+    def init(self, q_hist: torch.Tensor, sup_hist: torch.Tensor):
+        """Fill the caches from [B, H_q, n, 128] queries and [B, H_q, n, K] supports."""
+        n = q_hist.shape[2]
+        _need(q_hist, "q_hist", torch.float32)
+        _need(sup_hist, "sup_hist", torch.int32)
+        rc = load().retopk_state_init(ctypes.byref(self.layout), ctypes.byref(self.params), ctypes.byref(self.state),
+                                      q_hist.data_ptr(), sup_hist.data_ptr(), n, _stream())
+        check(rc)
+
+    def step(self, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, L_t: int, t: int,
+             *, out: Optional[dict] = None, want_cand: bool = False) -> dict:
+        """One decode step; returns support, o, lse, path, n_cand (and cand)."""
+        B, Hq, K = self.B, self.Hq, self.params.top_k
+        dev = q.device
+        _need(q, "q", torch.float32)
+        if out is None:
+            out = dict(support=torch.empty((B, Hq, K), dtype=torch.int32, device=dev),
+                       o=torch.empty((B, Hq, self.d), dtype=torch.float32, device=dev),
+                       lse=torch.empty((B, Hq), dtype=torch.float32, device=dev),
+                       path=torch.empty((B, Hq), dtype=torch.int32, device=dev),
+                       n_cand=torch.empty((B, Hq), dtype=torch.int32, device=dev))
+            if want_cand:
+                out["cand"] = torch.empty((B, Hq, self.cand_cap), dtype=torch.int32, device=dev)
+        rc = load().retopk_step(ctypes.byref(self.layout), ctypes.byref(self.params), ctypes.byref(self.state),
+                                q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), int(L_t), int(t),
+                                out["support"].data_ptr(), out["o"].data_ptr(), out["lse"].data_ptr(),
+                                _ptr(out.get("path")), _ptr(out.get("n_cand")), _ptr(out.get("cand")),
+                                self.workspace.data_ptr(), self.workspace.numel(), _stream())
+        check(rc)
+        return out
+
+
+class KernelTimer:
+    """Per-kernel durations from HIP events the library records around each
+    of its launches (on the launch stream)."""
+
+    def __init__(self, capacity: int = 1 << 16):
+        check(load().stdk_profile_enable(capacity))
+        check(load().stdk_profile_reset())
+
+    def read(self, name: str) -> Tuple[float, int]:
+        ms = ctypes.c_double(0.0)
+        n = ctypes.c_int64(0)
+        check(load().stdk_profile_read(name.encode(), ctypes.byref(ms), ctypes.byref(n)))
+        return ms.value, n.value
+
+    def reset(self):
+        check(load().stdk_profile_reset())
+
+    def close(self):
+        check(load().stdk_profile_disable())

@@ -1,0 +1,115 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the header
+declares, sizes workspaces, and rejects bad arguments on the host before any
+HIP call (so these run on a machine with no GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_top_decode_amd import native
+from sparse_top_decode_amd.native import Layout, RetopkParams, RetopkState
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x100000  # never dereferenced: every call below fails validation first
+
+
+def header_functions():
+    with open(os.path.join(ROOT, "include", "stdk.h")) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return native.load()
+
+
+def test_exports_match_header(lib):
+    declared = header_functions()
+    assert sorted(native.EXPORTS) == declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_version(lib):
+    assert lib.stdk_version() == 100
+
+
+def lay(B=1, Hq=32, Hkv=8, d=128, L=4096, dt=native.STDK_BF16):
+    return Layout(B, Hq, Hkv, d, L, dt, 0, Hkv * L * d, L * d)
+
+
+def test_workspace_size(lib):
+    a = lib.topk_attn_decode_workspace_size(ctypes.byref(lay()), 4000, 64)
+    b = lib.topk_attn_decode_workspace_size(ctypes.byref(lay()), 8000, 64)
+    assert a > 0 and b > a and a % 256 == 0
+    assert lib.topk_attn_decode_workspace_size(ctypes.byref(lay(d=64)), 4000, 64) == 0
+    p = RetopkParams(512, 32, 4, 32, 0.85, 128, 0.088)
+    assert lib.retopk_workspace_size(ctypes.byref(lay(Hq=28, Hkv=4)), ctypes.byref(p), 65536) > 0
+
+
+def call_topk(lib, L=None, ranges=((0, 100),), top_k=8, ws_bytes=1 << 30, q=FAKE, scale=0.1, idx=FAKE):
+    L = L or lay()
+    flat = [x for r in ranges for x in r]
+    arr = (ctypes.c_int64 * max(1, len(flat)))(*flat)
+    return lib.topk_attn_decode(ctypes.byref(L), q, FAKE, FAKE, arr, len(ranges), top_k, ctypes.c_float(scale),
+                                idx, FAKE, FAKE, FAKE, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(L=lay(d=64)), native.STDK_EUNSUPPORTED),
+    (dict(L=lay(Hq=30, Hkv=8)), native.STDK_EUNSUPPORTED),
+    (dict(L=lay(Hq=80, Hkv=8)), native.STDK_EUNSUPPORTED),
+    (dict(L=lay(dt=7)), native.STDK_EUNSUPPORTED),
+    (dict(top_k=0), native.STDK_EINVAL),
+    (dict(ranges=((0, 5000),)), native.STDK_EINVAL),
+    (dict(ranges=((10, 10),)), native.STDK_EINVAL),
+    (dict(ranges=((0, 100), (50, 200))), native.STDK_EINVAL),
+    (dict(ranges=((300, 400), (0, 100))), native.STDK_EINVAL),
+    (dict(ranges=tuple((2 * i, 2 * i + 1) for i in range(17))), native.STDK_EINVAL),
+    (dict(ws_bytes=16), native.STDK_EWORKSPACE),
+    (dict(q=0), native.STDK_EINVAL),
+    (dict(q=FAKE + 4), native.STDK_EINVAL),
+    (dict(idx=FAKE + 2), native.STDK_EINVAL),
+    (dict(scale=float("nan")), native.STDK_EINVAL),
+])
+def test_topk_rejects_before_launch(lib, kw, code):
+    assert call_topk(lib, **kw) == code
+    assert lib.stdk_last_error()
+
+
+def test_merge_rejects(lib):
+    assert lib.attn_merge_lse(4, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == native.STDK_EINVAL
+    assert lib.attn_merge_lse(-1, 128, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == native.STDK_EINVAL
+    assert lib.attn_merge_lse(4, 128, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None) == native.STDK_EINVAL
+    assert lib.attn_merge_lse(0, 128, 0, 0, 0, 0, 0, 0, None) == native.STDK_OK  # nothing to do
+
+
+def step(lib, p, L_t=100, t=0, ws=1 << 30, L=None, st=None, sup=FAKE):
+    L = L or lay(Hq=28, Hkv=4, L=4096)
+    st = st or RetopkState(FAKE, FAKE, FAKE, FAKE)
+    return lib.retopk_step(ctypes.byref(L), ctypes.byref(p), ctypes.byref(st), FAKE, FAKE, FAKE, L_t, t, sup, FAKE,
+                           FAKE, None, None, None, FAKE, ws, None)
+
+
+def test_retopk_rejects(lib):
+    good = RetopkParams(64, 8, 2, 8, 0.85, 16, 0.088)
+    assert step(lib, RetopkParams(0, 8, 2, 8, 0.85, 16, 0.088)) == native.STDK_EINVAL
+    assert step(lib, RetopkParams(64, 0, 1, 8, 0.85, 16, 0.088)) == native.STDK_EINVAL
+    assert step(lib, RetopkParams(64, 65, 2, 8, 0.85, 16, 0.088)) == native.STDK_EINVAL
+    assert step(lib, RetopkParams(64, 8, 9, 8, 0.85, 16, 0.088)) == native.STDK_EINVAL
+    assert step(lib, RetopkParams(64, 8, 2, -1, 0.85, 16, 0.088)) == native.STDK_EINVAL
+    assert step(lib, RetopkParams(64, 8, 2, 8, float("nan"), 16, 0.088)) == native.STDK_EINVAL
+    assert step(lib, RetopkParams(64, 8, 2, 8, 0.85, -3, 0.088)) == native.STDK_EINVAL
+    assert step(lib, good, L_t=0) == native.STDK_EINVAL
+    assert step(lib, good, L_t=5000) == native.STDK_EINVAL
+    assert step(lib, good, t=-1) == native.STDK_EINVAL
+    assert step(lib, good, ws=100) == native.STDK_EWORKSPACE
+    assert step(lib, good, sup=0) == native.STDK_EINVAL
+    assert step(lib, good, st=RetopkState(FAKE, 0, FAKE, FAKE)) == native.STDK_EINVAL
+    assert step(lib, good, L=lay(Hq=28, Hkv=4, L=4096, d=96)) == native.STDK_EUNSUPPORTED
+    big = lay(Hq=28, Hkv=4, L=2_000_000)
+    assert step(lib, good, L=big, L_t=1_500_000) == native.STDK_EUNSUPPORTED

@@ -1,0 +1,152 @@
+"""GPU parity of the ReTopK step, in lock-step with the oracle: before every
+step the GPU's cache state is copied to the host, the oracle runs the same
+step from it, and path, candidate set, support, o, lse and the pushed state
+are compared. A step whose decision is within 1e-6 of a tie (best cosine vs
+tau, or the R-th vs (R+1)-th cosine) is flagged, not failed."""
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import BAND, check_index_set, check_out, dev_kv, log
+from oracle import reference as ref
+from workloads import make_workload
+
+pytestmark = pytest.mark.gpu
+
+NEAR = 1e-6
+
+
+@pytest.fixture(scope="module")
+def ops(stdk):
+    from sparse_top_decode_amd import ops
+    return ops
+
+
+def host_state(rt):
+    return ref.RetopkState(rt.q_hat.cpu().numpy(), rt.support.cpu().numpy(), rt.head.cpu().numpy(),
+                           rt.count.cpu().numpy())
+
+
+def warm_cache(ops, w, rt, k, v, n_warm, K):
+    """The first n_warm queries go through the exact path over the initial
+    rows and fill the caches (oldest first)."""
+    L0 = w.retopk["L0"]
+    qs = torch.from_numpy(np.ascontiguousarray(w.q[:, :, :n_warm])).cuda()
+    sups = []
+    for j in range(n_warm):
+        idx, _, _ = ops.topk_attn_decode(qs[:, :, j].contiguous(), k, v, [(0, L0)], K, w.scale,
+                                         layout=rt.layout)
+        sups.append(idx)
+    sup = torch.stack(sups, dim=2).contiguous()
+    rt.init(qs, sup)
+    torch.cuda.synchronize()
+    return qs.cpu().numpy(), sup.cpu().numpy()
+
+
+def run_lockstep(ops, w, p, n_steps, heads, n_warm, check_every=1):
+    L0 = w.retopk["L0"]
+    k, v = dev_kv(w)
+    rt = ops.Retopk(k, w.H_q, top_k=p.top_k, cache_cap=p.cache_cap, top_r=p.top_r, recent=p.recent, tau=p.tau,
+                    refresh=p.refresh, scale=w.scale)
+    qh, sh = warm_cache(ops, w, rt, k, v, n_warm, p.top_k)
+    # the cache after init equals the oracle's init from the same history
+    st0 = ref.retopk_state_init(p, qh, sh)
+    g0 = host_state(rt)
+    assert np.array_equal(g0.support, st0.support)
+    assert np.array_equal(g0.head, st0.head) and np.array_equal(g0.count, st0.count)
+    assert np.max(np.abs(g0.q_hat - st0.q_hat)) < 1e-6
+    G = w.H_q // w.H_kv
+    stats = dict(reuse=0, exact=0, flagged=0, cand=[], swaps=0)
+    for t in range(n_steps):
+        L_t = L0 + t + 1
+        qt = np.ascontiguousarray(w.q[:, :, n_warm + t])
+        checking = (t % check_every) == 0
+        before = host_state(rt) if checking else None
+        out = rt.step(torch.from_numpy(qt).cuda(), k, v, L_t, t, want_cand=True)
+        torch.cuda.synchronize()
+        if not checking:
+            continue
+        g = {kk: vv.cpu().numpy() for kk, vv in out.items()}
+        after = host_state(rt)
+        o_ref, st_ref, tr = ref.retopk_step(p, before, qt, w.k, w.v, L_t, t, w.scale, heads=heads)
+        for b, h in heads:
+            r = tr[(b, h)]
+            rs = r["rho_sorted"]
+            near = rs.size > 0 and (abs(float(rs[0]) - p.tau) < NEAR or
+                                    (rs.size > p.top_r and abs(float(rs[p.top_r - 1]) - float(rs[p.top_r])) < NEAR))
+            if near:
+                stats["flagged"] += 1
+                continue
+            assert int(g["path"][b, h]) == r["path"], (t, b, h, int(g["path"][b, h]), r["path"])
+            if r["path"] == 0:
+                stats["reuse"] += 1
+                M = r["cand"].shape[0]
+                stats["cand"].append(M)
+                assert int(g["n_cand"][b, h]) == M
+                assert np.array_equal(g["cand"][b, h][:M], r["cand"]), (t, b, h)
+                assert np.all(g["cand"][b, h][M:] == -1)
+            else:
+                stats["exact"] += 1
+                assert int(g["n_cand"][b, h]) == L_t
+            stats["swaps"] += check_index_set(g["support"][b, h], r["rows"], r["z"], r["zk"], p.top_k)
+            check_out(g["o"][b, h], g["lse"][b, h], r["o"], r["lse"], w.kv_dtype == "f32", f"t={t} ({b},{h})")
+            # the pushed entry: unit query and the GPU's own support
+            C = p.cache_cap
+            slot = (int(before.head[b, h]) + 1) % C
+            assert int(after.head[b, h]) == slot
+            assert int(after.count[b, h]) == min(int(before.count[b, h]) + 1, C)
+            assert np.max(np.abs(after.q_hat[b, h, slot] - st_ref.q_hat[b, h, slot])) < 1e-6
+            assert np.array_equal(after.support[b, h, slot], g["support"][b, h])
+    return stats
+
+
+def test_retopk_lockstep_small(ops):
+    """c3 head layout (28 q / 4 KV, G = 7) at reduced length and parameters,
+    with a refresh every 8 steps and a threshold that gives both paths."""
+    w = make_workload(3, L=4096, steps=40, warm=8)
+    p = ref.RetopkParams(top_k=64, cache_cap=8, top_r=2, recent=16, tau=0.85, refresh=8)
+    heads = [(0, h) for h in range(28)]
+    s = run_lockstep(ops, w, p, 40, heads, n_warm=8)
+    log(f"retopk small: reuse {s['reuse']} exact {s['exact']} flagged {s['flagged']} "
+        f"mean M {np.mean(s['cand']) if s['cand'] else 0:.0f} band swaps {s['swaps']}")
+    assert s["reuse"] > 0 and s["exact"] > 0
+
+
+def test_retopk_tiny_cache_all_paths(ops):
+    """L_t <= K on the exact path and M <= K on the reuse path (tiny caches)."""
+    w = make_workload(3, L=100, steps=12, warm=3)
+    p = ref.RetopkParams(top_k=128, cache_cap=4, top_r=2, recent=8, tau=0.5, refresh=5)
+    s = run_lockstep(ops, w, p, 12, [(0, h) for h in range(28)], n_warm=3)
+    log(f"retopk tiny: reuse {s['reuse']} exact {s['exact']} flagged {s['flagged']}")
+
+
+def test_retopk_always_exact_equals_topk(ops):
+    """tau > 1: every step takes the exact path and equals topk_attn_decode."""
+    w = make_workload(3, L=2048, steps=6, warm=4)
+    k, v = dev_kv(w)
+    rt = ops.Retopk(k, 28, top_k=32, cache_cap=4, top_r=2, recent=8, tau=1.5, refresh=0, scale=w.scale)
+    warm_cache(ops, w, rt, k, v, 4, 32)
+    for t in range(6):
+        L_t = 2048 + t + 1
+        qt = torch.from_numpy(np.ascontiguousarray(w.q[:, :, 4 + t])).cuda()
+        out = rt.step(qt, k, v, L_t, t)
+        idx, o, lse = ops.topk_attn_decode(qt, k, v, [(0, L_t)], 32, w.scale)
+        torch.cuda.synchronize()
+        assert np.all(out["path"].cpu().numpy() == 1)
+        assert torch.equal(out["support"], idx)
+        assert torch.equal(out["o"], o) and torch.equal(out["lse"], lse)
+
+
+@pytest.mark.slow
+def test_retopk_c3_full_lockstep(ops):
+    """c3 at full size (L0 = 65536, K=512, C=32, R=4, W=32, tau=0.85,
+    T_r=128), all 256 steps, 4 sampled heads compared every step."""
+    w = make_workload(3)
+    P = w.retopk
+    p = ref.RetopkParams(top_k=P["top_k"], cache_cap=P["cache_cap"], top_r=P["top_r"], recent=P["recent"],
+                         tau=P["tau"], refresh=P["refresh"])
+    heads = [(0, 0), (0, 9), (0, 18), (0, 27)]
+    s = run_lockstep(ops, w, p, P["steps"], heads, n_warm=P["warmup"])
+    log(f"retopk c3 full: reuse {s['reuse']} exact {s['exact']} flagged {s['flagged']} "
+        f"mean M {np.mean(s['cand']) if s['cand'] else 0:.0f} (parity unpinned: context only) band swaps {s['swaps']}")

@@ -1,0 +1,172 @@
+"""GPU parity of topk_attn_decode and attn_merge_lse against the CPU oracle."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import check_heads, check_index_set, check_out, dev_kv, log, oracle_head
+from oracle import reference as ref
+from workloads import make_workload, static_window_ranges
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ops(stdk):
+    from sparse_top_decode_amd import ops
+    return ops
+
+
+def run(ops, w, ranges, K, **kw):
+    q = torch.from_numpy(w.q if w.q.ndim == 3 else w.q[:, :, 0]).cuda()
+    k, v = dev_kv(w)
+    idx, o, lse = ops.topk_attn_decode(q, k, v, ranges, K, w.scale, **kw)
+    torch.cuda.synchronize()
+    return (None if idx is None else idx.cpu().numpy()), o.cpu().numpy(), lse.cpu().numpy()
+
+
+def test_c1_exact_fp32(ops):
+    """1 q / 1 KV head, fp32 cache, L=4096, K=64: index set exact, o/lse 1e-4."""
+    log("case c1 fp32 L=4096 K=64")
+    w = make_workload(1)
+    idx, o, lse = run(ops, w, w.ranges, w.top_k)
+    want = ref.topk_attn_decode(w.q, w.k, w.v, w.ranges, w.top_k, w.scale)
+    check_heads(w, [(0, 0)], idx, o, lse, w.ranges, w.top_k, fp32=True, label="c1")
+    assert np.array_equal(idx, want["idx"])
+
+
+@pytest.mark.parametrize("L,K", [(8192, 2048), (8192, 97), (20000, 1), (3000, 2047)])
+def test_c2_shape_reduced(ops, L, K):
+    """Llama-3-8B head layout (32 q / 8 KV, bf16) at reduced length: the
+    dynamic-set top-K call on every head, several tiles and a ragged tail."""
+    log(f"case c2 reduced L={L} K={K}")
+    w = make_workload(2, L=L)
+    idx, o, lse = run(ops, w, w.ranges, K)
+    heads = [(0, h) for h in range(w.H_q)]
+    check_heads(w, heads, idx, o, lse, w.ranges, K, label=f"c2 L={L} K={K}")
+
+
+def test_c2_static_dense_and_merge(ops):
+    """The pages' decode step at reduced length: dense attention over the static
+    rows (first 128 + last 512), top-K over the rest, LSE merge; equals the
+    oracle's attention over the union of both row sets."""
+    log("case c2 static+dynamic+merge L=16384")
+    w = make_workload(2, L=16384)
+    K = 2048
+    q = torch.from_numpy(w.q).cuda()
+    k, v = dev_kv(w)
+    idx_d, o_d, l_d = ops.topk_attn_decode(q, k, v, w.ranges, K, w.scale)
+    idx_s, o_s, l_s = ops.topk_attn_decode(q, k, v, w.static_ranges, K, w.scale)
+    o_m, l_m = ops.attn_merge_lse(o_s, l_s, o_d, l_d)
+    torch.cuda.synchronize()
+    idx_s = idx_s.cpu().numpy()
+    srows = ref.range_rows(w.static_ranges)
+    assert np.all(idx_s[:, :, :srows.shape[0]] == srows[None, None, :])
+    assert np.all(idx_s[:, :, srows.shape[0]:] == -1)
+    idx_d = idx_d.cpu().numpy()
+    for h in range(w.H_q):
+        r, rows = oracle_head(w, 0, h, w.ranges, K)
+        check_index_set(idx_d[0, h], rows, r["z"], r["zk"], K)
+        rs, _ = oracle_head(w, 0, h, w.static_ranges, K)
+        om, lm = ref.attn_merge_lse(rs["o"], np.float64(rs["lse"]), r["o"], np.float64(r["lse"]))
+        check_out(o_s.cpu().numpy()[0, h], l_s.cpu().numpy()[0, h], rs["o"], rs["lse"], False, "static")
+        check_out(o_m.cpu().numpy()[0, h], l_m.cpu().numpy()[0, h], om, float(lm), False, "merged")
+        # the merged result is attention over W u S computed directly
+        union = np.union1d(srows, idx_d[0, h][idx_d[0, h] >= 0])
+        direct = ref.attend_rows(w.q[0, h], w.k[0, h // 4], w.v[0, h // 4], union, union.shape[0], w.scale)
+        check_out(o_m.cpu().numpy()[0, h], l_m.cpu().numpy()[0, h], direct["o"], direct["lse"], False, "union")
+
+
+def test_ragged_ranges_and_edges(ops):
+    """Several odd-sized ranges, K at 1, n-1, n and above n, fp32 and bf16."""
+    for cfg in (1, 2):
+        w = make_workload(cfg, L=4096) if cfg == 2 else make_workload(1)
+        ranges = [(3, 1000), (1500, 1501), (2000, 2777), (4000, 4096)]
+        n = sum(e - b for b, e in ranges)
+        for K in (1, 5, n - 1, n, n + 7):
+            log(f"case ragged cfg={cfg} K={K} n={n}")
+            idx, o, lse = run(ops, w, ranges, K)
+            heads = [(0, h) for h in range(w.H_q)][:8]
+            check_heads(w, heads, idx, o, lse, ranges, K, fp32=(cfg == 1), label=f"ragged c{cfg} K={K}")
+
+
+def test_empty_range(ops):
+    w = make_workload(2, L=1024)
+    idx, o, lse = run(ops, w, [], 16)
+    assert np.all(idx == -1) and np.all(o == 0) and np.all(np.isneginf(lse))
+
+
+def test_exact_ties_lowest_row_wins(ops):
+    """Duplicated key rows give bit-equal scores; the lowest rows must win."""
+    rng = np.random.default_rng(5)
+    L, K = 3000, 40
+    w = make_workload(2, L=L)
+    k = w.k.copy()
+    # 30 copies of one strong row and 30 of another, scattered
+    src = rng.choice(L, 2, replace=False)
+    for g in range(w.H_kv):
+        for j, s in enumerate(src):
+            dst = rng.choice(L, 30, replace=False)
+            k[0, g, dst] = k[0, g, s]
+    w.k = k
+    idx, o, lse = run(ops, w, [(0, L)], K)
+    want = ref.topk_attn_decode(w.q, w.k, w.v, [(0, L)], K, w.scale)
+    n_exact = 0
+    for h in range(w.H_q):
+        r, rows = oracle_head(w, 0, h, [(0, L)], K)
+        check_index_set(idx[0, h], rows, r["z"], r["zk"], K)
+        # where the K-th score is an exact tie among duplicates, the choice
+        # among the tied rows must be the lowest ones
+        tied = rows[r["z"] == r["zk"]]
+        if tied.shape[0] > 1:
+            n_exact += 1
+            got = set(int(x) for x in idx[0, h] if x >= 0) & set(int(x) for x in tied)
+            exp = set(int(x) for x in want["idx"][0, h] if x >= 0) & set(int(x) for x in tied)
+            assert got == exp, (h, sorted(got), sorted(exp))
+    log(f"tie heads checked exactly: {n_exact}")
+
+
+def test_c4_batch_reduced(ops):
+    """Batch of 16 sequences with per-sequence key offsets, K=1024."""
+    log("case c4 reduced B=16 L=4096 K=1024")
+    w = make_workload(4, L=4096)
+    idx, o, lse = run(ops, w, w.ranges, 1024)
+    heads = [(b, h) for b in range(16) for h in (0, 5, 31)]
+    check_heads(w, heads, idx, o, lse, w.ranges, 1024, label="c4 reduced")
+
+
+def test_merge_kernel(ops):
+    rng = np.random.default_rng(9)
+    rows, d = 37, 128
+    oa = rng.standard_normal((rows, d)).astype(np.float32)
+    ob = rng.standard_normal((rows, d)).astype(np.float32)
+    la = (rng.standard_normal(rows) * 5).astype(np.float32)
+    lb = (rng.standard_normal(rows) * 5).astype(np.float32)
+    la[3] = -np.inf
+    lb[4] = -np.inf
+    la[5] = lb[5] = -np.inf
+    oa[3] = np.nan  # an empty operand's o must not leak
+    want_o, want_l = ref.attn_merge_lse(oa.astype(np.float64), la.astype(np.float64), ob.astype(np.float64),
+                                        lb.astype(np.float64))
+    ta, tb = torch.from_numpy(oa).cuda(), torch.from_numpy(ob).cuda()
+    tla, tlb = torch.from_numpy(la).cuda(), torch.from_numpy(lb).cuda()
+    o, l = ops.attn_merge_lse(ta, tla, tb, tlb)
+    torch.cuda.synchronize()
+    assert np.max(np.abs(o.cpu().numpy() - want_o)) < 1e-5
+    lg = l.cpu().numpy()
+    fin = np.isfinite(want_l)
+    assert np.max(np.abs(lg[fin] - want_l[fin])) < 1e-5 and np.all(np.isneginf(lg[~fin]))
+    # in place (outputs alias the first operand)
+    ops.attn_merge_lse(ta, tla, tb, tlb, o_out=ta, lse_out=tla)
+    torch.cuda.synchronize()
+    assert np.max(np.abs(ta.cpu().numpy() - want_o)) < 1e-5
+
+
+def test_deterministic(ops):
+    w = make_workload(2, L=8192)
+    a = run(ops, w, w.ranges, 1000)
+    b = run(ops, w, w.ranges, 1000)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
