@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Benchmark: top-K decode-attention steps/sec at 128K context on one MI355X.
+
+One step is the whole decode-attention hot path of one Llama-3-8B-shaped
+layer (32 query heads, 8 KV heads, d=128, 131,072 cached rows, bf16 K/V):
+  1. top-K attention (K=2048) of every query head over the dynamic rows
+     [128, 130560): exact QK scan, per-head top-K select, softmax.V;
+  2. dense attention over the 640 static rows (first 128, last 512);
+  3. log-sum-exp merge of the two partial outputs.
+Inputs are synthetic and resident in HBM before timing starts.
+
+Prints ONE JSON line. The `roofline` object reports the K-cache scan kernel
+(k_scan): algorithmic bytes per launch (every scanned key row once, 256 B)
+over its average duration, measured with HIP events that the library records
+around each of its launches on the launch stream during the timed region.
+
+Options for profiling runs: --copy-calibration runs only a plain device copy
+of known size (to calibrate rocprofv3's FETCH_SIZE / WRITE_SIZE counters);
+--no-cpu skips the oracle baseline.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+SCAN_SOURCES = ["sparse_top_decode_amd/csrc/scan_kernels.h", "sparse_top_decode_amd/csrc/device.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_scan_c2_hbm_traffic.md")
+
+
+def scan_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in SCAN_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic():
+    """HBM bytes per k_scan launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            txt = f.read()
+    except OSError:
+        return None
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", txt)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m_hash or not m_bytes or m_hash.group(1) != scan_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def copy_calibration(nbytes: int):
+    import torch
+    x = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 5}), flush=True)
+
+
+def cpu_baseline(w, budget_s: float = 12.0):
+    """The oracle (untuned) on the host: whole decode steps of the same
+    workload, repeated until about budget_s of CPU time has passed."""
+    from oracle import reference as ref
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        dyn = ref.topk_attn_decode(w.q, w.k, w.v, w.ranges, w.top_k, w.scale)
+        stat = ref.topk_attn_decode(w.q, w.k, w.v, w.static_ranges, w.top_k, w.scale)
+        ref.attn_merge_lse(stat["o"], stat["lse"], dyn["o"], dyn["lse"])
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 20:
+            break
+    return dict(value=reps / el, unit="steps/s", cores=1, kind="oracle",
+                sample=f"{reps} full decode step(s) of the timed workload (all 32 query heads: dynamic top-K, "
+                       f"static dense, merge), {el:.1f} s on one host thread (numpy fp64, no BLAS)")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--L", type=int, default=131072)
+    ap.add_argument("--kernel-events", choices=["on", "off"], default="on",
+                    help="record per-kernel HIP events during the timed region (needed for the roofline)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no multi-GPU mode.",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+
+    import numpy as np
+    import torch
+
+    from sparse_top_decode_amd import ops
+    from workloads import make_workload
+
+    w = make_workload(2, L=args.L)
+    dev = torch.device("cuda:0")
+    q = torch.from_numpy(w.q).to(dev)
+    k = torch.from_numpy(w.k.view(np.int16)).to(dev).view(torch.bfloat16)
+    v = torch.from_numpy(w.v.view(np.int16)).to(dev).view(torch.bfloat16)
+    lay = ops.make_layout(k, w.H_q)
+    K = w.top_k
+    n_dyn = sum(e - b for b, e in w.ranges)
+    n_stat = sum(e - b for b, e in w.static_ranges)
+    ws_d = torch.empty(ops.topk_attn_decode_workspace_size(lay, n_dyn, K), dtype=torch.uint8, device=dev)
+    ws_s = torch.empty(ops.topk_attn_decode_workspace_size(lay, n_stat, K), dtype=torch.uint8, device=dev)
+    idx = torch.empty((1, w.H_q, K), dtype=torch.int32, device=dev)
+    o_d = torch.empty((1, w.H_q, 128), dtype=torch.float32, device=dev)
+    l_d = torch.empty((1, w.H_q), dtype=torch.float32, device=dev)
+    o_s = torch.empty_like(o_d)
+    l_s = torch.empty_like(l_d)
+    o_m = torch.empty_like(o_d)
+    l_m = torch.empty_like(l_d)
+
+    def step():
+        ops.topk_attn_decode(q, k, v, w.ranges, K, w.scale, idx_out=idx, o_out=o_d, lse_out=l_d,
+                             workspace=ws_d, layout=lay)
+        ops.topk_attn_decode(q, k, v, w.static_ranges, K, w.scale, o_out=o_s, lse_out=l_s, workspace=ws_s,
+                             want_idx=False, layout=lay)
+        ops.attn_merge_lse(o_s, l_s, o_d, l_d, o_out=o_m, lse_out=l_m)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # events around the scan kernel only, so that the timed steps carry two
+    # event records each
+    timer = ops.KernelTimer(capacity=2 * (args.steps + 4), only="k_scan") if args.kernel_events == "on" else None
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    total_ms = ev0.elapsed_time(ev1)
+    scan_bytes = w.H_kv * n_dyn * 256  # every dynamic key row once, bf16 d=128
+    achieved = scan_avg_s = None
+    if timer is not None:
+        scan_ms, scan_n = timer.read("k_scan")
+        timer.close()
+        scan_avg_s = scan_ms / scan_n / 1000.0
+        achieved = scan_bytes / scan_avg_s / 1e9
+    # per-kernel breakdown, from a separate short run with events around
+    # every launch (not part of the timed region)
+    kern = {}
+    names = ("ws_clear", "k_scan", "topk_filter", "topk_select", "sparse_sv", "dense_attn", "combine", "attn_merge")
+    t_all = ops.KernelTimer(capacity=16 * 24)
+    for _ in range(20):
+        step()
+    torch.cuda.synchronize()
+    for name in names:
+        ms, n = t_all.read(name)
+        if n:
+            kern[name] = round(1000.0 * ms / n, 2)
+    t_all.close()
+    traffic = committed_traffic()
+
+    ms_per_step = total_ms / args.steps
+    value = 1000.0 / ms_per_step
+    out = {
+        "metric": "top-K decode-attention steps/sec at 128K ctx; K-scan HBM GB/s vs peak",
+        "value": round(value, 1),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"Llama-3-8B-shaped decode attention layer: 32 q / 8 KV heads, d=128, L={w.L}, bf16 K/V, "
+                        f"top-K={K} over the {n_dyn} dynamic rows + dense over the {n_stat} static rows + LSE merge",
+            "batch": 1, "seq_len": w.L, "top_k": K, "kv_cache": "bf16", "parallelism": "none (1 GPU)",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": None if achieved is None else round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": None if achieved is None else round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "k_scan",
+            "algorithmic_bytes_per_launch": scan_bytes,
+            "avg_launch_us": None if scan_avg_s is None else round(scan_avg_s * 1e6, 2),
+        },
+        "kernels_avg_us": kern,
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(w)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

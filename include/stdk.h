@@ -87,7 +87,8 @@ typedef struct stdk_layout {
  *           range within [0, max_len), non-empty, ascending and disjoint.
  *           The same ranges apply to every sequence.
  *  n_ranges 0..STDK_MAX_RANGES.
- *  top_k    >= 1.
+ *  top_k    >= 1; when top_k < n it must be <= 65536, else
+ *           STDK_EUNSUPPORTED.
  *  idx_out  [B][H_q][top_k] int32: S in ascending row order, padded with -1
  *           when n < top_k. May be NULL.
  *  o_out    [B][H_q][128] fp32;  lse_out [B][H_q] fp32 (natural log).
@@ -123,7 +124,7 @@ int32_t attn_merge_lse(int64_t rows, int32_t d, const float* o_a, const float* l
  * ReTopK ([RT] 核心方法 1-5 and the per-step loop).
  * ---------------------------------------------------------------------- */
 typedef struct retopk_params {
-  int32_t top_k;     /* K, rows attended per step (>= 1) */
+  int32_t top_k;     /* K, rows attended per step (1..65536) */
   int32_t cache_cap; /* C, FIFO entries per query head (1..64) */
   int32_t top_r;     /* R, cache entries recalled (1..C) */
   int32_t recent;    /* W, newest rows always added to the candidates (>= 0) */
@@ -195,15 +196,17 @@ size_t retopk_workspace_size(const stdk_layout* lay, const retopk_params* p, int
 const char* stdk_last_error(void); /* host string, valid until the next call on this thread */
 int32_t stdk_version(void);        /* STDK_VERSION */
 
-/* Kernel timing: while enabled, every kernel the library enqueues is
- * bracketed by two hipEvents recorded on the same stream. `capacity` bounds
- * the number of launches recorded (events are created when enabling, not on
- * the hot path). stdk_profile_read waits for the recorded events and returns,
- * for the kernel family `name` (e.g. "k_scan"), the summed duration in
- * milliseconds and the launch count. Names: "k_scan", "topk_filter",
- * "topk_select", "sparse_sv", "dense_attn", "attn_merge", "ws_clear",
- * "retopk_select", "retopk_rerank", "retopk_push", "retopk_init". */
-int32_t stdk_profile_enable(int32_t capacity);
+/* Kernel timing: while enabled, every kernel the library enqueues (or only
+ * the kernel family `only`, if not NULL) is bracketed by two hipEvents
+ * recorded on the same stream. `capacity` bounds the number of launches
+ * recorded (events are created when enabling, not on the hot path).
+ * stdk_profile_read waits for the recorded events and returns, for the
+ * kernel family `name`, the summed duration in milliseconds and the launch
+ * count. Families: "ws_clear", "k_scan", "topk_filter", "topk_select",
+ * "sparse_sv", "dense_attn", "combine", "attn_merge", "fill_empty",
+ * "retopk_select", "retopk_rerank", "retopk_rerank_select", "retopk_push",
+ * "retopk_init". Unknown names return STDK_EINVAL. */
+int32_t stdk_profile_enable(int32_t capacity, const char* only);
 int32_t stdk_profile_disable(void);
 int32_t stdk_profile_reset(void);
 int32_t stdk_profile_read(const char* name, double* total_ms, int64_t* launches);

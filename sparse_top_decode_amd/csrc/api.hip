@@ -12,7 +12,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/stdk.h"
+#include "stdk.h"  // include/ (on the include path)
 #include "attend_kernels.h"
 #include "device.h"
 #include "retopk_kernels.h"
@@ -43,20 +43,28 @@ int32_t ok() {
   return STDK_OK;
 }
 
+#define STDK_TRY(x)                 \
+  do {                              \
+    const int32_t rc_ = (x);        \
+    if (rc_ != STDK_OK) return rc_; \
+  } while (0)
+
 // ---------------------------------------------------------------------------
 // launch timing
 // ---------------------------------------------------------------------------
 enum KernelId {
-  KID_SCAN, KID_FILTER, KID_SELECT, KID_SV, KID_DENSE, KID_MERGE, KID_CLEAR,
-  KID_RT_SELECT, KID_RT_RERANK, KID_RT_PUSH, KID_RT_INIT, KID_FILL, KID_COUNT
+  KID_CLEAR, KID_SCAN, KID_FILTER, KID_SELECT, KID_SV, KID_DENSE, KID_COMBINE, KID_MERGE, KID_FILL,
+  KID_RT_SELECT, KID_RT_RERANK, KID_RT_RSEL, KID_RT_PUSH, KID_RT_INIT, KID_COUNT
 };
 const char* const kKernelNames[KID_COUNT] = {
-    "k_scan",        "topk_filter",   "topk_select", "sparse_sv",   "dense_attn", "attn_merge", "ws_clear",
-    "retopk_select", "retopk_rerank", "retopk_push", "retopk_init", "fill_empty"};
+    "ws_clear",    "k_scan",        "topk_filter",   "topk_select",          "sparse_sv",
+    "dense_attn",  "combine",       "attn_merge",    "fill_empty",           "retopk_select",
+    "retopk_rerank", "retopk_rerank_select", "retopk_push", "retopk_init"};
 
 struct Profiler {
   std::mutex mu;
   bool on = false;
+  int only = -1;  // record only this kernel family (-1: all)
   std::vector<hipEvent_t> ev;  // 2 per slot
   std::vector<int> kid;
   size_t used = 0;
@@ -65,10 +73,11 @@ struct Profiler {
 };
 Profiler g_prof;
 
-// Returns the slot index whose first event was recorded, or -1.
+// Returns the slot whose first event was recorded, or -1.
 long prof_begin(int kid, hipStream_t s) {
   std::lock_guard<std::mutex> lk(g_prof.mu);
   if (!g_prof.on || g_prof.used >= g_prof.kid.size()) return -1;
+  if (g_prof.only >= 0 && g_prof.only != kid) return -1;
   const size_t slot = g_prof.used++;
   g_prof.kid[slot] = kid;
   (void)hipEventRecord(g_prof.ev[2 * slot], s);
@@ -91,11 +100,15 @@ int32_t launch(int kid, hipStream_t s, F&& f) {
   return STDK_OK;
 }
 
-#define STDK_TRY(x)              \
-  do {                           \
-    const int32_t rc_ = (x);     \
-    if (rc_ != STDK_OK) return rc_; \
-  } while (0)
+// ---------------------------------------------------------------------------
+// limits
+// ---------------------------------------------------------------------------
+constexpr int kMaxTopK = 65536;  // softmax.V partials of one head fit one combine workgroup
+constexpr int kDenseMaxWg = 32;  // workgroups per KV head on the dense path
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t rup(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+inline size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // ---------------------------------------------------------------------------
 // device limits (per device, queried once)
@@ -103,9 +116,24 @@ int32_t launch(int kid, hipStream_t s, F&& f) {
 struct DevInfo {
   bool init = false;
   int max_lds = 65536;
+  int n_cu = 256;
+  int scan_occ[2][STDK_MAX_GROUP + 1] = {};  // resident k_scan workgroups per CU, by (bf16, G)
 };
 std::mutex g_dev_mu;
 DevInfo g_dev[64];
+
+template <typename T, int G>
+int occ_of() {
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_scan<T, G>, kScanThreads, 0) != hipSuccess || nb < 1) nb = 1;
+  return nb;
+}
+
+template <typename T>
+void occ_row(int* o) {
+  o[1] = occ_of<T, 1>(); o[2] = occ_of<T, 2>(); o[3] = occ_of<T, 3>(); o[4] = occ_of<T, 4>();
+  o[5] = occ_of<T, 5>(); o[6] = occ_of<T, 6>(); o[7] = occ_of<T, 7>(); o[8] = occ_of<T, 8>();
+}
 
 int32_t dev_info(DevInfo** out) {
   int dev = 0;
@@ -119,11 +147,15 @@ int32_t dev_info(DevInfo** out) {
     e = hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
     if (e != hipSuccess) return fail(STDK_EHIP, "hipDeviceGetAttribute: %s", hipGetErrorString(e));
     d.max_lds = v;
-    const void* dyn_kernels[] = {(const void*)topk_select<true>, (const void*)retopk_select<true>};
-    for (const void* k : dyn_kernels) {
-      const int static_bytes = 12 * 1024;
-      (void)hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, std::max(0, v - static_bytes));
-    }
+    e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return fail(STDK_EHIP, "hipDeviceGetAttribute: %s", hipGetErrorString(e));
+    d.n_cu = v;
+    occ_row<float>(d.scan_occ[0]);
+    occ_row<uint16_t>(d.scan_occ[1]);
+    const int dyn_max = std::max(0, d.max_lds - (int)kSelStaticLds);
+    (void)hipFuncSetAttribute((const void*)topk_select, hipFuncAttributeMaxDynamicSharedMemorySize, dyn_max);
+    (void)hipFuncSetAttribute((const void*)retopk_select<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              std::max(0, d.max_lds - 12 * 1024));
     (void)hipGetLastError();
     d.init = true;
   }
@@ -132,12 +164,8 @@ int32_t dev_info(DevInfo** out) {
 }
 
 // ---------------------------------------------------------------------------
-// helpers
+// validation
 // ---------------------------------------------------------------------------
-inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
-inline int64_t rup(int64_t a, int64_t b) { return cdiv(a, b) * b; }
-inline size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
-
 int32_t check_layout(const stdk_layout* lay) {
   if (!lay) return fail(STDK_EINVAL, "layout is NULL");
   if (lay->batch < 1 || lay->n_q_heads < 1 || lay->n_kv_heads < 1)
@@ -150,7 +178,8 @@ int32_t check_layout(const stdk_layout* lay) {
   if (lay->head_dim != kHeadDim) return fail(STDK_EUNSUPPORTED, "head_dim %d (only 128 is supported)", lay->head_dim);
   if (lay->kv_dtype != STDK_F32 && lay->kv_dtype != STDK_BF16)
     return fail(STDK_EUNSUPPORTED, "kv_dtype %d", lay->kv_dtype);
-  if (lay->max_len < 1 || lay->max_len > 0x7FFFFFFFLL) return fail(STDK_EINVAL, "max_len %lld out of range", (long long)lay->max_len);
+  if (lay->max_len < 1 || lay->max_len > 0x7FFFFFFFLL)
+    return fail(STDK_EINVAL, "max_len %lld out of range", (long long)lay->max_len);
   if (lay->stride_h < lay->max_len * kHeadDim) return fail(STDK_EINVAL, "stride_h smaller than max_len * head_dim");
   if (lay->batch > 1 && lay->stride_b < (int64_t)lay->n_kv_heads * lay->stride_h)
     return fail(STDK_EINVAL, "stride_b smaller than n_kv_heads * stride_h");
@@ -164,76 +193,6 @@ int32_t check_ptr(const void* p, const char* what, size_t align) {
   if (!p) return fail(STDK_EINVAL, "%s is NULL", what);
   if (((uintptr_t)p) % align != 0) return fail(STDK_EINVAL, "%s is not %zu-byte aligned", what, align);
   return STDK_OK;
-}
-
-// Workspace of topk_attn_decode (and of the exact path of retopk_step).
-struct TopkWs {
-  int64_t S, groups, n, n_pad, K, nsplit, nwg_max, words;
-  size_t clear_off, clear_words;  // hist | list_cnt | done | done_grp | done_rr
-  size_t hist, list_cnt, done, done_grp, done_rr;
-  size_t scores, list, sel_row, sel_z, part, gbitmap, total;
-};
-
-constexpr int kDenseMaxWg = 32;
-
-TopkWs topk_ws(int64_t S, int64_t groups, int64_t n, int64_t K) {
-  TopkWs w{};
-  w.S = S;
-  w.groups = groups;
-  w.n = n;
-  w.n_pad = rup(std::max<int64_t>(n, 1), 64);
-  w.K = K;
-  w.nsplit = cdiv(K, kSvRows);
-  w.nwg_max = kDenseMaxWg;
-  w.words = cdiv(std::max<int64_t>(n, 1), 32);
-  size_t off = 0;
-  w.clear_off = off;
-  w.hist = off;
-  off += (size_t)S * kHistBins * 4;
-  w.list_cnt = off;
-  off += (size_t)S * 4;
-  w.done = off;
-  off += (size_t)S * 4;
-  w.done_rr = off;
-  off += (size_t)S * 4;
-  w.done_grp = off;
-  off += (size_t)groups * 4;
-  w.clear_words = (off - w.clear_off) / 4;
-  off = al256(off);
-  w.scores = off;
-  off = al256(off + (size_t)S * w.n_pad * 4);
-  w.list = off;
-  off = al256(off + (size_t)S * w.n_pad * 4);
-  w.sel_row = off;
-  off = al256(off + (size_t)S * K * 4);
-  w.sel_z = off;
-  off = al256(off + (size_t)S * K * 4);
-  w.part = off;
-  off = al256(off + (size_t)S * std::max<int64_t>(w.nsplit, w.nwg_max) * kPartStride * 4);
-  w.gbitmap = off;
-  off = al256(off + (size_t)S * w.words * 4);
-  w.total = off;
-  return w;
-}
-
-RangeTab make_tab(const int64_t* ranges, int n_ranges, int64_t* n_total) {
-  RangeTab t{};
-  t.n = n_ranges;
-  int64_t pos = 0;
-  for (int r = 0; r < n_ranges; ++r) {
-    t.row0[r] = ranges[2 * r];
-    t.pos0[r] = pos;
-    pos += ranges[2 * r + 1] - ranges[2 * r];
-  }
-  t.pos0[n_ranges] = pos;
-  if (n_ranges == 0) {
-    t.n = 1;
-    t.row0[0] = 0;
-    t.pos0[0] = 0;
-    t.pos0[1] = 0;
-  }
-  *n_total = pos;
-  return t;
 }
 
 struct Geo {
@@ -256,6 +215,67 @@ Geo geo_of(const stdk_layout* lay) {
   g.sb_bytes = lay->stride_b * esz;
   g.sh_bytes = lay->stride_h * esz;
   return g;
+}
+
+// ---------------------------------------------------------------------------
+// workspace: [hist (zeroed per call)] [scores] [spilled candidates] [partials]
+// ---------------------------------------------------------------------------
+struct TopkWs {
+  int64_t S, n, n_pad, K, nsplit, slice, nslice;
+  size_t hist, hist_words, scores, list, clist, slice_cnt, sel_row, sel_z, part, total;
+};
+
+TopkWs topk_ws(int64_t S, int64_t n, int64_t K) {
+  TopkWs w{};
+  w.S = S;
+  w.n = n;
+  const int64_t n1 = std::max<int64_t>(n, 1);
+  w.n_pad = rup(n1, 64);
+  w.K = K;
+  w.nsplit = cdiv(K, kSvRows);
+  // filter wave slices: at most 4 per select thread, about 4096 over the grid
+  w.slice = std::max<int64_t>(rup(cdiv(n1, 4 * kSelThreads), 64), std::min<int64_t>(8192, rup(cdiv(n1 * S, 4096), 64)));
+  w.nslice = cdiv(n1, w.slice);
+  size_t off = 0;
+  w.hist = off;
+  w.hist_words = (size_t)S * kHistBins;
+  off = al256(off + w.hist_words * 4);
+  w.scores = off;
+  off = al256(off + (size_t)S * w.n_pad * 4);
+  w.list = off;
+  off = al256(off + (size_t)S * w.n_pad * sizeof(Cand));
+  w.clist = off;
+  off = al256(off + (size_t)S * w.n_pad * sizeof(Cand));
+  w.slice_cnt = off;
+  off = al256(off + (size_t)S * w.nslice * 4);
+  w.sel_row = off;
+  off = al256(off + (size_t)S * K * 4);
+  w.sel_z = off;
+  off = al256(off + (size_t)S * K * 4);
+  w.part = off;
+  off = al256(off + (size_t)S * std::max<int64_t>(w.nsplit, kDenseMaxWg) * kPartStride * 4);
+  w.total = off;
+  return w;
+}
+
+RangeTab make_tab(const int64_t* ranges, int n_ranges, int64_t* n_total) {
+  RangeTab t{};
+  t.n = n_ranges;
+  int64_t pos = 0;
+  for (int r = 0; r < n_ranges; ++r) {
+    t.row0[r] = ranges[2 * r];
+    t.pos0[r] = pos;
+    pos += ranges[2 * r + 1] - ranges[2 * r];
+  }
+  t.pos0[n_ranges] = pos;
+  if (n_ranges == 0) {
+    t.n = 1;
+    t.row0[0] = 0;
+    t.pos0[0] = 0;
+    t.pos0[1] = 0;
+  }
+  *n_total = pos;
+  return t;
 }
 
 // ---------------------------------------------------------------------------
@@ -309,16 +329,18 @@ int32_t run_clear(hipStream_t s, uint32_t* p, int64_t words) {
   return launch(KID_CLEAR, s, [&] { hipLaunchKernelGGL(ws_clear, dim3((unsigned)blocks), dim3(256), 0, s, p, words); });
 }
 
-// Scan + filter + select over n positions (n > K) for every segment.
-// seg_active / head_active restrict the work (ReTopK exact heads).
+// The exact select over n positions (any n >= 1; n <= K takes every row):
+// histogram clear, scan, filter, select. Leaves the chosen rows and scores in
+// the workspace. `active` restricts the work to the listed segments (ReTopK
+// exact heads); null = all.
 int32_t run_exact_select(const Geo& g, const TopkWs& w, char* ws, const float* q, const void* k_cache,
                          const RangeTab& tab, float scale, const int32_t* active, int32_t* idx_out,
                          const DevInfo* di, hipStream_t s) {
   float* scores = (float*)(ws + w.scores);
   uint32_t* hist = (uint32_t*)(ws + w.hist);
-  int32_t* list = (int32_t*)(ws + w.list);
-  uint32_t* list_cnt = (uint32_t*)(ws + w.list_cnt);
-  // 1. scan
+  Cand* list = (Cand*)(ws + w.list);
+  uint32_t* slice_cnt = (uint32_t*)(ws + w.slice_cnt);
+  STDK_TRY(run_clear(s, hist, (int64_t)w.hist_words));
   {
     ScanArgs a{};
     a.q = q;
@@ -335,9 +357,9 @@ int32_t run_exact_select(const Geo& g, const TopkWs& w, char* ws, const float* q
     a.head_active = active;
     a.tab = tab;
     const int ri = g.bf16 ? scan_rows_iter<uint16_t>(g.G) : scan_rows_iter<float>(g.G);
-    // about 4 workgroups per CU over the whole grid, whole iterations each
-    const int64_t target_blocks = 1024;
-    const int64_t per_group = std::max<int64_t>(1, target_blocks / g.groups);
+    // one resident wave of workgroups over the whole chip, whole iterations each
+    const int64_t target_blocks = (int64_t)di->n_cu * di->scan_occ[g.bf16 ? 1 : 0][g.G];
+    const int64_t per_group = std::max<int64_t>(1, cdiv(target_blocks, g.groups));
     const int64_t rpb = std::max<int64_t>(ri, rup(cdiv(w.n, per_group), ri));
     a.rows_per_block = rpb;
     a.blocks_per_group = (int32_t)cdiv(w.n, rpb);
@@ -347,52 +369,54 @@ int32_t run_exact_select(const Geo& g, const TopkWs& w, char* ws, const float* q
       else launch_scan_t<float>(g.G, grid, s, a);
     }));
   }
-  // 2. filter
   {
     FilterArgs a{};
     a.scores = scores;
     a.hist = hist;
     a.list = list;
-    a.list_cnt = list_cnt;
+    a.slice_cnt = slice_cnt;
     a.n = w.n;
     a.n_pad = w.n_pad;
     a.K = (int32_t)w.K;
+    a.slice = (int32_t)w.slice;
+    a.nslice = (int32_t)w.nslice;
     a.seg_active = active;
-    a.chunk = std::max<int64_t>(4096, rup(cdiv(w.n * w.S, 1024), 1024));
-    const dim3 grid((unsigned)cdiv(w.n, a.chunk), (unsigned)w.S);
+    const dim3 grid((unsigned)cdiv(w.nslice, kFilterWaves), (unsigned)w.S);
     STDK_TRY(launch(KID_FILTER, s, [&] { hipLaunchKernelGGL(topk_filter, grid, dim3(kFilterThreads), 0, s, a); }));
   }
-  // 3. select
   {
     SelectArgs a{};
-    a.scores = scores;
     a.hist = hist;
     a.list = list;
-    a.list_cnt = list_cnt;
+    a.slice_cnt = slice_cnt;
+    a.clist = (Cand*)(ws + w.clist);
     a.n = w.n;
     a.n_pad = w.n_pad;
     a.K = (int32_t)w.K;
-    a.bitmap_words = (int32_t)w.words;
+    a.slice = (int32_t)w.slice;
+    a.nslice = (int32_t)w.nslice;
     a.sel_row = (int32_t*)(ws + w.sel_row);
     a.sel_z = (float*)(ws + w.sel_z);
     a.idx_out = idx_out;
-    a.gbitmap = (uint32_t*)(ws + w.gbitmap);
     a.seg_active = active;
     a.tab = tab;
-    const size_t bm_bytes = (size_t)w.words * 4;
-    const bool lds = bm_bytes + 12 * 1024 <= (size_t)di->max_lds;
+    const size_t pre_bytes = (size_t)((w.nslice + 2) & ~1LL) * 4;
+    const size_t avail = (size_t)di->max_lds - kSelStaticLds;
+    const size_t dyn = std::min(avail, pre_bytes + (size_t)w.n * sizeof(Cand));
+    a.cache_cap = (int32_t)((dyn - pre_bytes) / sizeof(Cand));
     STDK_TRY(launch(KID_SELECT, s, [&] {
-      if (lds)
-        hipLaunchKernelGGL(topk_select<true>, dim3((unsigned)w.S), dim3(kSelectThreads), bm_bytes, s, a);
-      else
-        hipLaunchKernelGGL(topk_select<false>, dim3((unsigned)w.S), dim3(kSelectThreads), 0, s, a);
+      hipLaunchKernelGGL(topk_select, dim3((unsigned)w.S), dim3(kSelThreads), dyn, s, a);
     }));
   }
   return STDK_OK;
 }
 
-int32_t run_sparse_sv(const Geo& g, const TopkWs& w, char* ws, const void* v_cache, float* o_out,
-                      float* lse_out, hipStream_t s) {
+int32_t run_combine(const TopkWs& w, char* ws, int32_t np, float* o_out, float* lse_out, hipStream_t s);
+
+// Softmax . V over the chosen rows left by the select kernels, in slices of
+// kSvRows rows, then the combine.
+int32_t run_sv(const Geo& g, const TopkWs& w, char* ws, const void* v_cache, float* o_out, float* lse_out,
+               hipStream_t s) {
   SvArgs a{};
   a.v = (const char*)v_cache;
   a.stride_b_bytes = g.sb_bytes;
@@ -400,18 +424,51 @@ int32_t run_sparse_sv(const Geo& g, const TopkWs& w, char* ws, const void* v_cac
   a.sel_row = (const int32_t*)(ws + w.sel_row);
   a.sel_z = (const float*)(ws + w.sel_z);
   a.part = (float*)(ws + w.part);
-  a.done = (uint32_t*)(ws + w.done);
-  a.o_out = o_out;
-  a.lse_out = lse_out;
   a.K = (int32_t)w.K;
   a.nsplit = (int32_t)w.nsplit;
   a.Hq = g.Hq;
   a.G = g.G;
   const dim3 grid((unsigned)w.nsplit, (unsigned)w.S);
-  return launch(KID_SV, s, [&] {
+  STDK_TRY(launch(KID_SV, s, [&] {
     if (g.bf16) hipLaunchKernelGGL(sparse_sv<uint16_t>, grid, dim3(kSvThreads), 0, s, a);
     else hipLaunchKernelGGL(sparse_sv<float>, grid, dim3(kSvThreads), 0, s, a);
-  });
+  }));
+  return run_combine(w, ws, (int32_t)w.nsplit, o_out, lse_out, s);
+}
+
+int32_t run_combine(const TopkWs& w, char* ws, int32_t np, float* o_out, float* lse_out, hipStream_t s) {
+  CombineArgs a{(const float*)(ws + w.part), o_out, lse_out, np, 0};
+  return launch(KID_COMBINE, s, [&] { hipLaunchKernelGGL(combine, dim3((unsigned)w.S), dim3(kHeadDim), 0, s, a); });
+}
+
+// Dense attention over all n rows (K >= n): one read of every K and V row
+// serves the G query heads of its KV head; partials combined per head.
+int32_t run_dense(const Geo& g, const TopkWs& w, char* ws, const float* q, const void* k_cache,
+                  const void* v_cache, const RangeTab& tab, float scale, int32_t top_k, int32_t* idx_out,
+                  float* o_out, float* lse_out, hipStream_t s) {
+  DenseArgs a{};
+  a.q = q;
+  a.k = (const char*)k_cache;
+  a.v = (const char*)v_cache;
+  a.stride_b_bytes = g.sb_bytes;
+  a.stride_h_bytes = g.sh_bytes;
+  a.part = (float*)(ws + w.part);
+  a.idx_out = idx_out;
+  a.n = w.n;
+  a.Hq = g.Hq;
+  a.Hkv = g.Hkv;
+  a.K = top_k;
+  a.scale = scale;
+  a.tab = tab;
+  const int64_t nwg = std::min<int64_t>(kDenseMaxWg, cdiv(w.n, kDenseTile));
+  a.rows_per_wg = rup(cdiv(w.n, nwg), kDenseTile);
+  a.nwg = (int32_t)cdiv(w.n, a.rows_per_wg);
+  const dim3 grid((unsigned)a.nwg, (unsigned)g.groups);
+  STDK_TRY(launch(KID_DENSE, s, [&] {
+    if (g.bf16) launch_dense_t<uint16_t>(g.G, grid, s, a);
+    else launch_dense_t<float>(g.G, grid, s, a);
+  }));
+  return run_combine(w, ws, a.nwg, o_out, lse_out, s);
 }
 
 }  // namespace
@@ -426,8 +483,7 @@ int32_t stdk_version(void) { return STDK_VERSION; }
 
 size_t topk_attn_decode_workspace_size(const stdk_layout* lay, int64_t n_scan, int32_t top_k) {
   if (check_layout(lay) != STDK_OK || n_scan < 0 || top_k < 1) return 0;
-  const Geo g = geo_of(lay);
-  return topk_ws(g.S, g.groups, n_scan, top_k).total;
+  return topk_ws(geo_of(lay).S, n_scan, top_k).total;
 }
 
 int32_t topk_attn_decode(const stdk_layout* lay, const float* q, const void* k_cache, const void* v_cache,
@@ -441,20 +497,24 @@ int32_t topk_attn_decode(const stdk_layout* lay, const float* q, const void* k_c
   STDK_TRY(check_ptr(lse_out, "lse_out", 4));
   if (idx_out && ((uintptr_t)idx_out) % 4) return fail(STDK_EINVAL, "idx_out is not 4-byte aligned");
   if (top_k < 1) return fail(STDK_EINVAL, "top_k %d < 1", top_k);
-  if (n_ranges < 0 || n_ranges > STDK_MAX_RANGES) return fail(STDK_EINVAL, "n_ranges %d outside 0..%d", n_ranges, STDK_MAX_RANGES);
+  if (n_ranges < 0 || n_ranges > STDK_MAX_RANGES)
+    return fail(STDK_EINVAL, "n_ranges %d outside 0..%d", n_ranges, STDK_MAX_RANGES);
   if (n_ranges > 0 && !ranges) return fail(STDK_EINVAL, "ranges is NULL");
   if (!std::isfinite(scale)) return fail(STDK_EINVAL, "scale is not finite");
   int64_t prev_end = 0;
   for (int r = 0; r < n_ranges; ++r) {
     const int64_t b = ranges[2 * r], e = ranges[2 * r + 1];
-    if (b < 0 || e > lay->max_len || e <= b) return fail(STDK_EINVAL, "range %d [%lld, %lld) invalid", r, (long long)b, (long long)e);
+    if (b < 0 || e > lay->max_len || e <= b)
+      return fail(STDK_EINVAL, "range %d [%lld, %lld) invalid", r, (long long)b, (long long)e);
     if (r > 0 && b < prev_end) return fail(STDK_EINVAL, "ranges must be ascending and disjoint");
     prev_end = e;
   }
   int64_t n = 0;
   const RangeTab tab = make_tab(ranges, n_ranges, &n);
+  if (top_k > kMaxTopK && top_k < n)
+    return fail(STDK_EUNSUPPORTED, "top_k %d > %d (below the row count)", top_k, kMaxTopK);
   const Geo g = geo_of(lay);
-  const TopkWs w = topk_ws(g.S, g.groups, n, top_k);
+  const TopkWs w = topk_ws(g.S, n, top_k);
   if (n > 0) {
     STDK_TRY(check_ptr(workspace, "workspace", 256));
     if (workspace_bytes < w.total)
@@ -473,37 +533,12 @@ int32_t topk_attn_decode(const stdk_layout* lay, const float* q, const void* k_c
     }));
     return ok();
   }
-  STDK_TRY(run_clear(s, (uint32_t*)(ws + w.clear_off), (int64_t)w.clear_words));
   if (top_k >= n) {
-    DenseArgs a{};
-    a.q = q;
-    a.k = (const char*)k_cache;
-    a.v = (const char*)v_cache;
-    a.stride_b_bytes = g.sb_bytes;
-    a.stride_h_bytes = g.sh_bytes;
-    a.part = (float*)(ws + w.part);
-    a.done = (uint32_t*)(ws + w.done_grp);
-    a.o_out = o_out;
-    a.lse_out = lse_out;
-    a.idx_out = idx_out;
-    a.n = n;
-    a.Hq = g.Hq;
-    a.Hkv = g.Hkv;
-    a.K = top_k;
-    a.scale = scale;
-    a.tab = tab;
-    const int64_t nwg = std::min<int64_t>(kDenseMaxWg, cdiv(n, kDenseTile));
-    a.rows_per_wg = rup(cdiv(n, nwg), kDenseTile);
-    a.nwg = (int32_t)cdiv(n, a.rows_per_wg);
-    const dim3 grid((unsigned)a.nwg, (unsigned)g.groups);
-    STDK_TRY(launch(KID_DENSE, s, [&] {
-      if (g.bf16) launch_dense_t<uint16_t>(g.G, grid, s, a);
-      else launch_dense_t<float>(g.G, grid, s, a);
-    }));
+    STDK_TRY(run_dense(g, w, ws, q, k_cache, v_cache, tab, scale, top_k, idx_out, o_out, lse_out, s));
     return ok();
   }
   STDK_TRY(run_exact_select(g, w, ws, q, k_cache, tab, scale, nullptr, idx_out, di, s));
-  STDK_TRY(run_sparse_sv(g, w, ws, v_cache, o_out, lse_out, s));
+  STDK_TRY(run_sv(g, w, ws, v_cache, o_out, lse_out, s));
   return ok();
 }
 
@@ -536,7 +571,9 @@ int32_t check_retopk(const stdk_layout* lay, const retopk_params* p, const retop
   if (!p) return fail(STDK_EINVAL, "params is NULL");
   if (!st) return fail(STDK_EINVAL, "state is NULL");
   if (p->top_k < 1) return fail(STDK_EINVAL, "top_k %d < 1", p->top_k);
-  if (p->cache_cap < 1 || p->cache_cap > kMaxCache) return fail(STDK_EINVAL, "cache_cap %d outside 1..%d", p->cache_cap, kMaxCache);
+  if (p->top_k > kMaxTopK) return fail(STDK_EUNSUPPORTED, "top_k %d > %d", p->top_k, kMaxTopK);
+  if (p->cache_cap < 1 || p->cache_cap > kMaxCache)
+    return fail(STDK_EINVAL, "cache_cap %d outside 1..%d", p->cache_cap, kMaxCache);
   if (p->top_r < 1 || p->top_r > p->cache_cap) return fail(STDK_EINVAL, "top_r %d outside 1..cache_cap", p->top_r);
   if (p->recent < 0) return fail(STDK_EINVAL, "recent %d < 0", p->recent);
   if (p->refresh < 0) return fail(STDK_EINVAL, "refresh %d < 0", p->refresh);
@@ -551,15 +588,16 @@ int32_t check_retopk(const stdk_layout* lay, const retopk_params* p, const retop
 }
 
 struct RetopkWs {
-  TopkWs t;  // exact path (scores, list, hist, sel, part, bitmap)
-  int64_t cand_cap;
-  size_t cand, n_cand, cz, qbar, path, exact, total;
+  TopkWs t;  // exact path
+  int64_t cand_cap, words;
+  size_t cand, n_cand, cz, qbar, path, exact, gbitmap, total;
 };
 
-RetopkWs retopk_ws(const Geo& g, const retopk_params* p, int64_t max_L) {
+RetopkWs retopk_ws(const Geo& g, const retopk_params* p, int64_t L) {
   RetopkWs r{};
-  r.t = topk_ws(g.S, g.groups, max_L, p->top_k);
+  r.t = topk_ws(g.S, L, p->top_k);
   r.cand_cap = (int64_t)p->top_r * p->top_k + p->recent;
+  r.words = cdiv(std::max<int64_t>(L, 1), 32);
   size_t off = r.t.total;
   r.cand = off;
   off = al256(off + (size_t)g.S * r.cand_cap * 4);
@@ -573,6 +611,8 @@ RetopkWs retopk_ws(const Geo& g, const retopk_params* p, int64_t max_L) {
   off = al256(off + (size_t)g.S * 4);
   r.exact = off;
   off = al256(off + (size_t)g.S * 4);
+  r.gbitmap = off;
+  off = al256(off + (size_t)g.S * r.words * 4);
   r.total = off;
   return r;
 }
@@ -625,7 +665,6 @@ int32_t retopk_step(const stdk_layout* lay, const retopk_params* p, const retopk
   const bool refresh_now = p->refresh > 0 && (t % p->refresh) == 0;
   int32_t* exact = (int32_t*)(ws + w.exact);
 
-  STDK_TRY(run_clear(s, (uint32_t*)(ws + w.t.clear_off), (int64_t)w.t.clear_words));
   // a6: selector (cosine, path, top-R, candidate union)
   {
     RtSelArgs a{};
@@ -642,7 +681,7 @@ int32_t retopk_step(const stdk_layout* lay, const retopk_params* p, const retopk
     a.refresh_now = refresh_now ? 1 : 0;
     a.L_t = L_t;
     a.cand_cap = (int32_t)w.cand_cap;
-    a.bitmap_words = (int32_t)cdiv(L_t, 32);
+    a.bitmap_words = (int32_t)w.words;
     a.qbar = (float*)(ws + w.qbar);
     a.path = (int32_t*)(ws + w.path);
     a.exact = exact;
@@ -651,59 +690,21 @@ int32_t retopk_step(const stdk_layout* lay, const retopk_params* p, const retopk
     a.path_out = path_out;
     a.n_cand_out = n_cand_out;
     a.cand_out = cand_out;
-    a.gbitmap = (uint32_t*)(ws + w.t.gbitmap);
-    const size_t bm_bytes = (size_t)a.bitmap_words * 4;
+    a.gbitmap = (uint32_t*)(ws + w.gbitmap);
+    const size_t bm_bytes = (size_t)w.words * 4;
     const bool lds = bm_bytes + 12 * 1024 <= (size_t)di->max_lds;
     STDK_TRY(launch(KID_RT_SELECT, s, [&] {
       if (lds) hipLaunchKernelGGL(retopk_select<true>, dim3((unsigned)g.S), dim3(kRtSelThreads), bm_bytes, s, a);
       else hipLaunchKernelGGL(retopk_select<false>, dim3((unsigned)g.S), dim3(kRtSelThreads), 0, s, a);
     }));
   }
-  // exact heads: a1 + a2 over [0, L_t)
+  // exact heads: scan + select + softmax.V over [0, L_t)
   const int64_t rng[2] = {0, L_t};
   int64_t n_all = 0;
   const RangeTab tab = make_tab(rng, 1, &n_all);
-  const TopkWs& tw = w.t;  // laid out for n = L_t
   const int32_t* active = refresh_now ? nullptr : exact;
-  if (L_t > p->top_k) {
-    STDK_TRY(run_exact_select(g, tw, ws, q, k_cache, tab, p->scale, active, support_out, di, s));
-  } else {
-    // every visible row is chosen: score them, then take all
-    ScanArgs a{};
-    a.q = q;
-    a.k = (const char*)k_cache;
-    a.stride_b_bytes = g.sb_bytes;
-    a.stride_h_bytes = g.sh_bytes;
-    a.scores = (float*)(ws + tw.scores);
-    a.hist = (uint32_t*)(ws + tw.hist);
-    a.n = L_t;
-    a.n_pad = tw.n_pad;
-    a.Hq = g.Hq;
-    a.Hkv = g.Hkv;
-    a.scale = p->scale;
-    a.head_active = active;
-    a.tab = tab;
-    const int ri = g.bf16 ? scan_rows_iter<uint16_t>(g.G) : scan_rows_iter<float>(g.G);
-    a.rows_per_block = rup(L_t, ri);
-    a.blocks_per_group = 1;
-    const dim3 grid((unsigned)g.groups);
-    STDK_TRY(launch(KID_SCAN, s, [&] {
-      if (g.bf16) launch_scan_t<uint16_t>(g.G, grid, s, a);
-      else launch_scan_t<float>(g.G, grid, s, a);
-    }));
-    SelectAllArgs b{};
-    b.scores = (const float*)(ws + tw.scores);
-    b.seg_active = active;
-    b.sel_row = (int32_t*)(ws + tw.sel_row);
-    b.sel_z = (float*)(ws + tw.sel_z);
-    b.idx_out = support_out;
-    b.n = L_t;
-    b.n_pad = tw.n_pad;
-    b.K = p->top_k;
-    b.tab = tab;
-    STDK_TRY(launch(KID_SELECT, s, [&] { hipLaunchKernelGGL(select_all, dim3((unsigned)g.S), dim3(256), 0, s, b); }));
-  }
-  // reuse heads: a7 indexed QK + rerank
+  STDK_TRY(run_exact_select(g, w.t, ws, q, k_cache, tab, p->scale, active, support_out, di, s));
+  // reuse heads: indexed QK over the candidates, rerank, softmax.V
   if (!refresh_now) {
     RtRerankArgs a{};
     a.q = q;
@@ -714,9 +715,8 @@ int32_t retopk_step(const stdk_layout* lay, const retopk_params* p, const retopk
     a.cand = (const int32_t*)(ws + w.cand);
     a.n_cand = (const int32_t*)(ws + w.n_cand);
     a.cz = (float*)(ws + w.cz);
-    a.done = (uint32_t*)(ws + tw.done_rr);
-    a.sel_row = (int32_t*)(ws + tw.sel_row);
-    a.sel_z = (float*)(ws + tw.sel_z);
+    a.sel_row = (int32_t*)(ws + w.t.sel_row);
+    a.sel_z = (float*)(ws + w.t.sel_z);
     a.support_out = support_out;
     a.cand_cap = (int32_t)w.cand_cap;
     a.K = p->top_k;
@@ -729,9 +729,13 @@ int32_t retopk_step(const stdk_layout* lay, const retopk_params* p, const retopk
       if (g.bf16) hipLaunchKernelGGL(retopk_rerank<uint16_t>, grid, dim3(kRerankThreads), 0, s, a);
       else hipLaunchKernelGGL(retopk_rerank<float>, grid, dim3(kRerankThreads), 0, s, a);
     }));
+    STDK_TRY(launch(KID_RT_RSEL, s, [&] {
+      hipLaunchKernelGGL(retopk_rerank_select, dim3((unsigned)g.S), dim3(kRerankSelThreads), 0, s, a);
+    }));
   }
-  // a8: softmax . V over the chosen rows, then the push
-  STDK_TRY(run_sparse_sv(g, tw, ws, v_cache, o_out, lse_out, s));
+  // a8: softmax . V over the chosen rows of every head (either path)
+  STDK_TRY(run_sv(g, w.t, ws, v_cache, o_out, lse_out, s));
+  // a8: push (q_bar, support)
   {
     RtPushArgs a{(const float*)(ws + w.qbar), support_out, st->q_hat, st->support, st->head, st->count,
                  p->cache_cap, p->top_k};
@@ -743,9 +747,16 @@ int32_t retopk_step(const stdk_layout* lay, const retopk_params* p, const retopk
 // ---------------------------------------------------------------------------
 // launch timing
 // ---------------------------------------------------------------------------
-int32_t stdk_profile_enable(int32_t capacity) {
+int32_t stdk_profile_enable(int32_t capacity, const char* only) {
   if (capacity < 1) return fail(STDK_EINVAL, "capacity %d < 1", capacity);
+  int only_id = -1;
+  if (only) {
+    for (int i = 0; i < KID_COUNT; ++i)
+      if (std::strcmp(only, kKernelNames[i]) == 0) only_id = i;
+    if (only_id < 0) return fail(STDK_EINVAL, "unknown kernel name %s", only);
+  }
   std::lock_guard<std::mutex> lk(g_prof.mu);
+  g_prof.only = only_id;
   const size_t want = (size_t)capacity * 2;
   while (g_prof.ev.size() < want) {
     hipEvent_t e;

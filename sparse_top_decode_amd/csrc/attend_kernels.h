@@ -5,8 +5,8 @@
 // maximum as in "CPU-GPU Co-Execution Architecture" (o_W, o_Omega), and the
 // rescaled combination of Eq. 4-5 (gamma_j = e^{lse_j - lse}). Work is split
 // over several workgroups per head; each produces (m, s, sum e^{z-m} v) for
-// its rows and the last workgroup to finish combines them in a fixed order
-// with the same rescaling, so the result does not depend on timing.
+// its rows and a combine kernel merges them in a fixed order with the same
+// rescaling, so the result does not depend on timing.
 #pragma once
 
 #include "device.h"
@@ -17,21 +17,35 @@ namespace stdk {
 constexpr int kPartStride = 132;  // m, s, pad, pad, o[128]
 
 // Combines `np` partials (m, s, o) starting at `part` into o_out[128] and
-// *lse_out. Runs on the first 128 threads of the block.
-STDK_DEV void combine_partials(const float* part, int np, float* o_out, float* lse_out) {
+// *lse_out, in partial order. Runs on a block of kHeadDim threads; `sm` and
+// `sf` are LDS scratch of np floats each (np <= kMaxPartials).
+constexpr int kMaxPartials = 1024;
+
+STDK_DEV void combine_partials(const float* part, int np, float* o_out, float* lse_out, float* sm, float* sf,
+                               float* red) {
   const int j = threadIdx.x;
-  if (j >= kHeadDim) return;
+  for (int i = j; i < np; i += kHeadDim) {
+    sm[i] = part[(int64_t)i * kPartStride];
+    sf[i] = part[(int64_t)i * kPartStride + 1];
+  }
+  __syncthreads();
   float M = -INFINITY;
-  for (int i = 0; i < np; ++i) M = fmaxf(M, part[(int64_t)i * kPartStride]);
+  for (int i = j; i < np; i += kHeadDim) M = fmaxf(M, sm[i]);
+  M = wave_max(M);
+  if ((j & 63) == 0) red[j >> 6] = M;
+  __syncthreads();
+  M = fmaxf(red[0], red[1]);
+  __syncthreads();
+  // weights e^{m_i - M}; the denominator in partial order
+  for (int i = j; i < np; i += kHeadDim) sm[i] = (sm[i] == -INFINITY) ? 0.f : __expf(sm[i] - M);
+  __syncthreads();
   float S = 0.f, O = 0.f;
   if (M != -INFINITY) {
+#pragma unroll 8
     for (int i = 0; i < np; ++i) {
-      const float* p = part + (int64_t)i * kPartStride;
-      const float mi = p[0];
-      if (mi == -INFINITY) continue;
-      const float f = __expf(mi - M);
-      S = fmaf(p[1], f, S);
-      O = fmaf(p[4 + j], f, O);
+      const float f = sm[i];
+      S = fmaf(sf[i], f, S);
+      O = fmaf(part[(int64_t)i * kPartStride + 4 + j], f, O);
     }
   }
   if (S > 0.f) {
@@ -43,111 +57,20 @@ STDK_DEV void combine_partials(const float* part, int np, float* o_out, float* l
   }
 }
 
-// Last-arriver election: returns true in every thread of the workgroup that
-// is the last of `expected` to arrive on `counter`, and resets the counter.
-STDK_DEV bool last_to_arrive(uint32_t* counter, uint32_t expected, int* s_flag) {
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t prev = atomicAdd(counter, 1u);
-    const bool last = prev == expected - 1;
-    if (last) atomicExch(counter, 0u);
-    *s_flag = last ? 1 : 0;
-  }
-  __syncthreads();
-  const bool last = *s_flag != 0;
-  if (last) __threadfence();
-  return last;
-}
-
-// ---------------------------------------------------------------------------
-// sparse_sv: gathered-row softmax . V over K chosen rows per segment.
-// ---------------------------------------------------------------------------
-struct SvArgs {
-  const char* v;           // value cache base
-  int64_t stride_b_bytes, stride_h_bytes;
-  const int32_t* sel_row;  // [S][K], -1 = unused slot
-  const float* sel_z;      // [S][K]
-  float* part;             // [S][nsplit][kPartStride]
-  uint32_t* done;          // [S] counters (start at 0, left at 0)
-  float* o_out;            // [S][128]
-  float* lse_out;          // [S]
-  int32_t K, nsplit, Hq, G;
+// Combines the per-workgroup partials of every segment (one workgroup per
+// segment; the kernel boundary makes the partials visible).
+struct CombineArgs {
+  const float* part;  // [S][np][kPartStride]
+  float* o_out;       // [S][128]
+  float* lse_out;     // [S]
+  int32_t np;
+  int32_t pad_;
 };
 
-constexpr int kSvThreads = 256;
-constexpr int kSvRows = 64;  // rows per workgroup
-
-template <typename T>
-__global__ __launch_bounds__(kSvThreads) void sparse_sv(SvArgs a) {
-  constexpr int EPL = KvTraits<T>::EPL, LPR = KvTraits<T>::LPR, RPL = KvTraits<T>::RPL, ROWB = KvTraits<T>::ROWB;
-  constexpr int NW = kSvThreads / 64;
-  constexpr int GROUPS = NW * RPL;  // row groups in the block
-  __shared__ int32_t rows[kSvRows];
-  __shared__ float wts[kSvRows];
-  __shared__ float red[GROUPS][kHeadDim];
-  __shared__ float s_m;
-  __shared__ int s_flag;
-  const int64_t seg = blockIdx.y;
-  const int split = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int rg = lane / LPR, c = lane % LPR;
-  const int b = (int)(seg / a.Hq), hq = (int)(seg % a.Hq), hkv = hq / a.G;
-  const int j0 = split * kSvRows;
-  const int nr = min(kSvRows, a.K - j0);
-
-  float z = -INFINITY;
-  if (tid < kSvRows) {
-    int32_t r = -1;
-    if (tid < nr) {
-      r = a.sel_row[seg * a.K + j0 + tid];
-      if (r >= 0) z = a.sel_z[seg * a.K + j0 + tid];
-    }
-    rows[tid] = r;
-  }
-  // block max over the 64 scores (held by wave 0)
-  if (w == 0) {
-    const float mx = wave_max(z);
-    if (lane == 0) s_m = mx;
-  }
-  __syncthreads();
-  const float m = s_m;
-  if (tid < kSvRows) wts[tid] = (m == -INFINITY || z == -INFINITY) ? 0.f : __expf(z - m);
-  __syncthreads();
-
-  const char* vb = a.v + (int64_t)b * a.stride_b_bytes + (int64_t)hkv * a.stride_h_bytes;
-  float acc[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-  const int gid = w * RPL + rg;  // row group id in the block
-  for (int i = gid; i < kSvRows; i += GROUPS) {
-    const int32_t r = rows[i];
-    if (r < 0) continue;
-    const float wt = wts[i];
-    float x[EPL];
-    unpack16<T>(load16(vb + (int64_t)r * ROWB + c * 16), x);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = fmaf(wt, x[e], acc[e]);
-  }
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) red[gid][c * EPL + e] = acc[e];
-  __syncthreads();
-  float* part = a.part + (seg * a.nsplit + split) * kPartStride;
-  if (tid < kHeadDim) {
-    float o = 0.f;
-#pragma unroll
-    for (int g = 0; g < GROUPS; ++g) o += red[g][tid];
-    part[4 + tid] = o;
-  }
-  if (w == 0) {
-    const float s = wave_sum(tid < kSvRows ? wts[tid] : 0.f);
-    if (lane == 0) {
-      part[0] = m;
-      part[1] = s;
-    }
-  }
-  if (last_to_arrive(&a.done[seg], (uint32_t)a.nsplit, &s_flag))
-    combine_partials(a.part + seg * a.nsplit * kPartStride, a.nsplit, a.o_out + seg * kHeadDim, a.lse_out + seg);
+__global__ __launch_bounds__(kHeadDim) void combine(CombineArgs a) {
+  __shared__ float sm[kMaxPartials], sf[kMaxPartials], red[2];
+  const int64_t seg = blockIdx.x;
+  combine_partials(a.part + seg * a.np * kPartStride, a.np, a.o_out + seg * kHeadDim, a.lse_out + seg, sm, sf, red);
 }
 
 // ---------------------------------------------------------------------------
@@ -161,9 +84,6 @@ struct DenseArgs {
   const char* v;
   int64_t stride_b_bytes, stride_h_bytes;
   float* part;             // [S][nwg][kPartStride]
-  uint32_t* done;          // [B*Hkv]
-  float* o_out;            // [S][128]
-  float* lse_out;          // [S]
   int32_t* idx_out;        // [S][K] or null
   int64_t n;
   int64_t rows_per_wg;
@@ -186,7 +106,6 @@ __global__ __launch_bounds__(kDenseThreads) void dense_attn(DenseArgs a) {
   __shared__ int64_t trow[kDenseTile];
   __shared__ float tmax[G], tsum[G];
   __shared__ float red[NW][G][kHeadDim];
-  __shared__ int s_flag;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int rg = lane / LPR, c = lane % LPR;
@@ -329,12 +248,6 @@ __global__ __launch_bounds__(kDenseThreads) void dense_attn(DenseArgs a) {
       for (int64_t p = a.n + tid; p < a.K; p += kDenseThreads)
 #pragma unroll
         for (int h = 0; h < G; ++h) a.idx_out[(seg0 + h) * a.K + p] = -1;
-  }
-  if (last_to_arrive(&a.done[group], (uint32_t)a.nwg, &s_flag)) {
-    for (int h = 0; h < G; ++h) {
-      combine_partials(a.part + (seg0 + h) * a.nwg * kPartStride, a.nwg, a.o_out + (seg0 + h) * kHeadDim,
-                       a.lse_out + seg0 + h);
-    }
   }
 }
 

@@ -84,6 +84,18 @@ STDK_DEV uint32_t lane_rank(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP: shifted adds
+// inside each 16-lane row, then row broadcasts across rows.
+STDK_DEV uint32_t wave_incl_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return x;
+}
+
 // Exclusive prefix sum over the block (NT threads, NT % 64 == 0). `tmp` is
 // LDS of at least NT/64 + 1 words. Returns the exclusive prefix; *total gets
 // the block sum. Ends with a barrier, so `tmp` may be reused afterwards.
@@ -91,27 +103,17 @@ template <int NT>
 STDK_DEV uint32_t block_excl_scan(uint32_t v, uint32_t* tmp, uint32_t* total) {
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = wave_incl_scan(v);
   if (lane == 63) tmp[w] = x;
   __syncthreads();
   if (w == 0) {
-    uint32_t t = (lane < NW) ? tmp[lane] : 0u;
-    uint32_t s = t;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      uint32_t y = __shfl_up(s, o, 64);
-      if (lane >= o) s += y;
-    }
+    const uint32_t t = (lane < NW) ? tmp[lane] : 0u;
+    const uint32_t s = wave_incl_scan(t);
     if (lane < NW) tmp[lane] = s - t;
     if (lane == NW - 1) tmp[NW] = s;
   }
   __syncthreads();
-  uint32_t res = x - v + tmp[w];
+  const uint32_t res = x - v + tmp[w];
   *total = tmp[NW];
   __syncthreads();
   return res;
@@ -159,9 +161,6 @@ STDK_DEV void find_bin(const uint32_t* hist, int nb, uint32_t need, uint32_t* tm
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-STDK_DEV u32x4 load16_nt(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-}
 STDK_DEV u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
 }  // namespace stdk

@@ -21,6 +21,7 @@
 #include "attend_kernels.h"
 #include "device.h"
 #include "scan_kernels.h"
+#include "select_kernels.h"
 
 namespace stdk {
 
@@ -187,9 +188,8 @@ __global__ __launch_bounds__(kRtSelThreads) void retopk_select(RtSelArgs a) {
   }
 }
 
-// Indexed QK over the candidates of reuse-path heads (rows read in place by
-// index, no gathered copy), then, in the last workgroup of each head, the
-// exact top-K among them in candidate (= ascending row) order.
+// Indexed QK over the candidates of reuse-path heads: rows read in place by
+// index, no gathered copy.
 struct RtRerankArgs {
   const float* q;           // [S][128]
   const char* k;
@@ -198,7 +198,6 @@ struct RtRerankArgs {
   const int32_t* cand;      // [S][cand_cap]
   const int32_t* n_cand;    // [S]
   float* cz;                // [S][cand_cap] scores
-  uint32_t* done;           // [S]
   int32_t* sel_row;         // [S][K]
   float* sel_z;             // [S][K]
   int32_t* support_out;     // [S][K]
@@ -214,10 +213,6 @@ __global__ __launch_bounds__(kRerankThreads) void retopk_rerank(RtRerankArgs a) 
   constexpr int EPL = KvTraits<T>::EPL, LPR = KvTraits<T>::LPR, RPL = KvTraits<T>::RPL, ROWB = KvTraits<T>::ROWB;
   constexpr int NW = kRerankThreads / 64;
   constexpr int GROUPS = NW * RPL;
-  __shared__ uint32_t h[kHistBins];
-  __shared__ uint32_t tmp[kRerankThreads / 64 + 1];
-  __shared__ int s_bin, s_flag;
-  __shared__ uint32_t s_beyond;
   const int64_t seg = blockIdx.y;
   if (a.exact[seg]) return;
   const int split = blockIdx.x;
@@ -231,131 +226,141 @@ __global__ __launch_bounds__(kRerankThreads) void retopk_rerank(RtRerankArgs a) 
   float qr[1][EPL];
   load_q_slice<T, 1>(a.q, seg, c, qr);
   const char* kb = a.k + (int64_t)b * a.stride_b_bytes + (int64_t)hkv * a.stride_h_bytes;
-  const int j0 = split * kRerankRows, j1 = min(M, j0 + kRerankRows);
-  for (int jb = j0; jb < j1; jb += GROUPS) {
-    const int j = jb + w * RPL + rg;
-    u32x4 kw = u32x4{0u, 0u, 0u, 0u};
-    if (j < j1) kw = load16(kb + (int64_t)cd[j] * ROWB + c * 16);
-    float d[1];
-    chunk_dots<T, 1>(kw, qr, d);
-    const float s = group_sum<LPR>(d[0]);
-    if (c == 0 && j < j1) cz[j] = s * a.scale;
+  // row group gid scores candidates j0 + gid + GROUPS*u, u < RU: the indices
+  // and then the rows are fetched in one batch each
+  constexpr int RU = kRerankRows / GROUPS;
+  const int gid = w * RPL + rg;
+  const int j0 = split * kRerankRows;
+  int32_t row[RU];
+#pragma unroll
+  for (int u = 0; u < RU; ++u) {
+    const int j = j0 + gid + GROUPS * u;
+    row[u] = (j < M) ? cd[j] : -1;
   }
-  if (!last_to_arrive(&a.done[seg], (uint32_t)a.nsplit, &s_flag)) return;
+  u32x4 kw[RU];
+#pragma unroll
+  for (int u = 0; u < RU; ++u) kw[u] = (row[u] >= 0) ? load16(kb + (int64_t)row[u] * ROWB + c * 16) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int u = 0; u < RU; ++u) {
+    float d[1];
+    chunk_dots<T, 1>(kw[u], qr, d);
+    const float s = group_sum<LPR>(d[0]);
+    const int j = j0 + gid + GROUPS * u;
+    if (c == 0 && j < M) cz[j] = s * a.scale;
+  }
+}
 
-  // top-K among the M candidates; ties -> lower candidate index (= lower row)
+// Exact top-K among the M candidates of each reuse-path head (ties -> lower
+// candidate index, i.e. lower row). One workgroup per head; writes the chosen
+// rows (ascending), their scores and the support output.
+constexpr int kRerankSelThreads = 256;
+
+__global__ __launch_bounds__(kRerankSelThreads) void retopk_rerank_select(RtRerankArgs a) {
+  constexpr int NT = kRerankSelThreads;
+  __shared__ uint32_t h[kHistBins];
+  __shared__ uint32_t tmp[NT / 64 + 1];
+  __shared__ int s_bin;
+  __shared__ uint32_t s_beyond;
+  const int64_t seg = blockIdx.x;
+  if (a.exact[seg]) return;
+  const int tid = threadIdx.x;
+  const uint32_t M = (uint32_t)a.n_cand[seg];
+  const int32_t* cd = a.cand + seg * a.cand_cap;
+  const float* cz = a.cz + seg * a.cand_cap;
   const int K = a.K;
   int32_t* srow = a.sel_row + seg * K;
   float* sz = a.sel_z + seg * K;
   int32_t* so = a.support_out + seg * K;
-  uint32_t Tk = 0u;
-  int32_t cut = 0x7FFFFFFF;
-  if (M > K) {
-    uint32_t need = (uint32_t)K, prefix = 0;
+  const bool take_all = M <= (uint32_t)K;
+  constexpr int U = 8;
+
+  uint32_t Tk = 0u, need = (uint32_t)K;
+  if (!take_all) {
+    uint32_t prefix = 0;
     const int shifts[3] = {21, 10, 0};
     const int bits[3] = {11, 11, 10};
 #pragma unroll
     for (int dgt = 0; dgt < 3; ++dgt) {
       const int nb = 1 << bits[dgt];
-      for (int i = tid; i < nb; i += kRerankThreads) h[i] = 0u;
+      for (int i = tid; i < nb; i += NT) h[i] = 0u;
       __syncthreads();
       const int hs = shifts[dgt] + bits[dgt];
-      for (int j = tid; j < M; j += kRerankThreads) {
-        const uint32_t key = f2key(cz[j]);
-        if (dgt == 0 || (key >> hs) == prefix) atomicAdd(&h[(key >> shifts[dgt]) & (uint32_t)(nb - 1)], 1u);
+      for (uint32_t base = 0; base < M; base += NT * U) {
+        uint32_t kv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const uint32_t j = base + u * NT + tid;
+          kv[u] = (j < M) ? f2key(cz[j]) : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const uint32_t j = base + u * NT + tid;
+          if (j < M && (dgt == 0 || (kv[u] >> hs) == prefix))
+            atomicAdd(&h[(kv[u] >> shifts[dgt]) & (uint32_t)(nb - 1)], 1u);
+        }
       }
       __syncthreads();
-      find_bin<kRerankThreads, true>(h, nb, need, tmp, &s_bin, &s_beyond);
+      find_bin<NT, true>(h, nb, need, tmp, &s_bin, &s_beyond);
       prefix = (prefix << bits[dgt]) | (uint32_t)(s_bin < 0 ? 0 : s_bin);
       need -= s_beyond;
       __syncthreads();
     }
-    Tk = prefix;
-    // count ties
-    if (tid == 0) h[0] = 0u;
-    __syncthreads();
-    for (int j = tid; j < M; j += kRerankThreads)
-      if (f2key(cz[j]) == Tk) atomicAdd(&h[0], 1u);
-    __syncthreads();
-    const uint32_t ties = h[0];
-    __syncthreads();
-    if (need < ties) {
-      uint32_t pfx = 0, rem = need;
-      const int psh[3] = {20, 9, 0};
-      const int pbt[3] = {11, 11, 9};
-#pragma unroll
-      for (int dgt = 0; dgt < 3; ++dgt) {
-        const int nb = 1 << pbt[dgt];
-        for (int i = tid; i < nb; i += kRerankThreads) h[i] = 0u;
-        __syncthreads();
-        const int hs = psh[dgt] + pbt[dgt];
-        for (int j = tid; j < M; j += kRerankThreads) {
-          if (f2key(cz[j]) == Tk && (dgt == 0 || ((uint32_t)j >> hs) == pfx))
-            atomicAdd(&h[((uint32_t)j >> psh[dgt]) & (uint32_t)(nb - 1)], 1u);
-        }
-        __syncthreads();
-        find_bin<kRerankThreads, false>(h, nb, rem, tmp, &s_bin, &s_beyond);
-        pfx = (pfx << pbt[dgt]) | (uint32_t)(s_bin < 0 ? 0 : s_bin);
-        rem -= s_beyond;
-        __syncthreads();
-      }
-      cut = (int32_t)pfx;
-    }
+    Tk = prefix;  // the K-th largest key; keep the first `need` candidates equal to it
   }
   // ordered compaction over candidate index
-  const int per = (M + kRerankThreads - 1) / kRerankThreads;
-  const int q0 = tid * per, q1 = min(M, q0 + per);
-  uint32_t cnt = 0;
-  for (int j = q0; j < q1; ++j) {
-    const uint32_t key = f2key(cz[j]);
-    cnt += (M <= K) || key > Tk || (key == Tk && j <= cut);
-  }
-  uint32_t total;
-  uint32_t r = block_excl_scan<kRerankThreads>(cnt, tmp, &total);
-  for (int j = q0; j < q1; ++j) {
-    const uint32_t key = f2key(cz[j]);
-    if ((M <= K) || key > Tk || (key == Tk && j <= cut)) {
-      if (r < (uint32_t)K) {
-        srow[r] = cd[j];
-        sz[r] = cz[j];
-        so[r] = cd[j];
+  const uint32_t per = (M + NT - 1) / NT;
+  const uint32_t q0 = min(M, tid * per), q1 = min(M, q0 + per);
+  uint32_t n_gt = 0, n_eq = 0;
+  for (uint32_t jb = q0; jb < q1; jb += U) {
+    uint32_t kv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) kv[u] = (jb + u < q1) ? f2key(cz[jb + u]) : 0u;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (jb + u < q1) {
+        n_gt += take_all || kv[u] > Tk;
+        n_eq += !take_all && kv[u] == Tk;
       }
-      ++r;
     }
   }
-  for (uint32_t i = total + tid; i < (uint32_t)K; i += kRerankThreads) {
+  uint32_t tot_eq, tot_all;
+  const uint32_t eq_before = block_excl_scan<NT>(n_eq, tmp, &tot_eq);
+  const uint32_t take_eq = min(n_eq, need > eq_before ? need - eq_before : 0u);
+  uint32_t r = block_excl_scan<NT>(n_gt + take_eq, tmp, &tot_all);
+  uint32_t eq_seen = eq_before;
+  for (uint32_t jb = q0; jb < q1; jb += U) {
+    float zv[U];
+    int32_t rv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (jb + u < q1) {
+        zv[u] = cz[jb + u];
+        rv[u] = cd[jb + u];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (jb + u >= q1) break;
+      const uint32_t key = f2key(zv[u]);
+      bool take = take_all || key > Tk;
+      if (!take_all && key == Tk) {
+        take = eq_seen < need;
+        ++eq_seen;
+      }
+      if (take) {
+        if (r < (uint32_t)K) {
+          srow[r] = rv[u];
+          sz[r] = zv[u];
+          so[r] = rv[u];
+        }
+        ++r;
+      }
+    }
+  }
+  for (uint32_t i = tot_all + tid; i < (uint32_t)K; i += NT) {
     srow[i] = -1;
     sz[i] = -INFINITY;
     so[i] = -1;
-  }
-}
-
-// Exact path when the visible rows do not exceed K: every row is chosen.
-struct SelectAllArgs {
-  const float* scores;        // [S][n_pad]
-  const int32_t* seg_active;  // [S] or null
-  int32_t* sel_row;
-  float* sel_z;
-  int32_t* idx_out;           // [S][K] or null
-  int64_t n, n_pad;
-  int32_t K;
-  int32_t pad_;
-  RangeTab tab;
-};
-
-__global__ __launch_bounds__(256) void select_all(SelectAllArgs a) {
-  const int64_t seg = blockIdx.x;
-  if (a.seg_active && a.seg_active[seg] == 0) return;
-  for (int64_t p = threadIdx.x; p < a.K; p += 256) {
-    int32_t row = -1;
-    float z = -INFINITY;
-    if (p < a.n) {
-      row = (int32_t)pos_to_row(a.tab, p);
-      z = a.scores[seg * a.n_pad + p];
-    }
-    a.sel_row[seg * a.K + p] = row;
-    a.sel_z[seg * a.K + p] = z;
-    if (a.idx_out) a.idx_out[seg * a.K + p] = row;
   }
 }
 

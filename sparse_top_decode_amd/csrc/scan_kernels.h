@@ -90,27 +90,51 @@ struct ScanArgs {
   RangeTab tab;
 };
 
+// The scan reads each key row with 8 lanes; lane c of the row owns the
+// 16-byte chunks c, c+8, ... (byte offsets k*128 + c*16), i.e. 16 elements.
+template <typename T>
+struct ScanTraits;
+template <>
+struct ScanTraits<uint16_t> {
+  static constexpr int NCH = 2, EPC = 8, ROWB = 256;
+};
+template <>
+struct ScanTraits<float> {
+  static constexpr int NCH = 4, EPC = 4, ROWB = 512;
+};
+
 constexpr int kScanThreads = 512;
+constexpr int kScanLPR = 8;  // lanes per key row
 
 template <typename T, int G>
 struct ScanShape {
-  static constexpr int LPR = KvTraits<T>::LPR;
-  static constexpr int RPL = KvTraits<T>::RPL;
-  static constexpr int U0 = LPR / G;
-  static constexpr int U = U0 < 1 ? 1 : (U0 > 8 ? 8 : U0);  // loads in flight per lane
+  static constexpr int UR0 = kScanLPR / G;
+  static constexpr int UR = UR0 < 1 ? 1 : (UR0 > 4 ? 4 : UR0);  // rows per row group and iteration
   static constexpr int NW = kScanThreads / 64;
-  static constexpr int ROWS_ITER = NW * U * RPL;
+  static constexpr int RPB = 64 / kScanLPR;  // rows per wave and row batch (8)
+  static constexpr int ROWS_ITER = NW * UR * RPB;
 };
+
+// Sum over aligned groups of 8 lanes with DPP (mirror within half rows, then
+// two quad permutations); all 8 lanes end with the same bits.
+STDK_DEV float sum8(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));  // row_half_mirror
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  return x;
+}
 
 template <typename T, int G>
 __global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
   using Sh = ScanShape<T, G>;
-  constexpr int EPL = KvTraits<T>::EPL, LPR = Sh::LPR, RPL = Sh::RPL, U = Sh::U, ROWB = KvTraits<T>::ROWB;
-  static_assert(U * G <= LPR, "one output lane per (load, head)");
+  using Tr = ScanTraits<T>;
+  constexpr int NCH = Tr::NCH, EPC = Tr::EPC, ROWB = Tr::ROWB, UR = Sh::UR, RPB = Sh::RPB;
+  constexpr int E = NCH * EPC;  // elements per lane (16)
+  static_assert(UR * G <= kScanLPR || UR == 1, "output lanes");
   __shared__ uint32_t lh[G * kHistBins];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int rg = lane / LPR, c = lane % LPR;
+  const int rg = lane / kScanLPR, c = lane % kScanLPR;
   const int group = blockIdx.x / a.blocks_per_group;
   const int blk = blockIdx.x % a.blocks_per_group;
   const int b = group / a.Hkv, hkv = group % a.Hkv;
@@ -122,12 +146,26 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
     if (!any) return;
   }
 
-  float qr[G][EPL];
-  load_q_slice<T, G>(a.q, seg0, c, qr);
+  // this lane's 16 query elements for each head
+  float qr[G][E];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+      const float4* qp = reinterpret_cast<const float4*>(a.q + (seg0 + h) * kHeadDim + k * (kHeadDim / NCH) + c * EPC);
+#pragma unroll
+      for (int e4 = 0; e4 < EPC / 4; ++e4) {
+        const float4 v = qp[e4];
+        qr[h][k * EPC + 4 * e4 + 0] = v.x;
+        qr[h][k * EPC + 4 * e4 + 1] = v.y;
+        qr[h][k * EPC + 4 * e4 + 2] = v.z;
+        qr[h][k * EPC + 4 * e4 + 3] = v.w;
+      }
+    }
   for (int i = tid; i < G * kHistBins; i += kScanThreads) lh[i] = 0u;
   __syncthreads();
 
-  const char* kb = a.k + (int64_t)b * a.stride_b_bytes + (int64_t)hkv * a.stride_h_bytes;
+  const char* kb = a.k + (int64_t)b * a.stride_b_bytes + (int64_t)hkv * a.stride_h_bytes + c * 16;
   const int64_t p_beg = (int64_t)blk * a.rows_per_block;
   const int64_t p_end = min(a.n, p_beg + a.rows_per_block);
   for (int r = 0; r < a.tab.n; ++r) {
@@ -135,36 +173,66 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
     const int64_t s1 = min(p_end, a.tab.pos0[r + 1]);
     if (s0 >= s1) continue;
     const int64_t rowoff = a.tab.row0[r] - a.tab.pos0[r];
-    for (int64_t base = s0; base < s1; base += Sh::ROWS_ITER) {
-      u32x4 kw[U];
+    // rows of row batch u of this lane for the iteration at `base`; loads are
+    // clamped to the last row of the piece and the extra results dropped
+    auto issue = [&](int64_t base, u32x4 (&kw)[UR][NCH]) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t p = base + (int64_t)(w * U + u) * RPL + rg;
-        if (p < s1)
-          kw[u] = load16_nt(kb + (p + rowoff) * ROWB + c * 16);
-        else
-          kw[u] = u32x4{0u, 0u, 0u, 0u};
+      for (int u = 0; u < UR; ++u) {
+        const int64_t p = min(base + (int64_t)(w * UR + u) * RPB + rg, s1 - 1);
+        const char* rp = kb + (p + rowoff) * ROWB;
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) kw[u][k] = load16(rp + k * 128);
       }
-      float acc[U][G];
+    };
+    auto consume = [&](int64_t base, const u32x4 (&kw)[UR][NCH]) {
+      float acc[UR][G];
 #pragma unroll
-      for (int u = 0; u < U; ++u) chunk_dots<T, G>(kw[u], qr, acc[u]);
+      for (int u = 0; u < UR; ++u) {
+        float x[E];
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+        for (int k = 0; k < NCH; ++k) unpack16<T>(kw[u][k], x + k * EPC);
 #pragma unroll
-        for (int h = 0; h < G; ++h) acc[u][h] = group_sum<LPR>(acc[u][h]);
-      if (c < U * G) {
-        float val = 0.f;
+        for (int h = 0; h < G; ++h) {
+          float s = qr[h][0] * x[0];
 #pragma unroll
-        for (int i = 0; i < U * G; ++i)
-          if (c == i) val = acc[i / G][i % G];
-        const int uu = c / G, hh = c % G;
-        const int64_t p = base + (int64_t)(w * U + uu) * RPL + rg;
-        if (p < s1) {
-          val *= a.scale;
-          a.scores[(seg0 + hh) * a.n_pad + p] = val;
-          atomicAdd(&lh[hh * kHistBins + (f2key(val) >> (32 - kHistBits))], 1u);
+          for (int e = 1; e < E; ++e) s = fmaf(qr[h][e], x[e], s);
+          acc[u][h] = sum8(s);
         }
       }
+#pragma unroll
+      for (int i0 = 0; i0 < UR * G; i0 += kScanLPR) {
+        const int i = i0 + c;
+        if (i < UR * G) {
+          float val = 0.f;
+#pragma unroll
+          for (int j = 0; j < UR * G; ++j)
+            if (i == j) val = acc[j / G][j % G];
+          const int uu = i / G, hh = i % G;
+          const int64_t p = base + (int64_t)(w * UR + uu) * RPB + rg;
+          if (p < s1) {
+            val *= a.scale;
+            a.scores[(seg0 + hh) * a.n_pad + p] = val;
+            atomicAdd(&lh[hh * kHistBins + (f2key(val) >> (32 - kHistBits))], 1u);
+          }
+        }
+      }
+    };
+    // two register sets: the loads of the next iteration are in flight while
+    // the current one is computed
+    u32x4 ka[UR][NCH], kc[UR][NCH];
+    int64_t base = s0;
+    issue(base, ka);
+    while (true) {
+      const int64_t nb = base + Sh::ROWS_ITER;
+      if (nb < s1) issue(nb, kc);
+      consume(base, ka);
+      if (nb >= s1) break;
+      base = nb;
+      const int64_t nb2 = base + Sh::ROWS_ITER;
+      if (nb2 < s1) issue(nb2, ka);
+      consume(base, kc);
+      if (nb2 >= s1) break;
+      base = nb2;
     }
   }
   __syncthreads();

@@ -1,38 +1,66 @@
-// Exact per-head top-K select over the scan's scores.
+// Exact per-head top-K select over the scan's scores, and the renormalised
+// softmax . V over the chosen rows.
 //
 // The index set is TopK over every score of the segment (ReTopK review,
 // "Exact Top-K 的隐藏成本": S_t = TopK(e, K) over all L_t scores), with ties
 // resolved towards the lowest row (a reading: the pages leave ties open).
+// The output follows Eq. 2 of the RetrievalAttention review ("Approximated
+// Attention Formulation"): softmax over the chosen rows only, written with
+// the local maximum of "CPU-GPU Co-Execution Architecture".
 //
-// Three passes, all exact:
-//  1. k_scan has counted the first radix digit (top 11 key bits). Every
-//     filter workgroup derives the same threshold bin b* (the bin holding the
-//     K-th largest key) and appends the positions whose digit is >= b* to a
-//     per-segment list (unordered; integer atomics only).
-//  2. One select workgroup per segment finishes the radix select on the list
-//     (digits 20..10 and 9..0) to get the exact K-th key T, and, if several
-//     rows share T, the position cut-off among them (radix select on the
-//     position). Chosen = key > T, or key == T and position <= cut-off.
-//  3. Chosen positions are marked in a bitmap of the segment's positions and
-//     read back in ascending order, which gives the ascending row list.
+// Steps, all integer work exact:
+//  1. k_scan has counted the first radix digit (top 11 bits of the
+//     order-preserving key); the bin b* holding the K-th largest key follows.
+//  2. topk_filter (many workgroups) keeps the positions whose digit is >= b*,
+//     in position order.
+//  3. topk_select (one workgroup per head, candidates only): radix digits
+//     20..10 and 9..0 on the candidates of bin b* give the exact K-th key T
+//     and how many rows with key == T to keep (`need`): chosen = key > T, or
+//     key == T among the first `need` such rows in position order. One
+//     ordered compaction writes the chosen rows in ascending order.
+//  4. sparse_sv (many workgroups) computes softmax . V partials over slices
+//     of the chosen rows with fp32 accumulation; `combine` merges them.
 #pragma once
 
+#include "attend_kernels.h"
 #include "device.h"
 
 namespace stdk {
 
+struct Cand {
+  uint32_t key;
+  int32_t pos;
+};
+
+STDK_DEV float key2f(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+constexpr int kSelThreads = 1024;
+constexpr size_t kSelStaticLds = 10 * 1024;  // static LDS of the select kernels, rounded up
+
+// ---------------------------------------------------------------------------
+// topk_filter: many workgroups per segment. Each wave scans its own slice of
+// positions in ascending order and writes the (key, position) pairs whose
+// first digit is >= b* into that slice's own region, plus a count. No
+// atomics: the regions concatenated in slice order are the candidate list
+// sorted by position.
+// ---------------------------------------------------------------------------
 struct FilterArgs {
-  const float* scores;      // [S][n_pad]
-  const uint32_t* hist;     // [S][2048]
-  int32_t* list;            // [S][n_pad] positions, unordered
-  uint32_t* list_cnt;       // [S]
-  int64_t n, n_pad, chunk;  // positions, row pitch, positions per workgroup
+  const float* scores;        // [S][n_pad]
+  const uint32_t* hist;       // [S][2048]
+  Cand* list;                 // [S][n_pad]: slice j owns [j*slice, (j+1)*slice)
+  uint32_t* slice_cnt;        // [S][nslice]
+  int64_t n, n_pad;
   int32_t K;
+  int32_t slice;              // positions per wave slice (multiple of 64)
+  int32_t nslice;             // slices per segment
   int32_t pad_;
   const int32_t* seg_active;  // [S] or null
 };
 
 constexpr int kFilterThreads = 256;
+constexpr int kFilterWaves = kFilterThreads / 64;
 
 __global__ __launch_bounds__(kFilterThreads) void topk_filter(FilterArgs a) {
   __shared__ uint32_t h[kHistBins];
@@ -41,166 +69,342 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter(FilterArgs a) {
   __shared__ uint32_t s_beyond;
   const int64_t seg = blockIdx.y;
   if (a.seg_active && a.seg_active[seg] == 0) return;
-  const int tid = threadIdx.x, lane = tid & 63;
-  for (int i = tid; i < kHistBins; i += kFilterThreads) h[i] = a.hist[seg * kHistBins + i];
-  __syncthreads();
-  find_bin<kFilterThreads, true>(h, kHistBins, (uint32_t)a.K, tmp, &s_bin, &s_beyond);
-  const int bstar = s_bin < 0 ? 0 : s_bin;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const bool take_all = a.n <= a.K;
+  uint32_t bstar = 0;
+  if (!take_all) {
+    {
+      constexpr int HU = kHistBins / kFilterThreads;
+      uint32_t hv[HU];
+#pragma unroll
+      for (int u = 0; u < HU; ++u) hv[u] = a.hist[seg * kHistBins + u * kFilterThreads + tid];
+#pragma unroll
+      for (int u = 0; u < HU; ++u) h[u * kFilterThreads + tid] = hv[u];
+    }
+    __syncthreads();
+    find_bin<kFilterThreads, true>(h, kHistBins, (uint32_t)a.K, tmp, &s_bin, &s_beyond);
+    bstar = (uint32_t)(s_bin < 0 ? 0 : s_bin);
+  }
+  const int js = blockIdx.x * kFilterWaves + w;  // this wave's slice
+  if (js >= a.nslice) return;
   const float* sc = a.scores + seg * a.n_pad;
-  int32_t* lst = a.list + seg * a.n_pad;
-  const int64_t p0 = (int64_t)blockIdx.x * a.chunk;
-  const int64_t p1 = min(a.n, p0 + a.chunk);
-  for (int64_t pb = p0; pb < p1; pb += kFilterThreads) {
-    const int64_t p = pb + tid;
-    bool take = false;
-    if (p < p1) take = (int)(f2key(sc[p]) >> (32 - kHistBits)) >= bstar;
-    const uint64_t m = __ballot(take);
-    if (m) {
-      const int leader = __ffsll((unsigned long long)m) - 1;
-      uint32_t base = 0;
-      if (lane == leader) base = atomicAdd(&a.list_cnt[seg], (uint32_t)__popcll(m));
-      base = __shfl(base, leader, 64);
-      if (take) lst[base + lane_rank(m)] = (int32_t)p;
+  Cand* out = a.list + seg * a.n_pad + (int64_t)js * a.slice;
+  const int64_t p0 = (int64_t)js * a.slice;
+  const int64_t p1 = min(a.n, p0 + a.slice);
+  uint32_t cnt = 0;
+  constexpr int FU = 16;  // loads in flight per lane
+  for (int64_t pb = p0; pb < p1; pb += 64 * FU) {
+    float v[FU];
+#pragma unroll
+    for (int u = 0; u < FU; ++u) {
+      const int64_t p = pb + 64 * u + lane;
+      v[u] = (p < p1) ? sc[p] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < FU; ++u) {
+      const int64_t p = pb + 64 * u + lane;
+      const uint32_t key = f2key(v[u]);
+      const bool take = p < p1 && (take_all || (key >> (32 - kHistBits)) >= bstar);
+      const uint64_t m = __ballot(take);
+      if (take) out[cnt + lane_rank(m)] = Cand{key, (int32_t)p};
+      cnt += (uint32_t)__popcll(m);
     }
   }
+  if (lane == 0) a.slice_cnt[seg * a.nslice + js] = cnt;
 }
 
+// ---------------------------------------------------------------------------
+// topk_select: one workgroup per segment, on the candidates only. Writes the
+// chosen rows (ascending) and their scores, and the index output.
+// ---------------------------------------------------------------------------
 struct SelectArgs {
-  const float* scores;       // [S][n_pad]
-  const uint32_t* hist;      // [S][2048]
-  const int32_t* list;       // [S][n_pad]
-  const uint32_t* list_cnt;  // [S]
+  const uint32_t* hist;       // [S][2048]
+  const Cand* list;           // [S][n_pad]
+  const uint32_t* slice_cnt;  // [S][nslice]
+  Cand* clist;                // [S][n_pad] contiguous copy when it does not fit in LDS
   int64_t n, n_pad;
   int32_t K;
-  int32_t bitmap_words;      // ceil(n / 32)
-  int32_t* sel_row;          // [S][K] chosen rows, ascending, -1 padded
-  float* sel_z;              // [S][K] their scores
-  int32_t* idx_out;          // [S][K] or null (copy of sel_row)
-  uint32_t* gbitmap;         // [S][bitmap_words] when the bitmap does not fit in LDS
-  const int32_t* seg_active; // [S] or null
+  int32_t slice, nslice;
+  int32_t cache_cap;          // candidates that fit in the LDS copy
+  int32_t* sel_row;           // [S][K] chosen rows, ascending, -1 padded
+  float* sel_z;               // [S][K] their scores
+  int32_t* idx_out;           // [S][K] or null (copy of sel_row)
+  const int32_t* seg_active;  // [S] or null
   RangeTab tab;
 };
 
-constexpr int kSelectThreads = 1024;
+constexpr int kSelectWaves = kSelThreads / 64;
 
-template <bool kLdsBitmap>
-__global__ __launch_bounds__(kSelectThreads) void topk_select(SelectArgs a) {
-  extern __shared__ uint32_t dyn[];  // bitmap (kLdsBitmap)
+// Dynamic LDS: pre[nslice + 1] (slice prefix) then, if the candidates fit,
+// their contiguous copy (position order); else the copy goes to clist.
+__global__ __launch_bounds__(kSelThreads) void topk_select(SelectArgs a) {
+  extern __shared__ uint32_t dyn[];
   __shared__ uint32_t h[kHistBins];
-  __shared__ uint32_t tmp[kSelectThreads / 64 + 1];
+  __shared__ uint32_t tmp[kSelThreads / 64 + 1];
   __shared__ int s_bin;
   __shared__ uint32_t s_beyond;
   const int64_t seg = blockIdx.x;
   if (a.seg_active && a.seg_active[seg] == 0) return;
-  const int tid = threadIdx.x;
-  const float* sc = a.scores + seg * a.n_pad;
-  const int32_t* lst = a.list + seg * a.n_pad;
-  const uint32_t m = a.list_cnt[seg];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int ns = a.nslice;
+  const int K = a.K;
+  const bool take_all = a.n <= K;
+  uint32_t* pre = dyn;
+  const Cand* lst = a.list + seg * a.n_pad;
 
-  // digit 0 (bits 31..21): from the scan's histogram
-  for (int i = tid; i < kHistBins; i += kSelectThreads) h[i] = a.hist[seg * kHistBins + i];
-  __syncthreads();
-  find_bin<kSelectThreads, true>(h, kHistBins, (uint32_t)a.K, tmp, &s_bin, &s_beyond);
-  const uint32_t b0 = (uint32_t)(s_bin < 0 ? 0 : s_bin);
-  uint32_t need = (uint32_t)a.K - s_beyond;
-  __syncthreads();
-
-  // digit 1 (bits 20..10) among list entries in bin b0
-  for (int i = tid; i < kHistBins; i += kSelectThreads) h[i] = 0u;
-  __syncthreads();
-  for (uint32_t i = tid; i < m; i += kSelectThreads) {
-    const uint32_t key = f2key(sc[lst[i]]);
-    if ((key >> 21) == b0) atomicAdd(&h[(key >> 10) & 0x7FFu], 1u);
-  }
-  __syncthreads();
-  find_bin<kSelectThreads, true>(h, 2048, need, tmp, &s_bin, &s_beyond);
-  const uint32_t b1 = (uint32_t)(s_bin < 0 ? 0 : s_bin);
-  need -= s_beyond;
-  __syncthreads();
-
-  // digit 2 (bits 9..0)
-  const uint32_t pre01 = (b0 << 11) | b1;
-  for (int i = tid; i < 1024; i += kSelectThreads) h[i] = 0u;
-  __syncthreads();
-  for (uint32_t i = tid; i < m; i += kSelectThreads) {
-    const uint32_t key = f2key(sc[lst[i]]);
-    if ((key >> 10) == pre01) atomicAdd(&h[key & 0x3FFu], 1u);
-  }
-  __syncthreads();
-  find_bin<kSelectThreads, true>(h, 1024, need, tmp, &s_bin, &s_beyond);
-  const uint32_t b2 = (uint32_t)(s_bin < 0 ? 0 : s_bin);
-  const uint32_t T = (pre01 << 10) | b2;
-  const uint32_t ties = h[b2];
-  need -= s_beyond;  // rows with key == T to keep (1..ties)
-  __syncthreads();
-
-  // position cut-off among the ties: the need-th smallest position
-  int32_t cut = 0x7FFFFFFF;
-  if (need < ties) {
-    uint32_t prefix = 0;
-    const int shifts[3] = {20, 9, 0};
-    const int bits[3] = {11, 11, 9};
-    uint32_t rem = need;
-    for (int d = 0; d < 3; ++d) {
-      const int nb = 1 << bits[d];
-      for (int i = tid; i < nb; i += kSelectThreads) h[i] = 0u;
-      __syncthreads();
-      const int hi_shift = shifts[d] + bits[d];
-      for (uint32_t i = tid; i < m; i += kSelectThreads) {
-        const uint32_t p = (uint32_t)lst[i];
-        if (f2key(sc[p]) == T && (d == 0 || (p >> hi_shift) == prefix))
-          atomicAdd(&h[(p >> shifts[d]) & (uint32_t)(nb - 1)], 1u);
-      }
-      __syncthreads();
-      find_bin<kSelectThreads, false>(h, nb, rem, tmp, &s_bin, &s_beyond);
-      prefix = (prefix << bits[d]) | (uint32_t)(s_bin < 0 ? 0 : s_bin);
-      rem -= s_beyond;
-      __syncthreads();
+  // slice prefix (ns <= kSelThreads * 4) and the first-digit histogram
+  {
+    uint32_t c[4];
+    uint32_t loc = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = tid * 4 + i;
+      c[i] = (j < ns) ? a.slice_cnt[seg * ns + j] : 0u;
     }
-    cut = (int32_t)prefix;
+    constexpr int HU = kHistBins / kSelThreads;
+    uint32_t hv[HU];
+#pragma unroll
+    for (int u = 0; u < HU; ++u) hv[u] = a.hist[seg * kHistBins + u * kSelThreads + tid];
+#pragma unroll
+    for (int u = 0; u < HU; ++u) h[u * kSelThreads + tid] = hv[u];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) loc += c[i];
+    uint32_t tot;
+    uint32_t ex = block_excl_scan<kSelThreads>(loc, tmp, &tot);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = tid * 4 + i;
+      if (j < ns) pre[j] = ex;
+      ex += c[i];
+    }
+    if (tid == 0) pre[ns] = tot;
   }
-
-  // mark the chosen positions
-  const int W = a.bitmap_words;
-  uint32_t* bm = kLdsBitmap ? dyn : (a.gbitmap + seg * (int64_t)W);
-  for (int i = tid; i < W; i += kSelectThreads) bm[i] = 0u;
   __syncthreads();
-  for (uint32_t i = tid; i < m; i += kSelectThreads) {
-    const int32_t p = lst[i];
-    const uint32_t key = f2key(sc[p]);
-    if (key > T || (key == T && p <= cut)) atomicOr(&bm[p >> 5], 1u << (p & 31));
-  }
-  __syncthreads();
-
-  // ascending compaction: thread t owns words [t*per, (t+1)*per)
-  const int per = (W + kSelectThreads - 1) / kSelectThreads;
-  const int w0 = tid * per, w1 = min(W, w0 + per);
-  uint32_t cnt = 0;
-  for (int i = w0; i < w1; ++i) cnt += __popc(bm[i]);
-  uint32_t total;
-  uint32_t r = block_excl_scan<kSelectThreads>(cnt, tmp, &total);
-  int32_t* srow = a.sel_row + seg * a.K;
-  float* sz = a.sel_z + seg * a.K;
-  int32_t* io = a.idx_out ? a.idx_out + seg * a.K : nullptr;
-  for (int i = w0; i < w1; ++i) {
-    uint32_t bits = bm[i];
-    while (bits) {
-      const int j = __ffs(bits) - 1;
-      bits &= bits - 1;
-      const int64_t p = (int64_t)i * 32 + j;
-      if (r < (uint32_t)a.K) {
-        const int32_t row = (int32_t)pos_to_row(a.tab, p);
-        srow[r] = row;
-        sz[r] = sc[p];
-        if (io) io[r] = row;
+  const uint32_t m = pre[ns];
+  const bool cached = m <= (uint32_t)a.cache_cap;
+  Cand* cl = cached ? reinterpret_cast<Cand*>(dyn + ((ns + 2) & ~1)) : (a.clist + seg * a.n_pad);
+  // contiguous copy: wave wv copies slices wv, wv + 16, ...; 8 slices per batch
+  {
+    constexpr int SU = 8;
+    for (int j0 = wv; j0 < ns; j0 += kSelectWaves * SU) {
+      for (uint32_t e0 = 0;; e0 += 64) {
+        Cand v[SU];
+        bool any = false;
+#pragma unroll
+        for (int u = 0; u < SU; ++u) {
+          const int j = j0 + u * kSelectWaves;
+          const uint32_t e = e0 + lane;
+          if (j < ns && e < pre[j + 1] - pre[j]) {
+            v[u] = lst[(int64_t)j * a.slice + e];
+            any = true;
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < SU; ++u) {
+          const int j = j0 + u * kSelectWaves;
+          const uint32_t e = e0 + lane;
+          if (j < ns && e < pre[j + 1] - pre[j]) cl[pre[j] + e] = v[u];
+        }
+        if (!__any(any)) break;
       }
-      ++r;
     }
   }
-  for (uint32_t i = total + tid; i < (uint32_t)a.K; i += kSelectThreads) {
+  __syncthreads();
+  auto fetch = [&](uint32_t i) -> Cand { return cl[i]; };
+  constexpr int U = 8;
+
+  uint32_t need = (uint32_t)K, Tk = 0;
+  if (!take_all) {
+    // digit 0 (bits 31..21): from the scan's histogram
+    find_bin<kSelThreads, true>(h, kHistBins, (uint32_t)K, tmp, &s_bin, &s_beyond);
+    const uint32_t b0 = (uint32_t)(s_bin < 0 ? 0 : s_bin);
+    need = (uint32_t)K - s_beyond;
+    __syncthreads();
+    // digit 1 (bits 20..10) among candidates in bin b0
+    for (int i = tid; i < kHistBins; i += kSelThreads) h[i] = 0u;
+    __syncthreads();
+    for (uint32_t base = 0; base < m; base += kSelThreads * U) {
+      uint32_t kv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t i = base + u * kSelThreads + tid;
+        kv[u] = (i < m) ? fetch(i).key : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t i = base + u * kSelThreads + tid;
+        if (i < m && (kv[u] >> 21) == b0) atomicAdd(&h[(kv[u] >> 10) & 0x7FFu], 1u);
+      }
+    }
+    __syncthreads();
+    find_bin<kSelThreads, true>(h, 2048, need, tmp, &s_bin, &s_beyond);
+    const uint32_t b1 = (uint32_t)(s_bin < 0 ? 0 : s_bin);
+    need -= s_beyond;
+    __syncthreads();
+    // digit 2 (bits 9..0)
+    const uint32_t pre01 = (b0 << 11) | b1;
+    for (int i = tid; i < 1024; i += kSelThreads) h[i] = 0u;
+    __syncthreads();
+    for (uint32_t base = 0; base < m; base += kSelThreads * U) {
+      uint32_t kv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t i = base + u * kSelThreads + tid;
+        kv[u] = (i < m) ? fetch(i).key : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t i = base + u * kSelThreads + tid;
+        if (i < m && (kv[u] >> 10) == pre01) atomicAdd(&h[kv[u] & 0x3FFu], 1u);
+      }
+    }
+    __syncthreads();
+    find_bin<kSelThreads, true>(h, 1024, need, tmp, &s_bin, &s_beyond);
+    Tk = (pre01 << 10) | (uint32_t)(s_bin < 0 ? 0 : s_bin);
+    need -= s_beyond;  // rows with key == Tk to keep, the first ones in position order
+    __syncthreads();
+  }
+
+  // ordered compaction: thread t owns candidates [t*per, (t+1)*per)
+  const uint32_t per = (m + kSelThreads - 1) / kSelThreads;
+  const uint32_t i0 = min(m, tid * per), i1 = min(m, i0 + per);
+  uint32_t n_gt = 0, n_eq = 0;
+  for (uint32_t ib = i0; ib < i1; ib += U) {
+    uint32_t kv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) kv[u] = (ib + u < i1) ? fetch(ib + u).key : 0u;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (ib + u < i1) {
+        n_gt += take_all || kv[u] > Tk;
+        n_eq += !take_all && kv[u] == Tk;
+      }
+    }
+  }
+  uint32_t tot_eq, tot_all;
+  const uint32_t eq_before = block_excl_scan<kSelThreads>(n_eq, tmp, &tot_eq);
+  const uint32_t take_eq = min(n_eq, need > eq_before ? need - eq_before : 0u);
+  uint32_t r = block_excl_scan<kSelThreads>(n_gt + take_eq, tmp, &tot_all);
+  int32_t* srow = a.sel_row + seg * K;
+  float* sz = a.sel_z + seg * K;
+  int32_t* io = a.idx_out ? a.idx_out + seg * K : nullptr;
+  uint32_t eq_seen = eq_before;
+  for (uint32_t ib = i0; ib < i1; ib += U) {
+    Cand cv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (ib + u < i1) cv[u] = fetch(ib + u);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (ib + u >= i1) break;
+      bool take = take_all || cv[u].key > Tk;
+      if (!take_all && cv[u].key == Tk) {
+        take = eq_seen < need;
+        ++eq_seen;
+      }
+      if (take) {
+        if (r < (uint32_t)K) {
+          const int32_t row = (int32_t)pos_to_row(a.tab, cv[u].pos);
+          srow[r] = row;
+          sz[r] = key2f(cv[u].key);
+          if (io) io[r] = row;
+        }
+        ++r;
+      }
+    }
+  }
+  for (uint32_t i = tot_all + tid; i < (uint32_t)K; i += kSelThreads) {
     srow[i] = -1;
     sz[i] = -INFINITY;
     if (io) io[i] = -1;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// sparse_sv: gathered-row softmax . V, kSvRows chosen rows per workgroup;
+// partial (m, s, o) per workgroup, merged by `combine`.
+// ---------------------------------------------------------------------------
+struct SvArgs {
+  const char* v;              // value cache base
+  int64_t stride_b_bytes, stride_h_bytes;
+  const int32_t* sel_row;     // [S][K], -1 = unused slot
+  const float* sel_z;         // [S][K]
+  float* part;                // [S][nsplit][kPartStride]
+  const int32_t* seg_active;  // [S] or null
+  int32_t K, nsplit, Hq, G;
+};
+
+constexpr int kSvThreads = 256;
+constexpr int kSvRows = 64;
+
+template <typename T>
+__global__ __launch_bounds__(kSvThreads) void sparse_sv(SvArgs a) {
+  constexpr int EPL = KvTraits<T>::EPL, LPR = KvTraits<T>::LPR, ROWB = KvTraits<T>::ROWB;
+  constexpr int NG = kSvThreads / LPR;  // row groups
+  constexpr int RU = kSvRows / NG;      // rows per row group
+  __shared__ int32_t rows[kSvRows];
+  __shared__ float wts[kSvRows];
+  __shared__ float red[NG][kHeadDim];
+  __shared__ float s_m;
+  const int64_t seg = blockIdx.y;
+  if (a.seg_active && a.seg_active[seg] == 0) return;
+  const int split = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int gid = tid / LPR, c = tid % LPR;
+  const int b = (int)(seg / a.Hq), hq = (int)(seg % a.Hq), hkv = hq / a.G;
+  const int j0 = split * kSvRows;
+  const int nr = min(kSvRows, a.K - j0);
+  float z = -INFINITY;
+  if (tid < kSvRows) {
+    int32_t r = -1;
+    if (tid < nr) {
+      r = a.sel_row[seg * a.K + j0 + tid];
+      if (r >= 0) z = a.sel_z[seg * a.K + j0 + tid];
+    }
+    rows[tid] = r;
+  }
+  if (w == 0) {
+    const float mx = wave_max(z);
+    if (lane == 0) s_m = mx;
+  }
+  __syncthreads();
+  const float m = s_m;
+  if (tid < kSvRows) wts[tid] = (m == -INFINITY || z == -INFINITY) ? 0.f : __expf(z - m);
+  __syncthreads();
+  const char* vb = a.v + (int64_t)b * a.stride_b_bytes + (int64_t)hkv * a.stride_h_bytes;
+  u32x4 vw[RU];
+#pragma unroll
+  for (int u = 0; u < RU; ++u) {
+    const int32_t r = rows[gid + NG * u];
+    vw[u] = (r >= 0) ? load16(vb + (int64_t)r * ROWB + c * 16) : u32x4{0u, 0u, 0u, 0u};
+  }
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int u = 0; u < RU; ++u) {
+    const float wt = wts[gid + NG * u];
+    float x[EPL];
+    unpack16<T>(vw[u], x);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = fmaf(wt, x[e], acc[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) red[gid][c * EPL + e] = acc[e];
+  __syncthreads();
+  float* part = a.part + (seg * a.nsplit + split) * kPartStride;
+  if (tid < kHeadDim) {
+    float o = 0.f;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) o += red[g][tid];
+    part[4 + tid] = o;
+  }
+  if (w == 0) {
+    const float s = wave_sum(tid < kSvRows ? wts[tid] : 0.f);
+    if (lane == 0) {
+      part[0] = m;
+      part[1] = s;
+    }
   }
 }
 

@@ -69,7 +69,7 @@ def _sig(lib):
     lib.stdk_last_error.restype = c_char_p
     lib.stdk_version.argtypes = []
     lib.stdk_version.restype = c_int32
-    lib.stdk_profile_enable.argtypes = [c_int32]
+    lib.stdk_profile_enable.argtypes = [c_int32, c_char_p]
     lib.stdk_profile_enable.restype = c_int32
     lib.stdk_profile_disable.argtypes = []
     lib.stdk_profile_disable.restype = c_int32

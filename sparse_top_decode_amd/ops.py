@@ -175,8 +175,8 @@ class KernelTimer:
     """Per-kernel durations from HIP events the library records around each
     of its launches (on the launch stream)."""
 
-    def __init__(self, capacity: int = 1 << 16):
-        check(load().stdk_profile_enable(capacity))
+    def __init__(self, capacity: int = 1 << 16, only: Optional[str] = None):
+        check(load().stdk_profile_enable(capacity, None if only is None else only.encode()))
         check(load().stdk_profile_reset())
 
     def read(self, name: str) -> Tuple[float, int]:
