@@ -197,15 +197,17 @@ const char* stdk_last_error(void); /* host string, valid until the next call on 
 int32_t stdk_version(void);        /* STDK_VERSION */
 
 /* Kernel timing: while enabled, every kernel the library enqueues (or only
- * the kernel family `only`, if not NULL) is bracketed by two hipEvents
- * recorded on the same stream. `capacity` bounds the number of launches
- * recorded (events are created when enabling, not on the hot path).
- * stdk_profile_read waits for the recorded events and returns, for the
- * kernel family `name`, the summed duration in milliseconds and the launch
- * count. Families: "ws_clear", "k_scan", "topk_filter", "topk_select",
- * "sparse_sv", "dense_attn", "combine", "attn_merge", "fill_empty",
- * "retopk_select", "retopk_rerank", "retopk_rerank_select", "retopk_push",
- * "retopk_init". Unknown names return STDK_EINVAL. */
+ * the kernel family `only`, if not NULL) is launched with a pair of
+ * hipEvents attached to its dispatch (hipExtLaunchKernelGGL start/stop
+ * events, on the launch stream), so the pair times the kernel itself.
+ * `capacity` bounds the number of launches recorded (events are created when
+ * enabling, not on the hot path). stdk_profile_read waits for the recorded
+ * events and returns, for the kernel family `name`, the summed duration in
+ * milliseconds and the launch count. Families: "ws_clear", "k_scan",
+ * "topk_filter", "topk_select", "sparse_sv", "dense_attn", "combine",
+ * "attn_merge", "fill_empty", "retopk_select", "retopk_rerank",
+ * "retopk_rerank_select", "retopk_push", "retopk_init". Unknown names return
+ * STDK_EINVAL. */
 int32_t stdk_profile_enable(int32_t capacity, const char* only);
 int32_t stdk_profile_disable(void);
 int32_t stdk_profile_reset(void);

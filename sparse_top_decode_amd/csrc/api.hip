@@ -1,6 +1,7 @@
 // Host side of libstdk: argument validation, workspace layout, kernel
 // launches and launch timing. The C entry points are declared in
 // include/stdk.h, which documents each operation and its source.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -73,32 +74,35 @@ struct Profiler {
 };
 Profiler g_prof;
 
-// Returns the slot whose first event was recorded, or -1.
-long prof_begin(int kid, hipStream_t s) {
+// Events for the next launch of kernel family `kid` (null if not recorded).
+// They are handed to the dispatch itself, so they time the kernel, not the
+// queue around it.
+long prof_slot(int kid, hipEvent_t* e0, hipEvent_t* e1) {
+  *e0 = *e1 = nullptr;
   std::lock_guard<std::mutex> lk(g_prof.mu);
   if (!g_prof.on || g_prof.used >= g_prof.kid.size()) return -1;
   if (g_prof.only >= 0 && g_prof.only != kid) return -1;
   const size_t slot = g_prof.used++;
   g_prof.kid[slot] = kid;
-  (void)hipEventRecord(g_prof.ev[2 * slot], s);
+  *e0 = g_prof.ev[2 * slot];
+  *e1 = g_prof.ev[2 * slot + 1];
   return (long)slot;
 }
 
-void prof_end(long slot, hipStream_t s) {
-  if (slot < 0) return;
-  std::lock_guard<std::mutex> lk(g_prof.mu);
-  (void)hipEventRecord(g_prof.ev[2 * slot + 1], s);
-}
-
+// f(e0, e1) enqueues one kernel with hipExtLaunchKernelGGL(..., e0, e1, 0, ...).
 template <typename F>
 int32_t launch(int kid, hipStream_t s, F&& f) {
-  const long slot = prof_begin(kid, s);
-  f();
+  (void)s;
+  hipEvent_t e0, e1;
+  prof_slot(kid, &e0, &e1);
+  f(e0, e1);
   const hipError_t e = hipGetLastError();
-  prof_end(slot, s);
   if (e != hipSuccess) return fail(STDK_EHIP, "%s launch failed: %s", kKernelNames[kid], hipGetErrorString(e));
   return STDK_OK;
 }
+
+#define STDK_LAUNCH(kernel, grid, block, shmem, stream, ...) \
+  hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, e0, e1, 0, __VA_ARGS__)
 
 // ---------------------------------------------------------------------------
 // limits
@@ -296,37 +300,37 @@ int scan_rows_iter(int G) {
 }
 
 template <typename T>
-void launch_scan_t(int G, dim3 grid, hipStream_t s, const ScanArgs& a) {
+void launch_scan_t(int G, dim3 grid, hipStream_t s, const ScanArgs& a, hipEvent_t e0, hipEvent_t e1) {
   switch (G) {
-    case 1: hipLaunchKernelGGL((k_scan<T, 1>), grid, dim3(kScanThreads), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_scan<T, 2>), grid, dim3(kScanThreads), 0, s, a); break;
-    case 3: hipLaunchKernelGGL((k_scan<T, 3>), grid, dim3(kScanThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((k_scan<T, 4>), grid, dim3(kScanThreads), 0, s, a); break;
-    case 5: hipLaunchKernelGGL((k_scan<T, 5>), grid, dim3(kScanThreads), 0, s, a); break;
-    case 6: hipLaunchKernelGGL((k_scan<T, 6>), grid, dim3(kScanThreads), 0, s, a); break;
-    case 7: hipLaunchKernelGGL((k_scan<T, 7>), grid, dim3(kScanThreads), 0, s, a); break;
-    default: hipLaunchKernelGGL((k_scan<T, 8>), grid, dim3(kScanThreads), 0, s, a); break;
+    case 1: STDK_LAUNCH((k_scan<T, 1>), grid, dim3(kScanThreads), 0, s, a); break;
+    case 2: STDK_LAUNCH((k_scan<T, 2>), grid, dim3(kScanThreads), 0, s, a); break;
+    case 3: STDK_LAUNCH((k_scan<T, 3>), grid, dim3(kScanThreads), 0, s, a); break;
+    case 4: STDK_LAUNCH((k_scan<T, 4>), grid, dim3(kScanThreads), 0, s, a); break;
+    case 5: STDK_LAUNCH((k_scan<T, 5>), grid, dim3(kScanThreads), 0, s, a); break;
+    case 6: STDK_LAUNCH((k_scan<T, 6>), grid, dim3(kScanThreads), 0, s, a); break;
+    case 7: STDK_LAUNCH((k_scan<T, 7>), grid, dim3(kScanThreads), 0, s, a); break;
+    default: STDK_LAUNCH((k_scan<T, 8>), grid, dim3(kScanThreads), 0, s, a); break;
   }
 }
 
 template <typename T>
-void launch_dense_t(int G, dim3 grid, hipStream_t s, const DenseArgs& a) {
+void launch_dense_t(int G, dim3 grid, hipStream_t s, const DenseArgs& a, hipEvent_t e0, hipEvent_t e1) {
   switch (G) {
-    case 1: hipLaunchKernelGGL((dense_attn<T, 1>), grid, dim3(kDenseThreads), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((dense_attn<T, 2>), grid, dim3(kDenseThreads), 0, s, a); break;
-    case 3: hipLaunchKernelGGL((dense_attn<T, 3>), grid, dim3(kDenseThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((dense_attn<T, 4>), grid, dim3(kDenseThreads), 0, s, a); break;
-    case 5: hipLaunchKernelGGL((dense_attn<T, 5>), grid, dim3(kDenseThreads), 0, s, a); break;
-    case 6: hipLaunchKernelGGL((dense_attn<T, 6>), grid, dim3(kDenseThreads), 0, s, a); break;
-    case 7: hipLaunchKernelGGL((dense_attn<T, 7>), grid, dim3(kDenseThreads), 0, s, a); break;
-    default: hipLaunchKernelGGL((dense_attn<T, 8>), grid, dim3(kDenseThreads), 0, s, a); break;
+    case 1: STDK_LAUNCH((dense_attn<T, 1>), grid, dim3(kDenseThreads), 0, s, a); break;
+    case 2: STDK_LAUNCH((dense_attn<T, 2>), grid, dim3(kDenseThreads), 0, s, a); break;
+    case 3: STDK_LAUNCH((dense_attn<T, 3>), grid, dim3(kDenseThreads), 0, s, a); break;
+    case 4: STDK_LAUNCH((dense_attn<T, 4>), grid, dim3(kDenseThreads), 0, s, a); break;
+    case 5: STDK_LAUNCH((dense_attn<T, 5>), grid, dim3(kDenseThreads), 0, s, a); break;
+    case 6: STDK_LAUNCH((dense_attn<T, 6>), grid, dim3(kDenseThreads), 0, s, a); break;
+    case 7: STDK_LAUNCH((dense_attn<T, 7>), grid, dim3(kDenseThreads), 0, s, a); break;
+    default: STDK_LAUNCH((dense_attn<T, 8>), grid, dim3(kDenseThreads), 0, s, a); break;
   }
 }
 
 int32_t run_clear(hipStream_t s, uint32_t* p, int64_t words) {
   if (words <= 0) return STDK_OK;
   const int64_t blocks = std::min<int64_t>(cdiv(words, 256), 1024);
-  return launch(KID_CLEAR, s, [&] { hipLaunchKernelGGL(ws_clear, dim3((unsigned)blocks), dim3(256), 0, s, p, words); });
+  return launch(KID_CLEAR, s, [&](hipEvent_t e0, hipEvent_t e1) { STDK_LAUNCH(ws_clear, dim3((unsigned)blocks), dim3(256), 0, s, p, words); });
 }
 
 // The exact select over n positions (any n >= 1; n <= K takes every row):
@@ -364,9 +368,9 @@ int32_t run_exact_select(const Geo& g, const TopkWs& w, char* ws, const float* q
     a.rows_per_block = rpb;
     a.blocks_per_group = (int32_t)cdiv(w.n, rpb);
     const dim3 grid((unsigned)(g.groups * a.blocks_per_group));
-    STDK_TRY(launch(KID_SCAN, s, [&] {
-      if (g.bf16) launch_scan_t<uint16_t>(g.G, grid, s, a);
-      else launch_scan_t<float>(g.G, grid, s, a);
+    STDK_TRY(launch(KID_SCAN, s, [&](hipEvent_t e0, hipEvent_t e1) {
+      if (g.bf16) launch_scan_t<uint16_t>(g.G, grid, s, a, e0, e1);
+      else launch_scan_t<float>(g.G, grid, s, a, e0, e1);
     }));
   }
   {
@@ -382,7 +386,7 @@ int32_t run_exact_select(const Geo& g, const TopkWs& w, char* ws, const float* q
     a.nslice = (int32_t)w.nslice;
     a.seg_active = active;
     const dim3 grid((unsigned)cdiv(w.nslice, kFilterWaves), (unsigned)w.S);
-    STDK_TRY(launch(KID_FILTER, s, [&] { hipLaunchKernelGGL(topk_filter, grid, dim3(kFilterThreads), 0, s, a); }));
+    STDK_TRY(launch(KID_FILTER, s, [&](hipEvent_t e0, hipEvent_t e1) { STDK_LAUNCH(topk_filter, grid, dim3(kFilterThreads), 0, s, a); }));
   }
   {
     SelectArgs a{};
@@ -404,8 +408,8 @@ int32_t run_exact_select(const Geo& g, const TopkWs& w, char* ws, const float* q
     const size_t avail = (size_t)di->max_lds - kSelStaticLds;
     const size_t dyn = std::min(avail, pre_bytes + (size_t)w.n * sizeof(Cand));
     a.cache_cap = (int32_t)((dyn - pre_bytes) / sizeof(Cand));
-    STDK_TRY(launch(KID_SELECT, s, [&] {
-      hipLaunchKernelGGL(topk_select, dim3((unsigned)w.S), dim3(kSelThreads), dyn, s, a);
+    STDK_TRY(launch(KID_SELECT, s, [&](hipEvent_t e0, hipEvent_t e1) {
+      STDK_LAUNCH(topk_select, dim3((unsigned)w.S), dim3(kSelThreads), dyn, s, a);
     }));
   }
   return STDK_OK;
@@ -429,16 +433,16 @@ int32_t run_sv(const Geo& g, const TopkWs& w, char* ws, const void* v_cache, flo
   a.Hq = g.Hq;
   a.G = g.G;
   const dim3 grid((unsigned)w.nsplit, (unsigned)w.S);
-  STDK_TRY(launch(KID_SV, s, [&] {
-    if (g.bf16) hipLaunchKernelGGL(sparse_sv<uint16_t>, grid, dim3(kSvThreads), 0, s, a);
-    else hipLaunchKernelGGL(sparse_sv<float>, grid, dim3(kSvThreads), 0, s, a);
+  STDK_TRY(launch(KID_SV, s, [&](hipEvent_t e0, hipEvent_t e1) {
+    if (g.bf16) STDK_LAUNCH(sparse_sv<uint16_t>, grid, dim3(kSvThreads), 0, s, a);
+    else STDK_LAUNCH(sparse_sv<float>, grid, dim3(kSvThreads), 0, s, a);
   }));
   return run_combine(w, ws, (int32_t)w.nsplit, o_out, lse_out, s);
 }
 
 int32_t run_combine(const TopkWs& w, char* ws, int32_t np, float* o_out, float* lse_out, hipStream_t s) {
   CombineArgs a{(const float*)(ws + w.part), o_out, lse_out, np, 0};
-  return launch(KID_COMBINE, s, [&] { hipLaunchKernelGGL(combine, dim3((unsigned)w.S), dim3(kHeadDim), 0, s, a); });
+  return launch(KID_COMBINE, s, [&](hipEvent_t e0, hipEvent_t e1) { STDK_LAUNCH(combine, dim3((unsigned)w.S), dim3(kHeadDim), 0, s, a); });
 }
 
 // Dense attention over all n rows (K >= n): one read of every K and V row
@@ -464,9 +468,9 @@ int32_t run_dense(const Geo& g, const TopkWs& w, char* ws, const float* q, const
   a.rows_per_wg = rup(cdiv(w.n, nwg), kDenseTile);
   a.nwg = (int32_t)cdiv(w.n, a.rows_per_wg);
   const dim3 grid((unsigned)a.nwg, (unsigned)g.groups);
-  STDK_TRY(launch(KID_DENSE, s, [&] {
-    if (g.bf16) launch_dense_t<uint16_t>(g.G, grid, s, a);
-    else launch_dense_t<float>(g.G, grid, s, a);
+  STDK_TRY(launch(KID_DENSE, s, [&](hipEvent_t e0, hipEvent_t e1) {
+    if (g.bf16) launch_dense_t<uint16_t>(g.G, grid, s, a, e0, e1);
+    else launch_dense_t<float>(g.G, grid, s, a, e0, e1);
   }));
   return run_combine(w, ws, a.nwg, o_out, lse_out, s);
 }
@@ -527,8 +531,8 @@ int32_t topk_attn_decode(const stdk_layout* lay, const float* q, const void* k_c
 
   if (n == 0) {
     const int64_t m = std::max<int64_t>(g.S * kHeadDim, g.S * (int64_t)top_k);
-    STDK_TRY(launch(KID_FILL, s, [&] {
-      hipLaunchKernelGGL(fill_empty, dim3((unsigned)cdiv(m, 256)), dim3(256), 0, s, o_out, lse_out, idx_out, g.S,
+    STDK_TRY(launch(KID_FILL, s, [&](hipEvent_t e0, hipEvent_t e1) {
+      STDK_LAUNCH(fill_empty, dim3((unsigned)cdiv(m, 256)), dim3(256), 0, s, o_out, lse_out, idx_out, g.S,
                          top_k);
     }));
     return ok();
@@ -555,8 +559,8 @@ int32_t attn_merge_lse(int64_t rows, int32_t d, const float* o_a, const float* l
   STDK_TRY(check_ptr(lse_out, "lse_out", 4));
   hipStream_t s = (hipStream_t)stream;
   MergeArgs a{o_a, lse_a, o_b, lse_b, o_out, lse_out, rows, d, 0};
-  STDK_TRY(launch(KID_MERGE, s, [&] {
-    hipLaunchKernelGGL(attn_merge, dim3((unsigned)cdiv(rows, 2)), dim3(kMergeThreads), 0, s, a);
+  STDK_TRY(launch(KID_MERGE, s, [&](hipEvent_t e0, hipEvent_t e1) {
+    STDK_LAUNCH(attn_merge, dim3((unsigned)cdiv(rows, 2)), dim3(kMergeThreads), 0, s, a);
   }));
   return ok();
 }
@@ -635,7 +639,7 @@ int32_t retopk_state_init(const stdk_layout* lay, const retopk_params* p, const 
   const Geo g = geo_of(lay);
   hipStream_t s = (hipStream_t)stream;
   RtInitArgs a{q_hist, sup_hist, st->q_hat, st->support, st->head, st->count, p->cache_cap, p->top_k, n_hist, 0};
-  STDK_TRY(launch(KID_RT_INIT, s, [&] { hipLaunchKernelGGL(retopk_init, dim3((unsigned)g.S), dim3(256), 0, s, a); }));
+  STDK_TRY(launch(KID_RT_INIT, s, [&](hipEvent_t e0, hipEvent_t e1) { STDK_LAUNCH(retopk_init, dim3((unsigned)g.S), dim3(256), 0, s, a); }));
   return ok();
 }
 
@@ -693,9 +697,9 @@ int32_t retopk_step(const stdk_layout* lay, const retopk_params* p, const retopk
     a.gbitmap = (uint32_t*)(ws + w.gbitmap);
     const size_t bm_bytes = (size_t)w.words * 4;
     const bool lds = bm_bytes + 12 * 1024 <= (size_t)di->max_lds;
-    STDK_TRY(launch(KID_RT_SELECT, s, [&] {
-      if (lds) hipLaunchKernelGGL(retopk_select<true>, dim3((unsigned)g.S), dim3(kRtSelThreads), bm_bytes, s, a);
-      else hipLaunchKernelGGL(retopk_select<false>, dim3((unsigned)g.S), dim3(kRtSelThreads), 0, s, a);
+    STDK_TRY(launch(KID_RT_SELECT, s, [&](hipEvent_t e0, hipEvent_t e1) {
+      if (lds) STDK_LAUNCH(retopk_select<true>, dim3((unsigned)g.S), dim3(kRtSelThreads), bm_bytes, s, a);
+      else STDK_LAUNCH(retopk_select<false>, dim3((unsigned)g.S), dim3(kRtSelThreads), 0, s, a);
     }));
   }
   // exact heads: scan + select + softmax.V over [0, L_t)
@@ -725,12 +729,12 @@ int32_t retopk_step(const stdk_layout* lay, const retopk_params* p, const retopk
     a.nsplit = (int32_t)cdiv(w.cand_cap, kRerankRows);
     a.scale = p->scale;
     const dim3 grid((unsigned)a.nsplit, (unsigned)g.S);
-    STDK_TRY(launch(KID_RT_RERANK, s, [&] {
-      if (g.bf16) hipLaunchKernelGGL(retopk_rerank<uint16_t>, grid, dim3(kRerankThreads), 0, s, a);
-      else hipLaunchKernelGGL(retopk_rerank<float>, grid, dim3(kRerankThreads), 0, s, a);
+    STDK_TRY(launch(KID_RT_RERANK, s, [&](hipEvent_t e0, hipEvent_t e1) {
+      if (g.bf16) STDK_LAUNCH(retopk_rerank<uint16_t>, grid, dim3(kRerankThreads), 0, s, a);
+      else STDK_LAUNCH(retopk_rerank<float>, grid, dim3(kRerankThreads), 0, s, a);
     }));
-    STDK_TRY(launch(KID_RT_RSEL, s, [&] {
-      hipLaunchKernelGGL(retopk_rerank_select, dim3((unsigned)g.S), dim3(kRerankSelThreads), 0, s, a);
+    STDK_TRY(launch(KID_RT_RSEL, s, [&](hipEvent_t e0, hipEvent_t e1) {
+      STDK_LAUNCH(retopk_rerank_select, dim3((unsigned)g.S), dim3(kRerankSelThreads), 0, s, a);
     }));
   }
   // a8: softmax . V over the chosen rows of every head (either path)
@@ -739,7 +743,7 @@ int32_t retopk_step(const stdk_layout* lay, const retopk_params* p, const retopk
   {
     RtPushArgs a{(const float*)(ws + w.qbar), support_out, st->q_hat, st->support, st->head, st->count,
                  p->cache_cap, p->top_k};
-    STDK_TRY(launch(KID_RT_PUSH, s, [&] { hipLaunchKernelGGL(retopk_push, dim3((unsigned)g.S), dim3(256), 0, s, a); }));
+    STDK_TRY(launch(KID_RT_PUSH, s, [&](hipEvent_t e0, hipEvent_t e1) { STDK_LAUNCH(retopk_push, dim3((unsigned)g.S), dim3(256), 0, s, a); }));
   }
   return ok();
 }
