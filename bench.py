@@ -5,7 +5,8 @@ One step is the whole decode-attention hot path of one Llama-3-8B-shaped
 layer (32 query heads, 8 KV heads, d=128, 131,072 cached rows, bf16 K/V):
   1. top-K attention (K=2048) of every query head over the dynamic rows
      [128, 130560): exact QK scan, per-head top-K select, softmax.V;
-  2. dense attention over the 640 static rows (first 128, last 512);
+  2. dense attention over the 640 static rows (first 128, last 512), on a
+     second stream beside step 1 (--streams 1 runs it after step 1);
   3. log-sum-exp merge of the two partial outputs.
 Inputs are synthetic and resident in HBM before timing starts.
 
@@ -99,6 +100,8 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--L", type=int, default=131072)
+    ap.add_argument("--streams", type=int, choices=[1, 2], default=2,
+                    help="2: the static-set call runs on a second stream beside the dynamic-set call")
     ap.add_argument("--kernel-events", choices=["on", "off"], default="on",
                     help="record per-kernel HIP events during the timed region (needed for the roofline)")
     args = ap.parse_args()
@@ -125,8 +128,8 @@ def main():
     K = w.top_k
     n_dyn = sum(e - b for b, e in w.ranges)
     n_stat = sum(e - b for b, e in w.static_ranges)
-    ws_d = torch.empty(ops.topk_attn_decode_workspace_size(lay, n_dyn, K), dtype=torch.uint8, device=dev)
-    ws_s = torch.empty(ops.topk_attn_decode_workspace_size(lay, n_stat, K), dtype=torch.uint8, device=dev)
+    ws_d = ops.new_workspace(ops.topk_attn_decode_workspace_size(lay, n_dyn, K), dev)
+    ws_s = ops.new_workspace(ops.topk_attn_decode_workspace_size(lay, n_stat, K), dev)
     idx = torch.empty((1, w.H_q, K), dtype=torch.int32, device=dev)
     o_d = torch.empty((1, w.H_q, 128), dtype=torch.float32, device=dev)
     l_d = torch.empty((1, w.H_q), dtype=torch.float32, device=dev)
@@ -135,11 +138,31 @@ def main():
     o_m = torch.empty_like(o_d)
     l_m = torch.empty_like(l_d)
 
-    def step():
-        ops.topk_attn_decode(q, k, v, w.ranges, K, w.scale, idx_out=idx, o_out=o_d, lse_out=l_d,
-                             workspace=ws_d, layout=lay)
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream() if args.streams == 2 else None  # default priority
+    ev_go = torch.cuda.Event()
+    ev_static = torch.cuda.Event()
+
+    def static_part():
         ops.topk_attn_decode(q, k, v, w.static_ranges, K, w.scale, o_out=o_s, lse_out=l_s, workspace=ws_s,
                              want_idx=False, layout=lay)
+
+    def step():
+        # The static-set and dynamic-set partial outputs are independent until
+        # the merge (as in the pages' co-execution); with two streams the
+        # static part runs beside the dynamic scan.
+        if side is not None:
+            ev_go.record(main)
+            side.wait_event(ev_go)
+            with torch.cuda.stream(side):
+                static_part()
+            ev_static.record(side)
+        ops.topk_attn_decode(q, k, v, w.ranges, K, w.scale, idx_out=idx, o_out=o_d, lse_out=l_d,
+                             workspace=ws_d, layout=lay)
+        if side is not None:
+            main.wait_event(ev_static)
+        else:
+            static_part()
         ops.attn_merge_lse(o_s, l_s, o_d, l_d, o_out=o_m, lse_out=l_m)
 
     for _ in range(args.warmup):
@@ -168,7 +191,7 @@ def main():
     # per-kernel breakdown, from a separate short run with events around
     # every launch (not part of the timed region)
     kern = {}
-    names = ("ws_clear", "k_scan", "topk_filter", "topk_select", "sparse_sv", "dense_attn", "combine", "attn_merge")
+    names = ("k_scan", "topk_filter", "topk_select", "sparse_sv", "dense_attn", "combine", "attn_merge")
     t_all = ops.KernelTimer(capacity=16 * 24)
     for _ in range(20):
         step()
@@ -199,6 +222,7 @@ def main():
             "workload": f"Llama-3-8B-shaped decode attention layer: 32 q / 8 KV heads, d=128, L={w.L}, bf16 K/V, "
                         f"top-K={K} over the {n_dyn} dynamic rows + dense over the {n_stat} static rows + LSE merge",
             "batch": 1, "seq_len": w.L, "top_k": K, "kv_cache": "bf16", "parallelism": "none (1 GPU)",
+            "streams": args.streams,
         },
         "roofline": {
             "bound": "hbm",

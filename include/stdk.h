@@ -17,6 +17,14 @@
  *  - Determinism: identical inputs give bit-identical outputs.
  *  - Concurrency: calls are reentrant; two calls that are in flight at the
  *    same time must not share a workspace buffer.
+ *  - Workspace state: the first B * n_q_heads * 8192 bytes of a workspace
+ *    hold radix-histogram counters that each call adds to and then clears
+ *    again. They must be zero before the first call that uses the buffer
+ *    (fill the new buffer with zeros once, e.g. hipMemset). Every call that
+ *    returns STDK_OK leaves them zero, so the buffer can be reused by later
+ *    calls with the same stdk_layout (topk_attn_decode and retopk_step
+ *    alike) without clearing. After a call that returned STDK_EHIP, or
+ *    before reuse with a different layout, zero the buffer again.
  *  - KV cache layout (stdk_layout): element (b, h_kv, row, j) lives at
  *        base + b*stride_b + h_kv*stride_h + row*head_dim + j
  *    (rows are contiguous, head_dim elements each). Keys and values share
@@ -94,7 +102,8 @@ typedef struct stdk_layout {
  *  o_out    [B][H_q][128] fp32;  lse_out [B][H_q] fp32 (natural log).
  *  workspace / workspace_bytes: device scratch of at least
  *           topk_attn_decode_workspace_size(lay, n, top_k) bytes, 256-byte
- *           aligned. Its contents on entry do not matter.
+ *           aligned, in the state described under "Workspace state" above
+ *           (zero-filled before its first use).
  * ---------------------------------------------------------------------- */
 int32_t topk_attn_decode(const stdk_layout* lay, const float* q, const void* k_cache,
                          const void* v_cache, const int64_t* ranges, int32_t n_ranges,
@@ -180,7 +189,8 @@ int32_t retopk_state_init(const stdk_layout* lay, const retopk_params* p, const 
  *               the exact path; may be NULL.
  *  cand_out     [B][H_q][R*K + W] int32: the ascending candidate rows of the
  *               reuse path (-1 padded; all -1 on the exact path); may be NULL.
- *  workspace    at least retopk_workspace_size(lay, p, L_t) bytes.
+ *  workspace    at least retopk_workspace_size(lay, p, L_t) bytes,
+ *               zero-filled before its first use ("Workspace state" above).
  * Limits: L_t <= 1,048,576 (the candidate bitmap lives in LDS). */
 int32_t retopk_step(const stdk_layout* lay, const retopk_params* p, const retopk_state* st,
                     const float* q, const void* k_cache, const void* v_cache, int64_t L_t,

@@ -54,11 +54,11 @@ int32_t ok() {
 // launch timing
 // ---------------------------------------------------------------------------
 enum KernelId {
-  KID_CLEAR, KID_SCAN, KID_FILTER, KID_SELECT, KID_SV, KID_DENSE, KID_COMBINE, KID_MERGE, KID_FILL,
+  KID_SCAN, KID_FILTER, KID_SELECT, KID_SV, KID_DENSE, KID_COMBINE, KID_MERGE, KID_FILL,
   KID_RT_SELECT, KID_RT_RERANK, KID_RT_RSEL, KID_RT_PUSH, KID_RT_INIT, KID_COUNT
 };
 const char* const kKernelNames[KID_COUNT] = {
-    "ws_clear",    "k_scan",        "topk_filter",   "topk_select",          "sparse_sv",
+    "k_scan",        "topk_filter",   "topk_select",          "sparse_sv",
     "dense_attn",  "combine",       "attn_merge",    "fill_empty",           "retopk_select",
     "retopk_rerank", "retopk_rerank_select", "retopk_push", "retopk_init"};
 
@@ -222,7 +222,7 @@ Geo geo_of(const stdk_layout* lay) {
 }
 
 // ---------------------------------------------------------------------------
-// workspace: [hist (zeroed per call)] [scores] [spilled candidates] [partials]
+// workspace: [hist (zero between calls)] [scores] [spilled candidates] [partials]
 // ---------------------------------------------------------------------------
 struct TopkWs {
   int64_t S, n, n_pad, K, nsplit, slice, nslice;
@@ -327,14 +327,9 @@ void launch_dense_t(int G, dim3 grid, hipStream_t s, const DenseArgs& a, hipEven
   }
 }
 
-int32_t run_clear(hipStream_t s, uint32_t* p, int64_t words) {
-  if (words <= 0) return STDK_OK;
-  const int64_t blocks = std::min<int64_t>(cdiv(words, 256), 1024);
-  return launch(KID_CLEAR, s, [&](hipEvent_t e0, hipEvent_t e1) { STDK_LAUNCH(ws_clear, dim3((unsigned)blocks), dim3(256), 0, s, p, words); });
-}
-
 // The exact select over n positions (any n >= 1; n <= K takes every row):
-// histogram clear, scan, filter, select. Leaves the chosen rows and scores in
+// scan, filter, select. The histogram region (the first S * 8 KiB of the
+// workspace) is zero on entry and the select kernel leaves it zero again. Leaves the chosen rows and scores in
 // the workspace. `active` restricts the work to the listed segments (ReTopK
 // exact heads); null = all.
 int32_t run_exact_select(const Geo& g, const TopkWs& w, char* ws, const float* q, const void* k_cache,
@@ -344,7 +339,6 @@ int32_t run_exact_select(const Geo& g, const TopkWs& w, char* ws, const float* q
   uint32_t* hist = (uint32_t*)(ws + w.hist);
   Cand* list = (Cand*)(ws + w.list);
   uint32_t* slice_cnt = (uint32_t*)(ws + w.slice_cnt);
-  STDK_TRY(run_clear(s, hist, (int64_t)w.hist_words));
   {
     ScanArgs a{};
     a.q = q;

@@ -297,11 +297,6 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge(MergeArgs a) {
 // ---------------------------------------------------------------------------
 // small utility kernels
 // ---------------------------------------------------------------------------
-// Zero `words` 32-bit words (counters and histograms of a call's workspace).
-__global__ __launch_bounds__(256) void ws_clear(uint32_t* p, int64_t words) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < words; i += (int64_t)gridDim.x * 256) p[i] = 0u;
-}
-
 // Empty row set: o = 0, lse = -inf, idx = -1.
 __global__ __launch_bounds__(256) void fill_empty(float* o, float* lse, int32_t* idx, int64_t S, int32_t K) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;

@@ -23,12 +23,20 @@ struct RangeTab {
   int64_t pos0[kMaxRanges + 1];
 };
 
+// Every table entry is addressed with a compile-time index, so the table is
+// read with uniform (scalar) loads; a per-lane index would turn each access
+// into a vector load from the kernel-argument segment.
 STDK_DEV int64_t pos_to_row(const RangeTab& t, int64_t p) {
-  int r = 0;
-#pragma unroll 1
-  for (int i = 1; i < t.n; ++i)
-    if (p >= t.pos0[i]) r = i;
-  return t.row0[r] + (p - t.pos0[r]);
+  int64_t row0 = t.row0[0], pos0 = t.pos0[0];
+#pragma unroll
+  for (int i = 1; i < kMaxRanges; ++i) {
+    if (i >= t.n) break;
+    if (p >= t.pos0[i]) {
+      row0 = t.row0[i];
+      pos0 = t.pos0[i];
+    }
+  }
+  return row0 + (p - pos0);
 }
 
 // Order-preserving map fp32 -> uint32: a > b (as floats) <=> key(a) > key(b).

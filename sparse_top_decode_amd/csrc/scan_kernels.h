@@ -79,7 +79,7 @@ struct ScanArgs {
   int64_t stride_b_bytes;  // bytes between sequences
   int64_t stride_h_bytes;  // bytes between KV heads
   float* scores;           // [B*Hq][n_pad]
-  uint32_t* hist;          // [B*Hq][2048], accumulated (must start at 0)
+  uint32_t* hist;          // [B*Hq][2048], accumulated (zero on entry; the select kernel re-zeroes it)
   int64_t n, n_pad;        // positions per segment
   int32_t Hq, Hkv;
   int32_t blocks_per_group, pad_;
@@ -90,78 +90,131 @@ struct ScanArgs {
   RangeTab tab;
 };
 
-// The scan reads each key row with 8 lanes; lane c of the row owns the
-// 16-byte chunks c, c+8, ... (byte offsets k*128 + c*16), i.e. 16 elements.
-template <typename T>
-struct ScanTraits;
-template <>
-struct ScanTraits<uint16_t> {
-  static constexpr int NCH = 2, EPC = 8, ROWB = 256;
-};
-template <>
-struct ScanTraits<float> {
-  static constexpr int NCH = 4, EPC = 4, ROWB = 512;
-};
-
 constexpr int kScanThreads = 512;
-constexpr int kScanLPR = 8;  // lanes per key row
 
+// Work shape of the scan for row type T and G query heads per KV head.
+//  - LPR lanes read one key row (8, or 16 when G > 4 to halve the query
+//    registers); lane c of a row owns the 16-byte chunks at byte offsets
+//    k*LPR*16 + c*16, i.e. E elements.
+//  - GP = G rounded up to a power of two; a lane computes V = UR*GP partial
+//    dot products per iteration (UR rows x GP heads), at most 4 chunk loads
+//    per row set.
 template <typename T, int G>
 struct ScanShape {
-  static constexpr int UR0 = kScanLPR / G;
-  static constexpr int UR = UR0 < 1 ? 1 : (UR0 > 4 ? 4 : UR0);  // rows per row group and iteration
+  static constexpr int GP = G <= 1 ? 1 : (G <= 2 ? 2 : (G <= 4 ? 4 : 8));
+  static constexpr int LPR = GP == 8 ? 16 : 8;
+  static constexpr int ROWB = (int)sizeof(T) * kHeadDim;
+  static constexpr int NCH = ROWB / (LPR * 16);
+  static constexpr int EPC = 16 / (int)sizeof(T);
+  static constexpr int E = NCH * EPC;
+  static constexpr int UR0 = LPR / GP < 4 / NCH ? LPR / GP : 4 / NCH;
+  static constexpr int UR = UR0 < 1 ? 1 : UR0;
+  static constexpr int V = UR * GP;
+  static constexpr int NSTEP = LPR == 16 ? 4 : 3;  // lane-exchange steps
+  static constexpr int LOGV = V >= 16 ? 4 : (V >= 8 ? 3 : (V >= 4 ? 2 : (V >= 2 ? 1 : 0)));
   static constexpr int NW = kScanThreads / 64;
-  static constexpr int RPB = 64 / kScanLPR;  // rows per wave and row batch (8)
-  static constexpr int ROWS_ITER = NW * UR * RPB;
+  static constexpr int RPW = 64 / LPR;  // rows per wave and row slot
+  static constexpr int ROWS_ITER = NW * UR * RPW;
+  static_assert(V <= LPR, "slots per lane");
 };
 
-// Sum over aligned groups of 8 lanes with DPP (mirror within half rows, then
-// two quad permutations); all 8 lanes end with the same bits.
-STDK_DEV float sum8(float x) {
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));  // row_half_mirror
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
-  return x;
+// Value of lane i ^ M within its row group (M = 15: row mirror, 7: half-row
+// mirror, 2 and 1: quad permutations).
+template <int M>
+STDK_DEV float xlane(float x) {
+  constexpr int ctrl = M == 15 ? 0x140 : (M == 7 ? 0x141 : (M == 2 ? 0x4E : 0xB1));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), ctrl, 0xF, 0xF, false));
+}
+
+// Exchange mask of reduction step k for LPR lanes per row: 15, 7, 2, 1 (the
+// first dropped when LPR = 8).
+template <int LPR>
+constexpr int step_mask(int k) {
+  return LPR == 16 ? (k == 0 ? 15 : (k == 1 ? 7 : (k == 2 ? 2 : 1))) : (k == 0 ? 7 : (k == 1 ? 2 : 1));
+}
+
+// Reduction of the V slot values of the LPR lanes of a row group. Step k
+// pairs lane c with lane c ^ mask_k. While more than one slot remains, a step
+// keeps the low half of the slots and adds the partner's high half; the slots
+// are laid out so that both partners then hold the same logical value: slot j
+// of lane c carries logical value j ^ pi(c), where pi is linear on the lane
+// bits and maps mask_k to the half-size V >> (k+1) of its step (to 0 once a
+// single slot is left, where the step is a plain all-reduce). Afterwards slot
+// 0 of lane c holds the full sum of logical value pi(c).
+template <int LPR, int V, int K = 0, int HV = V>
+STDK_DEV void reduce_slots(float (&acc)[V]) {
+  constexpr int NSTEP = LPR == 16 ? 4 : 3;
+  if constexpr (K < NSTEP) {
+    constexpr int M = step_mask<LPR>(K);
+    if constexpr (HV > 1) {
+#pragma unroll
+      for (int j = 0; j < HV / 2; ++j) acc[j] += xlane<M>(acc[j + HV / 2]);
+      reduce_slots<LPR, V, K + 1, HV / 2>(acc);
+    } else {
+      acc[0] += xlane<M>(acc[0]);
+      reduce_slots<LPR, V, K + 1, 1>(acc);
+    }
+  }
+}
+
+// pi(c) of the reduction above, and whether lane c writes its sum (lanes
+// that only repeat a sum after an all-reduce step do not).
+template <int LPR, int V>
+STDK_DEV int lane_perm(int c, bool* out_lane) {
+  constexpr int NSTEP = LPR == 16 ? 4 : 3;
+  int x = c, pi = 0, half = V;
+  bool out = true;
+#pragma unroll
+  for (int k = 0; k < NSTEP; ++k) {
+    half >>= 1;
+    if ((x >> (NSTEP - 1 - k)) & 1) {
+      x ^= step_mask<LPR>(k);
+      if (half > 0) pi ^= half;
+      else out = false;
+    }
+  }
+  *out_lane = out;
+  return pi;
 }
 
 template <typename T, int G>
 __global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
   using Sh = ScanShape<T, G>;
-  using Tr = ScanTraits<T>;
-  constexpr int NCH = Tr::NCH, EPC = Tr::EPC, ROWB = Tr::ROWB, UR = Sh::UR, RPB = Sh::RPB;
-  constexpr int E = NCH * EPC;  // elements per lane (16)
-  static_assert(UR * G <= kScanLPR || UR == 1, "output lanes");
-  __shared__ uint32_t lh[G * kHistBins];
+  constexpr int GP = Sh::GP, LPR = Sh::LPR, NCH = Sh::NCH, EPC = Sh::EPC, E = Sh::E, UR = Sh::UR, V = Sh::V;
+  constexpr int RPW = Sh::RPW, ROWB = Sh::ROWB, IT = Sh::ROWS_ITER;
+  __shared__ __attribute__((aligned(16))) uint32_t lh[G * kHistBins];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int rg = lane / kScanLPR, c = lane % kScanLPR;
+  const int rg = lane / LPR, c = lane % LPR;
+  bool out_lane;
+  const int pi = lane_perm<LPR, V>(c, &out_lane);
+  const int rowperm = pi / GP, headperm = pi % GP;
+  const int u_out = pi / GP, h_out = pi % GP;
+  const bool writer = out_lane && h_out < G;
   const int group = blockIdx.x / a.blocks_per_group;
   const int blk = blockIdx.x % a.blocks_per_group;
   const int b = group / a.Hkv, hkv = group % a.Hkv;
   const int64_t seg0 = (int64_t)b * a.Hq + (int64_t)hkv * G;
+  uint32_t act = (1u << G) - 1u;  // heads of this group that take part
   if (a.head_active) {
-    bool any = false;
+    act = 0u;
 #pragma unroll
-    for (int h = 0; h < G; ++h) any |= a.head_active[seg0 + h] != 0;
-    if (!any) return;
+    for (int h = 0; h < G; ++h) act |= (a.head_active[seg0 + h] != 0 ? 1u : 0u) << h;
+    if (act == 0u) return;
   }
 
-  // this lane's 16 query elements for each head
-  float qr[G][E];
+  // query elements of this lane; head slot hs holds head hs ^ headperm (zero
+  // when that head does not exist, G < GP)
+  float qr[GP][E];
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+  for (int hs = 0; hs < GP; ++hs) {
+    const int h = hs ^ headperm;
 #pragma unroll
-    for (int k = 0; k < NCH; ++k) {
-      const float4* qp = reinterpret_cast<const float4*>(a.q + (seg0 + h) * kHeadDim + k * (kHeadDim / NCH) + c * EPC);
+    for (int k = 0; k < NCH; ++k)
 #pragma unroll
-      for (int e4 = 0; e4 < EPC / 4; ++e4) {
-        const float4 v = qp[e4];
-        qr[h][k * EPC + 4 * e4 + 0] = v.x;
-        qr[h][k * EPC + 4 * e4 + 1] = v.y;
-        qr[h][k * EPC + 4 * e4 + 2] = v.z;
-        qr[h][k * EPC + 4 * e4 + 3] = v.w;
-      }
-    }
+      for (int e = 0; e < EPC; ++e)
+        qr[hs][k * EPC + e] = (h < G) ? a.q[(seg0 + h) * kHeadDim + (k * LPR + c) * EPC + e] : 0.f;
+  }
   for (int i = tid; i < G * kHistBins; i += kScanThreads) lh[i] = 0u;
   __syncthreads();
 
@@ -173,72 +226,76 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
     const int64_t s1 = min(p_end, a.tab.pos0[r + 1]);
     if (s0 >= s1) continue;
     const int64_t rowoff = a.tab.row0[r] - a.tab.pos0[r];
-    // rows of row batch u of this lane for the iteration at `base`; loads are
-    // clamped to the last row of the piece and the extra results dropped
+    // row slot s of an iteration at `base` holds row (s ^ rowperm); loads
+    // past the piece are clamped to its last row and their results dropped,
+    // so every load is issued unconditionally
     auto issue = [&](int64_t base, u32x4 (&kw)[UR][NCH]) {
 #pragma unroll
-      for (int u = 0; u < UR; ++u) {
-        const int64_t p = min(base + (int64_t)(w * UR + u) * RPB + rg, s1 - 1);
+      for (int s = 0; s < UR; ++s) {
+        const int64_t p = min(base + (int64_t)(w * UR + (s ^ rowperm)) * RPW + rg, s1 - 1);
         const char* rp = kb + (p + rowoff) * ROWB;
 #pragma unroll
-        for (int k = 0; k < NCH; ++k) kw[u][k] = load16(rp + k * 128);
+        for (int k = 0; k < NCH; ++k) kw[s][k] = load16(rp + k * LPR * 16);
       }
     };
     auto consume = [&](int64_t base, const u32x4 (&kw)[UR][NCH]) {
-      float acc[UR][G];
+      float acc[V];
 #pragma unroll
-      for (int u = 0; u < UR; ++u) {
+      for (int j = 0; j < V; ++j) {
+        const int s = j / GP, hs = j % GP;
         float x[E];
 #pragma unroll
-        for (int k = 0; k < NCH; ++k) unpack16<T>(kw[u][k], x + k * EPC);
+        for (int k = 0; k < NCH; ++k) unpack16<T>(kw[s][k], x + k * EPC);
+        float t = 0.f;
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          float s = qr[h][0] * x[0];
-#pragma unroll
-          for (int e = 1; e < E; ++e) s = fmaf(qr[h][e], x[e], s);
-          acc[u][h] = sum8(s);
-        }
+        for (int e = 0; e < E; ++e) t = fmaf(qr[hs][e], x[e], t);
+        acc[j] = t;
       }
-#pragma unroll
-      for (int i0 = 0; i0 < UR * G; i0 += kScanLPR) {
-        const int i = i0 + c;
-        if (i < UR * G) {
-          float val = 0.f;
-#pragma unroll
-          for (int j = 0; j < UR * G; ++j)
-            if (i == j) val = acc[j / G][j % G];
-          const int uu = i / G, hh = i % G;
-          const int64_t p = base + (int64_t)(w * UR + uu) * RPB + rg;
-          if (p < s1) {
-            val *= a.scale;
-            a.scores[(seg0 + hh) * a.n_pad + p] = val;
-            atomicAdd(&lh[hh * kHistBins + (f2key(val) >> (32 - kHistBits))], 1u);
-          }
-        }
+      reduce_slots<LPR, V>(acc);
+      const int64_t p = base + (int64_t)(w * UR + u_out) * RPW + rg;
+      if (writer && p < s1) {
+        const float val = acc[0] * a.scale;
+        a.scores[(seg0 + h_out) * a.n_pad + p] = val;
+        atomicAdd(&lh[h_out * kHistBins + (f2key(val) >> (32 - kHistBits))], 1u);
       }
     };
-    // two register sets: the loads of the next iteration are in flight while
-    // the current one is computed
-    u32x4 ka[UR][NCH], kc[UR][NCH];
+    // two register sets; the scheduling barriers keep each set's loads ahead
+    // of the arithmetic on the other set
+    u32x4 kw[2][UR][NCH];
     int64_t base = s0;
-    issue(base, ka);
-    while (true) {
-      const int64_t nb = base + Sh::ROWS_ITER;
-      if (nb < s1) issue(nb, kc);
-      consume(base, ka);
-      if (nb >= s1) break;
-      base = nb;
-      const int64_t nb2 = base + Sh::ROWS_ITER;
-      if (nb2 < s1) issue(nb2, ka);
-      consume(base, kc);
-      if (nb2 >= s1) break;
-      base = nb2;
+    issue(base, kw[0]);
+    bool done = false;
+    while (!done) {
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        if (!done) {
+          issue(base + IT, kw[st ^ 1]);
+          __builtin_amdgcn_sched_barrier(0);
+          consume(base, kw[st]);
+          __builtin_amdgcn_sched_barrier(0);
+          base += IT;
+          done = base >= s1;
+        }
+      }
     }
   }
   __syncthreads();
-  for (int i = tid; i < G * kHistBins; i += kScanThreads) {
-    const uint32_t v = lh[i];
-    if (v) atomicAdd(&a.hist[(seg0 + i / kHistBins) * kHistBins + (i % kHistBins)], v);
+  // Add the block histogram to the global one: all LDS reads of a thread are
+  // issued before the first wait, then one atomic per non-empty bin. Heads
+  // that do not take part are skipped, so their global bins stay zero.
+  constexpr int NV = G * kHistBins / 4 / kScanThreads;
+  u32x4 hv[NV];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) hv[k] = *reinterpret_cast<const u32x4*>(&lh[4 * (k * kScanThreads + tid)]);
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const uint32_t vals[4] = {hv[k].x, hv[k].y, hv[k].z, hv[k].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 4 * (k * kScanThreads + tid) + e;
+      const int hh = i / kHistBins;
+      if (vals[e] != 0u && ((act >> hh) & 1u)) atomicAdd(&a.hist[(seg0 + hh) * kHistBins + (i % kHistBins)], vals[e]);
+    }
   }
 }
 

@@ -11,6 +11,8 @@
 // Steps, all integer work exact:
 //  1. k_scan has counted the first radix digit (top 11 bits of the
 //     order-preserving key); the bin b* holding the K-th largest key follows.
+//     topk_select zeroes the counts again once it has read them, so the
+//     histogram needs no separate clearing pass per call.
 //  2. topk_filter (many workgroups) keeps the positions whose digit is >= b*,
 //     in position order.
 //  3. topk_select (one workgroup per head, candidates only): radix digits
@@ -37,7 +39,7 @@ STDK_DEV float key2f(uint32_t k) {
 }
 
 constexpr int kSelThreads = 1024;
-constexpr size_t kSelStaticLds = 10 * 1024;  // static LDS of the select kernels, rounded up
+constexpr size_t kSelStaticLds = 18 * 1024;  // static LDS of the select kernels, rounded up
 
 // ---------------------------------------------------------------------------
 // topk_filter: many workgroups per segment. Each wave scans its own slice of
@@ -118,7 +120,7 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter(FilterArgs a) {
 // chosen rows (ascending) and their scores, and the index output.
 // ---------------------------------------------------------------------------
 struct SelectArgs {
-  const uint32_t* hist;       // [S][2048]
+  uint32_t* hist;             // [S][2048]; read, then zeroed for the next call
   const Cand* list;           // [S][n_pad]
   const uint32_t* slice_cnt;  // [S][nslice]
   Cand* clist;                // [S][n_pad] contiguous copy when it does not fit in LDS
@@ -135,113 +137,67 @@ struct SelectArgs {
 
 constexpr int kSelectWaves = kSelThreads / 64;
 
-// Dynamic LDS: pre[nslice + 1] (slice prefix) then, if the candidates fit,
-// their contiguous copy (position order); else the copy goes to clist.
-__global__ __launch_bounds__(kSelThreads) void topk_select(SelectArgs a) {
-  extern __shared__ uint32_t dyn[];
-  __shared__ uint32_t h[kHistBins];
-  __shared__ uint32_t tmp[kSelThreads / 64 + 1];
-  __shared__ int s_bin;
-  __shared__ uint32_t s_beyond;
-  const int64_t seg = blockIdx.x;
-  if (a.seg_active && a.seg_active[seg] == 0) return;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+// The part of topk_select after the first digit, with the contiguous
+// candidate copy `cl` either in LDS (kLds) or in global memory. Keeping the
+// two cases in separate instantiations lets every access use its own address
+// space instead of generic (flat) accesses, which serialise on both counters.
+template <bool kLds>
+STDK_DEV void select_rest(const SelectArgs& a, int64_t seg, uint32_t m, uint32_t b0, uint32_t need, bool take_all,
+                          const uint32_t* pre, Cand* cl, uint32_t* h, uint32_t* h1, uint32_t* tmp, int* s_bin,
+                          uint32_t* s_beyond) {
+  const int tid = threadIdx.x;
   const int ns = a.nslice;
   const int K = a.K;
-  const bool take_all = a.n <= K;
-  uint32_t* pre = dyn;
   const Cand* lst = a.list + seg * a.n_pad;
 
-  // slice prefix (ns <= kSelThreads * 4) and the first-digit histogram
+  // Contiguous copy in position order. Candidate i lives in slice j with
+  // pre[j] <= i < pre[j+1]; a fixed-length binary search finds j, so the U
+  // searches and then the U loads of a thread proceed side by side. The same
+  // pass counts digit 1 (bits 20..10) of the candidates in bin b0.
   {
-    uint32_t c[4];
-    uint32_t loc = 0;
+    int nsteps = 0;
+    while ((1 << nsteps) < ns) ++nsteps;
+    constexpr int U = 4;
+    for (uint32_t base = 0; base < m; base += kSelThreads * U) {
+      uint32_t ii[U];
+      int lo[U], hi[U];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = tid * 4 + i;
-      c[i] = (j < ns) ? a.slice_cnt[seg * ns + j] : 0u;
-    }
-    constexpr int HU = kHistBins / kSelThreads;
-    uint32_t hv[HU];
+      for (int u = 0; u < U; ++u) {
+        ii[u] = min(base + (uint32_t)(u * kSelThreads + tid), m - 1u);
+        lo[u] = 0;
+        hi[u] = ns;
+      }
+      for (int st = 0; st < nsteps; ++st) {
 #pragma unroll
-    for (int u = 0; u < HU; ++u) hv[u] = a.hist[seg * kHistBins + u * kSelThreads + tid];
-#pragma unroll
-    for (int u = 0; u < HU; ++u) h[u * kSelThreads + tid] = hv[u];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) loc += c[i];
-    uint32_t tot;
-    uint32_t ex = block_excl_scan<kSelThreads>(loc, tmp, &tot);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = tid * 4 + i;
-      if (j < ns) pre[j] = ex;
-      ex += c[i];
-    }
-    if (tid == 0) pre[ns] = tot;
-  }
-  __syncthreads();
-  const uint32_t m = pre[ns];
-  const bool cached = m <= (uint32_t)a.cache_cap;
-  Cand* cl = cached ? reinterpret_cast<Cand*>(dyn + ((ns + 2) & ~1)) : (a.clist + seg * a.n_pad);
-  // contiguous copy: wave wv copies slices wv, wv + 16, ...; 8 slices per batch
-  {
-    constexpr int SU = 8;
-    for (int j0 = wv; j0 < ns; j0 += kSelectWaves * SU) {
-      for (uint32_t e0 = 0;; e0 += 64) {
-        Cand v[SU];
-        bool any = false;
-#pragma unroll
-        for (int u = 0; u < SU; ++u) {
-          const int j = j0 + u * kSelectWaves;
-          const uint32_t e = e0 + lane;
-          if (j < ns && e < pre[j + 1] - pre[j]) {
-            v[u] = lst[(int64_t)j * a.slice + e];
-            any = true;
+        for (int u = 0; u < U; ++u) {
+          const int mid = (lo[u] + hi[u]) >> 1;
+          if (hi[u] - lo[u] > 1) {
+            if (pre[mid] <= ii[u]) lo[u] = mid;
+            else hi[u] = mid;
           }
         }
+      }
+      Cand v[U];
 #pragma unroll
-        for (int u = 0; u < SU; ++u) {
-          const int j = j0 + u * kSelectWaves;
-          const uint32_t e = e0 + lane;
-          if (j < ns && e < pre[j + 1] - pre[j]) cl[pre[j] + e] = v[u];
+      for (int u = 0; u < U; ++u) v[u] = lst[(int64_t)lo[u] * a.slice + (ii[u] - pre[lo[u]])];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t i = base + (uint32_t)(u * kSelThreads + tid);
+        if (i < m) {
+          cl[i] = v[u];
+          if (!take_all && (v[u].key >> 21) == b0) atomicAdd(&h1[(v[u].key >> 10) & 0x7FFu], 1u);
         }
-        if (!__any(any)) break;
       }
     }
   }
   __syncthreads();
-  auto fetch = [&](uint32_t i) -> Cand { return cl[i]; };
   constexpr int U = 8;
-
-  uint32_t need = (uint32_t)K, Tk = 0;
+  uint32_t Tk = 0;
   if (!take_all) {
-    // digit 0 (bits 31..21): from the scan's histogram
-    find_bin<kSelThreads, true>(h, kHistBins, (uint32_t)K, tmp, &s_bin, &s_beyond);
-    const uint32_t b0 = (uint32_t)(s_bin < 0 ? 0 : s_bin);
-    need = (uint32_t)K - s_beyond;
-    __syncthreads();
-    // digit 1 (bits 20..10) among candidates in bin b0
-    for (int i = tid; i < kHistBins; i += kSelThreads) h[i] = 0u;
-    __syncthreads();
-    for (uint32_t base = 0; base < m; base += kSelThreads * U) {
-      uint32_t kv[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const uint32_t i = base + u * kSelThreads + tid;
-        kv[u] = (i < m) ? fetch(i).key : 0u;
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const uint32_t i = base + u * kSelThreads + tid;
-        if (i < m && (kv[u] >> 21) == b0) atomicAdd(&h[(kv[u] >> 10) & 0x7FFu], 1u);
-      }
-    }
-    __syncthreads();
-    find_bin<kSelThreads, true>(h, 2048, need, tmp, &s_bin, &s_beyond);
-    const uint32_t b1 = (uint32_t)(s_bin < 0 ? 0 : s_bin);
-    need -= s_beyond;
-    __syncthreads();
-    // digit 2 (bits 9..0)
+    find_bin<kSelThreads, true>(h1, kHistBins, need, tmp, s_bin, s_beyond);
+    const uint32_t b1 = (uint32_t)(*s_bin < 0 ? 0 : *s_bin);
+    need -= *s_beyond;
+    // digit 2 (bits 9..0) among the candidates with the first 22 bits found
     const uint32_t pre01 = (b0 << 11) | b1;
     for (int i = tid; i < 1024; i += kSelThreads) h[i] = 0u;
     __syncthreads();
@@ -249,20 +205,19 @@ __global__ __launch_bounds__(kSelThreads) void topk_select(SelectArgs a) {
       uint32_t kv[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const uint32_t i = base + u * kSelThreads + tid;
-        kv[u] = (i < m) ? fetch(i).key : 0u;
+        const uint32_t i = min(base + (uint32_t)(u * kSelThreads + tid), m - 1u);
+        kv[u] = cl[i].key;
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const uint32_t i = base + u * kSelThreads + tid;
+        const uint32_t i = base + (uint32_t)(u * kSelThreads + tid);
         if (i < m && (kv[u] >> 10) == pre01) atomicAdd(&h[kv[u] & 0x3FFu], 1u);
       }
     }
     __syncthreads();
-    find_bin<kSelThreads, true>(h, 1024, need, tmp, &s_bin, &s_beyond);
-    Tk = (pre01 << 10) | (uint32_t)(s_bin < 0 ? 0 : s_bin);
-    need -= s_beyond;  // rows with key == Tk to keep, the first ones in position order
-    __syncthreads();
+    find_bin<kSelThreads, true>(h, 1024, need, tmp, s_bin, s_beyond);
+    Tk = (pre01 << 10) | (uint32_t)(*s_bin < 0 ? 0 : *s_bin);
+    need -= *s_beyond;  // rows with key == Tk to keep, the first ones in position order
   }
 
   // ordered compaction: thread t owns candidates [t*per, (t+1)*per)
@@ -272,7 +227,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select(SelectArgs a) {
   for (uint32_t ib = i0; ib < i1; ib += U) {
     uint32_t kv[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) kv[u] = (ib + u < i1) ? fetch(ib + u).key : 0u;
+    for (int u = 0; u < U; ++u) kv[u] = cl[min(ib + u, i1 - 1)].key;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (ib + u < i1) {
@@ -292,24 +247,24 @@ __global__ __launch_bounds__(kSelThreads) void topk_select(SelectArgs a) {
   for (uint32_t ib = i0; ib < i1; ib += U) {
     Cand cv[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (ib + u < i1) cv[u] = fetch(ib + u);
+    for (int u = 0; u < U; ++u) cv[u] = cl[min(ib + u, i1 - 1)];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (ib + u >= i1) break;
-      bool take = take_all || cv[u].key > Tk;
-      if (!take_all && cv[u].key == Tk) {
-        take = eq_seen < need;
-        ++eq_seen;
-      }
-      if (take) {
-        if (r < (uint32_t)K) {
-          const int32_t row = (int32_t)pos_to_row(a.tab, cv[u].pos);
-          srow[r] = row;
-          sz[r] = key2f(cv[u].key);
-          if (io) io[r] = row;
+      if (ib + u < i1) {
+        bool take = take_all || cv[u].key > Tk;
+        if (!take_all && cv[u].key == Tk) {
+          take = eq_seen < need;
+          ++eq_seen;
         }
-        ++r;
+        if (take) {
+          if (r < (uint32_t)K) {
+            const int32_t row = (int32_t)pos_to_row(a.tab, cv[u].pos);
+            srow[r] = row;
+            sz[r] = key2f(cv[u].key);
+            if (io) io[r] = row;
+          }
+          ++r;
+        }
       }
     }
   }
@@ -317,6 +272,74 @@ __global__ __launch_bounds__(kSelThreads) void topk_select(SelectArgs a) {
     srow[i] = -1;
     sz[i] = -INFINITY;
     if (io) io[i] = -1;
+  }
+}
+
+// Dynamic LDS: pre[nslice + 1] (slice prefix) then, if the candidates fit,
+// their contiguous copy (position order); else the copy goes to clist.
+__global__ __launch_bounds__(kSelThreads) void topk_select(SelectArgs a) {
+  extern __shared__ uint32_t dyn[];
+  __shared__ uint32_t h[kHistBins];   // digit 0, later digit 2
+  __shared__ uint32_t h1[kHistBins];  // digit 1
+  __shared__ uint32_t tmp[kSelThreads / 64 + 1];
+  __shared__ int s_bin;
+  __shared__ uint32_t s_beyond;
+  const int64_t seg = blockIdx.x;
+  if (a.seg_active && a.seg_active[seg] == 0) return;
+  const int tid = threadIdx.x;
+  const int ns = a.nslice;
+  const int K = a.K;
+  const bool take_all = a.n <= K;
+  uint32_t* pre = dyn;
+
+  // slice prefix (ns <= kSelThreads * 4) and the first-digit histogram
+  {
+    uint32_t c[4];
+    uint32_t loc = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = tid * 4 + i;
+      c[i] = (j < ns) ? a.slice_cnt[seg * ns + j] : 0u;
+    }
+    constexpr int HU = kHistBins / kSelThreads;
+    uint32_t hv[HU];
+#pragma unroll
+    for (int u = 0; u < HU; ++u) hv[u] = a.hist[seg * kHistBins + u * kSelThreads + tid];
+#pragma unroll
+    for (int u = 0; u < HU; ++u) {
+      h[u * kSelThreads + tid] = hv[u];
+      h1[u * kSelThreads + tid] = 0u;
+      // the scan and the filter are done with this segment's histogram: leave
+      // it zeroed, as the next call's scan expects
+      a.hist[seg * kHistBins + u * kSelThreads + tid] = 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) loc += c[i];
+    uint32_t tot;
+    uint32_t ex = block_excl_scan<kSelThreads>(loc, tmp, &tot);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = tid * 4 + i;
+      if (j < ns) pre[j] = ex;
+      ex += c[i];
+    }
+    if (tid == 0) pre[ns] = tot;
+  }
+  __syncthreads();
+  const uint32_t m = pre[ns];
+  uint32_t need = (uint32_t)K, b0 = 0;
+  if (!take_all) {
+    // digit 0 (bits 31..21): from the scan's histogram
+    find_bin<kSelThreads, true>(h, kHistBins, (uint32_t)K, tmp, &s_bin, &s_beyond);
+    b0 = (uint32_t)(s_bin < 0 ? 0 : s_bin);
+    need = (uint32_t)K - s_beyond;
+  }
+  if (m <= (uint32_t)a.cache_cap) {
+    Cand* cl = reinterpret_cast<Cand*>(dyn + ((ns + 2) & ~1));
+    select_rest<true>(a, seg, m, b0, need, take_all, pre, cl, h, h1, tmp, &s_bin, &s_beyond);
+  } else {
+    select_rest<false>(a, seg, m, b0, need, take_all, pre, a.clist + seg * a.n_pad, h, h1, tmp, &s_bin,
+                       &s_beyond);
   }
 }
 

@@ -56,6 +56,12 @@ def _ranges_arr(ranges: Sequence[Tuple[int, int]]):
     return arr, len(ranges)
 
 
+def new_workspace(nbytes: int, device) -> torch.Tensor:
+    """A zero-filled workspace buffer (the library keeps its counters zero
+    between calls, so it must start that way)."""
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
 def topk_attn_decode_workspace_size(layout: Layout, n_scan: int, top_k: int) -> int:
     return int(load().topk_attn_decode_workspace_size(ctypes.byref(layout), int(n_scan), int(top_k)))
 
@@ -85,8 +91,7 @@ def topk_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
     if idx_out is None and want_idx:
         idx_out = torch.empty((B, Hq, top_k), dtype=torch.int32, device=q.device)
     if workspace is None:
-        nbytes = topk_attn_decode_workspace_size(lay, n, top_k)
-        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+        workspace = new_workspace(topk_attn_decode_workspace_size(lay, n, top_k), q.device)
     arr, nr = _ranges_arr(ranges)
     rc = lib.topk_attn_decode(ctypes.byref(lay), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), arr, nr,
                               int(top_k), ctypes.c_float(scale), _ptr(idx_out), o_out.data_ptr(), lse_out.data_ptr(),
@@ -137,7 +142,7 @@ class Retopk:
         self.cand_cap = top_r * top_k + recent
         mx = L if max_len_t is None else int(max_len_t)
         nbytes = int(load().retopk_workspace_size(ctypes.byref(self.layout), ctypes.byref(self.params), mx))
-        self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        self.workspace = new_workspace(nbytes, dev)
 
     def init(self, q_hist: torch.Tensor, sup_hist: torch.Tensor):
         """Fill the caches from [B, H_q, n, 128] queries and [B, H_q, n, K] supports."""

@@ -170,3 +170,25 @@ def test_deterministic(ops):
     b = run(ops, w, w.ranges, 1000)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+def test_workspace_reuse_counters_return_to_zero(ops):
+    """One workspace serves several calls of one layout with different n and
+    K: each call leaves the histogram counters (the first B*H_q*8 KiB) zero,
+    and every result equals the result with a fresh zero-filled workspace."""
+    log("case workspace reuse c2 layout L=20000")
+    w = make_workload(2, L=20000)
+    q = torch.from_numpy(w.q).cuda()
+    k, v = dev_kv(w)
+    lay = ops.make_layout(k, w.H_q)
+    n_full = sum(e - b for b, e in w.ranges)
+    ws = ops.new_workspace(ops.topk_attn_decode_workspace_size(lay, n_full, 2048), q.device)
+    counters = w.B * w.H_q * 8192
+    cases = [(w.ranges, 2048), ([(0, 5000)], 100), (w.ranges, 7), ([(100, 300), (9000, 19000)], 512)]
+    for ranges, K in cases:
+        got = ops.topk_attn_decode(q, k, v, ranges, K, w.scale, workspace=ws, layout=lay)
+        fresh = ops.topk_attn_decode(q, k, v, ranges, K, w.scale, layout=lay)
+        torch.cuda.synchronize()
+        assert int(torch.count_nonzero(ws[:counters]).item()) == 0, f"counters left dirty after K={K}"
+        for x, y in zip(got, fresh):
+            assert torch.equal(x, y), f"reused workspace differs for K={K}"
