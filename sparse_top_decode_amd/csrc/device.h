@@ -127,6 +127,39 @@ STDK_DEV uint32_t block_excl_scan(uint32_t v, uint32_t* tmp, uint32_t* total) {
   return res;
 }
 
+// Exclusive prefix sums of two values over the block in one pass (NT
+// threads; `tmp` is LDS of at least 2*NT/64 + 2 words). Ends with a barrier.
+template <int NT>
+STDK_DEV void block_excl_scan2(uint32_t v0, uint32_t v1, uint32_t* tmp, uint32_t* ex0, uint32_t* ex1,
+                               uint32_t* tot0, uint32_t* tot1) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint32_t x0 = wave_incl_scan(v0), x1 = wave_incl_scan(v1);
+  if (lane == 63) {
+    tmp[w] = x0;
+    tmp[NW + 1 + w] = x1;
+  }
+  __syncthreads();
+  if (w == 0) {
+    const uint32_t t0 = (lane < NW) ? tmp[lane] : 0u, t1 = (lane < NW) ? tmp[NW + 1 + lane] : 0u;
+    const uint32_t s0 = wave_incl_scan(t0), s1 = wave_incl_scan(t1);
+    if (lane < NW) {
+      tmp[lane] = s0 - t0;
+      tmp[NW + 1 + lane] = s1 - t1;
+    }
+    if (lane == NW - 1) {
+      tmp[NW] = s0;
+      tmp[2 * NW + 1] = s1;
+    }
+  }
+  __syncthreads();
+  *ex0 = x0 - v0 + tmp[w];
+  *ex1 = x1 - v1 + tmp[NW + 1 + w];
+  *tot0 = tmp[NW];
+  *tot1 = tmp[2 * NW + 1];
+  __syncthreads();
+}
+
 // Radix-bin search over an LDS histogram of `nb` bins.
 // DESC: the bin b where the count of strictly higher bins is < need and the
 //       count of bins >= b reaches need (the bin holding the need-th largest).
@@ -165,6 +198,43 @@ STDK_DEV void find_bin(const uint32_t* hist, int nb, uint32_t need, uint32_t* tm
     }
   }
   __syncthreads();
+}
+
+// Radix-bin search over an LDS histogram of NB bins by one wave (all 64
+// lanes of the calling wave; no barrier inside). Same result as find_bin.
+// Lane l owns the NB/64 bins at search ranks [l*NB/64, (l+1)*NB/64) (rank 0
+// = the highest bin when DESC); it sums them reading in a lane-rotated order
+// (fewer bank conflicts), a wave scan locates the owning lane, and the wave
+// then scans that lane's bins together to find the exact one.
+template <int NB, bool DESC>
+STDK_DEV void find_bin_wave(const uint32_t* hist, uint32_t need, int* bin, uint32_t* beyond) {
+  constexpr int PER = NB / 64;
+  static_assert(PER >= 1 && PER <= 64 && (PER & (PER - 1)) == 0, "bins per lane");
+  const int lane = threadIdx.x & 63;
+  auto bin_of = [](int rank) { return DESC ? NB - 1 - rank : rank; };
+  uint32_t local = 0;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) local += hist[bin_of(lane * PER + ((k + lane) & (PER - 1)))];
+  const uint32_t incl = wave_incl_scan(local);
+  const uint32_t before = incl - local;
+  const uint64_t own = __ballot(before < need && need <= incl);
+  if (own == 0) {  // fewer than `need` items in the histogram
+    if (lane == 0) {
+      *bin = -1;
+      *beyond = 0;
+    }
+    return;
+  }
+  const int L = __ffsll((unsigned long long)own) - 1;
+  const uint32_t before_L = __shfl(before, L, 64);
+  const uint32_t x = lane < PER ? hist[bin_of(L * PER + lane)] : 0u;
+  const uint32_t cum = before_L + wave_incl_scan(x);
+  const uint64_t hit = __ballot(lane < PER && cum >= need);
+  const int k = __ffsll((unsigned long long)hit) - 1;
+  if (lane == k) {
+    *bin = bin_of(L * PER + k);
+    *beyond = cum - x;
+  }
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

@@ -39,7 +39,7 @@ STDK_DEV float key2f(uint32_t k) {
 }
 
 constexpr int kSelThreads = 1024;
-constexpr size_t kSelStaticLds = 18 * 1024;  // static LDS of the select kernels, rounded up
+constexpr size_t kSelStaticLds = 22 * 1024;  // static LDS of the select kernels, rounded up
 
 // ---------------------------------------------------------------------------
 // topk_filter: many workgroups per segment. Each wave scans its own slice of
@@ -141,51 +141,47 @@ constexpr int kSelectWaves = kSelThreads / 64;
 // candidate copy `cl` either in LDS (kLds) or in global memory. Keeping the
 // two cases in separate instantiations lets every access use its own address
 // space instead of generic (flat) accesses, which serialise on both counters.
+// `h1` (2048 bins) and `h2` (1024 bins) are zero on entry.
 template <bool kLds>
 STDK_DEV void select_rest(const SelectArgs& a, int64_t seg, uint32_t m, uint32_t b0, uint32_t need, bool take_all,
-                          const uint32_t* pre, Cand* cl, uint32_t* h, uint32_t* h1, uint32_t* tmp, int* s_bin,
+                          const uint32_t* pre, Cand* cl, uint32_t* h1, uint32_t* h2, uint32_t* tmp, int* s_bin,
                           uint32_t* s_beyond) {
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int ns = a.nslice;
   const int K = a.K;
   const Cand* lst = a.list + seg * a.n_pad;
 
-  // Contiguous copy in position order. Candidate i lives in slice j with
-  // pre[j] <= i < pre[j+1]; a fixed-length binary search finds j, so the U
-  // searches and then the U loads of a thread proceed side by side. The same
-  // pass counts digit 1 (bits 20..10) of the candidates in bin b0.
+  // Contiguous copy in position order: wave wv copies slices wv, wv + 16,
+  // ..., SU of them per round. Every load is issued (clamped into the slice)
+  // before the first wait, and the results beyond a slice's count are
+  // dropped. The same pass counts digit 1 (bits 20..10) of the candidates in
+  // bin b0.
   {
-    int nsteps = 0;
-    while ((1 << nsteps) < ns) ++nsteps;
-    constexpr int U = 4;
-    for (uint32_t base = 0; base < m; base += kSelThreads * U) {
-      uint32_t ii[U];
-      int lo[U], hi[U];
+    constexpr int SU = 8;
+    for (int j0 = wv; j0 < ns; j0 += kSelectWaves * SU) {
+      uint32_t cnt[SU], off[SU];
+      int64_t src[SU];
+      uint32_t mx = 0;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        ii[u] = min(base + (uint32_t)(u * kSelThreads + tid), m - 1u);
-        lo[u] = 0;
-        hi[u] = ns;
+      for (int u = 0; u < SU; ++u) {
+        const int j = j0 + u * kSelectWaves;
+        const int jc = min(j, ns - 1);
+        cnt[u] = j < ns ? pre[jc + 1] - pre[jc] : 0u;
+        off[u] = pre[jc];
+        src[u] = (int64_t)jc * a.slice;
+        mx = max(mx, cnt[u]);
       }
-      for (int st = 0; st < nsteps; ++st) {
+      for (uint32_t e0 = 0; e0 < mx; e0 += 64) {
+        const uint32_t e = e0 + lane;
+        Cand v[SU];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int mid = (lo[u] + hi[u]) >> 1;
-          if (hi[u] - lo[u] > 1) {
-            if (pre[mid] <= ii[u]) lo[u] = mid;
-            else hi[u] = mid;
+        for (int u = 0; u < SU; ++u) v[u] = lst[src[u] + min(e, cnt[u] > 0 ? cnt[u] - 1 : 0u)];
+#pragma unroll
+        for (int u = 0; u < SU; ++u) {
+          if (e < cnt[u]) {
+            cl[off[u] + e] = v[u];
+            if (!take_all && (v[u].key >> 21) == b0) atomicAdd(&h1[(v[u].key >> 10) & 0x7FFu], 1u);
           }
-        }
-      }
-      Cand v[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) v[u] = lst[(int64_t)lo[u] * a.slice + (ii[u] - pre[lo[u]])];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const uint32_t i = base + (uint32_t)(u * kSelThreads + tid);
-        if (i < m) {
-          cl[i] = v[u];
-          if (!take_all && (v[u].key >> 21) == b0) atomicAdd(&h1[(v[u].key >> 10) & 0x7FFu], 1u);
         }
       }
     }
@@ -194,33 +190,32 @@ STDK_DEV void select_rest(const SelectArgs& a, int64_t seg, uint32_t m, uint32_t
   constexpr int U = 8;
   uint32_t Tk = 0;
   if (!take_all) {
-    find_bin<kSelThreads, true>(h1, kHistBins, need, tmp, s_bin, s_beyond);
+    if (wv == 0) find_bin_wave<kHistBins, true>(h1, need, s_bin, s_beyond);
+    __syncthreads();
     const uint32_t b1 = (uint32_t)(*s_bin < 0 ? 0 : *s_bin);
     need -= *s_beyond;
     // digit 2 (bits 9..0) among the candidates with the first 22 bits found
     const uint32_t pre01 = (b0 << 11) | b1;
-    for (int i = tid; i < 1024; i += kSelThreads) h[i] = 0u;
-    __syncthreads();
     for (uint32_t base = 0; base < m; base += kSelThreads * U) {
       uint32_t kv[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const uint32_t i = min(base + (uint32_t)(u * kSelThreads + tid), m - 1u);
-        kv[u] = cl[i].key;
-      }
+      for (int u = 0; u < U; ++u) kv[u] = cl[min(base + (uint32_t)(u * kSelThreads + tid), m - 1u)].key;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const uint32_t i = base + (uint32_t)(u * kSelThreads + tid);
-        if (i < m && (kv[u] >> 10) == pre01) atomicAdd(&h[kv[u] & 0x3FFu], 1u);
+        if (i < m && (kv[u] >> 10) == pre01) atomicAdd(&h2[kv[u] & 0x3FFu], 1u);
       }
     }
     __syncthreads();
-    find_bin<kSelThreads, true>(h, 1024, need, tmp, s_bin, s_beyond);
+    if (wv == 0) find_bin_wave<1024, true>(h2, need, s_bin, s_beyond);
+    __syncthreads();
     Tk = (pre01 << 10) | (uint32_t)(*s_bin < 0 ? 0 : *s_bin);
     need -= *s_beyond;  // rows with key == Tk to keep, the first ones in position order
   }
 
-  // ordered compaction: thread t owns candidates [t*per, (t+1)*per)
+  // Ordered compaction: thread t owns candidates [t*per, (t+1)*per). One block
+  // scan of (count > Tk, count == Tk) gives each thread its output offset:
+  // the rows above Tk before it plus the ties before it that are kept.
   const uint32_t per = (m + kSelThreads - 1) / kSelThreads;
   const uint32_t i0 = min(m, tid * per), i1 = min(m, i0 + per);
   uint32_t n_gt = 0, n_eq = 0;
@@ -236,10 +231,10 @@ STDK_DEV void select_rest(const SelectArgs& a, int64_t seg, uint32_t m, uint32_t
       }
     }
   }
-  uint32_t tot_eq, tot_all;
-  const uint32_t eq_before = block_excl_scan<kSelThreads>(n_eq, tmp, &tot_eq);
-  const uint32_t take_eq = min(n_eq, need > eq_before ? need - eq_before : 0u);
-  uint32_t r = block_excl_scan<kSelThreads>(n_gt + take_eq, tmp, &tot_all);
+  uint32_t gt_before, eq_before, tot_gt, tot_eq;
+  block_excl_scan2<kSelThreads>(n_gt, n_eq, tmp, &gt_before, &eq_before, &tot_gt, &tot_eq);
+  const uint32_t tot_all = tot_gt + min(tot_eq, need);
+  uint32_t r = gt_before + min(eq_before, need);
   int32_t* srow = a.sel_row + seg * K;
   float* sz = a.sel_z + seg * K;
   int32_t* io = a.idx_out ? a.idx_out + seg * K : nullptr;
@@ -279,28 +274,24 @@ STDK_DEV void select_rest(const SelectArgs& a, int64_t seg, uint32_t m, uint32_t
 // their contiguous copy (position order); else the copy goes to clist.
 __global__ __launch_bounds__(kSelThreads) void topk_select(SelectArgs a) {
   extern __shared__ uint32_t dyn[];
-  __shared__ uint32_t h[kHistBins];   // digit 0, later digit 2
+  __shared__ uint32_t h[kHistBins];   // digit 0
   __shared__ uint32_t h1[kHistBins];  // digit 1
-  __shared__ uint32_t tmp[kSelThreads / 64 + 1];
+  __shared__ uint32_t h2[1024];       // digit 2
+  __shared__ uint32_t tmp[2 * (kSelThreads / 64) + 2];
   __shared__ int s_bin;
   __shared__ uint32_t s_beyond;
   const int64_t seg = blockIdx.x;
   if (a.seg_active && a.seg_active[seg] == 0) return;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int ns = a.nslice;
   const int K = a.K;
   const bool take_all = a.n <= K;
   uint32_t* pre = dyn;
 
-  // slice prefix (ns <= kSelThreads * 4) and the first-digit histogram
+  // First-digit histogram into LDS (the global copy is zeroed for the next
+  // call: the scan and the filter are done with it), the other digit
+  // histograms cleared, and the slice prefix built by wave 0 (ns <= 4096).
   {
-    uint32_t c[4];
-    uint32_t loc = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = tid * 4 + i;
-      c[i] = (j < ns) ? a.slice_cnt[seg * ns + j] : 0u;
-    }
     constexpr int HU = kHistBins / kSelThreads;
     uint32_t hv[HU];
 #pragma unroll
@@ -309,36 +300,44 @@ __global__ __launch_bounds__(kSelThreads) void topk_select(SelectArgs a) {
     for (int u = 0; u < HU; ++u) {
       h[u * kSelThreads + tid] = hv[u];
       h1[u * kSelThreads + tid] = 0u;
-      // the scan and the filter are done with this segment's histogram: leave
-      // it zeroed, as the next call's scan expects
       a.hist[seg * kHistBins + u * kSelThreads + tid] = 0u;
     }
+    if (tid < 1024) h2[tid] = 0u;
+    if (wv == 0) {
+      uint32_t run = 0;
+      for (int j0 = 0; j0 < ns; j0 += 256) {
+        uint32_t c4[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) loc += c[i];
-    uint32_t tot;
-    uint32_t ex = block_excl_scan<kSelThreads>(loc, tmp, &tot);
+        for (int u = 0; u < 4; ++u) {
+          const int j = j0 + u * 64 + lane;
+          c4[u] = j < ns ? a.slice_cnt[seg * ns + j] : 0u;
+        }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = tid * 4 + i;
-      if (j < ns) pre[j] = ex;
-      ex += c[i];
+        for (int u = 0; u < 4; ++u) {
+          const int j = j0 + u * 64 + lane;
+          const uint32_t incl = wave_incl_scan(c4[u]);
+          if (j < ns) pre[j] = run + incl - c4[u];
+          run += __shfl(incl, 63, 64);
+        }
+      }
+      if (lane == 0) pre[ns] = run;
     }
-    if (tid == 0) pre[ns] = tot;
   }
   __syncthreads();
   const uint32_t m = pre[ns];
   uint32_t need = (uint32_t)K, b0 = 0;
   if (!take_all) {
     // digit 0 (bits 31..21): from the scan's histogram
-    find_bin<kSelThreads, true>(h, kHistBins, (uint32_t)K, tmp, &s_bin, &s_beyond);
+    if (wv == 0) find_bin_wave<kHistBins, true>(h, (uint32_t)K, &s_bin, &s_beyond);
+    __syncthreads();
     b0 = (uint32_t)(s_bin < 0 ? 0 : s_bin);
     need = (uint32_t)K - s_beyond;
   }
   if (m <= (uint32_t)a.cache_cap) {
     Cand* cl = reinterpret_cast<Cand*>(dyn + ((ns + 2) & ~1));
-    select_rest<true>(a, seg, m, b0, need, take_all, pre, cl, h, h1, tmp, &s_bin, &s_beyond);
+    select_rest<true>(a, seg, m, b0, need, take_all, pre, cl, h1, h2, tmp, &s_bin, &s_beyond);
   } else {
-    select_rest<false>(a, seg, m, b0, need, take_all, pre, a.clist + seg * a.n_pad, h, h1, tmp, &s_bin,
+    select_rest<false>(a, seg, m, b0, need, take_all, pre, a.clist + seg * a.n_pad, h1, h2, tmp, &s_bin,
                        &s_beyond);
   }
 }
