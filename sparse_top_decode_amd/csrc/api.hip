@@ -458,8 +458,10 @@ int32_t run_dense(const Geo& g, const TopkWs& w, char* ws, const float* q, const
   a.K = top_k;
   a.scale = scale;
   a.tab = tab;
-  const int64_t nwg = std::min<int64_t>(kDenseMaxWg, cdiv(w.n, kDenseTile));
-  a.rows_per_wg = rup(cdiv(w.n, nwg), kDenseTile);
+  // slices of at least kDenseSlice rows (a workgroup streams little data, so
+  // short row sets are spread over more workgroups)
+  const int64_t nwg = std::min<int64_t>(kDenseMaxWg, cdiv(w.n, kDenseSlice));
+  a.rows_per_wg = rup(cdiv(w.n, nwg), kDenseSlice);
   a.nwg = (int32_t)cdiv(w.n, a.rows_per_wg);
   const dim3 grid((unsigned)a.nwg, (unsigned)g.groups);
   STDK_TRY(launch(KID_DENSE, s, [&](hipEvent_t e0, hipEvent_t e1) {

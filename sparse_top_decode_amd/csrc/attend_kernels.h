@@ -94,7 +94,8 @@ struct DenseArgs {
 };
 
 constexpr int kDenseThreads = 256;
-constexpr int kDenseTile = 64;  // one row per lane of a wave in the tile reductions
+constexpr int kDenseTile = 64;   // one row per lane of a wave in the tile reductions
+constexpr int kDenseSlice = 32;  // rows per workgroup are a multiple of this
 
 template <typename T, int G>
 __global__ __launch_bounds__(kDenseThreads) void dense_attn(DenseArgs a) {
@@ -135,15 +136,24 @@ __global__ __launch_bounds__(kDenseThreads) void dense_attn(DenseArgs a) {
       trow[tid] = p < p1 ? pos_to_row(a.tab, p) : -1;
     }
     __syncthreads();
+    // key and value chunks of the tile, all loads issued before the first
+    // use (rows past the end read row 0 of the set and are masked)
+    u32x4 kwv[U], vwv[U];
+    const int64_t r_any = trow[0];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = (w * U + u) * RPL + rg;
+      const int64_t r = trow[i] >= 0 ? trow[i] : r_any;
+      kwv[u] = load16(kb + r * ROWB + c * 16);
+      vwv[u] = load16(vb + r * ROWB + c * 16);
+    }
     // scores of the tile
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i = (w * U + u) * RPL + rg;
       const int64_t r = trow[i];
-      u32x4 kw = u32x4{0u, 0u, 0u, 0u};
-      if (r >= 0) kw = load16(kb + r * ROWB + c * 16);
       float d[G];
-      chunk_dots<T, G>(kw, qr, d);
+      chunk_dots<T, G>(kwv[u], qr, d);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         const float s = group_sum<LPR>(d[h]);
@@ -184,14 +194,12 @@ __global__ __launch_bounds__(kDenseThreads) void dense_attn(DenseArgs a) {
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[h][e] *= f_old[h];
     }
-    // value rows of the tile
+    // value rows of the tile (masked rows have weight 0)
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i = (w * U + u) * RPL + rg;
-      const int64_t r = trow[i];
-      if (r < 0) continue;
       float x[EPL];
-      unpack16<T>(load16(vb + r * ROWB + c * 16), x);
+      unpack16<T>(vwv[u], x);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         const float wt = zt[h][i];

@@ -192,3 +192,27 @@ def test_workspace_reuse_counters_return_to_zero(ops):
         assert int(torch.count_nonzero(ws[:counters]).item()) == 0, f"counters left dirty after K={K}"
         for x, y in zip(got, fresh):
             assert torch.equal(x, y), f"reused workspace differs for K={K}"
+
+
+@pytest.mark.parametrize("cfg,n_rows", [(2, 640), (2, 1280), (2, 1281), (2, 3000), (1, 640), (1, 641), (3, 300), (3, 900)])
+def test_dense_path_sizes(ops, cfg, n_rows):
+    """K >= n is dense attention over the whole row set. Short sets run in one
+    workgroup per KV head, longer ones split over workgroups and combine;
+    sizes on both sides of the switch, bf16 (G = 4 and G = 7) and fp32."""
+    L = 4096
+    w = make_workload(cfg, L=L) if cfg != 1 else make_workload(1)
+    # two ranges so that positions map to rows through the range table
+    first = n_rows // 3
+    ranges = [(5, 5 + first), (L - (n_rows - first), L)]
+    K = n_rows + 3
+    log(f"case dense cfg={cfg} n={n_rows} K={K}")
+    q = w.q if w.q.ndim == 3 else w.q[:, :, 0]
+    qt = torch.from_numpy(np.ascontiguousarray(q)).cuda()
+    k, v = dev_kv(w)
+    idx, o, lse = ops.topk_attn_decode(qt, k, v, ranges, K, w.scale)
+    torch.cuda.synchronize()
+    idx, o, lse = idx.cpu().numpy(), o.cpu().numpy(), lse.cpu().numpy()
+    rows = ref.range_rows(ranges)
+    assert np.all(idx[:, :, :n_rows] == rows[None, None, :]) and np.all(idx[:, :, n_rows:] == -1)
+    heads = [(0, h) for h in range(w.H_q)]
+    check_heads(w, heads, None, o, lse, ranges, K, fp32=(cfg == 1), q=q, label=f"dense c{cfg} n={n_rows}")
