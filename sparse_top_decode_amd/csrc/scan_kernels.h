@@ -203,6 +203,40 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
     if (act == 0u) return;
   }
 
+  const char* kb = a.k + (int64_t)b * a.stride_b_bytes + (int64_t)hkv * a.stride_h_bytes + c * 16;
+  const int64_t p_beg = (int64_t)blk * a.rows_per_block;
+  const int64_t p_end = min(a.n, p_beg + a.rows_per_block);
+  // current piece of the block's positions: [s0, s1) inside range r
+  int r = -1;
+  int64_t s0 = 0, s1 = 0, rowoff = 0;
+  auto next_piece = [&]() -> bool {
+    for (++r; r < a.tab.n; ++r) {
+      s0 = max(p_beg, a.tab.pos0[r]);
+      s1 = min(p_end, a.tab.pos0[r + 1]);
+      if (s0 < s1) {
+        rowoff = a.tab.row0[r] - a.tab.pos0[r];
+        return true;
+      }
+    }
+    return false;
+  };
+  // row slot s of an iteration at `base` holds row (s ^ rowperm); loads past
+  // the piece are clamped to its last row and their results dropped, so every
+  // load is issued unconditionally
+  auto issue = [&](int64_t base, u32x4 (&kw)[UR][NCH]) {
+#pragma unroll
+    for (int s = 0; s < UR; ++s) {
+      const int64_t p = min(base + (int64_t)(w * UR + (s ^ rowperm)) * RPW + rg, s1 - 1);
+      const char* rp = kb + (p + rowoff) * ROWB;
+#pragma unroll
+      for (int k = 0; k < NCH; ++k) kw[s][k] = load16(rp + k * LPR * 16);
+    }
+  };
+  u32x4 kw[2][UR][NCH];
+  bool more = next_piece();
+  // the first key rows are requested before the query and the LDS set-up
+  if (more) issue(s0, kw[0]);
+
   // query elements of this lane; head slot hs holds head hs ^ headperm (zero
   // when that head does not exist, G < GP)
   float qr[GP][E];
@@ -212,58 +246,47 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
 #pragma unroll
     for (int k = 0; k < NCH; ++k)
 #pragma unroll
-      for (int e = 0; e < EPC; ++e)
-        qr[hs][k * EPC + e] = (h < G) ? a.q[(seg0 + h) * kHeadDim + (k * LPR + c) * EPC + e] : 0.f;
+      for (int e4 = 0; e4 < EPC / 4; ++e4) {
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (h < G) v = *reinterpret_cast<const float4*>(a.q + (seg0 + h) * kHeadDim + (k * LPR + c) * EPC + 4 * e4);
+        qr[hs][k * EPC + 4 * e4 + 0] = v.x;
+        qr[hs][k * EPC + 4 * e4 + 1] = v.y;
+        qr[hs][k * EPC + 4 * e4 + 2] = v.z;
+        qr[hs][k * EPC + 4 * e4 + 3] = v.w;
+      }
   }
   for (int i = tid; i < G * kHistBins; i += kScanThreads) lh[i] = 0u;
-  __syncthreads();
+  // LDS-only barrier: the key loads stay in flight
+  __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
 
-  const char* kb = a.k + (int64_t)b * a.stride_b_bytes + (int64_t)hkv * a.stride_h_bytes + c * 16;
-  const int64_t p_beg = (int64_t)blk * a.rows_per_block;
-  const int64_t p_end = min(a.n, p_beg + a.rows_per_block);
-  for (int r = 0; r < a.tab.n; ++r) {
-    const int64_t s0 = max(p_beg, a.tab.pos0[r]);
-    const int64_t s1 = min(p_end, a.tab.pos0[r + 1]);
-    if (s0 >= s1) continue;
-    const int64_t rowoff = a.tab.row0[r] - a.tab.pos0[r];
-    // row slot s of an iteration at `base` holds row (s ^ rowperm); loads
-    // past the piece are clamped to its last row and their results dropped,
-    // so every load is issued unconditionally
-    auto issue = [&](int64_t base, u32x4 (&kw)[UR][NCH]) {
+  auto consume = [&](int64_t base, const u32x4 (&kv)[UR][NCH]) {
+    float acc[V];
 #pragma unroll
-      for (int s = 0; s < UR; ++s) {
-        const int64_t p = min(base + (int64_t)(w * UR + (s ^ rowperm)) * RPW + rg, s1 - 1);
-        const char* rp = kb + (p + rowoff) * ROWB;
+    for (int j = 0; j < V; ++j) {
+      const int s = j / GP, hs = j % GP;
+      float x[E];
 #pragma unroll
-        for (int k = 0; k < NCH; ++k) kw[s][k] = load16(rp + k * LPR * 16);
-      }
-    };
-    auto consume = [&](int64_t base, const u32x4 (&kw)[UR][NCH]) {
-      float acc[V];
+      for (int k = 0; k < NCH; ++k) unpack16<T>(kv[s][k], x + k * EPC);
+      float t = 0.f;
 #pragma unroll
-      for (int j = 0; j < V; ++j) {
-        const int s = j / GP, hs = j % GP;
-        float x[E];
-#pragma unroll
-        for (int k = 0; k < NCH; ++k) unpack16<T>(kw[s][k], x + k * EPC);
-        float t = 0.f;
-#pragma unroll
-        for (int e = 0; e < E; ++e) t = fmaf(qr[hs][e], x[e], t);
-        acc[j] = t;
-      }
-      reduce_slots<LPR, V>(acc);
-      const int64_t p = base + (int64_t)(w * UR + u_out) * RPW + rg;
-      if (writer && p < s1) {
-        const float val = acc[0] * a.scale;
-        a.scores[(seg0 + h_out) * a.n_pad + p] = val;
-        atomicAdd(&lh[h_out * kHistBins + (f2key(val) >> (32 - kHistBits))], 1u);
-      }
-    };
+      for (int e = 0; e < E; ++e) t = fmaf(qr[hs][e], x[e], t);
+      acc[j] = t;
+    }
+    reduce_slots<LPR, V>(acc);
+    const int64_t p = base + (int64_t)(w * UR + u_out) * RPW + rg;
+    if (writer && p < s1) {
+      const float val = acc[0] * a.scale;
+      // streaming store: the scores are read once, by the next kernel
+      __builtin_nontemporal_store(val, &a.scores[(seg0 + h_out) * a.n_pad + p]);
+      atomicAdd(&lh[h_out * kHistBins + (f2key(val) >> (32 - kHistBits))], 1u);
+    }
+  };
+  while (more) {
     // two register sets; the scheduling barriers keep each set's loads ahead
     // of the arithmetic on the other set
-    u32x4 kw[2][UR][NCH];
     int64_t base = s0;
-    issue(base, kw[0]);
     bool done = false;
     while (!done) {
 #pragma unroll
@@ -278,6 +301,8 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
         }
       }
     }
+    more = next_piece();
+    if (more) issue(s0, kw[0]);
   }
   __syncthreads();
   // Add the block histogram to the global one: all LDS reads of a thread are
