@@ -24,6 +24,12 @@ constexpr int kMaxPartials = 1024;
 STDK_DEV void combine_partials(const float* part, int np, float* o_out, float* lse_out, float* sm, float* sf,
                                float* red) {
   const int j = threadIdx.x;
+  // this thread's output element of the first partials, requested together
+  // with the (m, s) pairs so that one memory round trip serves both
+  constexpr int PB = 32;
+  float ov[PB];
+#pragma unroll
+  for (int i = 0; i < PB; ++i) ov[i] = part[(int64_t)min(i, np - 1) * kPartStride + 4 + j];
   for (int i = j; i < np; i += kHeadDim) {
     sm[i] = part[(int64_t)i * kPartStride];
     sf[i] = part[(int64_t)i * kPartStride + 1];
@@ -36,16 +42,30 @@ STDK_DEV void combine_partials(const float* part, int np, float* o_out, float* l
   __syncthreads();
   M = fmaxf(red[0], red[1]);
   __syncthreads();
-  // weights e^{m_i - M}; the denominator in partial order
+  // weights e^{m_i - M}; the sums run in partial order
   for (int i = j; i < np; i += kHeadDim) sm[i] = (sm[i] == -INFINITY) ? 0.f : __expf(sm[i] - M);
   __syncthreads();
   float S = 0.f, O = 0.f;
   if (M != -INFINITY) {
-#pragma unroll 8
-    for (int i = 0; i < np; ++i) {
-      const float f = sm[i];
-      S = fmaf(sf[i], f, S);
-      O = fmaf(part[(int64_t)i * kPartStride + 4 + j], f, O);
+#pragma unroll
+    for (int i = 0; i < PB; ++i) {
+      if (i < np) {
+        const float f = sm[i];
+        S = fmaf(sf[i], f, S);
+        O = fmaf(ov[i], f, O);
+      }
+    }
+    for (int i0 = PB; i0 < np; i0 += PB) {
+#pragma unroll
+      for (int i = 0; i < PB; ++i) ov[i] = part[(int64_t)min(i0 + i, np - 1) * kPartStride + 4 + j];
+#pragma unroll
+      for (int i = 0; i < PB; ++i) {
+        if (i0 + i < np) {
+          const float f = sm[i0 + i];
+          S = fmaf(sf[i0 + i], f, S);
+          O = fmaf(ov[i], f, O);
+        }
+      }
     }
   }
   if (S > 0.f) {

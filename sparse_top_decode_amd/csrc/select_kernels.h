@@ -64,44 +64,75 @@ struct FilterArgs {
 constexpr int kFilterThreads = 256;
 constexpr int kFilterWaves = kFilterThreads / 64;
 
+// The first-digit bin that holds the K-th largest key, found by one wave
+// straight from the global histogram (no LDS, no barrier): lane l holds the 32
+// bins of search ranks [32l, 32l+32) (rank 0 = bin 2047), a wave scan of the
+// lane sums finds the owning lane, whose bins the wave then scans together.
+// Returns the bin (0 if the histogram holds fewer than `need` items).
+STDK_DEV uint32_t first_digit_bin(const uint32_t* hist, uint32_t need) {
+  const int lane = threadIdx.x & 63;
+  // ranks 32l .. 32l+31 are bins 2047-32l down to 2016-32l: 32 consecutive words
+  const uint32_t* base = hist + (kHistBins - 32 - 32 * lane);
+  u32x4 hv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) hv[i] = load16(base + 4 * i);
+  uint32_t local = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) local += hv[i].x + hv[i].y + hv[i].z + hv[i].w;
+  const uint32_t incl = wave_incl_scan(local);
+  const uint32_t before = incl - local;
+  const uint64_t own = __ballot(before < need && need <= incl);
+  if (own == 0) return 0u;
+  const int L = __ffsll((unsigned long long)own) - 1;
+  const uint32_t before_L = __shfl(before, L, 64);
+  // lane k < 32 takes rank k of lane L: bin word 31 - k of L's block
+  uint32_t x = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t w4[4] = {hv[i].x, hv[i].y, hv[i].z, hv[i].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t t = __shfl(w4[e], L, 64);
+      if (lane == 31 - (4 * i + e)) x = t;
+    }
+  }
+  const uint32_t cum = before_L + wave_incl_scan(lane < 32 ? x : 0u);
+  const uint64_t hit = __ballot(lane < 32 && cum >= need);
+  const int k = __ffsll((unsigned long long)hit) - 1;
+  return (uint32_t)(kHistBins - 1 - (32 * L + k));
+}
+
 __global__ __launch_bounds__(kFilterThreads) void topk_filter(FilterArgs a) {
-  __shared__ uint32_t h[kHistBins];
-  __shared__ uint32_t tmp[kFilterThreads / 64 + 1];
-  __shared__ int s_bin;
-  __shared__ uint32_t s_beyond;
+  __shared__ uint32_t s_bstar;
   const int64_t seg = blockIdx.y;
   if (a.seg_active && a.seg_active[seg] == 0) return;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int js = min(blockIdx.x * kFilterWaves + w, a.nslice - 1);  // this wave's slice
+  const bool live = blockIdx.x * kFilterWaves + w < a.nslice;
   const bool take_all = a.n <= a.K;
-  uint32_t bstar = 0;
-  if (!take_all) {
-    {
-      constexpr int HU = kHistBins / kFilterThreads;
-      uint32_t hv[HU];
-#pragma unroll
-      for (int u = 0; u < HU; ++u) hv[u] = a.hist[seg * kHistBins + u * kFilterThreads + tid];
-#pragma unroll
-      for (int u = 0; u < HU; ++u) h[u * kFilterThreads + tid] = hv[u];
-    }
-    __syncthreads();
-    find_bin<kFilterThreads, true>(h, kHistBins, (uint32_t)a.K, tmp, &s_bin, &s_beyond);
-    bstar = (uint32_t)(s_bin < 0 ? 0 : s_bin);
-  }
-  const int js = blockIdx.x * kFilterWaves + w;  // this wave's slice
-  if (js >= a.nslice) return;
   const float* sc = a.scores + seg * a.n_pad;
   Cand* out = a.list + seg * a.n_pad + (int64_t)js * a.slice;
   const int64_t p0 = (int64_t)js * a.slice;
   const int64_t p1 = min(a.n, p0 + a.slice);
-  uint32_t cnt = 0;
   constexpr int FU = 16;  // loads in flight per lane
-  for (int64_t pb = p0; pb < p1; pb += 64 * FU) {
-    float v[FU];
+  float v[FU];
+  auto load_batch = [&](int64_t pb) {
 #pragma unroll
-    for (int u = 0; u < FU; ++u) {
-      const int64_t p = pb + 64 * u + lane;
-      v[u] = (p < p1) ? sc[p] : 0.f;
-    }
+    for (int u = 0; u < FU; ++u) v[u] = sc[min(pb + 64 * u + lane, p1 - 1)];
+  };
+  // the first batch of scores is requested before the histogram search,
+  // which wave 0 does for the workgroup
+  load_batch(p0);
+  if (w == 0) {
+    const uint32_t bs = take_all ? 0u : first_digit_bin(a.hist + seg * kHistBins, (uint32_t)a.K);
+    if (lane == 0) s_bstar = bs;
+  }
+  __syncthreads();
+  if (!live) return;
+  const uint32_t bstar = s_bstar;
+  uint32_t cnt = 0;
+  for (int64_t pb = p0; pb < p1; pb += 64 * FU) {
+    if (pb != p0) load_batch(pb);
 #pragma unroll
     for (int u = 0; u < FU; ++u) {
       const int64_t p = pb + 64 * u + lane;
@@ -376,29 +407,26 @@ __global__ __launch_bounds__(kSvThreads) void sparse_sv(SvArgs a) {
   const int b = (int)(seg / a.Hq), hq = (int)(seg % a.Hq), hkv = hq / a.G;
   const int j0 = split * kSvRows;
   const int nr = min(kSvRows, a.K - j0);
-  float z = -INFINITY;
-  if (tid < kSvRows) {
-    int32_t r = -1;
-    if (tid < nr) {
-      r = a.sel_row[seg * a.K + j0 + tid];
-      if (r >= 0) z = a.sel_z[seg * a.K + j0 + tid];
-    }
-    rows[tid] = r;
-  }
+  // wave 0: the 64 chosen rows of this slice, their maximum and weights
   if (w == 0) {
-    const float mx = wave_max(z);
-    if (lane == 0) s_m = mx;
+    int32_t r = -1;
+    float z = -INFINITY;
+    if (lane < nr) {
+      r = a.sel_row[seg * a.K + j0 + lane];
+      if (r >= 0) z = a.sel_z[seg * a.K + j0 + lane];
+    }
+    const float m = wave_max(z);
+    rows[lane] = r;
+    wts[lane] = (m == -INFINITY || z == -INFINITY) ? 0.f : __expf(z - m);
+    if (lane == 0) s_m = m;
   }
   __syncthreads();
-  const float m = s_m;
-  if (tid < kSvRows) wts[tid] = (m == -INFINITY || z == -INFINITY) ? 0.f : __expf(z - m);
-  __syncthreads();
-  const char* vb = a.v + (int64_t)b * a.stride_b_bytes + (int64_t)hkv * a.stride_h_bytes;
+  const char* vb = a.v + (int64_t)b * a.stride_b_bytes + (int64_t)hkv * a.stride_h_bytes + c * 16;
   u32x4 vw[RU];
 #pragma unroll
   for (int u = 0; u < RU; ++u) {
     const int32_t r = rows[gid + NG * u];
-    vw[u] = (r >= 0) ? load16(vb + (int64_t)r * ROWB + c * 16) : u32x4{0u, 0u, 0u, 0u};
+    vw[u] = (r >= 0) ? load16(vb + (int64_t)r * ROWB) : u32x4{0u, 0u, 0u, 0u};
   }
   float acc[EPL];
 #pragma unroll
@@ -422,9 +450,9 @@ __global__ __launch_bounds__(kSvThreads) void sparse_sv(SvArgs a) {
     part[4 + tid] = o;
   }
   if (w == 0) {
-    const float s = wave_sum(tid < kSvRows ? wts[tid] : 0.f);
+    const float s = wave_sum(wts[lane]);
     if (lane == 0) {
-      part[0] = m;
+      part[0] = s_m;
       part[1] = s;
     }
   }
