@@ -5,13 +5,18 @@ One step is the whole decode-attention hot path of one Llama-3-8B-shaped
 layer (32 query heads, 8 KV heads, d=128, 131,072 cached rows, bf16 K/V):
   1. top-K attention (K=2048) of every query head over the dynamic rows
      [128, 130560): exact QK scan, per-head top-K select, softmax.V;
-  2. dense attention over the 640 static rows (first 128, last 512), after
-     step 1 on the same stream (--streams 2 runs it on a second stream);
+  2. dense attention over the 640 static rows (first 128, last 512);
   3. log-sum-exp merge of the two partial outputs.
-Inputs are synthetic and resident in HBM before timing starts.
+By default the step is one call of topk_attn_decode_static: the scan scores
+the static rows beside the dynamic ones, the select appends them to every
+chosen-row list, and one softmax.V pass plus one combine produce the merged
+output (Eq. 4-5 applied to the partials). --path three-calls runs the same
+step as topk_attn_decode (dynamic) + topk_attn_decode (static, dense) +
+attn_merge_lse. Inputs are synthetic and resident in HBM before timing starts.
 
 Prints ONE JSON line. `value` is steps/s over --steps timed steps bracketed
-by stream events. The `roofline` object reports the K-cache scan kernel
+by stream events (--graph on replays the step captured in a HIP graph
+instead of launching it from the host; slower on this stack). The `roofline` object reports the K-cache scan kernel
 (k_scan): algorithmic bytes per launch (every scanned key row once, 256 B)
 over its average duration, measured over a second pass of --steps steps in
 which the library attaches HIP start/stop events to every dispatch on the
@@ -102,8 +107,12 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--L", type=int, default=131072)
-    ap.add_argument("--streams", type=int, choices=[1, 2], default=1,
-                    help="2: the static-set call runs on a second stream beside the dynamic-set call")
+    ap.add_argument("--graph", choices=["on", "off"], default="off",
+                    help="on: the timed steps replay the step captured in a HIP graph (measured slower than "
+                         "direct launches for this five-kernel step)")
+    ap.add_argument("--path", choices=["one-pass", "three-calls"], default="one-pass",
+                    help="one-pass: topk_attn_decode_static; three-calls: topk_attn_decode over the dynamic "
+                         "rows, topk_attn_decode over the static rows, attn_merge_lse")
     ap.add_argument("--kernel-events", choices=["on", "off"], default="on",
                     help="record per-kernel HIP events during the timed region (needed for the roofline)")
     args = ap.parse_args()
@@ -130,46 +139,58 @@ def main():
     K = w.top_k
     n_dyn = sum(e - b for b, e in w.ranges)
     n_stat = sum(e - b for b, e in w.static_ranges)
-    ws_d = ops.new_workspace(ops.topk_attn_decode_workspace_size(lay, n_dyn, K), dev)
-    ws_s = ops.new_workspace(ops.topk_attn_decode_workspace_size(lay, n_stat, K), dev)
     idx = torch.empty((1, w.H_q, K), dtype=torch.int32, device=dev)
-    o_d = torch.empty((1, w.H_q, 128), dtype=torch.float32, device=dev)
-    l_d = torch.empty((1, w.H_q), dtype=torch.float32, device=dev)
-    o_s = torch.empty_like(o_d)
-    l_s = torch.empty_like(l_d)
-    o_m = torch.empty_like(o_d)
-    l_m = torch.empty_like(l_d)
+    o_m = torch.empty((1, w.H_q, 128), dtype=torch.float32, device=dev)
+    l_m = torch.empty((1, w.H_q), dtype=torch.float32, device=dev)
+    if args.path == "one-pass":
+        ws_f = ops.new_workspace(ops.topk_attn_decode_static_workspace_size(lay, n_dyn, n_stat, K), dev)
 
-    main = torch.cuda.current_stream()
-    side = torch.cuda.Stream() if args.streams == 2 else None  # default priority
-    ev_go = torch.cuda.Event()
-    ev_static = torch.cuda.Event()
+        def step():
+            # static rows scored by the same scan and appended to the chosen
+            # rows; one softmax.V pass and one combine give the merged output
+            ops.topk_attn_decode_static(q, k, v, w.ranges, w.static_ranges, K, w.scale, idx_out=idx, o_out=o_m,
+                                        lse_out=l_m, workspace=ws_f, layout=lay)
+    else:
+        ws_d = ops.new_workspace(ops.topk_attn_decode_workspace_size(lay, n_dyn, K), dev)
+        ws_s = ops.new_workspace(ops.topk_attn_decode_workspace_size(lay, n_stat, K), dev)
+        o_d = torch.empty_like(o_m)
+        l_d = torch.empty_like(l_m)
+        o_s = torch.empty_like(o_m)
+        l_s = torch.empty_like(l_m)
 
-    def static_part():
-        ops.topk_attn_decode(q, k, v, w.static_ranges, K, w.scale, o_out=o_s, lse_out=l_s, workspace=ws_s,
-                             want_idx=False, layout=lay)
-
-    def step():
-        # The static-set and dynamic-set partial outputs are independent until
-        # the merge (as in the pages' co-execution); with two streams the
-        # static part runs beside the dynamic scan.
-        if side is not None:
-            ev_go.record(main)
-            side.wait_event(ev_go)
-            with torch.cuda.stream(side):
-                static_part()
-            ev_static.record(side)
-        ops.topk_attn_decode(q, k, v, w.ranges, K, w.scale, idx_out=idx, o_out=o_d, lse_out=l_d,
-                             workspace=ws_d, layout=lay)
-        if side is not None:
-            main.wait_event(ev_static)
-        else:
-            static_part()
-        ops.attn_merge_lse(o_s, l_s, o_d, l_d, o_out=o_m, lse_out=l_m)
+        def step():
+            ops.topk_attn_decode(q, k, v, w.ranges, K, w.scale, idx_out=idx, o_out=o_d, lse_out=l_d,
+                                 workspace=ws_d, layout=lay)
+            ops.topk_attn_decode(q, k, v, w.static_ranges, K, w.scale, o_out=o_s, lse_out=l_s, workspace=ws_s,
+                                 want_idx=False, layout=lay)
+            ops.attn_merge_lse(o_s, l_s, o_d, l_d, o_out=o_m, lse_out=l_m)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+
+    # The step captured once in a HIP graph, replayed in the timed pass (no
+    # host work or launch gaps between its kernels). Falls back to eager
+    # launches if capture is unavailable.
+    graph = None
+    if args.graph == "on":
+        try:
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                step()
+            torch.cuda.current_stream().wait_stream(side)
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                step()
+            torch.cuda.synchronize()
+            for _ in range(3):
+                graph.replay()
+            torch.cuda.synchronize()
+        except Exception as e:  # capture unsupported: time eager launches
+            print(f"graph capture failed ({e}); timing eager launches", file=sys.stderr)
+            graph = None
+    run_step = graph.replay if graph is not None else step
 
     # Pass A: the timed steps, bracketed by stream events only (a timing
     # event attached to a dispatch costs several microseconds of step time).
@@ -178,7 +199,7 @@ def main():
     torch.cuda.synchronize()
     ev0.record()
     for _ in range(args.steps):
-        step()
+        run_step()
     ev1.record()
     torch.cuda.synchronize()
     total_ms = ev0.elapsed_time(ev1)
@@ -225,7 +246,7 @@ def main():
             "workload": f"Llama-3-8B-shaped decode attention layer: 32 q / 8 KV heads, d=128, L={w.L}, bf16 K/V, "
                         f"top-K={K} over the {n_dyn} dynamic rows + dense over the {n_stat} static rows + LSE merge",
             "batch": 1, "seq_len": w.L, "top_k": K, "kv_cache": "bf16", "parallelism": "none (1 GPU)",
-            "streams": args.streams,
+            "path": args.path, "hip_graph": graph is not None,
         },
         "roofline": {
             "bound": "hbm",

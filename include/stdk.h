@@ -115,6 +115,39 @@ int32_t topk_attn_decode(const stdk_layout* lay, const float* q, const void* k_c
 size_t topk_attn_decode_workspace_size(const stdk_layout* lay, int64_t n_scan, int32_t top_k);
 
 /* ------------------------------------------------------------------------
+ * topk_attn_decode_static — the decode step of [RA] "CPU-GPU Co-Execution
+ * Architecture": dense attention over a static row set W (static_ranges,
+ * e.g. the first 128 and the last 512 rows) together with exact top-K
+ * attention over the dynamic rows Omega (ranges), combined as in Eq. 3-5.
+ *
+ * o and lse equal attn_merge_lse of (a) topk_attn_decode over
+ * `static_ranges` with top_k >= |W| and (b) topk_attn_decode over `ranges`;
+ * by Eq. 4-5 that is softmax attention over W united with the chosen rows S.
+ * One pass computes it: the scan scores W beside Omega (W stays out of the
+ * top-K), W's rows are appended to every chosen-row list, and the softmax.V
+ * partials of S and W are combined once, with the rescaling of Eq. 4-5.
+ *
+ *  ranges, n_ranges               Omega, as topk_attn_decode's ranges.
+ *  static_ranges, n_static        W, the same rules; no static range may
+ *           overlap a dynamic one, and n_ranges + n_static <= STDK_MAX_RANGES.
+ *  top_k, scale, o_out, lse_out   as topk_attn_decode (top_k applies to Omega).
+ *  idx_out  [B][H_q][top_k] int32 or NULL: the chosen Omega rows S (ascending,
+ *           -1 padded), as topk_attn_decode over `ranges` would give.
+ *  workspace at least topk_attn_decode_static_workspace_size(lay, |Omega|,
+ *           |W|, top_k) bytes, zero-filled before first use.
+ * ---------------------------------------------------------------------- */
+int32_t topk_attn_decode_static(const stdk_layout* lay, const float* q, const void* k_cache,
+                                const void* v_cache, const int64_t* ranges, int32_t n_ranges,
+                                const int64_t* static_ranges, int32_t n_static, int32_t top_k,
+                                float scale, int32_t* idx_out, float* o_out, float* lse_out,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace topk_attn_decode_static needs for n_scan dynamic and
+ * n_static static rows per (b, h_q). */
+size_t topk_attn_decode_static_workspace_size(const stdk_layout* lay, int64_t n_scan,
+                                              int64_t n_static, int32_t top_k);
+
+/* ------------------------------------------------------------------------
  * attn_merge_lse — [RA] Eq. 4-5: combination of two partial attention
  * outputs over disjoint row sets a and b:
  *     M = max(lse_a, lse_b),  lse = M + ln(e^{lse_a - M} + e^{lse_b - M}),

@@ -224,19 +224,23 @@ Geo geo_of(const stdk_layout* lay) {
 // ---------------------------------------------------------------------------
 // workspace: [hist (zero between calls)] [scores] [spilled candidates] [partials]
 // ---------------------------------------------------------------------------
+// n positions take part in the top-K; n_extra more (a static row set) are
+// scored by the same scan and appended whole to every chosen-row list.
 struct TopkWs {
-  int64_t S, n, n_pad, K, nsplit, slice, nslice;
+  int64_t S, n, n_extra, n_pad, K, ksel, nsplit, slice, nslice;
   size_t hist, hist_words, scores, list, clist, slice_cnt, sel_row, sel_z, part, total;
 };
 
-TopkWs topk_ws(int64_t S, int64_t n, int64_t K) {
+TopkWs topk_ws(int64_t S, int64_t n, int64_t K, int64_t n_extra = 0) {
   TopkWs w{};
   w.S = S;
   w.n = n;
+  w.n_extra = n_extra;
   const int64_t n1 = std::max<int64_t>(n, 1);
-  w.n_pad = rup(n1, 64);
+  w.n_pad = rup(std::max<int64_t>(n + n_extra, 1), 64);
   w.K = K;
-  w.nsplit = cdiv(K, kSvRows);
+  w.ksel = K + n_extra;
+  w.nsplit = cdiv(w.ksel, kSvRows);
   // filter wave slices: at most 4 per select thread, about 4096 over the grid
   w.slice = std::max<int64_t>(rup(cdiv(n1, 4 * kSelThreads), 64), std::min<int64_t>(8192, rup(cdiv(n1 * S, 4096), 64)));
   w.nslice = cdiv(n1, w.slice);
@@ -347,7 +351,8 @@ int32_t run_exact_select(const Geo& g, const TopkWs& w, char* ws, const float* q
     a.stride_h_bytes = g.sh_bytes;
     a.scores = scores;
     a.hist = hist;
-    a.n = w.n;
+    a.n = w.n + w.n_extra;
+    a.n_hist = w.n;
     a.n_pad = w.n_pad;
     a.Hq = g.Hq;
     a.Hkv = g.Hkv;
@@ -358,9 +363,9 @@ int32_t run_exact_select(const Geo& g, const TopkWs& w, char* ws, const float* q
     // one resident wave of workgroups over the whole chip, whole iterations each
     const int64_t target_blocks = (int64_t)di->n_cu * di->scan_occ[g.bf16 ? 1 : 0][g.G];
     const int64_t per_group = std::max<int64_t>(1, cdiv(target_blocks, g.groups));
-    const int64_t rpb = std::max<int64_t>(ri, rup(cdiv(w.n, per_group), ri));
+    const int64_t rpb = std::max<int64_t>(ri, rup(cdiv(a.n, per_group), ri));
     a.rows_per_block = rpb;
-    a.blocks_per_group = (int32_t)cdiv(w.n, rpb);
+    a.blocks_per_group = (int32_t)cdiv(a.n, rpb);
     const dim3 grid((unsigned)(g.groups * a.blocks_per_group));
     STDK_TRY(launch(KID_SCAN, s, [&](hipEvent_t e0, hipEvent_t e1) {
       if (g.bf16) launch_scan_t<uint16_t>(g.G, grid, s, a, e0, e1);
@@ -414,15 +419,20 @@ int32_t run_combine(const TopkWs& w, char* ws, int32_t np, float* o_out, float* 
 // Softmax . V over the chosen rows left by the select kernels, in slices of
 // kSvRows rows, then the combine.
 int32_t run_sv(const Geo& g, const TopkWs& w, char* ws, const void* v_cache, float* o_out, float* lse_out,
-               hipStream_t s) {
+               hipStream_t s, const RangeTab* tab = nullptr) {
   SvArgs a{};
+  a.k_top = (int32_t)w.K;
+  a.scores = (const float*)(ws + w.scores);
+  a.n = w.n;
+  a.n_pad = w.n_pad;
+  if (tab) a.tab = *tab;
   a.v = (const char*)v_cache;
   a.stride_b_bytes = g.sb_bytes;
   a.stride_h_bytes = g.sh_bytes;
   a.sel_row = (const int32_t*)(ws + w.sel_row);
   a.sel_z = (const float*)(ws + w.sel_z);
   a.part = (float*)(ws + w.part);
-  a.K = (int32_t)w.K;
+  a.K = (int32_t)w.ksel;
   a.nsplit = (int32_t)w.nsplit;
   a.Hq = g.Hq;
   a.G = g.G;
@@ -443,8 +453,9 @@ int32_t run_combine(const TopkWs& w, char* ws, int32_t np, float* o_out, float* 
 // serves the G query heads of its KV head; partials combined per head.
 int32_t run_dense(const Geo& g, const TopkWs& w, char* ws, const float* q, const void* k_cache,
                   const void* v_cache, const RangeTab& tab, float scale, int32_t top_k, int32_t* idx_out,
-                  float* o_out, float* lse_out, hipStream_t s) {
+                  float* o_out, float* lse_out, hipStream_t s, int64_t n_idx = -1) {
   DenseArgs a{};
+  a.n_idx = n_idx < 0 ? w.n : n_idx;
   a.q = q;
   a.k = (const char*)k_cache;
   a.v = (const char*)v_cache;
@@ -469,6 +480,22 @@ int32_t run_dense(const Geo& g, const TopkWs& w, char* ws, const float* q, const
     else launch_dense_t<float>(g.G, grid, s, a, e0, e1);
   }));
   return run_combine(w, ws, a.nwg, o_out, lse_out, s);
+}
+
+// Host-side validation of one ascending, disjoint list of [begin, end) ranges.
+int32_t check_ranges(const stdk_layout* lay, const int64_t* ranges, int32_t n_ranges, const char* what) {
+  if (n_ranges < 0 || n_ranges > STDK_MAX_RANGES)
+    return fail(STDK_EINVAL, "%s: count %d outside 0..%d", what, n_ranges, STDK_MAX_RANGES);
+  if (n_ranges > 0 && !ranges) return fail(STDK_EINVAL, "%s is NULL", what);
+  int64_t prev_end = 0;
+  for (int r = 0; r < n_ranges; ++r) {
+    const int64_t b = ranges[2 * r], e = ranges[2 * r + 1];
+    if (b < 0 || e > lay->max_len || e <= b)
+      return fail(STDK_EINVAL, "%s %d [%lld, %lld) invalid", what, r, (long long)b, (long long)e);
+    if (r > 0 && b < prev_end) return fail(STDK_EINVAL, "%s must be ascending and disjoint", what);
+    prev_end = e;
+  }
+  return STDK_OK;
 }
 
 }  // namespace
@@ -497,18 +524,8 @@ int32_t topk_attn_decode(const stdk_layout* lay, const float* q, const void* k_c
   STDK_TRY(check_ptr(lse_out, "lse_out", 4));
   if (idx_out && ((uintptr_t)idx_out) % 4) return fail(STDK_EINVAL, "idx_out is not 4-byte aligned");
   if (top_k < 1) return fail(STDK_EINVAL, "top_k %d < 1", top_k);
-  if (n_ranges < 0 || n_ranges > STDK_MAX_RANGES)
-    return fail(STDK_EINVAL, "n_ranges %d outside 0..%d", n_ranges, STDK_MAX_RANGES);
-  if (n_ranges > 0 && !ranges) return fail(STDK_EINVAL, "ranges is NULL");
   if (!std::isfinite(scale)) return fail(STDK_EINVAL, "scale is not finite");
-  int64_t prev_end = 0;
-  for (int r = 0; r < n_ranges; ++r) {
-    const int64_t b = ranges[2 * r], e = ranges[2 * r + 1];
-    if (b < 0 || e > lay->max_len || e <= b)
-      return fail(STDK_EINVAL, "range %d [%lld, %lld) invalid", r, (long long)b, (long long)e);
-    if (r > 0 && b < prev_end) return fail(STDK_EINVAL, "ranges must be ascending and disjoint");
-    prev_end = e;
-  }
+  STDK_TRY(check_ranges(lay, ranges, n_ranges, "ranges"));
   int64_t n = 0;
   const RangeTab tab = make_tab(ranges, n_ranges, &n);
   if (top_k > kMaxTopK && top_k < n)
@@ -538,7 +555,79 @@ int32_t topk_attn_decode(const stdk_layout* lay, const float* q, const void* k_c
     return ok();
   }
   STDK_TRY(run_exact_select(g, w, ws, q, k_cache, tab, scale, nullptr, idx_out, di, s));
-  STDK_TRY(run_sv(g, w, ws, v_cache, o_out, lse_out, s));
+  STDK_TRY(run_sv(g, w, ws, v_cache, o_out, lse_out, s, &tab));
+  return ok();
+}
+
+size_t topk_attn_decode_static_workspace_size(const stdk_layout* lay, int64_t n_scan, int64_t n_static,
+                                              int32_t top_k) {
+  if (check_layout(lay) != STDK_OK || n_scan < 0 || n_static < 0 || top_k < 1) return 0;
+  const int64_t S = geo_of(lay).S;
+  // the fused path, or the dense path over the union of both sets
+  return std::max(topk_ws(S, n_scan, top_k, n_static).total,
+                  topk_ws(S, n_scan + n_static, std::max<int64_t>(top_k, n_scan + n_static)).total);
+}
+
+int32_t topk_attn_decode_static(const stdk_layout* lay, const float* q, const void* k_cache, const void* v_cache,
+                                const int64_t* ranges, int32_t n_ranges, const int64_t* static_ranges,
+                                int32_t n_static, int32_t top_k, float scale, int32_t* idx_out, float* o_out,
+                                float* lse_out, void* workspace, size_t workspace_bytes, void* stream) {
+  STDK_TRY(check_layout(lay));
+  STDK_TRY(check_ptr(q, "q", 16));
+  STDK_TRY(check_ptr(k_cache, "k_cache", 16));
+  STDK_TRY(check_ptr(v_cache, "v_cache", 16));
+  STDK_TRY(check_ptr(o_out, "o_out", 4));
+  STDK_TRY(check_ptr(lse_out, "lse_out", 4));
+  if (idx_out && ((uintptr_t)idx_out) % 4) return fail(STDK_EINVAL, "idx_out is not 4-byte aligned");
+  if (top_k < 1) return fail(STDK_EINVAL, "top_k %d < 1", top_k);
+  if (!std::isfinite(scale)) return fail(STDK_EINVAL, "scale is not finite");
+  STDK_TRY(check_ranges(lay, ranges, n_ranges, "ranges"));
+  STDK_TRY(check_ranges(lay, static_ranges, n_static, "static_ranges"));
+  if (n_ranges + n_static > STDK_MAX_RANGES)
+    return fail(STDK_EINVAL, "%d ranges in total, at most %d", n_ranges + n_static, STDK_MAX_RANGES);
+  for (int i = 0; i < n_ranges; ++i)
+    for (int j = 0; j < n_static; ++j)
+      if (ranges[2 * i] < static_ranges[2 * j + 1] && static_ranges[2 * j] < ranges[2 * i + 1])
+        return fail(STDK_EINVAL, "static range %d overlaps range %d", j, i);
+  // position space: the dynamic ranges first, then the static ones
+  std::vector<int64_t> all(2 * (size_t)(n_ranges + n_static));
+  for (int i = 0; i < 2 * n_ranges; ++i) all[i] = ranges[i];
+  for (int i = 0; i < 2 * n_static; ++i) all[2 * n_ranges + i] = static_ranges[i];
+  int64_t n_all = 0;
+  const RangeTab tab = make_tab(all.data(), n_ranges + n_static, &n_all);
+  int64_t n_dyn = 0;
+  for (int i = 0; i < n_ranges; ++i) n_dyn += ranges[2 * i + 1] - ranges[2 * i];
+  const int64_t n_st = n_all - n_dyn;
+  if (top_k > kMaxTopK && top_k < n_dyn)
+    return fail(STDK_EUNSUPPORTED, "top_k %d > %d (below the row count)", top_k, kMaxTopK);
+  const Geo g = geo_of(lay);
+  const bool fused = top_k < n_dyn;
+  const TopkWs w = fused ? topk_ws(g.S, n_dyn, top_k, n_st)
+                         : topk_ws(g.S, n_all, std::max<int64_t>(top_k, n_all));
+  if (n_all > 0) {
+    STDK_TRY(check_ptr(workspace, "workspace", 256));
+    if (workspace_bytes < w.total)
+      return fail(STDK_EWORKSPACE, "workspace is %zu bytes, %zu needed", workspace_bytes, w.total);
+  }
+  hipStream_t s = (hipStream_t)stream;
+  DevInfo* di = nullptr;
+  STDK_TRY(dev_info(&di));
+  char* ws = (char*)workspace;
+  if (n_all == 0) {
+    const int64_t m = std::max<int64_t>(g.S * kHeadDim, g.S * (int64_t)top_k);
+    STDK_TRY(launch(KID_FILL, s, [&](hipEvent_t e0, hipEvent_t e1) {
+      STDK_LAUNCH(fill_empty, dim3((unsigned)cdiv(m, 256)), dim3(256), 0, s, o_out, lse_out, idx_out, g.S, top_k);
+    }));
+    return ok();
+  }
+  if (!fused) {
+    // every dynamic row is chosen: dense attention over the union; idx_out
+    // lists the dynamic rows, then -1
+    STDK_TRY(run_dense(g, w, ws, q, k_cache, v_cache, tab, scale, top_k, idx_out, o_out, lse_out, s, n_dyn));
+    return ok();
+  }
+  STDK_TRY(run_exact_select(g, w, ws, q, k_cache, tab, scale, nullptr, idx_out, di, s));
+  STDK_TRY(run_sv(g, w, ws, v_cache, o_out, lse_out, s, &tab));
   return ok();
 }
 

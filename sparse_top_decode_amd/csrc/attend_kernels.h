@@ -105,6 +105,7 @@ struct DenseArgs {
   int64_t stride_b_bytes, stride_h_bytes;
   float* part;             // [S][nwg][kPartStride]
   int32_t* idx_out;        // [S][K] or null
+  int64_t n_idx;           // positions below this are listed in idx_out; the remaining slots get -1
   int64_t n;
   int64_t rows_per_wg;
   int32_t nwg, Hq, Hkv, K;
@@ -267,13 +268,13 @@ __global__ __launch_bounds__(kDenseThreads) void dense_attn(DenseArgs a) {
   }
   // the row list of a dense call is every position (ascending), -1 padded
   if (a.idx_out) {
-    for (int64_t p = p0 + tid; p < p1; p += kDenseThreads) {
+    for (int64_t p = p0 + tid; p < min(p1, a.n_idx); p += kDenseThreads) {
       const int32_t row = (int32_t)pos_to_row(a.tab, p);
 #pragma unroll
       for (int h = 0; h < G; ++h) a.idx_out[(seg0 + h) * a.K + p] = row;
     }
     if (wg == 0)
-      for (int64_t p = a.n + tid; p < a.K; p += kDenseThreads)
+      for (int64_t p = a.n_idx + tid; p < a.K; p += kDenseThreads)
 #pragma unroll
         for (int h = 0; h < G; ++h) a.idx_out[(seg0 + h) * a.K + p] = -1;
   }

@@ -87,6 +87,7 @@ struct ScanArgs {
   float scale;
   int32_t pad2_;
   const int32_t* head_active;  // [B*Hq] or null; a group with no active head exits
+  int64_t n_hist;              // positions below this are counted in the histogram; the rest are scored only
   RangeTab tab;
 };
 
@@ -280,7 +281,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
       const float val = acc[0] * a.scale;
       // streaming store: the scores are read once, by the next kernel
       __builtin_nontemporal_store(val, &a.scores[(seg0 + h_out) * a.n_pad + p]);
-      atomicAdd(&lh[h_out * kHistBins + (f2key(val) >> (32 - kHistBits))], 1u);
+      if (p < a.n_hist) atomicAdd(&lh[h_out * kHistBins + (f2key(val) >> (32 - kHistBits))], 1u);
     }
   };
   while (more) {

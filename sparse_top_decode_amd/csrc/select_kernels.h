@@ -161,7 +161,7 @@ struct SelectArgs {
   int32_t cache_cap;          // candidates that fit in the LDS copy
   int32_t* sel_row;           // [S][K] chosen rows, ascending, -1 padded
   float* sel_z;               // [S][K] their scores
-  int32_t* idx_out;           // [S][K] or null (copy of sel_row)
+  int32_t* idx_out;           // [S][K] or null (copy of the chosen rows)
   const int32_t* seg_active;  // [S] or null
   RangeTab tab;
 };
@@ -380,11 +380,18 @@ __global__ __launch_bounds__(kSelThreads) void topk_select(SelectArgs a) {
 struct SvArgs {
   const char* v;              // value cache base
   int64_t stride_b_bytes, stride_h_bytes;
-  const int32_t* sel_row;     // [S][K], -1 = unused slot
-  const float* sel_z;         // [S][K]
+  const int32_t* sel_row;     // [S][k_top], -1 = unused slot
+  const float* sel_z;         // [S][k_top]
   float* part;                // [S][nsplit][kPartStride]
   const int32_t* seg_active;  // [S] or null
-  int32_t K, nsplit, Hq, G;
+  int32_t K, nsplit, Hq, G;   // K = row slots per segment: k_top chosen rows, then the static rows
+  int32_t k_top, pad_;
+  // Row slots k_top .. K-1 are the static positions [n, n + K - k_top),
+  // taken whole: their rows come from the range table, their scores from the
+  // scan's score array.
+  const float* scores;        // [S][n_pad]
+  int64_t n, n_pad;
+  RangeTab tab;
 };
 
 constexpr int kSvThreads = 256;
@@ -411,9 +418,16 @@ __global__ __launch_bounds__(kSvThreads) void sparse_sv(SvArgs a) {
   if (w == 0) {
     int32_t r = -1;
     float z = -INFINITY;
+    const int j = j0 + lane;
     if (lane < nr) {
-      r = a.sel_row[seg * a.K + j0 + lane];
-      if (r >= 0) z = a.sel_z[seg * a.K + j0 + lane];
+      if (j < a.k_top) {
+        r = a.sel_row[seg * a.k_top + j];
+        if (r >= 0) z = a.sel_z[seg * a.k_top + j];
+      } else {
+        const int64_t p = a.n + (j - a.k_top);
+        r = (int32_t)pos_to_row(a.tab, p);
+        z = a.scores[seg * a.n_pad + p];
+      }
     }
     const float m = wave_max(z);
     rows[lane] = r;

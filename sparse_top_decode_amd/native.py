@@ -25,6 +25,7 @@ STDK_MAX_RANGES = 16
 # every symbol include/stdk.h declares
 EXPORTS = [
     "topk_attn_decode", "topk_attn_decode_workspace_size", "attn_merge_lse",
+    "topk_attn_decode_static", "topk_attn_decode_static_workspace_size",
     "retopk_state_init", "retopk_step", "retopk_workspace_size",
     "stdk_last_error", "stdk_version",
     "stdk_profile_enable", "stdk_profile_disable", "stdk_profile_reset", "stdk_profile_read",
@@ -56,6 +57,11 @@ def _sig(lib):
     lib.topk_attn_decode.restype = c_int32
     lib.topk_attn_decode_workspace_size.argtypes = [POINTER(Layout), c_int64, c_int32]
     lib.topk_attn_decode_workspace_size.restype = c_size_t
+    lib.topk_attn_decode_static.argtypes = [POINTER(Layout), P, P, P, POINTER(c_int64), c_int32,
+                                            POINTER(c_int64), c_int32, c_int32, c_float, P, P, P, P, c_size_t, P]
+    lib.topk_attn_decode_static.restype = c_int32
+    lib.topk_attn_decode_static_workspace_size.argtypes = [POINTER(Layout), c_int64, c_int64, c_int32]
+    lib.topk_attn_decode_static_workspace_size.restype = c_size_t
     lib.attn_merge_lse.argtypes = [c_int64, c_int32, P, P, P, P, P, P, P]
     lib.attn_merge_lse.restype = c_int32
     lib.retopk_state_init.argtypes = [POINTER(Layout), POINTER(RetopkParams), POINTER(RetopkState), P, P, c_int32, P]

@@ -100,6 +100,47 @@ def topk_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
     return idx_out, o_out, lse_out
 
 
+def topk_attn_decode_static_workspace_size(layout: Layout, n_scan: int, n_static: int, top_k: int) -> int:
+    return int(load().topk_attn_decode_static_workspace_size(ctypes.byref(layout), int(n_scan), int(n_static),
+                                                             int(top_k)))
+
+
+def topk_attn_decode_static(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                            ranges: Sequence[Tuple[int, int]], static_ranges: Sequence[Tuple[int, int]], top_k: int,
+                            scale: Optional[float] = None, *, idx_out: Optional[torch.Tensor] = None,
+                            o_out: Optional[torch.Tensor] = None, lse_out: Optional[torch.Tensor] = None,
+                            workspace: Optional[torch.Tensor] = None, want_idx: bool = True,
+                            layout: Optional[Layout] = None):
+    """Dense attention over ``static_ranges`` combined with top-K attention
+    over ``ranges`` (one pass; equals attn_merge_lse of the two calls).
+    Returns (idx of the chosen dynamic rows or None, o, lse)."""
+    lib = load()
+    B, Hq, d = q.shape
+    _need(q, "q", torch.float32)
+    _need(k_cache, "k_cache")
+    _need(v_cache, "v_cache", k_cache.dtype, k_cache.shape)
+    lay = layout if layout is not None else make_layout(k_cache, Hq)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    n = sum(int(e) - int(b) for b, e in ranges)
+    n_st = sum(int(e) - int(b) for b, e in static_ranges)
+    if o_out is None:
+        o_out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if lse_out is None:
+        lse_out = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if idx_out is None and want_idx:
+        idx_out = torch.empty((B, Hq, top_k), dtype=torch.int32, device=q.device)
+    if workspace is None:
+        workspace = new_workspace(topk_attn_decode_static_workspace_size(lay, n, n_st, top_k), q.device)
+    arr, nr = _ranges_arr(ranges)
+    sarr, ns = _ranges_arr(static_ranges)
+    rc = lib.topk_attn_decode_static(ctypes.byref(lay), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), arr,
+                                     nr, sarr, ns, int(top_k), ctypes.c_float(scale), _ptr(idx_out),
+                                     o_out.data_ptr(), lse_out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                     _stream())
+    check(rc)
+    return idx_out, o_out, lse_out
+
+
 def attn_merge_lse(o_a: torch.Tensor, lse_a: torch.Tensor, o_b: torch.Tensor, lse_b: torch.Tensor,
                    o_out: Optional[torch.Tensor] = None, lse_out: Optional[torch.Tensor] = None):
     """Log-sum-exp combination of two partial attention outputs."""

@@ -81,6 +81,37 @@ def test_topk_rejects_before_launch(lib, kw, code):
     assert lib.stdk_last_error()
 
 
+def call_static(lib, ranges=((128, 3584),), static=((0, 128), (3584, 4096)), top_k=8, ws_bytes=1 << 30):
+    L = lay()
+    flat = [x for r in ranges for x in r]
+    sflat = [x for r in static for x in r]
+    arr = (ctypes.c_int64 * max(1, len(flat)))(*flat)
+    sarr = (ctypes.c_int64 * max(1, len(sflat)))(*sflat)
+    return lib.topk_attn_decode_static(ctypes.byref(L), FAKE, FAKE, FAKE, arr, len(ranges), sarr, len(static),
+                                       top_k, ctypes.c_float(0.1), FAKE, FAKE, FAKE, FAKE, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(static=((0, 200),)), native.STDK_EINVAL),                       # overlaps the dynamic range
+    (dict(static=((3500, 3600),)), native.STDK_EINVAL),                   # overlaps at the end
+    (dict(static=((3584, 4096), (0, 128))), native.STDK_EINVAL),          # not ascending
+    (dict(static=((0, 128), (4000, 4097))), native.STDK_EINVAL),          # past max_len
+    (dict(ranges=tuple((200 + 2 * i, 201 + 2 * i) for i in range(15))), native.STDK_EINVAL),  # 17 ranges in total
+    (dict(top_k=0), native.STDK_EINVAL),
+    (dict(ws_bytes=1024), native.STDK_EWORKSPACE),
+])
+def test_static_rejects_before_launch(lib, kw, code):
+    assert call_static(lib, **kw) == code
+    assert lib.stdk_last_error()
+
+
+def test_static_workspace_size(lib):
+    a = lib.topk_attn_decode_static_workspace_size(ctypes.byref(lay()), 3456, 640, 64)
+    b = lib.topk_attn_decode_workspace_size(ctypes.byref(lay()), 3456, 64)
+    assert a > b > 0
+    assert lib.topk_attn_decode_static_workspace_size(ctypes.byref(lay(d=64)), 3456, 640, 64) == 0
+
+
 def test_merge_rejects(lib):
     assert lib.attn_merge_lse(4, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == native.STDK_EINVAL
     assert lib.attn_merge_lse(-1, 128, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == native.STDK_EINVAL

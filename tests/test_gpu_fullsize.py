@@ -35,13 +35,18 @@ def all_head_properties(idx, o, lse, rows_lo_hi, K):
 
 
 def decode_step(ops, w, K):
-    """Static-set dense call + dynamic-set top-K call + merge (bench step)."""
+    """Static-set dense call + dynamic-set top-K call + merge, and the same
+    step through the one-pass entry point (the benchmark's step)."""
     q = torch.from_numpy(w.q).cuda()
     k, v = dev_kv(w)
     idx_d, o_d, l_d = ops.topk_attn_decode(q, k, v, w.ranges, K, w.scale)
     _, o_s, l_s = ops.topk_attn_decode(q, k, v, w.static_ranges, K, w.scale, want_idx=False)
     o_m, l_m = ops.attn_merge_lse(o_s, l_s, o_d, l_d)
+    # the same step in one pass (static rows appended to the chosen rows)
+    idx_f, o_f, l_f = ops.topk_attn_decode_static(q, k, v, w.ranges, w.static_ranges, K, w.scale)
     torch.cuda.synchronize()
+    assert torch.equal(idx_f, idx_d), "one-pass step chose other rows"
+    assert torch.max(torch.abs(o_f - o_m)).item() < 1e-5 and torch.max(torch.abs(l_f - l_m)).item() < 1e-5
     out = [x.cpu().numpy() for x in (idx_d, o_d, l_d, o_s, l_s, o_m, l_m)]
     del k, v
     torch.cuda.empty_cache()
