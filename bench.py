@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark: top-K decode-attention steps/sec at 128K context on one MI355X.
 
-One step is the whole decode-attention hot path of one Llama-3-8B-shaped
-layer (32 query heads, 8 KV heads, d=128, 131,072 cached rows, bf16 K/V):
+Default workload (--config 2): one step is the whole decode-attention hot
+path of one Llama-3-8B-shaped layer (32 query heads, 8 KV heads, d=128,
+131,072 cached rows, bf16 K/V):
   1. top-K attention (K=2048) of every query head over the dynamic rows
      [128, 130560): exact QK scan, per-head top-K select, softmax.V;
   2. dense attention over the 640 static rows (first 128, last 512);
@@ -14,13 +15,28 @@ output (Eq. 4-5 applied to the partials). --path three-calls runs the same
 step as topk_attn_decode (dynamic) + topk_attn_decode (static, dense) +
 attn_merge_lse. Inputs are synthetic and resident in HBM before timing starts.
 
+The other workloads are measured the same way when asked for:
+  --config 3  ReTopK, Qwen2.5-7B-shaped (28 q / 4 KV heads), 65,536 initial
+              rows, K=512, C=32, R=4, W=32, tau=0.85, refresh 128: the cache
+              is warmed with 32 exact queries, then every timed pass runs the
+              256 decode steps (one row appended per step) from that state;
+  --config 4  batch of 16 sequences x 32,768 rows, K=1024, one
+              topk_attn_decode call per step;
+  --config 5  1,048,576 rows, K=8192, static window of 640 rows, one-pass step.
+
+Workload 2 steps through --layers distinct copies of the K/V cache in turn
+(default 4), as a model's decode does layer after layer: with a single copy
+the 268 MB scanned per step would partly stay in the 256 MB last-level cache
+between steps, and the scan would not be bound by HBM alone.
+
 Prints ONE JSON line. `value` is steps/s over --steps timed steps bracketed
 by stream events (--graph on replays the step captured in a HIP graph
-instead of launching it from the host; slower on this stack). The `roofline` object reports the K-cache scan kernel
-(k_scan): algorithmic bytes per launch (every scanned key row once, 256 B)
-over its average duration, measured over a second pass of --steps steps in
-which the library attaches HIP start/stop events to every dispatch on the
-launch stream (kernels_avg_us lists every kernel from the same pass).
+instead of launching it from the host; slower on this stack). The
+`roofline` object reports the kernel that dominates the step: algorithmic
+bytes per launch over its average duration, measured over a second pass of
+the same steps in which the library attaches HIP start/stop events to every
+dispatch on the launch stream (kernels_avg_us lists every kernel from the
+same pass).
 
 Options for profiling runs: --copy-calibration runs only a plain device copy
 of known size (to calibrate rocprofv3's FETCH_SIZE / WRITE_SIZE counters);
@@ -43,7 +59,10 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 SCAN_SOURCES = ["sparse_top_decode_amd/csrc/scan_kernels.h", "sparse_top_decode_amd/csrc/device.h"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_scan_c2_hbm_traffic.md")
+METRIC = "top-K decode-attention steps/sec at 128K ctx; K-scan HBM GB/s vs peak"
+TOPK_KERNELS = ("k_scan", "topk_filter", "topk_select", "sparse_sv", "dense_attn", "combine", "attn_merge")
+RETOPK_KERNELS = ("retopk_select", "retopk_rerank", "retopk_rerank_select", "k_scan", "topk_filter", "topk_select",
+                  "sparse_sv", "combine", "retopk_push")
 
 
 def scan_source_hash() -> str:
@@ -54,11 +73,11 @@ def scan_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def committed_traffic():
+def committed_traffic(cfg: int):
     """HBM bytes per k_scan launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source."""
+    summary of this workload, if it was taken on the current kernel source."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(os.path.join(ROOT, "profiles", f"k_scan_c{cfg}_hbm_traffic.md")) as f:
             txt = f.read()
     except OSError:
         return None
@@ -80,157 +99,143 @@ def copy_calibration(nbytes: int):
     print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 5}), flush=True)
 
 
-def cpu_baseline(w, budget_s: float = 12.0):
-    """The oracle (untuned) on the host: whole decode steps of the same
-    workload, repeated until about budget_s of CPU time has passed."""
+# ---------------------------------------------------------------------------
+# CPU baselines: the oracle as it stands, on a bounded sample of the workload
+# ---------------------------------------------------------------------------
+def cpu_baseline_topk(w, budget_s: float = 12.0, seqs=None, heads=None):
+    """Whole decode steps of the workload (or a stated sample of its
+    sequences / query heads, scaled to whole steps), repeated until about
+    budget_s of CPU time has passed."""
     from oracle import reference as ref
+    B, Hq = w.q.shape[0], w.q.shape[1]
+    seqs = list(range(B)) if seqs is None else list(seqs)
+    heads = list(range(Hq)) if heads is None else list(heads)
+    sel = [(b, h) for b in seqs for h in heads]
+    frac = len(sel) / float(B * Hq)
     t0 = time.perf_counter()
     reps = 0
     while True:
-        dyn = ref.topk_attn_decode(w.q, w.k, w.v, w.ranges, w.top_k, w.scale)
-        stat = ref.topk_attn_decode(w.q, w.k, w.v, w.static_ranges, w.top_k, w.scale)
-        ref.attn_merge_lse(stat["o"], stat["lse"], dyn["o"], dyn["lse"])
+        dyn = ref.topk_attn_decode(w.q, w.k, w.v, w.ranges, w.top_k, w.scale, heads=sel)
+        if w.static_ranges:
+            stat = ref.topk_attn_decode(w.q, w.k, w.v, w.static_ranges, w.top_k, w.scale, heads=sel)
+            ref.attn_merge_lse(stat["o"], stat["lse"], dyn["o"], dyn["lse"])
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s or reps >= 20:
             break
-    return dict(value=reps / el, unit="steps/s", cores=1, kind="oracle",
-                sample=f"{reps} full decode step(s) of the timed workload (all 32 query heads: dynamic top-K, "
-                       f"static dense, merge), {el:.1f} s on one host thread (numpy fp64, no BLAS)")
+    what = "dynamic top-K, static dense, merge" if w.static_ranges else "top-K attention"
+    scope = ("all" if frac == 1.0 else f"{len(sel)} of {B * Hq}") + " (sequence, query head) pairs"
+    return dict(value=reps * frac / el, unit="steps/s", cores=1, kind="oracle",
+                sample=f"{reps} decode step(s) of the timed workload on {scope} ({what}), {el:.1f} s on one host "
+                       f"thread (numpy fp64, no BLAS); value scaled to whole steps")
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
-    ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--L", type=int, default=131072)
-    ap.add_argument("--graph", choices=["on", "off"], default="off",
-                    help="on: the timed steps replay the step captured in a HIP graph (measured slower than "
-                         "direct launches for this five-kernel step)")
-    ap.add_argument("--path", choices=["one-pass", "three-calls"], default="one-pass",
-                    help="one-pass: topk_attn_decode_static; three-calls: topk_attn_decode over the dynamic "
-                         "rows, topk_attn_decode over the static rows, attn_merge_lse")
-    ap.add_argument("--kernel-events", choices=["on", "off"], default="on",
-                    help="record per-kernel HIP events during the timed region (needed for the roofline)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no multi-GPU mode.",
-              file=sys.stderr, flush=True)
-        sys.exit(2)
-    if args.copy_calibration:
-        copy_calibration(args.copy_calibration)
-        return
+def cpu_baseline_retopk(w, p, q_hist, sup_hist, budget_s: float = 12.0):
+    """The oracle's ReTopK steps from the same warmed cache, in step order,
+    until about budget_s of CPU time has passed."""
+    from oracle import reference as ref
+    rp = ref.RetopkParams(p["top_k"], p["cache_cap"], p["top_r"], p["recent"], p["tau"], p["refresh"])
+    st = ref.retopk_state_init(rp, q_hist, sup_hist)
+    warm, L0 = p["warmup"], p["L0"]
+    t0 = time.perf_counter()
+    steps = 0
+    for t in range(p["steps"]):
+        _, st, _ = ref.retopk_step(rp, st, w.q[:, :, warm + t], w.k, w.v, L0 + t + 1, t, w.scale)
+        steps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    return dict(value=steps / el, unit="steps/s", cores=1, kind="oracle",
+                sample=f"the first {steps} of the {p['steps']} timed ReTopK steps (all 28 query heads, from the "
+                       f"same warmed cache), {el:.1f} s on one host thread (numpy fp64, no BLAS)")
 
-    import numpy as np
+
+# ---------------------------------------------------------------------------
+# timing
+# ---------------------------------------------------------------------------
+def timed_passes(step, steps, names, reset=None, graph=None):
+    """Pass A: `steps` steps bracketed by stream events only (a timing event
+    attached to a dispatch costs several microseconds of step time). Pass B:
+    the same number of steps again with HIP start/stop events attached by the
+    library to every dispatch, on the launch stream; these give each kernel's
+    average duration, and because every dispatch carries them each start
+    stamp follows the previous kernel's end, so they agree with a rocprofv3
+    kernel trace. `reset` (if given) restores the starting state before each
+    pass. Returns (ms per step, {kernel: (avg_us, launches)})."""
     import torch
-
     from sparse_top_decode_amd import ops
-    from workloads import make_workload
-
-    w = make_workload(2, L=args.L)
-    dev = torch.device("cuda:0")
-    q = torch.from_numpy(w.q).to(dev)
-    k = torch.from_numpy(w.k.view(np.int16)).to(dev).view(torch.bfloat16)
-    v = torch.from_numpy(w.v.view(np.int16)).to(dev).view(torch.bfloat16)
-    lay = ops.make_layout(k, w.H_q)
-    K = w.top_k
-    n_dyn = sum(e - b for b, e in w.ranges)
-    n_stat = sum(e - b for b, e in w.static_ranges)
-    idx = torch.empty((1, w.H_q, K), dtype=torch.int32, device=dev)
-    o_m = torch.empty((1, w.H_q, 128), dtype=torch.float32, device=dev)
-    l_m = torch.empty((1, w.H_q), dtype=torch.float32, device=dev)
-    if args.path == "one-pass":
-        ws_f = ops.new_workspace(ops.topk_attn_decode_static_workspace_size(lay, n_dyn, n_stat, K), dev)
-
-        def step():
-            # static rows scored by the same scan and appended to the chosen
-            # rows; one softmax.V pass and one combine give the merged output
-            ops.topk_attn_decode_static(q, k, v, w.ranges, w.static_ranges, K, w.scale, idx_out=idx, o_out=o_m,
-                                        lse_out=l_m, workspace=ws_f, layout=lay)
-    else:
-        ws_d = ops.new_workspace(ops.topk_attn_decode_workspace_size(lay, n_dyn, K), dev)
-        ws_s = ops.new_workspace(ops.topk_attn_decode_workspace_size(lay, n_stat, K), dev)
-        o_d = torch.empty_like(o_m)
-        l_d = torch.empty_like(l_m)
-        o_s = torch.empty_like(o_m)
-        l_s = torch.empty_like(l_m)
-
-        def step():
-            ops.topk_attn_decode(q, k, v, w.ranges, K, w.scale, idx_out=idx, o_out=o_d, lse_out=l_d,
-                                 workspace=ws_d, layout=lay)
-            ops.topk_attn_decode(q, k, v, w.static_ranges, K, w.scale, o_out=o_s, lse_out=l_s, workspace=ws_s,
-                                 want_idx=False, layout=lay)
-            ops.attn_merge_lse(o_s, l_s, o_d, l_d, o_out=o_m, lse_out=l_m)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # The step captured once in a HIP graph, replayed in the timed pass (no
-    # host work or launch gaps between its kernels). Falls back to eager
-    # launches if capture is unavailable.
-    graph = None
-    if args.graph == "on":
-        try:
-            side = torch.cuda.Stream()
-            side.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(side):
-                step()
-            torch.cuda.current_stream().wait_stream(side)
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph):
-                step()
-            torch.cuda.synchronize()
-            for _ in range(3):
-                graph.replay()
-            torch.cuda.synchronize()
-        except Exception as e:  # capture unsupported: time eager launches
-            print(f"graph capture failed ({e}); timing eager launches", file=sys.stderr)
-            graph = None
-    run_step = graph.replay if graph is not None else step
-
-    # Pass A: the timed steps, bracketed by stream events only (a timing
-    # event attached to a dispatch costs several microseconds of step time).
+    run = graph.replay if graph is not None else step
+    if reset:
+        reset()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     ev0.record()
-    for _ in range(args.steps):
-        run_step()
+    for _ in range(steps):
+        run()
     ev1.record()
     torch.cuda.synchronize()
     total_ms = ev0.elapsed_time(ev1)
-    # Pass B: the same number of steps again with HIP start/stop events
-    # attached by the library to every dispatch, on the launch stream. These
-    # give each kernel's average duration, the scan's included; with events on
-    # every dispatch each start stamp follows the previous kernel's end, so
-    # the durations agree with a rocprofv3 kernel trace.
-    scan_bytes = w.H_kv * n_dyn * 256  # every dynamic key row once, bf16 d=128
-    achieved = scan_avg_s = None
     kern = {}
-    names = ("k_scan", "topk_filter", "topk_select", "sparse_sv", "dense_attn", "combine", "attn_merge")
-    if args.kernel_events == "on":
-        t_all = ops.KernelTimer(capacity=16 * (args.steps + 4))
-        for _ in range(args.steps):
+    if names:
+        if reset:
+            reset()
+        t_all = ops.KernelTimer(capacity=24 * (steps + 4))
+        for _ in range(steps):
             step()
         torch.cuda.synchronize()
         for name in names:
             ms, n = t_all.read(name)
             if n:
-                kern[name] = round(1000.0 * ms / n, 2)
-        scan_ms, scan_n = t_all.read("k_scan")
+                kern[name] = (1000.0 * ms / n, n)
         t_all.close()
-        scan_avg_s = scan_ms / scan_n / 1000.0
-        achieved = scan_bytes / scan_avg_s / 1e9
-    traffic = committed_traffic()
+    return total_ms / steps, kern
 
-    ms_per_step = total_ms / args.steps
+
+def capture(step):
+    """The step captured once in a HIP graph (None if capture fails)."""
+    import torch
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        torch.cuda.synchronize()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        return g
+    except Exception as e:  # capture unsupported: time direct launches
+        print(f"graph capture failed ({e}); timing direct launches", file=sys.stderr)
+        return None
+
+
+def roofline(kern, kernel, bytes_per_launch, traffic):
+    avg = kern.get(kernel, (None, 0))[0]
+    achieved = None if not avg else bytes_per_launch / (avg * 1e-6) / 1e9
+    return {
+        "bound": "hbm",
+        "achieved": None if achieved is None else round(achieved, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": None if achieved is None else round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": traffic,
+        "kernel": kernel,
+        "algorithmic_bytes_per_launch": int(bytes_per_launch),
+        "avg_launch_us": None if not avg else round(avg, 2),
+    }
+
+
+def line(args, ms_per_step, workload, cfg_extra, roof, kern, cpu):
     value = 1000.0 / ms_per_step
-    out = {
-        "metric": "top-K decode-attention steps/sec at 128K ctx; K-scan HBM GB/s vs peak",
+    config = {"workload": workload}
+    config.update(cfg_extra)
+    return {
+        "metric": METRIC,
         "value": round(value, 1),
         "unit": "steps/s",
         "n_gpus": 1,
@@ -242,29 +247,202 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {
-            "workload": f"Llama-3-8B-shaped decode attention layer: 32 q / 8 KV heads, d=128, L={w.L}, bf16 K/V, "
-                        f"top-K={K} over the {n_dyn} dynamic rows + dense over the {n_stat} static rows + LSE merge",
-            "batch": 1, "seq_len": w.L, "top_k": K, "kv_cache": "bf16", "parallelism": "none (1 GPU)",
-            "path": args.path, "hip_graph": graph is not None,
-        },
-        "roofline": {
-            "bound": "hbm",
-            "achieved": None if achieved is None else round(achieved, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": None if achieved is None else round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
-            "kernel": "k_scan",
-            "algorithmic_bytes_per_launch": scan_bytes,
-            "avg_launch_us": None if scan_avg_s is None else round(scan_avg_s * 1e6, 2),
-        },
-        "kernels_avg_us": kern,
+        "config": config,
+        "roofline": roof,
+        "kernels_avg_us": {k: round(v[0], 2) for k, v in kern.items()},
+        "cpu_baseline": cpu,
     }
-    if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(w)
+
+
+def to_dev(w):
+    import numpy as np
+    import torch
+    dev = torch.device("cuda:0")
+    k = torch.from_numpy(w.k.view(np.int16)).to(dev).view(torch.bfloat16)
+    v = torch.from_numpy(w.v.view(np.int16)).to(dev).view(torch.bfloat16)
+    return dev, k, v
+
+
+# ---------------------------------------------------------------------------
+# workloads
+# ---------------------------------------------------------------------------
+def bench_topk(args, cfg):
+    """c2 / c5: dynamic top-K + static window + merge; c4: batched top-K."""
+    import torch
+    from sparse_top_decode_amd import ops
+    from workloads import make_workload
+
+    w = make_workload(cfg, L=args.L if cfg == 2 else None)
+    dev, k0, v0 = to_dev(w)
+    # one cache per layer, used in turn (a decode step reads each layer's
+    # cache once per token); with several layers no layer's 268 MB stays in
+    # the 256 MB last-level cache between its steps, so the scan streams
+    # from HBM as it would in a model
+    n_layers = max(1, args.layers if cfg == 2 else 1)
+    caches = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(n_layers - 1)]
+    k, v = k0, v0
+    layer = {"i": 0}
+    q = torch.from_numpy(w.q).to(dev)
+    lay = ops.make_layout(k, w.H_q)
+    K = w.top_k
+    B = w.q.shape[0]
+    n_dyn = sum(e - b for b, e in w.ranges)
+    n_stat = sum(e - b for b, e in w.static_ranges) if w.static_ranges else 0
+    idx = torch.empty((B, w.H_q, K), dtype=torch.int32, device=dev)
+    o_m = torch.empty((B, w.H_q, 128), dtype=torch.float32, device=dev)
+    l_m = torch.empty((B, w.H_q), dtype=torch.float32, device=dev)
+    path = args.path if n_stat else "top-k only"
+    if n_stat and args.path == "one-pass":
+        ws_f = ops.new_workspace(ops.topk_attn_decode_static_workspace_size(lay, n_dyn, n_stat, K), dev)
+
+        def step():
+            # static rows scored by the same scan and appended to the chosen
+            # rows; one softmax.V pass and one combine give the merged output
+            k, v = caches[layer["i"]]
+            layer["i"] = (layer["i"] + 1) % n_layers
+            ops.topk_attn_decode_static(q, k, v, w.ranges, w.static_ranges, K, w.scale, idx_out=idx, o_out=o_m,
+                                        lse_out=l_m, workspace=ws_f, layout=lay)
+    elif n_stat:
+        ws_d = ops.new_workspace(ops.topk_attn_decode_workspace_size(lay, n_dyn, K), dev)
+        ws_s = ops.new_workspace(ops.topk_attn_decode_workspace_size(lay, n_stat, K), dev)
+        o_d, l_d, o_s, l_s = (torch.empty_like(o_m), torch.empty_like(l_m), torch.empty_like(o_m),
+                              torch.empty_like(l_m))
+
+        def step():
+            k, v = caches[layer["i"]]
+            layer["i"] = (layer["i"] + 1) % n_layers
+            ops.topk_attn_decode(q, k, v, w.ranges, K, w.scale, idx_out=idx, o_out=o_d, lse_out=l_d,
+                                 workspace=ws_d, layout=lay)
+            ops.topk_attn_decode(q, k, v, w.static_ranges, K, w.scale, o_out=o_s, lse_out=l_s, workspace=ws_s,
+                                 want_idx=False, layout=lay)
+            ops.attn_merge_lse(o_s, l_s, o_d, l_d, o_out=o_m, lse_out=l_m)
     else:
-        out["cpu_baseline"] = None
+        ws_d = ops.new_workspace(ops.topk_attn_decode_workspace_size(lay, n_dyn, K), dev)
+
+        def step():
+            ops.topk_attn_decode(q, k, v, w.ranges, K, w.scale, idx_out=idx, o_out=o_m, lse_out=l_m,
+                                 workspace=ws_d, layout=lay)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    graph = capture(step) if args.graph == "on" else None
+    names = TOPK_KERNELS if args.kernel_events == "on" else ()
+    ms, kern = timed_passes(step, args.steps, names, graph=graph)
+    scan_bytes = B * w.H_kv * n_dyn * 256  # every dynamic key row once, bf16 d=128
+    roof = roofline(kern, "k_scan", scan_bytes, committed_traffic(cfg))
+    if cfg == 4:
+        workload = (f"batched decode attention: {B} sequences x {w.L} rows, 32 q / 8 KV heads (Llama-3-8B layout), "
+                    f"d=128, bf16 K/V with per-sequence key offsets, top-K={K} per (sequence, query head)")
+        cpu = None if args.no_cpu else cpu_baseline_topk(w, seqs=[0])
+    else:
+        workload = (f"Llama-3-8B-shaped decode attention layer: 32 q / 8 KV heads, d=128, L={w.L}, bf16 K/V, "
+                    f"top-K={K} over the {n_dyn} dynamic rows + dense over the {n_stat} static rows + LSE merge")
+        if cfg == 5:
+            workload += " (64 planted rows per query head)"
+        sample_heads = None if cfg == 2 else [0, 9, 18, 27]
+        cpu = None if args.no_cpu else cpu_baseline_topk(w, heads=sample_heads)
+    extra = {"batch": B, "seq_len": w.L, "top_k": K, "kv_cache": "bf16", "parallelism": "none (1 GPU)",
+             "path": path, "hip_graph": graph is not None, "layer_caches": n_layers}
+    return line(args, ms, workload, extra, roof, kern, cpu)
+
+
+def bench_retopk(args):
+    """c3: 256 ReTopK decode steps from a warmed cache, per timed pass."""
+    import numpy as np
+    import torch
+    from sparse_top_decode_amd import ops
+    from workloads import make_workload
+
+    w = make_workload(3)
+    p = w.retopk
+    dev, k, v = to_dev(w)
+    K, warm, n_steps, L0 = p["top_k"], p["warmup"], p["steps"], p["L0"]
+    rt = ops.Retopk(k, w.H_q, top_k=K, cache_cap=p["cache_cap"], top_r=p["top_r"], recent=p["recent"],
+                    tau=p["tau"], refresh=p["refresh"], scale=w.scale)
+    qall = torch.from_numpy(np.ascontiguousarray(w.q)).to(dev)
+    qs = [qall[:, :, j].contiguous() for j in range(warm + n_steps)]
+    # the cache starts from the last 32 exact-path queries over the initial rows
+    sups = [ops.topk_attn_decode(qs[j], k, v, [(0, L0)], K, w.scale, layout=rt.layout)[0] for j in range(warm)]
+    q_hist = torch.stack(qs[:warm], dim=2).contiguous()
+    sup_hist = torch.stack(sups, dim=2).contiguous()
+    B = w.q.shape[0]
+    support = torch.empty((B, w.H_q, K), dtype=torch.int32, device=dev)
+    o = torch.empty((B, w.H_q, 128), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, w.H_q), dtype=torch.float32, device=dev)
+    paths = [torch.empty((B, w.H_q), dtype=torch.int32, device=dev) for _ in range(n_steps)]
+    ncands = [torch.empty((B, w.H_q), dtype=torch.int32, device=dev) for _ in range(n_steps)]
+    state = {"t": 0}
+
+    def reset():
+        rt.init(q_hist, sup_hist)
+        state["t"] = 0
+
+    def step():
+        t = state["t"]
+        rt.step(qs[warm + t], k, v, L0 + t + 1, t,
+                out=dict(support=support, o=o, lse=lse, path=paths[t], n_cand=ncands[t]))
+        state["t"] = (t + 1) % n_steps
+
+    reset()
+    for _ in range(n_steps):  # warm-up pass over the whole sequence
+        step()
+    torch.cuda.synchronize()
+    args.steps = n_steps
+    args.warmup = n_steps
+    names = RETOPK_KERNELS if args.kernel_events == "on" else ()
+    ms, kern = timed_passes(step, n_steps, names, reset=reset)
+    pth = torch.stack(paths, dim=-1).cpu().numpy()
+    nc = torch.stack(ncands, dim=-1).cpu().numpy()
+    reuse = pth == 0
+    mean_m = float(nc[reuse].mean()) if reuse.any() else 0.0
+    # rerank: every candidate key row of the reuse-path heads is read once
+    # (256 B); averaged over the launches (one per step with a reuse head)
+    n_rr = int(kern.get("retopk_rerank", (0, 0))[1])
+    rerank_bytes = float(nc[reuse].sum()) * 256 / max(1, n_rr)
+    roof = roofline(kern, "retopk_rerank", rerank_bytes, None)
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline_retopk(w, p, q_hist.cpu().numpy(), sup_hist.cpu().numpy())
+    workload = (f"ReTopK decode, Qwen2.5-7B-shaped layer: 28 q / 4 KV heads, d=128, {L0} initial rows + 1 per step, "
+                f"bf16 K/V, K={K}, C={p['cache_cap']}, R={p['top_r']}, W={p['recent']}, tau={p['tau']}, "
+                f"refresh every {p['refresh']} steps, AR(1) queries; {n_steps} steps per timed pass")
+    extra = {"batch": B, "seq_len": L0, "top_k": K, "kv_cache": "bf16", "parallelism": "none (1 GPU)",
+             "reuse_fraction": round(float(reuse.mean()), 4), "mean_candidates_reuse": round(mean_m, 1),
+             "rerank_launches": n_rr}
+    return line(args, ms, workload, extra, roof, kern, cpu)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, choices=[2, 3, 4, 5], default=2,
+                    help="workload: 2 (default, the headline), 3 ReTopK, 4 batched, 5 1M rows")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--L", type=int, default=131072, help="cache length of workload 2")
+    ap.add_argument("--layers", type=int, default=4,
+                    help="workload 2: distinct K/V caches used in turn, one per layer (1 = the same cache every "
+                         "step, partly served by the last-level cache)")
+    ap.add_argument("--graph", choices=["on", "off"], default="off",
+                    help="on: the timed steps replay the step captured in a HIP graph (measured slower than "
+                         "direct launches for this five-kernel step)")
+    ap.add_argument("--path", choices=["one-pass", "three-calls"], default="one-pass",
+                    help="one-pass: topk_attn_decode_static; three-calls: topk_attn_decode over the dynamic "
+                         "rows, topk_attn_decode over the static rows, attn_merge_lse")
+    ap.add_argument("--kernel-events", choices=["on", "off"], default="on",
+                    help="the second, evented pass that gives per-kernel durations and the roofline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no multi-GPU mode.",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+    out = bench_retopk(args) if args.config == 3 else bench_topk(args, args.config)
     print(json.dumps(out), flush=True)
 
 
