@@ -131,6 +131,8 @@ size_t topk_attn_decode_workspace_size(const stdk_layout* lay, int64_t n_scan, i
  *  static_ranges, n_static        W, the same rules; no static range may
  *           overlap a dynamic one, and n_ranges + n_static <= STDK_MAX_RANGES.
  *  top_k, scale, o_out, lse_out   as topk_attn_decode (top_k applies to Omega).
+ *           When top_k < |Omega|, top_k + |W| must be <= 65536
+ *           (STDK_EUNSUPPORTED otherwise).
  *  idx_out  [B][H_q][top_k] int32 or NULL: the chosen Omega rows S (ascending,
  *           -1 padded), as topk_attn_decode over `ranges` would give.
  *  workspace at least topk_attn_decode_static_workspace_size(lay, |Omega|,

@@ -332,10 +332,10 @@ void launch_dense_t(int G, dim3 grid, hipStream_t s, const DenseArgs& a, hipEven
 }
 
 // The exact select over n positions (any n >= 1; n <= K takes every row):
-// scan, filter, select. The histogram region (the first S * 8 KiB of the
-// workspace) is zero on entry and the select kernel leaves it zero again. Leaves the chosen rows and scores in
-// the workspace. `active` restricts the work to the listed segments (ReTopK
-// exact heads); null = all.
+// scan, filter, select. The histogram (the first S * 8 KiB of the
+// workspace) is zero on entry and the select kernel leaves it zero again.
+// Leaves the chosen rows and scores in the workspace. `active` restricts the
+// work to the listed segments (ReTopK exact heads); null = all.
 int32_t run_exact_select(const Geo& g, const TopkWs& w, char* ws, const float* q, const void* k_cache,
                          const RangeTab& tab, float scale, const int32_t* active, int32_t* idx_out,
                          const DevInfo* di, hipStream_t s) {
@@ -436,6 +436,7 @@ int32_t run_sv(const Geo& g, const TopkWs& w, char* ws, const void* v_cache, flo
   a.nsplit = (int32_t)w.nsplit;
   a.Hq = g.Hq;
   a.G = g.G;
+  if (w.nsplit > kMaxPartials) return fail(STDK_EUNSUPPORTED, "%lld softmax.V partials per head", (long long)w.nsplit);
   const dim3 grid((unsigned)w.nsplit, (unsigned)w.S);
   STDK_TRY(launch(KID_SV, s, [&](hipEvent_t e0, hipEvent_t e1) {
     if (g.bf16) STDK_LAUNCH(sparse_sv<uint16_t>, grid, dim3(kSvThreads), 0, s, a);
@@ -600,6 +601,8 @@ int32_t topk_attn_decode_static(const stdk_layout* lay, const float* q, const vo
   const int64_t n_st = n_all - n_dyn;
   if (top_k > kMaxTopK && top_k < n_dyn)
     return fail(STDK_EUNSUPPORTED, "top_k %d > %d (below the row count)", top_k, kMaxTopK);
+  if (top_k < n_dyn && top_k + n_st > kMaxTopK)
+    return fail(STDK_EUNSUPPORTED, "top_k %d + %lld static rows > %d", top_k, (long long)n_st, kMaxTopK);
   const Geo g = geo_of(lay);
   const bool fused = top_k < n_dyn;
   const TopkWs w = fused ? topk_ws(g.S, n_dyn, top_k, n_st)

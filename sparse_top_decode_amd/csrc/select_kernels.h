@@ -68,14 +68,19 @@ constexpr int kFilterWaves = kFilterThreads / 64;
 // straight from the global histogram (no LDS, no barrier): lane l holds the 32
 // bins of search ranks [32l, 32l+32) (rank 0 = bin 2047), a wave scan of the
 // lane sums finds the owning lane, whose bins the wave then scans together.
-// Returns the bin (0 if the histogram holds fewer than `need` items).
-STDK_DEV uint32_t first_digit_bin(const uint32_t* hist, uint32_t need) {
+// The loads and the search are separate steps so that other loads can be
+// issued between them.
+STDK_DEV void first_digit_load(const uint32_t* hist, u32x4 (&hv)[8]) {
   const int lane = threadIdx.x & 63;
   // ranks 32l .. 32l+31 are bins 2047-32l down to 2016-32l: 32 consecutive words
   const uint32_t* base = hist + (kHistBins - 32 - 32 * lane);
-  u32x4 hv[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) hv[i] = load16(base + 4 * i);
+}
+
+// Returns the bin (0 if the histogram holds fewer than `need` items).
+STDK_DEV uint32_t first_digit_search(const u32x4 (&hv)[8], uint32_t need) {
+  const int lane = threadIdx.x & 63;
   uint32_t local = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) local += hv[i].x + hv[i].y + hv[i].z + hv[i].w;
@@ -120,11 +125,13 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter(FilterArgs a) {
 #pragma unroll
     for (int u = 0; u < FU; ++u) v[u] = sc[min(pb + 64 * u + lane, p1 - 1)];
   };
-  // the first batch of scores is requested before the histogram search,
-  // which wave 0 does for the workgroup
+  // wave 0 requests the histogram first, then every wave its first batch of
+  // scores; wave 0's search waits on the histogram only
+  u32x4 hv[8];
+  if (w == 0) first_digit_load(a.hist + seg * kHistBins, hv);
   load_batch(p0);
   if (w == 0) {
-    const uint32_t bs = take_all ? 0u : first_digit_bin(a.hist + seg * kHistBins, (uint32_t)a.K);
+    const uint32_t bs = take_all ? 0u : first_digit_search(hv, (uint32_t)a.K);
     if (lane == 0) s_bstar = bs;
   }
   __syncthreads();

@@ -81,8 +81,8 @@ def test_topk_rejects_before_launch(lib, kw, code):
     assert lib.stdk_last_error()
 
 
-def call_static(lib, ranges=((128, 3584),), static=((0, 128), (3584, 4096)), top_k=8, ws_bytes=1 << 30):
-    L = lay()
+def call_static(lib, ranges=((128, 3584),), static=((0, 128), (3584, 4096)), top_k=8, ws_bytes=1 << 30, L=None):
+    L = L or lay()
     flat = [x for r in ranges for x in r]
     sflat = [x for r in static for x in r]
     arr = (ctypes.c_int64 * max(1, len(flat)))(*flat)
@@ -102,6 +102,14 @@ def call_static(lib, ranges=((128, 3584),), static=((0, 128), (3584, 4096)), top
 ])
 def test_static_rejects_before_launch(lib, kw, code):
     assert call_static(lib, **kw) == code
+    assert lib.stdk_last_error()
+
+
+def test_static_rejects_too_many_attended_rows(lib):
+    # the chosen rows plus the static rows exceed what one merge handles
+    big = lay(L=200000)
+    assert call_static(lib, ranges=((0, 150000),), static=((150000, 200000),), top_k=20000,
+                       L=big) == native.STDK_EUNSUPPORTED
     assert lib.stdk_last_error()
 
 
