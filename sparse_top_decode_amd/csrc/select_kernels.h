@@ -39,7 +39,7 @@ STDK_DEV float key2f(uint32_t k) {
 }
 
 constexpr int kSelThreads = 1024;
-constexpr size_t kSelStaticLds = 22 * 1024;  // static LDS of the select kernels, rounded up
+constexpr size_t kSelStaticLds = 14 * 1024;  // static LDS of the select kernels, rounded up
 
 // ---------------------------------------------------------------------------
 // topk_filter: many workgroups per segment. Each wave scans its own slice of
@@ -78,8 +78,9 @@ STDK_DEV void first_digit_load(const uint32_t* hist, u32x4 (&hv)[8]) {
   for (int i = 0; i < 8; ++i) hv[i] = load16(base + 4 * i);
 }
 
-// Returns the bin (0 if the histogram holds fewer than `need` items).
-STDK_DEV uint32_t first_digit_search(const u32x4 (&hv)[8], uint32_t need) {
+// Returns the bin (0 if the histogram holds fewer than `need` items) and, in
+// *beyond, the count in the bins above it.
+STDK_DEV uint32_t first_digit_search(const u32x4 (&hv)[8], uint32_t need, uint32_t* beyond = nullptr) {
   const int lane = threadIdx.x & 63;
   uint32_t local = 0;
 #pragma unroll
@@ -87,7 +88,10 @@ STDK_DEV uint32_t first_digit_search(const u32x4 (&hv)[8], uint32_t need) {
   const uint32_t incl = wave_incl_scan(local);
   const uint32_t before = incl - local;
   const uint64_t own = __ballot(before < need && need <= incl);
-  if (own == 0) return 0u;
+  if (own == 0) {
+    if (beyond) *beyond = 0u;
+    return 0u;
+  }
   const int L = __ffsll((unsigned long long)own) - 1;
   const uint32_t before_L = __shfl(before, L, 64);
   // lane k < 32 takes rank k of lane L: bin word 31 - k of L's block
@@ -104,6 +108,7 @@ STDK_DEV uint32_t first_digit_search(const u32x4 (&hv)[8], uint32_t need) {
   const uint32_t cum = before_L + wave_incl_scan(lane < 32 ? x : 0u);
   const uint64_t hit = __ballot(lane < 32 && cum >= need);
   const int k = __ffsll((unsigned long long)hit) - 1;
+  if (beyond) *beyond = __shfl(cum - x, k, 64);
   return (uint32_t)(kHistBins - 1 - (32 * L + k));
 }
 
@@ -312,7 +317,6 @@ STDK_DEV void select_rest(const SelectArgs& a, int64_t seg, uint32_t m, uint32_t
 // their contiguous copy (position order); else the copy goes to clist.
 __global__ __launch_bounds__(kSelThreads) void topk_select(SelectArgs a) {
   extern __shared__ uint32_t dyn[];
-  __shared__ uint32_t h[kHistBins];   // digit 0
   __shared__ uint32_t h1[kHistBins];  // digit 1
   __shared__ uint32_t h2[1024];       // digit 2
   __shared__ uint32_t tmp[2 * (kSelThreads / 64) + 2];
@@ -326,51 +330,50 @@ __global__ __launch_bounds__(kSelThreads) void topk_select(SelectArgs a) {
   const bool take_all = a.n <= K;
   uint32_t* pre = dyn;
 
-  // First-digit histogram into LDS (the global copy is zeroed for the next
-  // call: the scan and the filter are done with it), the other digit
-  // histograms cleared, and the slice prefix built by wave 0 (ns <= 4096).
-  {
-    constexpr int HU = kHistBins / kSelThreads;
-    uint32_t hv[HU];
-#pragma unroll
-    for (int u = 0; u < HU; ++u) hv[u] = a.hist[seg * kHistBins + u * kSelThreads + tid];
-#pragma unroll
-    for (int u = 0; u < HU; ++u) {
-      h[u * kSelThreads + tid] = hv[u];
-      h1[u * kSelThreads + tid] = 0u;
-      a.hist[seg * kHistBins + u * kSelThreads + tid] = 0u;
+  // Wave 0 finds the first digit's bin straight from the scan's histogram,
+  // in registers, then zeroes the global copy for the next call (the scan
+  // and the filter are done with it). Wave 1 builds the slice prefix
+  // (ns <= 4096). Every thread clears the other digits' histograms.
+  if (wv == 0) {
+    u32x4 hv[8];
+    uint32_t* hg = a.hist + seg * kHistBins;
+    first_digit_load(hg, hv);
+    uint32_t beyond = 0;
+    const uint32_t bin = take_all ? 0u : first_digit_search(hv, (uint32_t)K, &beyond);
+    if (lane == 0) {
+      s_bin = (int)bin;
+      s_beyond = beyond;
     }
-    if (tid < 1024) h2[tid] = 0u;
-    if (wv == 0) {
-      uint32_t run = 0;
-      for (int j0 = 0; j0 < ns; j0 += 256) {
-        uint32_t c4[4];
+    const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int j = j0 + u * 64 + lane;
-          c4[u] = j < ns ? a.slice_cnt[seg * ns + j] : 0u;
-        }
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(hg + (kHistBins - 32 - 32 * lane) + 4 * i) = z;
+  } else if (wv == 1) {
+    uint32_t run = 0;
+    for (int j0 = 0; j0 < ns; j0 += 256) {
+      uint32_t c4[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int j = j0 + u * 64 + lane;
-          const uint32_t incl = wave_incl_scan(c4[u]);
-          if (j < ns) pre[j] = run + incl - c4[u];
-          run += __shfl(incl, 63, 64);
-        }
+      for (int u = 0; u < 4; ++u) {
+        const int j = j0 + u * 64 + lane;
+        c4[u] = j < ns ? a.slice_cnt[seg * ns + j] : 0u;
       }
-      if (lane == 0) pre[ns] = run;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = j0 + u * 64 + lane;
+        const uint32_t incl = wave_incl_scan(c4[u]);
+        if (j < ns) pre[j] = run + incl - c4[u];
+        run += __shfl(incl, 63, 64);
+      }
     }
+    if (lane == 0) pre[ns] = run;
   }
+#pragma unroll
+  for (int u = 0; u < kHistBins / kSelThreads; ++u) h1[u * kSelThreads + tid] = 0u;
+  if (tid < 1024) h2[tid] = 0u;
   __syncthreads();
   const uint32_t m = pre[ns];
-  uint32_t need = (uint32_t)K, b0 = 0;
-  if (!take_all) {
-    // digit 0 (bits 31..21): from the scan's histogram
-    if (wv == 0) find_bin_wave<kHistBins, true>(h, (uint32_t)K, &s_bin, &s_beyond);
-    __syncthreads();
-    b0 = (uint32_t)(s_bin < 0 ? 0 : s_bin);
-    need = (uint32_t)K - s_beyond;
-  }
+  // digit 0 (bits 31..21)
+  const uint32_t b0 = take_all ? 0u : (uint32_t)s_bin;
+  const uint32_t need = take_all ? (uint32_t)K : (uint32_t)K - s_beyond;
   if (m <= (uint32_t)a.cache_cap) {
     Cand* cl = reinterpret_cast<Cand*>(dyn + ((ns + 2) & ~1));
     select_rest<true>(a, seg, m, b0, need, take_all, pre, cl, h1, h2, tmp, &s_bin, &s_beyond);
@@ -402,7 +405,7 @@ struct SvArgs {
 };
 
 constexpr int kSvThreads = 256;
-constexpr int kSvRows = 64;
+constexpr int kSvRows = 64;  // chosen rows per workgroup (a multiple of 64)
 
 template <typename T>
 __global__ __launch_bounds__(kSvThreads) void sparse_sv(SvArgs a) {
@@ -421,24 +424,38 @@ __global__ __launch_bounds__(kSvThreads) void sparse_sv(SvArgs a) {
   const int b = (int)(seg / a.Hq), hq = (int)(seg % a.Hq), hkv = hq / a.G;
   const int j0 = split * kSvRows;
   const int nr = min(kSvRows, a.K - j0);
-  // wave 0: the 64 chosen rows of this slice, their maximum and weights
+  // wave 0: the chosen rows of this slice (kSvRows / 64 per lane), their
+  // maximum and weights
   if (w == 0) {
-    int32_t r = -1;
-    float z = -INFINITY;
-    const int j = j0 + lane;
-    if (lane < nr) {
-      if (j < a.k_top) {
-        r = a.sel_row[seg * a.k_top + j];
-        if (r >= 0) z = a.sel_z[seg * a.k_top + j];
-      } else {
-        const int64_t p = a.n + (j - a.k_top);
-        r = (int32_t)pos_to_row(a.tab, p);
-        z = a.scores[seg * a.n_pad + p];
+    constexpr int PL = kSvRows / 64;
+    int32_t r[PL];
+    float z[PL];
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      r[i] = -1;
+      z[i] = -INFINITY;
+      const int jj = 64 * i + lane;
+      const int j = j0 + jj;
+      if (jj < nr) {
+        if (j < a.k_top) {
+          r[i] = a.sel_row[seg * a.k_top + j];
+          if (r[i] >= 0) z[i] = a.sel_z[seg * a.k_top + j];
+        } else {
+          const int64_t p = a.n + (j - a.k_top);
+          r[i] = (int32_t)pos_to_row(a.tab, p);
+          z[i] = a.scores[seg * a.n_pad + p];
+        }
       }
     }
-    const float m = wave_max(z);
-    rows[lane] = r;
-    wts[lane] = (m == -INFINITY || z == -INFINITY) ? 0.f : __expf(z - m);
+    float zm = z[0];
+#pragma unroll
+    for (int i = 1; i < PL; ++i) zm = fmaxf(zm, z[i]);
+    const float m = wave_max(zm);
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      rows[64 * i + lane] = r[i];
+      wts[64 * i + lane] = (m == -INFINITY || z[i] == -INFINITY) ? 0.f : __expf(z[i] - m);
+    }
     if (lane == 0) s_m = m;
   }
   __syncthreads();
@@ -471,7 +488,12 @@ __global__ __launch_bounds__(kSvThreads) void sparse_sv(SvArgs a) {
     part[4 + tid] = o;
   }
   if (w == 0) {
-    const float s = wave_sum(wts[lane]);
+    // the weight sum in a fixed order: lane-strided partial sums, then the
+    // wave reduction
+    float ws = 0.f;
+#pragma unroll
+    for (int i = 0; i < kSvRows / 64; ++i) ws += wts[64 * i + lane];
+    const float s = wave_sum(ws);
     if (lane == 0) {
       part[0] = s_m;
       part[1] = s;
