@@ -25,17 +25,31 @@
 
 namespace stdk {
 
-// Threads 0..127 each hold one query component; returns that component of
-// q / ||q||_2 (0 for a zero query). Same reduction order everywhere.
-STDK_DEV float unit_component(float x, float* tmp2) {
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  float s = (threadIdx.x < kHeadDim) ? x * x : 0.f;
-  s = wave_sum(s);
-  if (lane == 0 && w < 2) tmp2[w] = s;
-  __syncthreads();
-  const float nrm = sqrtf(tmp2[0] + tmp2[1]);
-  __syncthreads();
-  return nrm > 0.f ? x / nrm : 0.f;
+// q / ||q||_2 in one fixed arithmetic order, used wherever a unit query is
+// formed: part j (0..7) covers dims [16j, 16j+16); its squares are summed in
+// dim order, and the norm is the square root of the 8 part sums added in part
+// order. A zero query gives zeros.
+STDK_DEV float sumsq16(const float (&x)[16]) {
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) s = fmaf(x[e], x[e], s);
+  return s;
+}
+STDK_DEV float norm_of_parts(const float* sq) {
+  float t = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) t += sq[j];
+  return sqrtf(t);
+}
+STDK_DEV void load16f(const float* p, float (&x)[16]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 v = *reinterpret_cast<const float4*>(p + 4 * i);
+    x[4 * i] = v.x;
+    x[4 * i + 1] = v.y;
+    x[4 * i + 2] = v.z;
+    x[4 * i + 3] = v.w;
+  }
 }
 
 struct RtSelArgs {
@@ -67,41 +81,71 @@ constexpr int kMaxCache = 64;
 template <bool kLdsBitmap>
 __global__ __launch_bounds__(kRtSelThreads) void retopk_select(RtSelArgs a) {
   extern __shared__ uint32_t dyn[];
-  __shared__ float qb[kHeadDim];
+  constexpr int kGroups = kRtSelThreads / 8;  // cache slots per pass
+  __shared__ float part[kMaxCache][8];
+  __shared__ float sq[8];
   __shared__ float rho[kMaxCache];
   __shared__ int picked[kMaxCache];
-  __shared__ float tmp2[2];
+  __shared__ int slot_of[kMaxCache];
   __shared__ uint32_t tmp[kRtSelThreads / 64 + 1];
-  __shared__ int s_path;
+  __shared__ int s_path, s_npick;
   const int64_t seg = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x;
   const int C = a.C, K = a.K;
   const int hd = a.head[seg], cnt = a.count[seg];
+  const int j = tid & 7, g = tid >> 3;  // part of the 128 dims, cache slot within a pass
 
-  // unit query (fp32)
-  const float qx = (tid < kHeadDim) ? a.q[seg * kHeadDim + tid] : 0.f;
-  const float qn = unit_component(qx, tmp2);
-  if (tid < kHeadDim) {
-    qb[tid] = qn;
-    a.qbar[seg * kHeadDim + tid] = qn;
+  // One memory round trip: every thread requests its 16 query components and
+  // the same components of its cache slots (slot g + 32 * pass).
+  float qx[16];
+  load16f(a.q + seg * kHeadDim + 16 * j, qx);
+  constexpr int kPass = kMaxCache / kGroups;
+  float qh[kPass][16];
+#pragma unroll
+  for (int ps = 0; ps < kPass; ++ps) {
+    const int sl = min(g + kGroups * ps, C - 1);
+    load16f(a.q_hat + (seg * C + sl) * kHeadDim + 16 * j, qh[ps]);
+  }
+  // unit query
+  if (tid < 8) sq[j] = sumsq16(qx);
+  __syncthreads();
+  const float nrm = norm_of_parts(sq);
+  float qn[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) qn[e] = nrm > 0.f ? qx[e] / nrm : 0.f;
+  if (tid < 8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<float4*>(a.qbar + seg * kHeadDim + 16 * j + 4 * i) =
+          make_float4(qn[4 * i], qn[4 * i + 1], qn[4 * i + 2], qn[4 * i + 3]);
+  }
+  // cosines: 16-dim partial dot products, summed in part order below
+#pragma unroll
+  for (int ps = 0; ps < kPass; ++ps) {
+    const int sl = g + kGroups * ps;
+    if (sl < C) {
+      float t = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) t = fmaf(qn[e], qh[ps][e], t);
+      part[sl][j] = t;
+    }
   }
   __syncthreads();
-
-  // cosines with the valid entries (entry of slot s has age (head - s) mod C)
-  for (int s = w; s < C; s += kRtSelThreads / 64) {
-    const float* qh = a.q_hat + (seg * C + s) * kHeadDim;
-    const float part = qh[lane] * qb[lane] + qh[lane + 64] * qb[lane + 64];
-    const float r = wave_sum(part);
-    const int age = (hd - s + C) % C;
-    if (lane == 0) rho[s] = (age < cnt) ? r : -INFINITY;
+  // the entry of slot s has age (head - s) mod C; only the `count` newest are valid
+  if (tid < C) {
+    float r = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) r += part[tid][jj];
+    const int age = (hd - tid + C) % C;
+    rho[tid] = (age < cnt) ? r : -INFINITY;
   }
   __syncthreads();
 
   if (tid == 0) {
     float best = -INFINITY;
-    for (int s = 0; s < C; ++s) {
-      const int age = (hd - s + C) % C;
-      if (age < cnt) best = fmaxf(best, rho[s]);
+    for (int sl = 0; sl < C; ++sl) {
+      const int age = (hd - sl + C) % C;
+      if (age < cnt) best = fmaxf(best, rho[sl]);
     }
     int path;
     if (a.refresh_now) path = 2;
@@ -131,10 +175,10 @@ __global__ __launch_bounds__(kRtSelThreads) void retopk_select(RtSelArgs a) {
     if (age_e < cnt) {
       const float re = rho[tid];
       int rank = 0;
-      for (int s = 0; s < C; ++s) {
-        const int age_f = (hd - s + C) % C;
-        if (age_f >= cnt || s == tid) continue;
-        const float rf = rho[s];
+      for (int sl = 0; sl < C; ++sl) {
+        const int age_f = (hd - sl + C) % C;
+        if (age_f >= cnt || sl == tid) continue;
+        const float rf = rho[sl];
         if (rf > re || (rf == re && age_f < age_e)) ++rank;
       }
       pk = rank < a.R;
@@ -145,19 +189,38 @@ __global__ __launch_bounds__(kRtSelThreads) void retopk_select(RtSelArgs a) {
   uint32_t* bm = kLdsBitmap ? dyn : (a.gbitmap + seg * (int64_t)Wd);
   for (int i = tid; i < Wd; i += kRtSelThreads) bm[i] = 0u;
   __syncthreads();
+  // the picked slots in slot order
+  if (tid == 0) {
+    int np = 0;
+    for (int sl = 0; sl < C; ++sl)
+      if (picked[sl]) slot_of[np++] = sl;
+    s_npick = np;
+  }
+  __syncthreads();
   const int64_t L = a.L_t;
-  for (int s = 0; s < C; ++s) {
-    if (!picked[s]) continue;
-    const int32_t* sp = a.support + (seg * C + s) * (int64_t)K;
-    for (int i = tid; i < K; i += kRtSelThreads) {
-      const int32_t x = sp[i];
-      if (x >= 0 && x < L) atomicOr(&bm[x >> 5], 1u << (x & 31));
+  // union of the picked supports: index f of the flattened R x K list is
+  // entry f % K of picked slot f / K; kU loads per thread are in flight
+  // before their bits are set
+  {
+    constexpr int kU = 8;
+    const int total = s_npick * K;
+    for (int f0 = 0; f0 < total; f0 += kRtSelThreads * kU) {
+      int32_t x[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int f = min(f0 + u * kRtSelThreads + tid, total - 1);
+        x[u] = a.support[(seg * C + slot_of[f / K]) * (int64_t)K + f % K];
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int f = f0 + u * kRtSelThreads + tid;
+        if (f < total && x[u] >= 0 && x[u] < L) atomicOr(&bm[x[u] >> 5], 1u << (x[u] & 31));
+      }
     }
   }
   for (int64_t x = max((int64_t)0, L - a.W) + tid; x < L; x += kRtSelThreads)
     atomicOr(&bm[x >> 5], 1u << (x & 31));
   __syncthreads();
-
   // ascending compaction
   const int per = (Wd + kRtSelThreads - 1) / kRtSelThreads;
   const int w0 = tid * per, w1 = min(Wd, w0 + per);
@@ -403,7 +466,7 @@ struct RtInitArgs {
 };
 
 __global__ __launch_bounds__(256) void retopk_init(RtInitArgs a) {
-  __shared__ float tmp2[2];
+  __shared__ float sq[8];
   const int64_t seg = blockIdx.x;
   const int tid = threadIdx.x;
   const int m = min(a.n, a.C);
@@ -412,9 +475,19 @@ __global__ __launch_bounds__(256) void retopk_init(RtInitArgs a) {
     int32_t* ds = a.support + (seg * a.C + s) * (int64_t)a.K;
     if (s < m) {
       const int64_t src = (int64_t)a.n - m + s;
-      const float x = (tid < kHeadDim) ? a.q_hist[(seg * a.n + src) * kHeadDim + tid] : 0.f;
-      const float u = unit_component(x, tmp2);
-      if (tid < kHeadDim) dq[tid] = u;
+      // the unit query in the same arithmetic order as retopk_select
+      float x[16];
+      if (tid < 8) {
+        load16f(a.q_hist + (seg * a.n + src) * kHeadDim + 16 * tid, x);
+        sq[tid] = sumsq16(x);
+      }
+      __syncthreads();
+      const float nrm = norm_of_parts(sq);
+      if (tid < 8) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) dq[16 * tid + e] = nrm > 0.f ? x[e] / nrm : 0.f;
+      }
+      __syncthreads();
       for (int i = tid; i < a.K; i += 256) ds[i] = a.s_hist[(seg * a.n + src) * (int64_t)a.K + i];
     } else {
       if (tid < kHeadDim) dq[tid] = 0.f;
