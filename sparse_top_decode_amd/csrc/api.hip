@@ -128,6 +128,7 @@ DevInfo g_dev[64];
 
 template <typename T, int G>
 int occ_of() {
+  (void)hipFuncSetAttribute((const void*)k_scan<T, G>, hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
   int nb = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_scan<T, G>, kScanThreads, 0) != hipSuccess || nb < 1) nb = 1;
   return nb;
@@ -305,15 +306,16 @@ int scan_rows_iter(int G) {
 
 template <typename T>
 void launch_scan_t(int G, dim3 grid, hipStream_t s, const ScanArgs& a, hipEvent_t e0, hipEvent_t e1) {
+  const size_t lds = a.stage_stride > 0 ? (size_t)G * a.stage_stride * 4 : 0;
   switch (G) {
-    case 1: STDK_LAUNCH((k_scan<T, 1>), grid, dim3(kScanThreads), 0, s, a); break;
-    case 2: STDK_LAUNCH((k_scan<T, 2>), grid, dim3(kScanThreads), 0, s, a); break;
-    case 3: STDK_LAUNCH((k_scan<T, 3>), grid, dim3(kScanThreads), 0, s, a); break;
-    case 4: STDK_LAUNCH((k_scan<T, 4>), grid, dim3(kScanThreads), 0, s, a); break;
-    case 5: STDK_LAUNCH((k_scan<T, 5>), grid, dim3(kScanThreads), 0, s, a); break;
-    case 6: STDK_LAUNCH((k_scan<T, 6>), grid, dim3(kScanThreads), 0, s, a); break;
-    case 7: STDK_LAUNCH((k_scan<T, 7>), grid, dim3(kScanThreads), 0, s, a); break;
-    default: STDK_LAUNCH((k_scan<T, 8>), grid, dim3(kScanThreads), 0, s, a); break;
+    case 1: STDK_LAUNCH((k_scan<T, 1>), grid, dim3(kScanThreads), lds, s, a); break;
+    case 2: STDK_LAUNCH((k_scan<T, 2>), grid, dim3(kScanThreads), lds, s, a); break;
+    case 3: STDK_LAUNCH((k_scan<T, 3>), grid, dim3(kScanThreads), lds, s, a); break;
+    case 4: STDK_LAUNCH((k_scan<T, 4>), grid, dim3(kScanThreads), lds, s, a); break;
+    case 5: STDK_LAUNCH((k_scan<T, 5>), grid, dim3(kScanThreads), lds, s, a); break;
+    case 6: STDK_LAUNCH((k_scan<T, 6>), grid, dim3(kScanThreads), lds, s, a); break;
+    case 7: STDK_LAUNCH((k_scan<T, 7>), grid, dim3(kScanThreads), lds, s, a); break;
+    default: STDK_LAUNCH((k_scan<T, 8>), grid, dim3(kScanThreads), lds, s, a); break;
   }
 }
 
@@ -366,6 +368,14 @@ int32_t run_exact_select(const Geo& g, const TopkWs& w, char* ws, const float* q
     const int64_t rpb = std::max<int64_t>(ri, rup(cdiv(a.n, per_group), ri));
     a.rows_per_block = rpb;
     a.blocks_per_group = (int32_t)cdiv(a.n, rpb);
+    // stage the scores in LDS when the tile fits beside the histogram (row
+    // stride padded so that the G rows start on different banks)
+    const int64_t stride = rup(rpb, 64) + 16;
+    const size_t stage_bytes = (size_t)g.G * stride * 4;
+    const int occ = di->scan_occ[g.bf16 ? 1 : 0][g.G];
+    if (stage_bytes <= 96 * 1024 &&
+        (size_t)occ * (stage_bytes + (size_t)g.G * kHistBins * 4 + 1024) <= (size_t)di->max_lds)
+      a.stage_stride = (int32_t)stride;
     const dim3 grid((unsigned)(g.groups * a.blocks_per_group));
     STDK_TRY(launch(KID_SCAN, s, [&](hipEvent_t e0, hipEvent_t e1) {
       if (g.bf16) launch_scan_t<uint16_t>(g.G, grid, s, a, e0, e1);

@@ -88,6 +88,8 @@ struct ScanArgs {
   int32_t pad2_;
   const int32_t* head_active;  // [B*Hq] or null; a group with no active head exits
   int64_t n_hist;              // positions below this are counted in the histogram; the rest are scored only
+  int32_t stage_stride;        // > 0: scores are staged in LDS (G rows of this stride) and written at the end
+  int32_t pad3_;
   RangeTab tab;
 };
 
@@ -184,6 +186,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
   constexpr int GP = Sh::GP, LPR = Sh::LPR, NCH = Sh::NCH, EPC = Sh::EPC, E = Sh::E, UR = Sh::UR, V = Sh::V;
   constexpr int RPW = Sh::RPW, ROWB = Sh::ROWB, IT = Sh::ROWS_ITER;
   __shared__ __attribute__((aligned(16))) uint32_t lh[G * kHistBins];
+  extern __shared__ __attribute__((aligned(16))) float sst[];  // staged scores, when a.stage_stride > 0
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int rg = lane / LPR, c = lane % LPR;
@@ -279,8 +282,12 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
     const int64_t p = base + (int64_t)(w * UR + u_out) * RPW + rg;
     if (writer && p < s1) {
       const float val = acc[0] * a.scale;
-      // streaming store: the scores are read once, by the next kernel
-      __builtin_nontemporal_store(val, &a.scores[(seg0 + h_out) * a.n_pad + p]);
+      if (a.stage_stride > 0) {
+        sst[h_out * a.stage_stride + (p - p_beg)] = val;
+      } else {
+        // streaming store: the scores are read once, by the next kernel
+        __builtin_nontemporal_store(val, &a.scores[(seg0 + h_out) * a.n_pad + p]);
+      }
       if (p < a.n_hist) atomicAdd(&lh[h_out * kHistBins + (f2key(val) >> (32 - kHistBits))], 1u);
     }
   };
@@ -306,6 +313,30 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
     if (more) issue(s0, kw[0]);
   }
   __syncthreads();
+  // Staged scores: the workgroup's tile goes out once its reads are done,
+  // in whole 16-byte stores (positions [p_beg, p_end) of every head; p_beg
+  // and the rows' starts are multiples of 4 floats).
+  if (a.stage_stride > 0) {
+    const int64_t len = p_end - p_beg;
+    const int64_t nv = (len + 3) / 4;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      if (!((act >> h) & 1u)) continue;
+      float* dst = a.scores + (seg0 + h) * a.n_pad + p_beg;
+      const float* srcp = sst + h * a.stage_stride;
+      for (int64_t i = tid; i < nv; i += kScanThreads) {
+        typedef float f32x4 __attribute__((ext_vector_type(4)));
+        const f32x4 v = *reinterpret_cast<const f32x4*>(srcp + 4 * i);
+        if (4 * i + 3 < len) {
+          __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst + 4 * i));
+        } else {
+          const float e[4] = {v.x, v.y, v.z, v.w};
+          for (int k = 0; k < 4; ++k)
+            if (4 * i + k < len) dst[4 * i + k] = e[k];
+        }
+      }
+    }
+  }
   // Add the block histogram to the global one: all LDS reads of a thread are
   // issued before the first wait, then one atomic per non-empty bin. Heads
   // that do not take part are skipped, so their global bins stay zero.
