@@ -113,6 +113,7 @@ constexpr int kDenseMaxWg = 32;  // workgroups per KV head on the dense path
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t rup(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 inline size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
+constexpr int kScanStageMax = 96 * 1024;  // LDS bytes for staged scores
 
 // ---------------------------------------------------------------------------
 // device limits (per device, queried once)
@@ -128,7 +129,7 @@ DevInfo g_dev[64];
 
 template <typename T, int G>
 int occ_of() {
-  (void)hipFuncSetAttribute((const void*)k_scan<T, G>, hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+  (void)hipFuncSetAttribute((const void*)k_scan<T, G>, hipFuncAttributeMaxDynamicSharedMemorySize, kScanStageMax);
   int nb = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_scan<T, G>, kScanThreads, 0) != hipSuccess || nb < 1) nb = 1;
   return nb;
@@ -368,14 +369,16 @@ int32_t run_exact_select(const Geo& g, const TopkWs& w, char* ws, const float* q
     const int64_t rpb = std::max<int64_t>(ri, rup(cdiv(a.n, per_group), ri));
     a.rows_per_block = rpb;
     a.blocks_per_group = (int32_t)cdiv(a.n, rpb);
-    // stage the scores in LDS when the tile fits beside the histogram (row
-    // stride padded so that the G rows start on different banks)
-    const int64_t stride = rup(rpb, 64) + 16;
-    const size_t stage_bytes = (size_t)g.G * stride * 4;
+    // stage the scores in LDS, in chunks of whole iterations that fit
+    // beside the histogram (row stride padded so that the G rows start on
+    // different banks)
     const int occ = di->scan_occ[g.bf16 ? 1 : 0][g.G];
-    if (stage_bytes <= 96 * 1024 &&
-        (size_t)occ * (stage_bytes + (size_t)g.G * kHistBins * 4 + 1024) <= (size_t)di->max_lds)
-      a.stage_stride = (int32_t)stride;
+    const int64_t lds_free = std::min<int64_t>(kScanStageMax, (int64_t)di->max_lds / occ - (int64_t)g.G * kHistBins * 4 - 1024);
+    const int64_t chunk = std::min<int64_t>(rpb, (lds_free / (4 * g.G) - 16) / ri * ri);
+    if (chunk >= ri) {
+      a.stage_rows = (int32_t)chunk;
+      a.stage_stride = (int32_t)(rup(chunk, 64) + 16);
+    }
     const dim3 grid((unsigned)(g.groups * a.blocks_per_group));
     STDK_TRY(launch(KID_SCAN, s, [&](hipEvent_t e0, hipEvent_t e1) {
       if (g.bf16) launch_scan_t<uint16_t>(g.G, grid, s, a, e0, e1);

@@ -88,8 +88,8 @@ struct ScanArgs {
   int32_t pad2_;
   const int32_t* head_active;  // [B*Hq] or null; a group with no active head exits
   int64_t n_hist;              // positions below this are counted in the histogram; the rest are scored only
-  int32_t stage_stride;        // > 0: scores are staged in LDS (G rows of this stride) and written at the end
-  int32_t pad3_;
+  int32_t stage_stride;        // > 0: scores are staged in LDS (G rows of this stride) and written in chunks
+  int32_t stage_rows;          // positions per staged chunk (a multiple of the rows per iteration)
   RangeTab tab;
 };
 
@@ -265,7 +265,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
   __builtin_amdgcn_s_barrier();
   __asm__ volatile("" ::: "memory");
 
-  auto consume = [&](int64_t base, const u32x4 (&kv)[UR][NCH]) {
+  auto consume = [&](int64_t base, int64_t cstart, const u32x4 (&kv)[UR][NCH]) {
     float acc[V];
 #pragma unroll
     for (int j = 0; j < V; ++j) {
@@ -283,7 +283,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
     if (writer && p < s1) {
       const float val = acc[0] * a.scale;
       if (a.stage_stride > 0) {
-        sst[h_out * a.stage_stride + (p - p_beg)] = val;
+        sst[h_out * a.stage_stride + (p - cstart)] = val;
       } else {
         // streaming store: the scores are read once, by the next kernel
         __builtin_nontemporal_store(val, &a.scores[(seg0 + h_out) * a.n_pad + p]);
@@ -291,10 +291,37 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
       if (p < a.n_hist) atomicAdd(&lh[h_out * kHistBins + (f2key(val) >> (32 - kHistBits))], 1u);
     }
   };
+  // Staged scores: a chunk of the piece's positions [c0, c1) goes out once
+  // every wave has scored it, as coalesced non-temporal stores; LDS-only
+  // barriers around it keep the key loads in flight.
+  auto flush = [&](int64_t c0, int64_t c1) {
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    const int len = (int)(c1 - c0);
+    // rows start on 64-float boundaries, so a chunk that starts on a multiple
+    // of 4 positions goes out in 16-byte stores
+    const int nvec = (c0 & 3) == 0 ? len / 4 : 0;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      if (!((act >> h) & 1u)) continue;
+      float* dst = a.scores + (seg0 + h) * a.n_pad + c0;
+      const float* srcp = sst + h * a.stage_stride;
+      typedef float f32x4 __attribute__((ext_vector_type(4)));
+      for (int i = tid; i < nvec; i += kScanThreads)
+        __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(srcp + 4 * i),
+                                    reinterpret_cast<f32x4*>(dst + 4 * i));
+      for (int i = 4 * nvec + tid; i < len; i += kScanThreads) __builtin_nontemporal_store(srcp[i], dst + i);
+    }
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+  };
+  const bool staged = a.stage_stride > 0;
   while (more) {
     // two register sets; the scheduling barriers keep each set's loads ahead
     // of the arithmetic on the other set
-    int64_t base = s0;
+    int64_t base = s0, cstart = s0;
     bool done = false;
     while (!done) {
 #pragma unroll
@@ -302,10 +329,14 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
         if (!done) {
           issue(base + IT, kw[st ^ 1]);
           __builtin_amdgcn_sched_barrier(0);
-          consume(base, kw[st]);
+          consume(base, cstart, kw[st]);
           __builtin_amdgcn_sched_barrier(0);
           base += IT;
           done = base >= s1;
+          if (staged && (done || base - cstart >= a.stage_rows)) {
+            flush(cstart, min(base, s1));
+            cstart = base;
+          }
         }
       }
     }
@@ -313,30 +344,6 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
     if (more) issue(s0, kw[0]);
   }
   __syncthreads();
-  // Staged scores: the workgroup's tile goes out once its reads are done,
-  // in whole 16-byte stores (positions [p_beg, p_end) of every head; p_beg
-  // and the rows' starts are multiples of 4 floats).
-  if (a.stage_stride > 0) {
-    const int64_t len = p_end - p_beg;
-    const int64_t nv = (len + 3) / 4;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      if (!((act >> h) & 1u)) continue;
-      float* dst = a.scores + (seg0 + h) * a.n_pad + p_beg;
-      const float* srcp = sst + h * a.stage_stride;
-      for (int64_t i = tid; i < nv; i += kScanThreads) {
-        typedef float f32x4 __attribute__((ext_vector_type(4)));
-        const f32x4 v = *reinterpret_cast<const f32x4*>(srcp + 4 * i);
-        if (4 * i + 3 < len) {
-          __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst + 4 * i));
-        } else {
-          const float e[4] = {v.x, v.y, v.z, v.w};
-          for (int k = 0; k < 4; ++k)
-            if (4 * i + k < len) dst[4 * i + k] = e[k];
-        }
-      }
-    }
-  }
   // Add the block histogram to the global one: all LDS reads of a thread are
   // issued before the first wait, then one atomic per non-empty bin. Heads
   // that do not take part are skipped, so their global bins stay zero.
