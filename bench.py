@@ -19,7 +19,10 @@ The other workloads are measured the same way when asked for:
   --config 3  ReTopK, Qwen2.5-7B-shaped (28 q / 4 KV heads), 65,536 initial
               rows, K=512, C=32, R=4, W=32, tau=0.85, refresh 128: the cache
               is warmed with 32 exact queries, then every timed pass runs the
-              256 decode steps (one row appended per step) from that state;
+              256 decode steps (one row appended per step) from that state.
+              --requests B serves B independent requests per step (their own
+              caches); --tau and --top-k select the pages' variants (0.90,
+              1024);
   --config 4  batch of 16 sequences x 32,768 rows, K=1024, one
               topk_attn_decode call per step;
   --config 5  1,048,576 rows, K=8192, static window of 640 rows, one-pass step.
@@ -146,8 +149,9 @@ def cpu_baseline_retopk(w, p, q_hist, sup_hist, budget_s: float = 12.0):
             break
     el = time.perf_counter() - t0
     return dict(value=steps / el, unit="steps/s", cores=1, kind="oracle",
-                sample=f"the first {steps} of the {p['steps']} timed ReTopK steps (all 28 query heads, from the "
-                       f"same warmed cache), {el:.1f} s on one host thread (numpy fp64, no BLAS)")
+                sample=f"the first {steps} of the {p['steps']} timed ReTopK steps (all {w.q.shape[0]} x 28 (request, "
+                       f"query head) pairs, from the same warmed cache), {el:.1f} s on one host thread (numpy fp64, "
+                       f"no BLAS)")
 
 
 # ---------------------------------------------------------------------------
@@ -354,8 +358,12 @@ def bench_retopk(args):
     from sparse_top_decode_amd import ops
     from workloads import make_workload
 
-    w = make_workload(3)
-    p = w.retopk
+    w = make_workload(3, B=args.requests)
+    p = dict(w.retopk)
+    if args.tau is not None:
+        p["tau"] = args.tau
+    if args.top_k is not None:
+        p["top_k"] = args.top_k
     dev, k, v = to_dev(w)
     K, warm, n_steps, L0 = p["top_k"], p["warmup"], p["steps"], p["L0"]
     rt = ops.Retopk(k, w.H_q, top_k=K, cache_cap=p["cache_cap"], top_r=p["top_r"], recent=p["recent"],
@@ -404,7 +412,8 @@ def bench_retopk(args):
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline_retopk(w, p, q_hist.cpu().numpy(), sup_hist.cpu().numpy())
-    workload = (f"ReTopK decode, Qwen2.5-7B-shaped layer: 28 q / 4 KV heads, d=128, {L0} initial rows + 1 per step, "
+    workload = (f"ReTopK decode, Qwen2.5-7B-shaped layer: {B} request(s) per step, 28 q / 4 KV heads, d=128, "
+                f"{L0} initial rows + 1 per step, "
                 f"bf16 K/V, K={K}, C={p['cache_cap']}, R={p['top_r']}, W={p['recent']}, tau={p['tau']}, "
                 f"refresh every {p['refresh']} steps, AR(1) queries; {n_steps} steps per timed pass")
     extra = {"batch": B, "seq_len": L0, "top_k": K, "kv_cache": "bf16", "parallelism": "none (1 GPU)",
@@ -422,6 +431,9 @@ def main():
                     help="workload: 2 (default, the headline), 3 ReTopK, 4 batched, 5 1M rows")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--requests", type=int, default=1, help="workload 3: requests served per step, each with its own caches")
+    ap.add_argument("--tau", type=float, default=None, help="workload 3: similarity threshold (default 0.85)")
+    ap.add_argument("--top-k", type=int, default=None, help="workload 3: K (default 512)")
     ap.add_argument("--L", type=int, default=131072, help="cache length of workload 2")
     ap.add_argument("--layers", type=int, default=4,
                     help="workload 2: distinct K/V caches used in turn, one per layer (1 = the same cache every "

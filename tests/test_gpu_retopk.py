@@ -138,6 +138,20 @@ def test_retopk_always_exact_equals_topk(ops):
         assert torch.equal(out["o"], o) and torch.equal(out["lse"], lse)
 
 
+@pytest.mark.parametrize("B,tau,K,L", [(3, 0.90, 128, 8192), (1, 0.85, 1024, 16384)])
+def test_retopk_serving_variants(ops, B, tau, K, L):
+    """Serving-shaped steps: several requests in one call, each with its own
+    caches, at the pages' stricter threshold (tau = 0.90), and the K = 1024
+    budget of the cross-model runs; c3's head layout, C=32, R=4, W=32."""
+    w = make_workload(3, L=L, steps=24, warm=32, B=B)
+    p = ref.RetopkParams(top_k=K, cache_cap=32, top_r=4, recent=32, tau=tau, refresh=16)
+    heads = [(b, h) for b in range(B) for h in (0, 6, 13, 20, 27)]
+    s = run_lockstep(ops, w, p, 24, heads, n_warm=32)
+    log(f"retopk B={B} tau={tau} K={K}: reuse {s['reuse']} exact {s['exact']} flagged {s['flagged']} "
+        f"mean M {np.mean(s['cand']) if s['cand'] else 0:.0f} band swaps {s['swaps']}")
+    assert s["reuse"] + s["exact"] > 0
+
+
 @pytest.mark.slow
 def test_retopk_c3_full_lockstep(ops):
     """c3 at full size (L0 = 65536, K=512, C=32, R=4, W=32, tau=0.85,

@@ -194,8 +194,10 @@ def _c2(L: int) -> Workload:
                     1.0 / math.sqrt(HEAD_DIM), q, k, v, dynamic, static_ranges=static)
 
 
-def _c3(L: int, steps: int = 256, warm: int = 32) -> Workload:
-    cfg, B, Hq, Hkv = 3, 1, 28, 4
+def _c3(L: int, steps: int = 256, warm: int = 32, B: int = 1) -> Workload:
+    """B > 1: independent requests (their own query streams and K/V rows),
+    one ReTopK cache per (request, query head)."""
+    cfg, Hq, Hkv = 3, 28, 4
     L_max = L + steps
     k, v = _fill_kv(cfg, B, Hkv, L_max, "bf16")
     rng = np.random.default_rng([1000 + cfg, T_QUERY, 0, 0])
@@ -209,7 +211,8 @@ def _c3(L: int, steps: int = 256, warm: int = 32) -> Workload:
         seq[:, :, t] = cur
     params = dict(top_k=512, cache_cap=32, top_r=4, recent=32, tau=0.85, refresh=128,
                   warmup=warm, steps=steps, L0=L)
-    return Workload(f"c3_qwen25_7b_retopk_L{L}", cfg, B, Hq, Hkv, HEAD_DIM, L, L_max, "bf16", 512,
+    name = f"c3_qwen25_7b_retopk_L{L}" + (f"_B{B}" if B > 1 else "")
+    return Workload(name, cfg, B, Hq, Hkv, HEAD_DIM, L, L_max, "bf16", 512,
                     1.0 / math.sqrt(HEAD_DIM), seq, k, v, [(0, L)], retopk=params)
 
 
