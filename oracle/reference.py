@@ -170,6 +170,32 @@ def topk_attn_decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
 
 
 # --------------------------------------------------------------------------
+# multi-query exact top-K: the index sets of a block of queries, each the
+# exact TopK of its own scores over the ranges ([RT] "Exact Top-K 的隐藏成本":
+# S_t = TopK(e, K); "核心方法" 1: the cache holds the supports of the last
+# prefill queries; [RA] "CPU-GPU Co-Execution Architecture": the key index is
+# built from the prefill queries' nearest keys)
+# --------------------------------------------------------------------------
+def topk_multi_query(q: np.ndarray, k_cache: np.ndarray, ranges: Sequence[Tuple[int, int]], top_k: int,
+                     scale: float, queries: Optional[Sequence[Tuple[int, int, int]]] = None) -> Dict:
+    """q: [B, H_q, M, d] fp32. Returns idx [B, H_q, M, K] (ascending rows, -1
+    padded) and zk [B, H_q, M] (the K-th score). ``queries`` restricts the
+    work to the listed (b, h_q, m) triples (the other entries stay -2 / NaN)."""
+    B, Hq, M, d = q.shape
+    G = Hq // k_cache.shape[1]
+    rows = range_rows(ranges)
+    K = int(top_k)
+    idx = np.full((B, Hq, M, K), -2, dtype=np.int32)
+    zk = np.full((B, Hq, M), np.nan)
+    todo = queries if queries is not None else [(b, h, m) for b in range(B) for h in range(Hq) for m in range(M)]
+    for b, h, m in todo:
+        z = scores(q[b, h, m], k_cache[b, h // G], rows, scale)
+        sel, zk[b, h, m] = select_topk(z, rows, K)
+        idx[b, h, m] = pad_rows(sel, K)
+    return dict(idx=idx, zk=zk)
+
+
+# --------------------------------------------------------------------------
 # combination of two partial outputs   ([RA] Eq. 4-5; [RA-pc] appendix B.1)
 # --------------------------------------------------------------------------
 def attn_merge_lse(o_a: np.ndarray, lse_a: np.ndarray, o_b: np.ndarray, lse_b: np.ndarray):

@@ -235,6 +235,38 @@ def pin_brute_topk(ref, seed=0):
             assert abs(out["lse"][0, 0] - bf["lse"]) < 1e-10
 
 
+def pin_brute_multi_query(ref, seed=0):
+    """Multi-query top-K == pure-Python brute force per (b, h_q, m), on tiny
+    inputs with two KV heads (G = 2), several queries, duplicated key rows
+    (exact ties) and split ranges."""
+    rng = np.random.default_rng([83, seed])
+    for trial in range(6):
+        B, Hkv, G, M = int(rng.integers(1, 3)), 2, 2, 3
+        n = int(rng.integers(2, 30))
+        d = int(rng.integers(1, 7))
+        k = rng.standard_normal((B, Hkv, n, d)).astype(np.float32)
+        for _ in range(int(rng.integers(0, 5))):
+            b, h = int(rng.integers(0, B)), int(rng.integers(0, Hkv))
+            i, j = rng.integers(0, n, 2)
+            k[b, h, i] = k[b, h, j]
+        q = rng.standard_normal((B, Hkv * G, M, d)).astype(np.float32)
+        cut = int(rng.integers(0, n + 1))
+        ranges = [(0, cut), (cut + 1, n)] if 0 < cut < n - 1 else [(0, n)]
+        K = int(rng.integers(1, n + 2))
+        sc = float(rng.uniform(0.1, 1.0))
+        out = ref.topk_multi_query(q, k, ranges, K, sc)
+        rows = [r for b0, e in ranges for r in range(b0, e)]
+        for b in range(B):
+            for h in range(Hkv * G):
+                for m in range(M):
+                    kk = [[float(x) for x in k[b, h // G, r]] for r in rows]
+                    z = [brute.dot([float(x) for x in q[b, h, m]], row) * sc for row in kk]
+                    want = brute.topk_members(z, rows, K)
+                    got = [int(x) for x in out["idx"][b, h, m] if x >= 0]
+                    assert got == want, (trial, b, h, m, got, want)
+                    assert all(int(x) == -1 for x in out["idx"][b, h, m][len(want):])
+
+
 def pin_brute_gamma(ref, seed=0):
     """The (o, lse) combination equals the pages' gamma_1 o_W + gamma_2 o_Omega
     computed from the raw scores (brute force of Eq. 3-5)."""
@@ -436,5 +468,5 @@ ALL_PINS = [
     pin_golden_topk, pin_golden_merge, pin_golden_retopk, pin_dense_matches_library_attention,
     pin_split_merge_identity, pin_shift_invariance, pin_argmax_and_weights, pin_brute_topk,
     pin_brute_gamma, pin_merge_algebra, pin_retopk_invariants, pin_retopk_special_cases,
-    pin_retopk_brute,
+    pin_retopk_brute, pin_brute_multi_query,
 ]

@@ -92,6 +92,23 @@ def m_no_normalisation(q):
     return np.asarray(q, dtype=np.float32)
 
 
+_orig_multi = ref.topk_multi_query
+
+
+def m_multi_head_mapping(q, k_cache, ranges, top_k, scale, queries=None):
+    """query head h read against KV head h mod H_kv instead of h // G"""
+    B, Hq, M, d = q.shape
+    Hkv = k_cache.shape[1]
+    perm = np.concatenate([k_cache[:, [h % Hkv]] for h in range(Hq)], axis=1)
+    return _orig_multi(q, np.ascontiguousarray(perm), ranges, top_k, scale, queries)
+
+
+def m_multi_first_query_only(q, k_cache, ranges, top_k, scale, queries=None):
+    """every query of the block gets the first query's set"""
+    q0 = np.repeat(q[:, :, :1], q.shape[2], axis=2)
+    return _orig_multi(q0, k_cache, ranges, top_k, scale, queries)
+
+
 MUTANTS = [
     ("softmax_v", m_no_renormalisation),
     ("select_topk", m_ties_to_highest),
@@ -103,6 +120,8 @@ MUTANTS = [
     ("retopk_head_step", m_no_recent_window),
     ("retopk_head_step", m_topr_least_similar),
     ("unit_query_f32", m_no_normalisation),
+    ("topk_multi_query", m_multi_head_mapping),
+    ("topk_multi_query", m_multi_first_query_only),
 ]
 
 
