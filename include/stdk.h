@@ -150,6 +150,47 @@ size_t topk_attn_decode_static_workspace_size(const stdk_layout* lay, int64_t n_
                                               int64_t n_static, int32_t top_k);
 
 /* ------------------------------------------------------------------------
+ * topk_multi_query — the exact Top-K of [RT] ("Exact Top-K 的隐藏成本": TopK
+ * over every score) for a block of queries per head at once: the supports
+ * of the last prefill queries that start the ReTopK cache ([RT] 核心方法 1),
+ * and the exact nearest keys of each prefill query that [RA] "Attention-Aware
+ * ANNS Index Construction" starts from. No attention output.
+ *
+ * For every (b, h_q, m): z_i = scale * q[b][h_q][m] . k[b][h_kv][i] over the
+ * rows i of `ranges`; S = the top_k rows of largest z (ties go to the lowest
+ * row); all rows when top_k >= n.
+ *
+ *  q          [B][H_q][n_queries][128] fp32, 16-byte aligned, finite.
+ *  n_queries  M >= 1 queries per query head; H_q / H_kv * M <= 8,388,480.
+ *  ranges, n_ranges   as topk_attn_decode.
+ *  top_k      1..65536 (STDK_EUNSUPPORTED above).
+ *  idx_out    [B][H_q][M][top_k] int32, required: S ascending, -1 padded
+ *             when n < top_k.
+ *  z_out      [B][H_q][M][top_k] fp32 or NULL: the scores of the rows in
+ *             idx_out, -inf in the padding.
+ *  workspace  at least topk_multi_query_workspace_size(lay, M, n, top_k)
+ *             bytes, 256-byte aligned. Its first B * n_q_heads * M * 8192
+ *             bytes follow the "Workspace state" rule above (zero before the
+ *             first call, left zero by every call that returns STDK_OK).
+ *             Not read when n = 0.
+ *  Limits: B * n_kv_heads <= 65535.
+ * The scores are computed on the bf16 matrix cores with every fp32 query
+ * element split into a bf16 value and a bf16 remainder (and every fp32 key
+ * likewise); they differ from an fp32 dot product by about
+ * 2^-16 * scale * sum_j |q_j k_j| plus the accumulation rounding, so rows
+ * whose scores lie that close to the K-th score may be exchanged.
+ * ---------------------------------------------------------------------- */
+int32_t topk_multi_query(const stdk_layout* lay, const float* q, int32_t n_queries,
+                         const void* k_cache, const int64_t* ranges, int32_t n_ranges,
+                         int32_t top_k, float scale, int32_t* idx_out, float* z_out,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace topk_multi_query needs for n_queries queries per head
+ * and n_scan rows. */
+size_t topk_multi_query_workspace_size(const stdk_layout* lay, int32_t n_queries, int64_t n_scan,
+                                       int32_t top_k);
+
+/* ------------------------------------------------------------------------
  * attn_merge_lse — [RA] Eq. 4-5: combination of two partial attention
  * outputs over disjoint row sets a and b:
  *     M = max(lse_a, lse_b),  lse = M + ln(e^{lse_a - M} + e^{lse_b - M}),
@@ -248,10 +289,11 @@ int32_t stdk_version(void);        /* STDK_VERSION */
  * `capacity` bounds the number of launches recorded (events are created when
  * enabling, not on the hot path). stdk_profile_read waits for the recorded
  * events and returns, for the kernel family `name`, the summed duration in
- * milliseconds and the launch count. Families: "ws_clear", "k_scan",
+ * milliseconds and the launch count. Families: "k_scan",
  * "topk_filter", "topk_select", "sparse_sv", "dense_attn", "combine",
  * "attn_merge", "fill_empty", "retopk_select", "retopk_rerank",
- * "retopk_rerank_select", "retopk_push", "retopk_init". Unknown names return
+ * "retopk_rerank_select", "retopk_push", "retopk_init", "mq_blockmax",
+ * "mq_threshold", "mq_collect", "mq_fill". Unknown names return
  * STDK_EINVAL. */
 int32_t stdk_profile_enable(int32_t capacity, const char* only);
 int32_t stdk_profile_disable(void);

@@ -16,6 +16,7 @@
 #include "stdk.h"  // include/ (on the include path)
 #include "attend_kernels.h"
 #include "device.h"
+#include "mq_kernels.h"
 #include "retopk_kernels.h"
 #include "scan_kernels.h"
 #include "select_kernels.h"
@@ -55,12 +56,14 @@ int32_t ok() {
 // ---------------------------------------------------------------------------
 enum KernelId {
   KID_SCAN, KID_FILTER, KID_SELECT, KID_SV, KID_DENSE, KID_COMBINE, KID_MERGE, KID_FILL,
-  KID_RT_SELECT, KID_RT_RERANK, KID_RT_RSEL, KID_RT_PUSH, KID_RT_INIT, KID_COUNT
+  KID_RT_SELECT, KID_RT_RERANK, KID_RT_RSEL, KID_RT_PUSH, KID_RT_INIT, KID_MQ_BLOCKMAX, KID_MQ_THRESH,
+  KID_MQ_COLLECT, KID_MQ_FILL, KID_COUNT
 };
 const char* const kKernelNames[KID_COUNT] = {
     "k_scan",        "topk_filter",   "topk_select",          "sparse_sv",
     "dense_attn",  "combine",       "attn_merge",    "fill_empty",           "retopk_select",
-    "retopk_rerank", "retopk_rerank_select", "retopk_push", "retopk_init"};
+    "retopk_rerank", "retopk_rerank_select", "retopk_push", "retopk_init", "mq_blockmax",
+    "mq_threshold",  "mq_collect",    "mq_fill"};
 
 struct Profiler {
   std::mutex mu;
@@ -496,6 +499,121 @@ int32_t run_dense(const Geo& g, const TopkWs& w, char* ws, const float* q, const
   return run_combine(w, ws, a.nwg, o_out, lse_out, s);
 }
 
+// ---------------------------------------------------------------------------
+// multi-query exact top-K: workspace and dispatch
+// ---------------------------------------------------------------------------
+// [hist (zero between calls)] [block maxima] [thresholds] [candidate lists]
+// [spilled candidates] [slice counts] [chosen rows] [their scores]
+struct MqWs {
+  int64_t S, n, n_pad, K, nblk, chunk, nchunk, packs;
+  size_t hist, bmax, thr, list, clist, slice_cnt, sel_row, sel_z, total;
+};
+
+constexpr int kMqTargetWg = 512;   // workgroups per pass (2 per CU on 256 CUs)
+constexpr int kMqSelCache = 8192;  // candidates per query kept in the select's LDS
+
+// The chunking depends on the shapes only, so the workspace size does too.
+MqWs mq_ws(const Geo& g, int64_t M, int64_t n, int64_t K) {
+  MqWs w{};
+  w.S = g.S * M;
+  w.n = n;
+  w.K = K;
+  w.n_pad = rup(std::max<int64_t>(n, 1), 64);
+  w.nblk = cdiv(std::max<int64_t>(n, 1), kMqBlock);
+  const int64_t rows_per_pack = (int64_t)kMqWaves * (g.bf16 ? MqShape<uint16_t>::QT : MqShape<float>::QT) * 32;
+  w.packs = cdiv((int64_t)g.G * M, rows_per_pack);
+  int64_t nchunk = std::max<int64_t>(1, cdiv(kMqTargetWg, g.groups * w.packs));
+  nchunk = std::min<int64_t>(nchunk, w.nblk);
+  w.chunk = std::max<int64_t>(rup(cdiv(std::max<int64_t>(n, 1), nchunk), kMqBlock), rup(cdiv(std::max<int64_t>(n, 1), kMqMaxChunks), kMqBlock));
+  w.nchunk = cdiv(std::max<int64_t>(n, 1), w.chunk);
+  size_t off = 0;
+  w.hist = off;
+  off = al256(off + (size_t)w.S * kHistBins * 4);
+  w.bmax = off;
+  off = al256(off + (size_t)w.S * w.nblk * 4);
+  w.thr = off;
+  off = al256(off + (size_t)w.S * 4);
+  w.list = off;
+  off = al256(off + (size_t)w.S * w.n_pad * sizeof(Cand));
+  w.clist = off;
+  off = al256(off + (size_t)w.S * w.n_pad * sizeof(Cand));
+  w.slice_cnt = off;
+  off = al256(off + (size_t)w.S * w.nchunk * 4);
+  w.sel_row = off;
+  off = al256(off + (size_t)w.S * K * 4);
+  w.sel_z = off;
+  off = al256(off + (size_t)w.S * K * 4);
+  w.total = off;
+  return w;
+}
+
+int32_t run_multi_query(const Geo& g, const MqWs& w, char* ws, const float* q, int32_t M, const void* k_cache,
+                        const RangeTab& tab, float scale, int32_t* idx_out, float* z_out, const DevInfo* di,
+                        hipStream_t s) {
+  MqArgs a{};
+  a.q = q;
+  a.k = (const char*)k_cache;
+  a.stride_b_bytes = g.sb_bytes;
+  a.stride_h_bytes = g.sh_bytes;
+  a.n = w.n;
+  a.n_pad = w.n_pad;
+  a.M = M;
+  a.G = g.G;
+  a.Hq = g.Hq;
+  a.Hkv = g.Hkv;
+  a.rows = g.G * M;
+  a.chunk = (int32_t)w.chunk;
+  a.nchunk = (int32_t)w.nchunk;
+  a.nblk = (int32_t)w.nblk;
+  a.scale = scale;
+  a.bmax = (float*)(ws + w.bmax);
+  a.thr = (const uint32_t*)(ws + w.thr);
+  a.hist = (uint32_t*)(ws + w.hist);
+  a.list = (Cand*)(ws + w.list);
+  a.slice_cnt = (uint32_t*)(ws + w.slice_cnt);
+  a.tab = tab;
+  const dim3 grid((unsigned)w.nchunk, (unsigned)g.groups, (unsigned)w.packs);
+  STDK_TRY(launch(KID_MQ_BLOCKMAX, s, [&](hipEvent_t e0, hipEvent_t e1) {
+    if (g.bf16) STDK_LAUNCH(mq_blockmax<uint16_t>, grid, dim3(kMqThreads), 0, s, a);
+    else STDK_LAUNCH(mq_blockmax<float>, grid, dim3(kMqThreads), 0, s, a);
+  }));
+  {
+    MqThreshArgs t{(const float*)(ws + w.bmax), (uint32_t*)(ws + w.thr), w.n, (int32_t)w.nblk, (int32_t)w.K};
+    STDK_TRY(launch(KID_MQ_THRESH, s, [&](hipEvent_t e0, hipEvent_t e1) {
+      STDK_LAUNCH(mq_threshold, dim3((unsigned)w.S), dim3(kMqThreshThreads), 0, s, t);
+    }));
+  }
+  STDK_TRY(launch(KID_MQ_COLLECT, s, [&](hipEvent_t e0, hipEvent_t e1) {
+    if (g.bf16) STDK_LAUNCH(mq_collect<uint16_t>, grid, dim3(kMqThreads), 0, s, a);
+    else STDK_LAUNCH(mq_collect<float>, grid, dim3(kMqThreads), 0, s, a);
+  }));
+  {
+    SelectArgs sa{};
+    sa.hist = (uint32_t*)(ws + w.hist);
+    sa.list = (const Cand*)(ws + w.list);
+    sa.slice_cnt = (const uint32_t*)(ws + w.slice_cnt);
+    sa.clist = (Cand*)(ws + w.clist);
+    sa.n = w.n;
+    sa.n_pad = w.n_pad;
+    sa.K = (int32_t)w.K;
+    sa.slice = (int32_t)w.chunk;
+    sa.nslice = (int32_t)w.nchunk;
+    sa.sel_row = idx_out;
+    sa.sel_z = z_out ? z_out : (float*)(ws + w.sel_z);
+    sa.idx_out = nullptr;
+    sa.seg_active = nullptr;
+    sa.tab = tab;
+    const size_t pre_bytes = (size_t)((w.nchunk + 2) & ~1LL) * 4;
+    const size_t avail = (size_t)di->max_lds - kSelStaticLds;
+    const size_t dyn = std::min(avail, pre_bytes + (size_t)std::min<int64_t>(w.n, kMqSelCache) * sizeof(Cand));
+    sa.cache_cap = (int32_t)((dyn - pre_bytes) / sizeof(Cand));
+    STDK_TRY(launch(KID_SELECT, s, [&](hipEvent_t e0, hipEvent_t e1) {
+      STDK_LAUNCH(topk_select, dim3((unsigned)w.S), dim3(kSelThreads), dyn, s, sa);
+    }));
+  }
+  return STDK_OK;
+}
+
 // Host-side validation of one ascending, disjoint list of [begin, end) ranges.
 int32_t check_ranges(const stdk_layout* lay, const int64_t* ranges, int32_t n_ranges, const char* what) {
   if (n_ranges < 0 || n_ranges > STDK_MAX_RANGES)
@@ -644,6 +762,48 @@ int32_t topk_attn_decode_static(const stdk_layout* lay, const float* q, const vo
   }
   STDK_TRY(run_exact_select(g, w, ws, q, k_cache, tab, scale, nullptr, idx_out, di, s));
   STDK_TRY(run_sv(g, w, ws, v_cache, o_out, lse_out, s, &tab));
+  return ok();
+}
+
+size_t topk_multi_query_workspace_size(const stdk_layout* lay, int32_t n_queries, int64_t n_scan, int32_t top_k) {
+  if (check_layout(lay) != STDK_OK || n_queries < 1 || n_scan < 0 || top_k < 1) return 0;
+  return mq_ws(geo_of(lay), n_queries, n_scan, top_k).total;
+}
+
+int32_t topk_multi_query(const stdk_layout* lay, const float* q, int32_t n_queries, const void* k_cache,
+                         const int64_t* ranges, int32_t n_ranges, int32_t top_k, float scale, int32_t* idx_out,
+                         float* z_out, void* workspace, size_t workspace_bytes, void* stream) {
+  STDK_TRY(check_layout(lay));
+  STDK_TRY(check_ptr(q, "q", 16));
+  STDK_TRY(check_ptr(k_cache, "k_cache", 16));
+  STDK_TRY(check_ptr(idx_out, "idx_out", 4));
+  if (z_out && ((uintptr_t)z_out) % 4) return fail(STDK_EINVAL, "z_out is not 4-byte aligned");
+  if (n_queries < 1) return fail(STDK_EINVAL, "n_queries %d < 1", n_queries);
+  if (top_k < 1) return fail(STDK_EINVAL, "top_k %d < 1", top_k);
+  if (!std::isfinite(scale)) return fail(STDK_EINVAL, "scale is not finite");
+  STDK_TRY(check_ranges(lay, ranges, n_ranges, "ranges"));
+  int64_t n = 0;
+  const RangeTab tab = make_tab(ranges, n_ranges, &n);
+  if (top_k > kMaxTopK) return fail(STDK_EUNSUPPORTED, "top_k %d > %d", top_k, kMaxTopK);
+  const Geo g = geo_of(lay);
+  if (g.groups > 65535) return fail(STDK_EUNSUPPORTED, "batch * n_kv_heads = %lld > 65535", (long long)g.groups);
+  if ((int64_t)g.G * n_queries > (int64_t)65535 * 128)
+    return fail(STDK_EUNSUPPORTED, "%d queries per KV head", g.G * n_queries);
+  const MqWs w = mq_ws(g, n_queries, n, top_k);
+  hipStream_t s = (hipStream_t)stream;
+  if (n == 0) {
+    const int64_t cnt = w.S * (int64_t)top_k;
+    STDK_TRY(launch(KID_MQ_FILL, s, [&](hipEvent_t e0, hipEvent_t e1) {
+      STDK_LAUNCH(mq_fill, dim3((unsigned)cdiv(cnt, 256)), dim3(256), 0, s, idx_out, z_out, cnt);
+    }));
+    return ok();
+  }
+  STDK_TRY(check_ptr(workspace, "workspace", 256));
+  if (workspace_bytes < w.total)
+    return fail(STDK_EWORKSPACE, "workspace is %zu bytes, %zu needed", workspace_bytes, w.total);
+  DevInfo* di = nullptr;
+  STDK_TRY(dev_info(&di));
+  STDK_TRY(run_multi_query(g, w, (char*)workspace, q, n_queries, k_cache, tab, scale, idx_out, z_out, di, s));
   return ok();
 }
 

@@ -1,0 +1,317 @@
+// Multi-query exact top-K: for every query of a block of M queries per query
+// head, the index set of its K largest scores over the same key rows.
+//
+// This is the exact Top-K of the ReTopK review ("Exact Top-K 的隐藏成本":
+// TopK over every score) taken for a block of queries at once: the ReTopK
+// cache starts from the last prefill queries and their supports ("核心方法"
+// 1), and RetrievalAttention's index build starts from the exact nearest keys
+// of each prefill query ("Attention-Aware ANNS Index Construction"). Ties go
+// to the lowest row, as in the decode select.
+//
+// With R = G*M queries per KV head the scores of one KV head form the dense
+// product of an [R x 128] query matrix and a [128 x n] key matrix, so the
+// products run on the bf16 matrix cores (v_mfma_f32_32x32x16_bf16). Every
+// fp32 query element is split into a bf16 value and a bf16 remainder,
+// x = hi + lo + r with |r| <= 2^-17 |x|, and both parts are multiplied into
+// the same fp32 accumulator. A bf16 key is exact in that product; an fp32 key
+// is split the same way and the three products hi*hi, lo*hi and hi*lo are
+// kept. The scores therefore differ from an fp32 dot product by about
+// 2^-16 * scale * sum_j |q_j k_j| plus fp32 accumulation rounding.
+//
+// No score array is written. Two passes compute the same scores with the
+// same instructions, so they agree bit for bit:
+//  1. mq_blockmax: the largest score of every 32-position block, per query.
+//  2. mq_threshold: per query, a key t such that at least K block maxima are
+//     >= t (two radix digits of the maxima). Those maxima are K distinct
+//     positions, so the K-th largest score is >= t.
+//  3. mq_collect: the scores again; the (key, position) pairs with key >= t
+//     go to the query's candidate list in position order (one slice per
+//     workgroup chunk of positions), and their first radix digit is counted.
+//  4. topk_select (the decode select) finishes each query exactly on its
+//     candidates: the K-th largest score is among them, with every score
+//     above it.
+#pragma once
+
+#include "device.h"
+#include "select_kernels.h"
+
+namespace stdk {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float mq_f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMqWaves = 4;
+constexpr int kMqThreads = 64 * kMqWaves;
+constexpr int kMqBlock = 32;            // positions per key block (one MFMA tile edge)
+constexpr int kMqThreshThreads = 256;
+constexpr int kMqMaxChunks = 4096;      // slices per query (the select keeps their prefix in LDS)
+
+// Query tiles (32 queries each) held in registers by one wave.
+template <typename T>
+struct MqShape;
+template <>
+struct MqShape<uint16_t> {
+  static constexpr int QT = 2;
+  static constexpr int ROWB = 256;
+};
+template <>
+struct MqShape<float> {
+  static constexpr int QT = 1;
+  static constexpr int ROWB = 512;
+};
+
+struct MqArgs {
+  const float* q;            // [B][Hq][M][128] fp32
+  const char* k;             // key cache base
+  int64_t stride_b_bytes, stride_h_bytes;
+  int64_t n;                 // positions (rows in the ranges)
+  int64_t n_pad;             // candidate-list stride per query
+  int32_t M, G, Hq, Hkv;
+  int32_t rows;              // G * M queries per KV head
+  int32_t chunk;             // positions per workgroup, a multiple of kMqBlock
+  int32_t nchunk;            // workgroups along the positions
+  int32_t nblk;              // kMqBlock-position blocks per query
+  float scale;
+  int32_t pad_;
+  float* bmax;               // mq_blockmax output [S][nblk]
+  const uint32_t* thr;       // mq_collect input [S]: keep keys >= thr
+  uint32_t* hist;            // mq_collect: [S][2048] first-digit counts of the kept keys
+  Cand* list;                // mq_collect: [S][n_pad], slice j starts at j * chunk
+  uint32_t* slice_cnt;       // mq_collect: [S][nchunk]
+  RangeTab tab;
+};
+
+// Upper 16 bits of x rounded to nearest even (finite x).
+STDK_DEV uint32_t bf16_bits_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Splits 8 fp32 values into bf16 high parts and bf16 remainders, packed two
+// per word in element order (element 2i in the low half of word i).
+STDK_DEV void split8(const mq_f32x4& x0, const mq_f32x4& x1, u32x4& hi, u32x4& lo) {
+  const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+  uint32_t hb[8], lb[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    hb[i] = bf16_bits_rne(x[i]);
+    lb[i] = bf16_bits_rne(x[i] - __uint_as_float(hb[i] << 16));  // the difference is exact
+  }
+  hi = u32x4{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16), hb[6] | (hb[7] << 16)};
+  lo = u32x4{lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16), lb[4] | (lb[5] << 16), lb[6] | (lb[7] << 16)};
+}
+
+STDK_DEV bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+STDK_DEV int64_t min64(int64_t x, int64_t y) { return x < y ? x : y; }
+
+// One pass over the workgroup's chunk of positions for its waves' query
+// tiles.
+//
+// Operand layout of v_mfma_f32_32x32x16_bf16: the A operand of lane l is row
+// l%32, k = 8*(l/32) + i; the B operand is column l%32 with the same k; the
+// result register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+// Here A is 32 keys (rows) and B is 32 queries (columns). The head dimension
+// is permuted so that a lane's k values over the 8 steps are 64 consecutive
+// elements: step s, half h = l/32 uses elements 64h + 8s + i. The dot
+// product does not depend on the order, and each lane reads 128 contiguous
+// bytes of its key row (bf16) and 256 bytes of its query row.
+//
+// After the 8 steps lane (c = l%32, h) holds the scores of query c of the
+// tile against the 16 keys 8*(r/4) + 4h + r%4 of the block.
+template <typename T, bool kCollect>
+STDK_DEV void mq_pass(const MqArgs& a) {
+  constexpr int QT = MqShape<T>::QT, ROWB = MqShape<T>::ROWB;
+  constexpr bool kF32 = sizeof(T) == 4;
+  constexpr int NK = kF32 ? 16 : 8;  // 16-byte key pieces per lane and block
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = lane & 31, h = lane >> 5;
+  const int grp = blockIdx.y;
+  const int b = grp / a.Hkv, hk = grp - b * a.Hkv;
+  const int64_t seg0 = ((int64_t)b * a.Hq + (int64_t)hk * a.G) * a.M;  // query row 0 of this KV head
+  const char* kbase = a.k + b * a.stride_b_bytes + hk * a.stride_h_bytes + h * (ROWB / 2);
+  const int tile0 = ((int)blockIdx.z * kMqWaves + w) * QT;
+
+  // query operands of this wave's tiles, bf16 high parts and remainders
+  u32x4 qh[QT][8], ql[QT][8];
+  bool tv[QT], rv[QT];
+  int64_t seg[QT];
+  uint32_t thr[QT], cnt[QT];
+#pragma unroll
+  for (int u = 0; u < QT; ++u) {
+    const int r = (tile0 + u) * 32 + c;
+    tv[u] = (tile0 + u) * 32 < a.rows;  // uniform over the wave
+    rv[u] = r < a.rows;
+    seg[u] = seg0 + min(r, a.rows - 1);
+    const float* qp = a.q + seg[u] * kHeadDim + 64 * h;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const mq_f32x4 x0 = *reinterpret_cast<const mq_f32x4*>(qp + 8 * s);
+      const mq_f32x4 x1 = *reinterpret_cast<const mq_f32x4*>(qp + 8 * s + 4);
+      split8(x0, x1, qh[u][s], ql[u][s]);
+    }
+    thr[u] = 0u;
+    if constexpr (kCollect) thr[u] = a.thr[seg[u]];
+    cnt[u] = 0u;
+  }
+
+  const int64_t p_begin = (int64_t)blockIdx.x * a.chunk;
+  const int64_t p_end = min64(a.n, p_begin + a.chunk);
+  const int64_t b_begin = p_begin / kMqBlock, b_end = (p_end + kMqBlock - 1) / kMqBlock;
+
+  auto load_keys = [&](int64_t blk, u32x4 (&kr)[NK]) {
+    const int64_t p = min64(blk * kMqBlock + c, a.n - 1);
+    const char* kp = kbase + pos_to_row(a.tab, p) * ROWB;
+#pragma unroll
+    for (int i = 0; i < NK; ++i) kr[i] = load16(kp + 16 * i);
+  };
+
+  auto block = [&](int64_t blk, const u32x4 (&kr)[NK]) {
+    f32x16 acc[QT];
+#pragma unroll
+    for (int u = 0; u < QT; ++u) acc[u] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      bf16x8 kh, kl;
+      if constexpr (kF32) {
+        u32x4 hb, lb;
+        split8(__builtin_bit_cast(mq_f32x4, kr[2 * s]), __builtin_bit_cast(mq_f32x4, kr[2 * s + 1]), hb, lb);
+        kh = as_bf16x8(hb);
+        kl = as_bf16x8(lb);
+      } else {
+        kh = as_bf16x8(kr[s]);
+      }
+#pragma unroll
+      for (int u = 0; u < QT; ++u) {
+        if (!tv[u]) continue;
+        acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, as_bf16x8(qh[u][s]), acc[u], 0, 0, 0);
+        acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, as_bf16x8(ql[u][s]), acc[u], 0, 0, 0);
+        if constexpr (kF32) acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl, as_bf16x8(qh[u][s]), acc[u], 0, 0, 0);
+      }
+    }
+    const int lim = (int)min64(kMqBlock, a.n - blk * kMqBlock);  // valid keys in the block
+#pragma unroll
+    for (int u = 0; u < QT; ++u) {
+      if (!tv[u]) continue;
+      if constexpr (!kCollect) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kk = 8 * (r >> 2) + 4 * h + (r & 3);
+          if (kk < lim) mx = fmaxf(mx, a.scale * acc[u][r]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        if (h == 0 && rv[u]) a.bmax[seg[u] * a.nblk + blk] = mx;
+      } else {
+        uint32_t mine = 0;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kk = 8 * (r >> 2) + 4 * h + (r & 3);
+          const bool keep = kk < lim && f2key(a.scale * acc[u][r]) >= thr[u];
+          mine |= (uint32_t)keep << kk;
+        }
+        const uint32_t full = mine | (uint32_t)__shfl_xor((int)mine, 32, 64);
+        if (rv[u] && mine != 0u) {
+          Cand* out = a.list + seg[u] * a.n_pad + p_begin + cnt[u];
+          uint32_t* hg = a.hist + seg[u] * kHistBins;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kk = 8 * (r >> 2) + 4 * h + (r & 3);
+            if ((mine >> kk) & 1u) {
+              const uint32_t key = f2key(a.scale * acc[u][r]);
+              out[__popc(full & ((1u << kk) - 1u))] = Cand{key, (int32_t)(blk * kMqBlock + kk)};
+              atomicAdd(hg + (key >> (32 - kHistBits)), 1u);
+            }
+          }
+        }
+        cnt[u] += (uint32_t)__popc(full);
+      }
+    }
+  };
+
+  // two key register sets: the next block's loads are in flight during this
+  // block's products
+  u32x4 k0[NK], k1[NK];
+  if (b_begin < b_end) load_keys(b_begin, k0);
+  for (int64_t blk = b_begin; blk < b_end; blk += 2) {
+    if (blk + 1 < b_end) load_keys(blk + 1, k1);
+    block(blk, k0);
+    if (blk + 1 >= b_end) break;
+    if (blk + 2 < b_end) load_keys(blk + 2, k0);
+    block(blk + 1, k1);
+  }
+  if constexpr (kCollect) {
+#pragma unroll
+    for (int u = 0; u < QT; ++u)
+      if (h == 0 && rv[u]) a.slice_cnt[seg[u] * a.nchunk + blockIdx.x] = cnt[u];
+  }
+}
+
+// grid (nchunk, B * Hkv, row packs of kMqWaves * QT * 32 queries)
+template <typename T>
+__global__ __launch_bounds__(kMqThreads) void mq_blockmax(MqArgs a) {
+  mq_pass<T, false>(a);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kMqThreads) void mq_collect(MqArgs a) {
+  mq_pass<T, true>(a);
+}
+
+// ---------------------------------------------------------------------------
+// mq_threshold: one workgroup per query. thr = the 22-bit key prefix of the
+// bin (two radix digits) that holds the K-th largest block maximum, so that
+// at least K maxima have key >= thr. With fewer than K blocks, or n <= K,
+// thr = 0 keeps every position.
+// ---------------------------------------------------------------------------
+struct MqThreshArgs {
+  const float* bmax;  // [S][nblk]
+  uint32_t* thr;      // [S]
+  int64_t n;
+  int32_t nblk, K;
+};
+
+__global__ __launch_bounds__(kMqThreshThreads) void mq_threshold(MqThreshArgs a) {
+  __shared__ uint32_t hst[kHistBins];
+  __shared__ int s_bin;
+  __shared__ uint32_t s_beyond;
+  const int64_t seg = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (a.n <= a.K || a.nblk < a.K) {
+    if (tid == 0) a.thr[seg] = 0u;
+    return;
+  }
+  const float* bm = a.bmax + seg * a.nblk;
+  for (int i = tid; i < kHistBins; i += kMqThreshThreads) hst[i] = 0u;
+  __syncthreads();
+  for (int i = tid; i < a.nblk; i += kMqThreshThreads) atomicAdd(&hst[f2key(bm[i]) >> 21], 1u);
+  __syncthreads();
+  if (tid < 64) find_bin_wave<kHistBins, true>(hst, (uint32_t)a.K, &s_bin, &s_beyond);
+  __syncthreads();
+  const int b0 = s_bin;
+  const uint32_t need = (uint32_t)a.K - s_beyond;
+  for (int i = tid; i < kHistBins; i += kMqThreshThreads) hst[i] = 0u;
+  __syncthreads();
+  if (b0 >= 0) {
+    for (int i = tid; i < a.nblk; i += kMqThreshThreads) {
+      const uint32_t key = f2key(bm[i]);
+      if ((int)(key >> 21) == b0) atomicAdd(&hst[(key >> 10) & 0x7FFu], 1u);
+    }
+  }
+  __syncthreads();
+  if (b0 >= 0 && tid < 64) find_bin_wave<kHistBins, true>(hst, need, &s_bin, &s_beyond);
+  __syncthreads();
+  if (tid == 0) a.thr[seg] = (b0 < 0 || s_bin < 0) ? 0u : (((uint32_t)b0 << 21) | ((uint32_t)s_bin << 10));
+}
+
+// No positions: every index is -1 and every score -inf.
+__global__ __launch_bounds__(256) void mq_fill(int32_t* idx, float* z, int64_t count) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < count) {
+    idx[i] = -1;
+    if (z) z[i] = -INFINITY;
+  }
+}
+
+}  // namespace stdk

@@ -236,3 +236,37 @@ class KernelTimer:
 
     def close(self):
         check(load().stdk_profile_disable())
+
+
+def topk_multi_query_workspace_size(layout: Layout, n_queries: int, n_scan: int, top_k: int) -> int:
+    return int(load().topk_multi_query_workspace_size(ctypes.byref(layout), int(n_queries), int(n_scan), int(top_k)))
+
+
+def topk_multi_query(q: torch.Tensor, k_cache: torch.Tensor, ranges: Sequence[Tuple[int, int]], top_k: int,
+                     scale: Optional[float] = None, *, idx_out: Optional[torch.Tensor] = None,
+                     z_out: Optional[torch.Tensor] = None, want_z: bool = False,
+                     workspace: Optional[torch.Tensor] = None, layout: Optional[Layout] = None):
+    """Exact top-K index sets of a block of queries per head.
+
+    q [B, H_q, M, 128] fp32; k_cache [B, H_kv, L_max, 128] (bf16 or fp32).
+    Returns (idx [B, H_q, M, K] int32, z [B, H_q, M, K] fp32 or None).
+    """
+    lib = load()
+    B, Hq, M, d = q.shape
+    _need(q, "q", torch.float32)
+    _need(k_cache, "k_cache")
+    lay = layout if layout is not None else make_layout(k_cache, Hq)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    n = sum(int(e) - int(b) for b, e in ranges)
+    if idx_out is None:
+        idx_out = torch.empty((B, Hq, M, top_k), dtype=torch.int32, device=q.device)
+    if z_out is None and want_z:
+        z_out = torch.empty((B, Hq, M, top_k), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = new_workspace(topk_multi_query_workspace_size(lay, M, n, top_k), q.device)
+    arr, nr = _ranges_arr(ranges)
+    rc = lib.topk_multi_query(ctypes.byref(lay), q.data_ptr(), int(M), k_cache.data_ptr(), arr, nr, int(top_k),
+                              ctypes.c_float(scale), idx_out.data_ptr(), _ptr(z_out), workspace.data_ptr(),
+                              workspace.numel(), _stream())
+    check(rc)
+    return idx_out, z_out

@@ -152,3 +152,44 @@ def test_retopk_rejects(lib):
     assert step(lib, good, L=lay(Hq=28, Hkv=4, L=4096, d=96)) == native.STDK_EUNSUPPORTED
     big = lay(Hq=28, Hkv=4, L=2_000_000)
     assert step(lib, good, L=big, L_t=1_500_000) == native.STDK_EUNSUPPORTED
+
+
+def call_mq(lib, L=None, M=4, ranges=((0, 100),), top_k=8, ws_bytes=1 << 30, q=FAKE, scale=0.1, idx=FAKE, z=None):
+    L = L or lay()
+    flat = [x for r in ranges for x in r]
+    arr = (ctypes.c_int64 * max(1, len(flat)))(*flat)
+    return lib.topk_multi_query(ctypes.byref(L), q, M, FAKE, arr, len(ranges), top_k, ctypes.c_float(scale), idx, z,
+                                FAKE, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(L=lay(d=64)), native.STDK_EUNSUPPORTED),
+    (dict(L=lay(Hq=30, Hkv=8)), native.STDK_EUNSUPPORTED),
+    (dict(M=0), native.STDK_EINVAL),
+    (dict(top_k=0), native.STDK_EINVAL),
+    (dict(top_k=65537), native.STDK_EUNSUPPORTED),
+    (dict(ranges=((0, 5000),)), native.STDK_EINVAL),
+    (dict(ranges=((0, 100), (50, 200))), native.STDK_EINVAL),
+    (dict(ws_bytes=16), native.STDK_EWORKSPACE),
+    (dict(q=0), native.STDK_EINVAL),
+    (dict(q=FAKE + 4), native.STDK_EINVAL),
+    (dict(idx=0), native.STDK_EINVAL),
+    (dict(idx=FAKE + 2), native.STDK_EINVAL),
+    (dict(z=FAKE + 1), native.STDK_EINVAL),
+    (dict(scale=float("inf")), native.STDK_EINVAL),
+    (dict(L=lay(B=70000, Hq=8, Hkv=1)), native.STDK_EUNSUPPORTED),
+    (dict(L=lay(Hq=8, Hkv=1), M=1048576), native.STDK_EUNSUPPORTED),
+])
+def test_multi_query_rejects_before_launch(lib, kw, code):
+    assert call_mq(lib, **kw) == code
+
+
+def test_multi_query_workspace_size(lib):
+    L = lay(Hq=28, Hkv=4, L=65536)
+    a = lib.topk_multi_query_workspace_size(ctypes.byref(L), 32, 65536, 512)
+    b = lib.topk_multi_query_workspace_size(ctypes.byref(L), 16, 65536, 512)
+    assert a > b > 0 and a % 256 == 0
+    # the histogram region leads the workspace and the candidate lists are sized for every row
+    assert a >= 28 * 32 * (8192 + 2 * 65536 * 8)
+    assert lib.topk_multi_query_workspace_size(ctypes.byref(L), 0, 65536, 512) == 0
+    assert lib.topk_multi_query_workspace_size(ctypes.byref(lay(d=64)), 4, 100, 8) == 0

@@ -1,0 +1,150 @@
+"""GPU parity of topk_multi_query (exact top-K of a block of queries per head)
+against the CPU oracle's topk_multi_query.
+
+Acceptance: the index-set rule of gpu_util (band 1e-3 around the oracle's
+K-th fp64 score) for every checked query, and the returned scores within
+2^-15 * scale * sum_j |q_j k_j| of the oracle's fp64 scores (the error bound
+of the split-bf16 products plus fp32 accumulation). Where scores tie exactly
+the sets must match the oracle's exactly (lowest rows first).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import check_index_set, log
+from oracle import reference as ref
+from workloads import c3_prefill_block, make_multi_query
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ops(stdk):
+    from sparse_top_decode_amd import ops
+    return ops
+
+
+def dev_k(w):
+    if w.kv_dtype == "bf16":
+        return torch.from_numpy(w.k.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(w.k).cuda()
+
+
+def run(ops, w, ranges, K, q=None):
+    qd = torch.from_numpy(np.ascontiguousarray(w.q if q is None else q)).cuda()
+    idx, z = ops.topk_multi_query(qd, dev_k(w), ranges, K, w.scale, want_z=True)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), z.cpu().numpy()
+
+
+def check_queries(w, ranges, K, idx, z, todo, exact=False, label=""):
+    """Checks the listed (b, h, m) queries; returns the band swaps."""
+    G = w.H_q // w.H_kv
+    rows = ref.range_rows(ranges)
+    want = ref.topk_multi_query(w.q, w.k, ranges, K, w.scale, queries=todo)
+    swaps = 0
+    worst = 0.0
+    for b, h, m in todo:
+        zq = ref.scores(w.q[b, h, m], w.k[b, h // G], rows, w.scale)
+        got = idx[b, h, m]
+        if exact:
+            assert np.array_equal(got, want["idx"][b, h, m]), f"{label} query {(b, h, m)}"
+        else:
+            swaps += check_index_set(got, rows, zq, want["zk"][b, h, m], K)
+        # returned scores, position by position
+        n_sel = min(K, rows.shape[0])
+        pos = np.searchsorted(rows, got[:n_sel])
+        kr = ref.widen(w.k[b, h // G][got[:n_sel]])
+        bound = 2.0 ** -15 * w.scale * np.abs(kr * w.q[b, h, m].astype(np.float64)[None, :]).sum(axis=1) + 1e-7
+        err = np.abs(z[b, h, m, :n_sel].astype(np.float64) - zq[pos])
+        assert np.all(err <= bound), f"{label} query {(b, h, m)}: score error {err.max():.3g} > bound"
+        worst = max(worst, float(err.max()) if n_sel else 0.0)
+        assert np.all(np.isneginf(z[b, h, m, n_sel:])), f"{label} query {(b, h, m)}: padding scores"
+    log(f"[{label}] {len(todo)} queries ok: band swaps {swaps}, worst score err {worst:.2e}")
+    return swaps
+
+
+def all_queries(w):
+    return [(b, h, m) for b in range(w.B) for h in range(w.H_q) for m in range(w.q.shape[2])]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("case", [
+    # B, Hq, Hkv, M, L, ranges, K
+    (2, 4, 2, 5, 3000, [(0, 1000), (1500, 2713)], 37),   # two ranges, ragged tail, several chunks
+    (1, 8, 1, 40, 9000, [(0, 9000)], 256),               # 320 queries per KV head: several row packs
+    (1, 4, 4, 2, 5000, [(7, 4990)], 300),                # fewer blocks than K: every row a candidate
+    (1, 2, 2, 3, 500, [(10, 400)], 400),                 # K >= n: every row, -1 padding
+    (1, 2, 1, 33, 2100, [(0, 2100)], 1),                 # K = 1, 66 queries: a ragged query tile
+])
+def test_mq_shapes(ops, dtype, case):
+    B, Hq, Hkv, M, L, ranges, K = case
+    log(f"case mq {dtype} B={B} Hq={Hq} Hkv={Hkv} M={M} L={L} ranges={ranges} K={K}")
+    w = make_multi_query(B, Hq, Hkv, M, L, dtype, top_k=K, tag=L)
+    idx, z = run(ops, w, ranges, K)
+    check_queries(w, ranges, K, idx, z, all_queries(w), label=f"mq {dtype} {case[:5]}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_mq_exact_ties(ops, dtype):
+    """Keys drawn from a 6-row codebook: every score ties with thousands of
+    others, so the K-th score sits inside a tie group and the lowest rows of
+    it must be taken; all candidates exceed the select's LDS copy."""
+    log(f"case mq ties {dtype}")
+    w = make_multi_query(1, 4, 2, 3, 20000, dtype, codebook=6, tag=7)
+    ranges = [(0, 7000), (9000, 20000)]
+    for K in (100, 5000):
+        idx, z = run(ops, w, ranges, K)
+        check_queries(w, ranges, K, idx, z, all_queries(w), exact=True, label=f"mq ties {dtype} K={K}")
+
+
+def test_mq_all_equal_rows(ops):
+    """One key row repeated: all scores are equal; the first K rows are chosen."""
+    log("case mq all-equal rows")
+    w = make_multi_query(1, 2, 1, 2, 12000, "bf16", codebook=1, tag=9)
+    idx, z = run(ops, w, [(0, 12000)], 64)
+    want = np.arange(64, dtype=np.int32)
+    for h in range(2):
+        for m in range(2):
+            assert np.array_equal(idx[0, h, m], want)
+            assert np.all(z[0, h, m] == z[0, h, m, 0])
+
+
+def test_mq_empty_ranges(ops):
+    log("case mq empty")
+    w = make_multi_query(1, 2, 1, 3, 64, "bf16", tag=1)
+    idx, z = run(ops, w, [], 5)
+    assert np.all(idx == -1) and np.all(np.isneginf(z))
+
+
+def test_mq_c3_prefill_block(ops):
+    """The c3 prefill block at full size (28 q / 4 KV heads, 32 queries each,
+    65,536 bf16 rows, K=512): every query of one head of each KV group and a
+    seeded sample of the rest against the oracle."""
+    w = c3_prefill_block()
+    K = 512
+    log(f"case {w.name}")
+    idx, z = run(ops, w, w.ranges, K)
+    rng = np.random.default_rng(11)
+    todo = [(0, h, m) for h in (0, 13, 27) for m in range(32)]
+    todo += [(0, int(h), int(m)) for h, m in zip(rng.integers(0, 28, 24), rng.integers(0, 32, 24))]
+    check_queries(w, w.ranges, K, idx, z, todo, label=w.name)
+    # every query: a valid set (ascending, in range, K rows)
+    assert np.all(np.diff(idx, axis=-1) > 0) and idx.min() >= 0 and idx.max() < w.L
+
+
+def test_mq_repeat_is_deterministic_and_leaves_workspace_clean(ops):
+    """Two calls on one workspace give identical bits, and the counters are
+    zero again afterwards."""
+    w = make_multi_query(1, 4, 2, 6, 7000, "bf16", tag=3)
+    qd = torch.from_numpy(w.q).cuda()
+    k = dev_k(w)
+    lay = ops.make_layout(k, w.H_q)
+    ws = ops.new_workspace(ops.topk_multi_query_workspace_size(lay, 6, 7000, 50), qd.device)
+    a = ops.topk_multi_query(qd, k, [(0, 7000)], 50, w.scale, want_z=True, workspace=ws)
+    b = ops.topk_multi_query(qd, k, [(0, 7000)], 50, w.scale, want_z=True, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    S = w.B * w.H_q * 6
+    assert int(ws[:S * 8192].count_nonzero()) == 0

@@ -10,6 +10,8 @@ from .synth import (  # noqa: F401
     Workload,
     bf16_bits_from_f32,
     f32_from_bf16_bits,
+    c3_prefill_block,
+    make_multi_query,
     make_workload,
     static_window_ranges,
 )

@@ -33,6 +33,12 @@ parity runs, which keeps every distribution and only changes the length):
    every q head, 64 distinct rows of the dynamic set (disjoint between the
    heads of one KV group) are planted as 4*q_dir + N(0, 0.5 I) (variance 0.5),
    with q_dir the unit query direction. K=8192 plus the 640-row static set.
+
+Blocks of queries for the multi-query top-K (``make_multi_query``): the c3
+prefill block is c3's 32 warm-up queries of every head over its L0 rows
+(K=512). Reduced shapes draw keys N(0,1) plus one offset per (sequence, KV
+head) from N(0, I), queries N(0,1) fp32, with the seed id 6; ``codebook`` > 0
+draws every key row from that many N(0,1) rows instead (exact score ties).
 """
 
 from __future__ import annotations
@@ -272,3 +278,33 @@ def make_workload(cfg: int, L: Optional[int] = None, **kw) -> Workload:
     if cfg == 5:
         return _c5(L, **kw)
     raise ValueError(f"unknown workload {cfg}")
+
+
+def make_multi_query(B: int, Hq: int, Hkv: int, M: int, L: int, dtype: str = "bf16", top_k: int = 64,
+                     codebook: int = 0, tag: int = 0) -> Workload:
+    """A block of M queries per query head over an L-row cache (``q`` is
+    [B, Hq, M, d]); ``tag`` selects an independent draw."""
+    cfg = 6
+    side = np.random.default_rng([1000 + cfg, T_SIDE, tag, 0])
+    if codebook > 0:
+        store = np.uint16 if dtype == "bf16" else np.float32
+        book = side.standard_normal((codebook, HEAD_DIM)).astype(np.float32)
+        pick = side.integers(0, codebook, size=(B, Hkv, L))
+        k = book[pick]
+        k = bf16_bits_from_f32(k) if dtype == "bf16" else k.astype(store)
+        v = np.zeros_like(k)
+    else:
+        mu = side.standard_normal((B, Hkv, HEAD_DIM)).astype(np.float32)
+        k, v = _fill_kv(cfg, B, Hkv, L, dtype, offsets=mu)
+    q = np.random.default_rng([1000 + cfg, T_QUERY, tag, 0]).standard_normal((B, Hq, M, HEAD_DIM),
+                                                                            dtype=np.float32)
+    return Workload(f"mq_B{B}_H{Hq}x{Hkv}_M{M}_L{L}_{dtype}", cfg, B, Hq, Hkv, HEAD_DIM, L, L, dtype, top_k,
+                    1.0 / math.sqrt(HEAD_DIM), q, k, v, [(0, L)])
+
+
+def c3_prefill_block(L: Optional[int] = None) -> Workload:
+    """c3's warm-up queries [B, Hq, 32, d] over its first L0 rows."""
+    w = _c3(DEFAULT_L[3] if L is None else int(L), steps=0, warm=32)
+    w.q = np.ascontiguousarray(w.q[:, :, :32])
+    w.name = f"c3_prefill_block_M32_L{w.L}_K512"
+    return w
