@@ -26,6 +26,10 @@ The other workloads are measured the same way when asked for:
   --config 4  batch of 16 sequences x 32,768 rows, K=1024, one
               topk_attn_decode call per step;
   --config 5  1,048,576 rows, K=8192, static window of 640 rows, one-pass step.
+  --config 6  multi-query exact top-K of the c3 prefill block: the 32 warm-up
+              queries of all 28 query heads over the 65,536 initial rows,
+              K=512, one topk_multi_query call per step (the products run on
+              the bf16 matrix cores; the roofline is in TFLOP/s).
 
 Workload 2 steps through --layers distinct copies of the K/V cache in turn
 (default 4), as a model's decode does layer after layer: with a single copy
@@ -61,9 +65,11 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak of MI355X
 SCAN_SOURCES = ["sparse_top_decode_amd/csrc/scan_kernels.h", "sparse_top_decode_amd/csrc/device.h"]
 METRIC = "top-K decode-attention steps/sec at 128K ctx; K-scan HBM GB/s vs peak"
 TOPK_KERNELS = ("k_scan", "topk_filter", "topk_select", "sparse_sv", "dense_attn", "combine", "attn_merge")
+MQ_KERNELS = ("mq_blockmax", "mq_threshold", "mq_collect", "topk_select")
 RETOPK_KERNELS = ("retopk_select", "retopk_rerank", "retopk_rerank_select", "k_scan", "topk_filter", "topk_select",
                   "sparse_sv", "combine", "retopk_push")
 
@@ -154,6 +160,29 @@ def cpu_baseline_retopk(w, p, q_hist, sup_hist, budget_s: float = 12.0):
                        f"no BLAS)")
 
 
+def cpu_baseline_mq(w, K: int, budget_s: float = 12.0):
+    """The oracle's multi-query top-K on a seeded sample of the block's
+    queries, until about budget_s of CPU time has passed; scaled to whole
+    blocks."""
+    import numpy as np
+    from oracle import reference as ref
+    B, Hq, M = w.q.shape[:3]
+    rng = np.random.default_rng(5)
+    perm = rng.permutation(Hq * M)
+    order = [(0, int(j // M), int(j % M)) for j in perm]
+    t0 = time.perf_counter()
+    done = 0
+    for i in range(0, len(order), 4):
+        ref.topk_multi_query(w.q, w.k, w.ranges, K, w.scale, queries=order[i:i + 4])
+        done += len(order[i:i + 4])
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    return dict(value=done / (B * Hq * M) / el, unit="steps/s", cores=1, kind="oracle",
+                sample=f"{done} of the block's {B * Hq * M} queries (seeded sample), {el:.1f} s on one host thread "
+                       f"(numpy fp64, no BLAS); value scaled to whole blocks")
+
+
 # ---------------------------------------------------------------------------
 # timing
 # ---------------------------------------------------------------------------
@@ -216,6 +245,22 @@ def capture(step):
     except Exception as e:  # capture unsupported: time direct launches
         print(f"graph capture failed ({e}); timing direct launches", file=sys.stderr)
         return None
+
+
+def roofline_mfma(kern, kernel, flops_per_launch):
+    avg = kern.get(kernel, (None, 0))[0]
+    achieved = None if not avg else flops_per_launch / (avg * 1e-6) / 1e12
+    return {
+        "bound": "mfma",
+        "achieved": None if achieved is None else round(achieved, 1),
+        "peak": BF16_PEAK_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": None if achieved is None else round(achieved / BF16_PEAK_TFLOPS, 4),
+        "traffic": None,
+        "kernel": kernel,
+        "algorithmic_flops_per_launch": int(flops_per_launch),
+        "avg_launch_us": None if not avg else round(avg, 2),
+    }
 
 
 def roofline(kern, kernel, bytes_per_launch, traffic):
@@ -422,18 +467,55 @@ def bench_retopk(args):
     return line(args, ms, workload, extra, roof, kern, cpu)
 
 
+def bench_multi_query(args):
+    """c3 prefill block: one topk_multi_query call (28 x 32 queries over
+    65,536 rows, K=512) per step."""
+    import torch
+    from sparse_top_decode_amd import ops
+    from workloads import c3_prefill_block
+
+    w = c3_prefill_block()
+    K = 512 if args.top_k is None else args.top_k
+    dev, k, _ = to_dev(w)
+    q = torch.from_numpy(w.q).to(dev)
+    B, Hq, M = w.q.shape[:3]
+    lay = ops.make_layout(k, Hq)
+    n = w.L
+    idx = torch.empty((B, Hq, M, K), dtype=torch.int32, device=dev)
+    ws = ops.new_workspace(ops.topk_multi_query_workspace_size(lay, M, n, K), dev)
+
+    def step():
+        ops.topk_multi_query(q, k, w.ranges, K, w.scale, idx_out=idx, workspace=ws, layout=lay)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    names = MQ_KERNELS if args.kernel_events == "on" else ()
+    ms, kern = timed_passes(step, args.steps, names)
+    flops = 2.0 * B * Hq * M * n * 128  # one pass: every (query, row) product once
+    dom = max(("mq_blockmax", "mq_collect"), key=lambda x: kern.get(x, (0.0, 0))[0])
+    roof = roofline_mfma(kern, dom, flops)
+    cpu = None if args.no_cpu else cpu_baseline_mq(w, K)
+    workload = (f"multi-query exact top-K (prefill block): {M} queries x {Hq} q heads / {w.H_kv} KV heads "
+                f"(Qwen2.5-7B layout), d=128, {n} bf16 key rows, K={K} per query")
+    extra = {"batch": B, "seq_len": n, "top_k": K, "queries_per_head": M, "kv_cache": "bf16",
+             "parallelism": "none (1 GPU)"}
+    return line(args, ms, workload, extra, roof, kern, cpu)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, choices=[2, 3, 4, 5], default=2,
-                    help="workload: 2 (default, the headline), 3 ReTopK, 4 batched, 5 1M rows")
+    ap.add_argument("--config", type=int, choices=[2, 3, 4, 5, 6], default=2,
+                    help="workload: 2 (default, the headline), 3 ReTopK, 4 batched, 5 1M rows, "
+                         "6 multi-query top-K of the prefill block")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--requests", type=int, default=1, help="workload 3: requests served per step, each with its own caches")
     ap.add_argument("--tau", type=float, default=None, help="workload 3: similarity threshold (default 0.85)")
-    ap.add_argument("--top-k", type=int, default=None, help="workload 3: K (default 512)")
+    ap.add_argument("--top-k", type=int, default=None, help="workloads 3 and 6: K (default 512)")
     ap.add_argument("--L", type=int, default=131072, help="cache length of workload 2")
     ap.add_argument("--layers", type=int, default=4,
                     help="workload 2: distinct K/V caches used in turn, one per layer (1 = the same cache every "
@@ -454,7 +536,12 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
-    out = bench_retopk(args) if args.config == 3 else bench_topk(args, args.config)
+    if args.config == 3:
+        out = bench_retopk(args)
+    elif args.config == 6:
+        out = bench_multi_query(args)
+    else:
+        out = bench_topk(args, args.config)
     print(json.dumps(out), flush=True)
 
 

@@ -169,10 +169,8 @@ size_t topk_attn_decode_static_workspace_size(const stdk_layout* lay, int64_t n_
  *  z_out      [B][H_q][M][top_k] fp32 or NULL: the scores of the rows in
  *             idx_out, -inf in the padding.
  *  workspace  at least topk_multi_query_workspace_size(lay, M, n, top_k)
- *             bytes, 256-byte aligned. Its first B * n_q_heads * M * 8192
- *             bytes follow the "Workspace state" rule above (zero before the
- *             first call, left zero by every call that returns STDK_OK).
- *             Not read when n = 0.
+ *             bytes, 256-byte aligned, any contents (this call keeps no
+ *             counters in it). Not used when n = 0.
  *  Limits: B * n_kv_heads <= 65535.
  * The scores are computed on the bf16 matrix cores with every fp32 query
  * element split into a bf16 value and a bf16 remainder (and every fp32 key

@@ -502,11 +502,11 @@ int32_t run_dense(const Geo& g, const TopkWs& w, char* ws, const float* q, const
 // ---------------------------------------------------------------------------
 // multi-query exact top-K: workspace and dispatch
 // ---------------------------------------------------------------------------
-// [hist (zero between calls)] [block maxima] [thresholds] [candidate lists]
-// [spilled candidates] [slice counts] [chosen rows] [their scores]
+// [block maxima] [thresholds] [candidate lists] [spilled candidates]
+// [slice counts] [chosen-row scores]; nothing is kept between calls
 struct MqWs {
   int64_t S, n, n_pad, K, nblk, chunk, nchunk, packs;
-  size_t hist, bmax, thr, list, clist, slice_cnt, sel_row, sel_z, total;
+  size_t bmax, thr, list, clist, slice_cnt, sel_z, total;
 };
 
 constexpr int kMqTargetWg = 512;   // workgroups per pass (2 per CU on 256 CUs)
@@ -527,8 +527,6 @@ MqWs mq_ws(const Geo& g, int64_t M, int64_t n, int64_t K) {
   w.chunk = std::max<int64_t>(rup(cdiv(std::max<int64_t>(n, 1), nchunk), kMqBlock), rup(cdiv(std::max<int64_t>(n, 1), kMqMaxChunks), kMqBlock));
   w.nchunk = cdiv(std::max<int64_t>(n, 1), w.chunk);
   size_t off = 0;
-  w.hist = off;
-  off = al256(off + (size_t)w.S * kHistBins * 4);
   w.bmax = off;
   off = al256(off + (size_t)w.S * w.nblk * 4);
   w.thr = off;
@@ -539,8 +537,6 @@ MqWs mq_ws(const Geo& g, int64_t M, int64_t n, int64_t K) {
   off = al256(off + (size_t)w.S * w.n_pad * sizeof(Cand));
   w.slice_cnt = off;
   off = al256(off + (size_t)w.S * w.nchunk * 4);
-  w.sel_row = off;
-  off = al256(off + (size_t)w.S * K * 4);
   w.sel_z = off;
   off = al256(off + (size_t)w.S * K * 4);
   w.total = off;
@@ -568,7 +564,6 @@ int32_t run_multi_query(const Geo& g, const MqWs& w, char* ws, const float* q, i
   a.scale = scale;
   a.bmax = (float*)(ws + w.bmax);
   a.thr = (const uint32_t*)(ws + w.thr);
-  a.hist = (uint32_t*)(ws + w.hist);
   a.list = (Cand*)(ws + w.list);
   a.slice_cnt = (uint32_t*)(ws + w.slice_cnt);
   a.tab = tab;
@@ -589,7 +584,8 @@ int32_t run_multi_query(const Geo& g, const MqWs& w, char* ws, const float* q, i
   }));
   {
     SelectArgs sa{};
-    sa.hist = (uint32_t*)(ws + w.hist);
+    sa.hist = nullptr;
+    sa.cand_hist = 1;
     sa.list = (const Cand*)(ws + w.list);
     sa.slice_cnt = (const uint32_t*)(ws + w.slice_cnt);
     sa.clist = (Cand*)(ws + w.clist);

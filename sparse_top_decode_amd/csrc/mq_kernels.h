@@ -11,9 +11,9 @@
 // With R = G*M queries per KV head the scores of one KV head form the dense
 // product of an [R x 128] query matrix and a [128 x n] key matrix, so the
 // products run on the bf16 matrix cores (v_mfma_f32_32x32x16_bf16). Every
-// fp32 query element is split into a bf16 value and a bf16 remainder,
-// x = hi + lo + r with |r| <= 2^-17 |x|, and both parts are multiplied into
-// the same fp32 accumulator. A bf16 key is exact in that product; an fp32 key
+// element x of scale * q (fp32) is split into a bf16 value and a bf16
+// remainder, x = hi + lo + r with |r| <= 2^-17 |x|, and both parts are
+// multiplied into the same fp32 accumulator. A bf16 key is exact in that product; an fp32 key
 // is split the same way and the three products hi*hi, lo*hi and hi*lo are
 // kept. The scores therefore differ from an fp32 dot product by about
 // 2^-16 * scale * sum_j |q_j k_j| plus fp32 accumulation rounding.
@@ -26,10 +26,10 @@
 //     positions, so the K-th largest score is >= t.
 //  3. mq_collect: the scores again; the (key, position) pairs with key >= t
 //     go to the query's candidate list in position order (one slice per
-//     workgroup chunk of positions), and their first radix digit is counted.
+//     workgroup chunk of positions).
 //  4. topk_select (the decode select) finishes each query exactly on its
-//     candidates: the K-th largest score is among them, with every score
-//     above it.
+//     candidates, counting their radix digits itself: the K-th largest
+//     score is among them, with every score above it.
 #pragma once
 
 #include "device.h"
@@ -76,7 +76,6 @@ struct MqArgs {
   int32_t pad_;
   float* bmax;               // mq_blockmax output [S][nblk]
   const uint32_t* thr;       // mq_collect input [S]: keep keys >= thr
-  uint32_t* hist;            // mq_collect: [S][2048] first-digit counts of the kept keys
   Cand* list;                // mq_collect: [S][n_pad], slice j starts at j * chunk
   uint32_t* slice_cnt;       // mq_collect: [S][nchunk]
   RangeTab tab;
@@ -115,23 +114,44 @@ STDK_DEV int64_t min64(int64_t x, int64_t y) { return x < y ? x : y; }
 // Here A is 32 keys (rows) and B is 32 queries (columns). The head dimension
 // is permuted so that a lane's k values over the 8 steps are 64 consecutive
 // elements: step s, half h = l/32 uses elements 64h + 8s + i. The dot
-// product does not depend on the order, and each lane reads 128 contiguous
-// bytes of its key row (bf16) and 256 bytes of its query row.
+// product does not depend on the order; each lane reads its query row as 256
+// contiguous bytes and its key row as 16-byte LDS reads 128 bytes apart.
+//
+// Key blocks (32 positions) are loaded once per workgroup, every thread
+// taking 32 (bf16) or 64 (fp32) contiguous bytes of one row, kDepth blocks
+// ahead, and written to a two-slot LDS ring as bf16 (an fp32 key as its bf16
+// high part and remainder). One barrier per block: a slot is rewritten two
+// blocks after it was read, and every wave has passed the previous block's
+// barrier by then.
 //
 // After the 8 steps lane (c = l%32, h) holds the scores of query c of the
 // tile against the 16 keys 8*(r/4) + 4h + r%4 of the block.
-template <typename T, bool kCollect>
+constexpr int kMqLdsRow = 272;    // bytes per staged key row: 256 + 16 (rows start 4 banks apart)
+constexpr int kMqLdsSlot = kMqBlock * kMqLdsRow;
+constexpr int kMqMaxBuf = 32;     // blocks whose maxima a workgroup keeps in LDS between writes
+
+template <typename T, bool kCollect, int kDepth>
 STDK_DEV void mq_pass(const MqArgs& a) {
   constexpr int QT = MqShape<T>::QT, ROWB = MqShape<T>::ROWB;
   constexpr bool kF32 = sizeof(T) == 4;
-  constexpr int NK = kF32 ? 16 : 8;  // 16-byte key pieces per lane and block
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  constexpr int NL = kF32 ? 4 : 2;   // 16-byte pieces per thread and block
+  constexpr int NP = kF32 ? 2 : 1;   // staged parts per key (high, remainder)
+  __shared__ __attribute__((aligned(16))) char ring[2][NP][kMqLdsSlot];
+  // collect: one 36-word row per lane pair (query c of the wave's tile);
+  // rows 4 banks apart
+  __shared__ __attribute__((aligned(16))) uint32_t ckeys[kCollect ? kMqWaves : 1][32][kCollect ? 36 : 4];
+  // blockmax: the maxima of up to kMqMaxBuf blocks per query of the
+  // workgroup, written out as contiguous runs (rows 33 words apart)
+  __shared__ float mxs[kCollect ? 1 : kMqWaves * QT * 32][kCollect ? 1 : kMqMaxBuf + 1];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: the tile tests below are scalar
   const int c = lane & 31, h = lane >> 5;
   const int grp = blockIdx.y;
   const int b = grp / a.Hkv, hk = grp - b * a.Hkv;
   const int64_t seg0 = ((int64_t)b * a.Hq + (int64_t)hk * a.G) * a.M;  // query row 0 of this KV head
-  const char* kbase = a.k + b * a.stride_b_bytes + hk * a.stride_h_bytes + h * (ROWB / 2);
+  const char* kbase = a.k + b * a.stride_b_bytes + hk * a.stride_h_bytes;
   const int tile0 = ((int)blockIdx.z * kMqWaves + w) * QT;
+  uint32_t* ckrow = ckeys[kCollect ? w : 0][c];
 
   // query operands of this wave's tiles, bf16 high parts and remainders
   u32x4 qh[QT][8], ql[QT][8];
@@ -147,8 +167,9 @@ STDK_DEV void mq_pass(const MqArgs& a) {
     const float* qp = a.q + seg[u] * kHeadDim + 64 * h;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const mq_f32x4 x0 = *reinterpret_cast<const mq_f32x4*>(qp + 8 * s);
-      const mq_f32x4 x1 = *reinterpret_cast<const mq_f32x4*>(qp + 8 * s + 4);
+      // the scale is applied to the query, so the products are the scores
+      const mq_f32x4 x0 = *reinterpret_cast<const mq_f32x4*>(qp + 8 * s) * a.scale;
+      const mq_f32x4 x1 = *reinterpret_cast<const mq_f32x4*>(qp + 8 * s + 4) * a.scale;
       split8(x0, x1, qh[u][s], ql[u][s]);
     }
     thr[u] = 0u;
@@ -158,71 +179,119 @@ STDK_DEV void mq_pass(const MqArgs& a) {
 
   const int64_t p_begin = (int64_t)blockIdx.x * a.chunk;
   const int64_t p_end = min64(a.n, p_begin + a.chunk);
-  const int64_t b_begin = p_begin / kMqBlock, b_end = (p_end + kMqBlock - 1) / kMqBlock;
+  const int64_t b_begin = p_begin / kMqBlock;
+  const int nb = (int)((p_end + kMqBlock - 1) / kMqBlock - b_begin);  // blocks of this chunk
 
-  auto load_keys = [&](int64_t blk, u32x4 (&kr)[NK]) {
-    const int64_t p = min64(blk * kMqBlock + c, a.n - 1);
-    const char* kp = kbase + pos_to_row(a.tab, p) * ROWB;
+  // a chunk inside one range maps position p to row p + delta (found once,
+  // with scalar loads); a chunk across a range boundary looks every row up
+  int64_t delta = 0;
+  bool one_range = true;
+  {
+    const int64_t r_first = pos_to_row(a.tab, p_begin), r_last = pos_to_row(a.tab, p_end - 1);
+    delta = r_first - p_begin;
+    one_range = r_last - (p_end - 1) == delta;
+  }
+
+  // this thread's share of a block: key row lk, bytes [lb, lb + 16*NL)
+  const int lk = tid >> 3;
+  const int lb = (tid & 7) * 16 * NL;
+  auto issue = [&](int i, u32x4 (&rr)[NL]) {
+    const int64_t p = min64((b_begin + i) * kMqBlock + lk, a.n - 1);
+    const int64_t row = one_range ? p + delta : pos_to_row(a.tab, p);
+    const char* src = kbase + row * ROWB + lb;
 #pragma unroll
-    for (int i = 0; i < NK; ++i) kr[i] = load16(kp + 16 * i);
+    for (int j = 0; j < NL; ++j) rr[j] = load16(src + 16 * j);
+  };
+  auto stage = [&](int slot, const u32x4 (&rr)[NL]) {
+    if constexpr (kF32) {
+      // 16 fp32 elements [16*(tid&7), +16) -> 32 bytes of each part
+      u32x4 h0, l0, h1, l1;
+      split8(__builtin_bit_cast(mq_f32x4, rr[0]), __builtin_bit_cast(mq_f32x4, rr[1]), h0, l0);
+      split8(__builtin_bit_cast(mq_f32x4, rr[2]), __builtin_bit_cast(mq_f32x4, rr[3]), h1, l1);
+      char* dh = ring[slot][0] + lk * kMqLdsRow + (tid & 7) * 32;
+      char* dl = ring[slot][1] + lk * kMqLdsRow + (tid & 7) * 32;
+      *reinterpret_cast<u32x4*>(dh) = h0;
+      *reinterpret_cast<u32x4*>(dh + 16) = h1;
+      *reinterpret_cast<u32x4*>(dl) = l0;
+      *reinterpret_cast<u32x4*>(dl + 16) = l1;
+    } else {
+      char* d = ring[slot][0] + lk * kMqLdsRow + lb;
+      *reinterpret_cast<u32x4*>(d) = rr[0];
+      *reinterpret_cast<u32x4*>(d + 16) = rr[1];
+    }
   };
 
-  auto block = [&](int64_t blk, const u32x4 (&kr)[NK]) {
+  auto block = [&](int i, int slot) {
+    const int64_t blk = b_begin + i;
     f32x16 acc[QT];
 #pragma unroll
     for (int u = 0; u < QT; ++u) acc[u] = f32x16{};
+    // all of the block's key fragments first, then the products: the LDS
+    // reads overlap, and every tile is multiplied (a tile without queries
+    // costs no time, the busiest wave of the SIMD sets the pace), so the
+    // products carry no branches
+    const char* arow = ring[slot][0] + c * kMqLdsRow + 128 * h;
+    u32x4 kf[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) kf[s] = *reinterpret_cast<const u32x4*>(arow + 16 * s);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      bf16x8 kh, kl;
-      if constexpr (kF32) {
-        u32x4 hb, lb;
-        split8(__builtin_bit_cast(mq_f32x4, kr[2 * s]), __builtin_bit_cast(mq_f32x4, kr[2 * s + 1]), hb, lb);
-        kh = as_bf16x8(hb);
-        kl = as_bf16x8(lb);
-      } else {
-        kh = as_bf16x8(kr[s]);
-      }
+      const bf16x8 kh = as_bf16x8(kf[s]);
 #pragma unroll
       for (int u = 0; u < QT; ++u) {
-        if (!tv[u]) continue;
         acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, as_bf16x8(qh[u][s]), acc[u], 0, 0, 0);
         acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, as_bf16x8(ql[u][s]), acc[u], 0, 0, 0);
-        if constexpr (kF32) acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl, as_bf16x8(qh[u][s]), acc[u], 0, 0, 0);
       }
     }
+    if constexpr (kF32) {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) kf[s] = *reinterpret_cast<const u32x4*>(arow + kMqLdsSlot + 16 * s);
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+#pragma unroll
+        for (int u = 0; u < QT; ++u)
+          acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[s]), as_bf16x8(qh[u][s]), acc[u], 0, 0, 0);
+    }
     const int lim = (int)min64(kMqBlock, a.n - blk * kMqBlock);  // valid keys in the block
+    const bool whole = lim == kMqBlock;                             // uniform
 #pragma unroll
     for (int u = 0; u < QT; ++u) {
       if (!tv[u]) continue;
       if constexpr (!kCollect) {
-        float mx = -INFINITY;
+        float mx = acc[u][0];
+        if (whole) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kk = 8 * (r >> 2) + 4 * h + (r & 3);
-          if (kk < lim) mx = fmaxf(mx, a.scale * acc[u][r]);
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        if (h == 0 && rv[u]) a.bmax[seg[u] * a.nblk + blk] = mx;
-      } else {
-        uint32_t mine = 0;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kk = 8 * (r >> 2) + 4 * h + (r & 3);
-          const bool keep = kk < lim && f2key(a.scale * acc[u][r]) >= thr[u];
-          mine |= (uint32_t)keep << kk;
-        }
-        const uint32_t full = mine | (uint32_t)__shfl_xor((int)mine, 32, 64);
-        if (rv[u] && mine != 0u) {
-          Cand* out = a.list + seg[u] * a.n_pad + p_begin + cnt[u];
-          uint32_t* hg = a.hist + seg[u] * kHistBins;
+          for (int r = 1; r < 16; ++r) mx = fmaxf(mx, acc[u][r]);
+        } else {
+          mx = -INFINITY;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int kk = 8 * (r >> 2) + 4 * h + (r & 3);
-            if ((mine >> kk) & 1u) {
-              const uint32_t key = f2key(a.scale * acc[u][r]);
-              out[__popc(full & ((1u << kk) - 1u))] = Cand{key, (int32_t)(blk * kMqBlock + kk)};
-              atomicAdd(hg + (key >> (32 - kHistBits)), 1u);
-            }
+            if (kk < lim) mx = fmaxf(mx, acc[u][r]);
+          }
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        if (h == 0) mxs[(w * QT + u) * 32 + c][i % kMqMaxBuf] = mx;
+      } else {
+        uint32_t mine = 0, kv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kk = 8 * (r >> 2) + 4 * h + (r & 3);
+          kv[r] = f2key(acc[u][r]);
+          mine |= (uint32_t)(kv[r] >= thr[u]) << kk;
+        }
+        if (!whole) mine &= lim >= 32 ? ~0u : ((1u << lim) - 1u);
+        const uint32_t full = mine | (uint32_t)__shfl_xor((int)mine, 32, 64);
+        if (rv[u] && mine != 0u) {
+          // the lane's keys go to its own LDS row (key kk at word kk) and
+          // only the kept ones are read back, in position order
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<u32x4*>(ckrow + 8 * j + 4 * h) = u32x4{kv[4 * j], kv[4 * j + 1], kv[4 * j + 2], kv[4 * j + 3]};
+          Cand* out = a.list + seg[u] * a.n_pad + p_begin + cnt[u];
+          for (uint32_t bits = mine; bits != 0u; bits &= bits - 1u) {
+            const int kk = __ffs((int)bits) - 1;
+            out[__popc(full & ((1u << kk) - 1u))] = Cand{ckrow[kk], (int32_t)(blk * kMqBlock + kk)};
           }
         }
         cnt[u] += (uint32_t)__popc(full);
@@ -230,16 +299,37 @@ STDK_DEV void mq_pass(const MqArgs& a) {
     }
   };
 
-  // two key register sets: the next block's loads are in flight during this
-  // block's products
-  u32x4 k0[NK], k1[NK];
-  if (b_begin < b_end) load_keys(b_begin, k0);
-  for (int64_t blk = b_begin; blk < b_end; blk += 2) {
-    if (blk + 1 < b_end) load_keys(blk + 1, k1);
-    block(blk, k0);
-    if (blk + 1 >= b_end) break;
-    if (blk + 2 < b_end) load_keys(blk + 2, k0);
-    block(blk + 1, k1);
+  // blockmax: blocks [i_first, i_last] of the buffer go to the queries' rows
+  auto flush = [&](int i_first, int i_last) {
+    __syncthreads();
+    const int nbuf = i_last - i_first + 1;
+    constexpr int QW = kMqWaves * QT * 32;  // queries of the workgroup
+    const int q0 = (int)blockIdx.z * QW;
+    for (int e = tid; e < QW * nbuf; e += kMqThreads) {
+      const int ql = e / nbuf, j = e - ql * nbuf;
+      if (q0 + ql < a.rows) a.bmax[(seg0 + q0 + ql) * a.nblk + b_begin + i_first + j] = mxs[ql][(i_first + j) % kMqMaxBuf];
+    }
+    __syncthreads();
+  };
+
+  u32x4 rr[kDepth][NL];
+#pragma unroll
+  for (int j = 0; j < kDepth; ++j)
+    if (j < nb) issue(j, rr[j]);
+  for (int i0 = 0; i0 < nb; i0 += kDepth) {
+#pragma unroll
+    for (int j = 0; j < kDepth; ++j) {
+      const int i = i0 + j;
+      if (i < nb) {  // uniform over the workgroup
+        stage(i & 1, rr[j]);
+        if (i + kDepth < nb) issue(i + kDepth, rr[j]);
+        __syncthreads();
+        block(i, i & 1);
+        if constexpr (!kCollect) {
+          if (i % kMqMaxBuf == kMqMaxBuf - 1 || i == nb - 1) flush(i - i % kMqMaxBuf, i);
+        }
+      }
+    }
   }
   if constexpr (kCollect) {
 #pragma unroll
@@ -251,12 +341,12 @@ STDK_DEV void mq_pass(const MqArgs& a) {
 // grid (nchunk, B * Hkv, row packs of kMqWaves * QT * 32 queries)
 template <typename T>
 __global__ __launch_bounds__(kMqThreads) void mq_blockmax(MqArgs a) {
-  mq_pass<T, false>(a);
+  mq_pass<T, false, 3>(a);
 }
 
 template <typename T>
-__global__ __launch_bounds__(kMqThreads) void mq_collect(MqArgs a) {
-  mq_pass<T, true>(a);
+__global__ __launch_bounds__(kMqThreads) __attribute__((amdgpu_waves_per_eu(2))) void mq_collect(MqArgs a) {
+  mq_pass<T, true, 3>(a);
 }
 
 // ---------------------------------------------------------------------------

@@ -134,17 +134,19 @@ def test_mq_c3_prefill_block(ops):
     assert np.all(np.diff(idx, axis=-1) > 0) and idx.min() >= 0 and idx.max() < w.L
 
 
-def test_mq_repeat_is_deterministic_and_leaves_workspace_clean(ops):
-    """Two calls on one workspace give identical bits, and the counters are
-    zero again afterwards."""
+def test_mq_repeat_is_deterministic_on_a_dirty_workspace(ops):
+    """The call keeps no state in its workspace: a workspace full of garbage
+    and a reused one give the same bits as a fresh one."""
     w = make_multi_query(1, 4, 2, 6, 7000, "bf16", tag=3)
     qd = torch.from_numpy(w.q).cuda()
     k = dev_k(w)
     lay = ops.make_layout(k, w.H_q)
-    ws = ops.new_workspace(ops.topk_multi_query_workspace_size(lay, 6, 7000, 50), qd.device)
+    nbytes = ops.topk_multi_query_workspace_size(lay, 6, 7000, 50)
+    ws = ops.new_workspace(nbytes, qd.device)
     a = ops.topk_multi_query(qd, k, [(0, 7000)], 50, w.scale, want_z=True, workspace=ws)
     b = ops.topk_multi_query(qd, k, [(0, 7000)], 50, w.scale, want_z=True, workspace=ws)
+    ws.fill_(0xA5)
+    c = ops.topk_multi_query(qd, k, [(0, 7000)], 50, w.scale, want_z=True, workspace=ws)
     torch.cuda.synchronize()
-    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
-    S = w.B * w.H_q * 6
-    assert int(ws[:S * 8192].count_nonzero()) == 0
+    for x in (b, c):
+        assert torch.equal(a[0], x[0]) and torch.equal(a[1], x[1])
