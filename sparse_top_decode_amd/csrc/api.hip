@@ -57,13 +57,13 @@ int32_t ok() {
 enum KernelId {
   KID_SCAN, KID_FILTER, KID_SELECT, KID_SV, KID_DENSE, KID_COMBINE, KID_MERGE, KID_FILL,
   KID_RT_SELECT, KID_RT_RERANK, KID_RT_RSEL, KID_RT_PUSH, KID_RT_INIT, KID_MQ_BLOCKMAX, KID_MQ_THRESH,
-  KID_MQ_COLLECT, KID_MQ_FILL, KID_COUNT
+  KID_MQ_COLLECT, KID_MQ_SELECT, KID_MQ_FILL, KID_COUNT
 };
 const char* const kKernelNames[KID_COUNT] = {
     "k_scan",        "topk_filter",   "topk_select",          "sparse_sv",
     "dense_attn",  "combine",       "attn_merge",    "fill_empty",           "retopk_select",
     "retopk_rerank", "retopk_rerank_select", "retopk_push", "retopk_init", "mq_blockmax",
-    "mq_threshold",  "mq_collect",    "mq_fill"};
+    "mq_threshold",  "mq_collect",    "mq_select",     "mq_fill"};
 
 struct Profiler {
   std::mutex mu;
@@ -165,6 +165,8 @@ int32_t dev_info(DevInfo** out) {
     (void)hipFuncSetAttribute((const void*)topk_select, hipFuncAttributeMaxDynamicSharedMemorySize, dyn_max);
     (void)hipFuncSetAttribute((const void*)retopk_select<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               std::max(0, d.max_lds - 12 * 1024));
+    (void)hipFuncSetAttribute((const void*)mq_select, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              std::max(0, d.max_lds - 1024));
     (void)hipGetLastError();
     d.init = true;
   }
@@ -502,15 +504,15 @@ int32_t run_dense(const Geo& g, const TopkWs& w, char* ws, const float* q, const
 // ---------------------------------------------------------------------------
 // multi-query exact top-K: workspace and dispatch
 // ---------------------------------------------------------------------------
-// [block maxima] [thresholds] [candidate lists] [spilled candidates]
-// [slice counts] [chosen-row scores]; nothing is kept between calls
+// [block maxima] [thresholds] [candidate lists] [slice counts]; nothing is
+// kept between calls
 struct MqWs {
-  int64_t S, n, n_pad, K, nblk, chunk, nchunk, packs;
-  size_t bmax, thr, list, clist, slice_cnt, sel_z, total;
+  int64_t S, n, n_pad, K, nblk, ngrp, chunk, nchunk, packs;
+  size_t bmax, thr, list, slice_cnt, total;
 };
 
 constexpr int kMqTargetWg = 512;   // workgroups per pass (2 per CU on 256 CUs)
-constexpr int kMqSelCache = 8192;  // candidates per query kept in the select's LDS
+constexpr int kMqSelCache = 1024;  // candidates per query copied to the select wave's LDS
 
 // The chunking depends on the shapes only, so the workspace size does too.
 MqWs mq_ws(const Geo& g, int64_t M, int64_t n, int64_t K) {
@@ -520,6 +522,7 @@ MqWs mq_ws(const Geo& g, int64_t M, int64_t n, int64_t K) {
   w.K = K;
   w.n_pad = rup(std::max<int64_t>(n, 1), 64);
   w.nblk = cdiv(std::max<int64_t>(n, 1), kMqBlock);
+  w.ngrp = 2 * w.nblk;
   const int64_t rows_per_pack = (int64_t)kMqWaves * (g.bf16 ? MqShape<uint16_t>::QT : MqShape<float>::QT) * 32;
   w.packs = cdiv((int64_t)g.G * M, rows_per_pack);
   int64_t nchunk = std::max<int64_t>(1, cdiv(kMqTargetWg, g.groups * w.packs));
@@ -528,17 +531,13 @@ MqWs mq_ws(const Geo& g, int64_t M, int64_t n, int64_t K) {
   w.nchunk = cdiv(std::max<int64_t>(n, 1), w.chunk);
   size_t off = 0;
   w.bmax = off;
-  off = al256(off + (size_t)w.S * w.nblk * 4);
+  off = al256(off + (size_t)w.S * w.ngrp * 4);
   w.thr = off;
   off = al256(off + (size_t)w.S * 4);
   w.list = off;
   off = al256(off + (size_t)w.S * w.n_pad * sizeof(Cand));
-  w.clist = off;
-  off = al256(off + (size_t)w.S * w.n_pad * sizeof(Cand));
   w.slice_cnt = off;
   off = al256(off + (size_t)w.S * w.nchunk * 4);
-  w.sel_z = off;
-  off = al256(off + (size_t)w.S * K * 4);
   w.total = off;
   return w;
 }
@@ -560,7 +559,7 @@ int32_t run_multi_query(const Geo& g, const MqWs& w, char* ws, const float* q, i
   a.rows = g.G * M;
   a.chunk = (int32_t)w.chunk;
   a.nchunk = (int32_t)w.nchunk;
-  a.nblk = (int32_t)w.nblk;
+  a.ngrp = (int32_t)w.ngrp;
   a.scale = scale;
   a.bmax = (float*)(ws + w.bmax);
   a.thr = (const uint32_t*)(ws + w.thr);
@@ -573,7 +572,7 @@ int32_t run_multi_query(const Geo& g, const MqWs& w, char* ws, const float* q, i
     else STDK_LAUNCH(mq_blockmax<float>, grid, dim3(kMqThreads), 0, s, a);
   }));
   {
-    MqThreshArgs t{(const float*)(ws + w.bmax), (uint32_t*)(ws + w.thr), w.n, (int32_t)w.nblk, (int32_t)w.K};
+    MqThreshArgs t{(const float*)(ws + w.bmax), (uint32_t*)(ws + w.thr), w.n, (int32_t)w.ngrp, (int32_t)w.K};
     STDK_TRY(launch(KID_MQ_THRESH, s, [&](hipEvent_t e0, hipEvent_t e1) {
       STDK_LAUNCH(mq_threshold, dim3((unsigned)w.S), dim3(kMqThreshThreads), 0, s, t);
     }));
@@ -583,28 +582,24 @@ int32_t run_multi_query(const Geo& g, const MqWs& w, char* ws, const float* q, i
     else STDK_LAUNCH(mq_collect<float>, grid, dim3(kMqThreads), 0, s, a);
   }));
   {
-    SelectArgs sa{};
-    sa.hist = nullptr;
-    sa.cand_hist = 1;
+    MqSelArgs sa{};
     sa.list = (const Cand*)(ws + w.list);
     sa.slice_cnt = (const uint32_t*)(ws + w.slice_cnt);
-    sa.clist = (Cand*)(ws + w.clist);
+    sa.idx_out = idx_out;
+    sa.z_out = z_out;
+    sa.S = w.S;
     sa.n = w.n;
     sa.n_pad = w.n_pad;
+    sa.chunk = (int32_t)w.chunk;
+    sa.nchunk = (int32_t)w.nchunk;
     sa.K = (int32_t)w.K;
-    sa.slice = (int32_t)w.chunk;
-    sa.nslice = (int32_t)w.nchunk;
-    sa.sel_row = idx_out;
-    sa.sel_z = z_out ? z_out : (float*)(ws + w.sel_z);
-    sa.idx_out = nullptr;
-    sa.seg_active = nullptr;
+    sa.cap = (int32_t)std::min<int64_t>(w.n, kMqSelCache);
+    sa.lds_words = (int32_t)(kHistBins + ((w.nchunk + 4) & ~3LL) + 2LL * sa.cap);
     sa.tab = tab;
-    const size_t pre_bytes = (size_t)((w.nchunk + 2) & ~1LL) * 4;
-    const size_t avail = (size_t)di->max_lds - kSelStaticLds;
-    const size_t dyn = std::min(avail, pre_bytes + (size_t)std::min<int64_t>(w.n, kMqSelCache) * sizeof(Cand));
-    sa.cache_cap = (int32_t)((dyn - pre_bytes) / sizeof(Cand));
-    STDK_TRY(launch(KID_SELECT, s, [&](hipEvent_t e0, hipEvent_t e1) {
-      STDK_LAUNCH(topk_select, dim3((unsigned)w.S), dim3(kSelThreads), dyn, s, sa);
+    const size_t dyn = (size_t)kMqSelWaves * sa.lds_words * 4;
+    if (dyn > (size_t)di->max_lds) return fail(STDK_EUNSUPPORTED, "multi-query select needs %zu bytes of LDS", dyn);
+    STDK_TRY(launch(KID_MQ_SELECT, s, [&](hipEvent_t e0, hipEvent_t e1) {
+      STDK_LAUNCH(mq_select, dim3((unsigned)cdiv(w.S, kMqSelWaves)), dim3(64 * kMqSelWaves), dyn, s, sa);
     }));
   }
   return STDK_OK;

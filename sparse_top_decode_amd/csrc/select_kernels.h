@@ -17,8 +17,6 @@
 //     in position order.
 //  3. topk_select (one workgroup per head, candidates only): radix digits
 //     20..10 and 9..0 on the candidates of bin b* give the exact K-th key T
-//     (candidates gathered with a lower bound on the K-th key instead of
-//     the scan's histogram have their first digit counted here as well)
 //     and how many rows with key == T to keep (`need`): chosen = key > T, or
 //     key == T among the first `need` such rows in position order. One
 //     ordered compaction writes the chosen rows in ascending order.
@@ -177,9 +175,6 @@ struct SelectArgs {
   float* sel_z;               // [S][K] their scores
   int32_t* idx_out;           // [S][K] or null (copy of the chosen rows)
   const int32_t* seg_active;  // [S] or null
-  int32_t cand_hist;          // 1: the candidates hold the K-th largest key and every larger one, and
-                              // the first digit is counted on them here (hist is not used)
-  int32_t pad_;
   RangeTab tab;
 };
 
@@ -203,8 +198,7 @@ STDK_DEV void select_rest(const SelectArgs& a, int64_t seg, uint32_t m, uint32_t
   // ..., SU of them per round. Every load is issued (clamped into the slice)
   // before the first wait, and the results beyond a slice's count are
   // dropped. The same pass counts digit 1 (bits 20..10) of the candidates in
-  // bin b0, or, with cand_hist, digit 0 of every candidate.
-  const bool ch = a.cand_hist != 0 && !take_all;
+  // bin b0.
   {
     constexpr int SU = 8;
     for (int j0 = wv; j0 < ns; j0 += kSelectWaves * SU) {
@@ -229,8 +223,7 @@ STDK_DEV void select_rest(const SelectArgs& a, int64_t seg, uint32_t m, uint32_t
         for (int u = 0; u < SU; ++u) {
           if (e < cnt[u]) {
             cl[off[u] + e] = v[u];
-            if (ch) atomicAdd(&h1[v[u].key >> 21], 1u);
-            else if (!take_all && (v[u].key >> 21) == b0) atomicAdd(&h1[(v[u].key >> 10) & 0x7FFu], 1u);
+            if (!take_all && (v[u].key >> 21) == b0) atomicAdd(&h1[(v[u].key >> 10) & 0x7FFu], 1u);
           }
         }
       }
@@ -238,27 +231,6 @@ STDK_DEV void select_rest(const SelectArgs& a, int64_t seg, uint32_t m, uint32_t
   }
   __syncthreads();
   constexpr int U = 8;
-  if (ch) {
-    // digit 0 from the candidates' own counts, then digit 1 of bin b0
-    if (wv == 0) find_bin_wave<kHistBins, true>(h1, need, s_bin, s_beyond);
-    __syncthreads();
-    b0 = (uint32_t)(*s_bin < 0 ? 0 : *s_bin);
-    need -= *s_beyond;
-#pragma unroll
-    for (int u = 0; u < kHistBins / kSelThreads; ++u) h1[u * kSelThreads + tid] = 0u;
-    __syncthreads();
-    for (uint32_t base = 0; base < m; base += kSelThreads * U) {
-      uint32_t kv[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) kv[u] = cl[min(base + (uint32_t)(u * kSelThreads + tid), m - 1u)].key;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const uint32_t i = base + (uint32_t)(u * kSelThreads + tid);
-        if (i < m && (kv[u] >> 21) == b0) atomicAdd(&h1[(kv[u] >> 10) & 0x7FFu], 1u);
-      }
-    }
-    __syncthreads();
-  }
   uint32_t Tk = 0;
   if (!take_all) {
     if (wv == 0) find_bin_wave<kHistBins, true>(h1, need, s_bin, s_beyond);
@@ -362,12 +334,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select(SelectArgs a) {
   // in registers, then zeroes the global copy for the next call (the scan
   // and the filter are done with it). Wave 1 builds the slice prefix
   // (ns <= 4096). Every thread clears the other digits' histograms.
-  if (wv == 0 && a.cand_hist) {
-    if (lane == 0) {
-      s_bin = 0;
-      s_beyond = 0u;
-    }
-  } else if (wv == 0) {
+  if (wv == 0) {
     u32x4 hv[8];
     uint32_t* hg = a.hist + seg * kHistBins;
     first_digit_load(hg, hv);
