@@ -101,7 +101,7 @@ def unit_f32(q: Sequence[float]):
 def retopk_head_step(cache: List[Tuple[List[float], List[int]]], q: Sequence[float],
                      keys: Sequence[Sequence[float]], values: Sequence[Sequence[float]],
                      L_t: int, t: int, K: int, C: int, R: int, W: int, tau: float, T_r: int,
-                     scale: float, rho_fn=None) -> Dict:
+                     scale: float, rho_fn=None, budget: int = 0) -> Dict:
     """One ReTopK step of one head. ``cache`` is a list of (unit query,
     support rows) from oldest to newest, at most C long; it is updated in
     place (append, drop the oldest beyond C)."""
@@ -127,9 +127,23 @@ def retopk_head_step(cache: List[Tuple[List[float], List[int]]], q: Sequence[flo
             for x in newest_first[age][1]:
                 if 0 <= x < L_t:
                     pool.add(x)
-        for x in range(max(0, L_t - W), L_t):
-            pool.add(x)
-        rows = sorted(pool)
+        recent = set(range(max(0, L_t - W), L_t))
+        if budget > 0:
+            # confidence votes: each row of the union collects the cosines of
+            # the recalled entries whose support holds it, added one by one
+            # in fp32 in recall order
+            voted = sorted(pool - recent)
+            if len(voted) > budget:
+                conf = {}
+                for x in voted:
+                    f = np.float32(0.0)
+                    for r, age in ranked:
+                        if x in set(newest_first[age][1]):
+                            f = np.float32(f + np.float32(r))
+                    conf[x] = float(f)
+                best = sorted(voted, key=lambda x: (-conf[x], x))[:budget]
+                pool = set(best)
+        rows = sorted(pool | recent)
     else:
         rows = list(range(L_t))
     res = topk_attention(q, keys, values, rows, K, scale)

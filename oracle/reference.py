@@ -239,6 +239,7 @@ class RetopkParams:
     recent: int = 32        # W, recent rows always added to the candidates
     tau: float = 0.85       # similarity threshold of the fallback
     refresh: int = 128      # T_r; 0 disables the periodic refresh
+    budget: int = 0         # voted rows kept on the reuse path; 0 = the whole union
 
 
 @dataclass
@@ -284,6 +285,36 @@ def retopk_state_init(p: RetopkParams, q_hist: np.ndarray, sup_hist: np.ndarray)
     return st
 
 
+def vote_candidates(union_rows: np.ndarray, recent_rows: np.ndarray, supports: Sequence[np.ndarray],
+                    weights: Sequence[np.float32], budget: int) -> Tuple[np.ndarray, Dict]:
+    """Confidence-voted candidate set ([RT] "启发 4": the access confidence of
+    row i is f(i) = sum over the recalled entries c of w_c * [i in S_c]; the
+    high-confidence rows are read first under a candidate budget, 启发 5).
+
+    Readings: w_c is the recalled entry's cosine rho_c; f is summed in fp32
+    in recall-rank order (``supports`` / ``weights`` in that order); the
+    recent window is always kept (the recent guard of 核心方法 3) and the
+    budget applies to the other rows of the union: when more than ``budget``
+    of them exist, the ``budget`` rows of largest f are kept, ties to the
+    lowest row. Returns the ascending candidate rows and a trace (f and the
+    membership mask of every voted row, in ascending row order)."""
+    recent_rows = np.asarray(recent_rows, dtype=np.int64)
+    voted = np.setdiff1d(np.asarray(union_rows, dtype=np.int64), recent_rows)
+    f = np.zeros(voted.shape[0], dtype=np.float32)
+    mask = np.zeros(voted.shape[0], dtype=np.int64)
+    for r, (sup, w) in enumerate(zip(supports, weights)):
+        mem = np.isin(voted, np.asarray(sup, dtype=np.int64))
+        f = np.where(mem, (f + np.float32(w)).astype(np.float32), f)
+        mask |= mem.astype(np.int64) << r
+    trace = dict(voted=voted, f=f, mask=mask, cut=None)
+    if budget <= 0 or voted.shape[0] <= budget:
+        return np.union1d(voted, recent_rows), trace
+    order = np.lexsort((voted, -f.astype(np.float64)))  # f descending, then row ascending
+    keep = voted[order[:budget]]
+    trace["cut"] = (float(f[order[budget - 1]]), int(mask[order[budget - 1]]))
+    return np.union1d(keep, recent_rows), trace
+
+
 def retopk_head_step(p: RetopkParams, q_hat: np.ndarray, support: np.ndarray, head: int, count: int,
                      q: np.ndarray, kc_head: np.ndarray, vc_head: np.ndarray, L_t: int, t: int,
                      scale: float) -> Dict:
@@ -298,6 +329,8 @@ def retopk_head_step(p: RetopkParams, q_hat: np.ndarray, support: np.ndarray, he
     ages = np.array([(head - s) % C for s in range(C)], dtype=np.int64)
     valid = np.nonzero(ages < count)[0]
     rho = (q_hat[valid].astype(np.float32) @ qbar.astype(np.float32)).astype(np.float32) if valid.size else np.zeros(0, np.float32)
+    rho_of_slot = np.full(C, -np.inf, dtype=np.float32)
+    rho_of_slot[valid] = rho
     order = valid[np.lexsort((ages[valid], -rho.astype(np.float64)))] if valid.size else valid
     rho_sorted = np.sort(rho)[::-1]
     max_rho = float(rho_sorted[0]) if rho_sorted.size else float("nan")
@@ -310,11 +343,16 @@ def retopk_head_step(p: RetopkParams, q_hat: np.ndarray, support: np.ndarray, he
     else:
         path = PATH_REUSE
     cand = None
+    vote = None
     if path == PATH_REUSE:
         picked = order[:min(R, count)]
         parts = [support[s][(support[s] >= 0) & (support[s] < L_t)].astype(np.int64) for s in picked]
-        parts.append(np.arange(max(0, L_t - W), L_t, dtype=np.int64))  # recent window ([RT] 核心方法 3)
-        cand = np.unique(np.concatenate(parts))
+        recent = np.arange(max(0, L_t - W), L_t, dtype=np.int64)  # recent window ([RT] 核心方法 3)
+        if p.budget > 0:
+            union = np.unique(np.concatenate(parts)) if parts else np.zeros(0, np.int64)
+            cand, vote = vote_candidates(union, recent, parts, [rho_of_slot[s] for s in picked], p.budget)
+        else:
+            cand = np.unique(np.concatenate(parts + [recent]))
         rows = cand
     else:
         rows = np.arange(0, L_t, dtype=np.int64)
@@ -329,6 +367,7 @@ def retopk_head_step(p: RetopkParams, q_hat: np.ndarray, support: np.ndarray, he
     return dict(path=path, cand=cand, n_cand=(cand.shape[0] if cand is not None else L_t),
                 support=sup, o=r["o"], lse=r["lse"], zk=r["zk"], z=r["z"], rows=rows,
                 rho_sorted=rho_sorted, max_rho=max_rho, picked=(order[:min(R, count)] if path == PATH_REUSE else None),
+                vote=vote,
                 new=(q_hat, support, slot, min(count + 1, C)))
 
 

@@ -464,9 +464,80 @@ def pin_retopk_brute(ref, seed=0):
                          [int(x) for x in st.support[0, 0, (hd - a) % C]]) for a in range(cnt - 1, -1, -1)]
 
 
+def pin_retopk_vote(ref):
+    """Confidence-voted candidates (ReTopK review, 启发 4-5), worked by hand.
+    The current query is 3*e0, so its unit query is e0. Cached unit queries
+    (oldest first): e2, (e0+e1)/sqrt2, e0, with cosines 0, 1/sqrt2 and 1; R=2
+    recalls the last two. Supports: S_A = {5, 13, 21, 29} (cosine 1) and
+    S_B = {2, 5, 8, 13} (cosine 1/sqrt2), so f = 1 + 1/sqrt2 for rows 5 and 13,
+    1 for 21 and 29, 1/sqrt2 for 2 and 8. The recent window is {38, 39}.
+      budget 3 -> 5, 13, then the lowest of the f = 1 rows: {5, 13, 21};
+      budget 5 -> {5, 13, 21, 29, 2} (2 before 8);
+      budget 0 or >= 6 -> the whole union."""
+    d, L_t, K = 4, 40, 4
+    e = np.eye(d, dtype=np.float32)
+    q_hist = np.stack([e[2], e[0] + e[1], e[0]])[None, None]  # [1, 1, 3, d]
+    sup = np.array([[[30, 31, 32, 33], [2, 5, 8, 13], [5, 13, 21, 29]]], dtype=np.int32)[None]
+    rng = np.random.default_rng(3)
+    k = rng.standard_normal((1, 1, L_t, d)).astype(np.float32)
+    v = rng.standard_normal((1, 1, L_t, d)).astype(np.float32)
+    q = (3.0 * e[0])[None, None]
+    union = [2, 5, 8, 13, 21, 29, 38, 39]
+    want = {3: [5, 13, 21, 38, 39], 5: [2, 5, 13, 21, 29, 38, 39], 0: union, 6: union, 9: union}
+    for budget, rows in want.items():
+        p = ref.RetopkParams(top_k=K, cache_cap=3, top_r=2, recent=2, tau=-2.0, refresh=0, budget=budget)
+        st = ref.retopk_state_init(p, q_hist, sup)
+        out, new, tr = ref.retopk_step(p, st, q, k, v, L_t, 1, 0.5)
+        r = tr[(0, 0)]
+        assert r["path"] == 0
+        assert [int(x) for x in r["cand"]] == rows, (budget, r["cand"])
+        # the rerank stays exact inside the (capped) candidates
+        z = ref.scores(q[0, 0], k[0, 0], np.asarray(rows, dtype=np.int64), 0.5)
+        sel, _ = ref.select_topk(z, np.asarray(rows, dtype=np.int64), K)
+        assert [int(x) for x in out["support"][0, 0] if x >= 0] == [int(x) for x in sel]
+
+
+def pin_retopk_vote_brute(ref, seed=0):
+    """Oracle == pure-Python brute force with a candidate budget, over
+    multi-step runs (budgets below, at and above the union size), skipping
+    steps whose recall or vote decision is within 1e-6 of a tie."""
+    for variant in range(3):
+        k, v, qs, L0 = _ar1_setup(seed * 10 + 5 + variant, n_steps=10, L0=40, d=6, Hq=1)
+        sc = 0.5
+        budget = [3, 6, 40][variant]
+        p = ref.RetopkParams(top_k=5, cache_cap=4, top_r=3, recent=3, tau=-2.0, refresh=0, budget=budget)
+        st = _warm_state(ref, p, k, v, qs, L0, 4, sc)
+        C = p.cache_cap
+        kk = [[float(x) for x in row] for row in k[0, 0]]
+        vv = [[float(x) for x in row] for row in v[0, 0]]
+        checked = 0
+        for t in range(10):
+            cnt, hd = int(st.count[0, 0]), int(st.head[0, 0])
+            cache = [([float(x) for x in st.q_hat[0, 0, (hd - a) % C]],
+                      [int(x) for x in st.support[0, 0, (hd - a) % C]]) for a in range(cnt - 1, -1, -1)]
+            L_t = L0 + t + 1
+            out, st2, tr = ref.retopk_step(p, st, qs[8 + t], k, v, L_t, t, sc)
+            r = tr[(0, 0)]
+            bf = brute.retopk_head_step(cache, [float(x) for x in qs[8 + t][0, 0]], kk, vv, L_t, t,
+                                        p.top_k, C, p.top_r, p.recent, p.tau, p.refresh, sc, budget=budget)
+            rs = r["rho_sorted"]
+            near = rs.size > p.top_r and abs(float(rs[p.top_r - 1]) - float(rs[p.top_r])) < 1e-6
+            vt = r["vote"]
+            if vt is not None and vt["cut"] is not None:
+                fc, mc = vt["cut"]
+                near = near or bool(np.any((np.abs(vt["f"].astype(np.float64) - fc) < 1e-6) & (vt["mask"] != mc)))
+            if not near:
+                assert bf["path"] == r["path"] == 0
+                assert bf["cand"] == [int(x) for x in r["cand"]], (variant, t)
+                assert bf["support"] == [int(x) for x in out["support"][0, 0]]
+                checked += 1
+            st = st2
+        assert checked >= 8
+
+
 ALL_PINS = [
     pin_golden_topk, pin_golden_merge, pin_golden_retopk, pin_dense_matches_library_attention,
     pin_split_merge_identity, pin_shift_invariance, pin_argmax_and_weights, pin_brute_topk,
     pin_brute_gamma, pin_merge_algebra, pin_retopk_invariants, pin_retopk_special_cases,
-    pin_retopk_brute, pin_brute_multi_query,
+    pin_retopk_brute, pin_brute_multi_query, pin_retopk_vote, pin_retopk_vote_brute,
 ]

@@ -109,6 +109,21 @@ def m_multi_first_query_only(q, k_cache, ranges, top_k, scale, queries=None):
     return _orig_multi(q0, k_cache, ranges, top_k, scale, queries)
 
 
+_orig_vote = ref.vote_candidates
+
+
+def m_vote_count_only(union_rows, recent_rows, supports, weights, budget):
+    """votes counted without the similarity weights"""
+    return _orig_vote(union_rows, recent_rows, supports, [np.float32(1.0)] * len(weights), budget)
+
+
+def m_vote_ties_to_highest(union_rows, recent_rows, supports, weights, budget):
+    """equal confidence resolved towards the highest row"""
+    flip = lambda x: 10 ** 6 - np.asarray(x, dtype=np.int64)
+    rows, tr = _orig_vote(flip(union_rows), flip(recent_rows), [flip(s) for s in supports], weights, budget)
+    return np.sort(flip(rows)), tr
+
+
 MUTANTS = [
     ("softmax_v", m_no_renormalisation),
     ("select_topk", m_ties_to_highest),
@@ -122,6 +137,8 @@ MUTANTS = [
     ("unit_query_f32", m_no_normalisation),
     ("topk_multi_query", m_multi_head_mapping),
     ("topk_multi_query", m_multi_first_query_only),
+    ("vote_candidates", m_vote_count_only),
+    ("vote_candidates", m_vote_ties_to_highest),
 ]
 
 
