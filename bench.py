@@ -22,7 +22,8 @@ The other workloads are measured the same way when asked for:
               256 decode steps (one row appended per step) from that state.
               --requests B serves B independent requests per step (their own
               caches); --tau and --top-k select the pages' variants (0.90,
-              1024);
+              1024); --budget N caps the voted candidates of the reuse path
+              at N rows (confidence votes over the recalled supports);
   --config 4  batch of 16 sequences x 32,768 rows, K=1024, one
               topk_attn_decode call per step;
   --config 5  1,048,576 rows, K=8192, static window of 640 rows, one-pass step.
@@ -70,8 +71,8 @@ SCAN_SOURCES = ["sparse_top_decode_amd/csrc/scan_kernels.h", "sparse_top_decode_
 METRIC = "top-K decode-attention steps/sec at 128K ctx; K-scan HBM GB/s vs peak"
 TOPK_KERNELS = ("k_scan", "topk_filter", "topk_select", "sparse_sv", "dense_attn", "combine", "attn_merge")
 MQ_KERNELS = ("mq_blockmax", "mq_threshold", "mq_collect", "mq_select")
-RETOPK_KERNELS = ("retopk_select", "retopk_rerank", "retopk_rerank_select", "k_scan", "topk_filter", "topk_select",
-                  "sparse_sv", "combine", "retopk_push")
+RETOPK_KERNELS = ("retopk_select", "retopk_vote", "retopk_rerank", "retopk_rerank_select", "k_scan", "topk_filter",
+                  "topk_select", "sparse_sv", "combine", "retopk_push")
 
 
 def scan_source_hash() -> str:
@@ -143,7 +144,8 @@ def cpu_baseline_retopk(w, p, q_hist, sup_hist, budget_s: float = 12.0):
     """The oracle's ReTopK steps from the same warmed cache, in step order,
     until about budget_s of CPU time has passed."""
     from oracle import reference as ref
-    rp = ref.RetopkParams(p["top_k"], p["cache_cap"], p["top_r"], p["recent"], p["tau"], p["refresh"])
+    rp = ref.RetopkParams(p["top_k"], p["cache_cap"], p["top_r"], p["recent"], p["tau"], p["refresh"],
+                          p.get("budget", 0))
     st = ref.retopk_state_init(rp, q_hist, sup_hist)
     warm, L0 = p["warmup"], p["L0"]
     t0 = time.perf_counter()
@@ -409,10 +411,11 @@ def bench_retopk(args):
         p["tau"] = args.tau
     if args.top_k is not None:
         p["top_k"] = args.top_k
+    p["budget"] = args.budget
     dev, k, v = to_dev(w)
     K, warm, n_steps, L0 = p["top_k"], p["warmup"], p["steps"], p["L0"]
     rt = ops.Retopk(k, w.H_q, top_k=K, cache_cap=p["cache_cap"], top_r=p["top_r"], recent=p["recent"],
-                    tau=p["tau"], refresh=p["refresh"], scale=w.scale)
+                    tau=p["tau"], refresh=p["refresh"], scale=w.scale, budget=p["budget"])
     qall = torch.from_numpy(np.ascontiguousarray(w.q)).to(dev)
     qs = [qall[:, :, j].contiguous() for j in range(warm + n_steps)]
     # the cache starts from the last 32 exact-path queries over the initial rows
@@ -460,7 +463,8 @@ def bench_retopk(args):
     workload = (f"ReTopK decode, Qwen2.5-7B-shaped layer: {B} request(s) per step, 28 q / 4 KV heads, d=128, "
                 f"{L0} initial rows + 1 per step, "
                 f"bf16 K/V, K={K}, C={p['cache_cap']}, R={p['top_r']}, W={p['recent']}, tau={p['tau']}, "
-                f"refresh every {p['refresh']} steps, AR(1) queries; {n_steps} steps per timed pass")
+                f"refresh every {p['refresh']} steps, AR(1) queries; {n_steps} steps per timed pass"
+                + (f"; voted candidates capped at {p['budget']}" if p["budget"] else ""))
     extra = {"batch": B, "seq_len": L0, "top_k": K, "kv_cache": "bf16", "parallelism": "none (1 GPU)",
              "reuse_fraction": round(float(reuse.mean()), 4), "mean_candidates_reuse": round(mean_m, 1),
              "rerank_launches": n_rr}
@@ -516,6 +520,8 @@ def main():
     ap.add_argument("--requests", type=int, default=1, help="workload 3: requests served per step, each with its own caches")
     ap.add_argument("--tau", type=float, default=None, help="workload 3: similarity threshold (default 0.85)")
     ap.add_argument("--top-k", type=int, default=None, help="workloads 3 and 6: K (default 512)")
+    ap.add_argument("--budget", type=int, default=0,
+                    help="workload 3: voted candidates kept on the reuse path (0 = the whole union)")
     ap.add_argument("--L", type=int, default=131072, help="cache length of workload 2")
     ap.add_argument("--layers", type=int, default=4,
                     help="workload 2: distinct K/V caches used in turn, one per layer (1 = the same cache every "

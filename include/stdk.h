@@ -214,6 +214,7 @@ typedef struct retopk_params {
   float tau;         /* similarity threshold: max cosine < tau -> exact path */
   int32_t refresh;   /* T_r: step t with t % T_r == 0 -> exact path; 0 = never */
   float scale;       /* score scale (1/sqrt(d)) */
+  int32_t budget;    /* candidate budget of the reuse path (>= 0; 0 = the whole union); see below */
 } retopk_params;
 
 /* Caller-owned per-query-head state (device memory):
@@ -265,6 +266,13 @@ int32_t retopk_state_init(const stdk_layout* lay, const retopk_params* p, const 
  *               reuse path (-1 padded; all -1 on the exact path); may be NULL.
  *  workspace    at least retopk_workspace_size(lay, p, L_t) bytes,
  *               zero-filled before its first use ("Workspace state" above).
+ * Candidate budget ([RT] "启发 4-5": confidence votes over the recalled
+ * supports, high-confidence rows first under a budget). With budget > 0 the
+ * reuse path keeps the recent rows and, of the other rows of the union, the
+ * `budget` rows of largest f(i) = sum of rho_c over the recalled entries c
+ * whose support holds row i (rho_c added in fp32 in recall order; ties go to
+ * the lowest row); the exact rerank then runs on that set. budget > 0 needs
+ * top_r <= 8 and R*K + W <= 16384 (STDK_EUNSUPPORTED otherwise).
  * Limits: L_t <= 1,048,576 (the candidate bitmap lives in LDS). */
 int32_t retopk_step(const stdk_layout* lay, const retopk_params* p, const retopk_state* st,
                     const float* q, const void* k_cache, const void* v_cache, int64_t L_t,
@@ -290,9 +298,9 @@ int32_t stdk_version(void);        /* STDK_VERSION */
  * milliseconds and the launch count. Families: "k_scan",
  * "topk_filter", "topk_select", "sparse_sv", "dense_attn", "combine",
  * "attn_merge", "fill_empty", "retopk_select", "retopk_rerank",
- * "retopk_rerank_select", "retopk_push", "retopk_init", "mq_blockmax",
- * "mq_threshold", "mq_collect", "mq_fill". Unknown names return
- * STDK_EINVAL. */
+ * "retopk_rerank_select", "retopk_push", "retopk_init", "retopk_vote",
+ * "mq_blockmax", "mq_threshold", "mq_collect", "mq_select", "mq_fill".
+ * Unknown names return STDK_EINVAL. */
 int32_t stdk_profile_enable(int32_t capacity, const char* only);
 int32_t stdk_profile_disable(void);
 int32_t stdk_profile_reset(void);

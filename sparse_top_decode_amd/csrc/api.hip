@@ -57,13 +57,13 @@ int32_t ok() {
 enum KernelId {
   KID_SCAN, KID_FILTER, KID_SELECT, KID_SV, KID_DENSE, KID_COMBINE, KID_MERGE, KID_FILL,
   KID_RT_SELECT, KID_RT_RERANK, KID_RT_RSEL, KID_RT_PUSH, KID_RT_INIT, KID_MQ_BLOCKMAX, KID_MQ_THRESH,
-  KID_MQ_COLLECT, KID_MQ_SELECT, KID_MQ_FILL, KID_COUNT
+  KID_MQ_COLLECT, KID_MQ_SELECT, KID_MQ_FILL, KID_RT_VOTE, KID_COUNT
 };
 const char* const kKernelNames[KID_COUNT] = {
     "k_scan",        "topk_filter",   "topk_select",          "sparse_sv",
     "dense_attn",  "combine",       "attn_merge",    "fill_empty",           "retopk_select",
     "retopk_rerank", "retopk_rerank_select", "retopk_push", "retopk_init", "mq_blockmax",
-    "mq_threshold",  "mq_collect",    "mq_select",     "mq_fill"};
+    "mq_threshold",  "mq_collect",    "mq_select",     "mq_fill",       "retopk_vote"};
 
 struct Profiler {
   std::mutex mu;
@@ -167,6 +167,10 @@ int32_t dev_info(DevInfo** out) {
                               std::max(0, d.max_lds - 12 * 1024));
     (void)hipFuncSetAttribute((const void*)mq_select, hipFuncAttributeMaxDynamicSharedMemorySize,
                               std::max(0, d.max_lds - 1024));
+    (void)hipFuncSetAttribute((const void*)retopk_vote<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              std::max(0, d.max_lds - 4 * 1024));
+    (void)hipFuncSetAttribute((const void*)retopk_vote<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              std::max(0, d.max_lds - 4 * 1024));
     (void)hipGetLastError();
     d.init = true;
   }
@@ -836,6 +840,11 @@ int32_t check_retopk(const stdk_layout* lay, const retopk_params* p, const retop
   if (std::isnan(p->tau)) return fail(STDK_EINVAL, "tau is NaN");
   if (!std::isfinite(p->scale)) return fail(STDK_EINVAL, "scale is not finite");
   if ((int64_t)p->top_r * p->top_k + p->recent > 0x7FFFFFFFLL) return fail(STDK_EINVAL, "R*K + W too large");
+  if (p->budget < 0) return fail(STDK_EINVAL, "budget %d < 0", p->budget);
+  if (p->budget > 0 && p->top_r > kMaxVote)
+    return fail(STDK_EUNSUPPORTED, "a candidate budget needs top_r <= %d (got %d)", kMaxVote, p->top_r);
+  if (p->budget > 0 && (int64_t)p->top_r * p->top_k + p->recent > kVoteMaxCand)
+    return fail(STDK_EUNSUPPORTED, "a candidate budget needs R*K + W <= %d", kVoteMaxCand);
   STDK_TRY(check_ptr(st->q_hat, "state.q_hat", 16));
   STDK_TRY(check_ptr(st->support, "state.support", 4));
   STDK_TRY(check_ptr(st->head, "state.head", 4));
@@ -846,7 +855,7 @@ int32_t check_retopk(const stdk_layout* lay, const retopk_params* p, const retop
 struct RetopkWs {
   TopkWs t;  // exact path
   int64_t cand_cap, words;
-  size_t cand, n_cand, cz, qbar, path, exact, gbitmap, total;
+  size_t cand, n_cand, cz, qbar, path, exact, gbitmap, rec_slot, rec_rho, total;
 };
 
 RetopkWs retopk_ws(const Geo& g, const retopk_params* p, int64_t L) {
@@ -869,6 +878,10 @@ RetopkWs retopk_ws(const Geo& g, const retopk_params* p, int64_t L) {
   off = al256(off + (size_t)g.S * 4);
   r.gbitmap = off;
   off = al256(off + (size_t)g.S * r.words * 4);
+  r.rec_slot = off;
+  off = al256(off + (size_t)g.S * kMaxVote * 4);
+  r.rec_rho = off;
+  off = al256(off + (size_t)g.S * kMaxVote * 4);
   r.total = off;
   return r;
 }
@@ -947,11 +960,45 @@ int32_t retopk_step(const stdk_layout* lay, const retopk_params* p, const retopk
     a.n_cand_out = n_cand_out;
     a.cand_out = cand_out;
     a.gbitmap = (uint32_t*)(ws + w.gbitmap);
+    if (p->budget > 0) {
+      a.rec_slot = (int32_t*)(ws + w.rec_slot);
+      a.rec_rho = (float*)(ws + w.rec_rho);
+    }
     const size_t bm_bytes = (size_t)w.words * 4;
     const bool lds = bm_bytes + 12 * 1024 <= (size_t)di->max_lds;
     STDK_TRY(launch(KID_RT_SELECT, s, [&](hipEvent_t e0, hipEvent_t e1) {
       if (lds) STDK_LAUNCH(retopk_select<true>, dim3((unsigned)g.S), dim3(kRtSelThreads), bm_bytes, s, a);
       else STDK_LAUNCH(retopk_select<false>, dim3((unsigned)g.S), dim3(kRtSelThreads), 0, s, a);
+    }));
+  }
+  // confidence vote: cap the candidates of the reuse heads
+  if (p->budget > 0 && !refresh_now) {
+    RtVoteArgs a{};
+    a.exact = exact;
+    a.support = st->support;
+    a.count = st->count;
+    a.rec_slot = (const int32_t*)(ws + w.rec_slot);
+    a.rec_rho = (const float*)(ws + w.rec_rho);
+    a.cand = (int32_t*)(ws + w.cand);
+    a.n_cand = (int32_t*)(ws + w.n_cand);
+    a.n_cand_out = n_cand_out;
+    a.cand_out = cand_out;
+    a.L_t = L_t;
+    a.C = p->cache_cap;
+    a.K = p->top_k;
+    a.R = p->top_r;
+    a.W = p->recent;
+    a.cand_cap = (int32_t)w.cand_cap;
+    a.budget = p->budget;
+    // candidates and their masks, then (when they fit) the masks of every
+    // row below the recent window
+    const size_t base = (size_t)w.cand_cap * 4 + (((size_t)w.cand_cap + 15) & ~(size_t)15);
+    const size_t with_rows = base + (size_t)rup(std::max<int64_t>(L_t, 1), 4);
+    const bool row_masks = with_rows + 4 * 1024 <= (size_t)di->max_lds;
+    const size_t dyn = row_masks ? with_rows : base + 16;
+    STDK_TRY(launch(KID_RT_VOTE, s, [&](hipEvent_t e0, hipEvent_t e1) {
+      if (row_masks) STDK_LAUNCH(retopk_vote<true>, dim3((unsigned)g.S), dim3(kVoteThreads), dyn, s, a);
+      else STDK_LAUNCH(retopk_vote<false>, dim3((unsigned)g.S), dim3(kVoteThreads), dyn, s, a);
     }));
   }
   // exact heads: scan + select + softmax.V over [0, L_t)

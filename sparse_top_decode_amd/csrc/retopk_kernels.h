@@ -73,10 +73,13 @@ struct RtSelArgs {
   int32_t* n_cand_out;      // [S] or null
   int32_t* cand_out;        // [S][cand_cap] or null
   uint32_t* gbitmap;        // [S][bitmap_words] when not in LDS
+  int32_t* rec_slot;        // [S][kMaxVote] recalled slots in recall order, or null (no vote)
+  float* rec_rho;           // [S][kMaxVote] their cosines
 };
 
 constexpr int kRtSelThreads = 256;
 constexpr int kMaxCache = 64;
+constexpr int kMaxVote = 8;  // recalled entries a confidence vote can weigh (masks fit a byte)
 
 template <bool kLdsBitmap>
 __global__ __launch_bounds__(kRtSelThreads) void retopk_select(RtSelArgs a) {
@@ -182,6 +185,10 @@ __global__ __launch_bounds__(kRtSelThreads) void retopk_select(RtSelArgs a) {
         if (rf > re || (rf == re && age_f < age_e)) ++rank;
       }
       pk = rank < a.R;
+      if (pk && a.rec_slot && rank < kMaxVote) {
+        a.rec_slot[seg * kMaxVote + rank] = tid;
+        a.rec_rho[seg * kMaxVote + rank] = re;
+      }
     }
     picked[tid] = pk;
   }
@@ -248,6 +255,200 @@ __global__ __launch_bounds__(kRtSelThreads) void retopk_select(RtSelArgs a) {
     const int32_t M = (int32_t)min(total, (uint32_t)a.cand_cap);
     for (int i = tid; i < a.cand_cap; i += kRtSelThreads)
       a.cand_out[seg * a.cand_cap + i] = i < M ? cd[i] : -1;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// retopk_vote: confidence-voted candidates (ReTopK review, "启发 4-5"). The
+// access confidence of row i is f(i) = sum over the recalled entries c of
+// w_c * [i in S_c], with w_c the entry's cosine, added in fp32 in recall
+// order; rows of the union outside the recent window (which is always kept)
+// are capped at `budget`, keeping the largest f, ties to the lowest row.
+// One workgroup per reuse-path head, on retopk_select's ascending candidate
+// list. A row's membership is a byte mask (bit r: in the support of the r-th
+// recalled entry), so f takes at most 2^R values: a histogram over the masks
+// gives the cut, and an ordered compaction rewrites the list. kRowMasks: the
+// masks of all visible rows [0, L_t) fit in LDS and are set directly from
+// the supports; otherwise every support row is looked up in the list.
+// Dynamic LDS: candidates [cand_cap] int32, masks [cand_cap] bytes, then
+// (kRowMasks) row masks [L_t] bytes.
+// ---------------------------------------------------------------------------
+struct RtVoteArgs {
+  const int32_t* exact;     // [S]
+  const int32_t* support;   // [S][C][K]
+  const int32_t* count;     // [S] valid cache entries (the recalled ones are min(R, count))
+  const int32_t* rec_slot;  // [S][kMaxVote]
+  const float* rec_rho;     // [S][kMaxVote]
+  int32_t* cand;            // [S][cand_cap], rewritten
+  int32_t* n_cand;          // [S], rewritten
+  int32_t* n_cand_out;      // [S] or null
+  int32_t* cand_out;        // [S][cand_cap] or null
+  int64_t L_t;
+  int32_t C, K, R, W, cand_cap, budget;
+};
+
+constexpr int kVoteThreads = 256;
+constexpr int kVoteMaxCand = 16384;  // R*K + W a voting head may hold (LDS)
+
+template <bool kRowMasks>
+__global__ __launch_bounds__(kVoteThreads) void retopk_vote(RtVoteArgs a) {
+  extern __shared__ __attribute__((aligned(16))) int32_t vdyn[];
+  __shared__ uint32_t hist[1 << kMaxVote];
+  __shared__ float fm[1 << kMaxVote];
+  __shared__ uint32_t tmp[2 * (kVoteThreads / 64) + 2];
+  __shared__ int s_mv;
+  __shared__ float s_fc;
+  __shared__ uint32_t s_need;
+  const int64_t seg = blockIdx.x;
+  // the head's flags, counts and recall slots are requested together
+  const int ex = a.exact[seg];
+  const int M = a.n_cand[seg];
+  const int cnt = a.count[seg];
+  int slot[kMaxVote];
+#pragma unroll
+  for (int r = 0; r < kMaxVote; ++r) slot[r] = a.rec_slot[seg * kMaxVote + r];
+  if (ex) return;
+  const int tid = threadIdx.x;
+  const int64_t lo_recent = a.L_t - a.W > 0 ? a.L_t - a.W : 0;
+  int32_t* cl = vdyn;
+  uint8_t* mk = reinterpret_cast<uint8_t*>(vdyn + a.cand_cap);
+  int32_t* cd = a.cand + seg * a.cand_cap;
+  {
+    // the list, 8 loads per thread in flight
+    constexpr int kU = 8;
+    for (int i0 = 0; i0 < M; i0 += kVoteThreads * kU) {
+      int32_t x[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) x[u] = cd[min(i0 + u * kVoteThreads + tid, M - 1)];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int i = i0 + u * kVoteThreads + tid;
+        if (i < M) {
+          cl[i] = x[u];
+          mk[i] = 0;
+        }
+      }
+    }
+  }
+  for (int i = tid; i < (1 << kMaxVote); i += kVoteThreads) hist[i] = 0u;
+  __syncthreads();
+  // voted rows: the candidates below the recent window (a prefix of the list)
+  if (tid == 0) {
+    int lo = 0, hi = M;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if ((int64_t)cl[mid] < lo_recent) lo = mid + 1;
+      else hi = mid;
+    }
+    s_mv = lo;
+  }
+  __syncthreads();
+  const int Mv = s_mv;
+  if (Mv <= a.budget) return;  // nothing to cap: the select's list stands
+  const int nrec = min(a.R, cnt);  // R <= kMaxVote, checked on the host
+  const int total = nrec * a.K;
+  if constexpr (kRowMasks) {
+    // masks of the voted rows [0, lo_recent), set straight from the supports
+    uint32_t* rm = reinterpret_cast<uint32_t*>(mk + ((a.cand_cap + 15) & ~15));
+    const int nw = (int)((lo_recent + 3) >> 2);
+    for (int i = tid; i < nw; i += kVoteThreads) rm[i] = 0u;
+    __syncthreads();
+    constexpr int kU = 8;
+    for (int f0 = 0; f0 < total; f0 += kVoteThreads * kU) {
+      int32_t x[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int f = min(f0 + u * kVoteThreads + tid, total - 1);
+        const int r = f / a.K;
+        int sl = slot[0];
+#pragma unroll
+        for (int j = 1; j < kMaxVote; ++j) sl = r == j ? slot[j] : sl;
+        x[u] = a.support[((int64_t)seg * a.C + sl) * a.K + (f - r * a.K)];
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int f = f0 + u * kVoteThreads + tid;
+        if (f < total && x[u] >= 0 && (int64_t)x[u] < lo_recent)
+          atomicOr(&rm[x[u] >> 2], 1u << (8 * (x[u] & 3) + f / a.K));
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < Mv; i += kVoteThreads) mk[i] = (uint8_t)(rm[cl[i] >> 2] >> (8 * (cl[i] & 3)));
+  } else {
+    // membership: every support row of a recalled entry, found in the list
+    int top = 1;
+    while (top * 2 <= Mv) top *= 2;
+    for (int f = tid; f < total; f += kVoteThreads) {
+      const int r = f / a.K, e = f - r * a.K;
+      const int32_t x = a.support[((int64_t)seg * a.C + a.rec_slot[seg * kMaxVote + r]) * a.K + e];
+      if (x < 0 || (int64_t)x >= lo_recent) continue;
+      int lo = 0;  // last index with cl[lo] <= x
+      for (int step = top; step > 0; step >>= 1) {
+        const int t = lo + step;
+        const int32_t v = cl[min(t, Mv - 1)];
+        lo = (t < Mv && v <= x) ? t : lo;
+      }
+      if (cl[lo] == x) atomicOr(reinterpret_cast<uint32_t*>(mk) + (lo >> 2), 1u << (8 * (lo & 3) + r));
+    }
+  }
+  // confidence of each mask, in recall order
+  if (tid < (1 << nrec)) {
+    float f = 0.f;
+    for (int r = 0; r < nrec; ++r)
+      if ((tid >> r) & 1) f = f + a.rec_rho[seg * kMaxVote + r];
+    fm[tid] = f;
+  }
+  __syncthreads();
+  for (int i = tid; i < Mv; i += kVoteThreads) atomicAdd(&hist[mk[i]], 1u);
+  __syncthreads();
+  // the cut: the confidence group holding the budget-th row
+  if (tid < (1 << nrec) && hist[tid] > 0u) {
+    const float f = fm[tid];
+    uint32_t above = 0, same = 0;
+    for (int m = 0; m < (1 << nrec); ++m) {
+      if (fm[m] > f) above += hist[m];
+      else if (fm[m] == f) same += hist[m];
+    }
+    if (above < (uint32_t)a.budget && (uint32_t)a.budget <= above + same) {
+      s_fc = f;  // every mask of the group writes the same values
+      s_need = (uint32_t)a.budget - above;
+    }
+  }
+  __syncthreads();
+  const float fc = s_fc;
+  const uint32_t need = s_need;
+  // ordered compaction of the voted rows, then the recent window
+  const int per = (Mv + kVoteThreads - 1) / kVoteThreads;
+  const int i0 = min(Mv, tid * per), i1 = min(Mv, i0 + per);
+  uint32_t n_gt = 0, n_eq = 0;
+  for (int i = i0; i < i1; ++i) {
+    const float f = fm[mk[i]];
+    n_gt += f > fc;
+    n_eq += f == fc;
+  }
+  uint32_t gt_before, eq_before, tot_gt, tot_eq;
+  block_excl_scan2<kVoteThreads>(n_gt, n_eq, tmp, &gt_before, &eq_before, &tot_gt, &tot_eq);
+  uint32_t r = gt_before + min(eq_before, need);
+  uint32_t eq_seen = eq_before;
+  for (int i = i0; i < i1; ++i) {
+    const float f = fm[mk[i]];
+    bool take = f > fc;
+    if (f == fc) {
+      take = eq_seen < need;
+      ++eq_seen;
+    }
+    if (take) cd[r++] = cl[i];
+  }
+  const int kept = (int)(tot_gt + min(tot_eq, need));
+  for (int i = Mv + tid; i < M; i += kVoteThreads) cd[kept + (i - Mv)] = cl[i];
+  const int Mn = kept + (M - Mv);
+  if (tid == 0) {
+    a.n_cand[seg] = Mn;
+    if (a.n_cand_out) a.n_cand_out[seg] = Mn;
+  }
+  if (a.cand_out) {
+    __syncthreads();
+    for (int i = tid; i < a.cand_cap; i += kVoteThreads) a.cand_out[seg * a.cand_cap + i] = i < Mn ? cd[i] : -1;
   }
 }
 

@@ -41,7 +41,7 @@ class Layout(ctypes.Structure):
 
 class RetopkParams(ctypes.Structure):
     _fields_ = [("top_k", c_int32), ("cache_cap", c_int32), ("top_r", c_int32), ("recent", c_int32),
-                ("tau", c_float), ("refresh", c_int32), ("scale", c_float)]
+                ("tau", c_float), ("refresh", c_int32), ("scale", c_float), ("budget", c_int32)]
 
 
 class RetopkState(ctypes.Structure):

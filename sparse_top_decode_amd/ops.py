@@ -166,13 +166,13 @@ class Retopk:
 
     def __init__(self, k_cache: torch.Tensor, n_q_heads: int, top_k: int = 512, cache_cap: int = 32,
                  top_r: int = 4, recent: int = 32, tau: float = 0.85, refresh: int = 128,
-                 scale: Optional[float] = None, max_len_t: Optional[int] = None):
+                 scale: Optional[float] = None, max_len_t: Optional[int] = None, budget: int = 0):
         load()
         self.layout = make_layout(k_cache, n_q_heads)
         B, Hkv, L, d = k_cache.shape
         self.B, self.Hq, self.d = B, n_q_heads, d
         self.params = RetopkParams(top_k, cache_cap, top_r, recent, float(tau), refresh,
-                                   float(1.0 / math.sqrt(d) if scale is None else scale))
+                                   float(1.0 / math.sqrt(d) if scale is None else scale), int(budget))
         dev = k_cache.device
         self.q_hat = torch.zeros((B, n_q_heads, cache_cap, d), dtype=torch.float32, device=dev)
         self.support = torch.full((B, n_q_heads, cache_cap, top_k), -1, dtype=torch.int32, device=dev)

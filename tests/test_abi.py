@@ -152,6 +152,11 @@ def test_retopk_rejects(lib):
     assert step(lib, good, L=lay(Hq=28, Hkv=4, L=4096, d=96)) == native.STDK_EUNSUPPORTED
     big = lay(Hq=28, Hkv=4, L=2_000_000)
     assert step(lib, good, L=big, L_t=1_500_000) == native.STDK_EUNSUPPORTED
+    # candidate budget: >= 0, at most 8 recalled entries, R*K + W within the vote's LDS
+    assert step(lib, RetopkParams(64, 8, 2, 8, 0.85, 16, 0.088, -1)) == native.STDK_EINVAL
+    assert step(lib, RetopkParams(64, 16, 9, 8, 0.85, 16, 0.088, 100)) == native.STDK_EUNSUPPORTED
+    assert step(lib, RetopkParams(4096, 8, 4, 8, 0.85, 16, 0.088, 100), L=lay(Hq=28, Hkv=4, L=8192),
+                L_t=5000) == native.STDK_EUNSUPPORTED
 
 
 def call_mq(lib, L=None, M=4, ranges=((0, 100),), top_k=8, ws_bytes=1 << 30, q=FAKE, scale=0.1, idx=FAKE, z=None):

@@ -2,7 +2,8 @@
 step the GPU's cache state is copied to the host, the oracle runs the same
 step from it, and path, candidate set, support, o, lse and the pushed state
 are compared. A step whose decision is within 1e-6 of a tie (best cosine vs
-tau, or the R-th vs (R+1)-th cosine) is flagged, not failed."""
+tau, the R-th vs (R+1)-th cosine, or, with a candidate budget, two different
+vote sums at the cut) is flagged, not failed."""
 
 import numpy as np
 import pytest
@@ -48,7 +49,7 @@ def run_lockstep(ops, w, p, n_steps, heads, n_warm, check_every=1):
     L0 = w.retopk["L0"]
     k, v = dev_kv(w)
     rt = ops.Retopk(k, w.H_q, top_k=p.top_k, cache_cap=p.cache_cap, top_r=p.top_r, recent=p.recent, tau=p.tau,
-                    refresh=p.refresh, scale=w.scale)
+                    refresh=p.refresh, scale=w.scale, budget=p.budget)
     qh, sh = warm_cache(ops, w, rt, k, v, n_warm, p.top_k)
     # the cache after init equals the oracle's init from the same history
     st0 = ref.retopk_state_init(p, qh, sh)
@@ -57,7 +58,7 @@ def run_lockstep(ops, w, p, n_steps, heads, n_warm, check_every=1):
     assert np.array_equal(g0.head, st0.head) and np.array_equal(g0.count, st0.count)
     assert np.max(np.abs(g0.q_hat - st0.q_hat)) < 1e-6
     G = w.H_q // w.H_kv
-    stats = dict(reuse=0, exact=0, flagged=0, cand=[], swaps=0)
+    stats = dict(reuse=0, exact=0, flagged=0, cand=[], swaps=0, capped=0)
     for t in range(n_steps):
         L_t = L0 + t + 1
         qt = np.ascontiguousarray(w.q[:, :, n_warm + t])
@@ -75,6 +76,11 @@ def run_lockstep(ops, w, p, n_steps, heads, n_warm, check_every=1):
             rs = r["rho_sorted"]
             near = rs.size > 0 and (abs(float(rs[0]) - p.tau) < NEAR or
                                     (rs.size > p.top_r and abs(float(rs[p.top_r - 1]) - float(rs[p.top_r])) < NEAR))
+            vt = r.get("vote")
+            if vt is not None and vt["cut"] is not None:
+                fc, mc = vt["cut"]
+                near = near or bool(np.any((np.abs(vt["f"].astype(np.float64) - fc) < NEAR) & (vt["mask"] != mc)))
+                stats["capped"] += 1
             if near:
                 stats["flagged"] += 1
                 continue
@@ -164,3 +170,29 @@ def test_retopk_c3_full_lockstep(ops):
     s = run_lockstep(ops, w, p, P["steps"], heads, n_warm=P["warmup"])
     log(f"retopk c3 full: reuse {s['reuse']} exact {s['exact']} flagged {s['flagged']} "
         f"mean M {np.mean(s['cand']) if s['cand'] else 0:.0f} (parity unpinned: context only) band swaps {s['swaps']}")
+
+
+@pytest.mark.parametrize("budget", [100, 40])
+def test_retopk_vote_lockstep(ops, budget):
+    """Confidence-voted candidates (R = 4): the union outside the recent
+    window is capped at the budget by vote confidence; 40 leaves fewer
+    candidates than K = 64 (padded supports)."""
+    w = make_workload(3, L=4096, steps=30, warm=8)
+    p = ref.RetopkParams(top_k=64, cache_cap=8, top_r=4, recent=16, tau=0.85, refresh=10, budget=budget)
+    heads = [(0, h) for h in range(28)]
+    s = run_lockstep(ops, w, p, 30, heads, n_warm=8)
+    log(f"retopk vote budget {budget}: reuse {s['reuse']} exact {s['exact']} capped {s['capped']} "
+        f"flagged {s['flagged']} mean M {np.mean(s['cand']) if s['cand'] else 0:.0f}")
+    assert s["reuse"] > 0 and s["capped"] > 0
+
+
+def test_retopk_vote_full_size_sampled(ops):
+    """The c3 layout at full size (65,536 rows, K = 512, R = 4, W = 32) with a
+    budget of 600 voted rows, 6 steps checked on 8 heads."""
+    w = make_workload(3, steps=6, warm=32)
+    p = ref.RetopkParams(top_k=512, cache_cap=32, top_r=4, recent=32, tau=0.85, refresh=128, budget=600)
+    heads = [(0, h) for h in (0, 3, 7, 11, 15, 19, 23, 27)]
+    s = run_lockstep(ops, w, p, 6, heads, n_warm=32)
+    log(f"retopk vote full size: reuse {s['reuse']} capped {s['capped']} flagged {s['flagged']} "
+        f"mean M {np.mean(s['cand']) if s['cand'] else 0:.0f}")
+    assert s["reuse"] > 0
