@@ -152,3 +152,39 @@ def retopk_head_step(cache: List[Tuple[List[float], List[int]]], q: Sequence[flo
     while len(cache) > C:
         cache.pop(0)
     return dict(path=path, cand=(rows if path == 0 else None), support=sup, o=res["o"], lse=res["lse"])
+
+
+def quantize_row_int8(k: Sequence[float]) -> Tuple[List[int], float]:
+    """One key row to symmetric int8: scale = max |k| / 127, code = the
+    nearest integer to k / scale (halves to even), each step one fp32
+    operation; a zero row gives scale 0 and zero codes."""
+    import numpy as np
+    big = np.float32(0.0)
+    for x in k:
+        ax = np.float32(abs(np.float32(x)))
+        if ax > big:
+            big = ax
+    s = np.float32(big / np.float32(127.0))
+    if s == 0:
+        return [0] * len(k), 0.0
+    codes = []
+    for x in k:
+        t = float(np.float32(np.float32(x) / s))
+        f = math.floor(t)
+        frac = t - f
+        c = f + 1 if frac > 0.5 or (frac == 0.5 and f % 2 != 0) else f
+        codes.append(int(max(-127, min(127, c))))
+    return codes, float(s)
+
+
+def int8_recall_attention(q: Sequence[float], keys: Sequence[Sequence[float]], values: Sequence[Sequence[float]],
+                          rows: Sequence[int], k: int, recall_k: int, scale: float) -> Dict:
+    """Two-stage top-K of one head: the recall_k rows of largest score on the
+    int8 rows (scale_i * code_i), then top-K attention on the exact keys of
+    those rows."""
+    q8 = {r: quantize_row_int8(keys[r]) for r in rows}
+    z8 = [scale * q8[r][1] * math.fsum(a * b for a, b in zip(q, q8[r][0])) for r in rows]
+    sup = topk_members(z8, list(rows), recall_k)
+    res = topk_attention(q, keys, values, sup, k, scale)
+    res["sup"] = sup
+    return res

@@ -170,6 +170,72 @@ def topk_attn_decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
 
 
 # --------------------------------------------------------------------------
+# int8 keys as a recall stage ([RA] "CPU memory minimization (Appendix C)":
+# 8-bit scalar quantization of the key vectors, scheme left open; the review
+# asks whether quantized keys shift the nearest-key rankings, so here the
+# int8 scores only choose a superset and the exact scores decide inside it)
+# --------------------------------------------------------------------------
+def quantize_keys_int8(rows: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Per-row symmetric int8 codes of stored key rows [..., d] (bf16 bits or
+    fp32). Reading (the pages give no scheme): s = max_j |k_j| / 127 and
+    c_j = round-half-even(k_j / s), both one correctly rounded fp32 operation,
+    clamped to [-127, 127]; a row of zeros has s = 0 and codes 0. Returns
+    (codes int8 [..., d], scales float32 [...])."""
+    k = widen(rows).astype(np.float32)  # exact: bf16 and fp32 values are fp32
+    maxabs = np.max(np.abs(k), axis=-1).astype(np.float32)
+    s = (maxabs / np.float32(127.0)).astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    c = np.rint((k / safe[..., None]).astype(np.float32))
+    c = np.clip(c, -127, 127)
+    c = np.where((s > 0)[..., None], c, 0)
+    return c.astype(np.int8), s
+
+
+def int8_scores(q: np.ndarray, codes_head: np.ndarray, scales_head: np.ndarray, rows: np.ndarray,
+                scale: float) -> np.ndarray:
+    """Scores of q against the dequantized rows s_i * c_i, in fp64."""
+    qd = np.asarray(q, dtype=np.float64)
+    out = np.empty(rows.shape[0], dtype=np.float64)
+    for a in range(0, rows.shape[0], _ROW_CHUNK):
+        r = rows[a:a + _ROW_CHUNK]
+        c = codes_head[r].astype(np.float64)
+        out[a:a + r.shape[0]] = (c * qd[None, :]).sum(axis=1) * scales_head[r].astype(np.float64) * scale
+    return out
+
+
+def topk_attn_decode_int8(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, codes: np.ndarray,
+                          scales: np.ndarray, ranges: Sequence[Tuple[int, int]], top_k: int, recall_k: int,
+                          scale: float, heads: Optional[Sequence[Tuple[int, int]]] = None) -> Dict:
+    """Top-K attention with an int8 recall stage: S' = the recall_k rows of
+    largest int8 score (ties to the lowest row), then S = the top_k rows of
+    largest exact score inside S' (ties to the lowest row), then the
+    renormalised softmax . V over S ([RA] Eq. 2). codes [B, H_kv, L_max, d]
+    int8 and scales [B, H_kv, L_max] as quantize_keys_int8 gives them.
+    Returns idx [B, H_q, K], the superset sup [B, H_q, K'] (both ascending,
+    -1 padded), o, lse and zk8 (the K'-th int8 score)."""
+    B, Hq, d = q.shape
+    G = Hq // k_cache.shape[1]
+    rows = range_rows(ranges)
+    K, K2 = int(top_k), int(recall_k)
+    idx = np.full((B, Hq, K), -2, dtype=np.int32)
+    sup = np.full((B, Hq, K2), -2, dtype=np.int32)
+    o = np.full((B, Hq, d), np.nan)
+    lse = np.full((B, Hq), np.nan)
+    zk8 = np.full((B, Hq), np.nan)
+    todo = heads if heads is not None else [(b, h) for b in range(B) for h in range(Hq)]
+    for b, h in todo:
+        hk = h // G
+        z8 = int8_scores(q[b, h], codes[b, hk], scales[b, hk], rows, scale)
+        s8, zk8[b, h] = select_topk(z8, rows, K2)
+        r = attend_rows(q[b, h], k_cache[b, hk], v_cache[b, hk], s8, K, scale)
+        sup[b, h] = pad_rows(s8, K2)
+        idx[b, h] = pad_rows(r["rows"], K)
+        o[b, h] = r["o"]
+        lse[b, h] = r["lse"]
+    return dict(idx=idx, sup=sup, o=o, lse=lse, zk8=zk8)
+
+
+# --------------------------------------------------------------------------
 # multi-query exact top-K: the index sets of a block of queries, each the
 # exact TopK of its own scores over the ranges ([RT] "Exact Top-K 的隐藏成本":
 # S_t = TopK(e, K); "核心方法" 1: the cache holds the supports of the last

@@ -535,9 +535,88 @@ def pin_retopk_vote_brute(ref, seed=0):
         assert checked >= 8
 
 
+def pin_int8_quantization(ref):
+    """Per-row symmetric int8 codes (RetrievalAttention review, "CPU memory
+    minimization (Appendix C)"): a row on the integer grid of its scale comes
+    back exactly (0.5 * [127, -64, 3, ...] -> scale 0.5 and those integers);
+    a zero row gives scale 0; codes lie in [-127, 127], reach +-127 at the
+    largest |k|, are odd under k -> -k, and dequantize within half a step;
+    the pure-Python quantizer agrees code for code."""
+    grid = np.array([127, -64, 3, 0, 1, -1, 2, 5, -127, 100, 64, -3], dtype=np.float32)
+    c, s = ref.quantize_keys_int8((0.5 * grid)[None])
+    assert float(s[0]) == 0.5 and np.array_equal(c[0].astype(np.int64), grid.astype(np.int64))
+    c0, s0 = ref.quantize_keys_int8(np.zeros((1, 12), np.float32))
+    assert float(s0[0]) == 0.0 and not np.any(c0)
+    rng = np.random.default_rng(21)
+    k = (rng.standard_normal((40, 16)) * rng.uniform(0.01, 30, (40, 1))).astype(np.float32)
+    k[3, 5] = 0.0
+    c, s = ref.quantize_keys_int8(k)
+    cn, sn = ref.quantize_keys_int8(-k)
+    assert np.array_equal(sn, s) and np.array_equal(cn, -c)
+    ci = c.astype(np.int64)
+    assert np.all(np.abs(ci) <= 127)
+    am = np.argmax(np.abs(k), axis=1)
+    assert np.all(np.abs(ci[np.arange(40), am]) == 127)
+    err = np.abs(k.astype(np.float64) - s.astype(np.float64)[:, None] * ci)
+    assert np.all(err <= 0.5 * s.astype(np.float64)[:, None] * (1 + 1e-6))
+    for i in range(40):
+        bc, bs = brute.quantize_row_int8([float(x) for x in k[i]])
+        assert bs == float(s[i]) and bc == [int(x) for x in ci[i]], i
+    # bf16 rows: the codes of the widened values
+    kb = (k.view(np.uint32) >> 16).astype(np.uint16)
+    cb, sb = ref.quantize_keys_int8(kb)
+    cw, sw = ref.quantize_keys_int8((kb.astype(np.uint32) << 16).view(np.float32))
+    assert np.array_equal(cb, cw) and np.array_equal(sb, sw)
+
+
+def pin_int8_recall(ref):
+    """The int8 recall stage: with recall_k >= n it is exact top-K attention;
+    with keys on the int8 grid (k = s * c exactly) the int8 scores are the
+    exact scores, so recall_k = K gives the exact set too; the final set lies
+    in the superset and is the exact top-K of it; a pure-Python two-stage
+    brute force agrees on small inputs."""
+    rng = np.random.default_rng(22)
+    d, L = 8, 60
+    q = rng.standard_normal((1, 2, d)).astype(np.float32)
+    k = rng.standard_normal((1, 1, L, d)).astype(np.float32)
+    v = rng.standard_normal((1, 1, L, d)).astype(np.float32)
+    ranges = [(3, 25), (30, 58)]
+    codes, scales = ref.quantize_keys_int8(k)
+    sc = 0.3
+    ex = ref.topk_attn_decode(q, k, v, ranges, 6, sc)
+    full = ref.topk_attn_decode_int8(q, k, v, codes, scales, ranges, 6, 100, sc)
+    assert np.array_equal(full["idx"], ex["idx"])
+    np.testing.assert_allclose(full["o"], ex["o"], rtol=0, atol=1e-12)
+    # keys on the grid: codes times a power-of-two scale per row
+    cg = rng.integers(-127, 128, (1, 1, L, d)).astype(np.float32)
+    cg[..., 0] = 127.0
+    kg = (cg * np.float32(2.0) ** rng.integers(-4, 3, (1, 1, L, 1))).astype(np.float32)
+    cq, sq = ref.quantize_keys_int8(kg)
+    assert np.array_equal(cq.astype(np.float32), cg)
+    exg = ref.topk_attn_decode(q, kg, v, ranges, 6, sc)
+    g6 = ref.topk_attn_decode_int8(q, kg, v, cq, sq, ranges, 6, 6, sc)
+    assert np.array_equal(g6["idx"], exg["idx"])
+    # nesting, and agreement with the brute force
+    r = ref.topk_attn_decode_int8(q, k, v, codes, scales, ranges, 5, 9, sc)
+    rows = ref.range_rows(ranges)
+    kk = [[float(x) for x in row] for row in k[0, 0]]
+    vv = [[float(x) for x in row] for row in v[0, 0]]
+    for h in range(2):
+        sup = [int(x) for x in r["sup"][0, h] if x >= 0]
+        fin = [int(x) for x in r["idx"][0, h] if x >= 0]
+        assert len(sup) == 9 and set(fin) <= set(sup)
+        z = ref.scores(q[0, h], k[0, 0], np.asarray(sup, dtype=np.int64), sc)
+        sel, _ = ref.select_topk(z, np.asarray(sup, dtype=np.int64), 5)
+        assert [int(x) for x in sel] == fin
+        bf = brute.int8_recall_attention([float(x) for x in q[0, h]], kk, vv, [int(x) for x in rows], 5, 9, sc)
+        assert bf["sup"] == sup and bf["rows"] == fin
+        np.testing.assert_allclose(r["o"][0, h], bf["o"], rtol=1e-10, atol=1e-12)
+
+
 ALL_PINS = [
     pin_golden_topk, pin_golden_merge, pin_golden_retopk, pin_dense_matches_library_attention,
     pin_split_merge_identity, pin_shift_invariance, pin_argmax_and_weights, pin_brute_topk,
     pin_brute_gamma, pin_merge_algebra, pin_retopk_invariants, pin_retopk_special_cases,
     pin_retopk_brute, pin_brute_multi_query, pin_retopk_vote, pin_retopk_vote_brute,
+    pin_int8_quantization, pin_int8_recall,
 ]

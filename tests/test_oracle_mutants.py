@@ -124,6 +124,24 @@ def m_vote_ties_to_highest(union_rows, recent_rows, supports, weights, budget):
     return np.sort(flip(rows)), tr
 
 
+_orig_int8_scores = ref.int8_scores
+_orig_quant = ref.quantize_keys_int8
+
+
+def m_int8_no_row_scale(q, codes_head, scales_head, rows, scale):
+    """int8 scores without the per-row scale"""
+    return _orig_int8_scores(q, codes_head, np.ones_like(scales_head), rows, scale)
+
+
+def m_int8_truncating_codes(rows):
+    """codes truncated towards zero instead of rounded"""
+    k = ref.widen(rows).astype(np.float32)
+    c, s = _orig_quant(rows)
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    t = np.trunc((k / safe[..., None]).astype(np.float32))
+    return np.where((s > 0)[..., None], np.clip(t, -127, 127), 0).astype(np.int8), s
+
+
 MUTANTS = [
     ("softmax_v", m_no_renormalisation),
     ("select_topk", m_ties_to_highest),
@@ -139,6 +157,8 @@ MUTANTS = [
     ("topk_multi_query", m_multi_first_query_only),
     ("vote_candidates", m_vote_count_only),
     ("vote_candidates", m_vote_ties_to_highest),
+    ("int8_scores", m_int8_no_row_scale),
+    ("quantize_keys_int8", m_int8_truncating_codes),
 ]
 
 
