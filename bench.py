@@ -27,6 +27,12 @@ The other workloads are measured the same way when asked for:
   --config 4  batch of 16 sequences x 32,768 rows, K=1024, one
               topk_attn_decode call per step;
   --config 5  1,048,576 rows, K=8192, static window of 640 rows, one-pass step.
+  --int8-recall K'  (workloads 2 and 5) the dynamic rows go through the int8
+              recall stage instead: a scan of per-row int8 key codes (made
+              before timing, one set per layer cache) picks K' rows, the
+              exact keys choose K among them; then the static window and the
+              merge as three calls. Not exact; the line reports the share of
+              the exact top-K rows that the step chose.
   --config 6  multi-query exact top-K of the c3 prefill block: the 32 warm-up
               queries of all 28 query heads over the 65,536 initial rows,
               K=512, one topk_multi_query call per step (the products run on
@@ -138,6 +144,36 @@ def cpu_baseline_topk(w, budget_s: float = 12.0, seqs=None, heads=None):
     return dict(value=reps * frac / el, unit="steps/s", cores=1, kind="oracle",
                 sample=f"{reps} decode step(s) of the timed workload on {scope} ({what}), {el:.1f} s on one host "
                        f"thread (numpy fp64, no BLAS); value scaled to whole steps")
+
+
+def cpu_baseline_int8(w, K2: int, heads, budget_s: float = 12.0):
+    """The oracle's int8-recall decode step (quantization of the dynamic rows
+    included) on a stated sample of query heads, scaled to whole steps."""
+    import numpy as np
+    from oracle import reference as ref
+    B, Hq = w.q.shape[0], w.q.shape[1]
+    sel = [(0, h) for h in heads]
+    rows = ref.range_rows(w.ranges)
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        kvh = sorted({h // (Hq // w.H_kv) for h in heads})
+        codes = np.zeros(w.k.shape, dtype=np.int8)
+        scales = np.zeros(w.k.shape[:3], dtype=np.float32)
+        for hk in kvh:
+            codes[0, hk, rows], scales[0, hk, rows] = ref.quantize_keys_int8(w.k[0, hk, rows])
+        dyn = ref.topk_attn_decode_int8(w.q, w.k, w.v, codes, scales, w.ranges, w.top_k, K2, w.scale, heads=sel)
+        stat = ref.topk_attn_decode(w.q, w.k, w.v, w.static_ranges, w.top_k, w.scale, heads=sel)
+        ref.attn_merge_lse(stat["o"], stat["lse"], dyn["o"], dyn["lse"])
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 20:
+            break
+    frac = len(sel) / float(B * Hq)
+    return dict(value=reps * frac / el, unit="steps/s", cores=1, kind="oracle",
+                sample=f"{reps} int8-recall decode step(s) on {len(sel)} of {B * Hq} query heads (quantization of "
+                       f"their KV heads' dynamic rows, int8 top-{K2}, exact top-K inside, static dense, merge), "
+                       f"{el:.1f} s on one host thread (numpy fp64, no BLAS); value scaled to whole steps")
 
 
 def cpu_baseline_retopk(w, p, q_hist, sup_hist, budget_s: float = 12.0):
@@ -343,7 +379,26 @@ def bench_topk(args, cfg):
     o_m = torch.empty((B, w.H_q, 128), dtype=torch.float32, device=dev)
     l_m = torch.empty((B, w.H_q), dtype=torch.float32, device=dev)
     path = args.path if n_stat else "top-k only"
-    if n_stat and args.path == "one-pass":
+    q8 = None
+    if args.int8_recall and cfg in (2, 5):
+        path = f"int8 recall K'={args.int8_recall} + static dense + merge"
+        q8 = [ops.quantize_keys_int8(kc, w.ranges, w.H_q, layout=lay) for kc, _ in caches]
+        ws_d = ops.new_workspace(ops.topk_attn_decode_int8_workspace_size(lay, n_dyn, K, args.int8_recall), dev)
+        ws_s = ops.new_workspace(ops.topk_attn_decode_workspace_size(lay, n_stat, K), dev)
+        o_d, l_d, o_s, l_s = (torch.empty_like(o_m), torch.empty_like(l_m), torch.empty_like(o_m),
+                              torch.empty_like(l_m))
+
+        def step():
+            i = layer["i"]
+            k, v = caches[i]
+            codes, scales = q8[i]
+            layer["i"] = (i + 1) % n_layers
+            ops.topk_attn_decode_int8(q, k, v, codes, scales, w.ranges, K, args.int8_recall, w.scale, idx_out=idx,
+                                      o_out=o_d, lse_out=l_d, workspace=ws_d, layout=lay)
+            ops.topk_attn_decode(q, k, v, w.static_ranges, K, w.scale, o_out=o_s, lse_out=l_s, workspace=ws_s,
+                                 want_idx=False, layout=lay)
+            ops.attn_merge_lse(o_s, l_s, o_d, l_d, o_out=o_m, lse_out=l_m)
+    elif n_stat and args.path == "one-pass":
         ws_f = ops.new_workspace(ops.topk_attn_decode_static_workspace_size(lay, n_dyn, n_stat, K), dev)
 
         def step():
@@ -379,9 +434,17 @@ def bench_topk(args, cfg):
     torch.cuda.synchronize()
     graph = capture(step) if args.graph == "on" else None
     names = TOPK_KERNELS if args.kernel_events == "on" else ()
+    if q8 is not None:
+        names = names + ("retopk_rerank", "retopk_rerank_select") if names else ()
     ms, kern = timed_passes(step, args.steps, names, graph=graph)
-    scan_bytes = B * w.H_kv * n_dyn * 256  # every dynamic key row once, bf16 d=128
-    roof = roofline(kern, "k_scan", scan_bytes, committed_traffic(cfg))
+    if q8 is None:
+        scan_bytes = B * w.H_kv * n_dyn * 256  # every dynamic key row once, bf16 d=128
+        roof = roofline(kern, "k_scan", scan_bytes, committed_traffic(cfg))
+    else:
+        # the scan reads the int8 codes (128 B) and the scale (4 B) of every
+        # dynamic row; the static window's dense pass does not use k_scan
+        scan_bytes = B * w.H_kv * n_dyn * (128 + 4)
+        roof = roofline(kern, "k_scan", scan_bytes, None)
     if cfg == 4:
         workload = (f"batched decode attention: {B} sequences x {w.L} rows, 32 q / 8 KV heads (Llama-3-8B layout), "
                     f"d=128, bf16 K/V with per-sequence key offsets, top-K={K} per (sequence, query head)")
@@ -392,9 +455,24 @@ def bench_topk(args, cfg):
         if cfg == 5:
             workload += " (64 planted rows per query head)"
         sample_heads = None if cfg == 2 else [0, 9, 18, 27]
-        cpu = None if args.no_cpu else cpu_baseline_topk(w, heads=sample_heads)
+        cpu = None if args.no_cpu or q8 is not None else cpu_baseline_topk(w, heads=sample_heads)
     extra = {"batch": B, "seq_len": w.L, "top_k": K, "kv_cache": "bf16", "parallelism": "none (1 GPU)",
              "path": path, "hip_graph": graph is not None, "layer_caches": n_layers}
+    if q8 is not None:
+        # share of the exact top-K rows the int8 step chose (layer 0's cache)
+        k0c, v0c = caches[0]
+        ex_idx, _, _ = ops.topk_attn_decode(q, k0c, v0c, w.ranges, K, w.scale, layout=lay)
+        q8_idx, _, _, _ = ops.topk_attn_decode_int8(q, k0c, v0c, q8[0][0], q8[0][1], w.ranges, K, args.int8_recall,
+                                                    w.scale, layout=lay)
+        torch.cuda.synchronize()
+        a_ = ex_idx.cpu().numpy()
+        b_ = q8_idx.cpu().numpy()
+        import numpy as np
+        rec = np.mean([np.isin(a_[0, h][a_[0, h] >= 0], b_[0, h]).mean() for h in range(a_.shape[1])])
+        extra["recall_vs_exact"] = round(float(rec), 5)
+        extra["int8_recall_k"] = args.int8_recall
+        workload += f"; dynamic rows through the int8 recall stage (K'={args.int8_recall}), not exact"
+        cpu = None if args.no_cpu else cpu_baseline_int8(w, args.int8_recall, [0, 9, 18, 27])
     return line(args, ms, workload, extra, roof, kern, cpu)
 
 
@@ -520,6 +598,8 @@ def main():
     ap.add_argument("--requests", type=int, default=1, help="workload 3: requests served per step, each with its own caches")
     ap.add_argument("--tau", type=float, default=None, help="workload 3: similarity threshold (default 0.85)")
     ap.add_argument("--top-k", type=int, default=None, help="workloads 3 and 6: K (default 512)")
+    ap.add_argument("--int8-recall", type=int, default=0, metavar="K2",
+                    help="workloads 2 and 5: top-K' superset from int8 key codes, exact top-K inside it (0 = off)")
     ap.add_argument("--budget", type=int, default=0,
                     help="workload 3: voted candidates kept on the reuse path (0 = the whole union)")
     ap.add_argument("--L", type=int, default=131072, help="cache length of workload 2")

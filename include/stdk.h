@@ -189,6 +189,48 @@ size_t topk_multi_query_workspace_size(const stdk_layout* lay, int32_t n_queries
                                        int32_t top_k);
 
 /* ------------------------------------------------------------------------
+ * int8 keys as a recall stage. [RA] "CPU memory minimization (Appendix C)"
+ * proposes 8-bit scalar quantization of the key vectors without fixing a
+ * scheme, and the review asks whether quantized keys shift the nearest-key
+ * rankings; here the int8 codes only choose a superset and the exact keys
+ * decide inside it.
+ *
+ * quantize_keys_int8: per-row symmetric codes of the rows in `ranges`:
+ *   s = max_j |k_j| / 127,  c_j = k_j / s rounded to nearest (halves to even),
+ *   each a correctly rounded fp32 operation, clamped to [-127, 127]; a zero
+ *   row gives s = 0 and codes 0.
+ *  codes    [B][H_kv][max_len][128] int8 (16-byte aligned), packed whatever
+ *           the cache strides are; only the rows in `ranges` are written.
+ *  scales   [B][H_kv][max_len] fp32.
+ *  Limits: B * n_kv_heads <= 65535.
+ * ---------------------------------------------------------------------- */
+int32_t quantize_keys_int8(const stdk_layout* lay, const void* k_cache, const int64_t* ranges,
+                           int32_t n_ranges, int8_t* codes, float* scales, void* stream);
+
+/* topk_attn_decode_int8: for every (b, h_q), S' = the recall_k rows of the
+ * ranges with the largest z'_i = scale * s_i * (q . c_i) (ties to the lowest
+ * row), S = the top_k rows of S' with the largest exact z_i (ties to the
+ * lowest row), then o and lse over S as topk_attn_decode ([RA] Eq. 2). With
+ * recall_k >= n, S' is every row and the result is topk_attn_decode's.
+ *  codes, scales  as quantize_keys_int8 wrote them for every row of `ranges`.
+ *  top_k >= 1, recall_k >= top_k; recall_k <= 65536 when below n.
+ *  idx_out  [B][H_q][top_k] int32 or NULL: S, ascending, -1 padded.
+ *  sup_out  [B][H_q][recall_k] int32 or NULL: S', ascending, -1 padded.
+ *  o_out, lse_out as topk_attn_decode.
+ *  workspace at least topk_attn_decode_int8_workspace_size(lay, n, top_k,
+ *           recall_k) bytes, in the "Workspace state" above.
+ * Not exact: a row outside S' cannot be chosen. */
+int32_t topk_attn_decode_int8(const stdk_layout* lay, const float* q, const void* k_cache,
+                              const void* v_cache, const int8_t* codes, const float* scales,
+                              const int64_t* ranges, int32_t n_ranges, int32_t top_k,
+                              int32_t recall_k, float scale, int32_t* idx_out, int32_t* sup_out,
+                              float* o_out, float* lse_out, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+size_t topk_attn_decode_int8_workspace_size(const stdk_layout* lay, int64_t n_scan, int32_t top_k,
+                                            int32_t recall_k);
+
+/* ------------------------------------------------------------------------
  * attn_merge_lse — [RA] Eq. 4-5: combination of two partial attention
  * outputs over disjoint row sets a and b:
  *     M = max(lse_a, lse_b),  lse = M + ln(e^{lse_a - M} + e^{lse_b - M}),
@@ -299,7 +341,8 @@ int32_t stdk_version(void);        /* STDK_VERSION */
  * "topk_filter", "topk_select", "sparse_sv", "dense_attn", "combine",
  * "attn_merge", "fill_empty", "retopk_select", "retopk_rerank",
  * "retopk_rerank_select", "retopk_push", "retopk_init", "retopk_vote",
- * "mq_blockmax", "mq_threshold", "mq_collect", "mq_select", "mq_fill".
+ * "mq_blockmax", "mq_threshold", "mq_collect", "mq_select", "mq_fill",
+ * "k_quantize".
  * Unknown names return STDK_EINVAL. */
 int32_t stdk_profile_enable(int32_t capacity, const char* only);
 int32_t stdk_profile_disable(void);

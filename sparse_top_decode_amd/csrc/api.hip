@@ -17,6 +17,7 @@
 #include "attend_kernels.h"
 #include "device.h"
 #include "mq_kernels.h"
+#include "q8_kernels.h"
 #include "retopk_kernels.h"
 #include "scan_kernels.h"
 #include "select_kernels.h"
@@ -57,13 +58,13 @@ int32_t ok() {
 enum KernelId {
   KID_SCAN, KID_FILTER, KID_SELECT, KID_SV, KID_DENSE, KID_COMBINE, KID_MERGE, KID_FILL,
   KID_RT_SELECT, KID_RT_RERANK, KID_RT_RSEL, KID_RT_PUSH, KID_RT_INIT, KID_MQ_BLOCKMAX, KID_MQ_THRESH,
-  KID_MQ_COLLECT, KID_MQ_SELECT, KID_MQ_FILL, KID_RT_VOTE, KID_COUNT
+  KID_MQ_COLLECT, KID_MQ_SELECT, KID_MQ_FILL, KID_RT_VOTE, KID_Q8_QUANT, KID_COUNT
 };
 const char* const kKernelNames[KID_COUNT] = {
     "k_scan",        "topk_filter",   "topk_select",          "sparse_sv",
     "dense_attn",  "combine",       "attn_merge",    "fill_empty",           "retopk_select",
     "retopk_rerank", "retopk_rerank_select", "retopk_push", "retopk_init", "mq_blockmax",
-    "mq_threshold",  "mq_collect",    "mq_select",     "mq_fill",       "retopk_vote"};
+    "mq_threshold",  "mq_collect",    "mq_select",     "mq_fill",       "retopk_vote",   "k_quantize"};
 
 struct Profiler {
   std::mutex mu;
@@ -125,7 +126,7 @@ struct DevInfo {
   bool init = false;
   int max_lds = 65536;
   int n_cu = 256;
-  int scan_occ[2][STDK_MAX_GROUP + 1] = {};  // resident k_scan workgroups per CU, by (bf16, G)
+  int scan_occ[3][STDK_MAX_GROUP + 1] = {};  // resident k_scan workgroups per CU, by (fp32 / bf16 / int8, G)
 };
 std::mutex g_dev_mu;
 DevInfo g_dev[64];
@@ -161,6 +162,7 @@ int32_t dev_info(DevInfo** out) {
     d.n_cu = v;
     occ_row<float>(d.scan_occ[0]);
     occ_row<uint16_t>(d.scan_occ[1]);
+    occ_row<int8_t>(d.scan_occ[2]);
     const int dyn_max = std::max(0, d.max_lds - (int)kSelStaticLds);
     (void)hipFuncSetAttribute((const void*)topk_select, hipFuncAttributeMaxDynamicSharedMemorySize, dyn_max);
     (void)hipFuncSetAttribute((const void*)retopk_select<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -348,9 +350,17 @@ void launch_dense_t(int G, dim3 grid, hipStream_t s, const DenseArgs& a, hipEven
 // workspace) is zero on entry and the select kernel leaves it zero again.
 // Leaves the chosen rows and scores in the workspace. `active` restricts the
 // work to the listed segments (ReTopK exact heads); null = all.
+// int8 key codes and their row scales (packed: [B][H_kv][max_len][128] and
+// [B][H_kv][max_len]), scanned instead of the cache by the int8 recall stage
+struct Q8Keys {
+  const int8_t* codes;
+  const float* scales;
+  int64_t max_len;
+};
+
 int32_t run_exact_select(const Geo& g, const TopkWs& w, char* ws, const float* q, const void* k_cache,
                          const RangeTab& tab, float scale, const int32_t* active, int32_t* idx_out,
-                         const DevInfo* di, hipStream_t s) {
+                         const DevInfo* di, hipStream_t s, const Q8Keys* q8 = nullptr) {
   float* scores = (float*)(ws + w.scores);
   uint32_t* hist = (uint32_t*)(ws + w.hist);
   Cand* list = (Cand*)(ws + w.list);
@@ -361,6 +371,15 @@ int32_t run_exact_select(const Geo& g, const TopkWs& w, char* ws, const float* q
     a.k = (const char*)k_cache;
     a.stride_b_bytes = g.sb_bytes;
     a.stride_h_bytes = g.sh_bytes;
+    if (q8) {
+      a.k = (const char*)q8->codes;
+      a.stride_h_bytes = q8->max_len * kHeadDim;
+      a.stride_b_bytes = (int64_t)g.Hkv * a.stride_h_bytes;
+      a.kscale = q8->scales;
+      a.kscale_stride_h = q8->max_len;
+      a.kscale_stride_b = (int64_t)g.Hkv * q8->max_len;
+    }
+    const int ti = q8 ? 2 : (g.bf16 ? 1 : 0);
     a.scores = scores;
     a.hist = hist;
     a.n = w.n + w.n_extra;
@@ -371,9 +390,9 @@ int32_t run_exact_select(const Geo& g, const TopkWs& w, char* ws, const float* q
     a.scale = scale;
     a.head_active = active;
     a.tab = tab;
-    const int ri = g.bf16 ? scan_rows_iter<uint16_t>(g.G) : scan_rows_iter<float>(g.G);
+    const int ri = q8 ? scan_rows_iter<int8_t>(g.G) : (g.bf16 ? scan_rows_iter<uint16_t>(g.G) : scan_rows_iter<float>(g.G));
     // one resident wave of workgroups over the whole chip, whole iterations each
-    const int64_t target_blocks = (int64_t)di->n_cu * di->scan_occ[g.bf16 ? 1 : 0][g.G];
+    const int64_t target_blocks = (int64_t)di->n_cu * di->scan_occ[ti][g.G];
     const int64_t per_group = std::max<int64_t>(1, cdiv(target_blocks, g.groups));
     const int64_t rpb = std::max<int64_t>(ri, rup(cdiv(a.n, per_group), ri));
     a.rows_per_block = rpb;
@@ -381,7 +400,7 @@ int32_t run_exact_select(const Geo& g, const TopkWs& w, char* ws, const float* q
     // stage the scores in LDS, in chunks of whole iterations that fit
     // beside the histogram (row stride padded so that the G rows start on
     // different banks)
-    const int occ = di->scan_occ[g.bf16 ? 1 : 0][g.G];
+    const int occ = di->scan_occ[ti][g.G];
     const int64_t lds_free = std::min<int64_t>(kScanStageMax, (int64_t)di->max_lds / occ - (int64_t)g.G * kHistBins * 4 - 1024);
     const int64_t chunk = std::min<int64_t>(rpb, (lds_free / (4 * g.G) - 16) / ri * ri);
     if (chunk >= ri) {
@@ -390,7 +409,8 @@ int32_t run_exact_select(const Geo& g, const TopkWs& w, char* ws, const float* q
     }
     const dim3 grid((unsigned)(g.groups * a.blocks_per_group));
     STDK_TRY(launch(KID_SCAN, s, [&](hipEvent_t e0, hipEvent_t e1) {
-      if (g.bf16) launch_scan_t<uint16_t>(g.G, grid, s, a, e0, e1);
+      if (q8) launch_scan_t<int8_t>(g.G, grid, s, a, e0, e1);
+      else if (g.bf16) launch_scan_t<uint16_t>(g.G, grid, s, a, e0, e1);
       else launch_scan_t<float>(g.G, grid, s, a, e0, e1);
     }));
   }
@@ -609,6 +629,37 @@ int32_t run_multi_query(const Geo& g, const MqWs& w, char* ws, const float* q, i
   return STDK_OK;
 }
 
+// ---------------------------------------------------------------------------
+// top-K with the int8 recall stage: workspace
+// ---------------------------------------------------------------------------
+// [the int8 scan's top-K' workspace] [exact scores of the superset]
+// [chosen rows, scores and softmax.V partials of the final top-K]
+struct Q8Ws {
+  TopkWs t1;  // scan of the codes, top-K' superset
+  TopkWs t2;  // view for softmax . V over the final K rows
+  size_t cz, total;
+};
+
+Q8Ws q8_ws(const Geo& g, int64_t n, int64_t K, int64_t K2) {
+  Q8Ws w{};
+  w.t1 = topk_ws(g.S, n, K2);
+  size_t off = w.t1.total;
+  w.cz = off;
+  off = al256(off + (size_t)g.S * K2 * 4);
+  w.t2 = w.t1;
+  w.t2.K = K;
+  w.t2.ksel = K;
+  w.t2.nsplit = cdiv(K, kSvRows);
+  w.t2.sel_row = off;
+  off = al256(off + (size_t)g.S * K * 4);
+  w.t2.sel_z = off;
+  off = al256(off + (size_t)g.S * K * 4);
+  w.t2.part = off;
+  off = al256(off + (size_t)g.S * w.t2.nsplit * kPartStride * 4);
+  w.total = off;
+  return w;
+}
+
 // Host-side validation of one ascending, disjoint list of [begin, end) ranges.
 int32_t check_ranges(const stdk_layout* lay, const int64_t* ranges, int32_t n_ranges, const char* what) {
   if (n_ranges < 0 || n_ranges > STDK_MAX_RANGES)
@@ -799,6 +850,137 @@ int32_t topk_multi_query(const stdk_layout* lay, const float* q, int32_t n_queri
   DevInfo* di = nullptr;
   STDK_TRY(dev_info(&di));
   STDK_TRY(run_multi_query(g, w, (char*)workspace, q, n_queries, k_cache, tab, scale, idx_out, z_out, di, s));
+  return ok();
+}
+
+int32_t quantize_keys_int8(const stdk_layout* lay, const void* k_cache, const int64_t* ranges, int32_t n_ranges,
+                           int8_t* codes, float* scales, void* stream) {
+  STDK_TRY(check_layout(lay));
+  STDK_TRY(check_ptr(k_cache, "k_cache", 16));
+  STDK_TRY(check_ptr(codes, "codes", 16));
+  STDK_TRY(check_ptr(scales, "scales", 4));
+  STDK_TRY(check_ranges(lay, ranges, n_ranges, "ranges"));
+  int64_t n = 0;
+  const RangeTab tab = make_tab(ranges, n_ranges, &n);
+  if (n == 0) return ok();
+  const Geo g = geo_of(lay);
+  if (g.groups > 65535) return fail(STDK_EUNSUPPORTED, "batch * n_kv_heads = %lld > 65535", (long long)g.groups);
+  hipStream_t s = (hipStream_t)stream;
+  QuantArgs a{};
+  a.k = (const char*)k_cache;
+  a.stride_b_bytes = g.sb_bytes;
+  a.stride_h_bytes = g.sh_bytes;
+  a.codes = codes;
+  a.scales = scales;
+  a.max_len = lay->max_len;
+  a.n = n;
+  a.Hkv = g.Hkv;
+  a.tab = tab;
+  const int rpb = (kQuantThreads / 64) * (g.bf16 ? KvTraits<uint16_t>::RPL : KvTraits<float>::RPL);
+  const dim3 grid((unsigned)cdiv(n, rpb), (unsigned)g.groups);
+  STDK_TRY(launch(KID_Q8_QUANT, s, [&](hipEvent_t e0, hipEvent_t e1) {
+    if (g.bf16) STDK_LAUNCH(k_quantize<uint16_t>, grid, dim3(kQuantThreads), 0, s, a);
+    else STDK_LAUNCH(k_quantize<float>, grid, dim3(kQuantThreads), 0, s, a);
+  }));
+  return ok();
+}
+
+size_t topk_attn_decode_int8_workspace_size(const stdk_layout* lay, int64_t n_scan, int32_t top_k, int32_t recall_k) {
+  if (check_layout(lay) != STDK_OK || n_scan < 0 || top_k < 1 || recall_k < top_k) return 0;
+  const Geo g = geo_of(lay);
+  return std::max(q8_ws(g, n_scan, top_k, recall_k).total, topk_ws(g.S, n_scan, top_k).total);
+}
+
+int32_t topk_attn_decode_int8(const stdk_layout* lay, const float* q, const void* k_cache, const void* v_cache,
+                              const int8_t* codes, const float* scales, const int64_t* ranges, int32_t n_ranges,
+                              int32_t top_k, int32_t recall_k, float scale, int32_t* idx_out, int32_t* sup_out,
+                              float* o_out, float* lse_out, void* workspace, size_t workspace_bytes, void* stream) {
+  STDK_TRY(check_layout(lay));
+  STDK_TRY(check_ptr(q, "q", 16));
+  STDK_TRY(check_ptr(k_cache, "k_cache", 16));
+  STDK_TRY(check_ptr(v_cache, "v_cache", 16));
+  STDK_TRY(check_ptr(codes, "codes", 16));
+  STDK_TRY(check_ptr(scales, "scales", 4));
+  STDK_TRY(check_ptr(o_out, "o_out", 4));
+  STDK_TRY(check_ptr(lse_out, "lse_out", 4));
+  if (idx_out && ((uintptr_t)idx_out) % 4) return fail(STDK_EINVAL, "idx_out is not 4-byte aligned");
+  if (sup_out && ((uintptr_t)sup_out) % 4) return fail(STDK_EINVAL, "sup_out is not 4-byte aligned");
+  if (top_k < 1) return fail(STDK_EINVAL, "top_k %d < 1", top_k);
+  if (recall_k < top_k) return fail(STDK_EINVAL, "recall_k %d < top_k %d", recall_k, top_k);
+  if (!std::isfinite(scale)) return fail(STDK_EINVAL, "scale is not finite");
+  STDK_TRY(check_ranges(lay, ranges, n_ranges, "ranges"));
+  int64_t n = 0;
+  const RangeTab tab = make_tab(ranges, n_ranges, &n);
+  if (recall_k > kMaxTopK && recall_k < n)
+    return fail(STDK_EUNSUPPORTED, "recall_k %d > %d (below the row count)", recall_k, kMaxTopK);
+  const Geo g = geo_of(lay);
+  hipStream_t s = (hipStream_t)stream;
+  DevInfo* di = nullptr;
+  if (n > 0) {
+    STDK_TRY(check_ptr(workspace, "workspace", 256));
+    const size_t need = topk_attn_decode_int8_workspace_size(lay, n, top_k, recall_k);
+    if (workspace_bytes < need) return fail(STDK_EWORKSPACE, "workspace is %zu bytes, %zu needed", workspace_bytes, need);
+    STDK_TRY(dev_info(&di));
+  }
+  char* ws = (char*)workspace;
+  if (n == 0 || recall_k >= n) {
+    // the superset is every row: exact top-K attention (the superset output
+    // lists every row)
+    const TopkWs w = topk_ws(g.S, n, top_k);
+    if (n == 0) {
+      const int64_t m = std::max<int64_t>(g.S * kHeadDim, g.S * (int64_t)top_k);
+      STDK_TRY(launch(KID_FILL, s, [&](hipEvent_t e0, hipEvent_t e1) {
+        STDK_LAUNCH(fill_empty, dim3((unsigned)cdiv(m, 256)), dim3(256), 0, s, o_out, lse_out, idx_out, g.S, top_k);
+      }));
+    } else if (top_k >= n) {
+      STDK_TRY(run_dense(g, w, ws, q, k_cache, v_cache, tab, scale, top_k, idx_out, o_out, lse_out, s));
+    } else {
+      STDK_TRY(run_exact_select(g, w, ws, q, k_cache, tab, scale, nullptr, idx_out, di, s));
+      STDK_TRY(run_sv(g, w, ws, v_cache, o_out, lse_out, s, &tab));
+    }
+    if (sup_out) {
+      STDK_TRY(launch(KID_FILL, s, [&](hipEvent_t e0, hipEvent_t e1) {
+        STDK_LAUNCH(fill_rows, dim3((unsigned)cdiv(g.S * (int64_t)recall_k, 256)), dim3(256), 0, s, sup_out, g.S,
+                    recall_k, tab);
+      }));
+    }
+    return ok();
+  }
+  const Q8Ws w = q8_ws(g, n, top_k, recall_k);
+  const Q8Keys keys{codes, scales, lay->max_len};
+  // the superset: top-K' of the int8 scores
+  STDK_TRY(run_exact_select(g, w.t1, ws, q, nullptr, tab, scale, nullptr, sup_out, di, s, &keys));
+  // exact scores of the superset rows, then the top-K among them
+  {
+    RtRerankArgs a{};
+    a.q = q;
+    a.k = (const char*)k_cache;
+    a.stride_b_bytes = g.sb_bytes;
+    a.stride_h_bytes = g.sh_bytes;
+    a.exact = nullptr;
+    a.cand = (const int32_t*)(ws + w.t1.sel_row);
+    a.n_cand = nullptr;
+    a.n_const = recall_k;
+    a.cz = (float*)(ws + w.cz);
+    a.sel_row = (int32_t*)(ws + w.t2.sel_row);
+    a.sel_z = (float*)(ws + w.t2.sel_z);
+    a.support_out = idx_out ? idx_out : (int32_t*)(ws + w.t2.sel_row);
+    a.cand_cap = recall_k;
+    a.K = top_k;
+    a.Hq = g.Hq;
+    a.G = g.G;
+    a.nsplit = (int32_t)cdiv(recall_k, kRerankRows);
+    a.scale = scale;
+    const dim3 grid((unsigned)a.nsplit, (unsigned)g.S);
+    STDK_TRY(launch(KID_RT_RERANK, s, [&](hipEvent_t e0, hipEvent_t e1) {
+      if (g.bf16) STDK_LAUNCH(retopk_rerank<uint16_t>, grid, dim3(kRerankThreads), 0, s, a);
+      else STDK_LAUNCH(retopk_rerank<float>, grid, dim3(kRerankThreads), 0, s, a);
+    }));
+    STDK_TRY(launch(KID_RT_RSEL, s, [&](hipEvent_t e0, hipEvent_t e1) {
+      STDK_LAUNCH(retopk_rerank_select, dim3((unsigned)g.S), dim3(kRerankSelThreads), 0, s, a);
+    }));
+  }
+  STDK_TRY(run_sv(g, w.t2, ws, v_cache, o_out, lse_out, s));
   return ok();
 }
 

@@ -326,6 +326,15 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge(MergeArgs a) {
 // ---------------------------------------------------------------------------
 // small utility kernels
 // ---------------------------------------------------------------------------
+// Every row of the ranges, ascending, in each of S lists of K (-1 padded).
+__global__ __launch_bounds__(256) void fill_rows(int32_t* out, int64_t S, int32_t K, RangeTab tab) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= S * K) return;
+  const int64_t p = i % K;
+  out[i] = p < tab.pos0[tab.n] ? (int32_t)pos_to_row(tab, p) : -1;
+}
+
+// ---------------------------------------------------------------------------
 // Empty row set: o = 0, lse = -inf, idx = -1.
 __global__ __launch_bounds__(256) void fill_empty(float* o, float* lse, int32_t* idx, int64_t S, int32_t K) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;

@@ -467,6 +467,7 @@ struct RtRerankArgs {
   int32_t* support_out;     // [S][K]
   int32_t cand_cap, K, Hq, G, nsplit;
   float scale;
+  int32_t n_const;          // candidates per head when n_cand is null (exact and n_cand null: every head reranks)
 };
 
 constexpr int kRerankThreads = 256;
@@ -478,12 +479,12 @@ __global__ __launch_bounds__(kRerankThreads) void retopk_rerank(RtRerankArgs a) 
   constexpr int NW = kRerankThreads / 64;
   constexpr int GROUPS = NW * RPL;
   const int64_t seg = blockIdx.y;
-  if (a.exact[seg]) return;
+  if (a.exact && a.exact[seg]) return;
   const int split = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int rg = lane / LPR, c = lane % LPR;
   const int b = (int)(seg / a.Hq), hq = (int)(seg % a.Hq), hkv = hq / a.G;
-  const int M = a.n_cand[seg];
+  const int M = a.n_cand ? a.n_cand[seg] : a.n_const;
   const int32_t* cd = a.cand + seg * a.cand_cap;
   float* cz = a.cz + seg * a.cand_cap;
 
@@ -526,9 +527,9 @@ __global__ __launch_bounds__(kRerankSelThreads) void retopk_rerank_select(RtRera
   __shared__ int s_bin;
   __shared__ uint32_t s_beyond;
   const int64_t seg = blockIdx.x;
-  if (a.exact[seg]) return;
+  if (a.exact && a.exact[seg]) return;
   const int tid = threadIdx.x;
-  const uint32_t M = (uint32_t)a.n_cand[seg];
+  const uint32_t M = (uint32_t)(a.n_cand ? a.n_cand[seg] : a.n_const);
   const int32_t* cd = a.cand + seg * a.cand_cap;
   const float* cz = a.cz + seg * a.cand_cap;
   const int K = a.K;

@@ -40,6 +40,15 @@ STDK_DEV void unpack16<float>(const u32x4& w, float* x) {
   x[0] = __uint_as_float(w.x); x[1] = __uint_as_float(w.y);
   x[2] = __uint_as_float(w.z); x[3] = __uint_as_float(w.w);
 }
+// int8 key codes (the int8 recall stage): 16 signed bytes
+template <>
+STDK_DEV void unpack16<int8_t>(const u32x4& w, float* x) {
+  const uint32_t v[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[4 * i + e] = (float)(int32_t)(int8_t)((v[i] >> (8 * e)) & 0xFFu);
+}
 
 // Loads into registers the EPL query values this lane multiplies, for the
 // G query heads starting at q + seg0*128.
@@ -90,6 +99,9 @@ struct ScanArgs {
   int64_t n_hist;              // positions below this are counted in the histogram; the rest are scored only
   int32_t stage_stride;        // > 0: scores are staged in LDS (G rows of this stride) and written in chunks
   int32_t stage_rows;          // positions per staged chunk (a multiple of the rows per iteration)
+  const float* kscale;         // int8 keys only: per-row scales, element (b, h_kv, row) at
+  int64_t kscale_stride_b;     //   b*kscale_stride_b + h_kv*kscale_stride_h + row
+  int64_t kscale_stride_h;
   RangeTab tab;
 };
 
@@ -105,7 +117,7 @@ constexpr int kScanThreads = 512;
 template <typename T, int G>
 struct ScanShape {
   static constexpr int GP = G <= 1 ? 1 : (G <= 2 ? 2 : (G <= 4 ? 4 : 8));
-  static constexpr int LPR = GP == 8 ? 16 : 8;
+  static constexpr int LPR = GP == 8 && sizeof(T) > 1 ? 16 : 8;  // an int8 row is 8 chunks
   static constexpr int ROWB = (int)sizeof(T) * kHeadDim;
   static constexpr int NCH = ROWB / (LPR * 16);
   static constexpr int EPC = 16 / (int)sizeof(T);
@@ -183,6 +195,7 @@ STDK_DEV int lane_perm(int c, bool* out_lane) {
 template <typename T, int G>
 __global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
   using Sh = ScanShape<T, G>;
+  constexpr bool kQ8 = sizeof(T) == 1;  // int8 codes: score = scale * row scale * (q . code)
   constexpr int GP = Sh::GP, LPR = Sh::LPR, NCH = Sh::NCH, EPC = Sh::EPC, E = Sh::E, UR = Sh::UR, V = Sh::V;
   constexpr int RPW = Sh::RPW, ROWB = Sh::ROWB, IT = Sh::ROWS_ITER;
   __shared__ __attribute__((aligned(16))) uint32_t lh[G * kHistBins];
@@ -208,6 +221,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
   }
 
   const char* kb = a.k + (int64_t)b * a.stride_b_bytes + (int64_t)hkv * a.stride_h_bytes + c * 16;
+  const float* ksb = kQ8 ? a.kscale + (int64_t)b * a.kscale_stride_b + (int64_t)hkv * a.kscale_stride_h : nullptr;
   const int64_t p_beg = (int64_t)blk * a.rows_per_block;
   const int64_t p_end = min(a.n, p_beg + a.rows_per_block);
   // current piece of the block's positions: [s0, s1) inside range r
@@ -227,19 +241,21 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
   // row slot s of an iteration at `base` holds row (s ^ rowperm); loads past
   // the piece are clamped to its last row and their results dropped, so every
   // load is issued unconditionally
-  auto issue = [&](int64_t base, u32x4 (&kw)[UR][NCH]) {
+  auto issue = [&](int64_t base, u32x4 (&kw)[UR][NCH], float (&sc)[UR]) {
 #pragma unroll
     for (int s = 0; s < UR; ++s) {
       const int64_t p = min(base + (int64_t)(w * UR + (s ^ rowperm)) * RPW + rg, s1 - 1);
       const char* rp = kb + (p + rowoff) * ROWB;
 #pragma unroll
       for (int k = 0; k < NCH; ++k) kw[s][k] = load16(rp + k * LPR * 16);
+      if constexpr (kQ8) sc[s] = ksb[p + rowoff];
     }
   };
   u32x4 kw[2][UR][NCH];
+  float ksc[2][UR];
   bool more = next_piece();
   // the first key rows are requested before the query and the LDS set-up
-  if (more) issue(s0, kw[0]);
+  if (more) issue(s0, kw[0], ksc[0]);
 
   // query elements of this lane; head slot hs holds head hs ^ headperm (zero
   // when that head does not exist, G < GP)
@@ -265,23 +281,57 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
   __builtin_amdgcn_s_barrier();
   __asm__ volatile("" ::: "memory");
 
-  auto consume = [&](int64_t base, int64_t cstart, const u32x4 (&kv)[UR][NCH]) {
+  // int8 codes c are read as unsigned bytes u = c + 128 (one conversion per
+  // byte); q . c = q . u - 128 * sum(q), the sum taken once per lane and head
+  float qsum[GP];
+#pragma unroll
+  for (int hs = 0; hs < GP; ++hs) {
+    qsum[hs] = 0.f;
+    if constexpr (kQ8) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) qsum[hs] += qr[hs][e];
+    }
+  }
+  auto consume = [&](int64_t base, int64_t cstart, const u32x4 (&kv)[UR][NCH], const float (&sc)[UR]) {
     float acc[V];
 #pragma unroll
     for (int j = 0; j < V; ++j) {
       const int s = j / GP, hs = j % GP;
       float x[E];
+      if constexpr (kQ8) {
 #pragma unroll
-      for (int k = 0; k < NCH; ++k) unpack16<T>(kv[s][k], x + k * EPC);
+        for (int k = 0; k < NCH; ++k) {
+          const uint32_t v4[4] = {kv[s][k].x ^ 0x80808080u, kv[s][k].y ^ 0x80808080u, kv[s][k].z ^ 0x80808080u,
+                                  kv[s][k].w ^ 0x80808080u};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            x[k * EPC + 4 * i + 0] = (float)((v4[i] >> 0) & 0xFFu);
+            x[k * EPC + 4 * i + 1] = (float)((v4[i] >> 8) & 0xFFu);
+            x[k * EPC + 4 * i + 2] = (float)((v4[i] >> 16) & 0xFFu);
+            x[k * EPC + 4 * i + 3] = (float)((v4[i] >> 24) & 0xFFu);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) unpack16<T>(kv[s][k], x + k * EPC);
+      }
       float t = 0.f;
 #pragma unroll
       for (int e = 0; e < E; ++e) t = fmaf(qr[hs][e], x[e], t);
+      if constexpr (kQ8) t = fmaf(-128.f, qsum[hs], t);
       acc[j] = t;
     }
     reduce_slots<LPR, V>(acc);
     const int64_t p = base + (int64_t)(w * UR + u_out) * RPW + rg;
     if (writer && p < s1) {
-      const float val = acc[0] * a.scale;
+      float val = acc[0] * a.scale;
+      if constexpr (kQ8) {
+        // logical row u_out sits in slot u_out ^ rowperm
+        float r = sc[0];
+#pragma unroll
+        for (int s = 1; s < UR; ++s) r = (u_out ^ rowperm) == s ? sc[s] : r;
+        val = acc[0] * r * a.scale;
+      }
       if (a.stage_stride > 0) {
         sst[h_out * a.stage_stride + (p - cstart)] = val;
       } else {
@@ -327,9 +377,9 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         if (!done) {
-          issue(base + IT, kw[st ^ 1]);
+          issue(base + IT, kw[st ^ 1], ksc[st ^ 1]);
           __builtin_amdgcn_sched_barrier(0);
-          consume(base, cstart, kw[st]);
+          consume(base, cstart, kw[st], ksc[st]);
           __builtin_amdgcn_sched_barrier(0);
           base += IT;
           done = base >= s1;
@@ -341,7 +391,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
       }
     }
     more = next_piece();
-    if (more) issue(s0, kw[0]);
+    if (more) issue(s0, kw[0], ksc[0]);
   }
   __syncthreads();
   // Add the block histogram to the global one: all LDS reads of a thread are

@@ -198,3 +198,25 @@ def test_multi_query_workspace_size(lib):
     assert a >= 28 * 32 * 65536 * 8
     assert lib.topk_multi_query_workspace_size(ctypes.byref(L), 0, 65536, 512) == 0
     assert lib.topk_multi_query_workspace_size(ctypes.byref(lay(d=64)), 4, 100, 8) == 0
+
+
+def test_int8_entry_points_reject(lib):
+    L = lay()
+    flat = (ctypes.c_int64 * 2)(0, 100)
+    # quantize: bad pointers and ranges
+    assert lib.quantize_keys_int8(ctypes.byref(L), FAKE, flat, 1, 0, FAKE, None) == native.STDK_EINVAL
+    assert lib.quantize_keys_int8(ctypes.byref(L), FAKE, flat, 1, FAKE + 8, FAKE, None) == native.STDK_EINVAL
+    bad = (ctypes.c_int64 * 2)(0, 5000)
+    assert lib.quantize_keys_int8(ctypes.byref(L), FAKE, bad, 1, FAKE, FAKE, None) == native.STDK_EINVAL
+
+    def dec(top_k=8, recall_k=16, codes=FAKE, ws=1 << 30, scale=0.1):
+        return lib.topk_attn_decode_int8(ctypes.byref(L), FAKE, FAKE, FAKE, codes, FAKE, flat, 1, top_k, recall_k,
+                                         ctypes.c_float(scale), None, None, FAKE, FAKE, FAKE, ws, None)
+    assert dec(recall_k=4) == native.STDK_EINVAL
+    assert dec(top_k=0) == native.STDK_EINVAL
+    assert dec(codes=0) == native.STDK_EINVAL
+    assert dec(scale=float("nan")) == native.STDK_EINVAL
+    assert dec(ws=64) == native.STDK_EWORKSPACE
+    assert lib.topk_attn_decode_int8_workspace_size(ctypes.byref(L), 4000, 64, 128) > \
+        lib.topk_attn_decode_workspace_size(ctypes.byref(L), 4000, 64)
+    assert lib.topk_attn_decode_int8_workspace_size(ctypes.byref(L), 4000, 64, 32) == 0
