@@ -30,9 +30,11 @@ The other workloads are measured the same way when asked for:
   --int8-recall K'  (workloads 2 and 5) the dynamic rows go through the int8
               recall stage instead: a scan of per-row int8 key codes (made
               before timing, one set per layer cache) picks K' rows, the
-              exact keys choose K among them; then the static window and the
-              merge as three calls. Not exact; the line reports the share of
-              the exact top-K rows that the step chose.
+              exact keys choose K among them; the same exact-scoring pass
+              scores the static window, whose rows join the chosen ones in
+              one softmax.V pass (one topk_attn_decode_int8_static call).
+              Not exact; the line reports the share of the exact top-K rows
+              that the step chose.
   --config 6  multi-query exact top-K of the c3 prefill block: the 32 warm-up
               queries of all 28 query heads over the 65,536 initial rows,
               K=512, one topk_multi_query call per step (the products run on
@@ -381,23 +383,19 @@ def bench_topk(args, cfg):
     path = args.path if n_stat else "top-k only"
     q8 = None
     if args.int8_recall and cfg in (2, 5):
-        path = f"int8 recall K'={args.int8_recall} + static dense + merge"
+        path = f"int8 recall K'={args.int8_recall}, static rows in the same softmax.V pass"
         q8 = [ops.quantize_keys_int8(kc, w.ranges, w.H_q, layout=lay) for kc, _ in caches]
-        ws_d = ops.new_workspace(ops.topk_attn_decode_int8_workspace_size(lay, n_dyn, K, args.int8_recall), dev)
-        ws_s = ops.new_workspace(ops.topk_attn_decode_workspace_size(lay, n_stat, K), dev)
-        o_d, l_d, o_s, l_s = (torch.empty_like(o_m), torch.empty_like(l_m), torch.empty_like(o_m),
-                              torch.empty_like(l_m))
+        ws_q = ops.new_workspace(ops.topk_attn_decode_int8_static_workspace_size(lay, n_dyn, n_stat, K,
+                                                                                 args.int8_recall), dev)
 
         def step():
             i = layer["i"]
             k, v = caches[i]
             codes, scales = q8[i]
             layer["i"] = (i + 1) % n_layers
-            ops.topk_attn_decode_int8(q, k, v, codes, scales, w.ranges, K, args.int8_recall, w.scale, idx_out=idx,
-                                      o_out=o_d, lse_out=l_d, workspace=ws_d, layout=lay)
-            ops.topk_attn_decode(q, k, v, w.static_ranges, K, w.scale, o_out=o_s, lse_out=l_s, workspace=ws_s,
-                                 want_idx=False, layout=lay)
-            ops.attn_merge_lse(o_s, l_s, o_d, l_d, o_out=o_m, lse_out=l_m)
+            ops.topk_attn_decode_int8_static(q, k, v, codes, scales, w.ranges, w.static_ranges, K, args.int8_recall,
+                                             w.scale, idx_out=idx, o_out=o_m, lse_out=l_m, workspace=ws_q,
+                                             layout=lay)
     elif n_stat and args.path == "one-pass":
         ws_f = ops.new_workspace(ops.topk_attn_decode_static_workspace_size(lay, n_dyn, n_stat, K), dev)
 
@@ -442,7 +440,7 @@ def bench_topk(args, cfg):
         roof = roofline(kern, "k_scan", scan_bytes, committed_traffic(cfg))
     else:
         # the scan reads the int8 codes (128 B) and the scale (4 B) of every
-        # dynamic row; the static window's dense pass does not use k_scan
+        # dynamic row; the static window is scored by the rerank, not k_scan
         scan_bytes = B * w.H_kv * n_dyn * (128 + 4)
         roof = roofline(kern, "k_scan", scan_bytes, None)
     if cfg == 4:

@@ -230,6 +230,32 @@ int32_t topk_attn_decode_int8(const stdk_layout* lay, const float* q, const void
 size_t topk_attn_decode_int8_workspace_size(const stdk_layout* lay, int64_t n_scan, int32_t top_k,
                                             int32_t recall_k);
 
+/* topk_attn_decode_int8_static: the decode step of [RA] "CPU-GPU
+ * Co-Execution Architecture" with the int8 recall stage on the dynamic rows:
+ * o and lse equal attn_merge_lse of (a) topk_attn_decode over
+ * `static_ranges` with top_k >= |W| and (b) topk_attn_decode_int8 over
+ * `ranges` (Eq. 4-5). One pass: the exact scoring of the superset also
+ * scores W, and the softmax.V partials of S and W are combined once.
+ *  ranges, static_ranges  as topk_attn_decode_static (codes and scales need
+ *           only cover `ranges`).
+ *  top_k, recall_k, idx_out, sup_out  as topk_attn_decode_int8 over
+ *           `ranges`; when top_k < |Omega|, top_k + |W| <= 65536.
+ *           With recall_k >= |Omega| the result is topk_attn_decode_static's
+ *           and sup_out lists every dynamic row.
+ *  workspace at least topk_attn_decode_int8_static_workspace_size(lay,
+ *           |Omega|, |W|, top_k, recall_k) bytes, in the "Workspace state"
+ *           above. */
+int32_t topk_attn_decode_int8_static(const stdk_layout* lay, const float* q, const void* k_cache,
+                                     const void* v_cache, const int8_t* codes, const float* scales,
+                                     const int64_t* ranges, int32_t n_ranges,
+                                     const int64_t* static_ranges, int32_t n_static, int32_t top_k,
+                                     int32_t recall_k, float scale, int32_t* idx_out, int32_t* sup_out,
+                                     float* o_out, float* lse_out, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+size_t topk_attn_decode_int8_static_workspace_size(const stdk_layout* lay, int64_t n_scan,
+                                                   int64_t n_static, int32_t top_k, int32_t recall_k);
+
 /* ------------------------------------------------------------------------
  * attn_merge_lse — [RA] Eq. 4-5: combination of two partial attention
  * outputs over disjoint row sets a and b:

@@ -173,6 +173,8 @@ int32_t dev_info(DevInfo** out) {
                               std::max(0, d.max_lds - 4 * 1024));
     (void)hipFuncSetAttribute((const void*)retopk_vote<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               std::max(0, d.max_lds - 4 * 1024));
+    (void)hipFuncSetAttribute((const void*)retopk_rerank_select_lds, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              std::max(0, d.max_lds - 12 * 1024));
     (void)hipGetLastError();
     d.init = true;
   }
@@ -632,28 +634,43 @@ int32_t run_multi_query(const Geo& g, const MqWs& w, char* ws, const float* q, i
 // ---------------------------------------------------------------------------
 // top-K with the int8 recall stage: workspace
 // ---------------------------------------------------------------------------
-// [the int8 scan's top-K' workspace] [exact scores of the superset]
-// [chosen rows, scores and softmax.V partials of the final top-K]
+// [the int8 scan's top-K' workspace] [exact scores of the superset] [exact
+// scores of the n_st static rows] [chosen rows, scores and softmax.V
+// partials of the final top-K and the static rows]
 struct Q8Ws {
   TopkWs t1;  // scan of the codes, top-K' superset
-  TopkWs t2;  // view for softmax . V over the final K rows
-  size_t cz, total;
+  TopkWs t2;  // view for softmax . V over the final K rows, then the static rows
+  size_t cz, czs, total;
 };
 
-Q8Ws q8_ws(const Geo& g, int64_t n, int64_t K, int64_t K2) {
+Q8Ws q8_ws(const Geo& g, int64_t n, int64_t K, int64_t K2, int64_t n_st = 0) {
   Q8Ws w{};
   w.t1 = topk_ws(g.S, n, K2);
   size_t off = w.t1.total;
   w.cz = off;
   off = al256(off + (size_t)g.S * K2 * 4);
+  w.czs = off;
+  off = al256(off + (size_t)g.S * n_st * 4);
   w.t2 = w.t1;
   w.t2.K = K;
-  w.t2.ksel = K;
-  w.t2.nsplit = cdiv(K, kSvRows);
-  w.t2.sel_row = off;
-  off = al256(off + (size_t)g.S * K * 4);
-  w.t2.sel_z = off;
-  off = al256(off + (size_t)g.S * K * 4);
+  w.t2.ksel = K + n_st;
+  w.t2.nsplit = cdiv(K + n_st, kSvRows);
+  // softmax . V reads static slot K + i's score at scores[seg * n_pad + i]
+  w.t2.n = 0;
+  w.t2.n_extra = n_st;
+  w.t2.n_pad = n_st;
+  w.t2.scores = w.czs;
+  if (K == K2) {
+    // the superset is the final set: softmax . V reads the superset's rows
+    // and their exact scores in place
+    w.t2.sel_row = w.t1.sel_row;
+    w.t2.sel_z = w.cz;
+  } else {
+    w.t2.sel_row = off;
+    off = al256(off + (size_t)g.S * K * 4);
+    w.t2.sel_z = off;
+    off = al256(off + (size_t)g.S * K * 4);
+  }
   w.t2.part = off;
   off = al256(off + (size_t)g.S * w.t2.nsplit * kPartStride * 4);
   w.total = off;
@@ -674,6 +691,115 @@ int32_t check_ranges(const stdk_layout* lay, const int64_t* ranges, int32_t n_ra
     prev_end = e;
   }
   return STDK_OK;
+}
+
+// A dynamic and a static row set, validated: the position space of `all`
+// holds the dynamic ranges first, then the static ones.
+struct StaticSplit {
+  RangeTab all, dyn, st;
+  int64_t n_dyn, n_st;
+};
+
+int32_t split_static(const stdk_layout* lay, const int64_t* ranges, int32_t n_ranges, const int64_t* static_ranges,
+                     int32_t n_static, StaticSplit* sp) {
+  STDK_TRY(check_ranges(lay, ranges, n_ranges, "ranges"));
+  STDK_TRY(check_ranges(lay, static_ranges, n_static, "static_ranges"));
+  if (n_ranges + n_static > STDK_MAX_RANGES)
+    return fail(STDK_EINVAL, "%d ranges in total, at most %d", n_ranges + n_static, STDK_MAX_RANGES);
+  for (int i = 0; i < n_ranges; ++i)
+    for (int j = 0; j < n_static; ++j)
+      if (ranges[2 * i] < static_ranges[2 * j + 1] && static_ranges[2 * j] < ranges[2 * i + 1])
+        return fail(STDK_EINVAL, "static range %d overlaps range %d", j, i);
+  std::vector<int64_t> all(2 * (size_t)(n_ranges + n_static));
+  for (int i = 0; i < 2 * n_ranges; ++i) all[i] = ranges[i];
+  for (int i = 0; i < 2 * n_static; ++i) all[2 * n_ranges + i] = static_ranges[i];
+  int64_t n_all = 0;
+  sp->all = make_tab(all.data(), n_ranges + n_static, &n_all);
+  sp->dyn = make_tab(ranges, n_ranges, &sp->n_dyn);
+  sp->st = make_tab(static_ranges, n_static, &sp->n_st);
+  return STDK_OK;
+}
+
+// Exact top-K over the dynamic rows, the static rows whole (validated
+// inputs; the workspace holds topk_attn_decode_static's need).
+int32_t run_static(const Geo& g, const StaticSplit& sp, char* ws, const float* q, const void* k_cache,
+                   const void* v_cache, int32_t top_k, float scale, int32_t* idx_out, float* o_out, float* lse_out,
+                   const DevInfo* di, hipStream_t s) {
+  const int64_t n_all = sp.n_dyn + sp.n_st;
+  if (n_all == 0) {
+    const int64_t m = std::max<int64_t>(g.S * kHeadDim, g.S * (int64_t)top_k);
+    return launch(KID_FILL, s, [&](hipEvent_t e0, hipEvent_t e1) {
+      STDK_LAUNCH(fill_empty, dim3((unsigned)cdiv(m, 256)), dim3(256), 0, s, o_out, lse_out, idx_out, g.S, top_k);
+    });
+  }
+  if (top_k >= sp.n_dyn) {
+    // every dynamic row is chosen: dense attention over the union; idx_out
+    // lists the dynamic rows, then -1
+    const TopkWs w = topk_ws(g.S, n_all, std::max<int64_t>(top_k, n_all));
+    return run_dense(g, w, ws, q, k_cache, v_cache, sp.all, scale, top_k, idx_out, o_out, lse_out, s, sp.n_dyn);
+  }
+  const TopkWs w = topk_ws(g.S, sp.n_dyn, top_k, sp.n_st);
+  STDK_TRY(run_exact_select(g, w, ws, q, k_cache, sp.all, scale, nullptr, idx_out, di, s));
+  return run_sv(g, w, ws, v_cache, o_out, lse_out, s, &sp.all);
+}
+
+// The top-K among the reranked candidates: staged in LDS when every
+// candidate slot fits there, else read from global memory in each pass.
+int32_t run_rerank_select(const RtRerankArgs& a, int64_t S, const DevInfo* di, hipStream_t s) {
+  const size_t dyn = (size_t)a.cand_cap * 8;
+  const bool staged = a.cand_cap <= kRselStageMax && dyn + 12 * 1024 <= (size_t)di->max_lds;
+  return launch(KID_RT_RSEL, s, [&](hipEvent_t e0, hipEvent_t e1) {
+    if (staged) STDK_LAUNCH(retopk_rerank_select_lds, dim3((unsigned)S), dim3(kRerankSelThreads), dyn, s, a);
+    else STDK_LAUNCH(retopk_rerank_select, dim3((unsigned)S), dim3(kRerankSelThreads), 0, s, a);
+  });
+}
+
+// The int8 recall step proper (recall_k below the row count of `tab`): the
+// top-recall_k superset by the int8 scores, the exact scores of the superset
+// and of the n_st rows of `stab`, the top-K inside the superset, then
+// softmax . V over the K rows and the static ones in one pass.
+int32_t run_int8(const Geo& g, const Q8Ws& w, char* ws, const float* q, const void* k_cache, const void* v_cache,
+                 const Q8Keys& keys, const RangeTab& tab, const RangeTab& stab, int64_t n_st, int32_t top_k,
+                 int32_t recall_k, float scale, int32_t* idx_out, int32_t* sup_out, float* o_out, float* lse_out,
+                 const DevInfo* di, hipStream_t s) {
+  // recall_k == top_k: the superset is the answer, and only its exact
+  // scores are still needed
+  const bool same = recall_k == top_k;
+  int32_t* first = same && idx_out ? idx_out : sup_out;
+  STDK_TRY(run_exact_select(g, w.t1, ws, q, nullptr, tab, scale, nullptr, first, di, s, &keys));
+  if (same && idx_out && sup_out) {
+    const hipError_t e = hipMemcpyAsync(sup_out, idx_out, (size_t)g.S * top_k * 4, hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return fail(STDK_EHIP, "hipMemcpyAsync: %s", hipGetErrorString(e));
+  }
+  RtRerankArgs a{};
+  a.q = q;
+  a.k = (const char*)k_cache;
+  a.stride_b_bytes = g.sb_bytes;
+  a.stride_h_bytes = g.sh_bytes;
+  a.exact = nullptr;
+  a.cand = (const int32_t*)(ws + w.t1.sel_row);
+  a.n_cand = nullptr;
+  a.n_const = recall_k;
+  a.cz = (float*)(ws + w.cz);
+  a.sel_row = (int32_t*)(ws + w.t2.sel_row);
+  a.sel_z = (float*)(ws + w.t2.sel_z);
+  a.support_out = idx_out ? idx_out : (int32_t*)(ws + w.t2.sel_row);
+  a.cand_cap = recall_k;
+  a.K = top_k;
+  a.Hq = g.Hq;
+  a.G = g.G;
+  a.nsplit = (int32_t)cdiv(recall_k + n_st, kRerankRows);
+  a.scale = scale;
+  a.n_static = (int32_t)n_st;
+  a.cz_static = (float*)(ws + w.czs);
+  a.st_tab = stab;
+  const dim3 grid((unsigned)a.nsplit, (unsigned)g.S);
+  STDK_TRY(launch(KID_RT_RERANK, s, [&](hipEvent_t e0, hipEvent_t e1) {
+    if (g.bf16) STDK_LAUNCH(retopk_rerank<uint16_t>, grid, dim3(kRerankThreads), 0, s, a);
+    else STDK_LAUNCH(retopk_rerank<float>, grid, dim3(kRerankThreads), 0, s, a);
+  }));
+  if (!same) STDK_TRY(run_rerank_select(a, g.S, di, s));
+  return run_sv(g, w.t2, ws, v_cache, o_out, lse_out, s, &stab);
 }
 
 }  // namespace
@@ -759,55 +885,22 @@ int32_t topk_attn_decode_static(const stdk_layout* lay, const float* q, const vo
   if (idx_out && ((uintptr_t)idx_out) % 4) return fail(STDK_EINVAL, "idx_out is not 4-byte aligned");
   if (top_k < 1) return fail(STDK_EINVAL, "top_k %d < 1", top_k);
   if (!std::isfinite(scale)) return fail(STDK_EINVAL, "scale is not finite");
-  STDK_TRY(check_ranges(lay, ranges, n_ranges, "ranges"));
-  STDK_TRY(check_ranges(lay, static_ranges, n_static, "static_ranges"));
-  if (n_ranges + n_static > STDK_MAX_RANGES)
-    return fail(STDK_EINVAL, "%d ranges in total, at most %d", n_ranges + n_static, STDK_MAX_RANGES);
-  for (int i = 0; i < n_ranges; ++i)
-    for (int j = 0; j < n_static; ++j)
-      if (ranges[2 * i] < static_ranges[2 * j + 1] && static_ranges[2 * j] < ranges[2 * i + 1])
-        return fail(STDK_EINVAL, "static range %d overlaps range %d", j, i);
-  // position space: the dynamic ranges first, then the static ones
-  std::vector<int64_t> all(2 * (size_t)(n_ranges + n_static));
-  for (int i = 0; i < 2 * n_ranges; ++i) all[i] = ranges[i];
-  for (int i = 0; i < 2 * n_static; ++i) all[2 * n_ranges + i] = static_ranges[i];
-  int64_t n_all = 0;
-  const RangeTab tab = make_tab(all.data(), n_ranges + n_static, &n_all);
-  int64_t n_dyn = 0;
-  for (int i = 0; i < n_ranges; ++i) n_dyn += ranges[2 * i + 1] - ranges[2 * i];
-  const int64_t n_st = n_all - n_dyn;
-  if (top_k > kMaxTopK && top_k < n_dyn)
+  StaticSplit sp{};
+  STDK_TRY(split_static(lay, ranges, n_ranges, static_ranges, n_static, &sp));
+  if (top_k > kMaxTopK && top_k < sp.n_dyn)
     return fail(STDK_EUNSUPPORTED, "top_k %d > %d (below the row count)", top_k, kMaxTopK);
-  if (top_k < n_dyn && top_k + n_st > kMaxTopK)
-    return fail(STDK_EUNSUPPORTED, "top_k %d + %lld static rows > %d", top_k, (long long)n_st, kMaxTopK);
+  if (top_k < sp.n_dyn && top_k + sp.n_st > kMaxTopK)
+    return fail(STDK_EUNSUPPORTED, "top_k %d + %lld static rows > %d", top_k, (long long)sp.n_st, kMaxTopK);
   const Geo g = geo_of(lay);
-  const bool fused = top_k < n_dyn;
-  const TopkWs w = fused ? topk_ws(g.S, n_dyn, top_k, n_st)
-                         : topk_ws(g.S, n_all, std::max<int64_t>(top_k, n_all));
-  if (n_all > 0) {
+  if (sp.n_dyn + sp.n_st > 0) {
     STDK_TRY(check_ptr(workspace, "workspace", 256));
-    if (workspace_bytes < w.total)
-      return fail(STDK_EWORKSPACE, "workspace is %zu bytes, %zu needed", workspace_bytes, w.total);
+    const size_t need = topk_attn_decode_static_workspace_size(lay, sp.n_dyn, sp.n_st, top_k);
+    if (workspace_bytes < need) return fail(STDK_EWORKSPACE, "workspace is %zu bytes, %zu needed", workspace_bytes, need);
   }
-  hipStream_t s = (hipStream_t)stream;
   DevInfo* di = nullptr;
   STDK_TRY(dev_info(&di));
-  char* ws = (char*)workspace;
-  if (n_all == 0) {
-    const int64_t m = std::max<int64_t>(g.S * kHeadDim, g.S * (int64_t)top_k);
-    STDK_TRY(launch(KID_FILL, s, [&](hipEvent_t e0, hipEvent_t e1) {
-      STDK_LAUNCH(fill_empty, dim3((unsigned)cdiv(m, 256)), dim3(256), 0, s, o_out, lse_out, idx_out, g.S, top_k);
-    }));
-    return ok();
-  }
-  if (!fused) {
-    // every dynamic row is chosen: dense attention over the union; idx_out
-    // lists the dynamic rows, then -1
-    STDK_TRY(run_dense(g, w, ws, q, k_cache, v_cache, tab, scale, top_k, idx_out, o_out, lse_out, s, n_dyn));
-    return ok();
-  }
-  STDK_TRY(run_exact_select(g, w, ws, q, k_cache, tab, scale, nullptr, idx_out, di, s));
-  STDK_TRY(run_sv(g, w, ws, v_cache, o_out, lse_out, s, &tab));
+  STDK_TRY(run_static(g, sp, (char*)workspace, q, k_cache, v_cache, top_k, scale, idx_out, o_out, lse_out, di,
+                      (hipStream_t)stream));
   return ok();
 }
 
@@ -948,39 +1041,68 @@ int32_t topk_attn_decode_int8(const stdk_layout* lay, const float* q, const void
   }
   const Q8Ws w = q8_ws(g, n, top_k, recall_k);
   const Q8Keys keys{codes, scales, lay->max_len};
-  // the superset: top-K' of the int8 scores
-  STDK_TRY(run_exact_select(g, w.t1, ws, q, nullptr, tab, scale, nullptr, sup_out, di, s, &keys));
-  // exact scores of the superset rows, then the top-K among them
-  {
-    RtRerankArgs a{};
-    a.q = q;
-    a.k = (const char*)k_cache;
-    a.stride_b_bytes = g.sb_bytes;
-    a.stride_h_bytes = g.sh_bytes;
-    a.exact = nullptr;
-    a.cand = (const int32_t*)(ws + w.t1.sel_row);
-    a.n_cand = nullptr;
-    a.n_const = recall_k;
-    a.cz = (float*)(ws + w.cz);
-    a.sel_row = (int32_t*)(ws + w.t2.sel_row);
-    a.sel_z = (float*)(ws + w.t2.sel_z);
-    a.support_out = idx_out ? idx_out : (int32_t*)(ws + w.t2.sel_row);
-    a.cand_cap = recall_k;
-    a.K = top_k;
-    a.Hq = g.Hq;
-    a.G = g.G;
-    a.nsplit = (int32_t)cdiv(recall_k, kRerankRows);
-    a.scale = scale;
-    const dim3 grid((unsigned)a.nsplit, (unsigned)g.S);
-    STDK_TRY(launch(KID_RT_RERANK, s, [&](hipEvent_t e0, hipEvent_t e1) {
-      if (g.bf16) STDK_LAUNCH(retopk_rerank<uint16_t>, grid, dim3(kRerankThreads), 0, s, a);
-      else STDK_LAUNCH(retopk_rerank<float>, grid, dim3(kRerankThreads), 0, s, a);
-    }));
-    STDK_TRY(launch(KID_RT_RSEL, s, [&](hipEvent_t e0, hipEvent_t e1) {
-      STDK_LAUNCH(retopk_rerank_select, dim3((unsigned)g.S), dim3(kRerankSelThreads), 0, s, a);
-    }));
+  STDK_TRY(run_int8(g, w, ws, q, k_cache, v_cache, keys, tab, RangeTab{}, 0, top_k, recall_k, scale, idx_out, sup_out,
+                    o_out, lse_out, di, s));
+  return ok();
+}
+
+size_t topk_attn_decode_int8_static_workspace_size(const stdk_layout* lay, int64_t n_scan, int64_t n_static,
+                                                   int32_t top_k, int32_t recall_k) {
+  if (check_layout(lay) != STDK_OK || n_scan < 0 || n_static < 0 || top_k < 1 || recall_k < top_k) return 0;
+  return std::max(q8_ws(geo_of(lay), n_scan, top_k, recall_k, n_static).total,
+                  topk_attn_decode_static_workspace_size(lay, n_scan, n_static, top_k));
+}
+
+int32_t topk_attn_decode_int8_static(const stdk_layout* lay, const float* q, const void* k_cache,
+                                     const void* v_cache, const int8_t* codes, const float* scales,
+                                     const int64_t* ranges, int32_t n_ranges, const int64_t* static_ranges,
+                                     int32_t n_static, int32_t top_k, int32_t recall_k, float scale,
+                                     int32_t* idx_out, int32_t* sup_out, float* o_out, float* lse_out,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  STDK_TRY(check_layout(lay));
+  STDK_TRY(check_ptr(q, "q", 16));
+  STDK_TRY(check_ptr(k_cache, "k_cache", 16));
+  STDK_TRY(check_ptr(v_cache, "v_cache", 16));
+  STDK_TRY(check_ptr(codes, "codes", 16));
+  STDK_TRY(check_ptr(scales, "scales", 4));
+  STDK_TRY(check_ptr(o_out, "o_out", 4));
+  STDK_TRY(check_ptr(lse_out, "lse_out", 4));
+  if (idx_out && ((uintptr_t)idx_out) % 4) return fail(STDK_EINVAL, "idx_out is not 4-byte aligned");
+  if (sup_out && ((uintptr_t)sup_out) % 4) return fail(STDK_EINVAL, "sup_out is not 4-byte aligned");
+  if (top_k < 1) return fail(STDK_EINVAL, "top_k %d < 1", top_k);
+  if (recall_k < top_k) return fail(STDK_EINVAL, "recall_k %d < top_k %d", recall_k, top_k);
+  if (!std::isfinite(scale)) return fail(STDK_EINVAL, "scale is not finite");
+  StaticSplit sp{};
+  STDK_TRY(split_static(lay, ranges, n_ranges, static_ranges, n_static, &sp));
+  if (recall_k > kMaxTopK && recall_k < sp.n_dyn)
+    return fail(STDK_EUNSUPPORTED, "recall_k %d > %d (below the row count)", recall_k, kMaxTopK);
+  if (top_k < sp.n_dyn && top_k + sp.n_st > kMaxTopK)
+    return fail(STDK_EUNSUPPORTED, "top_k %d + %lld static rows > %d", top_k, (long long)sp.n_st, kMaxTopK);
+  const Geo g = geo_of(lay);
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  DevInfo* di = nullptr;
+  if (sp.n_dyn + sp.n_st > 0) {
+    STDK_TRY(check_ptr(workspace, "workspace", 256));
+    const size_t need = topk_attn_decode_int8_static_workspace_size(lay, sp.n_dyn, sp.n_st, top_k, recall_k);
+    if (workspace_bytes < need) return fail(STDK_EWORKSPACE, "workspace is %zu bytes, %zu needed", workspace_bytes, need);
   }
-  STDK_TRY(run_sv(g, w.t2, ws, v_cache, o_out, lse_out, s));
+  STDK_TRY(dev_info(&di));
+  if (recall_k >= sp.n_dyn) {
+    // the superset is every dynamic row: topk_attn_decode_static's result
+    STDK_TRY(run_static(g, sp, ws, q, k_cache, v_cache, top_k, scale, idx_out, o_out, lse_out, di, s));
+    if (sup_out) {
+      STDK_TRY(launch(KID_FILL, s, [&](hipEvent_t e0, hipEvent_t e1) {
+        STDK_LAUNCH(fill_rows, dim3((unsigned)cdiv(g.S * (int64_t)recall_k, 256)), dim3(256), 0, s, sup_out, g.S,
+                    recall_k, sp.dyn);
+      }));
+    }
+    return ok();
+  }
+  const Q8Ws w = q8_ws(g, sp.n_dyn, top_k, recall_k, sp.n_st);
+  const Q8Keys keys{codes, scales, lay->max_len};
+  STDK_TRY(run_int8(g, w, ws, q, k_cache, v_cache, keys, sp.dyn, sp.st, sp.n_st, top_k, recall_k, scale, idx_out,
+                    sup_out, o_out, lse_out, di, s));
   return ok();
 }
 
@@ -1214,9 +1336,7 @@ int32_t retopk_step(const stdk_layout* lay, const retopk_params* p, const retopk
       if (g.bf16) STDK_LAUNCH(retopk_rerank<uint16_t>, grid, dim3(kRerankThreads), 0, s, a);
       else STDK_LAUNCH(retopk_rerank<float>, grid, dim3(kRerankThreads), 0, s, a);
     }));
-    STDK_TRY(launch(KID_RT_RSEL, s, [&](hipEvent_t e0, hipEvent_t e1) {
-      STDK_LAUNCH(retopk_rerank_select, dim3((unsigned)g.S), dim3(kRerankSelThreads), 0, s, a);
-    }));
+    STDK_TRY(run_rerank_select(a, g.S, di, s));
   }
   // a8: softmax . V over the chosen rows of every head (either path)
   STDK_TRY(run_sv(g, w.t, ws, v_cache, o_out, lse_out, s));

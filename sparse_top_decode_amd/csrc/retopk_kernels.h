@@ -468,6 +468,14 @@ struct RtRerankArgs {
   int32_t cand_cap, K, Hq, G, nsplit;
   float scale;
   int32_t n_const;          // candidates per head when n_cand is null (exact and n_cand null: every head reranks)
+  // Static rows (the int8 recall step with a static window): the rerank
+  // also scores the n_static rows of st_tab, into cz_static [S][n_static];
+  // they never enter the top-K (softmax . V takes them from there). 0 for
+  // ReTopK.
+  int32_t n_static;
+  int32_t pad_;
+  float* cz_static;
+  RangeTab st_tab;
 };
 
 constexpr int kRerankThreads = 256;
@@ -485,8 +493,10 @@ __global__ __launch_bounds__(kRerankThreads) void retopk_rerank(RtRerankArgs a) 
   const int rg = lane / LPR, c = lane % LPR;
   const int b = (int)(seg / a.Hq), hq = (int)(seg % a.Hq), hkv = hq / a.G;
   const int M = a.n_cand ? a.n_cand[seg] : a.n_const;
+  const int Mt = M + a.n_static;  // candidates, then the static rows
   const int32_t* cd = a.cand + seg * a.cand_cap;
   float* cz = a.cz + seg * a.cand_cap;
+  float* czs = a.cz_static + seg * a.n_static;
 
   float qr[1][EPL];
   load_q_slice<T, 1>(a.q, seg, c, qr);
@@ -500,7 +510,7 @@ __global__ __launch_bounds__(kRerankThreads) void retopk_rerank(RtRerankArgs a) 
 #pragma unroll
   for (int u = 0; u < RU; ++u) {
     const int j = j0 + gid + GROUPS * u;
-    row[u] = (j < M) ? cd[j] : -1;
+    row[u] = (j < M) ? cd[j] : (j < Mt ? (int32_t)pos_to_row(a.st_tab, j - M) : -1);
   }
   u32x4 kw[RU];
 #pragma unroll
@@ -512,6 +522,7 @@ __global__ __launch_bounds__(kRerankThreads) void retopk_rerank(RtRerankArgs a) 
     const float s = group_sum<LPR>(d[0]);
     const int j = j0 + gid + GROUPS * u;
     if (c == 0 && j < M) cz[j] = s * a.scale;
+    else if (c == 0 && j < Mt) czs[j - M] = s * a.scale;
   }
 }
 
@@ -623,6 +634,171 @@ __global__ __launch_bounds__(kRerankSelThreads) void retopk_rerank_select(RtRera
     }
   }
   for (uint32_t i = tot_all + tid; i < (uint32_t)K; i += NT) {
+    srow[i] = -1;
+    sz[i] = -INFINITY;
+    so[i] = -1;
+  }
+}
+
+// Staged variant of retopk_rerank_select, same result: the candidate
+// scores and rows are read from global memory once, in one batch, into
+// dynamic LDS (8 bytes per candidate slot, cand_cap <= kRselStageMax); the
+// radix passes, sized to the candidates' key range, and the ordered
+// compaction run on that copy. The compaction gives each wave a contiguous
+// candidate segment and ranks with ballots.
+constexpr int kRselStageMax = 16384;
+
+__global__ __launch_bounds__(kRerankSelThreads) void retopk_rerank_select_lds(RtRerankArgs a) {
+  constexpr int NT = kRerankSelThreads, NW = NT / 64;
+  extern __shared__ uint32_t rsel_dyn[];
+  float* zs = reinterpret_cast<float*>(rsel_dyn);                 // [cand_cap]
+  int32_t* rs = reinterpret_cast<int32_t*>(rsel_dyn + a.cand_cap);  // [cand_cap]
+  __shared__ uint32_t h[kHistBins];
+  __shared__ uint32_t wc[2][NW];
+  __shared__ int s_bin;
+  __shared__ uint32_t s_beyond;
+  const int64_t seg = blockIdx.x;
+  if (a.exact && a.exact[seg]) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const uint32_t M = (uint32_t)(a.n_cand ? a.n_cand[seg] : a.n_const);
+  const int32_t* cd = a.cand + seg * a.cand_cap;
+  const float* cz = a.cz + seg * a.cand_cap;
+  const int K = a.K;
+  int32_t* srow = a.sel_row + seg * K;
+  float* sz = a.sel_z + seg * K;
+  int32_t* so = a.support_out + seg * K;
+  const bool take_all = M <= (uint32_t)K;
+
+  // stage: U loads of each array in flight per thread (clamped indices, so
+  // the loads carry no condition)
+  constexpr int U = 16;
+  if (M > 0) {
+    for (uint32_t base = 0; base < M; base += NT * U) {
+      float zv[U];
+      int32_t rv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t j = min(base + u * NT + tid, M - 1);
+        zv[u] = cz[j];
+        rv[u] = cd[j];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t j = base + u * NT + tid;
+        if (j < M) {
+          zs[j] = zv[u];
+          rs[j] = rv[u];
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // radix passes over a window of keys [lo, lo + 2048 << sh): the first
+  // spans the candidates' own key range, each later one the bin that holds
+  // the K-th key, 11 bits finer; stop at single keys (sh = 0) or once that
+  // bin is taken whole. The threshold Tk is then the bin's smallest key and
+  // `need` the number of keys equal to it to take.
+  uint32_t Tk = 0u, need = (uint32_t)K;
+  if (!take_all) {
+    uint32_t kmin = 0xffffffffu, kmax = 0u;
+    for (uint32_t j = tid; j < M; j += NT) {
+      const uint32_t kv = f2key(zs[j]);
+      kmin = min(kmin, kv);
+      kmax = max(kmax, kv);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
+      kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+    }
+    if (lane == 0) {
+      wc[0][w] = kmin;
+      wc[1][w] = kmax;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      kmin = min(kmin, wc[0][v]);
+      kmax = max(kmax, wc[1][v]);
+    }
+    __syncthreads();
+    uint32_t lo = kmin;
+    const uint32_t span = kmax - kmin;
+    int sh = span < 2048u ? 0 : (32 - __clz((int)span)) - 11;
+    // at most three passes: sh <= 21 and drops by 11 (to 0) each time
+    for (;;) {
+      for (int i = tid; i < 2048; i += NT) h[i] = 0u;
+      __syncthreads();
+      for (uint32_t j = tid; j < M; j += NT) {
+        const uint32_t kv = f2key(zs[j]);
+        if (kv >= lo) {
+          const uint32_t d = (kv - lo) >> sh;
+          if (d < 2048u) atomicAdd(&h[d], 1u);
+        }
+      }
+      __syncthreads();
+      if (w == 0) find_bin_wave<2048, true>(h, need, &s_bin, &s_beyond);
+      __syncthreads();
+      const int bin = s_bin < 0 ? 0 : s_bin;
+      need -= s_beyond;
+      lo += (uint32_t)bin << sh;
+      if (sh == 0 || h[bin] == need) break;
+      sh = sh > 11 ? sh - 11 : 0;
+      __syncthreads();
+    }
+    Tk = lo;
+  }
+
+  // ordered compaction: wave w owns candidates [s0, s1)
+  const uint32_t SEG = ((M + NW - 1) / NW + 63u) & ~63u;
+  const uint32_t s0 = min(M, (uint32_t)w * SEG), s1 = min(M, s0 + SEG);
+  uint32_t cg = 0, ce = 0;
+  for (uint32_t j = s0 + lane; j < s1; j += 64) {
+    const uint32_t kv = f2key(zs[j]);
+    cg += take_all || kv > Tk;
+    ce += !take_all && kv == Tk;
+  }
+  cg = __shfl(wave_incl_scan(cg), 63, 64);
+  ce = __shfl(wave_incl_scan(ce), 63, 64);
+  if (lane == 0) {
+    wc[0][w] = cg;
+    wc[1][w] = ce;
+  }
+  __syncthreads();
+  uint32_t out = 0, eq_seen = 0, tot = 0, eq_all = 0;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) {
+    const uint32_t e = wc[1][v];
+    const uint32_t te = min(e, need > eq_all ? need - eq_all : 0u);
+    if (v < w) {
+      out += wc[0][v] + te;
+      eq_seen += e;
+    }
+    tot += wc[0][v] + te;
+    eq_all += e;
+  }
+  for (uint32_t jb = s0; jb < s1; jb += 64) {
+    const uint32_t j = jb + lane;
+    const bool valid = j < s1;
+    const float z = valid ? zs[j] : 0.f;
+    const uint32_t kv = f2key(z);
+    const bool gt = valid && (take_all || kv > Tk);
+    const bool eq = valid && !take_all && kv == Tk;
+    const uint64_t em = __ballot(eq);
+    const bool take = gt || (eq && eq_seen + lane_rank(em) < need);
+    const uint64_t tm = __ballot(take);
+    const uint32_t pos = out + lane_rank(tm);
+    if (take && pos < (uint32_t)K) {
+      const int32_t r = rs[j];
+      srow[pos] = r;
+      sz[pos] = z;
+      so[pos] = r;
+    }
+    out += (uint32_t)__popcll(tm);
+    eq_seen += (uint32_t)__popcll(em);
+  }
+  for (uint32_t i = tot + tid; i < (uint32_t)K; i += NT) {
     srow[i] = -1;
     sz[i] = -INFINITY;
     so[i] = -1;

@@ -29,6 +29,7 @@ EXPORTS = [
     "retopk_state_init", "retopk_step", "retopk_workspace_size",
     "topk_multi_query", "topk_multi_query_workspace_size",
     "quantize_keys_int8", "topk_attn_decode_int8", "topk_attn_decode_int8_workspace_size",
+    "topk_attn_decode_int8_static", "topk_attn_decode_int8_static_workspace_size",
     "stdk_last_error", "stdk_version",
     "stdk_profile_enable", "stdk_profile_disable", "stdk_profile_reset", "stdk_profile_read",
 ]
@@ -83,6 +84,12 @@ def _sig(lib):
     lib.topk_attn_decode_int8.restype = c_int32
     lib.topk_attn_decode_int8_workspace_size.argtypes = [POINTER(Layout), c_int64, c_int32, c_int32]
     lib.topk_attn_decode_int8_workspace_size.restype = c_size_t
+    lib.topk_attn_decode_int8_static.argtypes = [POINTER(Layout), P, P, P, P, P, POINTER(c_int64), c_int32,
+                                                 POINTER(c_int64), c_int32, c_int32, c_int32, c_float, P, P, P, P,
+                                                 P, c_size_t, P]
+    lib.topk_attn_decode_int8_static.restype = c_int32
+    lib.topk_attn_decode_int8_static_workspace_size.argtypes = [POINTER(Layout), c_int64, c_int64, c_int32, c_int32]
+    lib.topk_attn_decode_int8_static_workspace_size.restype = c_size_t
     lib.retopk_workspace_size.argtypes = [POINTER(Layout), POINTER(RetopkParams), c_int64]
     lib.retopk_workspace_size.restype = c_size_t
     lib.stdk_last_error.argtypes = []

@@ -331,3 +331,52 @@ def topk_attn_decode_int8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
                                    lse_out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream())
     check(rc)
     return idx_out, sup_out, o_out, lse_out
+
+
+def topk_attn_decode_int8_static_workspace_size(layout: Layout, n_scan: int, n_static: int, top_k: int,
+                                                recall_k: int) -> int:
+    return int(load().topk_attn_decode_int8_static_workspace_size(ctypes.byref(layout), int(n_scan), int(n_static),
+                                                                  int(top_k), int(recall_k)))
+
+
+def topk_attn_decode_int8_static(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, codes: torch.Tensor,
+                                 scales: torch.Tensor, ranges: Sequence[Tuple[int, int]],
+                                 static_ranges: Sequence[Tuple[int, int]], top_k: int, recall_k: int,
+                                 scale: Optional[float] = None, *, idx_out: Optional[torch.Tensor] = None,
+                                 sup_out: Optional[torch.Tensor] = None, want_sup: bool = False,
+                                 o_out: Optional[torch.Tensor] = None, lse_out: Optional[torch.Tensor] = None,
+                                 workspace: Optional[torch.Tensor] = None, layout: Optional[Layout] = None):
+    """Dense attention over ``static_ranges`` together with the int8-recall
+    top-K attention over ``ranges``, in one pass (equals attn_merge_lse of the
+    dense call and topk_attn_decode_int8). Returns (idx, sup or None, o, lse)."""
+    lib = load()
+    B, Hq, d = q.shape
+    _need(q, "q", torch.float32)
+    _need(k_cache, "k_cache")
+    _need(v_cache, "v_cache", k_cache.dtype, k_cache.shape)
+    _need(codes, "codes", torch.int8, k_cache.shape)
+    _need(scales, "scales", torch.float32, k_cache.shape[:3])
+    lay = layout if layout is not None else make_layout(k_cache, Hq)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    n = sum(int(e) - int(b) for b, e in ranges)
+    n_st = sum(int(e) - int(b) for b, e in static_ranges)
+    if o_out is None:
+        o_out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if lse_out is None:
+        lse_out = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if idx_out is None:
+        idx_out = torch.empty((B, Hq, top_k), dtype=torch.int32, device=q.device)
+    if sup_out is None and want_sup:
+        sup_out = torch.empty((B, Hq, recall_k), dtype=torch.int32, device=q.device)
+    if workspace is None:
+        workspace = new_workspace(topk_attn_decode_int8_static_workspace_size(lay, n, n_st, top_k, recall_k),
+                                  q.device)
+    arr, nr = _ranges_arr(ranges)
+    sarr, ns = _ranges_arr(static_ranges)
+    rc = lib.topk_attn_decode_int8_static(ctypes.byref(lay), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                          codes.data_ptr(), scales.data_ptr(), arr, nr, sarr, ns, int(top_k),
+                                          int(recall_k), ctypes.c_float(scale), _ptr(idx_out), _ptr(sup_out),
+                                          o_out.data_ptr(), lse_out.data_ptr(), workspace.data_ptr(),
+                                          workspace.numel(), _stream())
+    check(rc)
+    return idx_out, sup_out, o_out, lse_out

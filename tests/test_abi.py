@@ -220,3 +220,35 @@ def test_int8_entry_points_reject(lib):
     assert lib.topk_attn_decode_int8_workspace_size(ctypes.byref(L), 4000, 64, 128) > \
         lib.topk_attn_decode_workspace_size(ctypes.byref(L), 4000, 64)
     assert lib.topk_attn_decode_int8_workspace_size(ctypes.byref(L), 4000, 64, 32) == 0
+
+
+def test_int8_static_entry_point_rejects(lib):
+    L = lay()
+    dyn = (ctypes.c_int64 * 2)(128, 3000)
+    st = (ctypes.c_int64 * 4)(0, 128, 3000, 3500)
+
+    def dec(top_k=8, recall_k=16, codes=FAKE, ws=1 << 30, ranges=dyn, n_r=1, static=st, n_s=2):
+        return lib.topk_attn_decode_int8_static(ctypes.byref(L), FAKE, FAKE, FAKE, codes, FAKE, ranges, n_r, static,
+                                                n_s, top_k, recall_k, ctypes.c_float(0.1), None, None, FAKE, FAKE,
+                                                FAKE, ws, None)
+    assert dec(recall_k=4) == native.STDK_EINVAL
+    assert dec(top_k=0) == native.STDK_EINVAL
+    assert dec(codes=0) == native.STDK_EINVAL
+    assert dec(ws=64) == native.STDK_EWORKSPACE
+    # a static range that overlaps a dynamic one
+    over = (ctypes.c_int64 * 4)(0, 130, 3000, 3500)
+    assert dec(static=over) == native.STDK_EINVAL
+    # too many ranges in total
+    many = (ctypes.c_int64 * 32)(*[v for i in range(16) for v in (3000 + 10 * i, 3005 + 10 * i)])
+    assert dec(static=many, n_s=16) == native.STDK_EINVAL
+    # top_k + |W| beyond the slot limit while top_k is below |Omega|
+    big = (ctypes.c_int64 * 2)(0, 70000)
+    L2 = lay(L=200000)
+    assert lib.topk_attn_decode_int8_static(ctypes.byref(L2), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                            (ctypes.c_int64 * 2)(70000, 190000), 1, big, 1, 8, 16,
+                                            ctypes.c_float(0.1), None, None, FAKE, FAKE, FAKE, 1 << 40,
+                                            None) == native.STDK_EUNSUPPORTED
+    a = lib.topk_attn_decode_int8_static_workspace_size(ctypes.byref(L), 2872, 628, 64, 512)
+    assert a >= lib.topk_attn_decode_int8_workspace_size(ctypes.byref(L), 2872, 64, 512)
+    assert a >= lib.topk_attn_decode_static_workspace_size(ctypes.byref(L), 2872, 628, 64)
+    assert lib.topk_attn_decode_int8_static_workspace_size(ctypes.byref(L), 2872, 628, 64, 32) == 0

@@ -69,9 +69,11 @@ def check_int8_heads(w, q, codes, scales, ranges, K, K2, idx, sup, o, lse, heads
     return float(np.mean(recall))
 
 
-@pytest.mark.parametrize("L,K,K2", [(8192, 256, 512), (8192, 256, 256), (5000, 100, 1500)])
+@pytest.mark.parametrize("L,K,K2", [(8192, 256, 512), (8192, 256, 256), (5000, 100, 1500),
+                                    (30000, 2000, 17000)])
 def test_int8_recall_c2_shape(ops, L, K, K2):
-    """Llama-3-8B head layout (32 q / 8 KV, bf16) at reduced length."""
+    """Llama-3-8B head layout (32 q / 8 KV, bf16) at reduced length; the last
+    case has more superset rows than the staged top-K keeps in LDS."""
     w = make_workload(2, L=L)
     log(f"case int8 recall c2 L={L} K={K} K'={K2}")
     q, codes, scales, idx, sup, o, lse = run_int8(ops, w, w.ranges, K, K2)
@@ -118,3 +120,139 @@ def test_int8_empty_ranges(ops):
     idx, sup, o, lse = ops.topk_attn_decode_int8(q, k, v, codes, scales, [], 8, 16, w.scale, want_sup=True)
     torch.cuda.synchronize()
     assert torch.all(idx == -1) and torch.all(sup == -1) and torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+# ---------------------------------------------------------------------------
+# int8 recall with a static window in one pass
+# ---------------------------------------------------------------------------
+def run_int8_static(ops, w, ranges, static, K, K2):
+    q = torch.from_numpy(w.q if w.q.ndim == 3 else np.ascontiguousarray(w.q[:, :, 0])).cuda()
+    k, v = dev_kv(w)
+    codes, scales = ops.quantize_keys_int8(k, ranges, w.H_q)
+    idx, sup, o, lse = ops.topk_attn_decode_int8_static(q, k, v, codes, scales, ranges, static, K, K2, w.scale,
+                                                        want_sup=True)
+    torch.cuda.synchronize()
+    return (q.cpu().numpy(), codes.cpu().numpy(), scales.cpu().numpy(), idx.cpu().numpy(), sup.cpu().numpy(),
+            o.cpu().numpy(), lse.cpu().numpy())
+
+
+def check_int8_static_heads(w, q, codes, scales, ranges, static, K, K2, idx, sup, o, lse, heads, label):
+    """Superset and chosen set as check_int8_heads; o / lse are the oracle's
+    attention over the chosen rows united with the static rows, and equal the
+    oracle's LSE merge of the two partial attentions."""
+    G = w.H_q // w.H_kv
+    rows = ref.range_rows(ranges)
+    srows_static = ref.range_rows(static)
+    for b, h in heads:
+        hk = h // G
+        z8 = ref.int8_scores(q[b, h], codes[b, hk], scales[b, hk], rows, w.scale)
+        _, zk8 = ref.select_topk(z8, rows, K2)
+        check_index_set(sup[b, h], rows, z8, zk8, K2)
+        srows = sup[b, h][sup[b, h] >= 0].astype(np.int64)
+        r = ref.attend_rows(q[b, h], w.k[b, hk], w.v[b, hk], srows, K, w.scale)
+        check_index_set(idx[b, h], srows, r["z"], r["zk"], K)
+        chosen = idx[b, h][idx[b, h] >= 0].astype(np.int64)
+        union = np.union1d(chosen, srows_static)
+        u = ref.attend_rows(q[b, h], w.k[b, hk], w.v[b, hk], union, union.shape[0], w.scale)
+        check_out(o[b, h], lse[b, h], u["o"], u["lse"], w.kv_dtype == "f32", f"{label} ({b},{h})")
+        if srows_static.shape[0] and chosen.shape[0]:
+            st = ref.attend_rows(q[b, h], w.k[b, hk], w.v[b, hk], srows_static, srows_static.shape[0], w.scale)
+            dy = ref.attend_rows(q[b, h], w.k[b, hk], w.v[b, hk], chosen, chosen.shape[0], w.scale)
+            mo, ml = ref.attn_merge_lse(st["o"][None], np.array([st["lse"]]), dy["o"][None], np.array([dy["lse"]]))
+            assert np.allclose(mo[0], u["o"], atol=1e-12) and abs(ml[0] - u["lse"]) < 1e-12
+
+
+@pytest.mark.parametrize("L,K,K2", [(8192, 256, 1024), (6000, 100, 700), (8192, 300, 300)])
+def test_int8_static_c2_shape(ops, L, K, K2):
+    """Llama-3-8B head layout, static window of the first 128 and last 512
+    rows, int8 recall over the rest."""
+    w = make_workload(2, L=L)
+    log(f"case int8 static c2 L={L} K={K} K'={K2}")
+    q, codes, scales, idx, sup, o, lse = run_int8_static(ops, w, w.ranges, w.static_ranges, K, K2)
+    check_int8_static_heads(w, q, codes, scales, w.ranges, w.static_ranges, K, K2, idx, sup, o, lse,
+                            [(0, h) for h in range(w.H_q)], f"int8 static L={L}")
+
+
+def test_int8_static_fp32_ragged(ops):
+    """fp32 cache, two dynamic and two static ranges, ragged lengths."""
+    w = make_multi_query(1, 4, 2, 1, 3000, "f32", tag=35)
+    w.q = np.ascontiguousarray(w.q[:, :, 0])
+    ranges = [(40, 900), (1000, 2811)]
+    static = [(0, 37), (2900, 3000)]
+    log("case int8 static fp32 ragged")
+    q, codes, scales, idx, sup, o, lse = run_int8_static(ops, w, ranges, static, 33, 130)
+    check_int8_static_heads(w, q, codes, scales, ranges, static, 33, 130, idx, sup, o, lse,
+                            [(0, h) for h in range(4)], "int8 static f32")
+
+
+def test_int8_static_equals_merge_of_calls(ops):
+    """The one pass against the dense static call, topk_attn_decode_int8 and
+    attn_merge_lse on the GPU: same chosen rows, outputs within fp32 rounding."""
+    w = make_workload(2, L=8192)
+    log("case int8 static vs merge of calls")
+    q = torch.from_numpy(w.q).cuda()
+    k, v = dev_kv(w)
+    codes, scales = ops.quantize_keys_int8(k, w.ranges, w.H_q)
+    K, K2 = 256, 1024
+    idx, sup, o, lse = ops.topk_attn_decode_int8_static(q, k, v, codes, scales, w.ranges, w.static_ranges, K, K2,
+                                                        w.scale, want_sup=True)
+    idx2, sup2, o_d, l_d = ops.topk_attn_decode_int8(q, k, v, codes, scales, w.ranges, K, K2, w.scale, want_sup=True)
+    n_st = sum(e - b for b, e in w.static_ranges)
+    _, o_s, l_s = ops.topk_attn_decode(q, k, v, w.static_ranges, n_st, w.scale)
+    o_m, l_m = ops.attn_merge_lse(o_s, l_s, o_d, l_d)
+    torch.cuda.synchronize()
+    assert torch.equal(sup, sup2) and torch.equal(idx, idx2)
+    assert torch.allclose(o, o_m, atol=1e-5, rtol=1e-4) and torch.allclose(lse, l_m, atol=1e-5, rtol=1e-5)
+
+
+def test_int8_static_full_superset_is_static_path(ops):
+    """recall_k >= |Omega|: topk_attn_decode_static's result, bit for bit, and
+    the superset lists every dynamic row; likewise with top_k >= |Omega|."""
+    w = make_workload(2, L=3000)
+    log("case int8 static recall_k >= n")
+    q = torch.from_numpy(w.q).cuda()
+    k, v = dev_kv(w)
+    codes, scales = ops.quantize_keys_int8(k, w.ranges, w.H_q)
+    n = sum(e - b for b, e in w.ranges)
+    for K in (200, n + 3):
+        idx, sup, o, lse = ops.topk_attn_decode_int8_static(q, k, v, codes, scales, w.ranges, w.static_ranges, K,
+                                                            max(K, n), w.scale, want_sup=True)
+        idx2, o2, lse2 = ops.topk_attn_decode_static(q, k, v, w.ranges, w.static_ranges, K, w.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(idx, idx2) and torch.equal(o, o2) and torch.equal(lse, lse2)
+        rows = torch.from_numpy(ref.range_rows(w.ranges).astype(np.int32)).cuda()
+        assert torch.equal(sup[:, :, :n], rows.expand(sup.shape[0], sup.shape[1], n))
+        assert torch.all(sup[:, :, n:] == -1)
+
+
+def test_int8_static_only_static_rows(ops):
+    """No dynamic rows: dense attention over the static window; idx and the
+    superset are all -1."""
+    w = make_workload(2, L=2048)
+    q = torch.from_numpy(w.q).cuda()
+    k, v = dev_kv(w)
+    codes = torch.zeros(k.shape, dtype=torch.int8, device="cuda")
+    scales = torch.zeros(k.shape[:3], dtype=torch.float32, device="cuda")
+    static = [(0, 128), (1536, 2048)]
+    idx, sup, o, lse = ops.topk_attn_decode_int8_static(q, k, v, codes, scales, [], static, 8, 16, w.scale,
+                                                        want_sup=True)
+    n_st = 640
+    _, o2, l2 = ops.topk_attn_decode(q, k, v, static, n_st, w.scale)
+    torch.cuda.synchronize()
+    assert torch.all(idx == -1) and torch.all(sup == -1)
+    assert torch.allclose(o, o2, atol=1e-6) and torch.allclose(lse, l2, atol=1e-6)
+
+
+def test_int8_static_equal_recall_without_sup(ops):
+    """recall_k == top_k with and without the superset output: the same
+    chosen rows, o and lse (the superset is then the chosen set)."""
+    w = make_workload(2, L=8192)
+    q = torch.from_numpy(w.q).cuda()
+    k, v = dev_kv(w)
+    codes, scales = ops.quantize_keys_int8(k, w.ranges, w.H_q)
+    a = ops.topk_attn_decode_int8_static(q, k, v, codes, scales, w.ranges, w.static_ranges, 300, 300, w.scale,
+                                         want_sup=True)
+    b = ops.topk_attn_decode_int8_static(q, k, v, codes, scales, w.ranges, w.static_ranges, 300, 300, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], a[1]) and torch.equal(a[0], b[0])
+    assert torch.equal(a[2], b[2]) and torch.equal(a[3], b[3])
