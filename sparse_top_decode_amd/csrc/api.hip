@@ -175,6 +175,10 @@ int32_t dev_info(DevInfo** out) {
                               std::max(0, d.max_lds - 4 * 1024));
     (void)hipFuncSetAttribute((const void*)retopk_rerank_select_lds, hipFuncAttributeMaxDynamicSharedMemorySize,
                               std::max(0, d.max_lds - 12 * 1024));
+    (void)hipFuncSetAttribute((const void*)sparse_sv_ds<uint16_t>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              std::max(0, d.max_lds - 20 * 1024));
+    (void)hipFuncSetAttribute((const void*)sparse_sv_ds<float>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              std::max(0, d.max_lds - 20 * 1024));
     (void)hipGetLastError();
     d.init = true;
   }
@@ -460,8 +464,10 @@ int32_t run_exact_select(const Geo& g, const TopkWs& w, char* ws, const float* q
 
 int32_t run_combine(const TopkWs& w, char* ws, int32_t np, float* o_out, float* lse_out, hipStream_t s);
 
-// Softmax . V over the chosen rows left by the select kernels, in slices of
-// kSvRows rows, then the combine.
+// Softmax . V over the chosen rows left by the select kernels: for few
+// heads with few rows (where the combine pass would cost as much as the
+// gather), one workgroup per (head, value slice); else slices of kSvRows
+// rows and the combine.
 int32_t run_sv(const Geo& g, const TopkWs& w, char* ws, const void* v_cache, float* o_out, float* lse_out,
                hipStream_t s, const RangeTab* tab = nullptr) {
   SvArgs a{};
@@ -480,6 +486,20 @@ int32_t run_sv(const Geo& g, const TopkWs& w, char* ws, const void* v_cache, flo
   a.nsplit = (int32_t)w.nsplit;
   a.Hq = g.Hq;
   a.G = g.G;
+  DevInfo* di = nullptr;
+  STDK_TRY(dev_info(&di));
+  const size_t ds_lds = (size_t)w.ksel * 8;
+  if (w.ksel <= kDsMaxSlots && w.S <= kDsMaxHeads && ds_lds + 20 * 1024 <= (size_t)di->max_lds) {
+    // one workgroup per (head, value slice): finished outputs, no combine
+    a.o_out = o_out;
+    a.lse_out = lse_out;
+    a.n_seg = w.S;
+    const dim3 grid((unsigned)(rup(w.S, kDsXcds) * kDsSlices));
+    return launch(KID_SV, s, [&](hipEvent_t e0, hipEvent_t e1) {
+      if (g.bf16) STDK_LAUNCH(sparse_sv_ds<uint16_t>, grid, dim3(kDsThreads), ds_lds, s, a);
+      else STDK_LAUNCH(sparse_sv_ds<float>, grid, dim3(kDsThreads), ds_lds, s, a);
+    });
+  }
   if (w.nsplit > kMaxPartials) return fail(STDK_EUNSUPPORTED, "%lld softmax.V partials per head", (long long)w.nsplit);
   const dim3 grid((unsigned)w.nsplit, (unsigned)w.S);
   STDK_TRY(launch(KID_SV, s, [&](hipEvent_t e0, hipEvent_t e1) {

@@ -402,6 +402,10 @@ struct SvArgs {
   const float* scores;        // [S][n_pad]
   int64_t n, n_pad;
   RangeTab tab;
+  // sparse_sv_ds only: the finished outputs and the number of segments
+  float* o_out;               // [S][128]
+  float* lse_out;             // [S]
+  int64_t n_seg;
 };
 
 constexpr int kSvThreads = 256;
@@ -498,6 +502,163 @@ __global__ __launch_bounds__(kSvThreads) void sparse_sv(SvArgs a) {
       part[0] = s_m;
       part[1] = s;
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// sparse_sv_ds: the same softmax . V with the work split over value
+// dimensions instead of rows. Workgroup (head, slice) takes every chosen row
+// of its head and the kDsDims value dimensions of its slice, so it finishes
+// its part of o by itself: no partials and no combine pass. Each workgroup
+// stages the head's rows and scores in LDS (8 bytes per slot) and takes
+// their maximum m, requests its slice of the first value rows, and forms
+// the sum of the weights e^{z - m} while they arrive (in a fixed order,
+// identical in every slice). Used where the heads and their rows are few:
+// the gathers of 32 B pieces need more requests per byte than whole rows.
+//
+// The kDsSlices workgroups of one head are placed on the same XCD (the
+// hardware deals consecutive workgroups to the 8 XCDs in turn), so the
+// value rows they share are fetched from HBM once, into that XCD's L2.
+// ---------------------------------------------------------------------------
+constexpr int kDsThreads = 256;
+constexpr int kDsDims = 16;                      // value dims per workgroup
+constexpr int kDsSlices = kHeadDim / kDsDims;    // workgroups per head
+constexpr int kDsMaxSlots = 1024;                // rows per head (LDS staging, one batch of loads)
+constexpr int kDsMaxHeads = 128;                 // beyond this the row split fills the chip better
+constexpr int kDsXcds = 8;
+
+template <typename T>
+__global__ __launch_bounds__(kDsThreads) void sparse_sv_ds(SvArgs a) {
+  constexpr int EPL = KvTraits<T>::EPL, ROWB = KvTraits<T>::ROWB;
+  constexpr int LPS = kDsDims / EPL;         // lanes per row slice (16 B each)
+  constexpr int NG = kDsThreads / LPS;       // row groups
+  constexpr int NW = kDsThreads / 64;
+  constexpr int U = 8;                       // value loads in flight per thread
+  extern __shared__ uint32_t ds_dyn[];
+  const int KT = a.K;                        // row slots of the head
+  int32_t* rows = reinterpret_cast<int32_t*>(ds_dyn);     // [KT]
+  float* zs = reinterpret_cast<float*>(ds_dyn + KT);     // [KT] scores, -inf for empty slots
+  constexpr int NP = kDsThreads / kDsDims;  // partial sums per value dim
+  constexpr int GP = NG / NP;               // row groups per partial sum
+  __shared__ float red[NG][kDsDims];
+  __shared__ float red2[NP][kDsDims];
+  __shared__ float wmax[NW], wsum[NW];
+  // XCD-aware placement: block L runs on XCD L % 8; the slices of one head
+  // share it
+  const int L = blockIdx.x;
+  const int xcd = L % kDsXcds, kk = L / kDsXcds;
+  const int64_t seg = (int64_t)(kk / kDsSlices) * kDsXcds + xcd;
+  const int slice = kk % kDsSlices;
+  if (seg >= a.n_seg) return;  // the grid covers the segments rounded up to a multiple of 8
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int b = (int)(seg / a.Hq), hq = (int)(seg % a.Hq), hkv = hq / a.G;
+
+  // 1. rows and scores of every slot, and the maximum: the chosen rows in
+  // batches of plain loads, then the static rows (rows from the range table)
+  float zm = -INFINITY;
+  const int kt = min(a.k_top, KT);
+  for (int j0 = 0; j0 < kt; j0 += kDsThreads * 4) {
+    int32_t r[4];
+    float z[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = min(j0 + u * kDsThreads + tid, kt - 1);
+      r[u] = a.sel_row[seg * a.k_top + j];
+      z[u] = a.sel_z[seg * a.k_top + j];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = j0 + u * kDsThreads + tid;
+      if (j < kt) {
+        const float zz = r[u] >= 0 ? z[u] : -INFINITY;
+        rows[j] = r[u];
+        zs[j] = zz;
+        zm = fmaxf(zm, zz);
+      }
+    }
+  }
+  const int nst = KT - kt;
+  for (int i0 = 0; i0 < nst; i0 += kDsThreads * 2) {
+    float z[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) z[u] = a.scores[seg * a.n_pad + a.n + min(i0 + u * kDsThreads + tid, nst - 1)];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = i0 + u * kDsThreads + tid;
+      if (i < nst) {
+        rows[kt + i] = (int32_t)pos_to_row(a.tab, a.n + i);
+        zs[kt + i] = z[u];
+        zm = fmaxf(zm, z[u]);
+      }
+    }
+  }
+  zm = wave_max(zm);
+  if (lane == 0) wmax[w] = zm;
+  __syncthreads();
+  float m = wmax[0];
+#pragma unroll
+  for (int v = 1; v < NW; ++v) m = fmaxf(m, wmax[v]);
+  auto weight = [&](float z) { return (m == -INFINITY || z == -INFINITY) ? 0.f : __expf(z - m); };
+
+  // 2. the slice of every value row, U rows per thread in flight; the first
+  // batch is requested before the weight sum is formed
+  const int gid = tid / LPS, c = tid % LPS;
+  const char* vb = a.v + (int64_t)b * a.stride_b_bytes + (int64_t)hkv * a.stride_h_bytes +
+                   slice * kDsDims * (int)sizeof(T) + c * 16;
+  auto issue = [&](int j0, u32x4 (&vw)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int32_t r = rows[min(j0 + NG * u, KT - 1)];
+      vw[u] = load16(vb + (int64_t)(r >= 0 ? r : 0) * ROWB);
+    }
+  };
+  u32x4 vw[U];
+  issue(gid, vw);
+  // weight sum: thread-strided partial sums in slot order, the wave
+  // butterflies, then the waves in order (the same in every slice)
+  float ps = 0.f;
+  for (int j = tid; j < KT; j += kDsThreads) ps += weight(zs[j]);
+  ps = wave_sum(ps);
+  if (lane == 0) wsum[w] = ps;
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  for (int j0 = gid;;) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + NG * u;
+      const float wt = j < KT ? weight(zs[j]) : 0.f;
+      float x[EPL];
+      unpack16<T>(vw[u], x);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(wt, x[e], acc[e]);
+    }
+    j0 += NG * U;
+    if (j0 >= KT) break;
+    issue(j0, vw);
+  }
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) red[gid][c * EPL + e] = acc[e];
+  __syncthreads();
+  float ssum = 0.f;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) ssum += wsum[v];
+  // 3. sum over the row groups in a fixed order (GP consecutive groups per
+  // thread, then the NP partial sums); the slice's outputs
+  {
+    const int d = tid % kDsDims, pp = tid / kDsDims;
+    float o = 0.f;
+#pragma unroll
+    for (int g = 0; g < GP; ++g) o += red[pp * GP + g][d];
+    red2[pp][d] = o;
+  }
+  __syncthreads();
+  if (tid < kDsDims) {
+    float o = 0.f;
+#pragma unroll
+    for (int g = 0; g < NP; ++g) o += red2[g][tid];
+    a.o_out[seg * kHeadDim + slice * kDsDims + tid] = ssum > 0.f ? o / ssum : 0.f;
+    if (slice == 0 && tid == 0) a.lse_out[seg] = ssum > 0.f ? m + __logf(ssum) : -INFINITY;
   }
 }
 
