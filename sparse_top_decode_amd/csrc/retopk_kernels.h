@@ -87,8 +87,6 @@ __global__ __launch_bounds__(kRtSelThreads) void retopk_select(RtSelArgs a) {
   constexpr int kGroups = kRtSelThreads / 8;  // cache slots per pass
   __shared__ float part[kMaxCache][8];
   __shared__ float sq[8];
-  __shared__ float rho[kMaxCache];
-  __shared__ int picked[kMaxCache];
   __shared__ int slot_of[kMaxCache];
   __shared__ uint32_t tmp[kRtSelThreads / 64 + 1];
   __shared__ int s_path, s_npick;
@@ -133,32 +131,61 @@ __global__ __launch_bounds__(kRtSelThreads) void retopk_select(RtSelArgs a) {
       part[sl][j] = t;
     }
   }
+  const int Wd = a.bitmap_words;
+  uint32_t* bm = kLdsBitmap ? dyn : (a.gbitmap + seg * (int64_t)Wd);
   __syncthreads();
-  // the entry of slot s has age (head - s) mod C; only the `count` newest are valid
-  if (tid < C) {
-    float r = 0.f;
+  // Wave 0 (C <= 64 slots, one per lane): the cosines, the path, the top R
+  // and the picked slots in slot order, with shuffles and ballots. The entry
+  // of slot s has age (head - s) mod C; only the `count` newest are valid.
+  if (tid < 64) {
+    const int sl = tid;
+    float re = -INFINITY;
+    int age = C;
+    bool valid = false;
+    if (sl < C) {
+      float r = 0.f;
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) r += part[tid][jj];
-    const int age = (hd - tid + C) % C;
-    rho[tid] = (age < cnt) ? r : -INFINITY;
-  }
-  __syncthreads();
-
-  if (tid == 0) {
-    float best = -INFINITY;
-    for (int sl = 0; sl < C; ++sl) {
-      const int age = (hd - sl + C) % C;
-      if (age < cnt) best = fmaxf(best, rho[sl]);
+      for (int jj = 0; jj < 8; ++jj) r += part[sl][jj];
+      age = hd - sl;
+      if (age < 0) age += C;
+      valid = age < cnt;
+      if (valid) re = r;
     }
+    const float best = wave_max(re);
     int path;
     if (a.refresh_now) path = 2;
     else if (cnt == 0 || best < a.tau) path = 1;
     else path = 0;
-    s_path = path;
-    a.path[seg] = path;
-    a.exact[seg] = path != 0;
-    if (a.path_out) a.path_out[seg] = path;
+    if (sl == 0) {
+      s_path = path;
+      a.path[seg] = path;
+      a.exact[seg] = path != 0;
+      if (a.path_out) a.path_out[seg] = path;
+    }
+    if (path == 0) {
+      // top-R by (cosine descending, age ascending): the rank is the number
+      // of valid entries with a larger (cosine key, ~age) pair; invalid
+      // lanes carry 0, below every valid pair
+      const uint32_t khi = valid ? f2key(re) : 0u, klo = valid ? ~(uint32_t)age : 0u;
+      int rank = 0;
+#pragma unroll
+      for (int f = 0; f < kMaxCache; ++f) {
+        const uint32_t fh = (uint32_t)__builtin_amdgcn_readlane((int)khi, f);
+        const uint32_t fl = (uint32_t)__builtin_amdgcn_readlane((int)klo, f);
+        rank += (fh > khi || (fh == khi && fl > klo)) ? 1 : 0;
+      }
+      const bool pk = valid && rank < a.R;
+      if (pk && a.rec_slot && rank < kMaxVote) {
+        a.rec_slot[seg * kMaxVote + rank] = sl;
+        a.rec_rho[seg * kMaxVote + rank] = re;
+      }
+      const uint64_t pm = __ballot(pk);
+      if (pk) slot_of[lane_rank(pm)] = sl;
+      if (sl == 0) s_npick = __popcll(pm);
+    }
   }
+  if (kLdsBitmap)
+    for (int i = tid; i < Wd; i += kRtSelThreads) bm[i] = 0u;
   __syncthreads();
   const int path = s_path;
   if (path != 0) {
@@ -170,40 +197,10 @@ __global__ __launch_bounds__(kRtSelThreads) void retopk_select(RtSelArgs a) {
       for (int i = tid; i < a.cand_cap; i += kRtSelThreads) a.cand_out[seg * a.cand_cap + i] = -1;
     return;
   }
-
-  // top-R by (cosine descending, age ascending)
-  if (tid < C) {
-    const int age_e = (hd - tid + C) % C;
-    int pk = 0;
-    if (age_e < cnt) {
-      const float re = rho[tid];
-      int rank = 0;
-      for (int sl = 0; sl < C; ++sl) {
-        const int age_f = (hd - sl + C) % C;
-        if (age_f >= cnt || sl == tid) continue;
-        const float rf = rho[sl];
-        if (rf > re || (rf == re && age_f < age_e)) ++rank;
-      }
-      pk = rank < a.R;
-      if (pk && a.rec_slot && rank < kMaxVote) {
-        a.rec_slot[seg * kMaxVote + rank] = tid;
-        a.rec_rho[seg * kMaxVote + rank] = re;
-      }
-    }
-    picked[tid] = pk;
+  if (!kLdsBitmap) {
+    for (int i = tid; i < Wd; i += kRtSelThreads) bm[i] = 0u;
+    __syncthreads();
   }
-  const int Wd = a.bitmap_words;
-  uint32_t* bm = kLdsBitmap ? dyn : (a.gbitmap + seg * (int64_t)Wd);
-  for (int i = tid; i < Wd; i += kRtSelThreads) bm[i] = 0u;
-  __syncthreads();
-  // the picked slots in slot order
-  if (tid == 0) {
-    int np = 0;
-    for (int sl = 0; sl < C; ++sl)
-      if (picked[sl]) slot_of[np++] = sl;
-    s_npick = np;
-  }
-  __syncthreads();
   const int64_t L = a.L_t;
   // union of the picked supports: index f of the flattened R x K list is
   // entry f % K of picked slot f / K; kU loads per thread are in flight
@@ -228,22 +225,33 @@ __global__ __launch_bounds__(kRtSelThreads) void retopk_select(RtSelArgs a) {
   for (int64_t x = max((int64_t)0, L - a.W) + tid; x < L; x += kRtSelThreads)
     atomicOr(&bm[x >> 5], 1u << (x & 31));
   __syncthreads();
-  // ascending compaction
-  const int per = (Wd + kRtSelThreads - 1) / kRtSelThreads;
-  const int w0 = tid * per, w1 = min(Wd, w0 + per);
+  // ascending compaction: wave w reads words [w0, w1) 64 at a time (lane l
+  // the word w0 + 64 i + l), counts its bits, and the waves' offsets come
+  // from one scan; then each word's bits go out at its wave-scan position
+  constexpr int NWv = kRtSelThreads / 64;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int wper = ((Wd + NWv - 1) / NWv + 63) & ~63;
+  const int w0 = min(Wd, wv * wper), w1 = min(Wd, w0 + wper);
   uint32_t c0 = 0;
-  for (int i = w0; i < w1; ++i) c0 += __popc(bm[i]);
+  for (int i = w0 + lane; i < w1; i += 64) c0 += __popc(bm[i]);
   uint32_t total;
-  uint32_t r = block_excl_scan<kRtSelThreads>(c0, tmp, &total);
+  const uint32_t wave_cnt = __shfl(wave_incl_scan(c0), 63, 64);
+  uint32_t r = block_excl_scan<kRtSelThreads>(lane == 0 ? wave_cnt : 0u, tmp, &total);
+  r = __shfl(r, 0, 64);
   int32_t* cd = a.cand + seg * a.cand_cap;
-  for (int i = w0; i < w1; ++i) {
-    uint32_t bits = bm[i];
+  for (int i0 = w0; i0 < w1; i0 += 64) {
+    const int i = i0 + lane;
+    uint32_t bits = i < w1 ? bm[i] : 0u;
+    const uint32_t n = __popc(bits);
+    const uint32_t incl = wave_incl_scan(n);
+    uint32_t pos = r + incl - n;
     while (bits) {
       const int j = __ffs(bits) - 1;
       bits &= bits - 1;
-      if (r < (uint32_t)a.cand_cap) cd[r] = i * 32 + j;
-      ++r;
+      if (pos < (uint32_t)a.cand_cap) cd[pos] = i * 32 + j;
+      ++pos;
     }
+    r += __shfl(incl, 63, 64);
   }
   if (tid == 0) {
     const int32_t M = (int32_t)min(total, (uint32_t)a.cand_cap);
