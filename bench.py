@@ -80,7 +80,7 @@ METRIC = "top-K decode-attention steps/sec at 128K ctx; K-scan HBM GB/s vs peak"
 TOPK_KERNELS = ("k_scan", "topk_filter", "topk_select", "sparse_sv", "dense_attn", "combine", "attn_merge")
 MQ_KERNELS = ("mq_blockmax", "mq_threshold", "mq_collect", "mq_select")
 RETOPK_KERNELS = ("retopk_select", "retopk_vote", "retopk_rerank", "retopk_rerank_select", "k_scan", "topk_filter",
-                  "topk_select", "sparse_sv", "combine", "retopk_push")
+                  "topk_select", "sparse_sv", "combine")
 
 
 def scan_source_hash() -> str:

@@ -366,7 +366,7 @@ int32_t stdk_version(void);        /* STDK_VERSION */
  * milliseconds and the launch count. Families: "k_scan",
  * "topk_filter", "topk_select", "sparse_sv", "dense_attn", "combine",
  * "attn_merge", "fill_empty", "retopk_select", "retopk_rerank",
- * "retopk_rerank_select", "retopk_push", "retopk_init", "retopk_vote",
+ * "retopk_rerank_select", "retopk_init", "retopk_vote",
  * "mq_blockmax", "mq_threshold", "mq_collect", "mq_select", "mq_fill",
  * "k_quantize".
  * Unknown names return STDK_EINVAL. */

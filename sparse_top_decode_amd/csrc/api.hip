@@ -57,13 +57,13 @@ int32_t ok() {
 // ---------------------------------------------------------------------------
 enum KernelId {
   KID_SCAN, KID_FILTER, KID_SELECT, KID_SV, KID_DENSE, KID_COMBINE, KID_MERGE, KID_FILL,
-  KID_RT_SELECT, KID_RT_RERANK, KID_RT_RSEL, KID_RT_PUSH, KID_RT_INIT, KID_MQ_BLOCKMAX, KID_MQ_THRESH,
+  KID_RT_SELECT, KID_RT_RERANK, KID_RT_RSEL, KID_RT_INIT, KID_MQ_BLOCKMAX, KID_MQ_THRESH,
   KID_MQ_COLLECT, KID_MQ_SELECT, KID_MQ_FILL, KID_RT_VOTE, KID_Q8_QUANT, KID_COUNT
 };
 const char* const kKernelNames[KID_COUNT] = {
     "k_scan",        "topk_filter",   "topk_select",          "sparse_sv",
     "dense_attn",  "combine",       "attn_merge",    "fill_empty",           "retopk_select",
-    "retopk_rerank", "retopk_rerank_select", "retopk_push", "retopk_init", "mq_blockmax",
+    "retopk_rerank", "retopk_rerank_select", "retopk_init", "mq_blockmax",
     "mq_threshold",  "mq_collect",    "mq_select",     "mq_fill",       "retopk_vote",   "k_quantize"};
 
 struct Profiler {
@@ -469,8 +469,12 @@ int32_t run_combine(const TopkWs& w, char* ws, int32_t np, float* o_out, float* 
 // gather), one workgroup per (head, value slice); else slices of kSvRows
 // rows and the combine.
 int32_t run_sv(const Geo& g, const TopkWs& w, char* ws, const void* v_cache, float* o_out, float* lse_out,
-               hipStream_t s, const RangeTab* tab = nullptr) {
+               hipStream_t s, const RangeTab* tab = nullptr, const SvPush* push = nullptr) {
   SvArgs a{};
+  if (push) {
+    a.do_push = 1;
+    a.push = *push;
+  }
   a.k_top = (int32_t)w.K;
   a.scores = (const float*)(ws + w.scores);
   a.n = w.n;
@@ -1358,14 +1362,11 @@ int32_t retopk_step(const stdk_layout* lay, const retopk_params* p, const retopk
     }));
     STDK_TRY(run_rerank_select(a, g.S, di, s));
   }
-  // a8: softmax . V over the chosen rows of every head (either path)
-  STDK_TRY(run_sv(g, w.t, ws, v_cache, o_out, lse_out, s));
-  // a8: push (q_bar, support)
-  {
-    RtPushArgs a{(const float*)(ws + w.qbar), support_out, st->q_hat, st->support, st->head, st->count,
-                 p->cache_cap, p->top_k};
-    STDK_TRY(launch(KID_RT_PUSH, s, [&](hipEvent_t e0, hipEvent_t e1) { STDK_LAUNCH(retopk_push, dim3((unsigned)g.S), dim3(256), 0, s, a); }));
-  }
+  // a8: softmax . V over the chosen rows of every head (either path), and
+  // the push of (q_bar, support) by one workgroup per head of that launch
+  const SvPush push{(const float*)(ws + w.qbar), support_out, st->q_hat, st->support, st->head, st->count,
+                    p->cache_cap, p->top_k};
+  STDK_TRY(run_sv(g, w.t, ws, v_cache, o_out, lse_out, s, nullptr, &push));
   return ok();
 }
 

@@ -813,32 +813,6 @@ __global__ __launch_bounds__(kRerankSelThreads) void retopk_rerank_select_lds(Rt
   }
 }
 
-// Push (q_bar, support) into slot (head + 1) mod C of every head.
-struct RtPushArgs {
-  const float* qbar;          // [S][128]
-  const int32_t* support_in;  // [S][K]
-  float* q_hat;
-  int32_t* support;
-  int32_t* head;
-  int32_t* count;
-  int32_t C, K;
-};
-
-__global__ __launch_bounds__(256) void retopk_push(RtPushArgs a) {
-  const int64_t seg = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int hd = a.head[seg], cnt = a.count[seg];
-  const int slot = (hd + 1) % a.C;
-  if (tid < kHeadDim) a.q_hat[(seg * a.C + slot) * kHeadDim + tid] = a.qbar[seg * kHeadDim + tid];
-  for (int i = tid; i < a.K; i += 256)
-    a.support[(seg * a.C + slot) * (int64_t)a.K + i] = a.support_in[seg * a.K + i];
-  __syncthreads();
-  if (tid == 0) {
-    a.head[seg] = slot;
-    a.count[seg] = min(cnt + 1, a.C);
-  }
-}
-
 // Fill the FIFO from a history of (query, support) pairs, oldest first.
 struct RtInitArgs {
   const float* q_hist;    // [S][n][128]

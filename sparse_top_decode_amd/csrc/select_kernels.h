@@ -387,6 +387,31 @@ __global__ __launch_bounds__(kSelThreads) void topk_select(SelectArgs a) {
 // sparse_sv: gathered-row softmax . V, kSvRows chosen rows per workgroup;
 // partial (m, s, o) per workgroup, merged by `combine`.
 // ---------------------------------------------------------------------------
+// The ReTopK cache push (q_bar and the chosen rows into FIFO slot
+// (head + 1) mod C of every head), done by one workgroup per head of the
+// softmax . V launch: every thread reads head and count before the kernel's
+// barriers, and thread 0 advances them after the last one.
+struct SvPush {
+  const float* qbar;          // [S][128]
+  const int32_t* support_in;  // [S][K]
+  float* q_hat;               // [S][C][128]
+  int32_t* support;           // [S][C][K]
+  int32_t* head;              // [S]
+  int32_t* count;             // [S]
+  int32_t C, K;
+};
+
+template <int NT>
+STDK_DEV int sv_push_copy(const SvPush& p, int64_t seg, int* cnt_out) {
+  const int tid = threadIdx.x;
+  const int hd = p.head[seg];
+  *cnt_out = p.count[seg];
+  const int slot = hd + 1 == p.C ? 0 : hd + 1;
+  if (tid < kHeadDim) p.q_hat[(seg * p.C + slot) * kHeadDim + tid] = p.qbar[seg * kHeadDim + tid];
+  for (int i = tid; i < p.K; i += NT) p.support[(seg * p.C + slot) * (int64_t)p.K + i] = p.support_in[seg * p.K + i];
+  return slot;
+}
+
 struct SvArgs {
   const char* v;              // value cache base
   int64_t stride_b_bytes, stride_h_bytes;
@@ -406,6 +431,8 @@ struct SvArgs {
   float* o_out;               // [S][128]
   float* lse_out;             // [S]
   int64_t n_seg;
+  int32_t do_push, pad2_;
+  SvPush push;
 };
 
 constexpr int kSvThreads = 256;
@@ -423,6 +450,9 @@ __global__ __launch_bounds__(kSvThreads) void sparse_sv(SvArgs a) {
   const int64_t seg = blockIdx.y;
   if (a.seg_active && a.seg_active[seg] == 0) return;
   const int split = blockIdx.x;
+  const bool pusher = a.do_push && split == 0;
+  int push_slot = 0, push_cnt = 0;
+  if (pusher) push_slot = sv_push_copy<kSvThreads>(a.push, seg, &push_cnt);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int gid = tid / LPR, c = tid % LPR;
   const int b = (int)(seg / a.Hq), hq = (int)(seg % a.Hq), hkv = hq / a.G;
@@ -503,6 +533,10 @@ __global__ __launch_bounds__(kSvThreads) void sparse_sv(SvArgs a) {
       part[1] = s;
     }
   }
+  if (pusher && tid == 0) {
+    a.push.head[seg] = push_slot;
+    a.push.count[seg] = min(push_cnt + 1, a.push.C);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -552,6 +586,9 @@ __global__ __launch_bounds__(kDsThreads) void sparse_sv_ds(SvArgs a) {
   if (seg >= a.n_seg) return;  // the grid covers the segments rounded up to a multiple of 8
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int b = (int)(seg / a.Hq), hq = (int)(seg % a.Hq), hkv = hq / a.G;
+  const bool pusher = a.do_push && slice == 0;
+  int push_slot = 0, push_cnt = 0;
+  if (pusher) push_slot = sv_push_copy<kDsThreads>(a.push, seg, &push_cnt);
 
   // 1. rows and scores of every slot, and the maximum: the chosen rows in
   // batches of plain loads, then the static rows (rows from the range table)
@@ -659,6 +696,10 @@ __global__ __launch_bounds__(kDsThreads) void sparse_sv_ds(SvArgs a) {
     for (int g = 0; g < NP; ++g) o += red2[g][tid];
     a.o_out[seg * kHeadDim + slice * kDsDims + tid] = ssum > 0.f ? o / ssum : 0.f;
     if (slice == 0 && tid == 0) a.lse_out[seg] = ssum > 0.f ? m + __logf(ssum) : -INFINITY;
+  }
+  if (pusher && tid == 0) {
+    a.push.head[seg] = push_slot;
+    a.push.count[seg] = min(push_cnt + 1, a.push.C);
   }
 }
 
