@@ -256,3 +256,22 @@ def test_int8_static_equal_recall_without_sup(ops):
     torch.cuda.synchronize()
     assert torch.equal(a[0], a[1]) and torch.equal(a[0], b[0])
     assert torch.equal(a[2], b[2]) and torch.equal(a[3], b[3])
+
+
+@pytest.mark.parametrize("K,K2", [(100, 700), (300, 300), (64, 5000)])
+def test_int8_exact_ties_codebook(ops, K, K2):
+    """Keys drawn from a 6-row codebook: int8 and exact scores tie in groups
+    of thousands, so both the superset and the final set are decided by the
+    lowest-row rule. Both must equal the oracle's exactly (with a static
+    window in the same call)."""
+    w = make_multi_query(1, 4, 2, 1, 12000, "bf16", codebook=6, tag=41)
+    w.q = np.ascontiguousarray(w.q[:, :, 0])
+    ranges = [(100, 7000), (7500, 11800)]
+    static = [(0, 100), (11800, 12000)]
+    log(f"case int8 codebook ties K={K} K'={K2}")
+    q, codes, scales, idx, sup, o, lse = run_int8_static(ops, w, ranges, static, K, K2)
+    want = ref.topk_attn_decode_int8(q, w.k, w.v, codes, scales, ranges, K, K2, w.scale)
+    assert np.array_equal(sup, want["sup"]), "superset differs from the oracle's"
+    assert np.array_equal(idx, want["idx"]), "chosen rows differ from the oracle's"
+    check_int8_static_heads(w, q, codes, scales, ranges, static, K, K2, idx, sup, o, lse,
+                            [(0, h) for h in range(4)], f"int8 ties K={K}")
