@@ -26,7 +26,7 @@ STDK_DEV void combine_partials(const float* part, int np, float* o_out, float* l
   const int j = threadIdx.x;
   // this thread's output element of the first partials, requested together
   // with the (m, s) pairs so that one memory round trip serves both
-  constexpr int PB = 32;
+  constexpr int PB = 64;
   float ov[PB];
 #pragma unroll
   for (int i = 0; i < PB; ++i) ov[i] = part[(int64_t)min(i, np - 1) * kPartStride + 4 + j];
