@@ -256,53 +256,123 @@ STDK_DEV void select_rest(const SelectArgs& a, int64_t seg, uint32_t m, uint32_t
     need -= *s_beyond;  // rows with key == Tk to keep, the first ones in position order
   }
 
-  // Ordered compaction: thread t owns candidates [t*per, (t+1)*per). One block
-  // scan of (count > Tk, count == Tk) gives each thread its output offset:
-  // the rows above Tk before it plus the ties before it that are kept.
-  const uint32_t per = (m + kSelThreads - 1) / kSelThreads;
-  const uint32_t i0 = min(m, tid * per), i1 = min(m, i0 + per);
-  uint32_t n_gt = 0, n_eq = 0;
-  for (uint32_t ib = i0; ib < i1; ib += U) {
-    uint32_t kv[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) kv[u] = cl[min(ib + u, i1 - 1)].key;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (ib + u < i1) {
-        n_gt += take_all || kv[u] > Tk;
-        n_eq += !take_all && kv[u] == Tk;
-      }
-    }
-  }
-  uint32_t gt_before, eq_before, tot_gt, tot_eq;
-  block_excl_scan2<kSelThreads>(n_gt, n_eq, tmp, &gt_before, &eq_before, &tot_gt, &tot_eq);
-  const uint32_t tot_all = tot_gt + min(tot_eq, need);
-  uint32_t r = gt_before + min(eq_before, need);
   int32_t* srow = a.sel_row + seg * K;
   float* sz = a.sel_z + seg * K;
   int32_t* io = a.idx_out ? a.idx_out + seg * K : nullptr;
-  uint32_t eq_seen = eq_before;
-  for (uint32_t ib = i0; ib < i1; ib += U) {
-    Cand cv[U];
+  uint32_t tot_all = 0;
+  if (m <= 8u * kSelThreads) {
+    // Ordered compaction for up to 8 candidates per thread: thread t owns
+    // candidates [t*per, (t+1)*per), all read at once. One block scan of
+    // (count > Tk, count == Tk) gives each thread its output offset: the
+    // rows above Tk before it plus the ties before it that are kept.
+    const uint32_t per = (m + kSelThreads - 1) / kSelThreads;
+    const uint32_t i0 = min(m, tid * per), i1 = min(m, i0 + per);
+    uint32_t n_gt = 0, n_eq = 0;
+    for (uint32_t ib = i0; ib < i1; ib += U) {
+      uint32_t kv[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) cv[u] = cl[min(ib + u, i1 - 1)];
+      for (int u = 0; u < U; ++u) kv[u] = cl[min(ib + u, i1 - 1)].key;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (ib + u < i1) {
-        bool take = take_all || cv[u].key > Tk;
-        if (!take_all && cv[u].key == Tk) {
-          take = eq_seen < need;
-          ++eq_seen;
+      for (int u = 0; u < U; ++u) {
+        if (ib + u < i1) {
+          n_gt += take_all || kv[u] > Tk;
+          n_eq += !take_all && kv[u] == Tk;
         }
-        if (take) {
-          if (r < (uint32_t)K) {
-            const int32_t row = (int32_t)pos_to_row(a.tab, cv[u].pos);
-            srow[r] = row;
-            sz[r] = key2f(cv[u].key);
-            if (io) io[r] = row;
+      }
+    }
+    uint32_t gt_before, eq_before, tot_gt, tot_eq;
+    block_excl_scan2<kSelThreads>(n_gt, n_eq, tmp, &gt_before, &eq_before, &tot_gt, &tot_eq);
+    tot_all = tot_gt + min(tot_eq, need);
+    uint32_t r = gt_before + min(eq_before, need);
+    uint32_t eq_seen = eq_before;
+    for (uint32_t ib = i0; ib < i1; ib += U) {
+      Cand cv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) cv[u] = cl[min(ib + u, i1 - 1)];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (ib + u < i1) {
+          bool take = take_all || cv[u].key > Tk;
+          if (!take_all && cv[u].key == Tk) {
+            take = eq_seen < need;
+            ++eq_seen;
           }
-          ++r;
+          if (take) {
+            if (r < (uint32_t)K) {
+              const int32_t row = (int32_t)pos_to_row(a.tab, cv[u].pos);
+              srow[r] = row;
+              sz[r] = key2f(cv[u].key);
+              if (io) io[r] = row;
+            }
+            ++r;
+          }
         }
+      }
+    }
+  } else {
+    // Ordered compaction for more candidates (contiguous runs per thread
+    // would conflict on LDS banks and scatter the stores): wave w owns
+    // candidates [w*SEG, (w+1)*SEG), read 64
+    // at a time with consecutive lanes on consecutive candidates. The waves'
+    // counts (above Tk, equal to Tk) give each wave its output offset: the
+    // rows above Tk before it plus the ties before it that are kept; inside a
+    // wave, ballots rank the ties and the taken rows, so consecutive lanes
+    // write consecutive slots.
+    const uint32_t SEG = ((m + kSelectWaves - 1) / kSelectWaves + 63u) & ~63u;
+    const uint32_t s0 = min(m, (uint32_t)wv * SEG), s1 = min(m, s0 + SEG);
+    constexpr int CU = 4;  // chunks of 64 whose reads are issued together
+    uint32_t cg = 0, ce = 0;
+    for (uint32_t jb = s0; jb < s1; jb += 64 * CU) {
+      uint32_t kv[CU];
+#pragma unroll
+      for (int u = 0; u < CU; ++u) kv[u] = cl[min(jb + 64 * u + lane, s1 - 1)].key;
+#pragma unroll
+      for (int u = 0; u < CU; ++u) {
+        const bool valid = jb + 64 * u + lane < s1;
+        cg += valid && (take_all || kv[u] > Tk);
+        ce += valid && !take_all && kv[u] == Tk;
+      }
+    }
+    cg = __shfl(wave_incl_scan(cg), 63, 64);
+    ce = __shfl(wave_incl_scan(ce), 63, 64);
+    if (lane == 0) {
+      tmp[wv] = cg;
+      tmp[kSelectWaves + wv] = ce;
+    }
+    __syncthreads();
+    uint32_t out = 0, eq_seen = 0, eq_all = 0;
+#pragma unroll
+    for (int v = 0; v < kSelectWaves; ++v) {
+      const uint32_t e = tmp[kSelectWaves + v];
+      const uint32_t te = min(e, need > eq_all ? need - eq_all : 0u);
+      if (v < wv) {
+        out += tmp[v] + te;
+        eq_seen += e;
+      }
+      tot_all += tmp[v] + te;
+      eq_all += e;
+    }
+    for (uint32_t jb = s0; jb < s1; jb += 64 * CU) {
+      Cand cv[CU];
+#pragma unroll
+      for (int u = 0; u < CU; ++u) cv[u] = cl[min(jb + 64 * u + lane, s1 - 1)];
+#pragma unroll
+      for (int u = 0; u < CU; ++u) {
+        const bool valid = jb + 64 * u + lane < s1;
+        const bool gt = valid && (take_all || cv[u].key > Tk);
+        const bool eq = valid && !take_all && cv[u].key == Tk;
+        const uint64_t em = __ballot(eq);
+        const bool take = gt || (eq && eq_seen + lane_rank(em) < need);
+        const uint64_t tm = __ballot(take);
+        const uint32_t pos = out + lane_rank(tm);
+        if (take && pos < (uint32_t)K) {
+          const int32_t row = (int32_t)pos_to_row(a.tab, cv[u].pos);
+          srow[pos] = row;
+          sz[pos] = key2f(cv[u].key);
+          if (io) io[pos] = row;
+        }
+        out += (uint32_t)__popcll(tm);
+        eq_seen += (uint32_t)__popcll(em);
       }
     }
   }

@@ -128,6 +128,24 @@ def test_exact_ties_lowest_row_wins(ops):
     log(f"tie heads checked exactly: {n_exact}")
 
 
+@pytest.mark.parametrize("K", [300, 9000])
+def test_codebook_ties_many_candidates(ops, K):
+    """Keys from a 6-row codebook over 24,000 rows: every score ties with
+    thousands of others. K = 9000 puts more than 8 candidates per select
+    thread into the tied bin (the wave-segment compaction), K = 300 fewer;
+    both sets must equal the oracle's exactly (lowest rows first)."""
+    from workloads import make_multi_query
+    w = make_multi_query(1, 4, 2, 1, 24000, "bf16", codebook=6, tag=43)
+    w.q = np.ascontiguousarray(w.q[:, :, 0])
+    ranges = [(0, 11000), (12000, 24000)]
+    log(f"case codebook ties K={K}")
+    idx, o, lse = run(ops, w, ranges, K)
+    want = ref.topk_attn_decode(w.q, w.k, w.v, ranges, K, w.scale)
+    assert np.array_equal(idx, want["idx"])
+    for h in range(w.H_q):
+        check_out(o[0, h], lse[0, h], want["o"][0, h], want["lse"][0, h], False, f"codebook K={K} head {h}")
+
+
 def test_c4_batch_reduced(ops):
     """Batch of 16 sequences with per-sequence key offsets, K=1024."""
     log("case c4 reduced B=16 L=4096 K=1024")
