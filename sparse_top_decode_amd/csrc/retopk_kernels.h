@@ -88,6 +88,7 @@ __global__ __launch_bounds__(kRtSelThreads) void retopk_select(RtSelArgs a) {
   __shared__ float part[kMaxCache][8];
   __shared__ float sq[8];
   __shared__ int slot_of[kMaxCache];
+  __shared__ uint2 rkey[kMaxCache];
   __shared__ uint32_t tmp[kRtSelThreads / 64 + 1];
   __shared__ int s_path, s_npick;
   const int64_t seg = blockIdx.x;
@@ -135,7 +136,7 @@ __global__ __launch_bounds__(kRtSelThreads) void retopk_select(RtSelArgs a) {
   uint32_t* bm = kLdsBitmap ? dyn : (a.gbitmap + seg * (int64_t)Wd);
   __syncthreads();
   // Wave 0 (C <= 64 slots, one per lane): the cosines, the path, the top R
-  // and the picked slots in slot order, with shuffles and ballots. The entry
+  // and the picked slots in slot order, with LDS broadcasts and ballots. The entry
   // of slot s has age (head - s) mod C; only the `count` newest are valid.
   if (tid < 64) {
     const int sl = tid;
@@ -165,14 +166,20 @@ __global__ __launch_bounds__(kRtSelThreads) void retopk_select(RtSelArgs a) {
     if (path == 0) {
       // top-R by (cosine descending, age ascending): the rank is the number
       // of valid entries with a larger (cosine key, ~age) pair; invalid
-      // lanes carry 0, below every valid pair
+      // lanes carry 0, below every valid pair. The pairs go through LDS and
+      // every lane reads all 64 (same address across the wave: broadcast
+      // reads, issued back to back).
       const uint32_t khi = valid ? f2key(re) : 0u, klo = valid ? ~(uint32_t)age : 0u;
+      rkey[sl] = make_uint2(khi, klo);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      const uint64_t mine = ((uint64_t)khi << 32) | klo;
       int rank = 0;
 #pragma unroll
       for (int f = 0; f < kMaxCache; ++f) {
-        const uint32_t fh = (uint32_t)__builtin_amdgcn_readlane((int)khi, f);
-        const uint32_t fl = (uint32_t)__builtin_amdgcn_readlane((int)klo, f);
-        rank += (fh > khi || (fh == khi && fl > klo)) ? 1 : 0;
+        const uint2 kf = rkey[f];
+        rank += ((((uint64_t)kf.x << 32) | kf.y) > mine) ? 1 : 0;
       }
       const bool pk = valid && rank < a.R;
       if (pk && a.rec_slot && rank < kMaxVote) {
