@@ -144,11 +144,13 @@ def test_retopk_always_exact_equals_topk(ops):
         assert torch.equal(out["o"], o) and torch.equal(out["lse"], lse)
 
 
-@pytest.mark.parametrize("B,tau,K,L", [(3, 0.90, 128, 8192), (1, 0.85, 1024, 16384)])
+@pytest.mark.parametrize("B,tau,K,L", [(3, 0.90, 128, 8192), (1, 0.85, 1024, 16384), (5, 0.85, 1100, 8192)])
 def test_retopk_serving_variants(ops, B, tau, K, L):
     """Serving-shaped steps: several requests in one call, each with its own
     caches, at the pages' stricter threshold (tau = 0.90), and the K = 1024
-    budget of the cross-model runs; c3's head layout, C=32, R=4, W=32."""
+    budget of the cross-model runs; c3's head layout, C=32, R=4, W=32. The
+    last case (140 heads, K = 1100) takes the row-split softmax . V, whose
+    split-0 workgroups push the cache."""
     w = make_workload(3, L=L, steps=24, warm=32, B=B)
     p = ref.RetopkParams(top_k=K, cache_cap=32, top_r=4, recent=32, tau=tau, refresh=16)
     heads = [(b, h) for b in range(B) for h in (0, 6, 13, 20, 27)]
