@@ -787,13 +787,38 @@ int32_t run_int8(const Geo& g, const Q8Ws& w, char* ws, const float* q, const vo
                  int32_t recall_k, float scale, int32_t* idx_out, int32_t* sup_out, float* o_out, float* lse_out,
                  const DevInfo* di, hipStream_t s) {
   // recall_k == top_k: the superset is the answer, and only its exact
-  // scores are still needed
+  // scores are still needed: the softmax . V workgroups score their own rows
   const bool same = recall_k == top_k;
   int32_t* first = same && idx_out ? idx_out : sup_out;
   STDK_TRY(run_exact_select(g, w.t1, ws, q, nullptr, tab, scale, nullptr, first, di, s, &keys));
   if (same && idx_out && sup_out) {
     const hipError_t e = hipMemcpyAsync(sup_out, idx_out, (size_t)g.S * top_k * 4, hipMemcpyDeviceToDevice, s);
     if (e != hipSuccess) return fail(STDK_EHIP, "hipMemcpyAsync: %s", hipGetErrorString(e));
+  }
+  if (same) {
+    SvArgs a{};
+    a.k_top = top_k;
+    a.K = (int32_t)(top_k + n_st);
+    a.nsplit = (int32_t)cdiv(a.K, kSvRows);
+    a.sel_row = (const int32_t*)(ws + w.t1.sel_row);
+    a.n = 0;
+    a.tab = stab;
+    a.v = (const char*)v_cache;
+    a.kc = (const char*)k_cache;
+    a.q = q;
+    a.scale = scale;
+    a.stride_b_bytes = g.sb_bytes;
+    a.stride_h_bytes = g.sh_bytes;
+    a.part = (float*)(ws + w.t2.part);
+    a.Hq = g.Hq;
+    a.G = g.G;
+    if (a.nsplit > kMaxPartials) return fail(STDK_EUNSUPPORTED, "%d softmax.V partials per head", a.nsplit);
+    const dim3 grid((unsigned)a.nsplit, (unsigned)g.S);
+    STDK_TRY(launch(KID_SV, s, [&](hipEvent_t e0, hipEvent_t e1) {
+      if (g.bf16) STDK_LAUNCH(sparse_sv_scored<uint16_t>, grid, dim3(kSvThreads), 0, s, a);
+      else STDK_LAUNCH(sparse_sv_scored<float>, grid, dim3(kSvThreads), 0, s, a);
+    }));
+    return run_combine(w.t2, ws, a.nsplit, o_out, lse_out, s);
   }
   RtRerankArgs a{};
   a.q = q;

@@ -503,6 +503,12 @@ struct SvArgs {
   int64_t n_seg;
   int32_t do_push, pad2_;
   SvPush push;
+  // sparse_sv_scored only: the queries and the key cache its rows are
+  // scored from
+  const float* q;             // [S][128]
+  const char* kc;             // key cache base (same layout as the values)
+  float scale;
+  int32_t pad3_;
 };
 
 constexpr int kSvThreads = 256;
@@ -770,6 +776,100 @@ __global__ __launch_bounds__(kDsThreads) void sparse_sv_ds(SvArgs a) {
   if (pusher && tid == 0) {
     a.push.head[seg] = push_slot;
     a.push.count[seg] = min(push_cnt + 1, a.push.C);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// sparse_sv_scored: sparse_sv for a row list that comes without scores (the
+// int8 recall step with recall_k == top_k, whose superset is the answer).
+// Each workgroup scores its own kSvRows slots from the key cache, z =
+// scale * (q . k) in fp32 (each lane's 16-byte chunk, then the sum over the
+// row's lanes, as the rerank does), and forms the partial (m, s, o) of its
+// slots as sparse_sv does; `combine` merges them. Slots past the chosen
+// rows are the static rows (range table), scored the same way.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(kSvThreads) void sparse_sv_scored(SvArgs a) {
+  constexpr int EPL = KvTraits<T>::EPL, LPR = KvTraits<T>::LPR, ROWB = KvTraits<T>::ROWB;
+  constexpr int NG = kSvThreads / LPR;  // row groups
+  constexpr int RU = kSvRows / NG;      // rows per row group
+  constexpr int NW = kSvThreads / 64;
+  __shared__ float red[NG][kHeadDim];
+  __shared__ float wmax[NW], wsum[NW];
+  const int64_t seg = blockIdx.y;
+  const int split = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int gid = tid / LPR, c = tid % LPR;
+  const int b = (int)(seg / a.Hq), hq = (int)(seg % a.Hq), hkv = hq / a.G;
+  const int j0 = split * kSvRows;
+  const int nr = min(kSvRows, a.K - j0);
+  float qr[1][EPL];
+  load_q_slice<T, 1>(a.q, seg, c, qr);
+  const int64_t hoff = (int64_t)b * a.stride_b_bytes + (int64_t)hkv * a.stride_h_bytes + c * 16;
+  // the row of each of this thread's RU slots (-1: padding), then its key
+  // and value chunks, all requested together
+  int32_t rr[RU];
+#pragma unroll
+  for (int u = 0; u < RU; ++u) {
+    const int jj = gid + NG * u;
+    const int j = j0 + jj;
+    rr[u] = -1;
+    if (jj < nr) rr[u] = j < a.k_top ? a.sel_row[seg * a.k_top + j] : (int32_t)pos_to_row(a.tab, a.n + (j - a.k_top));
+  }
+  u32x4 kw[RU], vw[RU];
+#pragma unroll
+  for (int u = 0; u < RU; ++u) {
+    const int64_t off = hoff + (int64_t)(rr[u] >= 0 ? rr[u] : 0) * ROWB;
+    kw[u] = load16(a.kc + off);
+    vw[u] = load16(a.v + off);
+  }
+  float z[RU];
+  float zm = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < RU; ++u) {
+    float d[1];
+    chunk_dots<T, 1>(kw[u], qr, d);
+    const float sdot = group_sum<LPR>(d[0]);
+    z[u] = rr[u] >= 0 ? sdot * a.scale : -INFINITY;
+    zm = fmaxf(zm, z[u]);
+  }
+  zm = wave_max(zm);
+  if (lane == 0) wmax[w] = zm;
+  __syncthreads();
+  float m = wmax[0];
+#pragma unroll
+  for (int v = 1; v < NW; ++v) m = fmaxf(m, wmax[v]);
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  float ps = 0.f;  // the weights of the slots, counted once (lane 0 of each row group)
+#pragma unroll
+  for (int u = 0; u < RU; ++u) {
+    const float wt = (m == -INFINITY || z[u] == -INFINITY) ? 0.f : __expf(z[u] - m);
+    float x[EPL];
+    unpack16<T>(rr[u] >= 0 ? vw[u] : u32x4{0u, 0u, 0u, 0u}, x);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = fmaf(wt, x[e], acc[e]);
+    if (c == 0) ps += wt;
+  }
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) red[gid][c * EPL + e] = acc[e];
+  ps = wave_sum(ps);
+  if (lane == 0) wsum[w] = ps;
+  __syncthreads();
+  float* part = a.part + (seg * a.nsplit + split) * kPartStride;
+  if (tid < kHeadDim) {
+    float o = 0.f;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) o += red[g][tid];
+    part[4 + tid] = o;
+  }
+  if (tid == 0) {
+    float st = 0.f;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) st += wsum[v];
+    part[0] = m;
+    part[1] = st;
   }
 }
 
