@@ -685,8 +685,9 @@ Q8Ws q8_ws(const Geo& g, int64_t n, int64_t K, int64_t K2, int64_t n_st = 0) {
   w.t2.n_pad = n_st;
   w.t2.scores = w.czs;
   if (K == K2) {
-    // the superset is the final set: softmax . V reads the superset's rows
-    // and their exact scores in place
+    // the superset is the final set: softmax . V (sparse_sv_scored) reads
+    // the superset's rows in place and scores them itself; the score arrays
+    // above stay unused
     w.t2.sel_row = w.t1.sel_row;
     w.t2.sel_z = w.cz;
   } else {
