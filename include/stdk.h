@@ -22,9 +22,14 @@
  *    again. They must be zero before the first call that uses the buffer
  *    (fill the new buffer with zeros once, e.g. hipMemset). Every call that
  *    returns STDK_OK leaves them zero, so the buffer can be reused by later
- *    calls with the same stdk_layout (topk_attn_decode and retopk_step
- *    alike) without clearing. After a call that returned STDK_EHIP, or
- *    before reuse with a different layout, zero the buffer again.
+ *    calls with the same stdk_layout (topk_attn_decode, its _static and
+ *    _int8 variants, retopk_step, and topk_multi_query, which leaves that
+ *    region untouched) without clearing. A call that returns STDK_EHIP after
+ *    its scan was enqueued leaves the counters non-zero: the library records
+ *    the buffer's address, and the next call given that address clears the
+ *    counter region on its stream before anything else (one small kernel).
+ *    A buffer reused with a larger layout must be zeroed again by the caller
+ *    over the larger counter region.
  *  - KV cache layout (stdk_layout): element (b, h_kv, row, j) lives at
  *        base + b*stride_b + h_kv*stride_h + row*head_dim + j
  *    (rows are contiguous, head_dim elements each). Keys and values share
@@ -170,7 +175,8 @@ size_t topk_attn_decode_static_workspace_size(const stdk_layout* lay, int64_t n_
  *             idx_out, -inf in the padding.
  *  workspace  at least topk_multi_query_workspace_size(lay, M, n, top_k)
  *             bytes, 256-byte aligned, any contents (this call keeps no
- *             counters in it). Not used when n = 0.
+ *             counters in it, and leaves the first B * H_q * 8192 bytes,
+ *             the decode calls' counters, untouched). Not used when n = 0.
  *  Limits: B * n_kv_heads <= 65535.
  * The scores are computed on the bf16 matrix cores with every fp32 query
  * element split into a bf16 value and a bf16 remainder (and every fp32 key
@@ -350,11 +356,30 @@ int32_t retopk_step(const stdk_layout* lay, const retopk_params* p, const retopk
 
 size_t retopk_workspace_size(const stdk_layout* lay, const retopk_params* p, int64_t max_L_t);
 
+/* Bytes of one allocation that holds the four state arrays of `lay` and
+ * `p`, placed at 256-byte aligned offsets in this order (S = B * H_q,
+ * C = cache_cap, K = top_k, al(x) = x rounded up to a multiple of 256):
+ *   q_hat   at 0                                  (S*C*128 fp32)
+ *   support at al(S*C*512)                        (S*C*K int32)
+ *   head    at al(S*C*512) + al(S*C*K*4)          (S int32)
+ *   count   at that + al(S*4)                     (S int32)
+ * The state is plain data: copying the four arrays out and back (e.g. to
+ * host memory and into a fresh buffer) checkpoints and resumes a decode.
+ * 0 for invalid arguments. */
+size_t retopk_state_size(const stdk_layout* lay, const retopk_params* p);
+
 /* ------------------------------------------------------------------------
  * Helpers
  * ---------------------------------------------------------------------- */
 const char* stdk_last_error(void); /* host string, valid until the next call on this thread */
 int32_t stdk_version(void);        /* STDK_VERSION */
+
+/* Testing aid for the error path: the library launch numbered
+ * `after_launches` (0-based, counted over all threads from this call on) is
+ * not enqueued; the call that reaches it returns STDK_EHIP as if the launch
+ * had failed, with the work before it already enqueued. Fires once; -1
+ * disarms. STDK_EINVAL below -1. */
+int32_t stdk_inject_launch_failure(int32_t after_launches);
 
 /* Kernel timing: while enabled, every kernel the library enqueues (or only
  * the kernel family `only`, if not NULL) is launched with a pair of

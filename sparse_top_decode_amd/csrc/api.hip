@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -93,15 +94,85 @@ long prof_slot(int kid, hipEvent_t* e0, hipEvent_t* e1) {
   return (long)slot;
 }
 
+// Testing aid (stdk_inject_launch_failure): the launch with this number,
+// counted from the moment it is armed, is not enqueued and reports STDK_EHIP.
+std::atomic<int64_t> g_fail_at{-1};
+std::atomic<int64_t> g_launch_no{0};
+
 // f(e0, e1) enqueues one kernel with hipExtLaunchKernelGGL(..., e0, e1, 0, ...).
 template <typename F>
 int32_t launch(int kid, hipStream_t s, F&& f) {
   (void)s;
+  const int64_t at = g_fail_at.load();
+  if (at >= 0 && g_launch_no.fetch_add(1) == at) {
+    g_fail_at.store(-1);
+    return fail(STDK_EHIP, "%s launch failed: injected failure", kKernelNames[kid]);
+  }
   hipEvent_t e0, e1;
   prof_slot(kid, &e0, &e1);
   f(e0, e1);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(STDK_EHIP, "%s launch failed: %s", kKernelNames[kid], hipGetErrorString(e));
+  return STDK_OK;
+}
+
+// ---------------------------------------------------------------------------
+// workspaces left dirty by a failed call
+// ---------------------------------------------------------------------------
+// A call chain keeps the radix-histogram counters at the start of its
+// workspace zero between calls (the scan adds to them, the select clears
+// them). A chain that stops with STDK_EHIP after its scan was enqueued
+// leaves them non-zero; the workspace is recorded here with the extent of
+// its counter region, and the next call on it clears that region first.
+std::mutex g_dirty_mu;
+std::vector<std::pair<uintptr_t, size_t>> g_dirty;
+
+void mark_dirty(const void* ws, size_t bytes) {
+  if (!ws || bytes == 0) return;
+  std::lock_guard<std::mutex> lk(g_dirty_mu);
+  for (auto& d : g_dirty)
+    if (d.first == (uintptr_t)ws) {
+      d.second = std::max(d.second, bytes);
+      return;
+    }
+  g_dirty.emplace_back((uintptr_t)ws, bytes);
+}
+
+__global__ __launch_bounds__(256) void clear_words(uint32_t* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0u;
+}
+
+// Clears the counter region of `ws` if a failed call left it dirty.
+int32_t clean_if_dirty(void* ws, size_t ws_bytes, hipStream_t s) {
+  if (!ws) return STDK_OK;
+  size_t bytes = 0;
+  {
+    std::lock_guard<std::mutex> lk(g_dirty_mu);
+    if (g_dirty.empty()) return STDK_OK;
+    for (auto& d : g_dirty)
+      if (d.first == (uintptr_t)ws) bytes = d.second;
+  }
+  if (bytes == 0) return STDK_OK;
+  const int64_t n = (int64_t)(std::min(bytes, ws_bytes) / 4);
+  hipLaunchKernelGGL(clear_words, dim3((unsigned)std::min<int64_t>(1024, std::max<int64_t>(1, (n + 255) / 256))),
+                     dim3(256), 0, s, (uint32_t*)ws, n);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(STDK_EHIP, "clearing a dirty workspace: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lk(g_dirty_mu);
+  for (size_t i = 0; i < g_dirty.size(); ++i)
+    if (g_dirty[i].first == (uintptr_t)ws) {
+      g_dirty.erase(g_dirty.begin() + (long)i);
+      break;
+    }
+  return STDK_OK;
+}
+
+// The result of a call chain on workspace `ws` whose counter region is
+// `hist_bytes` long: a launch failure marks the workspace dirty.
+int32_t finish(int32_t rc, const void* ws, size_t hist_bytes) {
+  if (rc == STDK_EHIP) mark_dirty(ws, hist_bytes);
+  if (rc != STDK_OK) return rc;
+  g_err.clear();
   return STDK_OK;
 }
 
@@ -579,7 +650,9 @@ MqWs mq_ws(const Geo& g, int64_t M, int64_t n, int64_t K) {
   nchunk = std::min<int64_t>(nchunk, w.nblk);
   w.chunk = std::max<int64_t>(rup(cdiv(std::max<int64_t>(n, 1), nchunk), kMqBlock), rup(cdiv(std::max<int64_t>(n, 1), kMqMaxChunks), kMqBlock));
   w.nchunk = cdiv(std::max<int64_t>(n, 1), w.chunk);
-  size_t off = 0;
+  // the first B * H_q * 8 KiB are the decode calls' radix counters, which
+  // are zero between calls: left untouched, so one buffer may serve both
+  size_t off = al256((size_t)g.S * kHistBins * 4);
   w.bmax = off;
   off = al256(off + (size_t)w.S * w.ngrp * 4);
   w.thr = off;
@@ -904,13 +977,15 @@ int32_t topk_attn_decode(const stdk_layout* lay, const float* q, const void* k_c
     }));
     return ok();
   }
+  STDK_TRY(clean_if_dirty(ws, workspace_bytes, s));
+  int32_t rc;
   if (top_k >= n) {
-    STDK_TRY(run_dense(g, w, ws, q, k_cache, v_cache, tab, scale, top_k, idx_out, o_out, lse_out, s));
-    return ok();
+    rc = run_dense(g, w, ws, q, k_cache, v_cache, tab, scale, top_k, idx_out, o_out, lse_out, s);
+  } else {
+    rc = run_exact_select(g, w, ws, q, k_cache, tab, scale, nullptr, idx_out, di, s);
+    if (rc == STDK_OK) rc = run_sv(g, w, ws, v_cache, o_out, lse_out, s, &tab);
   }
-  STDK_TRY(run_exact_select(g, w, ws, q, k_cache, tab, scale, nullptr, idx_out, di, s));
-  STDK_TRY(run_sv(g, w, ws, v_cache, o_out, lse_out, s, &tab));
-  return ok();
+  return finish(rc, ws, w.hist_words * 4);
 }
 
 size_t topk_attn_decode_static_workspace_size(const stdk_layout* lay, int64_t n_scan, int64_t n_static,
@@ -949,9 +1024,10 @@ int32_t topk_attn_decode_static(const stdk_layout* lay, const float* q, const vo
   }
   DevInfo* di = nullptr;
   STDK_TRY(dev_info(&di));
-  STDK_TRY(run_static(g, sp, (char*)workspace, q, k_cache, v_cache, top_k, scale, idx_out, o_out, lse_out, di,
-                      (hipStream_t)stream));
-  return ok();
+  STDK_TRY(clean_if_dirty(workspace, workspace_bytes, (hipStream_t)stream));
+  const int32_t rc = run_static(g, sp, (char*)workspace, q, k_cache, v_cache, top_k, scale, idx_out, o_out, lse_out,
+                                di, (hipStream_t)stream);
+  return finish(rc, workspace, (size_t)g.S * kHistBins * 4);
 }
 
 size_t topk_multi_query_workspace_size(const stdk_layout* lay, int32_t n_queries, int64_t n_scan, int32_t top_k) {
@@ -1066,34 +1142,37 @@ int32_t topk_attn_decode_int8(const stdk_layout* lay, const float* q, const void
     STDK_TRY(dev_info(&di));
   }
   char* ws = (char*)workspace;
+  const size_t hb = (size_t)g.S * kHistBins * 4;
+  if (n > 0) STDK_TRY(clean_if_dirty(ws, workspace_bytes, s));
   if (n == 0 || recall_k >= n) {
     // the superset is every row: exact top-K attention (the superset output
     // lists every row)
     const TopkWs w = topk_ws(g.S, n, top_k);
+    int32_t rc = STDK_OK;
     if (n == 0) {
       const int64_t m = std::max<int64_t>(g.S * kHeadDim, g.S * (int64_t)top_k);
       STDK_TRY(launch(KID_FILL, s, [&](hipEvent_t e0, hipEvent_t e1) {
         STDK_LAUNCH(fill_empty, dim3((unsigned)cdiv(m, 256)), dim3(256), 0, s, o_out, lse_out, idx_out, g.S, top_k);
       }));
     } else if (top_k >= n) {
-      STDK_TRY(run_dense(g, w, ws, q, k_cache, v_cache, tab, scale, top_k, idx_out, o_out, lse_out, s));
+      rc = run_dense(g, w, ws, q, k_cache, v_cache, tab, scale, top_k, idx_out, o_out, lse_out, s);
     } else {
-      STDK_TRY(run_exact_select(g, w, ws, q, k_cache, tab, scale, nullptr, idx_out, di, s));
-      STDK_TRY(run_sv(g, w, ws, v_cache, o_out, lse_out, s, &tab));
+      rc = run_exact_select(g, w, ws, q, k_cache, tab, scale, nullptr, idx_out, di, s);
+      if (rc == STDK_OK) rc = run_sv(g, w, ws, v_cache, o_out, lse_out, s, &tab);
     }
-    if (sup_out) {
-      STDK_TRY(launch(KID_FILL, s, [&](hipEvent_t e0, hipEvent_t e1) {
+    if (rc == STDK_OK && sup_out) {
+      rc = launch(KID_FILL, s, [&](hipEvent_t e0, hipEvent_t e1) {
         STDK_LAUNCH(fill_rows, dim3((unsigned)cdiv(g.S * (int64_t)recall_k, 256)), dim3(256), 0, s, sup_out, g.S,
                     recall_k, tab);
-      }));
+      });
     }
-    return ok();
+    return finish(rc, ws, hb);
   }
   const Q8Ws w = q8_ws(g, n, top_k, recall_k);
   const Q8Keys keys{codes, scales, lay->max_len};
-  STDK_TRY(run_int8(g, w, ws, q, k_cache, v_cache, keys, tab, RangeTab{}, 0, top_k, recall_k, scale, idx_out, sup_out,
-                    o_out, lse_out, di, s));
-  return ok();
+  const int32_t rc = run_int8(g, w, ws, q, k_cache, v_cache, keys, tab, RangeTab{}, 0, top_k, recall_k, scale,
+                              idx_out, sup_out, o_out, lse_out, di, s);
+  return finish(rc, ws, hb);
 }
 
 size_t topk_attn_decode_int8_static_workspace_size(const stdk_layout* lay, int64_t n_scan, int64_t n_static,
@@ -1138,22 +1217,24 @@ int32_t topk_attn_decode_int8_static(const stdk_layout* lay, const float* q, con
     if (workspace_bytes < need) return fail(STDK_EWORKSPACE, "workspace is %zu bytes, %zu needed", workspace_bytes, need);
   }
   STDK_TRY(dev_info(&di));
+  const size_t hb = (size_t)g.S * kHistBins * 4;
+  STDK_TRY(clean_if_dirty(ws, workspace_bytes, s));
   if (recall_k >= sp.n_dyn) {
     // the superset is every dynamic row: topk_attn_decode_static's result
-    STDK_TRY(run_static(g, sp, ws, q, k_cache, v_cache, top_k, scale, idx_out, o_out, lse_out, di, s));
-    if (sup_out) {
-      STDK_TRY(launch(KID_FILL, s, [&](hipEvent_t e0, hipEvent_t e1) {
+    int32_t rc = run_static(g, sp, ws, q, k_cache, v_cache, top_k, scale, idx_out, o_out, lse_out, di, s);
+    if (rc == STDK_OK && sup_out) {
+      rc = launch(KID_FILL, s, [&](hipEvent_t e0, hipEvent_t e1) {
         STDK_LAUNCH(fill_rows, dim3((unsigned)cdiv(g.S * (int64_t)recall_k, 256)), dim3(256), 0, s, sup_out, g.S,
                     recall_k, sp.dyn);
-      }));
+      });
     }
-    return ok();
+    return finish(rc, ws, hb);
   }
   const Q8Ws w = q8_ws(g, sp.n_dyn, top_k, recall_k, sp.n_st);
   const Q8Keys keys{codes, scales, lay->max_len};
-  STDK_TRY(run_int8(g, w, ws, q, k_cache, v_cache, keys, sp.dyn, sp.st, sp.n_st, top_k, recall_k, scale, idx_out,
-                    sup_out, o_out, lse_out, di, s));
-  return ok();
+  const int32_t rc = run_int8(g, w, ws, q, k_cache, v_cache, keys, sp.dyn, sp.st, sp.n_st, top_k, recall_k, scale,
+                              idx_out, sup_out, o_out, lse_out, di, s);
+  return finish(rc, ws, hb);
 }
 
 int32_t attn_merge_lse(int64_t rows, int32_t d, const float* o_a, const float* lse_a, const float* o_b,
@@ -1242,6 +1323,19 @@ RetopkWs retopk_ws(const Geo& g, const retopk_params* p, int64_t L) {
 
 }  // namespace
 
+size_t retopk_state_size(const stdk_layout* lay, const retopk_params* p) {
+  if (check_layout(lay) != STDK_OK || !p || p->top_k < 1 || p->cache_cap < 1) return 0;
+  const size_t S = (size_t)geo_of(lay).S, C = (size_t)p->cache_cap, K = (size_t)p->top_k;
+  return al256(S * C * kHeadDim * 4) + al256(S * C * K * 4) + al256(S * 4) + al256(S * 4);
+}
+
+int32_t stdk_inject_launch_failure(int32_t after_launches) {
+  if (after_launches < -1) return fail(STDK_EINVAL, "after_launches %d < -1", after_launches);
+  g_launch_no.store(0);
+  g_fail_at.store(after_launches);
+  return ok();
+}
+
 size_t retopk_workspace_size(const stdk_layout* lay, const retopk_params* p, int64_t max_L_t) {
   if (check_layout(lay) != STDK_OK || !p || p->top_k < 1 || p->top_r < 1 || p->recent < 0 || max_L_t < 1) return 0;
   return retopk_ws(geo_of(lay), p, max_L_t).total;
@@ -1285,115 +1379,118 @@ int32_t retopk_step(const stdk_layout* lay, const retopk_params* p, const retopk
   DevInfo* di = nullptr;
   STDK_TRY(dev_info(&di));
   char* ws = (char*)workspace;
-  const bool refresh_now = p->refresh > 0 && (t % p->refresh) == 0;
-  int32_t* exact = (int32_t*)(ws + w.exact);
+  STDK_TRY(clean_if_dirty(ws, workspace_bytes, s));
+  const int32_t rc = [&]() -> int32_t {
+    const bool refresh_now = p->refresh > 0 && (t % p->refresh) == 0;
+    int32_t* exact = (int32_t*)(ws + w.exact);
 
-  // a6: selector (cosine, path, top-R, candidate union)
-  {
-    RtSelArgs a{};
-    a.q = q;
-    a.q_hat = st->q_hat;
-    a.support = st->support;
-    a.head = st->head;
-    a.count = st->count;
-    a.C = p->cache_cap;
-    a.K = p->top_k;
-    a.R = p->top_r;
-    a.W = p->recent;
-    a.tau = p->tau;
-    a.refresh_now = refresh_now ? 1 : 0;
-    a.L_t = L_t;
-    a.cand_cap = (int32_t)w.cand_cap;
-    a.bitmap_words = (int32_t)w.words;
-    a.qbar = (float*)(ws + w.qbar);
-    a.path = (int32_t*)(ws + w.path);
-    a.exact = exact;
-    a.cand = (int32_t*)(ws + w.cand);
-    a.n_cand = (int32_t*)(ws + w.n_cand);
-    a.path_out = path_out;
-    a.n_cand_out = n_cand_out;
-    a.cand_out = cand_out;
-    a.gbitmap = (uint32_t*)(ws + w.gbitmap);
-    if (p->budget > 0) {
-      a.rec_slot = (int32_t*)(ws + w.rec_slot);
-      a.rec_rho = (float*)(ws + w.rec_rho);
+    // a6: selector (cosine, path, top-R, candidate union)
+    {
+      RtSelArgs a{};
+      a.q = q;
+      a.q_hat = st->q_hat;
+      a.support = st->support;
+      a.head = st->head;
+      a.count = st->count;
+      a.C = p->cache_cap;
+      a.K = p->top_k;
+      a.R = p->top_r;
+      a.W = p->recent;
+      a.tau = p->tau;
+      a.refresh_now = refresh_now ? 1 : 0;
+      a.L_t = L_t;
+      a.cand_cap = (int32_t)w.cand_cap;
+      a.bitmap_words = (int32_t)w.words;
+      a.qbar = (float*)(ws + w.qbar);
+      a.path = (int32_t*)(ws + w.path);
+      a.exact = exact;
+      a.cand = (int32_t*)(ws + w.cand);
+      a.n_cand = (int32_t*)(ws + w.n_cand);
+      a.path_out = path_out;
+      a.n_cand_out = n_cand_out;
+      a.cand_out = cand_out;
+      a.gbitmap = (uint32_t*)(ws + w.gbitmap);
+      if (p->budget > 0) {
+        a.rec_slot = (int32_t*)(ws + w.rec_slot);
+        a.rec_rho = (float*)(ws + w.rec_rho);
+      }
+      const size_t bm_bytes = (size_t)w.words * 4;
+      const bool lds = bm_bytes + 12 * 1024 <= (size_t)di->max_lds;
+      STDK_TRY(launch(KID_RT_SELECT, s, [&](hipEvent_t e0, hipEvent_t e1) {
+        if (lds) STDK_LAUNCH(retopk_select<true>, dim3((unsigned)g.S), dim3(kRtSelThreads), bm_bytes, s, a);
+        else STDK_LAUNCH(retopk_select<false>, dim3((unsigned)g.S), dim3(kRtSelThreads), 0, s, a);
+      }));
     }
-    const size_t bm_bytes = (size_t)w.words * 4;
-    const bool lds = bm_bytes + 12 * 1024 <= (size_t)di->max_lds;
-    STDK_TRY(launch(KID_RT_SELECT, s, [&](hipEvent_t e0, hipEvent_t e1) {
-      if (lds) STDK_LAUNCH(retopk_select<true>, dim3((unsigned)g.S), dim3(kRtSelThreads), bm_bytes, s, a);
-      else STDK_LAUNCH(retopk_select<false>, dim3((unsigned)g.S), dim3(kRtSelThreads), 0, s, a);
-    }));
-  }
-  // confidence vote: cap the candidates of the reuse heads
-  if (p->budget > 0 && !refresh_now) {
-    RtVoteArgs a{};
-    a.exact = exact;
-    a.support = st->support;
-    a.count = st->count;
-    a.rec_slot = (const int32_t*)(ws + w.rec_slot);
-    a.rec_rho = (const float*)(ws + w.rec_rho);
-    a.cand = (int32_t*)(ws + w.cand);
-    a.n_cand = (int32_t*)(ws + w.n_cand);
-    a.n_cand_out = n_cand_out;
-    a.cand_out = cand_out;
-    a.L_t = L_t;
-    a.C = p->cache_cap;
-    a.K = p->top_k;
-    a.R = p->top_r;
-    a.W = p->recent;
-    a.cand_cap = (int32_t)w.cand_cap;
-    a.budget = p->budget;
-    // candidates and their masks, then (when they fit) the masks of every
-    // row below the recent window
-    const size_t base = (size_t)w.cand_cap * 4 + (((size_t)w.cand_cap + 15) & ~(size_t)15);
-    const size_t with_rows = base + (size_t)rup(std::max<int64_t>(L_t, 1), 4);
-    const bool row_masks = with_rows + 4 * 1024 <= (size_t)di->max_lds;
-    const size_t dyn = row_masks ? with_rows : base + 16;
-    STDK_TRY(launch(KID_RT_VOTE, s, [&](hipEvent_t e0, hipEvent_t e1) {
-      if (row_masks) STDK_LAUNCH(retopk_vote<true>, dim3((unsigned)g.S), dim3(kVoteThreads), dyn, s, a);
-      else STDK_LAUNCH(retopk_vote<false>, dim3((unsigned)g.S), dim3(kVoteThreads), dyn, s, a);
-    }));
-  }
-  // exact heads: scan + select + softmax.V over [0, L_t)
-  const int64_t rng[2] = {0, L_t};
-  int64_t n_all = 0;
-  const RangeTab tab = make_tab(rng, 1, &n_all);
-  const int32_t* active = refresh_now ? nullptr : exact;
-  STDK_TRY(run_exact_select(g, w.t, ws, q, k_cache, tab, p->scale, active, support_out, di, s));
-  // reuse heads: indexed QK over the candidates, rerank, softmax.V
-  if (!refresh_now) {
-    RtRerankArgs a{};
-    a.q = q;
-    a.k = (const char*)k_cache;
-    a.stride_b_bytes = g.sb_bytes;
-    a.stride_h_bytes = g.sh_bytes;
-    a.exact = exact;
-    a.cand = (const int32_t*)(ws + w.cand);
-    a.n_cand = (const int32_t*)(ws + w.n_cand);
-    a.cz = (float*)(ws + w.cz);
-    a.sel_row = (int32_t*)(ws + w.t.sel_row);
-    a.sel_z = (float*)(ws + w.t.sel_z);
-    a.support_out = support_out;
-    a.cand_cap = (int32_t)w.cand_cap;
-    a.K = p->top_k;
-    a.Hq = g.Hq;
-    a.G = g.G;
-    a.nsplit = (int32_t)cdiv(w.cand_cap, kRerankRows);
-    a.scale = p->scale;
-    const dim3 grid((unsigned)a.nsplit, (unsigned)g.S);
-    STDK_TRY(launch(KID_RT_RERANK, s, [&](hipEvent_t e0, hipEvent_t e1) {
-      if (g.bf16) STDK_LAUNCH(retopk_rerank<uint16_t>, grid, dim3(kRerankThreads), 0, s, a);
-      else STDK_LAUNCH(retopk_rerank<float>, grid, dim3(kRerankThreads), 0, s, a);
-    }));
-    STDK_TRY(run_rerank_select(a, g.S, di, s));
-  }
-  // a8: softmax . V over the chosen rows of every head (either path), and
-  // the push of (q_bar, support) by one workgroup per head of that launch
-  const SvPush push{(const float*)(ws + w.qbar), support_out, st->q_hat, st->support, st->head, st->count,
-                    p->cache_cap, p->top_k};
-  STDK_TRY(run_sv(g, w.t, ws, v_cache, o_out, lse_out, s, nullptr, &push));
-  return ok();
+    // confidence vote: cap the candidates of the reuse heads
+    if (p->budget > 0 && !refresh_now) {
+      RtVoteArgs a{};
+      a.exact = exact;
+      a.support = st->support;
+      a.count = st->count;
+      a.rec_slot = (const int32_t*)(ws + w.rec_slot);
+      a.rec_rho = (const float*)(ws + w.rec_rho);
+      a.cand = (int32_t*)(ws + w.cand);
+      a.n_cand = (int32_t*)(ws + w.n_cand);
+      a.n_cand_out = n_cand_out;
+      a.cand_out = cand_out;
+      a.L_t = L_t;
+      a.C = p->cache_cap;
+      a.K = p->top_k;
+      a.R = p->top_r;
+      a.W = p->recent;
+      a.cand_cap = (int32_t)w.cand_cap;
+      a.budget = p->budget;
+      // candidates and their masks, then (when they fit) the masks of every
+      // row below the recent window
+      const size_t base = (size_t)w.cand_cap * 4 + (((size_t)w.cand_cap + 15) & ~(size_t)15);
+      const size_t with_rows = base + (size_t)rup(std::max<int64_t>(L_t, 1), 4);
+      const bool row_masks = with_rows + 4 * 1024 <= (size_t)di->max_lds;
+      const size_t dyn = row_masks ? with_rows : base + 16;
+      STDK_TRY(launch(KID_RT_VOTE, s, [&](hipEvent_t e0, hipEvent_t e1) {
+        if (row_masks) STDK_LAUNCH(retopk_vote<true>, dim3((unsigned)g.S), dim3(kVoteThreads), dyn, s, a);
+        else STDK_LAUNCH(retopk_vote<false>, dim3((unsigned)g.S), dim3(kVoteThreads), dyn, s, a);
+      }));
+    }
+    // exact heads: scan + select + softmax.V over [0, L_t)
+    const int64_t rng[2] = {0, L_t};
+    int64_t n_all = 0;
+    const RangeTab tab = make_tab(rng, 1, &n_all);
+    const int32_t* active = refresh_now ? nullptr : exact;
+    STDK_TRY(run_exact_select(g, w.t, ws, q, k_cache, tab, p->scale, active, support_out, di, s));
+    // reuse heads: indexed QK over the candidates, rerank, softmax.V
+    if (!refresh_now) {
+      RtRerankArgs a{};
+      a.q = q;
+      a.k = (const char*)k_cache;
+      a.stride_b_bytes = g.sb_bytes;
+      a.stride_h_bytes = g.sh_bytes;
+      a.exact = exact;
+      a.cand = (const int32_t*)(ws + w.cand);
+      a.n_cand = (const int32_t*)(ws + w.n_cand);
+      a.cz = (float*)(ws + w.cz);
+      a.sel_row = (int32_t*)(ws + w.t.sel_row);
+      a.sel_z = (float*)(ws + w.t.sel_z);
+      a.support_out = support_out;
+      a.cand_cap = (int32_t)w.cand_cap;
+      a.K = p->top_k;
+      a.Hq = g.Hq;
+      a.G = g.G;
+      a.nsplit = (int32_t)cdiv(w.cand_cap, kRerankRows);
+      a.scale = p->scale;
+      const dim3 grid((unsigned)a.nsplit, (unsigned)g.S);
+      STDK_TRY(launch(KID_RT_RERANK, s, [&](hipEvent_t e0, hipEvent_t e1) {
+        if (g.bf16) STDK_LAUNCH(retopk_rerank<uint16_t>, grid, dim3(kRerankThreads), 0, s, a);
+        else STDK_LAUNCH(retopk_rerank<float>, grid, dim3(kRerankThreads), 0, s, a);
+      }));
+      STDK_TRY(run_rerank_select(a, g.S, di, s));
+    }
+    // a8: softmax . V over the chosen rows of every head (either path), and
+    // the push of (q_bar, support) by one workgroup per head of that launch
+    const SvPush push{(const float*)(ws + w.qbar), support_out, st->q_hat, st->support, st->head, st->count,
+                      p->cache_cap, p->top_k};
+    return run_sv(g, w.t, ws, v_cache, o_out, lse_out, s, nullptr, &push);
+  }();
+  return finish(rc, ws, w.t.hist_words * 4);
 }
 
 // ---------------------------------------------------------------------------

@@ -42,38 +42,37 @@ STDK_DEV void combine_partials(const float* part, int np, float* o_out, float* l
   __syncthreads();
   M = fmaxf(red[0], red[1]);
   __syncthreads();
-  // weights e^{m_i - M}; the sums run in partial order
+  // weights e^{m_i - M} (0 for an empty partial); the sums run in partial
+  // order. A NaN score reaches S and O through its partial and propagates.
   for (int i = j; i < np; i += kHeadDim) sm[i] = (sm[i] == -INFINITY) ? 0.f : __expf(sm[i] - M);
   __syncthreads();
   float S = 0.f, O = 0.f;
-  if (M != -INFINITY) {
+#pragma unroll
+  for (int i = 0; i < PB; ++i) {
+    if (i < np) {
+      const float f = sm[i];
+      S = fmaf(sf[i], f, S);
+      O = fmaf(ov[i], f, O);
+    }
+  }
+  for (int i0 = PB; i0 < np; i0 += PB) {
+#pragma unroll
+    for (int i = 0; i < PB; ++i) ov[i] = part[(int64_t)min(i0 + i, np - 1) * kPartStride + 4 + j];
 #pragma unroll
     for (int i = 0; i < PB; ++i) {
-      if (i < np) {
-        const float f = sm[i];
-        S = fmaf(sf[i], f, S);
+      if (i0 + i < np) {
+        const float f = sm[i0 + i];
+        S = fmaf(sf[i0 + i], f, S);
         O = fmaf(ov[i], f, O);
       }
     }
-    for (int i0 = PB; i0 < np; i0 += PB) {
-#pragma unroll
-      for (int i = 0; i < PB; ++i) ov[i] = part[(int64_t)min(i0 + i, np - 1) * kPartStride + 4 + j];
-#pragma unroll
-      for (int i = 0; i < PB; ++i) {
-        if (i0 + i < np) {
-          const float f = sm[i0 + i];
-          S = fmaf(sf[i0 + i], f, S);
-          O = fmaf(ov[i], f, O);
-        }
-      }
-    }
   }
-  if (S > 0.f) {
-    o_out[j] = O / S;
-    if (j == 0) *lse_out = M + __logf(S);
-  } else {
+  if (S == 0.f) {  // no row: o = 0, lse = -inf
     o_out[j] = 0.f;
     if (j == 0) *lse_out = -INFINITY;
+  } else {
+    o_out[j] = O / S;
+    if (j == 0) *lse_out = M + __logf(S);
   }
 }
 

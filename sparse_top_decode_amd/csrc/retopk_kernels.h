@@ -709,11 +709,12 @@ __global__ __launch_bounds__(kRerankSelThreads) void retopk_rerank_select_lds(Rt
   }
   __syncthreads();
 
-  // radix passes over a window of keys [lo, lo + 2048 << sh): the first
-  // spans the candidates' own key range, each later one the bin that holds
-  // the K-th key, 11 bits finer; stop at single keys (sh = 0) or once that
-  // bin is taken whole. The threshold Tk is then the bin's smallest key and
-  // `need` the number of keys equal to it to take.
+  // radix passes over a window of keys [lo, lo + width): the first spans
+  // the candidates' own key range, each later one exactly the bin that
+  // holds the K-th key (keys above it were counted in `beyond` already and
+  // must not be counted again), in 2048 bins of 1 << sh keys; stop at single
+  // keys (sh = 0) or once that bin is taken whole. The threshold Tk is then
+  // the bin's smallest key and `need` the number of keys equal to it to take.
   uint32_t Tk = 0u, need = (uint32_t)K;
   if (!take_all) {
     uint32_t kmin = 0xffffffffu, kmax = 0u;
@@ -741,16 +742,14 @@ __global__ __launch_bounds__(kRerankSelThreads) void retopk_rerank_select_lds(Rt
     uint32_t lo = kmin;
     const uint32_t span = kmax - kmin;
     int sh = span < 2048u ? 0 : (32 - __clz((int)span)) - 11;
+    uint64_t width = 2048ull << sh;  // covers [kmin, kmax]
     // at most three passes: sh <= 21 and drops by 11 (to 0) each time
     for (;;) {
       for (int i = tid; i < 2048; i += NT) h[i] = 0u;
       __syncthreads();
       for (uint32_t j = tid; j < M; j += NT) {
         const uint32_t kv = f2key(zs[j]);
-        if (kv >= lo) {
-          const uint32_t d = (kv - lo) >> sh;
-          if (d < 2048u) atomicAdd(&h[d], 1u);
-        }
+        if (kv >= lo && (uint64_t)(kv - lo) < width) atomicAdd(&h[(kv - lo) >> sh], 1u);
       }
       __syncthreads();
       if (w == 0) find_bin_wave<2048, true>(h, need, &s_bin, &s_beyond);
@@ -758,6 +757,7 @@ __global__ __launch_bounds__(kRerankSelThreads) void retopk_rerank_select_lds(Rt
       const int bin = s_bin < 0 ? 0 : s_bin;
       need -= s_beyond;
       lo += (uint32_t)bin << sh;
+      width = 1ull << sh;
       if (sh == 0 || h[bin] == need) break;
       sh = sh > 11 ? sh - 11 : 0;
       __syncthreads();

@@ -564,7 +564,7 @@ __global__ __launch_bounds__(kSvThreads) void sparse_sv(SvArgs a) {
 #pragma unroll
     for (int i = 0; i < PL; ++i) {
       rows[64 * i + lane] = r[i];
-      wts[64 * i + lane] = (m == -INFINITY || z[i] == -INFINITY) ? 0.f : __expf(z[i] - m);
+      wts[64 * i + lane] = z[i] == -INFINITY ? 0.f : __expf(z[i] - m);  // a NaN score propagates
     }
     if (lane == 0) s_m = m;
   }
@@ -711,7 +711,7 @@ __global__ __launch_bounds__(kDsThreads) void sparse_sv_ds(SvArgs a) {
   float m = wmax[0];
 #pragma unroll
   for (int v = 1; v < NW; ++v) m = fmaxf(m, wmax[v]);
-  auto weight = [&](float z) { return (m == -INFINITY || z == -INFINITY) ? 0.f : __expf(z - m); };
+  auto weight = [&](float z) { return z == -INFINITY ? 0.f : __expf(z - m); };  // a NaN score propagates
 
   // 2. the slice of every value row, U rows per thread in flight; the first
   // batch is requested before the weight sum is formed
@@ -770,8 +770,9 @@ __global__ __launch_bounds__(kDsThreads) void sparse_sv_ds(SvArgs a) {
     float o = 0.f;
 #pragma unroll
     for (int g = 0; g < NP; ++g) o += red2[g][tid];
-    a.o_out[seg * kHeadDim + slice * kDsDims + tid] = ssum > 0.f ? o / ssum : 0.f;
-    if (slice == 0 && tid == 0) a.lse_out[seg] = ssum > 0.f ? m + __logf(ssum) : -INFINITY;
+    // ssum == 0: no row (o = 0, lse = -inf); a NaN sum propagates
+    a.o_out[seg * kHeadDim + slice * kDsDims + tid] = ssum == 0.f ? 0.f : o / ssum;
+    if (slice == 0 && tid == 0) a.lse_out[seg] = ssum == 0.f ? -INFINITY : m + __logf(ssum);
   }
   if (pusher && tid == 0) {
     a.push.head[seg] = push_slot;
@@ -845,7 +846,7 @@ __global__ __launch_bounds__(kSvThreads) void sparse_sv_scored(SvArgs a) {
   float ps = 0.f;  // the weights of the slots, counted once (lane 0 of each row group)
 #pragma unroll
   for (int u = 0; u < RU; ++u) {
-    const float wt = (m == -INFINITY || z[u] == -INFINITY) ? 0.f : __expf(z[u] - m);
+    const float wt = z[u] == -INFINITY ? 0.f : __expf(z[u] - m);
     float x[EPL];
     unpack16<T>(rr[u] >= 0 ? vw[u] : u32x4{0u, 0u, 0u, 0u}, x);
 #pragma unroll

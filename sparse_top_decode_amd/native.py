@@ -26,11 +26,11 @@ STDK_MAX_RANGES = 16
 EXPORTS = [
     "topk_attn_decode", "topk_attn_decode_workspace_size", "attn_merge_lse",
     "topk_attn_decode_static", "topk_attn_decode_static_workspace_size",
-    "retopk_state_init", "retopk_step", "retopk_workspace_size",
+    "retopk_state_init", "retopk_step", "retopk_workspace_size", "retopk_state_size",
     "topk_multi_query", "topk_multi_query_workspace_size",
     "quantize_keys_int8", "topk_attn_decode_int8", "topk_attn_decode_int8_workspace_size",
     "topk_attn_decode_int8_static", "topk_attn_decode_int8_static_workspace_size",
-    "stdk_last_error", "stdk_version",
+    "stdk_last_error", "stdk_version", "stdk_inject_launch_failure",
     "stdk_profile_enable", "stdk_profile_disable", "stdk_profile_reset", "stdk_profile_read",
 ]
 
@@ -92,6 +92,10 @@ def _sig(lib):
     lib.topk_attn_decode_int8_static_workspace_size.restype = c_size_t
     lib.retopk_workspace_size.argtypes = [POINTER(Layout), POINTER(RetopkParams), c_int64]
     lib.retopk_workspace_size.restype = c_size_t
+    lib.retopk_state_size.argtypes = [POINTER(Layout), POINTER(RetopkParams)]
+    lib.retopk_state_size.restype = c_size_t
+    lib.stdk_inject_launch_failure.argtypes = [c_int32]
+    lib.stdk_inject_launch_failure.restype = c_int32
     lib.stdk_last_error.argtypes = []
     lib.stdk_last_error.restype = c_char_p
     lib.stdk_version.argtypes = []

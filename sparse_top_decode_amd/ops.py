@@ -174,10 +174,24 @@ class Retopk:
         self.params = RetopkParams(top_k, cache_cap, top_r, recent, float(tau), refresh,
                                    float(1.0 / math.sqrt(d) if scale is None else scale), int(budget))
         dev = k_cache.device
-        self.q_hat = torch.zeros((B, n_q_heads, cache_cap, d), dtype=torch.float32, device=dev)
-        self.support = torch.full((B, n_q_heads, cache_cap, top_k), -1, dtype=torch.int32, device=dev)
-        self.head = torch.full((B, n_q_heads), cache_cap - 1, dtype=torch.int32, device=dev)
-        self.count = torch.zeros((B, n_q_heads), dtype=torch.int32, device=dev)
+        # one allocation of retopk_state_size bytes, carved at the offsets
+        # stdk.h documents for it
+        S, C = B * n_q_heads, cache_cap
+        nbytes = int(load().retopk_state_size(ctypes.byref(self.layout), ctypes.byref(self.params)))
+        if nbytes == 0:
+            raise ValueError("invalid ReTopK parameters")
+        self.state_buffer = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+        al = lambda x: (x + 255) // 256 * 256
+        o_sup = al(S * C * d * 4)
+        o_head = o_sup + al(S * C * top_k * 4)
+        o_cnt = o_head + al(S * 4)
+        buf = self.state_buffer
+        self.q_hat = buf[:S * C * d * 4].view(torch.float32).view(B, n_q_heads, C, d)
+        self.support = buf[o_sup:o_sup + S * C * top_k * 4].view(torch.int32).view(B, n_q_heads, C, top_k)
+        self.head = buf[o_head:o_head + S * 4].view(torch.int32).view(B, n_q_heads)
+        self.count = buf[o_cnt:o_cnt + S * 4].view(torch.int32).view(B, n_q_heads)
+        self.support.fill_(-1)
+        self.head.fill_(cache_cap - 1)
         self.state = RetopkState(self.q_hat.data_ptr(), self.support.data_ptr(), self.head.data_ptr(),
                                  self.count.data_ptr())
         self.cand_cap = top_r * top_k + recent
@@ -215,6 +229,12 @@ class Retopk:
                                 self.workspace.data_ptr(), self.workspace.numel(), _stream())
         check(rc)
         return out
+
+
+def inject_launch_failure(after_launches: int):
+    """Testing aid: the library launch numbered ``after_launches`` from now is
+    not enqueued and its call fails with STDK_EHIP (-1 disarms)."""
+    check(load().stdk_inject_launch_failure(int(after_launches)))
 
 
 class KernelTimer:

@@ -11,7 +11,9 @@ Acceptance (fixed before any kernel was written):
 
 from __future__ import annotations
 
+import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
@@ -87,12 +89,28 @@ def oracle_head(w, b: int, h: int, ranges, K: int, q=None):
     return ref.attend_rows(qv, w.k[b, h // G], w.v[b, h // G], rows, K, w.scale), rows
 
 
+# Oracle work over many heads runs in a thread pool (numpy releases the GIL
+# inside its array loops); the GPU box gives one GPU 16 host threads.
+ORACLE_THREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+def pmap(fn, items, threads: int = ORACLE_THREADS):
+    """[fn(x) for x in items], evaluated in a thread pool, in order."""
+    items = list(items)
+    if threads <= 1 or len(items) <= 1:
+        return [fn(x) for x in items]
+    with ThreadPoolExecutor(min(threads, len(items))) as ex:
+        return list(ex.map(fn, items))
+
+
 def check_heads(w, heads, idx, o, lse, ranges, K, fp32=False, q=None, label=""):
-    """Compares GPU outputs of the listed (b, h) heads with the oracle."""
+    """Compares GPU outputs of the listed (b, h) heads with the oracle (the
+    oracle's heads are computed in parallel threads, the checks in order)."""
     worst_o = worst_l = 0.0
     swaps = 0
-    for b, h in heads:
-        r, rows = oracle_head(w, b, h, ranges, K, q=q)
+    heads = list(heads)
+    results = pmap(lambda bh: oracle_head(w, bh[0], bh[1], ranges, K, q=q), heads)
+    for (b, h), (r, rows) in zip(heads, results):
         if idx is not None:
             swaps += check_index_set(idx[b, h], rows, r["z"], r["zk"], K)
         eo, el = check_out(o[b, h], lse[b, h], r["o"], r["lse"], fp32, f"{label} head ({b},{h})")

@@ -51,6 +51,25 @@ def test_workspace_size(lib):
     assert lib.retopk_workspace_size(ctypes.byref(lay(Hq=28, Hkv=4)), ctypes.byref(p), 65536) > 0
 
 
+def test_retopk_state_size(lib):
+    """One allocation for the four state arrays at the documented 256-byte
+    aligned offsets: q_hat, support, head, count."""
+    al = lambda x: (x + 255) // 256 * 256
+    for B, Hq, Hkv, C, K in [(1, 28, 4, 32, 512), (3, 32, 8, 5, 1100), (2, 4, 4, 1, 1)]:
+        p = RetopkParams(K, C, 1, 0, 0.85, 0, 0.088)
+        S = B * Hq
+        want = al(S * C * 128 * 4) + al(S * C * K * 4) + al(S * 4) + al(S * 4)
+        assert lib.retopk_state_size(ctypes.byref(lay(B=B, Hq=Hq, Hkv=Hkv)), ctypes.byref(p)) == want
+    bad = RetopkParams(0, 32, 4, 32, 0.85, 128, 0.088)
+    assert lib.retopk_state_size(ctypes.byref(lay(Hq=28, Hkv=4)), ctypes.byref(bad)) == 0
+    assert lib.retopk_state_size(ctypes.byref(lay(d=64)), ctypes.byref(RetopkParams(8, 2, 1, 0, 0.5, 0, 0.1))) == 0
+
+
+def test_inject_launch_failure_arguments(lib):
+    assert lib.stdk_inject_launch_failure(-2) == native.STDK_EINVAL
+    assert lib.stdk_inject_launch_failure(-1) == native.STDK_OK
+
+
 def call_topk(lib, L=None, ranges=((0, 100),), top_k=8, ws_bytes=1 << 30, q=FAKE, scale=0.1, idx=FAKE):
     L = L or lay()
     flat = [x for r in ranges for x in r]

@@ -51,9 +51,24 @@ def run_int8(ops, w, ranges, K, K2):
             o.cpu().numpy(), lse.cpu().numpy())
 
 
+def oracle_codes(w, codes, scales, rows, label):
+    """The oracle's codes and scales of every KV head's rows (zero outside
+    them), after checking that the GPU's equal them bit for bit; the int8
+    scores are then formed from the oracle's own codes, so no oracle input
+    comes from the GPU."""
+    want_c, want_s = ref.quantize_keys_int8(w.k[:, :, rows])
+    assert np.array_equal(codes[:, :, rows], want_c), f"{label}: int8 codes differ from the oracle's"
+    assert np.array_equal(scales[:, :, rows], want_s), f"{label}: row scales differ from the oracle's"
+    oc = np.zeros(codes.shape, np.int8)
+    osc = np.zeros(scales.shape, np.float32)
+    oc[:, :, rows], osc[:, :, rows] = want_c, want_s
+    return oc, osc
+
+
 def check_int8_heads(w, q, codes, scales, ranges, K, K2, idx, sup, o, lse, heads, label):
     G = w.H_q // w.H_kv
     rows = ref.range_rows(ranges)
+    codes, scales = oracle_codes(w, codes, scales, rows, label)
     recall = []
     for b, h in heads:
         hk = h // G
@@ -143,6 +158,7 @@ def check_int8_static_heads(w, q, codes, scales, ranges, static, K, K2, idx, sup
     G = w.H_q // w.H_kv
     rows = ref.range_rows(ranges)
     srows_static = ref.range_rows(static)
+    codes, scales = oracle_codes(w, codes, scales, rows, label)
     for b, h in heads:
         hk = h // G
         z8 = ref.int8_scores(q[b, h], codes[b, hk], scales[b, hk], rows, w.scale)
@@ -270,8 +286,52 @@ def test_int8_exact_ties_codebook(ops, K, K2):
     static = [(0, 100), (11800, 12000)]
     log(f"case int8 codebook ties K={K} K'={K2}")
     q, codes, scales, idx, sup, o, lse = run_int8_static(ops, w, ranges, static, K, K2)
+    codes, scales = oracle_codes(w, codes, scales, ref.range_rows(ranges), "codebook")
     want = ref.topk_attn_decode_int8(q, w.k, w.v, codes, scales, ranges, K, K2, w.scale)
     assert np.array_equal(sup, want["sup"]), "superset differs from the oracle's"
     assert np.array_equal(idx, want["idx"]), "chosen rows differ from the oracle's"
     check_int8_static_heads(w, q, codes, scales, ranges, static, K, K2, idx, sup, o, lse,
                             [(0, h) for h in range(4)], f"int8 ties K={K}")
+
+
+@pytest.mark.parametrize("K", [150, 333, 512, 599])
+def test_rerank_select_near_ties_exact(ops, K):
+    """The exact top-K inside a superset whose scores crowd into a few
+    thousand fp32 ulps above 1.0 (640 rows at 1.0 + u ulps, u < 4000, with
+    repeats) plus 60 negative rows that widen the key range: the radix
+    passes then narrow to 1024-key bins that hold many rows each, and the
+    last pass must count only the chosen bin (keys above it were counted
+    already). q = e_0, scale 1 and an fp32 cache make every score exactly
+    the row's first element on both sides, so the chosen rows (ties to the
+    lowest row) must equal the oracle's bit for bit. A window twice the bin
+    counted the next bin's rows twice and chose K - 1 rows here."""
+    rng = np.random.default_rng(77)
+    n, d = 700, 128
+    one = np.float32(1.0).view(np.uint32)
+    pos = (one + rng.integers(0, 4000, 640)).astype(np.uint32).view(np.float32)
+    neg = -rng.uniform(1, 5, 60).astype(np.float32)
+    x = np.empty(n, np.float32)
+    perm = rng.permutation(n)
+    x[perm[:640]], x[perm[640:]] = pos, neg
+    kc = np.zeros((1, 1, n, d), np.float32)
+    kc[0, 0, :, 0] = x
+    vc = rng.standard_normal((1, 1, n, d), dtype=np.float32)
+    q = np.zeros((1, 1, d), np.float32)
+    q[0, 0, 0] = 1.0
+    K2 = 650
+    log(f"case rerank select near ties K={K}")
+    k, v = torch.from_numpy(kc).cuda(), torch.from_numpy(vc).cuda()
+    codes, scales = ops.quantize_keys_int8(k, [(0, n)], 1)
+    idx, sup, o, lse = ops.topk_attn_decode_int8(torch.from_numpy(q).cuda(), k, v, codes, scales, [(0, n)], K, K2,
+                                                 1.0, want_sup=True)
+    torch.cuda.synchronize()
+
+    class W:  # the oracle's view of this input
+        pass
+    w = W()
+    w.k, w.v = kc, vc
+    oc, osc = oracle_codes(w, codes.cpu().numpy(), scales.cpu().numpy(), np.arange(n), "near ties")
+    want = ref.topk_attn_decode_int8(q, kc, vc, oc, osc, [(0, n)], K, K2, 1.0)
+    assert np.array_equal(sup.cpu().numpy(), want["sup"])
+    assert np.array_equal(idx.cpu().numpy(), want["idx"]), "chosen rows differ from the oracle's"
+    check_out(o.cpu().numpy()[0, 0], lse.cpu().numpy()[0, 0], want["o"][0, 0], want["lse"][0, 0], True, "near ties")

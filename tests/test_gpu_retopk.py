@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import BAND, check_index_set, check_out, dev_kv, log
+from gpu_util import BAND, check_index_set, check_out, dev_kv, log, pmap
 from oracle import reference as ref
 from workloads import make_workload
 
@@ -31,18 +31,37 @@ def host_state(rt):
 
 def warm_cache(ops, w, rt, k, v, n_warm, K):
     """The first n_warm queries go through the exact path over the initial
-    rows and fill the caches (oldest first)."""
+    rows and fill the caches (oldest first); n_warm = 0 leaves them empty."""
     L0 = w.retopk["L0"]
     qs = torch.from_numpy(np.ascontiguousarray(w.q[:, :, :n_warm])).cuda()
-    sups = []
-    for j in range(n_warm):
-        idx, _, _ = ops.topk_attn_decode(qs[:, :, j].contiguous(), k, v, [(0, L0)], K, w.scale,
-                                         layout=rt.layout)
-        sups.append(idx)
-    sup = torch.stack(sups, dim=2).contiguous()
+    if n_warm == 0:
+        sup = torch.zeros((w.q.shape[0], w.H_q, 0, K), dtype=torch.int32, device="cuda")
+    else:
+        sups = []
+        for j in range(n_warm):
+            idx, _, _ = ops.topk_attn_decode(qs[:, :, j].contiguous(), k, v, [(0, L0)], K, w.scale,
+                                             layout=rt.layout)
+            sups.append(idx)
+        sup = torch.stack(sups, dim=2).contiguous()
     rt.init(qs, sup)
     torch.cuda.synchronize()
     return qs.cpu().numpy(), sup.cpu().numpy()
+
+
+def oracle_step(p, before, qt, w, L_t, t, heads):
+    """The oracle's step for the listed heads from the pre-step state
+    `before`, one head per thread. Returns {(b, h): trace}; a trace's "new"
+    holds the head's state after the push."""
+    G = w.H_q // w.H_kv
+
+    def one(bh):
+        b, h = bh
+        return ref.retopk_head_step(p, before.q_hat[b, h], before.support[b, h], int(before.head[b, h]),
+                                    int(before.count[b, h]), qt[b, h], w.k[b, h // G], w.v[b, h // G], L_t, t,
+                                    w.scale)
+
+    heads = list(heads)
+    return dict(zip(heads, pmap(one, heads)))
 
 
 def run_lockstep(ops, w, p, n_steps, heads, n_warm, check_every=1):
@@ -57,8 +76,7 @@ def run_lockstep(ops, w, p, n_steps, heads, n_warm, check_every=1):
     assert np.array_equal(g0.support, st0.support)
     assert np.array_equal(g0.head, st0.head) and np.array_equal(g0.count, st0.count)
     assert np.max(np.abs(g0.q_hat - st0.q_hat)) < 1e-6
-    G = w.H_q // w.H_kv
-    stats = dict(reuse=0, exact=0, flagged=0, cand=[], swaps=0, capped=0)
+    stats = dict(reuse=0, exact=0, fallback=0, refresh=0, mixed_steps=0, flagged=0, cand=[], swaps=0, capped=0)
     for t in range(n_steps):
         L_t = L0 + t + 1
         qt = np.ascontiguousarray(w.q[:, :, n_warm + t])
@@ -70,7 +88,8 @@ def run_lockstep(ops, w, p, n_steps, heads, n_warm, check_every=1):
             continue
         g = {kk: vv.cpu().numpy() for kk, vv in out.items()}
         after = host_state(rt)
-        o_ref, st_ref, tr = ref.retopk_step(p, before, qt, w.k, w.v, L_t, t, w.scale, heads=heads)
+        tr = oracle_step(p, before, qt, w, L_t, t, heads)
+        paths_checked = set()
         for b, h in heads:
             r = tr[(b, h)]
             rs = r["rho_sorted"]
@@ -85,6 +104,11 @@ def run_lockstep(ops, w, p, n_steps, heads, n_warm, check_every=1):
                 stats["flagged"] += 1
                 continue
             assert int(g["path"][b, h]) == r["path"], (t, b, h, int(g["path"][b, h]), r["path"])
+            paths_checked.add(r["path"])
+            if r["path"] == 1:
+                stats["fallback"] += 1
+            elif r["path"] == 2:
+                stats["refresh"] += 1
             if r["path"] == 0:
                 stats["reuse"] += 1
                 M = r["cand"].shape[0]
@@ -102,8 +126,10 @@ def run_lockstep(ops, w, p, n_steps, heads, n_warm, check_every=1):
             slot = (int(before.head[b, h]) + 1) % C
             assert int(after.head[b, h]) == slot
             assert int(after.count[b, h]) == min(int(before.count[b, h]) + 1, C)
-            assert np.max(np.abs(after.q_hat[b, h, slot] - st_ref.q_hat[b, h, slot])) < 1e-6
+            assert np.max(np.abs(after.q_hat[b, h, slot] - r["new"][0][slot])) < 1e-6
             assert np.array_equal(after.support[b, h, slot], g["support"][b, h])
+        if 0 in paths_checked and 1 in paths_checked:
+            stats["mixed_steps"] += 1
     return stats
 
 
@@ -163,15 +189,122 @@ def test_retopk_serving_variants(ops, B, tau, K, L):
 @pytest.mark.slow
 def test_retopk_c3_full_lockstep(ops):
     """c3 at full size (L0 = 65536, K=512, C=32, R=4, W=32, tau=0.85,
-    T_r=128), all 256 steps, 4 sampled heads compared every step."""
+    T_r=128), all 256 steps, every one of the 28 heads compared every step."""
     w = make_workload(3)
     P = w.retopk
     p = ref.RetopkParams(top_k=P["top_k"], cache_cap=P["cache_cap"], top_r=P["top_r"], recent=P["recent"],
                          tau=P["tau"], refresh=P["refresh"])
-    heads = [(0, 0), (0, 9), (0, 18), (0, 27)]
+    heads = [(0, h) for h in range(w.H_q)]
     s = run_lockstep(ops, w, p, P["steps"], heads, n_warm=P["warmup"])
-    log(f"retopk c3 full: reuse {s['reuse']} exact {s['exact']} flagged {s['flagged']} "
-        f"mean M {np.mean(s['cand']) if s['cand'] else 0:.0f} (parity unpinned: context only) band swaps {s['swaps']}")
+    log(f"retopk c3 full: {len(heads)} heads x {P['steps']} steps: reuse {s['reuse']} fallback {s['fallback']} "
+        f"refresh {s['refresh']} flagged {s['flagged']} mean M {np.mean(s['cand']) if s['cand'] else 0:.0f} "
+        f"(parity unpinned: context only) band swaps {s['swaps']}")
+    assert s["reuse"] + s["exact"] + s["flagged"] == len(heads) * P["steps"]
+
+
+def test_retopk_fallback_mixed_with_reuse(ops):
+    """Similarity fallback (ReTopK review, 核心方法 5) on some heads while the
+    others reuse the cache in the same step: no periodic refresh, and tau at
+    the lag-1 cosine of the AR(1) queries (about 0.95), so about half of the
+    heads fall back at each step. The exact kernels then run on the fallback
+    heads only (per-head masks), the rerank on the others; every head is
+    compared with the oracle."""
+    w = make_workload(3, L=4096, steps=40, warm=8)
+    p = ref.RetopkParams(top_k=64, cache_cap=8, top_r=2, recent=16, tau=0.95, refresh=0)
+    heads = [(0, h) for h in range(28)]
+    s = run_lockstep(ops, w, p, 40, heads, n_warm=8)
+    log(f"retopk fallback mix: reuse {s['reuse']} fallback {s['fallback']} refresh {s['refresh']} "
+        f"steps with both paths checked {s['mixed_steps']} flagged {s['flagged']}")
+    assert s["refresh"] == 0
+    assert s["fallback"] > 0 and s["reuse"] > 0
+    assert s["mixed_steps"] >= 10
+
+
+def test_retopk_empty_cache_start(ops):
+    """retopk_state_init with no history: the first step falls back on every
+    head (count = 0), the cache then fills one entry per step; reuse and
+    fallback both occur afterwards (no refresh)."""
+    w = make_workload(3, L=4096, steps=24, warm=0)
+    p = ref.RetopkParams(top_k=64, cache_cap=8, top_r=2, recent=16, tau=0.9, refresh=0)
+    heads = [(0, h) for h in range(28)]
+    s = run_lockstep(ops, w, p, 24, heads, n_warm=0)
+    log(f"retopk empty start: reuse {s['reuse']} fallback {s['fallback']} flagged {s['flagged']}")
+    assert s["fallback"] >= 28 and s["reuse"] > 0
+
+
+def test_retopk_checkpoint_resume_bit_exact(ops):
+    """128 steps, the state (q_hat, support, head, count) copied to the host
+    and restored into a fresh state and workspace, 128 more steps: every
+    output of the resumed run equals the uninterrupted run's bit for bit."""
+    w = make_workload(3, L=16384, steps=256, warm=32)
+    P = w.retopk
+    kw = dict(top_k=256, cache_cap=32, top_r=4, recent=32, tau=0.85, refresh=64, scale=w.scale)
+    k, v = dev_kv(w)
+    L0 = P["L0"]
+    qs = torch.from_numpy(np.ascontiguousarray(w.q)).cuda()
+
+    def run(rt, t0, t1):
+        outs = []
+        for t in range(t0, t1):
+            o = rt.step(qs[:, :, 32 + t].contiguous(), k, v, L0 + t + 1, t, want_cand=True)
+            outs.append({kk: vv.clone() for kk, vv in o.items()})
+        return outs
+
+    rt = ops.Retopk(k, w.H_q, **kw)
+    warm_cache(ops, w, rt, k, v, 32, kw["top_k"])
+    whole = run(rt, 0, 256)
+    torch.cuda.synchronize()
+
+    rt1 = ops.Retopk(k, w.H_q, **kw)
+    warm_cache(ops, w, rt1, k, v, 32, kw["top_k"])
+    run(rt1, 0, 128)
+    torch.cuda.synchronize()
+    saved = {name: getattr(rt1, name).cpu().numpy().copy() for name in ("q_hat", "support", "head", "count")}
+    del rt1
+    rt2 = ops.Retopk(k, w.H_q, **kw)
+    for name, arr in saved.items():
+        getattr(rt2, name).copy_(torch.from_numpy(arr))
+    resumed = run(rt2, 128, 256)
+    torch.cuda.synchronize()
+    paths = set()
+    for i, o in enumerate(resumed):
+        ref_o = whole[128 + i]
+        for name in ("support", "o", "lse", "path", "n_cand", "cand"):
+            assert torch.equal(o[name], ref_o[name]), (128 + i, name)
+        paths |= set(np.unique(o["path"].cpu().numpy()).tolist())
+    for name in ("q_hat", "support", "head", "count"):
+        assert torch.equal(getattr(rt2, name), getattr(rt, name)), name
+    log(f"retopk resume: 128 resumed steps bit-exact, paths seen {sorted(paths)}")
+    assert 0 in paths and 2 in paths
+
+
+def test_retopk_nan_query_propagates(ops):
+    """A NaN in one head's query: the call succeeds, that head's o and lse are
+    not finite, and every other head's outputs and state equal those of the
+    same step without the NaN, bit for bit (heads never mix)."""
+    w = make_workload(3, L=4096, steps=4, warm=8)
+    p = dict(top_k=64, cache_cap=8, top_r=2, recent=16, tau=0.85, refresh=0, scale=w.scale)
+    k, v = dev_kv(w)
+    outs, states = [], []
+    for poison in (False, True):
+        rt = ops.Retopk(k, w.H_q, **p)
+        warm_cache(ops, w, rt, k, v, 8, 64)
+        res = []
+        for t in range(3):
+            q = np.ascontiguousarray(w.q[:, :, 8 + t]).copy()
+            if poison:
+                q[0, 5, 17] = np.nan
+            res.append(rt.step(torch.from_numpy(q).cuda(), k, v, 4096 + t + 1, t + 1))
+        torch.cuda.synchronize()
+        outs.append([{kk: vv.cpu().numpy() for kk, vv in r.items()} for r in res])
+        states.append({n: getattr(rt, n).cpu().numpy() for n in ("q_hat", "support", "head", "count")})
+    others = [h for h in range(w.H_q) if h != 5]
+    for clean, bad in zip(*outs):
+        assert not np.all(np.isfinite(bad["o"][0, 5])) and not np.isfinite(bad["lse"][0, 5])
+        for name in ("support", "o", "lse", "path", "n_cand"):
+            assert np.array_equal(clean[name][0, others], bad[name][0, others]), name
+    for name in ("q_hat", "support", "head", "count"):
+        assert np.array_equal(states[0][name][0, others], states[1][name][0, others]), name
 
 
 @pytest.mark.parametrize("budget", [100, 40])

@@ -182,12 +182,47 @@ def test_merge_kernel(ops):
     assert np.max(np.abs(ta.cpu().numpy() - want_o)) < 1e-5
 
 
-def test_deterministic(ops):
+def test_deterministic_repeats_and_grids(ops):
+    """Ten calls give bit-identical outputs; so does the same sequence inside a
+    batch of three, where the scan splits its rows over a different number
+    of workgroups per KV head (the results do not depend on the grid)."""
     w = make_workload(2, L=8192)
-    a = run(ops, w, w.ranges, 1000)
-    b = run(ops, w, w.ranges, 1000)
-    for x, y in zip(a, b):
-        assert np.array_equal(x, y)
+    first = run(ops, w, w.ranges, 1000)
+    for _ in range(9):
+        again = run(ops, w, w.ranges, 1000)
+        for x, y in zip(first, again):
+            assert np.array_equal(x, y)
+    q = torch.from_numpy(np.repeat(w.q, 3, axis=0)).cuda()
+    k, v = dev_kv(w)
+    k3, v3 = k.repeat(3, 1, 1, 1).contiguous(), v.repeat(3, 1, 1, 1).contiguous()
+    idx, o, lse = ops.topk_attn_decode(q, k3, v3, w.ranges, 1000, w.scale)
+    torch.cuda.synchronize()
+    for b in range(3):
+        for x, y in zip(first, (idx[b:b + 1].cpu().numpy(), o[b:b + 1].cpu().numpy(), lse[b:b + 1].cpu().numpy())):
+            assert np.array_equal(x, y), f"sequence {b} of the batch differs"
+
+
+@pytest.mark.parametrize("K", [500, 10000])
+def test_nan_query_propagates(ops, K):
+    """A NaN in one head's query makes every score of that head NaN: the call
+    returns STDK_OK, that head's o and lse are NaN, and every other head
+    (including the other heads of its KV group, which share the scan) equals
+    the clean call bit for bit. K = 10000 >= n takes the dense path."""
+    w = make_workload(2, L=8192 if K < 8192 else 7000)
+    clean = run(ops, w, w.ranges, K)
+    qn = w.q.copy()
+    qn[0, 5, 17] = np.nan
+    qt = torch.from_numpy(qn).cuda()
+    k, v = dev_kv(w)
+    idx, o, lse = ops.topk_attn_decode(qt, k, v, w.ranges, K, w.scale)
+    torch.cuda.synchronize()
+    idx, o, lse = idx.cpu().numpy(), o.cpu().numpy(), lse.cpu().numpy()
+    assert np.all(np.isnan(o[0, 5])) and np.isnan(lse[0, 5])
+    sel = idx[0, 5][idx[0, 5] >= 0]
+    assert sel.shape[0] == min(K, sum(e - b for b, e in w.ranges)) and np.all(np.diff(sel) > 0)
+    others = [h for h in range(w.H_q) if h != 5]
+    for x, y in zip(clean, (idx, o, lse)):
+        assert np.array_equal(x[0, others], y[0, others])
 
 
 def test_workspace_reuse_counters_return_to_zero(ops):
@@ -210,6 +245,76 @@ def test_workspace_reuse_counters_return_to_zero(ops):
         assert int(torch.count_nonzero(ws[:counters]).item()) == 0, f"counters left dirty after K={K}"
         for x, y in zip(got, fresh):
             assert torch.equal(x, y), f"reused workspace differs for K={K}"
+
+
+def test_workspace_shared_with_multi_query(ops):
+    """topk_multi_query leaves the decode calls' counter region alone: a
+    buffer used by it and then by topk_attn_decode gives the result of a
+    fresh zero-filled buffer, with the counters zero afterwards."""
+    w = make_workload(2, L=8192)
+    q = torch.from_numpy(w.q).cuda()
+    k, v = dev_kv(w)
+    lay = ops.make_layout(k, w.H_q)
+    n = sum(e - b for b, e in w.ranges)
+    qm = torch.from_numpy(np.random.default_rng(3).standard_normal((1, w.H_q, 3, 128), dtype=np.float32)).cuda()
+    size = max(ops.topk_attn_decode_workspace_size(lay, n, 500), ops.topk_multi_query_workspace_size(lay, 3, n, 500))
+    ws = ops.new_workspace(size, q.device)
+    ops.topk_multi_query(qm, k, w.ranges, 500, w.scale, workspace=ws, layout=lay)
+    got = ops.topk_attn_decode(q, k, v, w.ranges, 500, w.scale, workspace=ws, layout=lay)
+    fresh = ops.topk_attn_decode(q, k, v, w.ranges, 500, w.scale, layout=lay)
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(ws[:w.B * w.H_q * 8192]).item()) == 0
+    for x, y in zip(got, fresh):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("entry", ["topk", "static", "retopk"])
+def test_failed_call_leaves_workspace_usable(ops, entry):
+    """A launch failure forced from the host right after the scan (the
+    filter is never enqueued) leaves the workspace's counters non-zero; the
+    call returns STDK_EHIP, and the next call on the same buffer repairs them
+    first: its results equal those of a fresh buffer."""
+    from sparse_top_decode_amd.native import STDK_EHIP, StdkError
+    w = make_workload(2, L=8192)
+    q = torch.from_numpy(w.q).cuda()
+    k, v = dev_kv(w)
+    lay = ops.make_layout(k, w.H_q)
+    n = sum(e - b for b, e in w.ranges)
+    counters = w.B * w.H_q * 8192
+    if entry == "retopk":
+        rt = ops.Retopk(k, w.H_q, top_k=300, cache_cap=4, top_r=2, recent=8, tau=0.5, refresh=1, scale=w.scale)
+        ws = rt.workspace
+        first = 1  # retopk_select, then the scan
+        call = lambda: rt.step(q, k, v, 8192, 0)
+        fresh_rt = ops.Retopk(k, w.H_q, top_k=300, cache_cap=4, top_r=2, recent=8, tau=0.5, refresh=1, scale=w.scale)
+        fresh_call = lambda: fresh_rt.step(q, k, v, 8192, 0)
+    else:
+        size = (ops.topk_attn_decode_workspace_size(lay, n, 500) if entry == "topk" else
+                ops.topk_attn_decode_static_workspace_size(lay, n, 640, 500))
+        ws = ops.new_workspace(size, q.device)
+        first = 0
+        if entry == "topk":
+            call = lambda: ops.topk_attn_decode(q, k, v, w.ranges, 500, w.scale, workspace=ws, layout=lay)
+            fresh_call = lambda: ops.topk_attn_decode(q, k, v, w.ranges, 500, w.scale, layout=lay)
+        else:
+            call = lambda: ops.topk_attn_decode_static(q, k, v, w.ranges, w.static_ranges, 500, w.scale,
+                                                       workspace=ws, layout=lay)
+            fresh_call = lambda: ops.topk_attn_decode_static(q, k, v, w.ranges, w.static_ranges, 500, w.scale,
+                                                             layout=lay)
+    ops.inject_launch_failure(first + 1)
+    with pytest.raises(StdkError) as ei:
+        call()
+    assert ei.value.code == STDK_EHIP
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(ws[:counters]).item()) > 0, "the forced failure should leave counters set"
+    got = call()
+    want = fresh_call()
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(ws[:counters]).item()) == 0
+    for name in (got if isinstance(got, dict) else range(len(got))):
+        x, y = got[name], want[name]
+        if x is not None:
+            assert torch.equal(x, y), name
 
 
 @pytest.mark.parametrize("cfg,n_rows", [(2, 640), (2, 1280), (2, 1281), (2, 3000), (1, 640), (1, 641), (3, 300), (3, 900)])
