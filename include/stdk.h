@@ -155,6 +155,31 @@ size_t topk_attn_decode_static_workspace_size(const stdk_layout* lay, int64_t n_
                                               int64_t n_static, int32_t top_k);
 
 /* ------------------------------------------------------------------------
+ * topk_attn_decode_static_noalloc — topk_attn_decode_static for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation. Same arguments, results and
+ * errors, without the workspace: the scratch is one array of
+ * STDK_NOALLOC_SCRATCH_BYTES that the library holds per GPU until the
+ * process ends. The call allocates nothing (no hipMalloc, no allocating
+ * library routine).
+ *  - Calls whose workspace need (topk_attn_decode_static_workspace_size)
+ *    exceeds the array return STDK_EWORKSPACE before any launch. The
+ *    Llama-3-8B-shaped layer at 131,072 rows (32 query heads, K = 2048, 640
+ *    static rows) needs about 85 MB.
+ *  - Every call on one GPU uses that GPU's one array, which keeps the last
+ *    call's contents; each call clears the counters it needs first (a fill
+ *    kernel on `stream`). Calls that overlap on one GPU (other streams or
+ *    host threads) race on the array: the caller serialises them.
+ * ---------------------------------------------------------------------- */
+#define STDK_NOALLOC_SCRATCH_BYTES (96u << 20)
+
+int32_t topk_attn_decode_static_noalloc(const stdk_layout* lay, const float* q, const void* k_cache,
+                                        const void* v_cache, const int64_t* ranges, int32_t n_ranges,
+                                        const int64_t* static_ranges, int32_t n_static, int32_t top_k,
+                                        float scale, int32_t* idx_out, float* o_out, float* lse_out,
+                                        void* stream);
+
+/* ------------------------------------------------------------------------
  * topk_multi_query — the exact Top-K of [RT] ("Exact Top-K 的隐藏成本": TopK
  * over every score) for a block of queries per head at once: the supports
  * of the last prefill queries that start the ReTopK cache ([RT] 核心方法 1),

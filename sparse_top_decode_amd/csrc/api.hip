@@ -356,6 +356,20 @@ TopkWs topk_ws(int64_t S, int64_t n, int64_t K, int64_t n_extra = 0) {
   return w;
 }
 
+// Dense attention over n rows (K >= n) needs only its softmax.V partials;
+// they follow the counter region, which stays untouched (zero).
+TopkWs dense_ws(int64_t S, int64_t n) {
+  TopkWs w{};
+  w.S = S;
+  w.n = n;
+  w.n_pad = rup(std::max<int64_t>(n, 1), 64);
+  w.K = n;
+  w.hist_words = (size_t)S * kHistBins;
+  w.part = al256(w.hist_words * 4);
+  w.total = al256(w.part + (size_t)S * kDenseMaxWg * kPartStride * 4);
+  return w;
+}
+
 RangeTab make_tab(const int64_t* ranges, int n_ranges, int64_t* n_total) {
   RangeTab t{};
   t.n = n_ranges;
@@ -833,12 +847,63 @@ int32_t run_static(const Geo& g, const StaticSplit& sp, char* ws, const float* q
   if (top_k >= sp.n_dyn) {
     // every dynamic row is chosen: dense attention over the union; idx_out
     // lists the dynamic rows, then -1
-    const TopkWs w = topk_ws(g.S, n_all, std::max<int64_t>(top_k, n_all));
-    return run_dense(g, w, ws, q, k_cache, v_cache, sp.all, scale, top_k, idx_out, o_out, lse_out, s, sp.n_dyn);
+    return run_dense(g, dense_ws(g.S, n_all), ws, q, k_cache, v_cache, sp.all, scale, top_k, idx_out, o_out,
+                     lse_out, s, sp.n_dyn);
   }
   const TopkWs w = topk_ws(g.S, sp.n_dyn, top_k, sp.n_st);
   STDK_TRY(run_exact_select(g, w, ws, q, k_cache, sp.all, scale, nullptr, idx_out, di, s));
   return run_sv(g, w, ws, v_cache, o_out, lse_out, s, &sp.all);
+}
+
+// Validation shared by topk_attn_decode_static and its allocation-free
+// variant (everything but the workspace).
+int32_t check_static_args(const stdk_layout* lay, const float* q, const void* k_cache, const void* v_cache,
+                          const int64_t* ranges, int32_t n_ranges, const int64_t* static_ranges, int32_t n_static,
+                          int32_t top_k, float scale, const int32_t* idx_out, const float* o_out,
+                          const float* lse_out, StaticSplit* sp) {
+  STDK_TRY(check_layout(lay));
+  STDK_TRY(check_ptr(q, "q", 16));
+  STDK_TRY(check_ptr(k_cache, "k_cache", 16));
+  STDK_TRY(check_ptr(v_cache, "v_cache", 16));
+  STDK_TRY(check_ptr(o_out, "o_out", 4));
+  STDK_TRY(check_ptr(lse_out, "lse_out", 4));
+  if (idx_out && ((uintptr_t)idx_out) % 4) return fail(STDK_EINVAL, "idx_out is not 4-byte aligned");
+  if (top_k < 1) return fail(STDK_EINVAL, "top_k %d < 1", top_k);
+  if (!std::isfinite(scale)) return fail(STDK_EINVAL, "scale is not finite");
+  STDK_TRY(split_static(lay, ranges, n_ranges, static_ranges, n_static, sp));
+  if (top_k > kMaxTopK && top_k < sp->n_dyn)
+    return fail(STDK_EUNSUPPORTED, "top_k %d > %d (below the row count)", top_k, kMaxTopK);
+  if (top_k < sp->n_dyn && top_k + sp->n_st > kMaxTopK)
+    return fail(STDK_EUNSUPPORTED, "top_k %d + %lld static rows > %d", top_k, (long long)sp->n_st, kMaxTopK);
+  return STDK_OK;
+}
+
+// ---------------------------------------------------------------------------
+// scratch of the allocation-free entry point: one array per GPU, owned by the
+// library for the life of the process. Host code never uses the array's name
+// as an address (that is a host-side stand-in); the device address comes
+// from hipGetSymbolAddress, once per device with that device current.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[STDK_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+
+int32_t scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(STDK_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(STDK_EUNSUPPORTED, "device index %d", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(STDK_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return STDK_OK;
 }
 
 // The top-K among the reranked candidates: staged in LDS when every
@@ -937,7 +1002,8 @@ int32_t stdk_version(void) { return STDK_VERSION; }
 
 size_t topk_attn_decode_workspace_size(const stdk_layout* lay, int64_t n_scan, int32_t top_k) {
   if (check_layout(lay) != STDK_OK || n_scan < 0 || top_k < 1) return 0;
-  return topk_ws(geo_of(lay).S, n_scan, top_k).total;
+  const int64_t S = geo_of(lay).S;
+  return top_k >= n_scan ? dense_ws(S, n_scan).total : topk_ws(S, n_scan, top_k).total;
 }
 
 int32_t topk_attn_decode(const stdk_layout* lay, const float* q, const void* k_cache, const void* v_cache,
@@ -961,8 +1027,9 @@ int32_t topk_attn_decode(const stdk_layout* lay, const float* q, const void* k_c
   const TopkWs w = topk_ws(g.S, n, top_k);
   if (n > 0) {
     STDK_TRY(check_ptr(workspace, "workspace", 256));
-    if (workspace_bytes < w.total)
-      return fail(STDK_EWORKSPACE, "workspace is %zu bytes, %zu needed", workspace_bytes, w.total);
+    const size_t need = topk_attn_decode_workspace_size(lay, n, top_k);
+    if (workspace_bytes < need)
+      return fail(STDK_EWORKSPACE, "workspace is %zu bytes, %zu needed", workspace_bytes, need);
   }
   hipStream_t s = (hipStream_t)stream;
   DevInfo* di = nullptr;
@@ -980,7 +1047,7 @@ int32_t topk_attn_decode(const stdk_layout* lay, const float* q, const void* k_c
   STDK_TRY(clean_if_dirty(ws, workspace_bytes, s));
   int32_t rc;
   if (top_k >= n) {
-    rc = run_dense(g, w, ws, q, k_cache, v_cache, tab, scale, top_k, idx_out, o_out, lse_out, s);
+    rc = run_dense(g, dense_ws(g.S, n), ws, q, k_cache, v_cache, tab, scale, top_k, idx_out, o_out, lse_out, s);
   } else {
     rc = run_exact_select(g, w, ws, q, k_cache, tab, scale, nullptr, idx_out, di, s);
     if (rc == STDK_OK) rc = run_sv(g, w, ws, v_cache, o_out, lse_out, s, &tab);
@@ -992,30 +1059,18 @@ size_t topk_attn_decode_static_workspace_size(const stdk_layout* lay, int64_t n_
                                               int32_t top_k) {
   if (check_layout(lay) != STDK_OK || n_scan < 0 || n_static < 0 || top_k < 1) return 0;
   const int64_t S = geo_of(lay).S;
-  // the fused path, or the dense path over the union of both sets
-  return std::max(topk_ws(S, n_scan, top_k, n_static).total,
-                  topk_ws(S, n_scan + n_static, std::max<int64_t>(top_k, n_scan + n_static)).total);
+  // the one-pass path, or (every dynamic row chosen) dense attention over
+  // the union of both sets
+  return top_k >= n_scan ? dense_ws(S, n_scan + n_static).total : topk_ws(S, n_scan, top_k, n_static).total;
 }
 
 int32_t topk_attn_decode_static(const stdk_layout* lay, const float* q, const void* k_cache, const void* v_cache,
                                 const int64_t* ranges, int32_t n_ranges, const int64_t* static_ranges,
                                 int32_t n_static, int32_t top_k, float scale, int32_t* idx_out, float* o_out,
                                 float* lse_out, void* workspace, size_t workspace_bytes, void* stream) {
-  STDK_TRY(check_layout(lay));
-  STDK_TRY(check_ptr(q, "q", 16));
-  STDK_TRY(check_ptr(k_cache, "k_cache", 16));
-  STDK_TRY(check_ptr(v_cache, "v_cache", 16));
-  STDK_TRY(check_ptr(o_out, "o_out", 4));
-  STDK_TRY(check_ptr(lse_out, "lse_out", 4));
-  if (idx_out && ((uintptr_t)idx_out) % 4) return fail(STDK_EINVAL, "idx_out is not 4-byte aligned");
-  if (top_k < 1) return fail(STDK_EINVAL, "top_k %d < 1", top_k);
-  if (!std::isfinite(scale)) return fail(STDK_EINVAL, "scale is not finite");
   StaticSplit sp{};
-  STDK_TRY(split_static(lay, ranges, n_ranges, static_ranges, n_static, &sp));
-  if (top_k > kMaxTopK && top_k < sp.n_dyn)
-    return fail(STDK_EUNSUPPORTED, "top_k %d > %d (below the row count)", top_k, kMaxTopK);
-  if (top_k < sp.n_dyn && top_k + sp.n_st > kMaxTopK)
-    return fail(STDK_EUNSUPPORTED, "top_k %d + %lld static rows > %d", top_k, (long long)sp.n_st, kMaxTopK);
+  STDK_TRY(check_static_args(lay, q, k_cache, v_cache, ranges, n_ranges, static_ranges, n_static, top_k, scale,
+                             idx_out, o_out, lse_out, &sp));
   const Geo g = geo_of(lay);
   if (sp.n_dyn + sp.n_st > 0) {
     STDK_TRY(check_ptr(workspace, "workspace", 256));
@@ -1028,6 +1083,38 @@ int32_t topk_attn_decode_static(const stdk_layout* lay, const float* q, const vo
   const int32_t rc = run_static(g, sp, (char*)workspace, q, k_cache, v_cache, top_k, scale, idx_out, o_out, lse_out,
                                 di, (hipStream_t)stream);
   return finish(rc, workspace, (size_t)g.S * kHistBins * 4);
+}
+
+int32_t topk_attn_decode_static_noalloc(const stdk_layout* lay, const float* q, const void* k_cache,
+                                        const void* v_cache, const int64_t* ranges, int32_t n_ranges,
+                                        const int64_t* static_ranges, int32_t n_static, int32_t top_k, float scale,
+                                        int32_t* idx_out, float* o_out, float* lse_out, void* stream) {
+  StaticSplit sp{};
+  STDK_TRY(check_static_args(lay, q, k_cache, v_cache, ranges, n_ranges, static_ranges, n_static, top_k, scale,
+                             idx_out, o_out, lse_out, &sp));
+  const Geo g = geo_of(lay);
+  hipStream_t s = (hipStream_t)stream;
+  void* ws = nullptr;
+  const size_t counters = (size_t)g.S * kHistBins * 4;
+  if (sp.n_dyn + sp.n_st > 0) {
+    const size_t need = topk_attn_decode_static_workspace_size(lay, sp.n_dyn, sp.n_st, top_k);
+    if (need > (size_t)STDK_NOALLOC_SCRATCH_BYTES)
+      return fail(STDK_EWORKSPACE, "this call needs %zu bytes of scratch; the library's array holds %zu", need,
+                  (size_t)STDK_NOALLOC_SCRATCH_BYTES);
+    STDK_TRY(scratch_ptr(&ws));
+    // the array keeps the previous call's contents: the radix counters
+    // must start at zero, so they are cleared first (a fill kernel, which
+    // is also safe under graph capture)
+    const int64_t nw = (int64_t)(counters / 4);
+    STDK_TRY(launch(KID_FILL, s, [&](hipEvent_t e0, hipEvent_t e1) {
+      STDK_LAUNCH(clear_words, dim3((unsigned)std::min<int64_t>(1024, cdiv(nw, 256))), dim3(256), 0, s,
+                  (uint32_t*)ws, nw);
+    }));
+  }
+  DevInfo* di = nullptr;
+  STDK_TRY(dev_info(&di));
+  return finish(run_static(g, sp, (char*)ws, q, k_cache, v_cache, top_k, scale, idx_out, o_out, lse_out, di, s),
+                nullptr, 0);
 }
 
 size_t topk_multi_query_workspace_size(const stdk_layout* lay, int32_t n_queries, int64_t n_scan, int32_t top_k) {
@@ -1155,7 +1242,7 @@ int32_t topk_attn_decode_int8(const stdk_layout* lay, const float* q, const void
         STDK_LAUNCH(fill_empty, dim3((unsigned)cdiv(m, 256)), dim3(256), 0, s, o_out, lse_out, idx_out, g.S, top_k);
       }));
     } else if (top_k >= n) {
-      rc = run_dense(g, w, ws, q, k_cache, v_cache, tab, scale, top_k, idx_out, o_out, lse_out, s);
+      rc = run_dense(g, dense_ws(g.S, n), ws, q, k_cache, v_cache, tab, scale, top_k, idx_out, o_out, lse_out, s);
     } else {
       rc = run_exact_select(g, w, ws, q, k_cache, tab, scale, nullptr, idx_out, di, s);
       if (rc == STDK_OK) rc = run_sv(g, w, ws, v_cache, o_out, lse_out, s, &tab);

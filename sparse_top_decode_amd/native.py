@@ -21,11 +21,12 @@ STDK_EHIP = -4
 STDK_F32 = 0
 STDK_BF16 = 1
 STDK_MAX_RANGES = 16
+STDK_NOALLOC_SCRATCH_BYTES = 96 << 20
 
 # every symbol include/stdk.h declares
 EXPORTS = [
     "topk_attn_decode", "topk_attn_decode_workspace_size", "attn_merge_lse",
-    "topk_attn_decode_static", "topk_attn_decode_static_workspace_size",
+    "topk_attn_decode_static", "topk_attn_decode_static_workspace_size", "topk_attn_decode_static_noalloc",
     "retopk_state_init", "retopk_step", "retopk_workspace_size", "retopk_state_size",
     "topk_multi_query", "topk_multi_query_workspace_size",
     "quantize_keys_int8", "topk_attn_decode_int8", "topk_attn_decode_int8_workspace_size",
@@ -67,6 +68,9 @@ def _sig(lib):
     lib.topk_attn_decode_static_workspace_size.restype = c_size_t
     lib.attn_merge_lse.argtypes = [c_int64, c_int32, P, P, P, P, P, P, P]
     lib.attn_merge_lse.restype = c_int32
+    lib.topk_attn_decode_static_noalloc.argtypes = [POINTER(Layout), P, P, P, POINTER(c_int64), c_int32,
+                                                    POINTER(c_int64), c_int32, c_int32, c_float, P, P, P, P]
+    lib.topk_attn_decode_static_noalloc.restype = c_int32
     lib.retopk_state_init.argtypes = [POINTER(Layout), POINTER(RetopkParams), POINTER(RetopkState), P, P, c_int32, P]
     lib.retopk_state_init.restype = c_int32
     lib.retopk_step.argtypes = [POINTER(Layout), POINTER(RetopkParams), POINTER(RetopkState), P, P, P, c_int64,

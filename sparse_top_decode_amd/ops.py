@@ -141,6 +141,37 @@ def topk_attn_decode_static(q: torch.Tensor, k_cache: torch.Tensor, v_cache: tor
     return idx_out, o_out, lse_out
 
 
+def topk_attn_decode_static_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                    ranges: Sequence[Tuple[int, int]], static_ranges: Sequence[Tuple[int, int]],
+                                    top_k: int, scale: Optional[float] = None, *,
+                                    idx_out: Optional[torch.Tensor] = None, o_out: Optional[torch.Tensor] = None,
+                                    lse_out: Optional[torch.Tensor] = None, want_idx: bool = True,
+                                    layout: Optional[Layout] = None):
+    """topk_attn_decode_static with the library's own scratch array instead of
+    a workspace (no allocation inside the call when the outputs are given).
+    Returns (idx or None, o, lse)."""
+    lib = load()
+    B, Hq, d = q.shape
+    _need(q, "q", torch.float32)
+    _need(k_cache, "k_cache")
+    _need(v_cache, "v_cache", k_cache.dtype, k_cache.shape)
+    lay = layout if layout is not None else make_layout(k_cache, Hq)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if o_out is None:
+        o_out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if lse_out is None:
+        lse_out = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if idx_out is None and want_idx:
+        idx_out = torch.empty((B, Hq, top_k), dtype=torch.int32, device=q.device)
+    arr, nr = _ranges_arr(ranges)
+    sarr, ns = _ranges_arr(static_ranges)
+    rc = lib.topk_attn_decode_static_noalloc(ctypes.byref(lay), q.data_ptr(), k_cache.data_ptr(),
+                                             v_cache.data_ptr(), arr, nr, sarr, ns, int(top_k), ctypes.c_float(scale),
+                                             _ptr(idx_out), o_out.data_ptr(), lse_out.data_ptr(), _stream())
+    check(rc)
+    return idx_out, o_out, lse_out
+
+
 def attn_merge_lse(o_a: torch.Tensor, lse_a: torch.Tensor, o_b: torch.Tensor, lse_b: torch.Tensor,
                    o_out: Optional[torch.Tensor] = None, lse_out: Optional[torch.Tensor] = None):
     """Log-sum-exp combination of two partial attention outputs."""

@@ -65,6 +65,30 @@ def test_retopk_state_size(lib):
     assert lib.retopk_state_size(ctypes.byref(lay(d=64)), ctypes.byref(RetopkParams(8, 2, 1, 0, 0.5, 0, 0.1))) == 0
 
 
+def test_noalloc_rejects_before_launch(lib):
+    """The allocation-free step rejects bad arguments like the workspace
+    variant, and a call whose scratch need exceeds the library's array with
+    STDK_EWORKSPACE, all before any HIP call."""
+    def call(L, ranges, static, top_k=64, q=FAKE):
+        flat = [x for r in ranges for x in r]
+        sflat = [x for r in static for x in r]
+        arr = (ctypes.c_int64 * max(1, len(flat)))(*flat)
+        sarr = (ctypes.c_int64 * max(1, len(sflat)))(*sflat)
+        return lib.topk_attn_decode_static_noalloc(ctypes.byref(L), q, FAKE, FAKE, arr, len(ranges), sarr,
+                                                   len(static), top_k, ctypes.c_float(0.1), FAKE, FAKE, FAKE, None)
+    big = lay(L=1 << 20)
+    assert call(big, [(128, (1 << 20) - 512)], [(0, 128), ((1 << 20) - 512, 1 << 20)], 8192) == native.STDK_EWORKSPACE
+    need = lib.topk_attn_decode_static_workspace_size(ctypes.byref(big), (1 << 20) - 640, 640, 8192)
+    assert need > native.STDK_NOALLOC_SCRATCH_BYTES
+    c2 = lay(L=131072)
+    need2 = lib.topk_attn_decode_static_workspace_size(ctypes.byref(c2), 130432, 640, 2048)
+    assert 0 < need2 <= native.STDK_NOALLOC_SCRATCH_BYTES
+    assert call(c2, [(128, 130560)], [(0, 128), (130560, 131072)], 0) == native.STDK_EINVAL
+    assert call(c2, [(128, 130560)], [(100, 200)], 64) == native.STDK_EINVAL  # overlap
+    assert call(lay(d=64), [(0, 10)], [], 4) == native.STDK_EUNSUPPORTED
+    assert call(c2, [(0, 10)], [], 4, q=0) == native.STDK_EINVAL
+
+
 def test_inject_launch_failure_arguments(lib):
     assert lib.stdk_inject_launch_failure(-2) == native.STDK_EINVAL
     assert lib.stdk_inject_launch_failure(-1) == native.STDK_OK
