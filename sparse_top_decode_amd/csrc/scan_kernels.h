@@ -9,6 +9,8 @@
 // top-K select starts from.
 #pragma once
 
+#include <type_traits>
+
 #include "device.h"
 
 namespace stdk {
@@ -192,12 +194,43 @@ STDK_DEV int lane_perm(int c, bool* out_lane) {
   return pi;
 }
 
+// Wait until at most N of this wave's key loads are in flight (vmcnt(N),
+// N < 16; expcnt and lgkmcnt left at their maximum).
+template <int N>
+STDK_DEV void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(N | 0x0F70);
+}
+
+// The key rows are requested with explicit load instructions that the
+// compiler's wait insertion does not track, and each register set is waited
+// for explicitly before it is used (wait_vm, then an empty asm that "writes"
+// the set's registers so that no use is scheduled above the wait). The
+// compiler, left to itself, merged the loop's entry and back edges into a
+// wait for every outstanding load at the top of each iteration, which left
+// one register set in flight instead of two.
+STDK_DEV void load16_async(u32x4& dst, const char* p, std::integral_constant<int, 0>) {
+  __asm__ volatile("global_load_dwordx4 %0, %1, off" : "=v"(dst) : "v"(p));
+}
+template <int OFF>
+STDK_DEV void load16_async(u32x4& dst, const char* p, std::integral_constant<int, OFF>) {
+  __asm__ volatile("global_load_dwordx4 %0, %1, off offset:%2" : "=v"(dst) : "v"(p), "i"(OFF));
+}
+STDK_DEV void load4_async(float& dst, const float* p) {
+  __asm__ volatile("global_load_dword %0, %1, off" : "=v"(dst) : "v"(p));
+}
+template <typename X>
+STDK_DEV void arrived(X& x) {
+  __asm__ volatile("" : "+v"(x));
+}
+
 template <typename T, int G>
 __global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
   using Sh = ScanShape<T, G>;
   constexpr bool kQ8 = sizeof(T) == 1;  // int8 codes: score = scale * row scale * (q . code)
   constexpr int GP = Sh::GP, LPR = Sh::LPR, NCH = Sh::NCH, EPC = Sh::EPC, E = Sh::E, UR = Sh::UR, V = Sh::V;
   constexpr int RPW = Sh::RPW, ROWB = Sh::ROWB, IT = Sh::ROWS_ITER;
+  constexpr int NL = UR * NCH + (kQ8 ? UR : 0);  // loads per register set
   __shared__ __attribute__((aligned(16))) uint32_t lh[G * kHistBins];
   extern __shared__ __attribute__((aligned(16))) float sst[];  // staged scores, when a.stage_stride > 0
 
@@ -224,38 +257,63 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
   const float* ksb = kQ8 ? a.kscale + (int64_t)b * a.kscale_stride_b + (int64_t)hkv * a.kscale_stride_h : nullptr;
   const int64_t p_beg = (int64_t)blk * a.rows_per_block;
   const int64_t p_end = min(a.n, p_beg + a.rows_per_block);
-  // current piece of the block's positions: [s0, s1) inside range r
-  int r = -1;
-  int64_t s0 = 0, s1 = 0, rowoff = 0;
-  auto next_piece = [&]() -> bool {
-    for (++r; r < a.tab.n; ++r) {
-      s0 = max(p_beg, a.tab.pos0[r]);
-      s1 = min(p_end, a.tab.pos0[r + 1]);
-      if (s0 < s1) {
-        rowoff = a.tab.row0[r] - a.tab.pos0[r];
-        return true;
+  // An iteration covers positions [base, base + IT) of the piece [.., pe) of
+  // one range, whose rows are position + ro. Past the block's end `ok` is
+  // false: the iteration keeps the last piece (its loads stay clamped to a
+  // valid row) and scores nothing.
+  struct Iter {
+    int64_t base, pe, ro;
+    bool ok;
+  };
+  // the piece that holds position p (p_beg <= p < p_end), from p on; the
+  // range table is read with compile-time indices (scalar loads)
+  auto piece_at = [&](int64_t p) -> Iter {
+    Iter it{p, a.tab.pos0[1], a.tab.row0[0] - a.tab.pos0[0], true};
+#pragma unroll
+    for (int i = 1; i < kMaxRanges; ++i) {
+      if (i >= a.tab.n) break;
+      if (p >= a.tab.pos0[i]) {
+        it.pe = a.tab.pos0[i + 1];
+        it.ro = a.tab.row0[i] - a.tab.pos0[i];
       }
     }
-    return false;
+    it.pe = min(it.pe, p_end);
+    return it;
   };
-  // row slot s of an iteration at `base` holds row (s ^ rowperm); loads past
-  // the piece are clamped to its last row and their results dropped, so every
-  // load is issued unconditionally
-  auto issue = [&](int64_t base, u32x4 (&kw)[UR][NCH], float (&sc)[UR]) {
+  auto advance = [&](const Iter& it) -> Iter {
+    const int64_t nb = it.base + IT;
+    if (nb < it.pe) return Iter{nb, it.pe, it.ro, it.ok};
+    if (it.ok && it.pe < p_end) return piece_at(it.pe);
+    return Iter{p_end + IT, it.pe, it.ro, false};
+  };
+  // row slot s of an iteration holds row (s ^ rowperm); loads past the piece
+  // are clamped to its last row and their results dropped, so every load is
+  // issued unconditionally
+  auto issue = [&](const Iter& it, u32x4 (&kw)[UR][NCH], float (&sc)[UR]) {
 #pragma unroll
     for (int s = 0; s < UR; ++s) {
-      const int64_t p = min(base + (int64_t)(w * UR + (s ^ rowperm)) * RPW + rg, s1 - 1);
-      const char* rp = kb + (p + rowoff) * ROWB;
-#pragma unroll
-      for (int k = 0; k < NCH; ++k) kw[s][k] = load16(rp + k * LPR * 16);
-      if constexpr (kQ8) sc[s] = ksb[p + rowoff];
+      const int64_t p = min(it.base + (int64_t)(w * UR + (s ^ rowperm)) * RPW + rg, it.pe - 1);
+      const char* rp = kb + (p + it.ro) * ROWB;
+      load16_async(kw[s][0], rp, std::integral_constant<int, 0>{});
+      if constexpr (NCH > 1) load16_async(kw[s][1], rp, std::integral_constant<int, LPR * 16>{});
+      if constexpr (NCH > 2) load16_async(kw[s][2], rp, std::integral_constant<int, 2 * LPR * 16>{});
+      if constexpr (NCH > 3) load16_async(kw[s][3], rp, std::integral_constant<int, 3 * LPR * 16>{});
+      if constexpr (kQ8) load4_async(sc[s], ksb + p + it.ro);
     }
   };
+  // the set's loads have arrived once at most NL newer loads are in flight
+  auto wait_set = [&](u32x4 (&kw)[UR][NCH], float (&sc)[UR]) {
+    wait_vm<NL>();
+#pragma unroll
+    for (int s = 0; s < UR; ++s) {
+#pragma unroll
+      for (int k = 0; k < NCH; ++k) arrived(kw[s][k]);
+      if constexpr (kQ8) arrived(sc[s]);
+    }
+  };
+  static_assert(NCH <= 4 && NL < 16, "load shape");
   u32x4 kw[2][UR][NCH];
   float ksc[2][UR];
-  bool more = next_piece();
-  // the first key rows are requested before the query and the LDS set-up
-  if (more) issue(s0, kw[0], ksc[0]);
 
   // query elements of this lane; head slot hs holds head hs ^ headperm (zero
   // when that head does not exist, G < GP)
@@ -275,11 +333,16 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
         qr[hs][k * EPC + 4 * e4 + 3] = v.w;
       }
   }
+  // both register sets of key rows are requested right after the query
+  Iter d0 = piece_at(p_beg);
+  Iter d1 = advance(d0);
+  issue(d0, kw[0], ksc[0]);
+  issue(d1, kw[1], ksc[1]);
   for (int i = tid; i < G * kHistBins; i += kScanThreads) lh[i] = 0u;
   // LDS-only barrier: the key loads stay in flight
-  __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
-  __asm__ volatile("" ::: "memory");
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 
   // int8 codes c are read as unsigned bytes u = c + 128 (one conversion per
   // byte); q . c = q . u - 128 * sum(q), the sum taken once per lane and head
@@ -292,7 +355,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
       for (int e = 0; e < E; ++e) qsum[hs] += qr[hs][e];
     }
   }
-  auto consume = [&](int64_t base, int64_t cstart, const u32x4 (&kv)[UR][NCH], const float (&sc)[UR]) {
+  auto consume = [&](const Iter& it, int64_t cstart, const u32x4 (&kv)[UR][NCH], const float (&sc)[UR]) {
     float acc[V];
 #pragma unroll
     for (int j = 0; j < V; ++j) {
@@ -322,8 +385,8 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
       acc[j] = t;
     }
     reduce_slots<LPR, V>(acc);
-    const int64_t p = base + (int64_t)(w * UR + u_out) * RPW + rg;
-    if (writer && p < s1) {
+    const int64_t p = it.base + (int64_t)(w * UR + u_out) * RPW + rg;
+    if (writer && p < it.pe) {
       float val = acc[0] * a.scale;
       if constexpr (kQ8) {
         // logical row u_out sits in slot u_out ^ rowperm
@@ -341,13 +404,13 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
       if (p < a.n_hist) atomicAdd(&lh[h_out * kHistBins + (f2key(val) >> (32 - kHistBits))], 1u);
     }
   };
-  // Staged scores: a chunk of the piece's positions [c0, c1) goes out once
+  // Staged scores: a chunk of consecutive positions [c0, c1) goes out once
   // every wave has scored it, as coalesced non-temporal stores; LDS-only
   // barriers around it keep the key loads in flight.
   auto flush = [&](int64_t c0, int64_t c1) {
-    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
-    __asm__ volatile("" ::: "memory");
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     const int len = (int)(c1 - c0);
     // rows start on 64-float boundaries, so a chunk that starts on a multiple
     // of 4 positions goes out in 16-byte stores
@@ -363,36 +426,46 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
                                     reinterpret_cast<f32x4*>(dst + 4 * i));
       for (int i = 4 * nvec + tid; i < len; i += kScanThreads) __builtin_nontemporal_store(srcp[i], dst + i);
     }
-    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
-    __asm__ volatile("" ::: "memory");
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
   };
   const bool staged = a.stage_stride > 0;
-  while (more) {
-    // two register sets; the scheduling barriers keep each set's loads ahead
-    // of the arithmetic on the other set
-    int64_t base = s0, cstart = s0;
-    bool done = false;
-    while (!done) {
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        if (!done) {
-          issue(base + IT, kw[st ^ 1], ksc[st ^ 1]);
-          __builtin_amdgcn_sched_barrier(0);
-          consume(base, cstart, kw[st], ksc[st]);
-          __builtin_amdgcn_sched_barrier(0);
-          base += IT;
-          done = base >= s1;
-          if (staged && (done || base - cstart >= a.stage_rows)) {
-            flush(cstart, min(base, s1));
-            cstart = base;
-          }
-        }
-      }
+  int64_t cstart = d0.base;
+  // after consuming `it`: the staged chunk goes out when the next iteration
+  // would not fit beside it, or at the end (with the whole block staged,
+  // that is once, after the last iteration)
+  auto after = [&](const Iter& it, const Iter& nx) {
+    if (staged && (!nx.ok || nx.base + IT - cstart > a.stage_rows)) {
+      flush(cstart, min(it.base + IT, it.pe));
+      cstart = nx.base;
     }
-    more = next_piece();
-    if (more) issue(s0, kw[0], ksc[0]);
+  };
+  // Two register sets: each is requested again as soon as it has been
+  // consumed, so while one is consumed the other is in flight, and while a
+  // wave waits both are. An iteration past the end is issued clamped and
+  // scores nothing.
+  for (;;) {
+    wait_set(kw[0], ksc[0]);
+    consume(d0, cstart, kw[0], ksc[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    after(d0, d1);
+    if (!d1.ok) break;
+    d0 = advance(d1);
+    issue(d0, kw[0], ksc[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_set(kw[1], ksc[1]);
+    consume(d1, cstart, kw[1], ksc[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    after(d1, d0);
+    if (!d0.ok) break;
+    d1 = advance(d0);
+    issue(d1, kw[1], ksc[1]);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  // the clamped loads past the end are still in flight: drain them before
+  // their registers are reused
+  wait_vm<0>();
   __syncthreads();
   // Add the block histogram to the global one: all LDS reads of a thread are
   // issued before the first wait, then one atomic per non-empty bin. Heads
