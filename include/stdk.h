@@ -17,10 +17,11 @@
  *  - Determinism: identical inputs give bit-identical outputs.
  *  - Concurrency: calls are reentrant; two calls that are in flight at the
  *    same time must not share a workspace buffer.
- *  - Workspace state: the first B * n_q_heads * 8192 bytes of a workspace
- *    hold radix-histogram counters that each call adds to and then clears
- *    again. They must be zero before the first call that uses the buffer
- *    (fill the new buffer with zeros once, e.g. hipMemset). Every call that
+ *  - Workspace state: the first B * n_q_heads * 16448 bytes of a workspace
+ *    hold counters (two radix histograms and an arrival counter per query
+ *    head) that each call adds to and then clears again. They must be zero
+ *    before the first call that uses the buffer (fill the new buffer with
+ *    zeros once, e.g. hipMemset). Every call that
  *    returns STDK_OK leaves them zero, so the buffer can be reused by later
  *    calls with the same stdk_layout (topk_attn_decode, its _static and
  *    _int8 variants, retopk_step, and topk_multi_query, which leaves that
@@ -200,7 +201,7 @@ int32_t topk_attn_decode_static_noalloc(const stdk_layout* lay, const float* q, 
  *             idx_out, -inf in the padding.
  *  workspace  at least topk_multi_query_workspace_size(lay, M, n, top_k)
  *             bytes, 256-byte aligned, any contents (this call keeps no
- *             counters in it, and leaves the first B * H_q * 8192 bytes,
+ *             counters in it, and leaves the first B * H_q * 16448 bytes,
  *             the decode calls' counters, untouched). Not used when n = 0.
  *  Limits: B * n_kv_heads <= 65535.
  * The scores are computed on the bf16 matrix cores with every fp32 query

@@ -57,12 +57,12 @@ int32_t ok() {
 // launch timing
 // ---------------------------------------------------------------------------
 enum KernelId {
-  KID_SCAN, KID_FILTER, KID_SELECT, KID_SV, KID_DENSE, KID_COMBINE, KID_MERGE, KID_FILL,
+  KID_SCAN, KID_SELECT, KID_SV, KID_DENSE, KID_COMBINE, KID_MERGE, KID_FILL,
   KID_RT_SELECT, KID_RT_RERANK, KID_RT_RSEL, KID_RT_INIT, KID_MQ_BLOCKMAX, KID_MQ_THRESH,
   KID_MQ_COLLECT, KID_MQ_SELECT, KID_MQ_FILL, KID_RT_VOTE, KID_Q8_QUANT, KID_COUNT
 };
 const char* const kKernelNames[KID_COUNT] = {
-    "k_scan",        "topk_filter",   "topk_select",          "sparse_sv",
+    "k_scan",        "topk_filter_select",             "sparse_sv",
     "dense_attn",  "combine",       "attn_merge",    "fill_empty",           "retopk_select",
     "retopk_rerank", "retopk_rerank_select", "retopk_init", "mq_blockmax",
     "mq_threshold",  "mq_collect",    "mq_select",     "mq_fill",       "retopk_vote",   "k_quantize"};
@@ -119,9 +119,9 @@ int32_t launch(int kid, hipStream_t s, F&& f) {
 // ---------------------------------------------------------------------------
 // workspaces left dirty by a failed call
 // ---------------------------------------------------------------------------
-// A call chain keeps the radix-histogram counters at the start of its
-// workspace zero between calls (the scan adds to them, the select clears
-// them). A chain that stops with STDK_EHIP after its scan was enqueued
+// A call chain keeps the counters at the start of its workspace (radix
+// histograms and the select's arrival counters) zero between calls: the
+// scan and the filter-select add to them, the filter-select clears them. A chain that stops with STDK_EHIP after its scan was enqueued
 // leaves them non-zero; the workspace is recorded here with the extent of
 // its counter region, and the next call on it clears that region first.
 std::mutex g_dirty_mu;
@@ -235,7 +235,7 @@ int32_t dev_info(DevInfo** out) {
     occ_row<uint16_t>(d.scan_occ[1]);
     occ_row<int8_t>(d.scan_occ[2]);
     const int dyn_max = std::max(0, d.max_lds - (int)kSelStaticLds);
-    (void)hipFuncSetAttribute((const void*)topk_select, hipFuncAttributeMaxDynamicSharedMemorySize, dyn_max);
+    (void)hipFuncSetAttribute((const void*)topk_filter_select, hipFuncAttributeMaxDynamicSharedMemorySize, dyn_max);
     (void)hipFuncSetAttribute((const void*)retopk_select<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               std::max(0, d.max_lds - 12 * 1024));
     (void)hipFuncSetAttribute((const void*)mq_select, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -312,13 +312,22 @@ Geo geo_of(const stdk_layout* lay) {
 }
 
 // ---------------------------------------------------------------------------
-// workspace: [hist (zero between calls)] [scores] [spilled candidates] [partials]
+// workspace: [counters (zero between calls)] [scores] [candidates] [partials]
 // ---------------------------------------------------------------------------
+// The counter region: per segment a 2048-bin first-digit histogram, then
+// per segment a 2048-bin second-digit histogram, then per segment
+// kCtlWords control words (word 0: the select's arrival counter).
+inline size_t counter_bytes(int64_t S) { return al256((size_t)S * (2 * kHistBins + kCtlWords) * 4); }
+
+// Filter-select geometry: about one workgroup per CU over the grid, each
+// wave's slice (a multiple of 64 positions) loaded whole in one round.
+constexpr int64_t kFselTargetWg = 256;
+
 // n positions take part in the top-K; n_extra more (a static row set) are
 // scored by the same scan and appended whole to every chosen-row list.
 struct TopkWs {
-  int64_t S, n, n_extra, n_pad, K, ksel, nsplit, slice, nslice;
-  size_t hist, hist_words, scores, list, clist, slice_cnt, sel_row, sel_z, part, total;
+  int64_t S, n, n_extra, n_pad, K, ksel, nsplit, slice, wg;
+  size_t hist, hist1, done, counters, scores, list, clist, wg_cnt, sel_row, sel_z, part, total;
 };
 
 TopkWs topk_ws(int64_t S, int64_t n, int64_t K, int64_t n_extra = 0) {
@@ -331,21 +340,27 @@ TopkWs topk_ws(int64_t S, int64_t n, int64_t K, int64_t n_extra = 0) {
   w.K = K;
   w.ksel = K + n_extra;
   w.nsplit = cdiv(w.ksel, kSvRows);
-  // filter wave slices: at most 4 per select thread, about 4096 over the grid
-  w.slice = std::max<int64_t>(rup(cdiv(n1, 4 * kSelThreads), 64), std::min<int64_t>(8192, rup(cdiv(n1 * S, 4096), 64)));
-  w.nslice = cdiv(n1, w.slice);
-  size_t off = 0;
-  w.hist = off;
-  w.hist_words = (size_t)S * kHistBins;
-  off = al256(off + w.hist_words * 4);
+  // filter-select: P workgroups per segment (at least 64 positions per
+  // wave), 16 wave slices of at most 64 * kFselLoads positions each
+  constexpr int64_t WV = kSelectWaves;
+  constexpr int64_t kMaxSlice = 64 * kFselLoads;
+  int64_t wg = std::max(cdiv(kFselTargetWg, S), cdiv(n1, kMaxSlice * WV));
+  wg = std::max<int64_t>(1, std::min(wg, cdiv(n1, 64 * WV)));
+  w.slice = rup(cdiv(n1, wg * WV), 64);
+  w.wg = cdiv(n1, WV * w.slice);
+  w.hist = 0;
+  w.hist1 = (size_t)S * kHistBins * 4;
+  w.done = (size_t)S * 2 * kHistBins * 4;
+  w.counters = counter_bytes(S);
+  size_t off = w.counters;
   w.scores = off;
   off = al256(off + (size_t)S * w.n_pad * 4);
   w.list = off;
   off = al256(off + (size_t)S * w.n_pad * sizeof(Cand));
   w.clist = off;
   off = al256(off + (size_t)S * w.n_pad * sizeof(Cand));
-  w.slice_cnt = off;
-  off = al256(off + (size_t)S * w.nslice * 4);
+  w.wg_cnt = off;
+  off = al256(off + (size_t)S * w.wg * 4);
   w.sel_row = off;
   off = al256(off + (size_t)S * K * 4);
   w.sel_z = off;
@@ -364,8 +379,8 @@ TopkWs dense_ws(int64_t S, int64_t n) {
   w.n = n;
   w.n_pad = rup(std::max<int64_t>(n, 1), 64);
   w.K = n;
-  w.hist_words = (size_t)S * kHistBins;
-  w.part = al256(w.hist_words * 4);
+  w.counters = counter_bytes(S);
+  w.part = w.counters;
   w.total = al256(w.part + (size_t)S * kDenseMaxWg * kPartStride * 4);
   return w;
 }
@@ -437,8 +452,8 @@ void launch_dense_t(int G, dim3 grid, hipStream_t s, const DenseArgs& a, hipEven
 }
 
 // The exact select over n positions (any n >= 1; n <= K takes every row):
-// scan, filter, select. The histogram (the first S * 8 KiB of the
-// workspace) is zero on entry and the select kernel leaves it zero again.
+// scan, then filter-select. The counter region (the first counter_bytes(S)
+// of the workspace) is zero on entry and the filter-select leaves it zero.
 // Leaves the chosen rows and scores in the workspace. `active` restricts the
 // work to the listed segments (ReTopK exact heads); null = all.
 // int8 key codes and their row scales (packed: [B][H_kv][max_len][128] and
@@ -455,7 +470,6 @@ int32_t run_exact_select(const Geo& g, const TopkWs& w, char* ws, const float* q
   float* scores = (float*)(ws + w.scores);
   uint32_t* hist = (uint32_t*)(ws + w.hist);
   Cand* list = (Cand*)(ws + w.list);
-  uint32_t* slice_cnt = (uint32_t*)(ws + w.slice_cnt);
   {
     ScanArgs a{};
     a.q = q;
@@ -506,42 +520,34 @@ int32_t run_exact_select(const Geo& g, const TopkWs& w, char* ws, const float* q
     }));
   }
   {
-    FilterArgs a{};
+    SelectArgs a{};
     a.scores = scores;
     a.hist = hist;
+    a.hist1 = (uint32_t*)(ws + w.hist1);
+    a.done = (uint32_t*)(ws + w.done);
     a.list = list;
-    a.slice_cnt = slice_cnt;
-    a.n = w.n;
-    a.n_pad = w.n_pad;
-    a.K = (int32_t)w.K;
-    a.slice = (int32_t)w.slice;
-    a.nslice = (int32_t)w.nslice;
-    a.seg_active = active;
-    const dim3 grid((unsigned)cdiv(w.nslice, kFilterWaves), (unsigned)w.S);
-    STDK_TRY(launch(KID_FILTER, s, [&](hipEvent_t e0, hipEvent_t e1) { STDK_LAUNCH(topk_filter, grid, dim3(kFilterThreads), 0, s, a); }));
-  }
-  {
-    SelectArgs a{};
-    a.hist = hist;
-    a.list = list;
-    a.slice_cnt = slice_cnt;
+    a.wg_cnt = (uint32_t*)(ws + w.wg_cnt);
     a.clist = (Cand*)(ws + w.clist);
     a.n = w.n;
     a.n_pad = w.n_pad;
     a.K = (int32_t)w.K;
     a.slice = (int32_t)w.slice;
-    a.nslice = (int32_t)w.nslice;
     a.sel_row = (int32_t*)(ws + w.sel_row);
     a.sel_z = (float*)(ws + w.sel_z);
     a.idx_out = idx_out;
     a.seg_active = active;
     a.tab = tab;
-    const size_t pre_bytes = (size_t)((w.nslice + 2) & ~1LL) * 4;
+    // LDS for the workgroups' offsets and the candidates (typically under
+    // 2K of them): room for max(8192, 2K)
+    const size_t pre_bytes = (size_t)((w.wg + 2) & ~1LL) * 4;
     const size_t avail = (size_t)di->max_lds - kSelStaticLds;
-    const size_t dyn = std::min(avail, pre_bytes + (size_t)w.n * sizeof(Cand));
+    const int64_t want = std::min<int64_t>(w.n, std::max<int64_t>(8192, 2 * w.K));
+    const size_t dyn = std::min(avail, pre_bytes + (size_t)want * sizeof(Cand));
     a.cache_cap = (int32_t)((dyn - pre_bytes) / sizeof(Cand));
+    if (w.wg > 65535) return fail(STDK_EUNSUPPORTED, "%lld select workgroups per head", (long long)w.wg);
+    const dim3 grid((unsigned)w.wg, (unsigned)w.S);
     STDK_TRY(launch(KID_SELECT, s, [&](hipEvent_t e0, hipEvent_t e1) {
-      STDK_LAUNCH(topk_select, dim3((unsigned)w.S), dim3(kSelThreads), dyn, s, a);
+      STDK_LAUNCH(topk_filter_select, grid, dim3(kSelThreads), dyn, s, a);
     }));
   }
   return STDK_OK;
@@ -664,9 +670,9 @@ MqWs mq_ws(const Geo& g, int64_t M, int64_t n, int64_t K) {
   nchunk = std::min<int64_t>(nchunk, w.nblk);
   w.chunk = std::max<int64_t>(rup(cdiv(std::max<int64_t>(n, 1), nchunk), kMqBlock), rup(cdiv(std::max<int64_t>(n, 1), kMqMaxChunks), kMqBlock));
   w.nchunk = cdiv(std::max<int64_t>(n, 1), w.chunk);
-  // the first B * H_q * 8 KiB are the decode calls' radix counters, which
-  // are zero between calls: left untouched, so one buffer may serve both
-  size_t off = al256((size_t)g.S * kHistBins * 4);
+  // the decode calls' counter region, which is zero between calls, is left
+  // untouched, so one buffer may serve both
+  size_t off = counter_bytes(g.S);
   w.bmax = off;
   off = al256(off + (size_t)w.S * w.ngrp * 4);
   w.thr = off;
@@ -1052,7 +1058,7 @@ int32_t topk_attn_decode(const stdk_layout* lay, const float* q, const void* k_c
     rc = run_exact_select(g, w, ws, q, k_cache, tab, scale, nullptr, idx_out, di, s);
     if (rc == STDK_OK) rc = run_sv(g, w, ws, v_cache, o_out, lse_out, s, &tab);
   }
-  return finish(rc, ws, w.hist_words * 4);
+  return finish(rc, ws, w.counters);
 }
 
 size_t topk_attn_decode_static_workspace_size(const stdk_layout* lay, int64_t n_scan, int64_t n_static,
@@ -1082,7 +1088,7 @@ int32_t topk_attn_decode_static(const stdk_layout* lay, const float* q, const vo
   STDK_TRY(clean_if_dirty(workspace, workspace_bytes, (hipStream_t)stream));
   const int32_t rc = run_static(g, sp, (char*)workspace, q, k_cache, v_cache, top_k, scale, idx_out, o_out, lse_out,
                                 di, (hipStream_t)stream);
-  return finish(rc, workspace, (size_t)g.S * kHistBins * 4);
+  return finish(rc, workspace, counter_bytes(g.S));
 }
 
 int32_t topk_attn_decode_static_noalloc(const stdk_layout* lay, const float* q, const void* k_cache,
@@ -1095,7 +1101,7 @@ int32_t topk_attn_decode_static_noalloc(const stdk_layout* lay, const float* q, 
   const Geo g = geo_of(lay);
   hipStream_t s = (hipStream_t)stream;
   void* ws = nullptr;
-  const size_t counters = (size_t)g.S * kHistBins * 4;
+  const size_t counters = counter_bytes(g.S);
   if (sp.n_dyn + sp.n_st > 0) {
     const size_t need = topk_attn_decode_static_workspace_size(lay, sp.n_dyn, sp.n_st, top_k);
     if (need > (size_t)STDK_NOALLOC_SCRATCH_BYTES)
@@ -1229,7 +1235,7 @@ int32_t topk_attn_decode_int8(const stdk_layout* lay, const float* q, const void
     STDK_TRY(dev_info(&di));
   }
   char* ws = (char*)workspace;
-  const size_t hb = (size_t)g.S * kHistBins * 4;
+  const size_t hb = counter_bytes(g.S);
   if (n > 0) STDK_TRY(clean_if_dirty(ws, workspace_bytes, s));
   if (n == 0 || recall_k >= n) {
     // the superset is every row: exact top-K attention (the superset output
@@ -1304,7 +1310,7 @@ int32_t topk_attn_decode_int8_static(const stdk_layout* lay, const float* q, con
     if (workspace_bytes < need) return fail(STDK_EWORKSPACE, "workspace is %zu bytes, %zu needed", workspace_bytes, need);
   }
   STDK_TRY(dev_info(&di));
-  const size_t hb = (size_t)g.S * kHistBins * 4;
+  const size_t hb = counter_bytes(g.S);
   STDK_TRY(clean_if_dirty(ws, workspace_bytes, s));
   if (recall_k >= sp.n_dyn) {
     // the superset is every dynamic row: topk_attn_decode_static's result
@@ -1577,7 +1583,7 @@ int32_t retopk_step(const stdk_layout* lay, const retopk_params* p, const retopk
                       p->cache_cap, p->top_k};
     return run_sv(g, w.t, ws, v_cache, o_out, lse_out, s, nullptr, &push);
   }();
-  return finish(rc, ws, w.t.hist_words * 4);
+  return finish(rc, ws, w.t.counters);
 }
 
 // ---------------------------------------------------------------------------

@@ -11,15 +11,17 @@
 // Steps, all integer work exact:
 //  1. k_scan has counted the first radix digit (top 11 bits of the
 //     order-preserving key); the bin b* holding the K-th largest key follows.
-//     topk_select zeroes the counts again once it has read them, so the
-//     histogram needs no separate clearing pass per call.
-//  2. topk_filter (many workgroups) keeps the positions whose digit is >= b*,
-//     in position order.
-//  3. topk_select (one workgroup per head, candidates only): radix digits
-//     20..10 and 9..0 on the candidates of bin b* give the exact K-th key T
-//     and how many rows with key == T to keep (`need`): chosen = key > T, or
-//     key == T among the first `need` such rows in position order. One
-//     ordered compaction writes the chosen rows in ascending order.
+//  2. topk_filter_select, P workgroups per head: every wave keeps the
+//     positions of its slice whose digit is >= b*, in position order, in the
+//     slice's own region of the candidate list. A workgroup then counts
+//     itself in the head's arrival counter; the one that arrives last (no
+//     workgroup ever waits for another) finishes the head:
+//  3. radix digits 20..10 and 9..0 on the candidates of bin b* give the exact
+//     K-th key T and how many rows with key == T to keep (`need`): chosen =
+//     key > T, or key == T among the first `need` such rows in position
+//     order. One ordered compaction writes the chosen rows in ascending
+//     order. The last workgroup also zeroes the histogram and the counter
+//     again, so they need no separate clearing pass per call.
 //  4. sparse_sv (many workgroups) computes softmax . V partials over slices
 //     of the chosen rows with fp32 accumulation; `combine` merges them.
 #pragma once
@@ -39,30 +41,7 @@ STDK_DEV float key2f(uint32_t k) {
 }
 
 constexpr int kSelThreads = 1024;
-constexpr size_t kSelStaticLds = 14 * 1024;  // static LDS of the select kernels, rounded up
-
-// ---------------------------------------------------------------------------
-// topk_filter: many workgroups per segment. Each wave scans its own slice of
-// positions in ascending order and writes the (key, position) pairs whose
-// first digit is >= b* into that slice's own region, plus a count. No
-// atomics: the regions concatenated in slice order are the candidate list
-// sorted by position.
-// ---------------------------------------------------------------------------
-struct FilterArgs {
-  const float* scores;        // [S][n_pad]
-  const uint32_t* hist;       // [S][2048]
-  Cand* list;                 // [S][n_pad]: slice j owns [j*slice, (j+1)*slice)
-  uint32_t* slice_cnt;        // [S][nslice]
-  int64_t n, n_pad;
-  int32_t K;
-  int32_t slice;              // positions per wave slice (multiple of 64)
-  int32_t nslice;             // slices per segment
-  int32_t pad_;
-  const int32_t* seg_active;  // [S] or null
-};
-
-constexpr int kFilterThreads = 256;
-constexpr int kFilterWaves = kFilterThreads / 64;
+constexpr size_t kSelStaticLds = 14 * 1024;  // static LDS of the select kernel, rounded up
 
 // The first-digit bin that holds the K-th largest key, found by one wave
 // straight from the global histogram (no LDS, no barrier): lane l holds the 32
@@ -112,65 +91,34 @@ STDK_DEV uint32_t first_digit_search(const u32x4 (&hv)[8], uint32_t need, uint32
   return (uint32_t)(kHistBins - 1 - (32 * L + k));
 }
 
-__global__ __launch_bounds__(kFilterThreads) void topk_filter(FilterArgs a) {
-  __shared__ uint32_t s_bstar;
-  const int64_t seg = blockIdx.y;
-  if (a.seg_active && a.seg_active[seg] == 0) return;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int js = min(blockIdx.x * kFilterWaves + w, a.nslice - 1);  // this wave's slice
-  const bool live = blockIdx.x * kFilterWaves + w < a.nslice;
-  const bool take_all = a.n <= a.K;
-  const float* sc = a.scores + seg * a.n_pad;
-  Cand* out = a.list + seg * a.n_pad + (int64_t)js * a.slice;
-  const int64_t p0 = (int64_t)js * a.slice;
-  const int64_t p1 = min(a.n, p0 + a.slice);
-  constexpr int FU = 16;  // loads in flight per lane
-  float v[FU];
-  auto load_batch = [&](int64_t pb) {
-#pragma unroll
-    for (int u = 0; u < FU; ++u) v[u] = sc[min(pb + 64 * u + lane, p1 - 1)];
-  };
-  // wave 0 requests the histogram first, then every wave its first batch of
-  // scores; wave 0's search waits on the histogram only
-  u32x4 hv[8];
-  if (w == 0) first_digit_load(a.hist + seg * kHistBins, hv);
-  load_batch(p0);
-  if (w == 0) {
-    const uint32_t bs = take_all ? 0u : first_digit_search(hv, (uint32_t)a.K);
-    if (lane == 0) s_bstar = bs;
-  }
-  __syncthreads();
-  if (!live) return;
-  const uint32_t bstar = s_bstar;
-  uint32_t cnt = 0;
-  for (int64_t pb = p0; pb < p1; pb += 64 * FU) {
-    if (pb != p0) load_batch(pb);
-#pragma unroll
-    for (int u = 0; u < FU; ++u) {
-      const int64_t p = pb + 64 * u + lane;
-      const uint32_t key = f2key(v[u]);
-      const bool take = p < p1 && (take_all || (key >> (32 - kHistBits)) >= bstar);
-      const uint64_t m = __ballot(take);
-      if (take) out[cnt + lane_rank(m)] = Cand{key, (int32_t)p};
-      cnt += (uint32_t)__popcll(m);
-    }
-  }
-  if (lane == 0) a.slice_cnt[seg * a.nslice + js] = cnt;
-}
-
 // ---------------------------------------------------------------------------
-// topk_select: one workgroup per segment, on the candidates only. Writes the
-// chosen rows (ascending) and their scores, and the index output.
+// topk_filter_select: P workgroups per segment filter the scores into the
+// candidate list; the last of them to arrive selects the head's K rows from
+// the candidates. Writes the chosen rows (ascending) and their scores, and
+// the index output.
+//
+// The workgroups of a segment may run on different XCDs, each with its own
+// L2. What they hand over (the candidates, the per-workgroup counts and the
+// second-digit histogram) is written and read only with agent-scope atomic
+// accesses, which are coherent across the XCDs (written through to, and
+// read from, the device's coherence point), so no cache-wide write-back or
+// invalidate is needed. A workgroup waits until all its accesses are
+// complete before it counts itself in; the last workgroup reads only after
+// it has seen the full count, so it observes every workgroup's writes.
 // ---------------------------------------------------------------------------
 struct SelectArgs {
-  uint32_t* hist;             // [S][2048]; read, then zeroed for the next call
-  const Cand* list;           // [S][n_pad]
-  const uint32_t* slice_cnt;  // [S][nslice]
+  const float* scores;        // [S][n_pad]
+  uint32_t* hist;             // [S][2048] first digit (the scan's counts); zeroed by the last workgroup
+  uint32_t* hist1;            // [S][2048] second digit of the candidates in bin b*; zero on entry and exit
+  uint32_t* done;             // [S][16]: word 0 counts the arrived workgroups; zero on entry and exit
+  Cand* list;                 // [S][n_pad]: workgroup x's candidates from position x * 16 * slice on
+  uint32_t* wg_cnt;           // [S][P] candidates per workgroup
   Cand* clist;                // [S][n_pad] contiguous copy when it does not fit in LDS
   int64_t n, n_pad;
   int32_t K;
-  int32_t slice, nslice;
+  int32_t slice;              // positions per wave: a multiple of 64, at most 64 * kFselLoads
   int32_t cache_cap;          // candidates that fit in the LDS copy
+  int32_t pad_;
   int32_t* sel_row;           // [S][K] chosen rows, ascending, -1 padded
   float* sel_z;               // [S][K] their scores
   int32_t* idx_out;           // [S][K] or null (copy of the chosen rows)
@@ -179,80 +127,75 @@ struct SelectArgs {
 };
 
 constexpr int kSelectWaves = kSelThreads / 64;
+static_assert(kSelThreads == 1024, "one thread per bin of the third digit");
+constexpr int kFselLoads = 16;  // score loads per lane: a wave's whole slice
+constexpr int kCtlWords = 16;   // control words per segment
 
-// The part of topk_select after the first digit, with the contiguous
-// candidate copy `cl` either in LDS (kLds) or in global memory. Keeping the
-// two cases in separate instantiations lets every access use its own address
-// space instead of generic (flat) accesses, which serialise on both counters.
-// `h1` (2048 bins) and `h2` (1024 bins) are zero on entry.
+STDK_DEV void store_agent(Cand* p, Cand c) {
+  const uint64_t v = (uint64_t)c.key | ((uint64_t)(uint32_t)c.pos << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+STDK_DEV Cand load_agent(const Cand* p) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<Cand*>(p)), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return Cand{(uint32_t)v, (int32_t)(uint32_t)(v >> 32)};
+}
+STDK_DEV void store_agent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+STDK_DEV uint32_t load_agent(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The last workgroup's part after the first two digits: the contiguous
+// candidate copy `cl` (in LDS when kLds, else in global memory; separate
+// instantiations keep every access in its own address space instead of
+// generic accesses, which serialise on both counters), the third digit
+// (bits 9..0) over the candidates whose top 22 bits are `pre22`, and the
+// ordered compaction. `pre` holds the workgroups' candidate offsets [P + 1];
+// `h2` (1024 bins) is zero on entry.
 template <bool kLds>
-STDK_DEV void select_rest(const SelectArgs& a, int64_t seg, uint32_t m, uint32_t b0, uint32_t need, bool take_all,
-                          const uint32_t* pre, Cand* cl, uint32_t* h1, uint32_t* h2, uint32_t* tmp, int* s_bin,
-                          uint32_t* s_beyond) {
+STDK_DEV void select_tail(const SelectArgs& a, int64_t seg, int P, int64_t span, uint32_t m, uint32_t pre22,
+                          uint32_t need, bool take_all, const uint32_t* pre, Cand* cl, uint32_t* h2,
+                          uint32_t* tmp, int* s_bin, uint32_t* s_beyond) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int ns = a.nslice;
   const int K = a.K;
   const Cand* lst = a.list + seg * a.n_pad;
 
-  // Contiguous copy in position order: wave wv copies slices wv, wv + 16,
-  // ..., SU of them per round. Every load is issued (clamped into the slice)
-  // before the first wait, and the results beyond a slice's count are
-  // dropped. The same pass counts digit 1 (bits 20..10) of the candidates in
-  // bin b0.
+  // Copy in position order: candidate i lives in the region of the last
+  // workgroup r with pre[r] <= i. All loads of a round are issued before the
+  // first is used.
   {
-    constexpr int SU = 8;
-    for (int j0 = wv; j0 < ns; j0 += kSelectWaves * SU) {
-      uint32_t cnt[SU], off[SU];
-      int64_t src[SU];
-      uint32_t mx = 0;
+    constexpr int CU = 4;
+    for (uint32_t base = 0; base < m; base += kSelThreads * CU) {
+      Cand c[CU];
 #pragma unroll
-      for (int u = 0; u < SU; ++u) {
-        const int j = j0 + u * kSelectWaves;
-        const int jc = min(j, ns - 1);
-        cnt[u] = j < ns ? pre[jc + 1] - pre[jc] : 0u;
-        off[u] = pre[jc];
-        src[u] = (int64_t)jc * a.slice;
-        mx = max(mx, cnt[u]);
+      for (int u = 0; u < CU; ++u) {
+        const uint32_t i = min(base + (uint32_t)(u * kSelThreads + tid), m - 1u);
+        int lo = 0, hi = P - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (pre[mid] <= i) lo = mid;
+          else hi = mid - 1;
+        }
+        c[u] = load_agent(lst + (int64_t)lo * span + (i - pre[lo]));
       }
-      for (uint32_t e0 = 0; e0 < mx; e0 += 64) {
-        const uint32_t e = e0 + lane;
-        Cand v[SU];
 #pragma unroll
-        for (int u = 0; u < SU; ++u) v[u] = lst[src[u] + min(e, cnt[u] > 0 ? cnt[u] - 1 : 0u)];
-#pragma unroll
-        for (int u = 0; u < SU; ++u) {
-          if (e < cnt[u]) {
-            cl[off[u] + e] = v[u];
-            if (!take_all && (v[u].key >> 21) == b0) atomicAdd(&h1[(v[u].key >> 10) & 0x7FFu], 1u);
-          }
+      for (int u = 0; u < CU; ++u) {
+        const uint32_t i = base + (uint32_t)(u * kSelThreads + tid);
+        if (i < m) {
+          cl[i] = c[u];
+          if (!take_all && (c[u].key >> 10) == pre22) atomicAdd(&h2[c[u].key & 0x3FFu], 1u);
         }
       }
     }
   }
   __syncthreads();
-  constexpr int U = 8;
   uint32_t Tk = 0;
   if (!take_all) {
-    if (wv == 0) find_bin_wave<kHistBins, true>(h1, need, s_bin, s_beyond);
-    __syncthreads();
-    const uint32_t b1 = (uint32_t)(*s_bin < 0 ? 0 : *s_bin);
-    need -= *s_beyond;
-    // digit 2 (bits 9..0) among the candidates with the first 22 bits found
-    const uint32_t pre01 = (b0 << 11) | b1;
-    for (uint32_t base = 0; base < m; base += kSelThreads * U) {
-      uint32_t kv[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) kv[u] = cl[min(base + (uint32_t)(u * kSelThreads + tid), m - 1u)].key;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const uint32_t i = base + (uint32_t)(u * kSelThreads + tid);
-        if (i < m && (kv[u] >> 10) == pre01) atomicAdd(&h2[kv[u] & 0x3FFu], 1u);
-      }
-    }
-    __syncthreads();
     if (wv == 0) find_bin_wave<1024, true>(h2, need, s_bin, s_beyond);
     __syncthreads();
-    Tk = (pre01 << 10) | (uint32_t)(*s_bin < 0 ? 0 : *s_bin);
+    Tk = (pre22 << 10) | (uint32_t)(*s_bin < 0 ? 0 : *s_bin);
     need -= *s_beyond;  // rows with key == Tk to keep, the first ones in position order
   }
 
@@ -265,6 +208,7 @@ STDK_DEV void select_rest(const SelectArgs& a, int64_t seg, uint32_t m, uint32_t
     // candidates [t*per, (t+1)*per), all read at once. One block scan of
     // (count > Tk, count == Tk) gives each thread its output offset: the
     // rows above Tk before it plus the ties before it that are kept.
+    constexpr int U = 8;
     const uint32_t per = (m + kSelThreads - 1) / kSelThreads;
     const uint32_t i0 = min(m, tid * per), i1 = min(m, i0 + per);
     uint32_t n_gt = 0, n_eq = 0;
@@ -312,21 +256,20 @@ STDK_DEV void select_rest(const SelectArgs& a, int64_t seg, uint32_t m, uint32_t
   } else {
     // Ordered compaction for more candidates (contiguous runs per thread
     // would conflict on LDS banks and scatter the stores): wave w owns
-    // candidates [w*SEG, (w+1)*SEG), read 64
-    // at a time with consecutive lanes on consecutive candidates. The waves'
-    // counts (above Tk, equal to Tk) give each wave its output offset: the
-    // rows above Tk before it plus the ties before it that are kept; inside a
-    // wave, ballots rank the ties and the taken rows, so consecutive lanes
-    // write consecutive slots.
+    // candidates [w*SEG, (w+1)*SEG), read 64 at a time with consecutive
+    // lanes on consecutive candidates. The waves' counts (above Tk, equal to
+    // Tk) give each wave its output offset: the rows above Tk before it plus
+    // the ties before it that are kept; inside a wave, ballots rank the ties
+    // and the taken rows, so consecutive lanes write consecutive slots.
     const uint32_t SEG = ((m + kSelectWaves - 1) / kSelectWaves + 63u) & ~63u;
     const uint32_t s0 = min(m, (uint32_t)wv * SEG), s1 = min(m, s0 + SEG);
     constexpr int CU = 4;  // chunks of 64 whose reads are issued together
     uint32_t cg = 0, ce = 0;
     for (uint32_t jb = s0; jb < s1; jb += 64 * CU) {
       uint32_t kv[CU];
-#pragma unroll
+  #pragma unroll
       for (int u = 0; u < CU; ++u) kv[u] = cl[min(jb + 64 * u + lane, s1 - 1)].key;
-#pragma unroll
+  #pragma unroll
       for (int u = 0; u < CU; ++u) {
         const bool valid = jb + 64 * u + lane < s1;
         cg += valid && (take_all || kv[u] > Tk);
@@ -341,7 +284,7 @@ STDK_DEV void select_rest(const SelectArgs& a, int64_t seg, uint32_t m, uint32_t
     }
     __syncthreads();
     uint32_t out = 0, eq_seen = 0, eq_all = 0;
-#pragma unroll
+  #pragma unroll
     for (int v = 0; v < kSelectWaves; ++v) {
       const uint32_t e = tmp[kSelectWaves + v];
       const uint32_t te = min(e, need > eq_all ? need - eq_all : 0u);
@@ -354,9 +297,9 @@ STDK_DEV void select_rest(const SelectArgs& a, int64_t seg, uint32_t m, uint32_t
     }
     for (uint32_t jb = s0; jb < s1; jb += 64 * CU) {
       Cand cv[CU];
-#pragma unroll
+  #pragma unroll
       for (int u = 0; u < CU; ++u) cv[u] = cl[min(jb + 64 * u + lane, s1 - 1)];
-#pragma unroll
+  #pragma unroll
       for (int u = 0; u < CU; ++u) {
         const bool valid = jb + 64 * u + lane < s1;
         const bool gt = valid && (take_all || cv[u].key > Tk);
@@ -383,72 +326,163 @@ STDK_DEV void select_rest(const SelectArgs& a, int64_t seg, uint32_t m, uint32_t
   }
 }
 
-// Dynamic LDS: pre[nslice + 1] (slice prefix) then, if the candidates fit,
-// their contiguous copy (position order); else the copy goes to clist.
-__global__ __launch_bounds__(kSelThreads) void topk_select(SelectArgs a) {
+// Grid (P, S), kSelThreads threads: workgroup x of segment s filters the
+// positions [x * 16 * slice, (x + 1) * 16 * slice), one slice per wave.
+// Dynamic LDS (last workgroup): pre[P + 1] (the workgroups' candidate
+// offsets) then, if the candidates fit, their contiguous copy (position
+// order); else the copy goes to clist.
+__global__ __launch_bounds__(kSelThreads) void topk_filter_select(SelectArgs a) {
   extern __shared__ uint32_t dyn[];
-  __shared__ uint32_t h1[kHistBins];  // digit 1
-  __shared__ uint32_t h2[1024];       // digit 2
-  __shared__ uint32_t tmp[2 * (kSelThreads / 64) + 2];
+  __shared__ uint32_t h1[kHistBins];  // second digit, this workgroup's candidates in bin b*
+  __shared__ uint32_t h2[1024];       // third digit
+  __shared__ uint32_t tmp[2 * kSelectWaves + 2];
+  __shared__ uint32_t s_wc[kSelectWaves];
   __shared__ int s_bin;
-  __shared__ uint32_t s_beyond;
-  const int64_t seg = blockIdx.x;
+  __shared__ uint32_t s_beyond, s_b1, s_beyond1, s_last;
+  const int64_t seg = blockIdx.y;
   if (a.seg_active && a.seg_active[seg] == 0) return;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int ns = a.nslice;
+  const int P = (int)gridDim.x;
   const int K = a.K;
   const bool take_all = a.n <= K;
-  uint32_t* pre = dyn;
+  uint32_t* hg = a.hist + seg * kHistBins;
+  uint32_t* h1g = a.hist1 + seg * kHistBins;
+  const int64_t span = (int64_t)kSelectWaves * a.slice;
 
-  // Wave 0 finds the first digit's bin straight from the scan's histogram,
-  // in registers, then zeroes the global copy for the next call (the scan
-  // and the filter are done with it). Wave 1 builds the slice prefix
-  // (ns <= 4096). Every thread clears the other digits' histograms.
-  if (wv == 0) {
+  // 1. Filter. Wave 0 requests the histogram first, then every wave its
+  // whole slice of scores; wave 0 finds b* (the first digit's bin of the
+  // K-th largest key) while they arrive. The candidates (first digit >= b*)
+  // go to this workgroup's region in position order: the waves' counts give
+  // each wave its offset, ballots rank the lanes. The candidates in bin b*
+  // are counted by their second digit (bits 20..10) in LDS; the non-zero
+  // bins are then added to the segment's global histogram, after the
+  // candidate stores so that those are not queued behind them.
+  {
+    const float* sc = a.scores + seg * a.n_pad;
+    const int64_t p0 = (int64_t)blockIdx.x * span + (int64_t)wv * a.slice;
+    const int64_t p1 = min(a.n, p0 + a.slice);
+    const int64_t plast = max((int64_t)0, p1 - 1);  // loads past the slice are clamped into the scores
+    float v[kFselLoads];
     u32x4 hv[8];
-    uint32_t* hg = a.hist + seg * kHistBins;
-    first_digit_load(hg, hv);
-    uint32_t beyond = 0;
-    const uint32_t bin = take_all ? 0u : first_digit_search(hv, (uint32_t)K, &beyond);
-    if (lane == 0) {
-      s_bin = (int)bin;
-      s_beyond = beyond;
+    if (wv == 0 && !take_all) first_digit_load(hg, hv);
+#pragma unroll
+    for (int u = 0; u < kFselLoads; ++u) v[u] = sc[min(p0 + 64 * u + lane, plast)];
+#pragma unroll
+    for (int u = 0; u < kHistBins / kSelThreads; ++u) h1[u * kSelThreads + tid] = 0u;
+    if (wv == 0) {
+      uint32_t beyond = 0;
+      const uint32_t bin = take_all ? 0u : first_digit_search(hv, (uint32_t)K, &beyond);
+      if (lane == 0) {
+        s_bin = (int)bin;
+        s_beyond = beyond;
+      }
+    }
+    __syncthreads();
+    const uint32_t b0 = (uint32_t)s_bin;
+    uint32_t key[kFselLoads];
+    uint64_t tm[kFselLoads];
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int u = 0; u < kFselLoads; ++u) {
+      const int64_t p = p0 + 64 * u + lane;
+      key[u] = f2key(v[u]);
+      const uint32_t d0 = key[u] >> (32 - kHistBits);
+      const bool take = p < p1 && (take_all || d0 >= b0);
+      tm[u] = __ballot(take);
+      cnt += (uint32_t)__popcll(tm[u]);
+      if (take && !take_all && d0 == b0) atomicAdd(&h1[(key[u] >> 10) & 0x7FFu], 1u);
+    }
+    if (lane == 0) s_wc[wv] = cnt;
+    __syncthreads();
+    uint32_t off = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kSelectWaves; ++w) {
+      const uint32_t c = s_wc[w];
+      off += w < wv ? c : 0u;
+      tot += c;
+    }
+    Cand* out = a.list + seg * a.n_pad + (int64_t)blockIdx.x * span;
+#pragma unroll
+    for (int u = 0; u < kFselLoads; ++u) {
+      if ((tm[u] >> lane) & 1ull) store_agent(out + off + lane_rank(tm[u]), Cand{key[u], (int32_t)(p0 + 64 * u + lane)});
+      off += (uint32_t)__popcll(tm[u]);
+    }
+    if (tid == 0) store_agent(a.wg_cnt + seg * P + blockIdx.x, tot);
+    if (!take_all) {
+#pragma unroll
+      for (int u = 0; u < kHistBins / kSelThreads; ++u) {
+        const uint32_t c = h1[u * kSelThreads + tid];
+        if (c != 0u) atomicAdd(&h1g[u * kSelThreads + tid], c);
+      }
+    }
+  }
+
+  // 2. Arrival: once every wave's writes and histogram adds are complete,
+  // thread 0 counts the workgroup in. The workgroup that takes the count to
+  // P finishes the segment; the others are done.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t before = __hip_atomic_fetch_add(a.done + seg * kCtlWords, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = before + 1 == (uint32_t)P ? 1u : 0u;
+  }
+  __syncthreads();
+  if (s_last == 0u) return;
+
+  // 3. Select. Wave 0 finds the second digit's bin from the global
+  // histogram, then zeroes both histograms and the counter for the next call
+  // (every workgroup of the segment read the first before it arrived, and
+  // its adds to the second are complete); wave 1 builds the workgroups'
+  // candidate offsets; every thread clears the third digit's histogram.
+  uint32_t* pre = dyn;
+  if (wv == 0) {
+    if (!take_all) {
+      const uint32_t* base = h1g + (kHistBins - 32 - 32 * lane);
+      u32x4 hv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        hv[i].x = load_agent(base + 4 * i);
+        hv[i].y = load_agent(base + 4 * i + 1);
+        hv[i].z = load_agent(base + 4 * i + 2);
+        hv[i].w = load_agent(base + 4 * i + 3);
+      }
+      uint32_t beyond1 = 0;
+      const uint32_t b1 = first_digit_search(hv, (uint32_t)K - s_beyond, &beyond1);
+      if (lane == 0) {
+        s_b1 = b1;
+        s_beyond1 = beyond1;
+      }
     }
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(hg + (kHistBins - 32 - 32 * lane) + 4 * i) = z;
+    for (int i = 0; i < 8; ++i) {
+      *reinterpret_cast<u32x4*>(hg + (kHistBins - 32 - 32 * lane) + 4 * i) = z;
+      *reinterpret_cast<u32x4*>(h1g + (kHistBins - 32 - 32 * lane) + 4 * i) = z;
+    }
+    if (lane == 0) a.done[seg * kCtlWords] = 0u;
   } else if (wv == 1) {
     uint32_t run = 0;
-    for (int j0 = 0; j0 < ns; j0 += 256) {
-      uint32_t c4[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int j = j0 + u * 64 + lane;
-        c4[u] = j < ns ? a.slice_cnt[seg * ns + j] : 0u;
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int j = j0 + u * 64 + lane;
-        const uint32_t incl = wave_incl_scan(c4[u]);
-        if (j < ns) pre[j] = run + incl - c4[u];
-        run += __shfl(incl, 63, 64);
-      }
+    for (int j0 = 0; j0 < P; j0 += 64) {
+      const int j = j0 + lane;
+      const uint32_t c = j < P ? load_agent(a.wg_cnt + seg * P + j) : 0u;
+      const uint32_t incl = wave_incl_scan(c);
+      if (j < P) pre[j] = run + incl - c;
+      run += __shfl(incl, 63, 64);
     }
-    if (lane == 0) pre[ns] = run;
+    if (lane == 0) pre[P] = run;
   }
-#pragma unroll
-  for (int u = 0; u < kHistBins / kSelThreads; ++u) h1[u * kSelThreads + tid] = 0u;
-  if (tid < 1024) h2[tid] = 0u;
+  h2[tid] = 0u;
   __syncthreads();
-  const uint32_t m = pre[ns];
-  // digit 0 (bits 31..21)
+  const uint32_t m = pre[P];
   const uint32_t b0 = take_all ? 0u : (uint32_t)s_bin;
-  const uint32_t need = take_all ? (uint32_t)K : (uint32_t)K - s_beyond;
+  const uint32_t b1 = take_all ? 0u : s_b1;
+  const uint32_t need = take_all ? (uint32_t)K : (uint32_t)K - s_beyond - s_beyond1;
+  const uint32_t pre22 = (b0 << 11) | b1;
   if (m <= (uint32_t)a.cache_cap) {
-    Cand* cl = reinterpret_cast<Cand*>(dyn + ((ns + 2) & ~1));
-    select_rest<true>(a, seg, m, b0, need, take_all, pre, cl, h1, h2, tmp, &s_bin, &s_beyond);
+    Cand* cl = reinterpret_cast<Cand*>(dyn + ((P + 2) & ~1));
+    select_tail<true>(a, seg, P, span, m, pre22, need, take_all, pre, cl, h2, tmp, &s_bin, &s_beyond);
   } else {
-    select_rest<false>(a, seg, m, b0, need, take_all, pre, a.clist + seg * a.n_pad, h1, h2, tmp, &s_bin,
+    select_tail<false>(a, seg, P, span, m, pre22, need, take_all, pre, a.clist + seg * a.n_pad, h2, tmp, &s_bin,
                        &s_beyond);
   }
 }

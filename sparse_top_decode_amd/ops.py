@@ -56,6 +56,11 @@ def _ranges_arr(ranges: Sequence[Tuple[int, int]]):
     return arr, len(ranges)
 
 
+# Bytes per query head of the counter region at the start of every decode
+# workspace (two radix histograms and an arrival counter), zero between calls.
+COUNTER_BYTES_PER_HEAD = 16448
+
+
 def new_workspace(nbytes: int, device) -> torch.Tensor:
     """A zero-filled workspace buffer (the library keeps its counters zero
     between calls, so it must start that way)."""

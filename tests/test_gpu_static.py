@@ -165,7 +165,7 @@ def test_graph_replays_match_eager(ops):
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         step()
-    counters = w.B * w.H_q * 8192
+    counters = w.B * w.H_q * ops.COUNTER_BYTES_PER_HEAD
     for rep in range(4):
         for t in (idx, o, lse):
             t.fill_(-7)

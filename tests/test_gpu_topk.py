@@ -37,6 +37,19 @@ def test_c1_exact_fp32(ops):
     assert np.array_equal(idx, want["idx"])
 
 
+@pytest.mark.parametrize("K", [64, 5000])
+def test_long_head_filter_batches(ops, K):
+    """One head over 1.2M rows (fp32): more positions than 64 filter
+    workgroups take in one pass, so each takes several batches; the index
+    set equals the oracle's, o/lse to the fp32 bar."""
+    log(f"case c1 fp32 L=1200000 K={K} (several filter batches per workgroup)")
+    w = make_workload(1, L=1_200_000)
+    idx, o, lse = run(ops, w, w.ranges, K)
+    want = ref.topk_attn_decode(w.q, w.k, w.v, w.ranges, K, w.scale)
+    check_heads(w, [(0, 0)], idx, o, lse, w.ranges, K, fp32=True, label=f"c1 L=1.2M K={K}")
+    assert np.array_equal(idx, want["idx"])
+
+
 @pytest.mark.parametrize("L,K", [(8192, 2048), (8192, 97), (20000, 1), (3000, 2047)])
 def test_c2_shape_reduced(ops, L, K):
     """Llama-3-8B head layout (32 q / 8 KV, bf16) at reduced length: the
@@ -227,7 +240,7 @@ def test_nan_query_propagates(ops, K):
 
 def test_workspace_reuse_counters_return_to_zero(ops):
     """One workspace serves several calls of one layout with different n and
-    K: each call leaves the histogram counters (the first B*H_q*8 KiB) zero,
+    K: each call leaves the counters (the first B*H_q*16448 bytes) zero,
     and every result equals the result with a fresh zero-filled workspace."""
     log("case workspace reuse c2 layout L=20000")
     w = make_workload(2, L=20000)
@@ -236,7 +249,7 @@ def test_workspace_reuse_counters_return_to_zero(ops):
     lay = ops.make_layout(k, w.H_q)
     n_full = sum(e - b for b, e in w.ranges)
     ws = ops.new_workspace(ops.topk_attn_decode_workspace_size(lay, n_full, 2048), q.device)
-    counters = w.B * w.H_q * 8192
+    counters = w.B * w.H_q * ops.COUNTER_BYTES_PER_HEAD
     cases = [(w.ranges, 2048), ([(0, 5000)], 100), (w.ranges, 7), ([(100, 300), (9000, 19000)], 512)]
     for ranges, K in cases:
         got = ops.topk_attn_decode(q, k, v, ranges, K, w.scale, workspace=ws, layout=lay)
@@ -263,7 +276,7 @@ def test_workspace_shared_with_multi_query(ops):
     got = ops.topk_attn_decode(q, k, v, w.ranges, 500, w.scale, workspace=ws, layout=lay)
     fresh = ops.topk_attn_decode(q, k, v, w.ranges, 500, w.scale, layout=lay)
     torch.cuda.synchronize()
-    assert int(torch.count_nonzero(ws[:w.B * w.H_q * 8192]).item()) == 0
+    assert int(torch.count_nonzero(ws[:w.B * w.H_q * ops.COUNTER_BYTES_PER_HEAD]).item()) == 0
     for x, y in zip(got, fresh):
         assert torch.equal(x, y)
 
@@ -271,7 +284,7 @@ def test_workspace_shared_with_multi_query(ops):
 @pytest.mark.parametrize("entry", ["topk", "static", "retopk"])
 def test_failed_call_leaves_workspace_usable(ops, entry):
     """A launch failure forced from the host right after the scan (the
-    filter is never enqueued) leaves the workspace's counters non-zero; the
+    filter-select is never enqueued) leaves the workspace's counters non-zero; the
     call returns STDK_EHIP, and the next call on the same buffer repairs them
     first: its results equal those of a fresh buffer."""
     from sparse_top_decode_amd.native import STDK_EHIP, StdkError
@@ -280,7 +293,7 @@ def test_failed_call_leaves_workspace_usable(ops, entry):
     k, v = dev_kv(w)
     lay = ops.make_layout(k, w.H_q)
     n = sum(e - b for b, e in w.ranges)
-    counters = w.B * w.H_q * 8192
+    counters = w.B * w.H_q * ops.COUNTER_BYTES_PER_HEAD
     if entry == "retopk":
         rt = ops.Retopk(k, w.H_q, top_k=300, cache_cap=4, top_r=2, recent=8, tau=0.5, refresh=1, scale=w.scale)
         ws = rt.workspace
