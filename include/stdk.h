@@ -407,6 +407,21 @@ int32_t stdk_version(void);        /* STDK_VERSION */
  * disarms. STDK_EINVAL below -1. */
 int32_t stdk_inject_launch_failure(int32_t after_launches);
 
+/* Measurement aid: the plain HBM read rate of the key scan's partition.
+ * Reads every byte of n_groups regions once: region g is group_bytes bytes
+ * from base + g * group_stride_bytes, streamed by wg_per_group workgroups
+ * of 512 threads that each take an equal contiguous share (16-byte loads,
+ * two sets of four in flight), the way k_scan splits a KV head's rows over
+ * its workgroups. Nothing is written except, in a case that does not occur
+ * for real data (an XOR of all words equal to a fixed constant), one word
+ * of `sink` (4 bytes of device memory). Its duration (kernel family
+ * "hbm_read") is the ceiling the scan's HBM rate is compared against.
+ * base 16-byte aligned, group_bytes a positive multiple of 16, n_groups and
+ * wg_per_group >= 1 with n_groups * wg_per_group <= 2^31 - 1: else
+ * STDK_EINVAL. */
+int32_t stdk_hbm_read(const void* base, int64_t group_stride_bytes, int32_t n_groups, int64_t group_bytes,
+                      int32_t wg_per_group, uint32_t* sink, void* stream);
+
 /* Kernel timing: while enabled, every kernel the library enqueues (or only
  * the kernel family `only`, if not NULL) is launched with a pair of
  * hipEvents attached to its dispatch (hipExtLaunchKernelGGL start/stop
@@ -415,11 +430,11 @@ int32_t stdk_inject_launch_failure(int32_t after_launches);
  * enabling, not on the hot path). stdk_profile_read waits for the recorded
  * events and returns, for the kernel family `name`, the summed duration in
  * milliseconds and the launch count. Families: "k_scan",
- * "topk_filter", "topk_select", "sparse_sv", "dense_attn", "combine",
+ * "topk_filter_select", "sparse_sv", "dense_attn", "combine",
  * "attn_merge", "fill_empty", "retopk_select", "retopk_rerank",
  * "retopk_rerank_select", "retopk_init", "retopk_vote",
  * "mq_blockmax", "mq_threshold", "mq_collect", "mq_select", "mq_fill",
- * "k_quantize".
+ * "k_quantize", "hbm_read".
  * Unknown names return STDK_EINVAL. */
 int32_t stdk_profile_enable(int32_t capacity, const char* only);
 int32_t stdk_profile_disable(void);

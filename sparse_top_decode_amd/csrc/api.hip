@@ -59,13 +59,14 @@ int32_t ok() {
 enum KernelId {
   KID_SCAN, KID_SELECT, KID_SV, KID_DENSE, KID_COMBINE, KID_MERGE, KID_FILL,
   KID_RT_SELECT, KID_RT_RERANK, KID_RT_RSEL, KID_RT_INIT, KID_MQ_BLOCKMAX, KID_MQ_THRESH,
-  KID_MQ_COLLECT, KID_MQ_SELECT, KID_MQ_FILL, KID_RT_VOTE, KID_Q8_QUANT, KID_COUNT
+  KID_MQ_COLLECT, KID_MQ_SELECT, KID_MQ_FILL, KID_RT_VOTE, KID_Q8_QUANT, KID_READ, KID_COUNT
 };
 const char* const kKernelNames[KID_COUNT] = {
     "k_scan",        "topk_filter_select",             "sparse_sv",
     "dense_attn",  "combine",       "attn_merge",    "fill_empty",           "retopk_select",
     "retopk_rerank", "retopk_rerank_select", "retopk_init", "mq_blockmax",
-    "mq_threshold",  "mq_collect",    "mq_select",     "mq_fill",       "retopk_vote",   "k_quantize"};
+    "mq_threshold",  "mq_collect",    "mq_select",     "mq_fill",       "retopk_vote",   "k_quantize",
+    "hbm_read"};
 
 struct Profiler {
   std::mutex mu;
@@ -326,7 +327,7 @@ constexpr int64_t kFselTargetWg = 256;
 // n positions take part in the top-K; n_extra more (a static row set) are
 // scored by the same scan and appended whole to every chosen-row list.
 struct TopkWs {
-  int64_t S, n, n_extra, n_pad, K, ksel, nsplit, slice, wg;
+  int64_t S, n, n_extra, n_pad, K, ksel, nsplit, slice, nb, wg;
   size_t hist, hist1, done, counters, scores, list, clist, wg_cnt, sel_row, sel_z, part, total;
 };
 
@@ -340,14 +341,15 @@ TopkWs topk_ws(int64_t S, int64_t n, int64_t K, int64_t n_extra = 0) {
   w.K = K;
   w.ksel = K + n_extra;
   w.nsplit = cdiv(w.ksel, kSvRows);
-  // filter-select: P workgroups per segment (at least 64 positions per
-  // wave), 16 wave slices of at most 64 * kFselLoads positions each
+  // filter-select: about one workgroup per CU over the grid (P per
+  // segment, each with at least 64 positions per wave), each taking nb
+  // batches of 16 wave slices of at most 64 * kFselLoads positions
   constexpr int64_t WV = kSelectWaves;
   constexpr int64_t kMaxSlice = 64 * kFselLoads;
-  int64_t wg = std::max(cdiv(kFselTargetWg, S), cdiv(n1, kMaxSlice * WV));
-  wg = std::max<int64_t>(1, std::min(wg, cdiv(n1, 64 * WV)));
-  w.slice = rup(cdiv(n1, wg * WV), 64);
-  w.wg = cdiv(n1, WV * w.slice);
+  const int64_t wg = std::max<int64_t>(1, std::min(cdiv(kFselTargetWg, S), cdiv(n1, 64 * WV)));
+  w.nb = cdiv(n1, wg * WV * kMaxSlice);
+  w.slice = rup(cdiv(n1, wg * WV * w.nb), 64);
+  w.wg = cdiv(n1, w.nb * WV * w.slice);
   w.hist = 0;
   w.hist1 = (size_t)S * kHistBins * 4;
   w.done = (size_t)S * 2 * kHistBins * 4;
@@ -532,6 +534,7 @@ int32_t run_exact_select(const Geo& g, const TopkWs& w, char* ws, const float* q
     a.n_pad = w.n_pad;
     a.K = (int32_t)w.K;
     a.slice = (int32_t)w.slice;
+    a.nb = (int32_t)w.nb;
     a.sel_row = (int32_t*)(ws + w.sel_row);
     a.sel_z = (float*)(ws + w.sel_z);
     a.idx_out = idx_out;
@@ -1420,6 +1423,57 @@ size_t retopk_state_size(const stdk_layout* lay, const retopk_params* p) {
   if (check_layout(lay) != STDK_OK || !p || p->top_k < 1 || p->cache_cap < 1) return 0;
   const size_t S = (size_t)geo_of(lay).S, C = (size_t)p->cache_cap, K = (size_t)p->top_k;
   return al256(S * C * kHeadDim * 4) + al256(S * C * K * 4) + al256(S * 4) + al256(S * 4);
+}
+
+// ---------------------------------------------------------------------------
+// plain-read reference: region g of n_groups, workgroup blk of wpg streams
+// bytes [blk * share, min(group_bytes, (blk + 1) * share)) of it
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(512) void hbm_read(const char* base, int64_t stride, int64_t group_bytes, int64_t share,
+                                                int32_t wpg, uint32_t* sink) {
+  const int grp = blockIdx.x / wpg, blk = blockIdx.x % wpg;
+  const char* p = base + (int64_t)grp * stride;
+  const int64_t b0 = (int64_t)blk * share, b1 = min(group_bytes, b0 + share);
+  if (b0 >= b1) return;
+  constexpr int64_t kStep = 512 * 16;  // one 16-byte load per thread
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  u32x4 v[2][4];
+  int64_t off = b0 + (int64_t)threadIdx.x * 16;
+  // loads past the share are clamped onto its last 16 bytes
+#pragma unroll
+  for (int u = 0; u < 4; ++u) v[0][u] = load16(p + min(off + u * kStep, b1 - 16));
+  for (; off < b1; off += 8 * kStep) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[1][u] = load16(p + min(off + (4 + u) * kStep, b1 - 16));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc ^= v[0][u];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[0][u] = load16(p + min(off + (8 + u) * kStep, b1 - 16));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc ^= v[1][u];
+  }
+  if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x9E3779B9u) sink[0] = acc.x;
+}
+
+int32_t stdk_hbm_read(const void* base, int64_t group_stride_bytes, int32_t n_groups, int64_t group_bytes,
+                      int32_t wg_per_group, uint32_t* sink, void* stream) {
+  STDK_TRY(check_ptr(base, "base", 16));
+  STDK_TRY(check_ptr(sink, "sink", 4));
+  if (n_groups < 1 || wg_per_group < 1) return fail(STDK_EINVAL, "n_groups %d, wg_per_group %d", n_groups, wg_per_group);
+  if ((int64_t)n_groups * wg_per_group > INT32_MAX) return fail(STDK_EINVAL, "too many workgroups");
+  if (group_bytes < 16 || group_bytes % 16) return fail(STDK_EINVAL, "group_bytes %lld", (long long)group_bytes);
+  if (group_stride_bytes % 16) return fail(STDK_EINVAL, "group_stride_bytes %lld", (long long)group_stride_bytes);
+  const int64_t share = rup(cdiv(group_bytes, wg_per_group), 16);
+  hipStream_t s = (hipStream_t)stream;
+  const dim3 grid((unsigned)(n_groups * wg_per_group));
+  STDK_TRY(launch(KID_READ, s, [&](hipEvent_t e0, hipEvent_t e1) {
+    STDK_LAUNCH(hbm_read, grid, dim3(512), 0, s, (const char*)base, group_stride_bytes, group_bytes, share,
+                wg_per_group, sink);
+  }));
+  return ok();
 }
 
 int32_t stdk_inject_launch_failure(int32_t after_launches) {

@@ -239,6 +239,32 @@ STDK_DEV void find_bin_wave(const uint32_t* hist, uint32_t need, int* bin, uint3
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Agent-scope (device-wide) relaxed atomic loads and stores: coherent across
+// the XCDs, whose L2 caches are not, without a cache-wide fence. Used for
+// what one workgroup hands to another inside a kernel; the writer waits
+// until its stores are complete before it signals (an atomic counter), and
+// the reader issues its loads only after it has seen the signal.
+STDK_DEV void store_agent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+STDK_DEV uint32_t load_agent(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Thread 0 counts the workgroup in at `counter` once every wave's memory
+// accesses are complete; true in every thread of the workgroup that brings
+// the count to `total` (which then resets the counter for the next call).
+STDK_DEV bool arrive_last(uint32_t* counter, uint32_t total, uint32_t* s_flag) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t before = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_flag = before + 1 == total ? 1u : 0u;
+    if (before + 1 == total) store_agent(counter, 0u);
+  }
+  __syncthreads();
+  return *s_flag != 0u;
+}
+
 STDK_DEV u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
 }  // namespace stdk

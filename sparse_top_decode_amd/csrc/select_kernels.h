@@ -110,15 +110,15 @@ struct SelectArgs {
   const float* scores;        // [S][n_pad]
   uint32_t* hist;             // [S][2048] first digit (the scan's counts); zeroed by the last workgroup
   uint32_t* hist1;            // [S][2048] second digit of the candidates in bin b*; zero on entry and exit
-  uint32_t* done;             // [S][16]: word 0 counts the arrived workgroups; zero on entry and exit
-  Cand* list;                 // [S][n_pad]: workgroup x's candidates from position x * 16 * slice on
+  uint32_t* done;             // [S][kCtlWords]: word 0 counts the arrived workgroups; zero on entry and exit
+  Cand* list;                 // [S][n_pad]: workgroup x's candidates from position x * nb * 16 * slice on
   uint32_t* wg_cnt;           // [S][P] candidates per workgroup
   Cand* clist;                // [S][n_pad] contiguous copy when it does not fit in LDS
   int64_t n, n_pad;
   int32_t K;
-  int32_t slice;              // positions per wave: a multiple of 64, at most 64 * kFselLoads
+  int32_t slice;              // positions per wave and batch: a multiple of 64, at most 64 * kFselLoads
+  int32_t nb;                 // batches per workgroup
   int32_t cache_cap;          // candidates that fit in the LDS copy
-  int32_t pad_;
   int32_t* sel_row;           // [S][K] chosen rows, ascending, -1 padded
   float* sel_z;               // [S][K] their scores
   int32_t* idx_out;           // [S][K] or null (copy of the chosen rows)
@@ -139,12 +139,6 @@ STDK_DEV Cand load_agent(const Cand* p) {
   const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<Cand*>(p)), __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
   return Cand{(uint32_t)v, (int32_t)(uint32_t)(v >> 32)};
-}
-STDK_DEV void store_agent(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-STDK_DEV uint32_t load_agent(const uint32_t* p) {
-  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The last workgroup's part after the first two digits: the contiguous
@@ -327,7 +321,8 @@ STDK_DEV void select_tail(const SelectArgs& a, int64_t seg, int P, int64_t span,
 }
 
 // Grid (P, S), kSelThreads threads: workgroup x of segment s filters the
-// positions [x * 16 * slice, (x + 1) * 16 * slice), one slice per wave.
+// positions [x * span, (x + 1) * span), span = nb * 16 * slice; in batch b,
+// wave w takes the slice at x * span + (b * 16 + w) * slice.
 // Dynamic LDS (last workgroup): pre[P + 1] (the workgroups' candidate
 // offsets) then, if the candidates fit, their contiguous copy (position
 // order); else the copy goes to clist.
@@ -336,7 +331,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_filter_select(SelectArgs a) 
   __shared__ uint32_t h1[kHistBins];  // second digit, this workgroup's candidates in bin b*
   __shared__ uint32_t h2[1024];       // third digit
   __shared__ uint32_t tmp[2 * kSelectWaves + 2];
-  __shared__ uint32_t s_wc[kSelectWaves];
+  __shared__ uint32_t s_wc[2][kSelectWaves];
   __shared__ int s_bin;
   __shared__ uint32_t s_beyond, s_b1, s_beyond1, s_last;
   const int64_t seg = blockIdx.y;
@@ -347,26 +342,32 @@ __global__ __launch_bounds__(kSelThreads) void topk_filter_select(SelectArgs a) 
   const bool take_all = a.n <= K;
   uint32_t* hg = a.hist + seg * kHistBins;
   uint32_t* h1g = a.hist1 + seg * kHistBins;
-  const int64_t span = (int64_t)kSelectWaves * a.slice;
+  const int64_t span = (int64_t)a.nb * kSelectWaves * a.slice;
 
-  // 1. Filter. Wave 0 requests the histogram first, then every wave its
-  // whole slice of scores; wave 0 finds b* (the first digit's bin of the
-  // K-th largest key) while they arrive. The candidates (first digit >= b*)
-  // go to this workgroup's region in position order: the waves' counts give
-  // each wave its offset, ballots rank the lanes. The candidates in bin b*
-  // are counted by their second digit (bits 20..10) in LDS; the non-zero
-  // bins are then added to the segment's global histogram, after the
-  // candidate stores so that those are not queued behind them.
+  // 1. Filter, in nb batches of 16 wave slices. Wave 0 requests the
+  // histogram first, then every wave the scores of its first slice; wave 0
+  // finds b* (the first digit's bin of the K-th largest key) while they
+  // arrive. The candidates (first digit >= b*) go to this workgroup's region
+  // in position order: the waves' counts give each wave its offset, ballots
+  // rank the lanes. The candidates in bin b* are counted by their second
+  // digit (bits 20..10) in LDS; the non-zero bins are then added to the
+  // segment's global histogram, after the candidate stores so that those are
+  // not queued behind them. A batch's loads are issued after the previous
+  // batch's stores: every workgroup of the grid streams at once, which keeps
+  // the memory system busy without deeper pipelining inside one.
   {
     const float* sc = a.scores + seg * a.n_pad;
-    const int64_t p0 = (int64_t)blockIdx.x * span + (int64_t)wv * a.slice;
-    const int64_t p1 = min(a.n, p0 + a.slice);
-    const int64_t plast = max((int64_t)0, p1 - 1);  // loads past the slice are clamped into the scores
+    Cand* out = a.list + seg * a.n_pad + (int64_t)blockIdx.x * span;
     float v[kFselLoads];
+    auto load_batch = [&](int bt) {
+      const int64_t p0 = (int64_t)blockIdx.x * span + ((int64_t)bt * kSelectWaves + wv) * a.slice;
+      const int64_t plast = max((int64_t)0, min(a.n, p0 + a.slice) - 1);  // clamped into the scores
+#pragma unroll
+      for (int u = 0; u < kFselLoads; ++u) v[u] = sc[min(p0 + 64 * u + lane, plast)];
+    };
     u32x4 hv[8];
     if (wv == 0 && !take_all) first_digit_load(hg, hv);
-#pragma unroll
-    for (int u = 0; u < kFselLoads; ++u) v[u] = sc[min(p0 + 64 * u + lane, plast)];
+    load_batch(0);
 #pragma unroll
     for (int u = 0; u < kHistBins / kSelThreads; ++u) h1[u * kSelThreads + tid] = 0u;
     if (wv == 0) {
@@ -379,35 +380,45 @@ __global__ __launch_bounds__(kSelThreads) void topk_filter_select(SelectArgs a) 
     }
     __syncthreads();
     const uint32_t b0 = (uint32_t)s_bin;
-    uint32_t key[kFselLoads];
-    uint64_t tm[kFselLoads];
-    uint32_t cnt = 0;
+    uint32_t written = 0;
+    for (int bt = 0;;) {
+      const int64_t p0 = (int64_t)blockIdx.x * span + ((int64_t)bt * kSelectWaves + wv) * a.slice;
+      const int64_t p1 = min(a.n, p0 + a.slice);
+      uint32_t key[kFselLoads];
+      uint64_t tm[kFselLoads];
+      uint32_t cnt = 0;
 #pragma unroll
-    for (int u = 0; u < kFselLoads; ++u) {
-      const int64_t p = p0 + 64 * u + lane;
-      key[u] = f2key(v[u]);
-      const uint32_t d0 = key[u] >> (32 - kHistBits);
-      const bool take = p < p1 && (take_all || d0 >= b0);
-      tm[u] = __ballot(take);
-      cnt += (uint32_t)__popcll(tm[u]);
-      if (take && !take_all && d0 == b0) atomicAdd(&h1[(key[u] >> 10) & 0x7FFu], 1u);
-    }
-    if (lane == 0) s_wc[wv] = cnt;
-    __syncthreads();
-    uint32_t off = 0, tot = 0;
+      for (int u = 0; u < kFselLoads; ++u) {
+        const int64_t p = p0 + 64 * u + lane;
+        key[u] = f2key(v[u]);
+        const uint32_t d0 = key[u] >> (32 - kHistBits);
+        const bool take = p < p1 && (take_all || d0 >= b0);
+        tm[u] = __ballot(take);
+        cnt += (uint32_t)__popcll(tm[u]);
+        if (take && !take_all && d0 == b0) atomicAdd(&h1[(key[u] >> 10) & 0x7FFu], 1u);
+      }
+      // the counts alternate between two arrays, so one barrier per batch
+      // suffices: a batch's array is rewritten two batches later, after
+      // every wave has passed the barrier between
+      if (lane == 0) s_wc[bt & 1][wv] = cnt;
+      __syncthreads();
+      uint32_t off = written, tot = 0;
 #pragma unroll
-    for (int w = 0; w < kSelectWaves; ++w) {
-      const uint32_t c = s_wc[w];
-      off += w < wv ? c : 0u;
-      tot += c;
-    }
-    Cand* out = a.list + seg * a.n_pad + (int64_t)blockIdx.x * span;
+      for (int w = 0; w < kSelectWaves; ++w) {
+        const uint32_t c = s_wc[bt & 1][w];
+        off += w < wv ? c : 0u;
+        tot += c;
+      }
 #pragma unroll
-    for (int u = 0; u < kFselLoads; ++u) {
-      if ((tm[u] >> lane) & 1ull) store_agent(out + off + lane_rank(tm[u]), Cand{key[u], (int32_t)(p0 + 64 * u + lane)});
-      off += (uint32_t)__popcll(tm[u]);
+      for (int u = 0; u < kFselLoads; ++u) {
+        if ((tm[u] >> lane) & 1ull) store_agent(out + off + lane_rank(tm[u]), Cand{key[u], (int32_t)(p0 + 64 * u + lane)});
+        off += (uint32_t)__popcll(tm[u]);
+      }
+      written += tot;
+      if (++bt == a.nb) break;
+      load_batch(bt);
     }
-    if (tid == 0) store_agent(a.wg_cnt + seg * P + blockIdx.x, tot);
+    if (tid == 0) store_agent(a.wg_cnt + seg * P + blockIdx.x, written);
     if (!take_all) {
 #pragma unroll
       for (int u = 0; u < kHistBins / kSelThreads; ++u) {
@@ -419,21 +430,14 @@ __global__ __launch_bounds__(kSelThreads) void topk_filter_select(SelectArgs a) 
 
   // 2. Arrival: once every wave's writes and histogram adds are complete,
   // thread 0 counts the workgroup in. The workgroup that takes the count to
-  // P finishes the segment; the others are done.
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t before = __hip_atomic_fetch_add(a.done + seg * kCtlWords, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = before + 1 == (uint32_t)P ? 1u : 0u;
-  }
-  __syncthreads();
-  if (s_last == 0u) return;
+  // P finishes the segment (and resets the counter); the others are done.
+  if (!arrive_last(a.done + seg * kCtlWords, (uint32_t)P, &s_last)) return;
 
   // 3. Select. Wave 0 finds the second digit's bin from the global
-  // histogram, then zeroes both histograms and the counter for the next call
-  // (every workgroup of the segment read the first before it arrived, and
-  // its adds to the second are complete); wave 1 builds the workgroups'
-  // candidate offsets; every thread clears the third digit's histogram.
+  // histogram, then zeroes both histograms for the next call (every
+  // workgroup of the segment read the first before it arrived, and its adds
+  // to the second are complete); wave 1 builds the workgroups' candidate
+  // offsets; every thread clears the third digit's histogram.
   uint32_t* pre = dyn;
   if (wv == 0) {
     if (!take_all) {
@@ -459,7 +463,6 @@ __global__ __launch_bounds__(kSelThreads) void topk_filter_select(SelectArgs a) 
       *reinterpret_cast<u32x4*>(hg + (kHistBins - 32 - 32 * lane) + 4 * i) = z;
       *reinterpret_cast<u32x4*>(h1g + (kHistBins - 32 - 32 * lane) + 4 * i) = z;
     }
-    if (lane == 0) a.done[seg * kCtlWords] = 0u;
   } else if (wv == 1) {
     uint32_t run = 0;
     for (int j0 = 0; j0 < P; j0 += 64) {

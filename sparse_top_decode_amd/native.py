@@ -31,7 +31,7 @@ EXPORTS = [
     "topk_multi_query", "topk_multi_query_workspace_size",
     "quantize_keys_int8", "topk_attn_decode_int8", "topk_attn_decode_int8_workspace_size",
     "topk_attn_decode_int8_static", "topk_attn_decode_int8_static_workspace_size",
-    "stdk_last_error", "stdk_version", "stdk_inject_launch_failure",
+    "stdk_last_error", "stdk_version", "stdk_inject_launch_failure", "stdk_hbm_read",
     "stdk_profile_enable", "stdk_profile_disable", "stdk_profile_reset", "stdk_profile_read",
 ]
 
@@ -98,6 +98,8 @@ def _sig(lib):
     lib.retopk_workspace_size.restype = c_size_t
     lib.retopk_state_size.argtypes = [POINTER(Layout), POINTER(RetopkParams)]
     lib.retopk_state_size.restype = c_size_t
+    lib.stdk_hbm_read.argtypes = [P, c_int64, c_int32, c_int64, c_int32, P, P]
+    lib.stdk_hbm_read.restype = c_int32
     lib.stdk_inject_launch_failure.argtypes = [c_int32]
     lib.stdk_inject_launch_failure.restype = c_int32
     lib.stdk_last_error.argtypes = []

@@ -267,6 +267,16 @@ class Retopk:
         return out
 
 
+def hbm_read(buf: torch.Tensor, group_stride_bytes: int, n_groups: int, group_bytes: int, wg_per_group: int,
+             sink: torch.Tensor):
+    """Measurement aid: stream n_groups regions of ``buf`` once with the key
+    scan's workgroup split (kernel family "hbm_read")."""
+    _need(buf, "buf")
+    _need(sink, "sink")
+    check(load().stdk_hbm_read(buf.data_ptr(), int(group_stride_bytes), int(n_groups), int(group_bytes),
+                               int(wg_per_group), sink.data_ptr(), _stream()))
+
+
 def inject_launch_failure(after_launches: int):
     """Testing aid: the library launch numbered ``after_launches`` from now is
     not enqueued and its call fails with STDK_EHIP (-1 disarms)."""

@@ -170,6 +170,17 @@ def test_merge_rejects(lib):
     assert lib.attn_merge_lse(0, 128, 0, 0, 0, 0, 0, 0, None) == native.STDK_OK  # nothing to do
 
 
+def test_hbm_read_rejects(lib):
+    E = native.STDK_EINVAL
+    assert lib.stdk_hbm_read(0, 4096, 8, 4096, 32, FAKE, None) == E             # no buffer
+    assert lib.stdk_hbm_read(FAKE + 4, 4096, 8, 4096, 32, FAKE, None) == E      # misaligned
+    assert lib.stdk_hbm_read(FAKE, 4096, 0, 4096, 32, FAKE, None) == E          # no region
+    assert lib.stdk_hbm_read(FAKE, 4096, 8, 4100, 32, FAKE, None) == E          # not whole 16-byte loads
+    assert lib.stdk_hbm_read(FAKE, 4096, 8, 4096, 0, FAKE, None) == E           # no workgroup
+    assert lib.stdk_hbm_read(FAKE, 4096, 8, 4096, 32, 0, None) == E             # no sink
+    assert lib.stdk_hbm_read(FAKE, 4096, 1 << 20, 4096, 1 << 12, FAKE, None) == E  # grid too large
+
+
 def step(lib, p, L_t=100, t=0, ws=1 << 30, L=None, st=None, sup=FAKE):
     L = L or lay(Hq=28, Hkv=4, L=4096)
     st = st or RetopkState(FAKE, FAKE, FAKE, FAKE)

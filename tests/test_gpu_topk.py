@@ -50,6 +50,16 @@ def test_long_head_filter_batches(ops, K):
     assert np.array_equal(idx, want["idx"])
 
 
+def test_c2_shape_two_filter_batches(ops):
+    """The c2 head layout over 200,000 rows: each filter workgroup takes two
+    batches of wave slices; every head against the oracle."""
+    log("case c2 layout L=200000 K=3000 (two filter batches per workgroup)")
+    w = make_workload(2, L=200_000)
+    idx, o, lse = run(ops, w, w.ranges, 3000)
+    heads = [(0, h) for h in range(w.H_q)]
+    check_heads(w, heads, idx, o, lse, w.ranges, 3000, label="c2 L=200000 K=3000")
+
+
 @pytest.mark.parametrize("L,K", [(8192, 2048), (8192, 97), (20000, 1), (3000, 2047)])
 def test_c2_shape_reduced(ops, L, K):
     """Llama-3-8B head layout (32 q / 8 KV, bf16) at reduced length: the
