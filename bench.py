@@ -623,7 +623,50 @@ def bench_retopk(args):
     args.steps = n_steps
     args.warmup = n_steps
     names = RETOPK_KERNELS if args.kernel_events == "on" else ()
-    ms, kern = timed_passes(step, n_steps, names, reset=reset)
+    step_api = "retopk_step"
+    if args.graph == "on":
+        # retopk_step_device: [L_t, t] in device memory, advanced by every
+        # step; the whole pass (one call per step, each with its own query
+        # and per-step outputs) captured once in a HIP graph and replayed
+        step_api = "retopk_step_device, the timed pass replayed from one HIP graph"
+        step_t = torch.tensor([L0 + 1, 0], dtype=torch.int64, device=dev)
+        start = torch.tensor([L0 + 1, 0], dtype=torch.int64, device=dev)
+
+        def reset_dev():
+            rt.init(q_hist, sup_hist)
+            step_t.copy_(start)
+            state["t"] = 0
+
+        def step_dev():
+            t = state["t"]
+            rt.step_device(qs[warm + t], k, v, step_t,
+                           out=dict(support=support, o=o, lse=lse, path=paths[t], n_cand=ncands[t]))
+            state["t"] = (t + 1) % n_steps
+
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n_steps):
+                step_dev()
+        torch.cuda.synchronize()
+        reset_dev()
+        g.replay()  # warm-up replay
+        torch.cuda.synchronize()
+        reset_dev()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        g.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / n_steps
+        # per-kernel durations from a pass of the same calls launched directly
+        _, kern = timed_passes(step_dev, n_steps, names, reset=reset_dev) if names else (None, {})
+        reset_dev()
+        for _ in range(n_steps):  # the per-step paths and counts of one pass, for the statistics below
+            step_dev()
+        torch.cuda.synchronize()
+    else:
+        ms, kern = timed_passes(step, n_steps, names, reset=reset)
     pth = torch.stack(paths, dim=-1).cpu().numpy()
     nc = torch.stack(ncands, dim=-1).cpu().numpy()
     reuse = pth == 0
@@ -644,7 +687,8 @@ def bench_retopk(args):
                 + (f"; voted candidates capped at {p['budget']}" if p["budget"] else ""))
     extra = {"batch": B, "seq_len": L0, "top_k": K, "kv_cache": "bf16", "parallelism": "none (1 GPU)",
              "reuse_fraction": round(float(reuse.mean()), 4), "mean_candidates_reuse": round(mean_m, 1),
-             "rerank_launches": n_rr, "vs_exact_free_running": vs_exact}
+             "rerank_launches": n_rr, "step_api": step_api, "hip_graph": args.graph == "on",
+             "vs_exact_free_running": vs_exact}
     return line(args, ms, workload, extra, roof, kern, cpu)
 
 
@@ -777,8 +821,8 @@ def main():
                     help="workload 2: distinct K/V caches used in turn, one per layer (1 = the same cache every "
                          "step, partly served by the last-level cache)")
     ap.add_argument("--graph", choices=["on", "off"], default="off",
-                    help="on: the timed steps replay the step captured in a HIP graph (measured slower than "
-                         "direct launches for this five-kernel step)")
+                    help="on: the timed steps replay the step captured in a HIP graph (workload 3: the 256 steps "
+                         "of a pass through retopk_step_device, captured as one graph)")
     ap.add_argument("--path", choices=["one-pass", "three-calls"], default="one-pass",
                     help="one-pass: topk_attn_decode_static; three-calls: topk_attn_decode over the dynamic "
                          "rows, topk_attn_decode over the static rows, attn_merge_lse")

@@ -380,6 +380,29 @@ int32_t retopk_step(const stdk_layout* lay, const retopk_params* p, const retopk
                     int32_t* path_out, int32_t* n_cand_out, int32_t* cand_out, void* workspace,
                     size_t workspace_bytes, void* stream);
 
+/* retopk_step for serving loops that replay a captured step (a HIP graph):
+ * the same step, with L_t and t read on the device from `step` and advanced
+ * there at the end of the step, so that every call enqueues the same
+ * launches with the same arguments ([RT] "GPU Kernel": a resident,
+ * pre-allocated workspace; "局限性": serving workloads).
+ *  step         device memory, two int64 words [L_t, t] (8-byte aligned).
+ *               The step reads them as retopk_step takes its arguments (L_t
+ *               clamped to 1..max_len, t below 0 taken as 0) and, after its
+ *               last launch, has added 1 to both on `stream`.
+ *  workspace    at least retopk_workspace_size(lay, p, lay->max_len) bytes
+ *               (every launch is sized for L_t = max_len; rows at or past the
+ *               device L_t are not read).
+ * Everything else, results included, is as for retopk_step with the same
+ * L_t and t. The library enqueues no memory set or copy; the caller may
+ * capture the call in a graph and replay it for successive steps, writing
+ * the new query into `q` (and the new key and value rows into the caches)
+ * between replays. STDK_EINVAL if `step` is NULL. */
+int32_t retopk_step_device(const stdk_layout* lay, const retopk_params* p, const retopk_state* st,
+                           const float* q, const void* k_cache, const void* v_cache, int64_t* step,
+                           int32_t* support_out, float* o_out, float* lse_out, int32_t* path_out,
+                           int32_t* n_cand_out, int32_t* cand_out, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
 size_t retopk_workspace_size(const stdk_layout* lay, const retopk_params* p, int64_t max_L_t);
 
 /* Bytes of one allocation that holds the four state arrays of `lay` and

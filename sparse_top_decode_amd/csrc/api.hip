@@ -468,7 +468,8 @@ struct Q8Keys {
 
 int32_t run_exact_select(const Geo& g, const TopkWs& w, char* ws, const float* q, const void* k_cache,
                          const RangeTab& tab, float scale, const int32_t* active, int32_t* idx_out,
-                         const DevInfo* di, hipStream_t s, const Q8Keys* q8 = nullptr) {
+                         const DevInfo* di, hipStream_t s, const Q8Keys* q8 = nullptr,
+                         const int64_t* n_dev = nullptr) {
   float* scores = (float*)(ws + w.scores);
   uint32_t* hist = (uint32_t*)(ws + w.hist);
   Cand* list = (Cand*)(ws + w.list);
@@ -496,6 +497,7 @@ int32_t run_exact_select(const Geo& g, const TopkWs& w, char* ws, const float* q
     a.Hkv = g.Hkv;
     a.scale = scale;
     a.head_active = active;
+    a.n_dev = n_dev;
     a.tab = tab;
     const int ri = q8 ? scan_rows_iter<int8_t>(g.G) : (g.bf16 ? scan_rows_iter<uint16_t>(g.G) : scan_rows_iter<float>(g.G));
     // one resident wave of workgroups over the whole chip, whole iterations each
@@ -539,6 +541,7 @@ int32_t run_exact_select(const Geo& g, const TopkWs& w, char* ws, const float* q
     a.sel_z = (float*)(ws + w.sel_z);
     a.idx_out = idx_out;
     a.seg_active = active;
+    a.n_dev = n_dev;
     a.tab = tab;
     // LDS for the workgroups' offsets and the candidates (typically under
     // 2K of them): room for max(8192, 2K)
@@ -563,11 +566,13 @@ int32_t run_combine(const TopkWs& w, char* ws, int32_t np, float* o_out, float* 
 // gather), one workgroup per (head, value slice); else slices of kSvRows
 // rows and the combine.
 int32_t run_sv(const Geo& g, const TopkWs& w, char* ws, const void* v_cache, float* o_out, float* lse_out,
-               hipStream_t s, const RangeTab* tab = nullptr, const SvPush* push = nullptr) {
+               hipStream_t s, const RangeTab* tab = nullptr, const SvPush* push = nullptr,
+               int64_t* step_adv = nullptr) {
   SvArgs a{};
   if (push) {
     a.do_push = 1;
     a.push = *push;
+    a.step_adv = step_adv;
   }
   a.k_top = (int32_t)w.K;
   a.scores = (const float*)(ws + w.scores);
@@ -1503,10 +1508,14 @@ int32_t retopk_state_init(const stdk_layout* lay, const retopk_params* p, const 
   return ok();
 }
 
-int32_t retopk_step(const stdk_layout* lay, const retopk_params* p, const retopk_state* st, const float* q,
-                    const void* k_cache, const void* v_cache, int64_t L_t, int64_t t, int32_t* support_out,
-                    float* o_out, float* lse_out, int32_t* path_out, int32_t* n_cand_out, int32_t* cand_out,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+// One ReTopK step. step_dev == null: L_t and t are the host's. Otherwise
+// they are read on the device from step_dev ([L_t, t]) and advanced there at
+// the end of the step; every launch is then sized for L_t = max_len (clamped
+// on the device), so the same sequence of launches serves every step.
+int32_t run_retopk(const stdk_layout* lay, const retopk_params* p, const retopk_state* st, const float* q,
+                   const void* k_cache, const void* v_cache, int64_t L_t, int64_t t, int64_t* step_dev,
+                   int32_t* support_out, float* o_out, float* lse_out, int32_t* path_out, int32_t* n_cand_out,
+                   int32_t* cand_out, void* workspace, size_t workspace_bytes, void* stream) {
   STDK_TRY(check_retopk(lay, p, st));
   STDK_TRY(check_ptr(q, "q", 16));
   STDK_TRY(check_ptr(k_cache, "k_cache", 16));
@@ -1514,6 +1523,12 @@ int32_t retopk_step(const stdk_layout* lay, const retopk_params* p, const retopk
   STDK_TRY(check_ptr(support_out, "support_out", 4));
   STDK_TRY(check_ptr(o_out, "o_out", 4));
   STDK_TRY(check_ptr(lse_out, "lse_out", 4));
+  const bool dev = step_dev != nullptr;
+  if (dev) {
+    STDK_TRY(check_ptr(step_dev, "step", 8));
+    L_t = lay->max_len;
+    t = 0;
+  }
   if (L_t < 1 || L_t > lay->max_len) return fail(STDK_EINVAL, "L_t %lld outside 1..max_len", (long long)L_t);
   if (L_t > (1 << 20)) return fail(STDK_EUNSUPPORTED, "L_t %lld > 1048576", (long long)L_t);
   if (t < 0) return fail(STDK_EINVAL, "t %lld < 0", (long long)t);
@@ -1528,7 +1543,9 @@ int32_t retopk_step(const stdk_layout* lay, const retopk_params* p, const retopk
   char* ws = (char*)workspace;
   STDK_TRY(clean_if_dirty(ws, workspace_bytes, s));
   const int32_t rc = [&]() -> int32_t {
-    const bool refresh_now = p->refresh > 0 && (t % p->refresh) == 0;
+    // with device-side steps the refresh is decided by retopk_select, which
+    // marks every head exact then; the launches below stay the same
+    const bool refresh_now = !dev && p->refresh > 0 && (t % p->refresh) == 0;
     int32_t* exact = (int32_t*)(ws + w.exact);
 
     // a6: selector (cosine, path, top-R, candidate union)
@@ -1546,6 +1563,8 @@ int32_t retopk_step(const stdk_layout* lay, const retopk_params* p, const retopk
       a.tau = p->tau;
       a.refresh_now = refresh_now ? 1 : 0;
       a.L_t = L_t;
+      a.step = step_dev;
+      a.refresh = p->refresh;
       a.cand_cap = (int32_t)w.cand_cap;
       a.bitmap_words = (int32_t)w.words;
       a.qbar = (float*)(ws + w.qbar);
@@ -1581,6 +1600,7 @@ int32_t retopk_step(const stdk_layout* lay, const retopk_params* p, const retopk
       a.n_cand_out = n_cand_out;
       a.cand_out = cand_out;
       a.L_t = L_t;
+      a.step = step_dev;
       a.C = p->cache_cap;
       a.K = p->top_k;
       a.R = p->top_r;
@@ -1603,7 +1623,7 @@ int32_t retopk_step(const stdk_layout* lay, const retopk_params* p, const retopk
     int64_t n_all = 0;
     const RangeTab tab = make_tab(rng, 1, &n_all);
     const int32_t* active = refresh_now ? nullptr : exact;
-    STDK_TRY(run_exact_select(g, w.t, ws, q, k_cache, tab, p->scale, active, support_out, di, s));
+    STDK_TRY(run_exact_select(g, w.t, ws, q, k_cache, tab, p->scale, active, support_out, di, s, nullptr, step_dev));
     // reuse heads: indexed QK over the candidates, rerank, softmax.V
     if (!refresh_now) {
       RtRerankArgs a{};
@@ -1635,10 +1655,28 @@ int32_t retopk_step(const stdk_layout* lay, const retopk_params* p, const retopk
     // the push of (q_bar, support) by one workgroup per head of that launch
     const SvPush push{(const float*)(ws + w.qbar), support_out, st->q_hat, st->support, st->head, st->count,
                       p->cache_cap, p->top_k};
-    return run_sv(g, w.t, ws, v_cache, o_out, lse_out, s, nullptr, &push);
+    return run_sv(g, w.t, ws, v_cache, o_out, lse_out, s, nullptr, &push, step_dev);
   }();
   return finish(rc, ws, w.t.counters);
 }
+
+int32_t retopk_step(const stdk_layout* lay, const retopk_params* p, const retopk_state* st, const float* q,
+                    const void* k_cache, const void* v_cache, int64_t L_t, int64_t t, int32_t* support_out,
+                    float* o_out, float* lse_out, int32_t* path_out, int32_t* n_cand_out, int32_t* cand_out,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  return run_retopk(lay, p, st, q, k_cache, v_cache, L_t, t, nullptr, support_out, o_out, lse_out, path_out,
+                    n_cand_out, cand_out, workspace, workspace_bytes, stream);
+}
+
+int32_t retopk_step_device(const stdk_layout* lay, const retopk_params* p, const retopk_state* st, const float* q,
+                           const void* k_cache, const void* v_cache, int64_t* step, int32_t* support_out,
+                           float* o_out, float* lse_out, int32_t* path_out, int32_t* n_cand_out, int32_t* cand_out,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (!step) return fail(STDK_EINVAL, "step is NULL");
+  return run_retopk(lay, p, st, q, k_cache, v_cache, 0, 0, step, support_out, o_out, lse_out, path_out, n_cand_out,
+                    cand_out, workspace, workspace_bytes, stream);
+}
+
 
 // ---------------------------------------------------------------------------
 // launch timing

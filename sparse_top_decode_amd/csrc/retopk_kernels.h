@@ -60,10 +60,13 @@ struct RtSelArgs {
   const int32_t* count;     // [S]
   int32_t C, K, R, W;
   float tau;
-  int32_t refresh_now;      // this step is a periodic refresh (host decided)
-  int64_t L_t;
+  int32_t refresh_now;      // this step is a periodic refresh (host decided; unused with `step`)
+  int64_t L_t;              // visible rows; with `step`, the most there can be
   int32_t cand_cap;         // R*K + W
   int32_t bitmap_words;     // ceil(L_t / 32)
+  const int64_t* step;      // or null: device memory [L_t, t] for this step; L_t is clamped to
+                            // [1, L_t above], and the refresh (t % refresh == 0) is decided here
+  int32_t refresh, pad_;
   float* qbar;              // [S][128]
   int32_t* path;            // [S]
   int32_t* exact;           // [S]: 1 = this head takes the exact path
@@ -96,6 +99,13 @@ __global__ __launch_bounds__(kRtSelThreads) void retopk_select(RtSelArgs a) {
   const int C = a.C, K = a.K;
   const int hd = a.head[seg], cnt = a.count[seg];
   const int j = tid & 7, g = tid >> 3;  // part of the 128 dims, cache slot within a pass
+  int64_t L_t = a.L_t;
+  int refresh_now = a.refresh_now;
+  if (a.step) {
+    L_t = min(a.L_t, max((int64_t)1, a.step[0]));
+    const int64_t t = max((int64_t)0, a.step[1]);
+    refresh_now = a.refresh > 0 && t % a.refresh == 0;
+  }
 
   // One memory round trip: every thread requests its 16 query components and
   // the same components of its cache slots (slot g + 32 * pass).
@@ -132,8 +142,8 @@ __global__ __launch_bounds__(kRtSelThreads) void retopk_select(RtSelArgs a) {
       part[sl][j] = t;
     }
   }
-  const int Wd = a.bitmap_words;
-  uint32_t* bm = kLdsBitmap ? dyn : (a.gbitmap + seg * (int64_t)Wd);
+  const int Wd = a.step ? (int)((L_t + 31) / 32) : a.bitmap_words;
+  uint32_t* bm = kLdsBitmap ? dyn : (a.gbitmap + seg * (int64_t)a.bitmap_words);
   __syncthreads();
   // Wave 0 (C <= 64 slots, one per lane): the cosines, the path, the top R
   // and the picked slots in slot order, with LDS broadcasts and ballots. The entry
@@ -154,7 +164,7 @@ __global__ __launch_bounds__(kRtSelThreads) void retopk_select(RtSelArgs a) {
     }
     const float best = wave_max(re);
     int path;
-    if (a.refresh_now) path = 2;
+    if (refresh_now) path = 2;
     else if (cnt == 0 || best < a.tau) path = 1;
     else path = 0;
     if (sl == 0) {
@@ -197,8 +207,8 @@ __global__ __launch_bounds__(kRtSelThreads) void retopk_select(RtSelArgs a) {
   const int path = s_path;
   if (path != 0) {
     if (tid == 0) {
-      a.n_cand[seg] = (int32_t)a.L_t;
-      if (a.n_cand_out) a.n_cand_out[seg] = (int32_t)a.L_t;
+      a.n_cand[seg] = (int32_t)L_t;
+      if (a.n_cand_out) a.n_cand_out[seg] = (int32_t)L_t;
     }
     if (a.cand_out)
       for (int i = tid; i < a.cand_cap; i += kRtSelThreads) a.cand_out[seg * a.cand_cap + i] = -1;
@@ -208,7 +218,7 @@ __global__ __launch_bounds__(kRtSelThreads) void retopk_select(RtSelArgs a) {
     for (int i = tid; i < Wd; i += kRtSelThreads) bm[i] = 0u;
     __syncthreads();
   }
-  const int64_t L = a.L_t;
+  const int64_t L = L_t;
   // union of the picked supports: index f of the flattened R x K list is
   // entry f % K of picked slot f / K; kU loads per thread are in flight
   // before their bits are set
@@ -298,8 +308,9 @@ struct RtVoteArgs {
   int32_t* n_cand;          // [S], rewritten
   int32_t* n_cand_out;      // [S] or null
   int32_t* cand_out;        // [S][cand_cap] or null
-  int64_t L_t;
+  int64_t L_t;              // visible rows; with `step`, the most there can be
   int32_t C, K, R, W, cand_cap, budget;
+  const int64_t* step;      // or null: device memory [L_t, t] (L_t clamped to [1, L_t above])
 };
 
 constexpr int kVoteThreads = 256;
@@ -324,7 +335,8 @@ __global__ __launch_bounds__(kVoteThreads) void retopk_vote(RtVoteArgs a) {
   for (int r = 0; r < kMaxVote; ++r) slot[r] = a.rec_slot[seg * kMaxVote + r];
   if (ex) return;
   const int tid = threadIdx.x;
-  const int64_t lo_recent = a.L_t - a.W > 0 ? a.L_t - a.W : 0;
+  const int64_t L_t = a.step ? min(a.L_t, max((int64_t)1, a.step[0])) : a.L_t;
+  const int64_t lo_recent = L_t - a.W > 0 ? L_t - a.W : 0;
   int32_t* cl = vdyn;
   uint8_t* mk = reinterpret_cast<uint8_t*>(vdyn + a.cand_cap);
   int32_t* cd = a.cand + seg * a.cand_cap;

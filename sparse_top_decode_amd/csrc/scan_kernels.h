@@ -104,6 +104,8 @@ struct ScanArgs {
   const float* kscale;         // int8 keys only: per-row scales, element (b, h_kv, row) at
   int64_t kscale_stride_b;     //   b*kscale_stride_b + h_kv*kscale_stride_h + row
   int64_t kscale_stride_h;
+  const int64_t* n_dev;        // or null: device memory holding a row count; positions at or past it
+                               // are neither scored nor counted (the launch is sized for n)
   RangeTab tab;
 };
 
@@ -255,8 +257,15 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
 
   const char* kb = a.k + (int64_t)b * a.stride_b_bytes + (int64_t)hkv * a.stride_h_bytes + c * 16;
   const float* ksb = kQ8 ? a.kscale + (int64_t)b * a.kscale_stride_b + (int64_t)hkv * a.kscale_stride_h : nullptr;
+  int64_t n_all = a.n, n_hist = a.n_hist;
+  if (a.n_dev) {
+    const int64_t nd = max((int64_t)0, *a.n_dev);
+    n_all = min(n_all, nd);
+    n_hist = min(n_hist, nd);
+  }
   const int64_t p_beg = (int64_t)blk * a.rows_per_block;
-  const int64_t p_end = min(a.n, p_beg + a.rows_per_block);
+  const int64_t p_end = min(n_all, p_beg + a.rows_per_block);
+  if (p_beg >= p_end) return;  // no row of this workgroup's block is in use
   // An iteration covers positions [base, base + IT) of the piece [.., pe) of
   // one range, whose rows are position + ro. Past the block's end `ok` is
   // false: the iteration keeps the last piece (its loads stay clamped to a
@@ -401,7 +410,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
         // streaming store: the scores are read once, by the next kernel
         __builtin_nontemporal_store(val, &a.scores[(seg0 + h_out) * a.n_pad + p]);
       }
-      if (p < a.n_hist) atomicAdd(&lh[h_out * kHistBins + (f2key(val) >> (32 - kHistBits))], 1u);
+      if (p < n_hist) atomicAdd(&lh[h_out * kHistBins + (f2key(val) >> (32 - kHistBits))], 1u);
     }
   };
   // Staged scores: a chunk of consecutive positions [c0, c1) goes out once

@@ -123,6 +123,7 @@ struct SelectArgs {
   float* sel_z;               // [S][K] their scores
   int32_t* idx_out;           // [S][K] or null (copy of the chosen rows)
   const int32_t* seg_active;  // [S] or null
+  const int64_t* n_dev;       // or null: device memory holding a position count that replaces n when smaller
   RangeTab tab;
 };
 
@@ -339,7 +340,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_filter_select(SelectArgs a) 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int P = (int)gridDim.x;
   const int K = a.K;
-  const bool take_all = a.n <= K;
+  const int64_t n = a.n_dev ? min(a.n, max((int64_t)0, *a.n_dev)) : a.n;
+  const bool take_all = n <= K;
   uint32_t* hg = a.hist + seg * kHistBins;
   uint32_t* h1g = a.hist1 + seg * kHistBins;
   const int64_t span = (int64_t)a.nb * kSelectWaves * a.slice;
@@ -361,7 +363,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_filter_select(SelectArgs a) 
     float v[kFselLoads];
     auto load_batch = [&](int bt) {
       const int64_t p0 = (int64_t)blockIdx.x * span + ((int64_t)bt * kSelectWaves + wv) * a.slice;
-      const int64_t plast = max((int64_t)0, min(a.n, p0 + a.slice) - 1);  // clamped into the scores
+      const int64_t plast = max((int64_t)0, min(n, p0 + a.slice) - 1);  // clamped into the scores
 #pragma unroll
       for (int u = 0; u < kFselLoads; ++u) v[u] = sc[min(p0 + 64 * u + lane, plast)];
     };
@@ -383,7 +385,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_filter_select(SelectArgs a) 
     uint32_t written = 0;
     for (int bt = 0;;) {
       const int64_t p0 = (int64_t)blockIdx.x * span + ((int64_t)bt * kSelectWaves + wv) * a.slice;
-      const int64_t p1 = min(a.n, p0 + a.slice);
+      const int64_t p1 = min(n, p0 + a.slice);
       uint32_t key[kFselLoads];
       uint64_t tm[kFselLoads];
       uint32_t cnt = 0;
@@ -540,6 +542,7 @@ struct SvArgs {
   int64_t n_seg;
   int32_t do_push, pad2_;
   SvPush push;
+  int64_t* step_adv;          // or null: the pusher of segment 0 adds 1 to both words ([L_t, t]) at its end
   // sparse_sv_scored only: the queries and the key cache its rows are
   // scored from
   const float* q;             // [S][128]
@@ -649,6 +652,10 @@ __global__ __launch_bounds__(kSvThreads) void sparse_sv(SvArgs a) {
   if (pusher && tid == 0) {
     a.push.head[seg] = push_slot;
     a.push.count[seg] = min(push_cnt + 1, a.push.C);
+    if (a.step_adv && seg == 0) {
+      a.step_adv[0] += 1;
+      a.step_adv[1] += 1;
+    }
   }
 }
 
@@ -814,6 +821,10 @@ __global__ __launch_bounds__(kDsThreads) void sparse_sv_ds(SvArgs a) {
   if (pusher && tid == 0) {
     a.push.head[seg] = push_slot;
     a.push.count[seg] = min(push_cnt + 1, a.push.C);
+    if (a.step_adv && seg == 0) {
+      a.step_adv[0] += 1;
+      a.step_adv[1] += 1;
+    }
   }
 }
 

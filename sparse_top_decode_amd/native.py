@@ -27,7 +27,7 @@ STDK_NOALLOC_SCRATCH_BYTES = 96 << 20
 EXPORTS = [
     "topk_attn_decode", "topk_attn_decode_workspace_size", "attn_merge_lse",
     "topk_attn_decode_static", "topk_attn_decode_static_workspace_size", "topk_attn_decode_static_noalloc",
-    "retopk_state_init", "retopk_step", "retopk_workspace_size", "retopk_state_size",
+    "retopk_state_init", "retopk_step", "retopk_step_device", "retopk_workspace_size", "retopk_state_size",
     "topk_multi_query", "topk_multi_query_workspace_size",
     "quantize_keys_int8", "topk_attn_decode_int8", "topk_attn_decode_int8_workspace_size",
     "topk_attn_decode_int8_static", "topk_attn_decode_int8_static_workspace_size",
@@ -76,6 +76,9 @@ def _sig(lib):
     lib.retopk_step.argtypes = [POINTER(Layout), POINTER(RetopkParams), POINTER(RetopkState), P, P, P, c_int64,
                                 c_int64, P, P, P, P, P, P, P, c_size_t, P]
     lib.retopk_step.restype = c_int32
+    lib.retopk_step_device.argtypes = [POINTER(Layout), POINTER(RetopkParams), POINTER(RetopkState), P, P, P, P,
+                                       P, P, P, P, P, P, P, c_size_t, P]
+    lib.retopk_step_device.restype = c_int32
     lib.topk_multi_query.argtypes = [POINTER(Layout), P, c_int32, P, POINTER(c_int64), c_int32, c_int32, c_float,
                                      P, P, P, c_size_t, P]
     lib.topk_multi_query.restype = c_int32

@@ -234,6 +234,10 @@ class Retopk:
         mx = L if max_len_t is None else int(max_len_t)
         nbytes = int(load().retopk_workspace_size(ctypes.byref(self.layout), ctypes.byref(self.params), mx))
         self.workspace = new_workspace(nbytes, dev)
+        # step_device sizes every launch for the cache's full length; the
+        # workspace above serves it unless max_len_t was set lower
+        need = int(load().retopk_workspace_size(ctypes.byref(self.layout), ctypes.byref(self.params), L))
+        self.device_workspace = self.workspace if self.workspace.numel() >= need else new_workspace(need, dev)
 
     def init(self, q_hist: torch.Tensor, sup_hist: torch.Tensor):
         """Fill the caches from [B, H_q, n, 128] queries and [B, H_q, n, K] supports."""
@@ -263,6 +267,25 @@ class Retopk:
                                 out["support"].data_ptr(), out["o"].data_ptr(), out["lse"].data_ptr(),
                                 _ptr(out.get("path")), _ptr(out.get("n_cand")), _ptr(out.get("cand")),
                                 self.workspace.data_ptr(), self.workspace.numel(), _stream())
+        check(rc)
+        return out
+
+
+    def step_device(self, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, step: torch.Tensor,
+                    out: dict, want_cand: bool = False) -> dict:
+        """One decode step with L_t and t read from the device tensor ``step``
+        (int64 [L_t, t]) and advanced there by the step; nothing is allocated
+        (``out`` holds support, o, lse and optionally path, n_cand, cand), so
+        the call can be captured in a graph and replayed for later steps."""
+        _need(q, "q", torch.float32)
+        _need(step, "step", torch.int64, (2,))
+        ws = self.device_workspace
+        rc = load().retopk_step_device(ctypes.byref(self.layout), ctypes.byref(self.params),
+                                       ctypes.byref(self.state), q.data_ptr(), k_cache.data_ptr(),
+                                       v_cache.data_ptr(), step.data_ptr(), out["support"].data_ptr(),
+                                       out["o"].data_ptr(), out["lse"].data_ptr(), _ptr(out.get("path")),
+                                       _ptr(out.get("n_cand")), _ptr(out.get("cand")), ws.data_ptr(), ws.numel(),
+                                       _stream())
         check(rc)
         return out
 

@@ -213,6 +213,24 @@ def test_retopk_rejects(lib):
                 L_t=5000) == native.STDK_EUNSUPPORTED
 
 
+def test_retopk_device_rejects(lib):
+    """retopk_step_device: the step words are required and 8-byte aligned;
+    the workspace must cover L_t = max_len (every launch is sized for it)."""
+    good = RetopkParams(64, 8, 2, 8, 0.85, 16, 0.088)
+    L = lay(Hq=28, Hkv=4, L=4096)
+    st = RetopkState(FAKE, FAKE, FAKE, FAKE)
+
+    def dstep(step_ptr, ws=1 << 30):
+        return lib.retopk_step_device(ctypes.byref(L), ctypes.byref(good), ctypes.byref(st), FAKE, FAKE, FAKE,
+                                      step_ptr, FAKE, FAKE, FAKE, None, None, None, FAKE, ws, None)
+
+    assert dstep(0) == native.STDK_EINVAL
+    assert dstep(FAKE + 4) == native.STDK_EINVAL
+    need = lib.retopk_workspace_size(ctypes.byref(L), ctypes.byref(good), 4096)
+    assert need > lib.retopk_workspace_size(ctypes.byref(L), ctypes.byref(good), 100)
+    assert dstep(FAKE, ws=need - 1) == native.STDK_EWORKSPACE
+
+
 def call_mq(lib, L=None, M=4, ranges=((0, 100),), top_k=8, ws_bytes=1 << 30, q=FAKE, scale=0.1, idx=FAKE, z=None):
     L = L or lay()
     flat = [x for r in ranges for x in r]

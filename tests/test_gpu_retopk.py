@@ -64,7 +64,12 @@ def oracle_step(p, before, qt, w, L_t, t, heads):
     return dict(zip(heads, pmap(one, heads)))
 
 
-def run_lockstep(ops, w, p, n_steps, heads, n_warm, check_every=1):
+def run_lockstep(ops, w, p, n_steps, heads, n_warm, check_every=1, mode="host"):
+    """mode "host": retopk_step with L_t, t from the host; "device":
+    retopk_step_device with [L_t, t] in device memory, advanced by the step;
+    "graph": that call captured once in a HIP graph and replayed for every
+    step (the query copied into the captured input buffer before each
+    replay, the host-side state copies between replays)."""
     L0 = w.retopk["L0"]
     k, v = dev_kv(w)
     rt = ops.Retopk(k, w.H_q, top_k=p.top_k, cache_cap=p.cache_cap, top_r=p.top_r, recent=p.recent, tau=p.tau,
@@ -77,12 +82,39 @@ def run_lockstep(ops, w, p, n_steps, heads, n_warm, check_every=1):
     assert np.array_equal(g0.head, st0.head) and np.array_equal(g0.count, st0.count)
     assert np.max(np.abs(g0.q_hat - st0.q_hat)) < 1e-6
     stats = dict(reuse=0, exact=0, fallback=0, refresh=0, mixed_steps=0, flagged=0, cand=[], swaps=0, capped=0)
+    if mode != "host":
+        B, K = w.q.shape[0], p.top_k
+        i32 = dict(dtype=torch.int32, device="cuda")
+        fixed = dict(support=torch.empty((B, w.H_q, K), **i32),
+                     o=torch.empty((B, w.H_q, 128), dtype=torch.float32, device="cuda"),
+                     lse=torch.empty((B, w.H_q), dtype=torch.float32, device="cuda"),
+                     path=torch.empty((B, w.H_q), **i32), n_cand=torch.empty((B, w.H_q), **i32),
+                     cand=torch.empty((B, w.H_q, rt.cand_cap), **i32))
+        q_buf = torch.empty((B, w.H_q, 128), dtype=torch.float32, device="cuda")
+        step_t = torch.tensor([L0 + 1, 0], dtype=torch.int64, device="cuda")
+        graph = None
+        if mode == "graph":
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                rt.step_device(q_buf, k, v, step_t, fixed)
+            torch.cuda.synchronize()
+            assert step_t.cpu().tolist() == [L0 + 1, 0], "capture must not run the step"
     for t in range(n_steps):
         L_t = L0 + t + 1
         qt = np.ascontiguousarray(w.q[:, :, n_warm + t])
         checking = (t % check_every) == 0
         before = host_state(rt) if checking else None
-        out = rt.step(torch.from_numpy(qt).cuda(), k, v, L_t, t, want_cand=True)
+        if mode == "host":
+            out = rt.step(torch.from_numpy(qt).cuda(), k, v, L_t, t, want_cand=True)
+        else:
+            q_buf.copy_(torch.from_numpy(qt).cuda())
+            if graph is not None:
+                graph.replay()
+            else:
+                rt.step_device(q_buf, k, v, step_t, fixed)
+            out = fixed
+            torch.cuda.synchronize()
+            assert step_t.cpu().tolist() == [L_t + 1, t + 1], (t, step_t.cpu().tolist())
         torch.cuda.synchronize()
         if not checking:
             continue
@@ -143,6 +175,38 @@ def test_retopk_lockstep_small(ops):
     log(f"retopk small: reuse {s['reuse']} exact {s['exact']} flagged {s['flagged']} "
         f"mean M {np.mean(s['cand']) if s['cand'] else 0:.0f} band swaps {s['swaps']}")
     assert s["reuse"] > 0 and s["exact"] > 0
+
+
+@pytest.mark.parametrize("mode", ["device", "graph"])
+def test_retopk_device_step_lockstep(ops, mode):
+    """retopk_step_device (L_t and t in device memory, advanced by the step)
+    on the small c3-shaped case, called directly and replayed from one
+    captured HIP graph: every step of every head against the oracle, with
+    refreshes, fallbacks and reuse."""
+    w = make_workload(3, L=4096, steps=40, warm=8)
+    p = ref.RetopkParams(top_k=64, cache_cap=8, top_r=2, recent=16, tau=0.9, refresh=8)
+    heads = [(0, h) for h in range(28)]
+    s = run_lockstep(ops, w, p, 40, heads, n_warm=8, mode=mode)
+    log(f"retopk {mode} step: reuse {s['reuse']} fallback {s['fallback']} refresh {s['refresh']} "
+        f"flagged {s['flagged']}")
+    assert s["reuse"] > 0 and s["refresh"] > 0
+
+
+@pytest.mark.slow
+def test_retopk_c3_graph_replay_lockstep(ops):
+    """c3 at full size (L0 = 65536, K=512, C=32, R=4, W=32, tau=0.85,
+    T_r=128): the step captured once in a HIP graph and replayed for all 256
+    steps, every head compared with the oracle at every step."""
+    w = make_workload(3)
+    P = w.retopk
+    p = ref.RetopkParams(top_k=P["top_k"], cache_cap=P["cache_cap"], top_r=P["top_r"], recent=P["recent"],
+                         tau=P["tau"], refresh=P["refresh"])
+    heads = [(0, h) for h in range(w.H_q)]
+    s = run_lockstep(ops, w, p, P["steps"], heads, n_warm=P["warmup"], mode="graph")
+    log(f"retopk c3 graph replay: {len(heads)} heads x {P['steps']} steps: reuse {s['reuse']} "
+        f"refresh {s['refresh']} flagged {s['flagged']}")
+    assert s["reuse"] + s["exact"] + s["flagged"] == len(heads) * P["steps"]
+    assert s["refresh"] == 2 * len(heads)
 
 
 def test_retopk_tiny_cache_all_paths(ops):
