@@ -91,8 +91,8 @@ SCAN_SOURCES = ["sparse_top_decode_amd/csrc/scan_kernels.h", "sparse_top_decode_
 METRIC = "top-K decode-attention steps/sec at 128K ctx; K-scan HBM GB/s vs peak"
 TOPK_KERNELS = ("k_scan", "topk_filter_select", "sparse_sv", "dense_attn", "combine", "attn_merge")
 MQ_KERNELS = ("mq_blockmax", "mq_threshold", "mq_collect", "mq_select")
-RETOPK_KERNELS = ("retopk_select", "retopk_vote", "retopk_rerank", "retopk_rerank_select", "k_scan",
-                  "topk_filter_select", "sparse_sv", "combine")
+RETOPK_KERNELS = ("retopk_select", "retopk_vote", "retopk_attend", "retopk_rerank", "retopk_rerank_select",
+                  "k_scan", "topk_filter_select", "sparse_sv", "combine")
 
 
 def scan_source_hash() -> str:

@@ -59,14 +59,14 @@ int32_t ok() {
 enum KernelId {
   KID_SCAN, KID_SELECT, KID_SV, KID_DENSE, KID_COMBINE, KID_MERGE, KID_FILL,
   KID_RT_SELECT, KID_RT_RERANK, KID_RT_RSEL, KID_RT_INIT, KID_MQ_BLOCKMAX, KID_MQ_THRESH,
-  KID_MQ_COLLECT, KID_MQ_SELECT, KID_MQ_FILL, KID_RT_VOTE, KID_Q8_QUANT, KID_READ, KID_COUNT
+  KID_MQ_COLLECT, KID_MQ_SELECT, KID_MQ_FILL, KID_RT_VOTE, KID_Q8_QUANT, KID_READ, KID_RT_ATTEND, KID_COUNT
 };
 const char* const kKernelNames[KID_COUNT] = {
     "k_scan",        "topk_filter_select",             "sparse_sv",
     "dense_attn",  "combine",       "attn_merge",    "fill_empty",           "retopk_select",
     "retopk_rerank", "retopk_rerank_select", "retopk_init", "mq_blockmax",
     "mq_threshold",  "mq_collect",    "mq_select",     "mq_fill",       "retopk_vote",   "k_quantize",
-    "hbm_read"};
+    "hbm_read",      "retopk_attend"};
 
 struct Profiler {
   std::mutex mu;
@@ -245,6 +245,10 @@ int32_t dev_info(DevInfo** out) {
                               std::max(0, d.max_lds - 4 * 1024));
     (void)hipFuncSetAttribute((const void*)retopk_vote<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               std::max(0, d.max_lds - 4 * 1024));
+    (void)hipFuncSetAttribute((const void*)retopk_attend<uint16_t>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              std::max(0, d.max_lds - kAttStaticLds));
+    (void)hipFuncSetAttribute((const void*)retopk_attend<float>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              std::max(0, d.max_lds - kAttStaticLds));
     (void)hipFuncSetAttribute((const void*)retopk_rerank_select_lds, hipFuncAttributeMaxDynamicSharedMemorySize,
                               std::max(0, d.max_lds - 12 * 1024));
     (void)hipFuncSetAttribute((const void*)sparse_sv_ds<uint16_t>, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -559,7 +563,8 @@ int32_t run_exact_select(const Geo& g, const TopkWs& w, char* ws, const float* q
   return STDK_OK;
 }
 
-int32_t run_combine(const TopkWs& w, char* ws, int32_t np, float* o_out, float* lse_out, hipStream_t s);
+int32_t run_combine(const TopkWs& w, char* ws, int32_t np, float* o_out, float* lse_out, hipStream_t s,
+                    const int32_t* seg_active = nullptr);
 
 // Softmax . V over the chosen rows left by the select kernels: for few
 // heads with few rows (where the combine pass would cost as much as the
@@ -567,13 +572,14 @@ int32_t run_combine(const TopkWs& w, char* ws, int32_t np, float* o_out, float* 
 // rows and the combine.
 int32_t run_sv(const Geo& g, const TopkWs& w, char* ws, const void* v_cache, float* o_out, float* lse_out,
                hipStream_t s, const RangeTab* tab = nullptr, const SvPush* push = nullptr,
-               int64_t* step_adv = nullptr) {
+               int64_t* step_adv = nullptr, const int32_t* seg_active = nullptr) {
   SvArgs a{};
   if (push) {
     a.do_push = 1;
     a.push = *push;
-    a.step_adv = step_adv;
   }
+  a.step_adv = step_adv;
+  a.seg_active = seg_active;
   a.k_top = (int32_t)w.K;
   a.scores = (const float*)(ws + w.scores);
   a.n = w.n;
@@ -609,11 +615,12 @@ int32_t run_sv(const Geo& g, const TopkWs& w, char* ws, const void* v_cache, flo
     if (g.bf16) STDK_LAUNCH(sparse_sv<uint16_t>, grid, dim3(kSvThreads), 0, s, a);
     else STDK_LAUNCH(sparse_sv<float>, grid, dim3(kSvThreads), 0, s, a);
   }));
-  return run_combine(w, ws, (int32_t)w.nsplit, o_out, lse_out, s);
+  return run_combine(w, ws, (int32_t)w.nsplit, o_out, lse_out, s, seg_active);
 }
 
-int32_t run_combine(const TopkWs& w, char* ws, int32_t np, float* o_out, float* lse_out, hipStream_t s) {
-  CombineArgs a{(const float*)(ws + w.part), o_out, lse_out, np, 0};
+int32_t run_combine(const TopkWs& w, char* ws, int32_t np, float* o_out, float* lse_out, hipStream_t s,
+                    const int32_t* seg_active) {
+  CombineArgs a{(const float*)(ws + w.part), o_out, lse_out, np, 0, seg_active};
   return launch(KID_COMBINE, s, [&](hipEvent_t e0, hipEvent_t e1) { STDK_LAUNCH(combine, dim3((unsigned)w.S), dim3(kHeadDim), 0, s, a); });
 }
 
@@ -1624,8 +1631,41 @@ int32_t run_retopk(const stdk_layout* lay, const retopk_params* p, const retopk_
     const RangeTab tab = make_tab(rng, 1, &n_all);
     const int32_t* active = refresh_now ? nullptr : exact;
     STDK_TRY(run_exact_select(g, w.t, ws, q, k_cache, tab, p->scale, active, support_out, di, s, nullptr, step_dev));
-    // reuse heads: indexed QK over the candidates, rerank, softmax.V
-    if (!refresh_now) {
+    // reuse heads: one workgroup per head scores the candidates, keeps the
+    // top K, forms softmax . V and pushes the cache entry (retopk_attend),
+    // when its LDS holds the candidates; else the rerank, its select and the
+    // softmax . V launch below
+    const size_t att_dyn = attend_lds_bytes((int)w.cand_cap, p->top_k);
+    const bool fused = att_dyn + (size_t)kAttStaticLds <= (size_t)di->max_lds;
+    if (!refresh_now && fused) {
+      RtAttendArgs a{};
+      a.q = q;
+      a.k = (const char*)k_cache;
+      a.v = (const char*)v_cache;
+      a.stride_b_bytes = g.sb_bytes;
+      a.stride_h_bytes = g.sh_bytes;
+      a.exact = exact;
+      a.cand = (const int32_t*)(ws + w.cand);
+      a.n_cand = (const int32_t*)(ws + w.n_cand);
+      a.support_out = support_out;
+      a.o_out = o_out;
+      a.lse_out = lse_out;
+      a.qbar = (const float*)(ws + w.qbar);
+      a.q_hat = st->q_hat;
+      a.support = st->support;
+      a.head = st->head;
+      a.count = st->count;
+      a.cand_cap = (int32_t)w.cand_cap;
+      a.K = p->top_k;
+      a.Hq = g.Hq;
+      a.G = g.G;
+      a.C = p->cache_cap;
+      a.scale = p->scale;
+      STDK_TRY(launch(KID_RT_ATTEND, s, [&](hipEvent_t e0, hipEvent_t e1) {
+        if (g.bf16) STDK_LAUNCH(retopk_attend<uint16_t>, dim3((unsigned)g.S), dim3(kAttThreads), att_dyn, s, a);
+        else STDK_LAUNCH(retopk_attend<float>, dim3((unsigned)g.S), dim3(kAttThreads), att_dyn, s, a);
+      }));
+    } else if (!refresh_now) {
       RtRerankArgs a{};
       a.q = q;
       a.k = (const char*)k_cache;
@@ -1651,11 +1691,12 @@ int32_t run_retopk(const stdk_layout* lay, const retopk_params* p, const retopk_
       }));
       STDK_TRY(run_rerank_select(a, g.S, di, s));
     }
-    // a8: softmax . V over the chosen rows of every head (either path), and
-    // the push of (q_bar, support) by one workgroup per head of that launch
+    // a8: softmax . V over the chosen rows of the heads not done above (the
+    // exact-path heads, or every head without the fused kernel), and the
+    // push of (q_bar, support) by one workgroup per head of that launch
     const SvPush push{(const float*)(ws + w.qbar), support_out, st->q_hat, st->support, st->head, st->count,
                       p->cache_cap, p->top_k};
-    return run_sv(g, w.t, ws, v_cache, o_out, lse_out, s, nullptr, &push, step_dev);
+    return run_sv(g, w.t, ws, v_cache, o_out, lse_out, s, nullptr, &push, step_dev, fused ? exact : nullptr);
   }();
   return finish(rc, ws, w.t.counters);
 }

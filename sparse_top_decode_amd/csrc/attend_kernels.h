@@ -84,11 +84,13 @@ struct CombineArgs {
   float* lse_out;     // [S]
   int32_t np;
   int32_t pad_;
+  const int32_t* seg_active;  // [S] or null: segments whose partials were not written are skipped
 };
 
 __global__ __launch_bounds__(kHeadDim) void combine(CombineArgs a) {
   __shared__ float sm[kMaxPartials], sf[kMaxPartials], red[2];
   const int64_t seg = blockIdx.x;
+  if (a.seg_active && a.seg_active[seg] == 0) return;
   combine_partials(a.part + seg * a.np * kPartStride, a.np, a.o_out + seg * kHeadDim, a.lse_out + seg, sm, sf, red);
 }
 

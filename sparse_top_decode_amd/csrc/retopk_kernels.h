@@ -675,52 +675,21 @@ __global__ __launch_bounds__(kRerankSelThreads) void retopk_rerank_select(RtRera
 // candidate segment and ranks with ballots.
 constexpr int kRselStageMax = 16384;
 
-__global__ __launch_bounds__(kRerankSelThreads) void retopk_rerank_select_lds(RtRerankArgs a) {
-  constexpr int NT = kRerankSelThreads, NW = NT / 64;
-  extern __shared__ uint32_t rsel_dyn[];
-  float* zs = reinterpret_cast<float*>(rsel_dyn);                 // [cand_cap]
-  int32_t* rs = reinterpret_cast<int32_t*>(rsel_dyn + a.cand_cap);  // [cand_cap]
-  __shared__ uint32_t h[kHistBins];
-  __shared__ uint32_t wc[2][NW];
-  __shared__ int s_bin;
-  __shared__ uint32_t s_beyond;
-  const int64_t seg = blockIdx.x;
-  if (a.exact && a.exact[seg]) return;
+// The exact top-K of the M candidate scores zs (rows rs) staged in LDS,
+// ties to the lower candidate index (the candidates ascend by row): radix
+// passes sized to the candidates' key range, then an ordered compaction in
+// which wave w owns a contiguous candidate segment and ballots rank the
+// taken ones. emit(pos, row, z) receives the chosen candidates in ascending
+// order (pos < K); returns how many there are before the cap at K. NT
+// threads; every thread must call it.
+template <int NT, typename Emit>
+STDK_DEV uint32_t lds_topk(const float* zs, const int32_t* rs, uint32_t M, int K, uint32_t* h,
+                           uint32_t (*wc)[NT / 64], int* s_bin_p, uint32_t* s_beyond_p, Emit emit) {
+  constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const uint32_t M = (uint32_t)(a.n_cand ? a.n_cand[seg] : a.n_const);
-  const int32_t* cd = a.cand + seg * a.cand_cap;
-  const float* cz = a.cz + seg * a.cand_cap;
-  const int K = a.K;
-  int32_t* srow = a.sel_row + seg * K;
-  float* sz = a.sel_z + seg * K;
-  int32_t* so = a.support_out + seg * K;
   const bool take_all = M <= (uint32_t)K;
-
-  // stage: U loads of each array in flight per thread (clamped indices, so
-  // the loads carry no condition)
-  constexpr int U = 16;
-  if (M > 0) {
-    for (uint32_t base = 0; base < M; base += NT * U) {
-      float zv[U];
-      int32_t rv[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const uint32_t j = min(base + u * NT + tid, M - 1);
-        zv[u] = cz[j];
-        rv[u] = cd[j];
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const uint32_t j = base + u * NT + tid;
-        if (j < M) {
-          zs[j] = zv[u];
-          rs[j] = rv[u];
-        }
-      }
-    }
-  }
-  __syncthreads();
-
+  int& s_bin = *s_bin_p;
+  uint32_t& s_beyond = *s_beyond_p;
   // radix passes over a window of keys [lo, lo + width): the first spans
   // the candidates' own key range, each later one exactly the bin that
   // holds the K-th key (keys above it were counted in `beyond` already and
@@ -816,19 +785,231 @@ __global__ __launch_bounds__(kRerankSelThreads) void retopk_rerank_select_lds(Rt
     const bool take = gt || (eq && eq_seen + lane_rank(em) < need);
     const uint64_t tm = __ballot(take);
     const uint32_t pos = out + lane_rank(tm);
-    if (take && pos < (uint32_t)K) {
-      const int32_t r = rs[j];
-      srow[pos] = r;
-      sz[pos] = z;
-      so[pos] = r;
-    }
+    if (take && pos < (uint32_t)K) emit(pos, rs[j], z);
     out += (uint32_t)__popcll(tm);
     eq_seen += (uint32_t)__popcll(em);
   }
+  return tot;
+}
+
+
+__global__ __launch_bounds__(kRerankSelThreads) void retopk_rerank_select_lds(RtRerankArgs a) {
+  constexpr int NT = kRerankSelThreads, NW = NT / 64;
+  extern __shared__ uint32_t rsel_dyn[];
+  float* zs = reinterpret_cast<float*>(rsel_dyn);                 // [cand_cap]
+  int32_t* rs = reinterpret_cast<int32_t*>(rsel_dyn + a.cand_cap);  // [cand_cap]
+  __shared__ uint32_t h[kHistBins];
+  __shared__ uint32_t wc[2][NW];
+  __shared__ int s_bin;
+  __shared__ uint32_t s_beyond;
+  const int64_t seg = blockIdx.x;
+  if (a.exact && a.exact[seg]) return;
+  const int tid = threadIdx.x;
+  const uint32_t M = (uint32_t)(a.n_cand ? a.n_cand[seg] : a.n_const);
+  const int32_t* cd = a.cand + seg * a.cand_cap;
+  const float* cz = a.cz + seg * a.cand_cap;
+  const int K = a.K;
+  int32_t* srow = a.sel_row + seg * K;
+  float* sz = a.sel_z + seg * K;
+  int32_t* so = a.support_out + seg * K;
+
+  // stage: U loads of each array in flight per thread (clamped indices, so
+  // the loads carry no condition)
+  constexpr int U = 16;
+  if (M > 0) {
+    for (uint32_t base = 0; base < M; base += NT * U) {
+      float zv[U];
+      int32_t rv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t j = min(base + u * NT + tid, M - 1);
+        zv[u] = cz[j];
+        rv[u] = cd[j];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t j = base + u * NT + tid;
+        if (j < M) {
+          zs[j] = zv[u];
+          rs[j] = rv[u];
+        }
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t tot = lds_topk<NT>(zs, rs, M, K, h, wc, &s_bin, &s_beyond, [&](uint32_t pos, int32_t r, float z) {
+    srow[pos] = r;
+    sz[pos] = z;
+    so[pos] = r;
+  });
   for (uint32_t i = tot + tid; i < (uint32_t)K; i += NT) {
     srow[i] = -1;
     sz[i] = -INFINITY;
     so[i] = -1;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// retopk_attend: the whole reuse path of one head in one workgroup ([RT]
+// 核心方法 4 and the per-step loop): exact scores of the candidates, their
+// top K, renormalised softmax . V over them ([RA] Eq. 2) and the push of
+// (q_bar, support). Candidate rows and scores stay in LDS from scoring to
+// the softmax, so no phase waits on global memory written by another.
+// Scores, selection and support equal those of retopk_rerank +
+// retopk_rerank_select (same per-lane products and sums); o and lse are
+// summed in this kernel's order.
+// ---------------------------------------------------------------------------
+struct RtAttendArgs {
+  const float* q;          // [S][128]
+  const char* k;           // key cache base
+  const char* v;           // value cache base (same layout)
+  int64_t stride_b_bytes, stride_h_bytes;
+  const int32_t* exact;    // [S]: heads on the exact path are skipped
+  const int32_t* cand;     // [S][cand_cap] ascending candidate rows
+  const int32_t* n_cand;   // [S]
+  int32_t* support_out;    // [S][K]
+  float* o_out;            // [S][128]
+  float* lse_out;          // [S]
+  const float* qbar;       // [S][128] unit queries (retopk_select)
+  float* q_hat;            // [S][C][128]
+  int32_t* support;        // [S][C][K]
+  int32_t* head;           // [S]
+  int32_t* count;          // [S]
+  int32_t cand_cap, K, Hq, G, C;
+  float scale;
+};
+
+constexpr int kAttThreads = 1024;
+constexpr int kAttStaticLds = 42 * 1024;  // static LDS of retopk_attend, rounded up
+
+// dynamic LDS bytes of retopk_attend: candidate scores and rows, then the
+// chosen rows' scores and rows
+inline size_t attend_lds_bytes(int cand_cap, int K) { return ((size_t)2 * cand_cap + 2 * (size_t)K) * 4; }
+
+template <typename T>
+__global__ __launch_bounds__(kAttThreads) void retopk_attend(RtAttendArgs a) {
+  constexpr int NT = kAttThreads, NW = NT / 64;
+  constexpr int EPL = KvTraits<T>::EPL, LPR = KvTraits<T>::LPR, ROWB = KvTraits<T>::ROWB;
+  constexpr int NG = NT / LPR;  // row groups: one row per group and load
+  constexpr int U = 8;          // rows per group in flight
+  extern __shared__ uint32_t att_dyn[];
+  float* zs = reinterpret_cast<float*>(att_dyn);                             // [cand_cap]
+  int32_t* rs = reinterpret_cast<int32_t*>(att_dyn + a.cand_cap);            // [cand_cap]
+  float* cz = reinterpret_cast<float*>(att_dyn + 2 * a.cand_cap);            // [K] chosen scores, then weights
+  int32_t* cr = reinterpret_cast<int32_t*>(att_dyn + 2 * a.cand_cap + a.K);  // [K] chosen rows
+  __shared__ uint32_t h[kHistBins];
+  __shared__ uint32_t wc[2][NW];
+  __shared__ float red[NG][kHeadDim];
+  __shared__ float wred[NW];
+  __shared__ int s_bin;
+  __shared__ uint32_t s_beyond;
+  const int64_t seg = blockIdx.x;
+  if (a.exact[seg]) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int gid = tid / LPR, c = tid % LPR;
+  const int b = (int)(seg / a.Hq), hq = (int)(seg % a.Hq), hkv = hq / a.G;
+  const int K = a.K;
+  const uint32_t M = (uint32_t)a.n_cand[seg];
+  const int32_t* cd = a.cand + seg * a.cand_cap;
+  const int hd = a.head[seg], cnt0 = a.count[seg];  // read before any barrier; updated at the end
+  float qr[1][EPL];
+  load_q_slice<T, 1>(a.q, seg, c, qr);
+  for (uint32_t j = tid; j < M; j += NT) rs[j] = cd[j];
+  __syncthreads();
+
+  // 1. exact scores of the candidates: row group gid takes candidates
+  // gid + NG * u, U rows in flight (clamped to the last candidate)
+  const int64_t hoff = (int64_t)b * a.stride_b_bytes + (int64_t)hkv * a.stride_h_bytes + c * 16;
+  const char* kb = a.k + hoff;
+  for (uint32_t base = 0; base < M; base += NG * U) {
+    u32x4 kw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) kw[u] = load16(kb + (int64_t)rs[min(base + gid + NG * u, M - 1)] * ROWB);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float d[1];
+      chunk_dots<T, 1>(kw[u], qr, d);
+      const float sc = group_sum<LPR>(d[0]);
+      const uint32_t j = base + gid + NG * u;
+      if (c == 0 && j < M) zs[j] = sc * a.scale;
+    }
+  }
+  __syncthreads();
+
+  // 2. the top K in candidate (= row) order, into LDS; the support output
+  int32_t* so = a.support_out + seg * K;
+  const uint32_t tot = lds_topk<NT>(zs, rs, M, K, h, wc, &s_bin, &s_beyond, [&](uint32_t pos, int32_t r, float z) {
+    cz[pos] = z;
+    cr[pos] = r;
+    so[pos] = r;
+  });
+  const int nk = (int)min(tot, (uint32_t)K);
+  for (int i = nk + tid; i < K; i += NT) so[i] = -1;
+  __syncthreads();
+
+  // 3. softmax . V over the nk chosen rows: their maximum, the weights
+  // e^{z - m} in place (a -inf score weighs 0, a NaN propagates), their sum
+  // in a fixed order, then the value rows, U per row group in flight
+  float zm = -INFINITY;
+  for (int i = tid; i < nk; i += NT) zm = fmaxf(zm, cz[i]);
+  zm = wave_max(zm);
+  if (lane == 0) wred[w] = zm;
+  __syncthreads();
+  float m = wred[0];
+#pragma unroll
+  for (int v = 1; v < NW; ++v) m = fmaxf(m, wred[v]);
+  __syncthreads();
+  float ps = 0.f;
+  for (int i = tid; i < nk; i += NT) {
+    const float z = cz[i];
+    const float wt = z == -INFINITY ? 0.f : __expf(z - m);
+    cz[i] = wt;
+    ps += wt;
+  }
+  ps = wave_sum(ps);
+  if (lane == 0) wred[w] = ps;
+  __syncthreads();
+  float ssum = 0.f;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) ssum += wred[v];
+  const char* vb = a.v + hoff;
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  for (int base = 0; base < nk; base += NG * U) {
+    u32x4 vw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) vw[u] = load16(vb + (int64_t)cr[min(base + gid + NG * u, nk - 1)] * ROWB);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = base + gid + NG * u;
+      const float wt = i < nk ? cz[i] : 0.f;
+      float x[EPL];
+      unpack16<T>(vw[u], x);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(wt, x[e], acc[e]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) red[gid][c * EPL + e] = acc[e];
+  __syncthreads();
+  if (tid < kHeadDim) {
+    float o = 0.f;
+#pragma unroll 8
+    for (int g = 0; g < NG; ++g) o += red[g][tid];
+    // ssum == 0: no row (o = 0, lse = -inf); a NaN sum propagates
+    a.o_out[seg * kHeadDim + tid] = ssum == 0.f ? 0.f : o / ssum;
+    if (tid == 0) a.lse_out[seg] = ssum == 0.f ? -INFINITY : m + __logf(ssum);
+  }
+
+  // 4. push (q_bar, support) into slot (head + 1) mod C
+  const int slot = hd + 1 == a.C ? 0 : hd + 1;
+  if (tid < kHeadDim) a.q_hat[(seg * a.C + slot) * kHeadDim + tid] = a.qbar[seg * kHeadDim + tid];
+  int32_t* dst = a.support + (seg * a.C + slot) * (int64_t)K;
+  for (int i = tid; i < K; i += NT) dst[i] = i < nk ? cr[i] : -1;
+  if (tid == 0) {
+    a.head[seg] = slot;
+    a.count[seg] = min(cnt0 + 1, a.C);
   }
 }
 

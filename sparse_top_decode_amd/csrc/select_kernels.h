@@ -542,7 +542,8 @@ struct SvArgs {
   int64_t n_seg;
   int32_t do_push, pad2_;
   SvPush push;
-  int64_t* step_adv;          // or null: the pusher of segment 0 adds 1 to both words ([L_t, t]) at its end
+  int64_t* step_adv;          // or null: workgroup 0 adds 1 to both words ([L_t, t]) when it starts (the
+                              // launch is the last of its step; nothing in it reads them)
   // sparse_sv_scored only: the queries and the key cache its rows are
   // scored from
   const float* q;             // [S][128]
@@ -564,6 +565,10 @@ __global__ __launch_bounds__(kSvThreads) void sparse_sv(SvArgs a) {
   __shared__ float red[NG][kHeadDim];
   __shared__ float s_m;
   const int64_t seg = blockIdx.y;
+  if (a.step_adv && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+    a.step_adv[0] += 1;
+    a.step_adv[1] += 1;
+  }
   if (a.seg_active && a.seg_active[seg] == 0) return;
   const int split = blockIdx.x;
   const bool pusher = a.do_push && split == 0;
@@ -652,10 +657,6 @@ __global__ __launch_bounds__(kSvThreads) void sparse_sv(SvArgs a) {
   if (pusher && tid == 0) {
     a.push.head[seg] = push_slot;
     a.push.count[seg] = min(push_cnt + 1, a.push.C);
-    if (a.step_adv && seg == 0) {
-      a.step_adv[0] += 1;
-      a.step_adv[1] += 1;
-    }
   }
 }
 
@@ -703,7 +704,12 @@ __global__ __launch_bounds__(kDsThreads) void sparse_sv_ds(SvArgs a) {
   const int xcd = L % kDsXcds, kk = L / kDsXcds;
   const int64_t seg = (int64_t)(kk / kDsSlices) * kDsXcds + xcd;
   const int slice = kk % kDsSlices;
+  if (a.step_adv && L == 0 && threadIdx.x == 0) {
+    a.step_adv[0] += 1;
+    a.step_adv[1] += 1;
+  }
   if (seg >= a.n_seg) return;  // the grid covers the segments rounded up to a multiple of 8
+  if (a.seg_active && a.seg_active[seg] == 0) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int b = (int)(seg / a.Hq), hq = (int)(seg % a.Hq), hkv = hq / a.G;
   const bool pusher = a.do_push && slice == 0;
@@ -821,10 +827,6 @@ __global__ __launch_bounds__(kDsThreads) void sparse_sv_ds(SvArgs a) {
   if (pusher && tid == 0) {
     a.push.head[seg] = push_slot;
     a.push.count[seg] = min(push_cnt + 1, a.push.C);
-    if (a.step_adv && seg == 0) {
-      a.step_adv[0] += 1;
-      a.step_adv[1] += 1;
-    }
   }
 }
 
