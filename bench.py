@@ -91,7 +91,7 @@ SCAN_SOURCES = ["sparse_top_decode_amd/csrc/scan_kernels.h", "sparse_top_decode_
 METRIC = "top-K decode-attention steps/sec at 128K ctx; K-scan HBM GB/s vs peak"
 TOPK_KERNELS = ("k_scan", "topk_filter_select", "sparse_sv", "dense_attn", "combine", "attn_merge")
 MQ_KERNELS = ("mq_blockmax", "mq_threshold", "mq_collect", "mq_select")
-RETOPK_KERNELS = ("retopk_select", "retopk_vote", "retopk_attend", "retopk_rerank", "retopk_rerank_select",
+RETOPK_KERNELS = ("retopk_reuse", "retopk_select", "retopk_vote", "retopk_attend", "retopk_rerank", "retopk_rerank_select",
                   "k_scan", "topk_filter_select", "sparse_sv", "combine")
 
 
@@ -671,11 +671,23 @@ def bench_retopk(args):
     nc = torch.stack(ncands, dim=-1).cpu().numpy()
     reuse = pth == 0
     mean_m = float(nc[reuse].mean()) if reuse.any() else 0.0
-    # rerank: every candidate key row of the reuse-path heads is read once
-    # (256 B); averaged over the launches (one per step with a reuse head)
+    # reuse heads: every candidate key row is read once (256 B) and, where
+    # one workgroup also forms softmax . V (retopk_reuse, retopk_attend), the
+    # value rows of the min(K, M) kept candidates; retopk_reuse also reads
+    # every head's C cached unit queries (512 B each) and a reuse head's R
+    # picked supports (4 B per row). Averaged over that kernel's launches.
     n_rr = int(kern.get("retopk_rerank", (0, 0))[1])
-    rerank_bytes = float(nc[reuse].sum()) * 256 / max(1, n_rr)
-    roof = roofline(kern, "retopk_rerank", rerank_bytes, None)
+    n_att = int(kern.get("retopk_attend", (0, 0))[1])
+    n_ru = int(kern.get("retopk_reuse", (0, 0))[1])
+    att_rows = float(nc[reuse].sum()) + float(np.minimum(nc[reuse], K).sum())
+    if n_ru:
+        ru_bytes = (att_rows * 256 + float(pth.size) * p["cache_cap"] * 512
+                    + float(reuse.sum()) * p["top_r"] * K * 4)
+        roof = roofline(kern, "retopk_reuse", ru_bytes / n_ru, None)
+    elif n_att:
+        roof = roofline(kern, "retopk_attend", att_rows * 256 / n_att, None)
+    else:
+        roof = roofline(kern, "retopk_rerank", float(nc[reuse].sum()) * 256 / max(1, n_rr), None)
     vs_exact = free_running_vs_exact(rt, reset, qs, k, v, w, p, support, o, lse)
     cpu = None
     if not args.no_cpu:
@@ -687,7 +699,7 @@ def bench_retopk(args):
                 + (f"; voted candidates capped at {p['budget']}" if p["budget"] else ""))
     extra = {"batch": B, "seq_len": L0, "top_k": K, "kv_cache": "bf16", "parallelism": "none (1 GPU)",
              "reuse_fraction": round(float(reuse.mean()), 4), "mean_candidates_reuse": round(mean_m, 1),
-             "rerank_launches": n_rr, "step_api": step_api, "hip_graph": args.graph == "on",
+             "rerank_launches": n_rr, "attend_launches": n_att, "reuse_launches": n_ru, "step_api": step_api, "hip_graph": args.graph == "on",
              "vs_exact_free_running": vs_exact}
     return line(args, ms, workload, extra, roof, kern, cpu)
 

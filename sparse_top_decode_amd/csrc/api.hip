@@ -59,14 +59,14 @@ int32_t ok() {
 enum KernelId {
   KID_SCAN, KID_SELECT, KID_SV, KID_DENSE, KID_COMBINE, KID_MERGE, KID_FILL,
   KID_RT_SELECT, KID_RT_RERANK, KID_RT_RSEL, KID_RT_INIT, KID_MQ_BLOCKMAX, KID_MQ_THRESH,
-  KID_MQ_COLLECT, KID_MQ_SELECT, KID_MQ_FILL, KID_RT_VOTE, KID_Q8_QUANT, KID_READ, KID_RT_ATTEND, KID_COUNT
+  KID_MQ_COLLECT, KID_MQ_SELECT, KID_MQ_FILL, KID_RT_VOTE, KID_Q8_QUANT, KID_READ, KID_RT_ATTEND, KID_RT_REUSE, KID_COUNT
 };
 const char* const kKernelNames[KID_COUNT] = {
     "k_scan",        "topk_filter_select",             "sparse_sv",
     "dense_attn",  "combine",       "attn_merge",    "fill_empty",           "retopk_select",
     "retopk_rerank", "retopk_rerank_select", "retopk_init", "mq_blockmax",
     "mq_threshold",  "mq_collect",    "mq_select",     "mq_fill",       "retopk_vote",   "k_quantize",
-    "hbm_read",      "retopk_attend"};
+    "hbm_read",      "retopk_attend", "retopk_reuse"};
 
 struct Profiler {
   std::mutex mu;
@@ -249,6 +249,10 @@ int32_t dev_info(DevInfo** out) {
                               std::max(0, d.max_lds - kAttStaticLds));
     (void)hipFuncSetAttribute((const void*)retopk_attend<float>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               std::max(0, d.max_lds - kAttStaticLds));
+    (void)hipFuncSetAttribute((const void*)retopk_reuse<uint16_t>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              std::max(0, d.max_lds - kReuseStaticLds));
+    (void)hipFuncSetAttribute((const void*)retopk_reuse<float>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              std::max(0, d.max_lds - kReuseStaticLds));
     (void)hipFuncSetAttribute((const void*)retopk_rerank_select_lds, hipFuncAttributeMaxDynamicSharedMemorySize,
                               std::max(0, d.max_lds - 12 * 1024));
     (void)hipFuncSetAttribute((const void*)sparse_sv_ds<uint16_t>, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1555,7 +1559,38 @@ int32_t run_retopk(const stdk_layout* lay, const retopk_params* p, const retopk_
     const bool refresh_now = !dev && p->refresh > 0 && (t % p->refresh) == 0;
     int32_t* exact = (int32_t*)(ws + w.exact);
 
-    // a6: selector (cosine, path, top-R, candidate union)
+    // a6: selector (cosine, path, top-R, candidate union); without a vote,
+    // and when the bitmap and the reuse path's LDS fit, one workgroup per
+    // head also scores the candidates, keeps the top K, forms softmax . V
+    // and pushes the cache entry (retopk_reuse); else retopk_select, then
+    // (vote,) retopk_attend or the rerank launches below
+    const size_t att_dyn = attend_lds_bytes((int)w.cand_cap, p->top_k);
+    const size_t bm_bytes = (size_t)w.words * 4;
+    const bool one_launch =
+        p->budget == 0 && att_dyn + bm_bytes + (size_t)kReuseStaticLds <= (size_t)di->max_lds;
+    RtAttendArgs at{};
+    at.q = q;
+    at.k = (const char*)k_cache;
+    at.v = (const char*)v_cache;
+    at.stride_b_bytes = g.sb_bytes;
+    at.stride_h_bytes = g.sh_bytes;
+    at.exact = exact;
+    at.cand = (const int32_t*)(ws + w.cand);
+    at.n_cand = (const int32_t*)(ws + w.n_cand);
+    at.support_out = support_out;
+    at.o_out = o_out;
+    at.lse_out = lse_out;
+    at.qbar = (const float*)(ws + w.qbar);
+    at.q_hat = st->q_hat;
+    at.support = st->support;
+    at.head = st->head;
+    at.count = st->count;
+    at.cand_cap = (int32_t)w.cand_cap;
+    at.K = p->top_k;
+    at.Hq = g.Hq;
+    at.G = g.G;
+    at.C = p->cache_cap;
+    at.scale = p->scale;
     {
       RtSelArgs a{};
       a.q = q;
@@ -1587,12 +1622,18 @@ int32_t run_retopk(const stdk_layout* lay, const retopk_params* p, const retopk_
         a.rec_slot = (int32_t*)(ws + w.rec_slot);
         a.rec_rho = (float*)(ws + w.rec_rho);
       }
-      const size_t bm_bytes = (size_t)w.words * 4;
       const bool lds = bm_bytes + 12 * 1024 <= (size_t)di->max_lds;
-      STDK_TRY(launch(KID_RT_SELECT, s, [&](hipEvent_t e0, hipEvent_t e1) {
-        if (lds) STDK_LAUNCH(retopk_select<true>, dim3((unsigned)g.S), dim3(kRtSelThreads), bm_bytes, s, a);
-        else STDK_LAUNCH(retopk_select<false>, dim3((unsigned)g.S), dim3(kRtSelThreads), 0, s, a);
-      }));
+      if (one_launch) {
+        STDK_TRY(launch(KID_RT_REUSE, s, [&](hipEvent_t e0, hipEvent_t e1) {
+          if (g.bf16) STDK_LAUNCH(retopk_reuse<uint16_t>, dim3((unsigned)g.S), dim3(kAttThreads), att_dyn + bm_bytes, s, a, at);
+          else STDK_LAUNCH(retopk_reuse<float>, dim3((unsigned)g.S), dim3(kAttThreads), att_dyn + bm_bytes, s, a, at);
+        }));
+      } else {
+        STDK_TRY(launch(KID_RT_SELECT, s, [&](hipEvent_t e0, hipEvent_t e1) {
+          if (lds) STDK_LAUNCH(retopk_select<true>, dim3((unsigned)g.S), dim3(kRtSelThreads), bm_bytes, s, a);
+          else STDK_LAUNCH(retopk_select<false>, dim3((unsigned)g.S), dim3(kRtSelThreads), 0, s, a);
+        }));
+      }
     }
     // confidence vote: cap the candidates of the reuse heads
     if (p->budget > 0 && !refresh_now) {
@@ -1631,41 +1672,17 @@ int32_t run_retopk(const stdk_layout* lay, const retopk_params* p, const retopk_
     const RangeTab tab = make_tab(rng, 1, &n_all);
     const int32_t* active = refresh_now ? nullptr : exact;
     STDK_TRY(run_exact_select(g, w.t, ws, q, k_cache, tab, p->scale, active, support_out, di, s, nullptr, step_dev));
-    // reuse heads: one workgroup per head scores the candidates, keeps the
-    // top K, forms softmax . V and pushes the cache entry (retopk_attend),
-    // when its LDS holds the candidates; else the rerank, its select and the
-    // softmax . V launch below
-    const size_t att_dyn = attend_lds_bytes((int)w.cand_cap, p->top_k);
-    const bool fused = att_dyn + (size_t)kAttStaticLds <= (size_t)di->max_lds;
-    if (!refresh_now && fused) {
-      RtAttendArgs a{};
-      a.q = q;
-      a.k = (const char*)k_cache;
-      a.v = (const char*)v_cache;
-      a.stride_b_bytes = g.sb_bytes;
-      a.stride_h_bytes = g.sh_bytes;
-      a.exact = exact;
-      a.cand = (const int32_t*)(ws + w.cand);
-      a.n_cand = (const int32_t*)(ws + w.n_cand);
-      a.support_out = support_out;
-      a.o_out = o_out;
-      a.lse_out = lse_out;
-      a.qbar = (const float*)(ws + w.qbar);
-      a.q_hat = st->q_hat;
-      a.support = st->support;
-      a.head = st->head;
-      a.count = st->count;
-      a.cand_cap = (int32_t)w.cand_cap;
-      a.K = p->top_k;
-      a.Hq = g.Hq;
-      a.G = g.G;
-      a.C = p->cache_cap;
-      a.scale = p->scale;
+    // reuse heads (not done above): one workgroup per head scores the
+    // candidates, keeps the top K, forms softmax . V and pushes the cache
+    // entry (retopk_attend), when its LDS holds the candidates; else the
+    // rerank, its select and the softmax . V launch below
+    const bool fused = one_launch || att_dyn + (size_t)kAttStaticLds <= (size_t)di->max_lds;
+    if (!refresh_now && !one_launch && fused) {
       STDK_TRY(launch(KID_RT_ATTEND, s, [&](hipEvent_t e0, hipEvent_t e1) {
-        if (g.bf16) STDK_LAUNCH(retopk_attend<uint16_t>, dim3((unsigned)g.S), dim3(kAttThreads), att_dyn, s, a);
-        else STDK_LAUNCH(retopk_attend<float>, dim3((unsigned)g.S), dim3(kAttThreads), att_dyn, s, a);
+        if (g.bf16) STDK_LAUNCH(retopk_attend<uint16_t>, dim3((unsigned)g.S), dim3(kAttThreads), att_dyn, s, at);
+        else STDK_LAUNCH(retopk_attend<float>, dim3((unsigned)g.S), dim3(kAttThreads), att_dyn, s, at);
       }));
-    } else if (!refresh_now) {
+    } else if (!refresh_now && !fused) {
       RtRerankArgs a{};
       a.q = q;
       a.k = (const char*)k_cache;

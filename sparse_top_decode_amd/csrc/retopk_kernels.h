@@ -84,20 +84,43 @@ constexpr int kRtSelThreads = 256;
 constexpr int kMaxCache = 64;
 constexpr int kMaxVote = 8;  // recalled entries a confidence vote can weigh (masks fit a byte)
 
-template <bool kLdsBitmap>
-__global__ __launch_bounds__(kRtSelThreads) void retopk_select(RtSelArgs a) {
-  extern __shared__ uint32_t dyn[];
-  constexpr int kGroups = kRtSelThreads / 8;  // cache slots per pass
-  __shared__ float part[kMaxCache][8];
-  __shared__ float sq[8];
-  __shared__ int slot_of[kMaxCache];
-  __shared__ uint2 rkey[kMaxCache];
-  __shared__ uint32_t tmp[kRtSelThreads / 64 + 1];
-  __shared__ int s_path, s_npick;
-  const int64_t seg = blockIdx.x;
+// Shared-memory state of the selector phases of one head.
+template <int NT>
+struct RtSelLds {
+  float part[kMaxCache][8];
+  float sq[8];
+  float qb[kHeadDim];  // the unit query
+  int slot_of[kMaxCache];
+  uint2 rkey[kMaxCache];
+  uint32_t tmp[NT / 64 + 1];
+  int rec_slot[kMaxVote];
+  float rec_rho[kMaxVote];
+  int path, npick, nrec;
+};
+
+// What the selector of one head decided (uniform over the workgroup).
+struct RtSelOut {
+  int path;      // 0 reuse, 1 similarity fallback, 2 refresh
+  uint32_t M;    // reuse path: candidates written
+  int64_t L_t;   // visible rows this step
+};
+
+// The selector of head `seg` with NT threads: the unit query (to ls.qb), the
+// cosines with the cached entries, the path, and on the reuse path the union
+// of the R most similar supports with the recent window, written in
+// ascending row order to cd[0, min(union, cand_cap)) (global or LDS). `hd`
+// and `cnt` are the FIFO's head and count as they stood before this step.
+// bm: the bitmap of the visible rows, in LDS (kLdsBitmap) or global memory.
+// Nothing else goes to global memory here: rt_select_store writes the
+// per-head results once the workgroup's loads are done (a store issued
+// before a wait on an earlier load makes that wait include the store).
+template <int NT, bool kLdsBitmap>
+STDK_DEV RtSelOut rt_select_head(const RtSelArgs& a, int64_t seg, int hd, int cnt, RtSelLds<NT>& ls,
+                                 uint32_t* bm, int32_t* cd) {
+  constexpr int kGroups = NT / 8;  // cache slots per pass
+  constexpr int kPass = (kMaxCache + kGroups - 1) / kGroups;
   const int tid = threadIdx.x;
   const int C = a.C, K = a.K;
-  const int hd = a.head[seg], cnt = a.count[seg];
   const int j = tid & 7, g = tid >> 3;  // part of the 128 dims, cache slot within a pass
   int64_t L_t = a.L_t;
   int refresh_now = a.refresh_now;
@@ -108,10 +131,9 @@ __global__ __launch_bounds__(kRtSelThreads) void retopk_select(RtSelArgs a) {
   }
 
   // One memory round trip: every thread requests its 16 query components and
-  // the same components of its cache slots (slot g + 32 * pass).
+  // the same components of its cache slots (slot g + kGroups * pass).
   float qx[16];
   load16f(a.q + seg * kHeadDim + 16 * j, qx);
-  constexpr int kPass = kMaxCache / kGroups;
   float qh[kPass][16];
 #pragma unroll
   for (int ps = 0; ps < kPass; ++ps) {
@@ -119,17 +141,15 @@ __global__ __launch_bounds__(kRtSelThreads) void retopk_select(RtSelArgs a) {
     load16f(a.q_hat + (seg * C + sl) * kHeadDim + 16 * j, qh[ps]);
   }
   // unit query
-  if (tid < 8) sq[j] = sumsq16(qx);
+  if (tid < 8) ls.sq[j] = sumsq16(qx);
   __syncthreads();
-  const float nrm = norm_of_parts(sq);
+  const float nrm = norm_of_parts(ls.sq);
   float qn[16];
 #pragma unroll
   for (int e = 0; e < 16; ++e) qn[e] = nrm > 0.f ? qx[e] / nrm : 0.f;
   if (tid < 8) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<float4*>(a.qbar + seg * kHeadDim + 16 * j + 4 * i) =
-          make_float4(qn[4 * i], qn[4 * i + 1], qn[4 * i + 2], qn[4 * i + 3]);
+    for (int e = 0; e < 16; ++e) ls.qb[16 * j + e] = qn[e];
   }
   // cosines: 16-dim partial dot products, summed in part order below
 #pragma unroll
@@ -139,11 +159,10 @@ __global__ __launch_bounds__(kRtSelThreads) void retopk_select(RtSelArgs a) {
       float t = 0.f;
 #pragma unroll
       for (int e = 0; e < 16; ++e) t = fmaf(qn[e], qh[ps][e], t);
-      part[sl][j] = t;
+      ls.part[sl][j] = t;
     }
   }
   const int Wd = a.step ? (int)((L_t + 31) / 32) : a.bitmap_words;
-  uint32_t* bm = kLdsBitmap ? dyn : (a.gbitmap + seg * (int64_t)a.bitmap_words);
   __syncthreads();
   // Wave 0 (C <= 64 slots, one per lane): the cosines, the path, the top R
   // and the picked slots in slot order, with LDS broadcasts and ballots. The entry
@@ -156,7 +175,7 @@ __global__ __launch_bounds__(kRtSelThreads) void retopk_select(RtSelArgs a) {
     if (sl < C) {
       float r = 0.f;
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) r += part[sl][jj];
+      for (int jj = 0; jj < 8; ++jj) r += ls.part[sl][jj];
       age = hd - sl;
       if (age < 0) age += C;
       valid = age < cnt;
@@ -167,12 +186,7 @@ __global__ __launch_bounds__(kRtSelThreads) void retopk_select(RtSelArgs a) {
     if (refresh_now) path = 2;
     else if (cnt == 0 || best < a.tau) path = 1;
     else path = 0;
-    if (sl == 0) {
-      s_path = path;
-      a.path[seg] = path;
-      a.exact[seg] = path != 0;
-      if (a.path_out) a.path_out[seg] = path;
-    }
+    if (sl == 0) ls.path = path;
     if (path == 0) {
       // top-R by (cosine descending, age ascending): the rank is the number
       // of valid entries with a larger (cosine key, ~age) pair; invalid
@@ -180,7 +194,7 @@ __global__ __launch_bounds__(kRtSelThreads) void retopk_select(RtSelArgs a) {
       // every lane reads all 64 (same address across the wave: broadcast
       // reads, issued back to back).
       const uint32_t khi = valid ? f2key(re) : 0u, klo = valid ? ~(uint32_t)age : 0u;
-      rkey[sl] = make_uint2(khi, klo);
+      ls.rkey[sl] = make_uint2(khi, klo);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
@@ -188,64 +202,57 @@ __global__ __launch_bounds__(kRtSelThreads) void retopk_select(RtSelArgs a) {
       int rank = 0;
 #pragma unroll
       for (int f = 0; f < kMaxCache; ++f) {
-        const uint2 kf = rkey[f];
+        const uint2 kf = ls.rkey[f];
         rank += ((((uint64_t)kf.x << 32) | kf.y) > mine) ? 1 : 0;
       }
       const bool pk = valid && rank < a.R;
-      if (pk && a.rec_slot && rank < kMaxVote) {
-        a.rec_slot[seg * kMaxVote + rank] = sl;
-        a.rec_rho[seg * kMaxVote + rank] = re;
+      if (pk && rank < kMaxVote) {
+        ls.rec_slot[rank] = sl;
+        ls.rec_rho[rank] = re;
       }
       const uint64_t pm = __ballot(pk);
-      if (pk) slot_of[lane_rank(pm)] = sl;
-      if (sl == 0) s_npick = __popcll(pm);
+      if (pk) ls.slot_of[lane_rank(pm)] = sl;
+      if (sl == 0) ls.npick = __popcll(pm);
+    } else if (sl == 0) {
+      ls.npick = 0;
     }
   }
   if (kLdsBitmap)
-    for (int i = tid; i < Wd; i += kRtSelThreads) bm[i] = 0u;
+    for (int i = tid; i < Wd; i += NT) bm[i] = 0u;
   __syncthreads();
-  const int path = s_path;
-  if (path != 0) {
-    if (tid == 0) {
-      a.n_cand[seg] = (int32_t)L_t;
-      if (a.n_cand_out) a.n_cand_out[seg] = (int32_t)L_t;
-    }
-    if (a.cand_out)
-      for (int i = tid; i < a.cand_cap; i += kRtSelThreads) a.cand_out[seg * a.cand_cap + i] = -1;
-    return;
-  }
+  const int path = ls.path;
+  if (path != 0) return RtSelOut{path, 0u, L_t};
   if (!kLdsBitmap) {
-    for (int i = tid; i < Wd; i += kRtSelThreads) bm[i] = 0u;
+    for (int i = tid; i < Wd; i += NT) bm[i] = 0u;
     __syncthreads();
   }
   const int64_t L = L_t;
   // union of the picked supports: index f of the flattened R x K list is
   // entry f % K of picked slot f / K; kU loads per thread are in flight
-  // before their bits are set
+  // (clamped to the last entry, no branches) before their bits are set
   {
-    constexpr int kU = 8;
-    const int total = s_npick * K;
-    for (int f0 = 0; f0 < total; f0 += kRtSelThreads * kU) {
+    constexpr int kU = NT >= 1024 ? 4 : 8;
+    const int total = ls.npick * K;
+    for (int f0 = 0; f0 < total; f0 += NT * kU) {
       int32_t x[kU];
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
-        const int f = min(f0 + u * kRtSelThreads + tid, total - 1);
-        x[u] = a.support[(seg * C + slot_of[f / K]) * (int64_t)K + f % K];
+        const int f = min(f0 + u * NT + tid, total - 1);
+        x[u] = a.support[(seg * C + ls.slot_of[f / K]) * (int64_t)K + f % K];
       }
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
-        const int f = f0 + u * kRtSelThreads + tid;
+        const int f = f0 + u * NT + tid;
         if (f < total && x[u] >= 0 && x[u] < L) atomicOr(&bm[x[u] >> 5], 1u << (x[u] & 31));
       }
     }
   }
-  for (int64_t x = max((int64_t)0, L - a.W) + tid; x < L; x += kRtSelThreads)
-    atomicOr(&bm[x >> 5], 1u << (x & 31));
+  for (int64_t x = max((int64_t)0, L - a.W) + tid; x < L; x += NT) atomicOr(&bm[x >> 5], 1u << (x & 31));
   __syncthreads();
   // ascending compaction: wave w reads words [w0, w1) 64 at a time (lane l
   // the word w0 + 64 i + l), counts its bits, and the waves' offsets come
   // from one scan; then each word's bits go out at its wave-scan position
-  constexpr int NWv = kRtSelThreads / 64;
+  constexpr int NWv = NT / 64;
   const int lane = tid & 63, wv = tid >> 6;
   const int wper = ((Wd + NWv - 1) / NWv + 63) & ~63;
   const int w0 = min(Wd, wv * wper), w1 = min(Wd, w0 + wper);
@@ -253,9 +260,8 @@ __global__ __launch_bounds__(kRtSelThreads) void retopk_select(RtSelArgs a) {
   for (int i = w0 + lane; i < w1; i += 64) c0 += __popc(bm[i]);
   uint32_t total;
   const uint32_t wave_cnt = __shfl(wave_incl_scan(c0), 63, 64);
-  uint32_t r = block_excl_scan<kRtSelThreads>(lane == 0 ? wave_cnt : 0u, tmp, &total);
+  uint32_t r = block_excl_scan<NT>(lane == 0 ? wave_cnt : 0u, ls.tmp, &total);
   r = __shfl(r, 0, 64);
-  int32_t* cd = a.cand + seg * a.cand_cap;
   for (int i0 = w0; i0 < w1; i0 += 64) {
     const int i = i0 + lane;
     uint32_t bits = i < w1 ? bm[i] : 0u;
@@ -263,24 +269,53 @@ __global__ __launch_bounds__(kRtSelThreads) void retopk_select(RtSelArgs a) {
     const uint32_t incl = wave_incl_scan(n);
     uint32_t pos = r + incl - n;
     while (bits) {
-      const int j = __ffs(bits) - 1;
+      const int jb = __ffs(bits) - 1;
       bits &= bits - 1;
-      if (pos < (uint32_t)a.cand_cap) cd[pos] = i * 32 + j;
+      if (pos < (uint32_t)a.cand_cap) cd[pos] = i * 32 + jb;
       ++pos;
     }
     r += __shfl(incl, 63, 64);
   }
+  return RtSelOut{0, min(total, (uint32_t)a.cand_cap), L_t};
+}
+
+// The per-head results of rt_select_head: the unit query, the path and the
+// exact flag, the candidate count (L_t on the exact path), the recalled
+// entries of a vote, and the optional copies for the caller. cd: the
+// candidate list, complete and visible to every thread (after a barrier).
+template <int NT>
+STDK_DEV void rt_select_store(const RtSelArgs& a, int64_t seg, const RtSelLds<NT>& ls, const RtSelOut& r,
+                              const int32_t* cd) {
+  const int tid = threadIdx.x;
+  for (int e = tid; e < kHeadDim; e += NT) a.qbar[seg * kHeadDim + e] = ls.qb[e];
+  const int32_t nc = r.path == 0 ? (int32_t)r.M : (int32_t)r.L_t;
   if (tid == 0) {
-    const int32_t M = (int32_t)min(total, (uint32_t)a.cand_cap);
-    a.n_cand[seg] = M;
-    if (a.n_cand_out) a.n_cand_out[seg] = M;
+    a.path[seg] = r.path;
+    a.exact[seg] = r.path != 0;
+    a.n_cand[seg] = nc;
+    if (a.path_out) a.path_out[seg] = r.path;
+    if (a.n_cand_out) a.n_cand_out[seg] = nc;
   }
-  if (a.cand_out) {
-    __syncthreads();
-    const int32_t M = (int32_t)min(total, (uint32_t)a.cand_cap);
-    for (int i = tid; i < a.cand_cap; i += kRtSelThreads)
-      a.cand_out[seg * a.cand_cap + i] = i < M ? cd[i] : -1;
+  if (a.rec_slot && r.path == 0 && tid < min(ls.npick, kMaxVote)) {
+    a.rec_slot[seg * kMaxVote + tid] = ls.rec_slot[tid];
+    a.rec_rho[seg * kMaxVote + tid] = ls.rec_rho[tid];
   }
+  if (a.cand_out)
+    for (int i = tid; i < a.cand_cap; i += NT)
+      a.cand_out[seg * a.cand_cap + i] = r.path == 0 && i < (int)r.M ? cd[i] : -1;
+}
+
+template <bool kLdsBitmap>
+__global__ __launch_bounds__(kRtSelThreads) void retopk_select(RtSelArgs a) {
+  extern __shared__ uint32_t dyn[];
+  __shared__ RtSelLds<kRtSelThreads> ls;
+  const int64_t seg = blockIdx.x;
+  const int hd = a.head[seg], cnt = a.count[seg];
+  uint32_t* bm = kLdsBitmap ? dyn : (a.gbitmap + seg * (int64_t)a.bitmap_words);
+  int32_t* cd = a.cand + seg * a.cand_cap;
+  const RtSelOut r = rt_select_head<kRtSelThreads, kLdsBitmap>(a, seg, hd, cnt, ls, bm, cd);
+  __syncthreads();
+  rt_select_store<kRtSelThreads>(a, seg, ls, r, cd);
 }
 
 // ---------------------------------------------------------------------------
@@ -850,14 +885,15 @@ __global__ __launch_bounds__(kRerankSelThreads) void retopk_rerank_select_lds(Rt
 }
 
 // ---------------------------------------------------------------------------
-// retopk_attend: the whole reuse path of one head in one workgroup ([RT]
-// 核心方法 4 and the per-step loop): exact scores of the candidates, their
-// top K, renormalised softmax . V over them ([RA] Eq. 2) and the push of
-// (q_bar, support). Candidate rows and scores stay in LDS from scoring to
-// the softmax, so no phase waits on global memory written by another.
-// Scores, selection and support equal those of retopk_rerank +
-// retopk_rerank_select (same per-lane products and sums); o and lse are
-// summed in this kernel's order.
+// The reuse path of one head after its candidates are known ([RT] 核心方法 4
+// and the per-step loop): exact scores of the candidates, their top K,
+// renormalised softmax . V over them ([RA] Eq. 2) and the push of (q_bar,
+// support). Candidate rows and scores stay in LDS from scoring to the
+// softmax, so no phase waits on global memory written by another. Scores,
+// selection and support equal those of retopk_rerank + retopk_rerank_select
+// (same per-lane products and sums); o and lse are summed in this order.
+// retopk_attend runs it on retopk_select's candidate list; retopk_reuse
+// runs the selector and it in one workgroup, the candidates never leaving LDS.
 // ---------------------------------------------------------------------------
 struct RtAttendArgs {
   const float* q;          // [S][128]
@@ -880,53 +916,52 @@ struct RtAttendArgs {
 };
 
 constexpr int kAttThreads = 1024;
-constexpr int kAttStaticLds = 42 * 1024;  // static LDS of retopk_attend, rounded up
+constexpr int kAttStaticLds = 42 * 1024;    // static LDS of retopk_attend, rounded up
+constexpr int kReuseStaticLds = 46 * 1024;  // static LDS of retopk_reuse, rounded up
 
 // dynamic LDS bytes of retopk_attend: candidate scores and rows, then the
 // chosen rows' scores and rows
 inline size_t attend_lds_bytes(int cand_cap, int K) { return ((size_t)2 * cand_cap + 2 * (size_t)K) * 4; }
 
-template <typename T>
-__global__ __launch_bounds__(kAttThreads) void retopk_attend(RtAttendArgs a) {
-  constexpr int NT = kAttThreads, NW = NT / 64;
+template <typename T, int NT>
+struct RtAttLds {
+  uint32_t h[kHistBins];
+  uint32_t wc[2][NT / 64];
+  float red[NT / KvTraits<T>::LPR][kHeadDim];
+  float wred[NT / 64];
+  int s_bin;
+  uint32_t s_beyond;
+};
+
+// rs: the M ascending candidate rows of head seg, in LDS; zs, cz, cr: LDS
+// for cand_cap candidate scores, K chosen scores and K chosen rows. qbar:
+// the head's unit query (LDS or global). hd, cnt0: the FIFO's head and count
+// before this step.
+template <typename T, int NT>
+STDK_DEV void rt_attend_head(const RtAttendArgs& a, int64_t seg, const int32_t* rs, uint32_t M, float* zs,
+                             float* cz, int32_t* cr, RtAttLds<T, NT>& ls, const float* qbar, int hd, int cnt0) {
+  constexpr int NW = NT / 64;
   constexpr int EPL = KvTraits<T>::EPL, LPR = KvTraits<T>::LPR, ROWB = KvTraits<T>::ROWB;
   constexpr int NG = NT / LPR;  // row groups: one row per group and load
-  constexpr int U = 8;          // rows per group in flight
-  extern __shared__ uint32_t att_dyn[];
-  float* zs = reinterpret_cast<float*>(att_dyn);                             // [cand_cap]
-  int32_t* rs = reinterpret_cast<int32_t*>(att_dyn + a.cand_cap);            // [cand_cap]
-  float* cz = reinterpret_cast<float*>(att_dyn + 2 * a.cand_cap);            // [K] chosen scores, then weights
-  int32_t* cr = reinterpret_cast<int32_t*>(att_dyn + 2 * a.cand_cap + a.K);  // [K] chosen rows
-  __shared__ uint32_t h[kHistBins];
-  __shared__ uint32_t wc[2][NW];
-  __shared__ float red[NG][kHeadDim];
-  __shared__ float wred[NW];
-  __shared__ int s_bin;
-  __shared__ uint32_t s_beyond;
-  const int64_t seg = blockIdx.x;
-  if (a.exact[seg]) return;
+  constexpr int U = 8;          // value rows per group in flight
+  constexpr int UK = 16;        // key rows per group in flight
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int gid = tid / LPR, c = tid % LPR;
   const int b = (int)(seg / a.Hq), hq = (int)(seg % a.Hq), hkv = hq / a.G;
   const int K = a.K;
-  const uint32_t M = (uint32_t)a.n_cand[seg];
-  const int32_t* cd = a.cand + seg * a.cand_cap;
-  const int hd = a.head[seg], cnt0 = a.count[seg];  // read before any barrier; updated at the end
   float qr[1][EPL];
   load_q_slice<T, 1>(a.q, seg, c, qr);
-  for (uint32_t j = tid; j < M; j += NT) rs[j] = cd[j];
-  __syncthreads();
 
   // 1. exact scores of the candidates: row group gid takes candidates
-  // gid + NG * u, U rows in flight (clamped to the last candidate)
+  // gid + NG * u, UK rows in flight (clamped to the last candidate)
   const int64_t hoff = (int64_t)b * a.stride_b_bytes + (int64_t)hkv * a.stride_h_bytes + c * 16;
   const char* kb = a.k + hoff;
-  for (uint32_t base = 0; base < M; base += NG * U) {
-    u32x4 kw[U];
+  for (uint32_t base = 0; base < M; base += NG * UK) {
+    u32x4 kw[UK];
 #pragma unroll
-    for (int u = 0; u < U; ++u) kw[u] = load16(kb + (int64_t)rs[min(base + gid + NG * u, M - 1)] * ROWB);
+    for (int u = 0; u < UK; ++u) kw[u] = load16(kb + (int64_t)rs[min(base + gid + NG * u, M - 1)] * ROWB);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < UK; ++u) {
       float d[1];
       chunk_dots<T, 1>(kw[u], qr, d);
       const float sc = group_sum<LPR>(d[0]);
@@ -936,15 +971,13 @@ __global__ __launch_bounds__(kAttThreads) void retopk_attend(RtAttendArgs a) {
   }
   __syncthreads();
 
-  // 2. the top K in candidate (= row) order, into LDS; the support output
-  int32_t* so = a.support_out + seg * K;
-  const uint32_t tot = lds_topk<NT>(zs, rs, M, K, h, wc, &s_bin, &s_beyond, [&](uint32_t pos, int32_t r, float z) {
-    cz[pos] = z;
-    cr[pos] = r;
-    so[pos] = r;
-  });
+  // 2. the top K in candidate (= row) order, into LDS
+  const uint32_t tot = lds_topk<NT>(zs, rs, M, K, ls.h, ls.wc, &ls.s_bin, &ls.s_beyond,
+                                    [&](uint32_t pos, int32_t r, float z) {
+                                      cz[pos] = z;
+                                      cr[pos] = r;
+                                    });
   const int nk = (int)min(tot, (uint32_t)K);
-  for (int i = nk + tid; i < K; i += NT) so[i] = -1;
   __syncthreads();
 
   // 3. softmax . V over the nk chosen rows: their maximum, the weights
@@ -953,11 +986,11 @@ __global__ __launch_bounds__(kAttThreads) void retopk_attend(RtAttendArgs a) {
   float zm = -INFINITY;
   for (int i = tid; i < nk; i += NT) zm = fmaxf(zm, cz[i]);
   zm = wave_max(zm);
-  if (lane == 0) wred[w] = zm;
+  if (lane == 0) ls.wred[w] = zm;
   __syncthreads();
-  float m = wred[0];
+  float m = ls.wred[0];
 #pragma unroll
-  for (int v = 1; v < NW; ++v) m = fmaxf(m, wred[v]);
+  for (int v = 1; v < NW; ++v) m = fmaxf(m, ls.wred[v]);
   __syncthreads();
   float ps = 0.f;
   for (int i = tid; i < nk; i += NT) {
@@ -967,11 +1000,11 @@ __global__ __launch_bounds__(kAttThreads) void retopk_attend(RtAttendArgs a) {
     ps += wt;
   }
   ps = wave_sum(ps);
-  if (lane == 0) wred[w] = ps;
+  if (lane == 0) ls.wred[w] = ps;
   __syncthreads();
   float ssum = 0.f;
 #pragma unroll
-  for (int v = 0; v < NW; ++v) ssum += wred[v];
+  for (int v = 0; v < NW; ++v) ssum += ls.wred[v];
   const char* vb = a.v + hoff;
   float acc[EPL];
 #pragma unroll
@@ -991,26 +1024,76 @@ __global__ __launch_bounds__(kAttThreads) void retopk_attend(RtAttendArgs a) {
     }
   }
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) red[gid][c * EPL + e] = acc[e];
+  for (int e = 0; e < EPL; ++e) ls.red[gid][c * EPL + e] = acc[e];
   __syncthreads();
   if (tid < kHeadDim) {
     float o = 0.f;
 #pragma unroll 8
-    for (int g = 0; g < NG; ++g) o += red[g][tid];
+    for (int g = 0; g < NG; ++g) o += ls.red[g][tid];
     // ssum == 0: no row (o = 0, lse = -inf); a NaN sum propagates
     a.o_out[seg * kHeadDim + tid] = ssum == 0.f ? 0.f : o / ssum;
     if (tid == 0) a.lse_out[seg] = ssum == 0.f ? -INFINITY : m + __logf(ssum);
   }
 
-  // 4. push (q_bar, support) into slot (head + 1) mod C
+  // 4. the support output, and the push of (q_bar, support) into slot
+  // (head + 1) mod C; every global store of the head comes after its last load
   const int slot = hd + 1 == a.C ? 0 : hd + 1;
-  if (tid < kHeadDim) a.q_hat[(seg * a.C + slot) * kHeadDim + tid] = a.qbar[seg * kHeadDim + tid];
+  if (tid < kHeadDim) a.q_hat[(seg * a.C + slot) * kHeadDim + tid] = qbar[tid];
+  int32_t* so = a.support_out + seg * K;
   int32_t* dst = a.support + (seg * a.C + slot) * (int64_t)K;
-  for (int i = tid; i < K; i += NT) dst[i] = i < nk ? cr[i] : -1;
+  for (int i = tid; i < K; i += NT) {
+    const int32_t r = i < nk ? cr[i] : -1;
+    so[i] = r;
+    dst[i] = r;
+  }
   if (tid == 0) {
     a.head[seg] = slot;
     a.count[seg] = min(cnt0 + 1, a.C);
   }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kAttThreads) void retopk_attend(RtAttendArgs a) {
+  extern __shared__ uint32_t att_dyn[];
+  __shared__ RtAttLds<T, kAttThreads> ls;
+  const int64_t seg = blockIdx.x;
+  if (a.exact[seg]) return;
+  float* zs = reinterpret_cast<float*>(att_dyn);                             // [cand_cap]
+  int32_t* rs = reinterpret_cast<int32_t*>(att_dyn + a.cand_cap);            // [cand_cap]
+  float* cz = reinterpret_cast<float*>(att_dyn + 2 * a.cand_cap);            // [K] chosen scores, then weights
+  int32_t* cr = reinterpret_cast<int32_t*>(att_dyn + 2 * a.cand_cap + a.K);  // [K] chosen rows
+  const uint32_t M = (uint32_t)a.n_cand[seg];
+  const int32_t* cd = a.cand + seg * a.cand_cap;
+  const int hd = a.head[seg], cnt0 = a.count[seg];  // read before any barrier; updated at the end
+  for (uint32_t j = threadIdx.x; j < M; j += kAttThreads) rs[j] = cd[j];
+  __syncthreads();
+  rt_attend_head<T, kAttThreads>(a, seg, rs, M, zs, cz, cr, ls, a.qbar + seg * kHeadDim, hd, cnt0);
+}
+
+// ---------------------------------------------------------------------------
+// retopk_reuse: one workgroup per head runs the selector and, on the reuse
+// path, rt_attend_head on the candidates it leaves in LDS: one launch for
+// the whole reuse path, with no candidate list in global memory. Same
+// results as retopk_select<true> followed by retopk_attend. Dynamic LDS:
+// candidate scores and rows [cand_cap] each, chosen scores and rows [K]
+// each, then the bitmap of the visible rows.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(kAttThreads) void retopk_reuse(RtSelArgs s, RtAttendArgs a) {
+  extern __shared__ uint32_t ru_dyn[];
+  __shared__ RtSelLds<kAttThreads> ss;
+  __shared__ RtAttLds<T, kAttThreads> ls;
+  const int64_t seg = blockIdx.x;
+  const int hd = s.head[seg], cnt = s.count[seg];  // read before any barrier; updated at the end
+  float* zs = reinterpret_cast<float*>(ru_dyn);
+  int32_t* rs = reinterpret_cast<int32_t*>(ru_dyn + a.cand_cap);
+  float* cz = reinterpret_cast<float*>(ru_dyn + 2 * a.cand_cap);
+  int32_t* cr = reinterpret_cast<int32_t*>(ru_dyn + 2 * a.cand_cap + a.K);
+  uint32_t* bm = ru_dyn + 2 * a.cand_cap + 2 * a.K;
+  const RtSelOut r = rt_select_head<kAttThreads, true>(s, seg, hd, cnt, ss, bm, rs);
+  __syncthreads();
+  if (r.path == 0) rt_attend_head<T, kAttThreads>(a, seg, rs, r.M, zs, cz, cr, ls, ss.qb, hd, cnt);
+  rt_select_store<kAttThreads>(s, seg, ss, r, rs);
 }
 
 // Fill the FIFO from a history of (query, support) pairs, oldest first.
