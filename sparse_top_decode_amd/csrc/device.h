@@ -81,6 +81,12 @@ STDK_DEV float wave_max(float x) {
   return x;
 }
 
+STDK_DEV float wave_min(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fminf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+
 STDK_DEV float wave_sum(float x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);

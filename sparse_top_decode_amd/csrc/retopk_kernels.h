@@ -87,15 +87,16 @@ constexpr int kMaxVote = 8;  // recalled entries a confidence vote can weigh (ma
 // Shared-memory state of the selector phases of one head.
 template <int NT>
 struct RtSelLds {
-  float part[kMaxCache][8];
-  float sq[8];
   float qb[kHeadDim];  // the unit query
-  int slot_of[kMaxCache];
   uint2 rkey[kMaxCache];
+  float rcos[kMaxCache];
+  float sq[8];
+  int slot_of[kMaxCache];
   uint32_t tmp[NT / 64 + 1];
   int rec_slot[kMaxVote];
   float rec_rho[kMaxVote];
-  int path, npick, nrec;
+  float best;
+  int npick;
 };
 
 // What the selector of one head decided (uniform over the workgroup).
@@ -151,132 +152,132 @@ STDK_DEV RtSelOut rt_select_head(const RtSelArgs& a, int64_t seg, int hd, int cn
 #pragma unroll
     for (int e = 0; e < 16; ++e) ls.qb[16 * j + e] = qn[e];
   }
-  // cosines: 16-dim partial dot products, summed in part order below
+  // cosines: 16-dim partial dot products; the 8 of a slot sit in 8
+  // consecutive lanes and are summed in part order. Entry sl (< kMaxCache)
+  // gets its cosine and rank key; the entry of slot s has age (head - s) mod
+  // C, and only the `count` newest are valid (invalid: key 0, below every
+  // valid key; cosine -inf).
+  const int lane = tid & 63;
 #pragma unroll
   for (int ps = 0; ps < kPass; ++ps) {
     const int sl = g + kGroups * ps;
-    if (sl < C) {
-      float t = 0.f;
+    float t = 0.f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) t = fmaf(qn[e], qh[ps][e], t);
-      ls.part[sl][j] = t;
+    for (int e = 0; e < 16; ++e) t = fmaf(qn[e], qh[ps][e], t);
+    float r = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) r += __shfl(t, (lane & ~7) | jj, 64);
+    if (j == 0 && sl < kMaxCache) {
+      int age = hd - sl;
+      if (age < 0) age += C;
+      const bool valid = sl < C && age < cnt;
+      ls.rkey[sl] = valid ? make_uint2(f2key(r), ~(uint32_t)age) : make_uint2(0u, 0u);
+      ls.rcos[sl] = valid ? r : -INFINITY;
     }
   }
   const int Wd = a.step ? (int)((L_t + 31) / 32) : a.bitmap_words;
-  __syncthreads();
-  // Wave 0 (C <= 64 slots, one per lane): the cosines, the path, the top R
-  // and the picked slots in slot order, with LDS broadcasts and ballots. The entry
-  // of slot s has age (head - s) mod C; only the `count` newest are valid.
-  if (tid < 64) {
-    const int sl = tid;
-    float re = -INFINITY;
-    int age = C;
-    bool valid = false;
-    if (sl < C) {
-      float r = 0.f;
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) r += ls.part[sl][jj];
-      age = hd - sl;
-      if (age < 0) age += C;
-      valid = age < cnt;
-      if (valid) re = r;
-    }
-    const float best = wave_max(re);
-    int path;
-    if (refresh_now) path = 2;
-    else if (cnt == 0 || best < a.tau) path = 1;
-    else path = 0;
-    if (sl == 0) ls.path = path;
-    if (path == 0) {
-      // top-R by (cosine descending, age ascending): the rank is the number
-      // of valid entries with a larger (cosine key, ~age) pair; invalid
-      // lanes carry 0, below every valid pair. The pairs go through LDS and
-      // every lane reads all 64 (same address across the wave: broadcast
-      // reads, issued back to back).
-      const uint32_t khi = valid ? f2key(re) : 0u, klo = valid ? ~(uint32_t)age : 0u;
-      ls.rkey[sl] = make_uint2(khi, klo);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-      const uint64_t mine = ((uint64_t)khi << 32) | klo;
-      int rank = 0;
-#pragma unroll
-      for (int f = 0; f < kMaxCache; ++f) {
-        const uint2 kf = ls.rkey[f];
-        rank += ((((uint64_t)kf.x << 32) | kf.y) > mine) ? 1 : 0;
-      }
-      const bool pk = valid && rank < a.R;
-      if (pk && rank < kMaxVote) {
-        ls.rec_slot[rank] = sl;
-        ls.rec_rho[rank] = re;
-      }
-      const uint64_t pm = __ballot(pk);
-      if (pk) ls.slot_of[lane_rank(pm)] = sl;
-      if (sl == 0) ls.npick = __popcll(pm);
-    } else if (sl == 0) {
-      ls.npick = 0;
-    }
-  }
   if (kLdsBitmap)
     for (int i = tid; i < Wd; i += NT) bm[i] = 0u;
   __syncthreads();
-  const int path = ls.path;
+  // top R by (cosine descending, age ascending): the rank of entry i is the
+  // number of entries with a larger key, counted by TPS threads over E
+  // entries each; the picked entries go out in rank order. Wave 0 also
+  // forms the best cosine (maximum over the valid entries; NaN ignored).
+  {
+    constexpr int TPS = NT / kMaxCache, E = kMaxCache / TPS;
+    const int i = tid / TPS, sub = tid % TPS;
+    const uint2 ki = ls.rkey[i];
+    const uint64_t mine = ((uint64_t)ki.x << 32) | ki.y;
+    int gt = 0;
+#pragma unroll
+    for (int f = 0; f < E; ++f) {
+      const uint2 kf = ls.rkey[sub * E + f];
+      gt += ((((uint64_t)kf.x << 32) | kf.y) > mine) ? 1 : 0;
+    }
+#pragma unroll
+    for (int o = 1; o < TPS; o <<= 1) gt += __shfl_xor(gt, o, 64);
+    const bool pk = mine != 0u && gt < a.R;
+    if (sub == 0 && pk) {
+      ls.slot_of[gt] = i;
+      if (gt < kMaxVote) {
+        ls.rec_slot[gt] = i;
+        ls.rec_rho[gt] = ls.rcos[i];
+      }
+    }
+    if (tid < 64) {
+      const float best = wave_max(ls.rcos[tid]);
+      if (tid == 0) ls.best = best;
+    }
+  }
+  __syncthreads();
+  int path;
+  if (refresh_now) path = 2;
+  else if (cnt == 0 || ls.best < a.tau) path = 1;
+  else path = 0;
   if (path != 0) return RtSelOut{path, 0u, L_t};
+  const int npick = min(a.R, min(cnt, C));
+  if (tid == 0) ls.npick = npick;
   if (!kLdsBitmap) {
     for (int i = tid; i < Wd; i += NT) bm[i] = 0u;
     __syncthreads();
   }
+  // The recent window [Lw, L) holds the largest visible rows: it is appended
+  // after the bitmap's rows, which are the picked supports' rows below Lw.
   const int64_t L = L_t;
-  // union of the picked supports: index f of the flattened R x K list is
-  // entry f % K of picked slot f / K; kU loads per thread are in flight
-  // (clamped to the last entry, no branches) before their bits are set
+  const int64_t Lw = max((int64_t)0, L - a.W);
+  // union of the picked supports: thread t takes entries f = t + NT * s of
+  // the flattened npick x K list, entry e of picked slot p (f = p * K + e,
+  // stepped without a division); kU loads per thread are in flight (past
+  // the list: clamped to its last entry, no branches) before their bits are set
   {
     constexpr int kU = NT >= 1024 ? 4 : 8;
-    const int total = ls.npick * K;
+    const int total = npick * K;
+    const int dp = NT / K, de = NT - dp * K;
+    int p = tid / K, e = tid - p * K;
     for (int f0 = 0; f0 < total; f0 += NT * kU) {
       int32_t x[kU];
+      bool in[kU];
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
-        const int f = min(f0 + u * NT + tid, total - 1);
-        x[u] = a.support[(seg * C + ls.slot_of[f / K]) * (int64_t)K + f % K];
+        in[u] = p < npick;
+        const int pc = in[u] ? p : npick - 1, ec = in[u] ? e : K - 1;
+        x[u] = a.support[(seg * C + ls.slot_of[pc]) * (int64_t)K + ec];
+        e += de;
+        p += dp;
+        if (e >= K) {
+          e -= K;
+          ++p;
+        }
       }
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int f = f0 + u * NT + tid;
-        if (f < total && x[u] >= 0 && x[u] < L) atomicOr(&bm[x[u] >> 5], 1u << (x[u] & 31));
-      }
+      for (int u = 0; u < kU; ++u)
+        if (in[u] && x[u] >= 0 && x[u] < Lw) atomicOr(&bm[x[u] >> 5], 1u << (x[u] & 31));
     }
   }
-  for (int64_t x = max((int64_t)0, L - a.W) + tid; x < L; x += NT) atomicOr(&bm[x >> 5], 1u << (x & 31));
   __syncthreads();
-  // ascending compaction: wave w reads words [w0, w1) 64 at a time (lane l
-  // the word w0 + 64 i + l), counts its bits, and the waves' offsets come
-  // from one scan; then each word's bits go out at its wave-scan position
-  constexpr int NWv = NT / 64;
-  const int lane = tid & 63, wv = tid >> 6;
-  const int wper = ((Wd + NWv - 1) / NWv + 63) & ~63;
-  const int w0 = min(Wd, wv * wper), w1 = min(Wd, w0 + wper);
+  // ascending compaction of the words below Lw: thread t owns the words
+  // [t * CH, t * CH + CH); one block scan of the per-thread bit counts gives
+  // each its first slot; then the window
+  const int Wb = (int)((Lw + 31) / 32);
+  const int CH = (Wb + NT - 1) / NT;
+  const int w0 = min(Wb, tid * CH), w1 = min(Wb, w0 + CH);
   uint32_t c0 = 0;
-  for (int i = w0 + lane; i < w1; i += 64) c0 += __popc(bm[i]);
+  for (int i = w0; i < w1; ++i) c0 += __popc(bm[i]);
   uint32_t total;
-  const uint32_t wave_cnt = __shfl(wave_incl_scan(c0), 63, 64);
-  uint32_t r = block_excl_scan<NT>(lane == 0 ? wave_cnt : 0u, ls.tmp, &total);
-  r = __shfl(r, 0, 64);
-  for (int i0 = w0; i0 < w1; i0 += 64) {
-    const int i = i0 + lane;
-    uint32_t bits = i < w1 ? bm[i] : 0u;
-    const uint32_t n = __popc(bits);
-    const uint32_t incl = wave_incl_scan(n);
-    uint32_t pos = r + incl - n;
+  uint32_t pos = block_excl_scan<NT>(c0, ls.tmp, &total);
+  for (int i = w0; i < w1; ++i) {
+    uint32_t bits = bm[i];
     while (bits) {
       const int jb = __ffs(bits) - 1;
       bits &= bits - 1;
       if (pos < (uint32_t)a.cand_cap) cd[pos] = i * 32 + jb;
       ++pos;
     }
-    r += __shfl(incl, 63, 64);
   }
-  return RtSelOut{0, min(total, (uint32_t)a.cand_cap), L_t};
+  const uint32_t nw = (uint32_t)(L - Lw);
+  for (uint32_t t = tid; t < nw; t += NT)
+    if (total + t < (uint32_t)a.cand_cap) cd[total + t] = (int32_t)(Lw + t);
+  return RtSelOut{0, min(total + nw, (uint32_t)a.cand_cap), L_t};
 }
 
 // The per-head results of rt_select_head: the unit query, the path and the
@@ -711,77 +712,142 @@ __global__ __launch_bounds__(kRerankSelThreads) void retopk_rerank_select(RtRera
 constexpr int kRselStageMax = 16384;
 
 // The exact top-K of the M candidate scores zs (rows rs) staged in LDS,
-// ties to the lower candidate index (the candidates ascend by row): radix
-// passes sized to the candidates' key range, then an ordered compaction in
-// which wave w owns a contiguous candidate segment and ballots rank the
-// taken ones. emit(pos, row, z) receives the chosen candidates in ascending
-// order (pos < K); returns how many there are before the cap at K. NT
-// threads; every thread must call it.
-template <int NT, typename Emit>
-STDK_DEV uint32_t lds_topk(const float* zs, const int32_t* rs, uint32_t M, int K, uint32_t* h,
-                           uint32_t (*wc)[NT / 64], int* s_bin_p, uint32_t* s_beyond_p, Emit emit) {
+// ties to the lower candidate index (the candidates ascend by row), in two
+// steps: the cut (lds_cut_radix or lds_cut_linear), then an ordered
+// compaction (lds_emit) in which wave w owns a contiguous candidate segment
+// and ballots rank the taken ones. emit(pos, row, z) receives the chosen
+// candidates in ascending order (pos < K); the count before the cap at K is
+// returned. NT threads; every thread must call them.
+//
+// The cut of a top-K selection: keys (f2key of the scores) above Tk are
+// taken and, of the keys equal to Tk, the first `need` in candidate order;
+// take_all: every candidate (M <= K).
+struct TopkCut {
+  uint32_t Tk, need;
+  bool take_all;
+};
+
+// Radix passes over a window of keys [lo, lo + width): the first spans the
+// candidates' own key range, each later one exactly the bin that holds the
+// K-th key (keys above it were counted in `beyond` already and must not be
+// counted again), in 2048 bins of 1 << sh keys; stop at single keys (sh = 0)
+// or once that bin is taken whole. The threshold Tk is then the bin's
+// smallest key and `need` the number of keys equal to it to take.
+template <int NT>
+STDK_DEV TopkCut lds_cut_radix(const float* zs, uint32_t M, int K, uint32_t* h, uint32_t (*wc)[NT / 64],
+                               int* s_bin_p, uint32_t* s_beyond_p) {
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const bool take_all = M <= (uint32_t)K;
+  if (M <= (uint32_t)K) return TopkCut{0u, (uint32_t)K, true};
   int& s_bin = *s_bin_p;
   uint32_t& s_beyond = *s_beyond_p;
-  // radix passes over a window of keys [lo, lo + width): the first spans
-  // the candidates' own key range, each later one exactly the bin that
-  // holds the K-th key (keys above it were counted in `beyond` already and
-  // must not be counted again), in 2048 bins of 1 << sh keys; stop at single
-  // keys (sh = 0) or once that bin is taken whole. The threshold Tk is then
-  // the bin's smallest key and `need` the number of keys equal to it to take.
-  uint32_t Tk = 0u, need = (uint32_t)K;
-  if (!take_all) {
-    uint32_t kmin = 0xffffffffu, kmax = 0u;
+  uint32_t need = (uint32_t)K;
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+  for (uint32_t j = tid; j < M; j += NT) {
+    const uint32_t kv = f2key(zs[j]);
+    kmin = min(kmin, kv);
+    kmax = max(kmax, kv);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+  }
+  if (lane == 0) {
+    wc[0][w] = kmin;
+    wc[1][w] = kmax;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int v = 0; v < NW; ++v) {
+    kmin = min(kmin, wc[0][v]);
+    kmax = max(kmax, wc[1][v]);
+  }
+  __syncthreads();
+  uint32_t lo = kmin;
+  const uint32_t span = kmax - kmin;
+  int sh = span < 2048u ? 0 : (32 - __clz((int)span)) - 11;
+  uint64_t width = 2048ull << sh;  // covers [kmin, kmax]
+  // at most three passes: sh <= 21 and drops by 11 (to 0) each time
+  for (;;) {
+    for (int i = tid; i < 2048; i += NT) h[i] = 0u;
+    __syncthreads();
     for (uint32_t j = tid; j < M; j += NT) {
       const uint32_t kv = f2key(zs[j]);
-      kmin = min(kmin, kv);
-      kmax = max(kmax, kv);
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
-      kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
-    }
-    if (lane == 0) {
-      wc[0][w] = kmin;
-      wc[1][w] = kmax;
+      if (kv >= lo && (uint64_t)(kv - lo) < width) atomicAdd(&h[(kv - lo) >> sh], 1u);
     }
     __syncthreads();
-#pragma unroll
-    for (int v = 0; v < NW; ++v) {
-      kmin = min(kmin, wc[0][v]);
-      kmax = max(kmax, wc[1][v]);
-    }
+    if (w == 0) find_bin_wave<2048, true>(h, need, &s_bin, &s_beyond);
     __syncthreads();
-    uint32_t lo = kmin;
-    const uint32_t span = kmax - kmin;
-    int sh = span < 2048u ? 0 : (32 - __clz((int)span)) - 11;
-    uint64_t width = 2048ull << sh;  // covers [kmin, kmax]
-    // at most three passes: sh <= 21 and drops by 11 (to 0) each time
-    for (;;) {
-      for (int i = tid; i < 2048; i += NT) h[i] = 0u;
-      __syncthreads();
-      for (uint32_t j = tid; j < M; j += NT) {
-        const uint32_t kv = f2key(zs[j]);
-        if (kv >= lo && (uint64_t)(kv - lo) < width) atomicAdd(&h[(kv - lo) >> sh], 1u);
-      }
-      __syncthreads();
-      if (w == 0) find_bin_wave<2048, true>(h, need, &s_bin, &s_beyond);
-      __syncthreads();
-      const int bin = s_bin < 0 ? 0 : s_bin;
-      need -= s_beyond;
-      lo += (uint32_t)bin << sh;
-      width = 1ull << sh;
-      if (sh == 0 || h[bin] == need) break;
-      sh = sh > 11 ? sh - 11 : 0;
-      __syncthreads();
-    }
-    Tk = lo;
+    const int bin = s_bin < 0 ? 0 : s_bin;
+    need -= s_beyond;
+    lo += (uint32_t)bin << sh;
+    width = 1ull << sh;
+    if (sh == 0 || h[bin] == need) break;
+    sh = sh > 11 ? sh - 11 : 0;
+    __syncthreads();
   }
+  return TopkCut{lo, need, false};
+}
 
-  // ordered compaction: wave w owns candidates [s0, s1)
+// One histogram pass instead of radix passes when the scores are finite
+// with lo < hi (their minimum and maximum): bin(z) = min(2047, (z - lo) *
+// 2048 / (hi - lo)) truncated is non-decreasing in z, so every score in a
+// higher bin is larger than every score in a lower one. The bin holding the
+// K-th largest score is then ranked exactly (its keys, at most kCutList of
+// them) to give Tk and the number of keys equal to it to take. h must be
+// zero and *s_cnt 0 on entry. Returns false (workgroup-uniform, nothing
+// decided) when that bin holds more than kCutList scores.
+constexpr int kCutList = 64;
+template <int NT>
+STDK_DEV bool lds_cut_linear(const float* zs, uint32_t M, int K, float lo, float hi, uint32_t* h,
+                             uint32_t* lst, uint32_t* s_cnt, uint32_t* s_cut, int* s_bin, uint32_t* s_beyond,
+                             TopkCut* out) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const float sc = 2048.f / (hi - lo);
+  auto bin_of = [&](float z) { return (int)fminf((z - lo) * sc, 2047.f); };
+  for (uint32_t j = tid; j < M; j += NT) atomicAdd(&h[bin_of(zs[j])], 1u);
+  __syncthreads();
+  if (w == 0) find_bin_wave<2048, true>(h, (uint32_t)K, s_bin, s_beyond);
+  __syncthreads();
+  const int b = *s_bin;
+  const uint32_t need = (uint32_t)K - *s_beyond, cb = h[b];
+  if (cb > (uint32_t)kCutList) return false;
+  for (uint32_t j = tid; j < M; j += NT) {
+    const float z = zs[j];
+    if (bin_of(z) == b) lst[atomicAdd(s_cnt, 1u)] = f2key(z);
+  }
+  __syncthreads();
+  if (w == 0) {
+    // Tk: the key with fewer than `need` keys above it and at least `need`
+    // at or above it
+    const uint32_t k = lane < (int)cb ? lst[lane] : 0u;
+    uint32_t gt = 0, ge = 0;
+    for (uint32_t f = 0; f < cb; ++f) {
+      const uint32_t kf = lst[f];
+      gt += kf > k;
+      ge += kf >= k;
+    }
+    if (lane < (int)cb && gt < need && need <= ge) {
+      s_cut[0] = k;
+      s_cut[1] = need - gt;
+    }
+  }
+  __syncthreads();
+  *out = TopkCut{s_cut[0], s_cut[1], false};
+  return true;
+}
+
+// Ordered compaction of the selection: wave w owns candidates [s0, s1);
+// emit(pos, row, score) for each taken candidate in candidate order, pos <
+// K. Returns the number taken.
+template <int NT, typename Emit>
+STDK_DEV uint32_t lds_emit(const float* zs, const int32_t* rs, uint32_t M, int K, const TopkCut& cut,
+                           uint32_t (*wc)[NT / 64], Emit emit) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const bool take_all = cut.take_all;
+  const uint32_t Tk = cut.Tk, need = cut.need;
   const uint32_t SEG = ((M + NW - 1) / NW + 63u) & ~63u;
   const uint32_t s0 = min(M, (uint32_t)w * SEG), s1 = min(M, s0 + SEG);
   uint32_t cg = 0, ce = 0;
@@ -825,6 +891,15 @@ STDK_DEV uint32_t lds_topk(const float* zs, const int32_t* rs, uint32_t M, int K
     eq_seen += (uint32_t)__popcll(em);
   }
   return tot;
+}
+
+
+// lds_cut_radix, then lds_emit
+template <int NT, typename Emit>
+STDK_DEV uint32_t lds_topk(const float* zs, const int32_t* rs, uint32_t M, int K, uint32_t* h,
+                           uint32_t (*wc)[NT / 64], int* s_bin_p, uint32_t* s_beyond_p, Emit emit) {
+  const TopkCut cut = lds_cut_radix<NT>(zs, M, K, h, wc, s_bin_p, s_beyond_p);
+  return lds_emit<NT>(zs, rs, M, K, cut, wc, emit);
 }
 
 
@@ -929,17 +1004,24 @@ struct RtAttLds {
   uint32_t wc[2][NT / 64];
   float red[NT / KvTraits<T>::LPR][kHeadDim];
   float wred[NT / 64];
+  float wlo[NT / 64], whi[NT / 64], wsum[NT / 64];
+  uint32_t wbad[NT / 64];
+  uint32_t lst[kCutList];
+  uint32_t s_cut[2];
+  uint32_t s_cnt;
   int s_bin;
   uint32_t s_beyond;
 };
 
 // rs: the M ascending candidate rows of head seg, in LDS; zs, cz, cr: LDS
-// for cand_cap candidate scores, K chosen scores and K chosen rows. qbar:
-// the head's unit query (LDS or global). hd, cnt0: the FIFO's head and count
+// for cand_cap candidate scores, K chosen scores and K chosen rows. qr: this
+// thread's query slice (load_q_slice, issued early by the caller). qbar: the
+// head's unit query (LDS or global). hd, cnt0: the FIFO's head and count
 // before this step.
 template <typename T, int NT>
 STDK_DEV void rt_attend_head(const RtAttendArgs& a, int64_t seg, const int32_t* rs, uint32_t M, float* zs,
-                             float* cz, int32_t* cr, RtAttLds<T, NT>& ls, const float* qbar, int hd, int cnt0) {
+                             float* cz, int32_t* cr, RtAttLds<T, NT>& ls, const float (&qr)[1][KvTraits<T>::EPL],
+                             const float* qbar, int hd, int cnt0) {
   constexpr int NW = NT / 64;
   constexpr int EPL = KvTraits<T>::EPL, LPR = KvTraits<T>::LPR, ROWB = KvTraits<T>::ROWB;
   constexpr int NG = NT / LPR;  // row groups: one row per group and load
@@ -949,63 +1031,113 @@ STDK_DEV void rt_attend_head(const RtAttendArgs& a, int64_t seg, const int32_t* 
   const int gid = tid / LPR, c = tid % LPR;
   const int b = (int)(seg / a.Hq), hq = (int)(seg % a.Hq), hkv = hq / a.G;
   const int K = a.K;
-  float qr[1][EPL];
-  load_q_slice<T, 1>(a.q, seg, c, qr);
+  for (int i = tid; i < kHistBins; i += NT) ls.h[i] = 0u;  // for lds_cut_linear
+  if (tid == 0) ls.s_cnt = 0u;
 
   // 1. exact scores of the candidates: row group gid takes candidates
-  // gid + NG * u, UK rows in flight (clamped to the last candidate)
+  // gid + NG * u, UK rows in flight (loads clamped to the last candidate; a
+  // wave skips the products of rows past M). Their minimum and maximum, and
+  // whether any is not finite, per wave.
   const int64_t hoff = (int64_t)b * a.stride_b_bytes + (int64_t)hkv * a.stride_h_bytes + c * 16;
   const char* kb = a.k + hoff;
+  const uint32_t g0 = (uint32_t)(w * (64 / LPR));  // first row group of this wave
+  float lo = INFINITY, hi = -INFINITY;
+  bool bad = false;
   for (uint32_t base = 0; base < M; base += NG * UK) {
     u32x4 kw[UK];
 #pragma unroll
     for (int u = 0; u < UK; ++u) kw[u] = load16(kb + (int64_t)rs[min(base + gid + NG * u, M - 1)] * ROWB);
 #pragma unroll
     for (int u = 0; u < UK; ++u) {
-      float d[1];
-      chunk_dots<T, 1>(kw[u], qr, d);
-      const float sc = group_sum<LPR>(d[0]);
-      const uint32_t j = base + gid + NG * u;
-      if (c == 0 && j < M) zs[j] = sc * a.scale;
+      if (base + g0 + NG * u < M) {  // wave-uniform
+        float d[1];
+        chunk_dots<T, 1>(kw[u], qr, d);
+        const float sc = group_sum<LPR>(d[0]);
+        const uint32_t j = base + gid + NG * u;
+        if (c == 0 && j < M) {
+          const float z = sc * a.scale;
+          zs[j] = z;
+          lo = fminf(lo, z);
+          hi = fmaxf(hi, z);
+          bad |= !(fabsf(z) <= __FLT_MAX__);
+        }
+      }
     }
   }
+  lo = wave_min(lo);
+  hi = wave_max(hi);
+  const bool wbad = __ballot(bad) != 0;
+  if (lane == 0) {
+    ls.wlo[w] = lo;
+    ls.whi[w] = hi;
+    ls.wbad[w] = wbad;
+  }
   __syncthreads();
+  bool any_bad = false;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) {
+    lo = fminf(lo, ls.wlo[v]);
+    hi = fmaxf(hi, ls.whi[v]);
+    any_bad |= ls.wbad[v] != 0u;
+  }
 
-  // 2. the top K in candidate (= row) order, into LDS
-  const uint32_t tot = lds_topk<NT>(zs, rs, M, K, ls.h, ls.wc, &ls.s_bin, &ls.s_beyond,
-                                    [&](uint32_t pos, int32_t r, float z) {
-                                      cz[pos] = z;
-                                      cr[pos] = r;
-                                    });
+  const char* vb = a.v + hoff;
+
+  // 2-3. the top K in candidate (= row) order into LDS, with their softmax
+  // weights e^{z - m}. Finite scores: m is their maximum (always kept), the
+  // cut comes from one histogram pass (lds_cut_linear) and the weights are
+  // formed as the rows are emitted. Otherwise (or when that cut gives up):
+  // the radix cut, then the maximum of the kept scores, the weights in place
+  // (a -inf score weighs 0, a NaN propagates). Each thread sums its weights
+  // in emission order; the per-wave sums are added in wave order.
+  float m = hi, ps = 0.f;
+  uint32_t tot = 0;
+  bool weighted = false;
+  if (!any_bad && M > 0) {
+    TopkCut cut{0u, (uint32_t)K, true};
+    bool ok = true;
+    if (M > (uint32_t)K)
+      ok = hi > lo && 2048.f / (hi - lo) <= __FLT_MAX__ &&
+           lds_cut_linear<NT>(zs, M, K, lo, hi, ls.h, ls.lst, &ls.s_cnt, ls.s_cut, &ls.s_bin, &ls.s_beyond, &cut);
+    if (ok) {
+      tot = lds_emit<NT>(zs, rs, M, K, cut, ls.wc, [&](uint32_t pos, int32_t r, float z) {
+        const float wt = __expf(z - m);
+        cz[pos] = wt;
+        cr[pos] = r;
+        ps += wt;
+      });
+      weighted = true;
+    }
+  }
+  if (!weighted) {
+    tot = lds_topk<NT>(zs, rs, M, K, ls.h, ls.wc, &ls.s_bin, &ls.s_beyond, [&](uint32_t pos, int32_t r, float z) {
+      cz[pos] = z;
+      cr[pos] = r;
+    });
+  }
   const int nk = (int)min(tot, (uint32_t)K);
   __syncthreads();
-
-  // 3. softmax . V over the nk chosen rows: their maximum, the weights
-  // e^{z - m} in place (a -inf score weighs 0, a NaN propagates), their sum
-  // in a fixed order, then the value rows, U per row group in flight
-  float zm = -INFINITY;
-  for (int i = tid; i < nk; i += NT) zm = fmaxf(zm, cz[i]);
-  zm = wave_max(zm);
-  if (lane == 0) ls.wred[w] = zm;
-  __syncthreads();
-  float m = ls.wred[0];
+  if (!weighted) {
+    float zm = -INFINITY;
+    for (int i = tid; i < nk; i += NT) zm = fmaxf(zm, cz[i]);
+    zm = wave_max(zm);
+    if (lane == 0) ls.wred[w] = zm;
+    __syncthreads();
+    m = ls.wred[0];
 #pragma unroll
-  for (int v = 1; v < NW; ++v) m = fmaxf(m, ls.wred[v]);
-  __syncthreads();
-  float ps = 0.f;
-  for (int i = tid; i < nk; i += NT) {
-    const float z = cz[i];
-    const float wt = z == -INFINITY ? 0.f : __expf(z - m);
-    cz[i] = wt;
-    ps += wt;
+    for (int v = 1; v < NW; ++v) m = fmaxf(m, ls.wred[v]);
+    for (int i = tid; i < nk; i += NT) {
+      const float z = cz[i];
+      const float wt = z == -INFINITY ? 0.f : __expf(z - m);
+      cz[i] = wt;
+      ps += wt;
+    }
+    __syncthreads();
   }
   ps = wave_sum(ps);
-  if (lane == 0) ls.wred[w] = ps;
-  __syncthreads();
-  float ssum = 0.f;
-#pragma unroll
-  for (int v = 0; v < NW; ++v) ssum += ls.wred[v];
-  const char* vb = a.v + hoff;
+  if (lane == 0) ls.wsum[w] = ps;
+
+  // softmax . V over the nk chosen rows, U value rows per row group in flight
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
@@ -1026,6 +1158,9 @@ STDK_DEV void rt_attend_head(const RtAttendArgs& a, int64_t seg, const int32_t* 
 #pragma unroll
   for (int e = 0; e < EPL; ++e) ls.red[gid][c * EPL + e] = acc[e];
   __syncthreads();
+  float ssum = 0.f;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) ssum += ls.wsum[v];
   if (tid < kHeadDim) {
     float o = 0.f;
 #pragma unroll 8
@@ -1065,9 +1200,11 @@ __global__ __launch_bounds__(kAttThreads) void retopk_attend(RtAttendArgs a) {
   const uint32_t M = (uint32_t)a.n_cand[seg];
   const int32_t* cd = a.cand + seg * a.cand_cap;
   const int hd = a.head[seg], cnt0 = a.count[seg];  // read before any barrier; updated at the end
+  float qr[1][KvTraits<T>::EPL];
+  load_q_slice<T, 1>(a.q, seg, threadIdx.x % KvTraits<T>::LPR, qr);
   for (uint32_t j = threadIdx.x; j < M; j += kAttThreads) rs[j] = cd[j];
   __syncthreads();
-  rt_attend_head<T, kAttThreads>(a, seg, rs, M, zs, cz, cr, ls, a.qbar + seg * kHeadDim, hd, cnt0);
+  rt_attend_head<T, kAttThreads>(a, seg, rs, M, zs, cz, cr, ls, qr, a.qbar + seg * kHeadDim, hd, cnt0);
 }
 
 // ---------------------------------------------------------------------------
@@ -1090,9 +1227,11 @@ __global__ __launch_bounds__(kAttThreads) void retopk_reuse(RtSelArgs s, RtAtten
   float* cz = reinterpret_cast<float*>(ru_dyn + 2 * a.cand_cap);
   int32_t* cr = reinterpret_cast<int32_t*>(ru_dyn + 2 * a.cand_cap + a.K);
   uint32_t* bm = ru_dyn + 2 * a.cand_cap + 2 * a.K;
+  float qr[1][KvTraits<T>::EPL];  // in flight with the selector's loads
+  load_q_slice<T, 1>(a.q, seg, threadIdx.x % KvTraits<T>::LPR, qr);
   const RtSelOut r = rt_select_head<kAttThreads, true>(s, seg, hd, cnt, ss, bm, rs);
   __syncthreads();
-  if (r.path == 0) rt_attend_head<T, kAttThreads>(a, seg, rs, r.M, zs, cz, cr, ls, ss.qb, hd, cnt);
+  if (r.path == 0) rt_attend_head<T, kAttThreads>(a, seg, rs, r.M, zs, cz, cr, ls, qr, ss.qb, hd, cnt);
   rt_select_store<kAttThreads>(s, seg, ss, r, rs);
 }
 
