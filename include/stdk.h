@@ -47,7 +47,7 @@
  *        (Eq. 2) and "CPU-GPU Co-Execution Architecture" (Eq. 3-5).
  *  [RT]  "Recall Before You Rank: Similarity-Guided Top-K Reuse for
  *        Efficient Long-Context Attention" (review): the exact Top-K cost
- *        section and "核心方法" 1-5 with the per-step loop.
+ *        section and "核心方法" 1-5.
  */
 #ifndef STDK_H
 #define STDK_H
@@ -304,7 +304,7 @@ int32_t attn_merge_lse(int64_t rows, int32_t d, const float* o_a, const float* l
                        void* stream);
 
 /* ------------------------------------------------------------------------
- * ReTopK ([RT] 核心方法 1-5 and the per-step loop).
+ * ReTopK ([RT] 核心方法 1-5).
  * ---------------------------------------------------------------------- */
 typedef struct retopk_params {
   int32_t top_k;     /* K, rows attended per step (1..65536) */
@@ -343,7 +343,7 @@ int32_t retopk_state_init(const stdk_layout* lay, const retopk_params* p, const 
                           const float* q_hist, const int32_t* sup_hist, int32_t n_hist,
                           void* stream);
 
-/* One decode step for every (b, h_q) ([RT] per-step loop):
+/* One decode step for every (b, h_q) ([RT] 核心方法 1-5):
  *   q_bar = q / ||q||;  rho_c = q_bar . q_hat_c over the valid entries;
  *   exact path if t % T_r == 0 (refresh), or count = 0, or max rho < tau;
  *   else: recall the R entries of largest rho (ties: newest first), take the

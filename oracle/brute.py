@@ -17,7 +17,7 @@ the two can pin each other on inputs small enough for plain loops
 
 Sources: RetrievalAttention review, "Approximated Attention Formulation"
 (Eq. 2) and "CPU-GPU Co-Execution Architecture" (Eq. 3-5); the ReTopK review
-"Recall Before You Rank", "核心方法" 1-5 and its per-step loop.
+"Recall Before You Rank", "核心方法" 1-5.
 """
 
 from __future__ import annotations

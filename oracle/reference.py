@@ -23,7 +23,7 @@ Sources (cited by page title and section):
   Long-Context Attention" (blog review): "Exact Top-K 的隐藏成本" (full scan and
   global Top-K), "核心方法" 1-5 (query-support cache, similar-query recall,
   candidate union with the recent window, exact rerank, similarity fallback
-  and periodic refresh) and the per-step loop printed after them.
+  and periodic refresh).
 
 Readings where the pages are silent (each also listed in the design doc):
 
@@ -292,7 +292,7 @@ def attn_merge_lse(o_a: np.ndarray, lse_a: np.ndarray, o_b: np.ndarray, lse_b: n
 
 
 # --------------------------------------------------------------------------
-# ReTopK   ([RT] 核心方法 1-5 and the per-step loop)
+# ReTopK   ([RT] 核心方法 1-5)
 # --------------------------------------------------------------------------
 PATH_REUSE, PATH_FALLBACK, PATH_REFRESH = 0, 1, 2
 
@@ -384,14 +384,22 @@ def vote_candidates(union_rows: np.ndarray, recent_rows: np.ndarray, supports: S
 def retopk_head_step(p: RetopkParams, q_hat: np.ndarray, support: np.ndarray, head: int, count: int,
                      q: np.ndarray, kc_head: np.ndarray, vc_head: np.ndarray, L_t: int, t: int,
                      scale: float) -> Dict:
-    """One decode step of one query head, in the order of the pages' loop:
-    normalise, cosine against the cache, choose the path, (recall + union +
-    rerank) or exact Top-K, renormalised softmax . V, push.
+    """One decode step of one query head, from the definitions of [RT]
+    "核心方法": the cosines rho_{t,c} = qbar_t . qbar_c against the valid
+    entries of the head's FIFO B_t (sections 1-2); the two guards of section
+    5 (a refresh every T_r steps, or the best rho_{t,c} below tau) choose
+    the exact path; otherwise the candidate set A_t = Unique(union of the
+    supports S^_c of the R most similar entries, and the recent window L_t
+    of the W newest rows), with M_t = |A_t| <= R*K + W (section 3); the
+    support S^_t = TopK over A_t of e^_{t,i} = q_t . k_i / sqrt(d) (section
+    4), or over all L_t rows on the exact path; renormalised softmax . V
+    over S^_t ([RA] Eq. 2); and (qbar_t, S^_t) entering B_t on either path
+    (section 1).
 
     Returns the outputs and the updated (q_hat, support, head, count)."""
     C, K, R, W = p.cache_cap, p.top_k, p.top_r, p.recent
     qbar = unit_query_f32(q)
-    # cosine rho_c = qbar . q_hat_c over valid entries ([RT] 核心方法 2), fp32
+    # rho_{t,c} = qbar_t . qbar_c over the valid entries of B_t ([RT] 核心方法 2), fp32
     ages = np.array([(head - s) % C for s in range(C)], dtype=np.int64)
     valid = np.nonzero(ages < count)[0]
     rho = (q_hat[valid].astype(np.float32) @ qbar.astype(np.float32)).astype(np.float32) if valid.size else np.zeros(0, np.float32)
@@ -400,7 +408,7 @@ def retopk_head_step(p: RetopkParams, q_hat: np.ndarray, support: np.ndarray, he
     order = valid[np.lexsort((ages[valid], -rho.astype(np.float64)))] if valid.size else valid
     rho_sorted = np.sort(rho)[::-1]
     max_rho = float(rho_sorted[0]) if rho_sorted.size else float("nan")
-    # path ([RT] 核心方法 5 and the loop's condition)
+    # the two guards of [RT] 核心方法 5: periodic refresh, similarity fallback
     refresh = p.refresh > 0 and (t % p.refresh) == 0
     if refresh:
         path = PATH_REFRESH
@@ -413,18 +421,18 @@ def retopk_head_step(p: RetopkParams, q_hat: np.ndarray, support: np.ndarray, he
     if path == PATH_REUSE:
         picked = order[:min(R, count)]
         parts = [support[s][(support[s] >= 0) & (support[s] < L_t)].astype(np.int64) for s in picked]
-        recent = np.arange(max(0, L_t - W), L_t, dtype=np.int64)  # recent window ([RT] 核心方法 3)
+        recent = np.arange(max(0, L_t - W), L_t, dtype=np.int64)  # L_t, the W newest rows ([RT] 核心方法 3)
         if p.budget > 0:
             union = np.unique(np.concatenate(parts)) if parts else np.zeros(0, np.int64)
             cand, vote = vote_candidates(union, recent, parts, [rho_of_slot[s] for s in picked], p.budget)
         else:
-            cand = np.unique(np.concatenate(parts + [recent]))
+            cand = np.unique(np.concatenate(parts + [recent]))  # A_t ([RT] 核心方法 3)
         rows = cand
     else:
         rows = np.arange(0, L_t, dtype=np.int64)
-    r = attend_rows(q, kc_head, vc_head, rows, K, scale)  # exact rerank ([RT] 核心方法 4) or exact Top-K
+    r = attend_rows(q, kc_head, vc_head, rows, K, scale)  # S^_t = TopK of e^_{t,i} over A_t ([RT] 核心方法 4), or over all rows
     sup = pad_rows(r["rows"], K)
-    # push on both paths ([RT] 核心方法 1)
+    # (qbar_t, S^_t) enters the FIFO on either path ([RT] 核心方法 1)
     q_hat = q_hat.copy()
     support = support.copy()
     slot = (head + 1) % C

@@ -2,8 +2,7 @@
 // recent window, exact rerank inside the candidates, and the cache push.
 //
 // Follows the ReTopK review "Recall Before You Rank: Similarity-Guided Top-K
-// Reuse for Efficient Long-Context Attention", sections "核心方法" 1-5 and the
-// per-step loop printed after them:
+// Reuse for Efficient Long-Context Attention", sections "核心方法" 1-5:
 //  1. each query head keeps a FIFO of C (unit query, support) pairs, filled
 //     from the last C prefill queries and pushed after every step on either
 //     path;
@@ -960,8 +959,8 @@ __global__ __launch_bounds__(kRerankSelThreads) void retopk_rerank_select_lds(Rt
 }
 
 // ---------------------------------------------------------------------------
-// The reuse path of one head after its candidates are known ([RT] 核心方法 4
-// and the per-step loop): exact scores of the candidates, their top K,
+// The reuse path of one head after its candidates are known ([RT] 核心方法 1
+// and 4): exact scores of the candidates, their top K,
 // renormalised softmax . V over them ([RA] Eq. 2) and the push of (q_bar,
 // support). Candidate rows and scores stay in LDS from scoring to the
 // softmax, so no phase waits on global memory written by another. Scores,
