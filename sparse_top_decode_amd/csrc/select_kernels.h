@@ -125,9 +125,19 @@ struct SelectArgs {
   const int32_t* seg_active;  // [S] or null
   const int64_t* n_dev;       // or null: device memory holding a position count that replaces n when smaller
   RangeTab tab;
+  // topk_filter_select_sv only: softmax . V in the last workgroup, over the
+  // chosen rows and the n_extra static slots [n, n + n_extra) (rows from the
+  // range table, scores from `scores`); o and lse go to o_out and lse_out
+  const char* v;              // value cache base
+  int64_t stride_b_bytes, stride_h_bytes;
+  float* o_out;               // [S][128]
+  float* lse_out;             // [S]
+  int32_t n_extra, Hq, G, pad_;
 };
 
 constexpr int kSelectWaves = kSelThreads / 64;
+constexpr int kFuseMaxSlots = 4096;   // chosen + static slots a fused softmax . V takes (LDS)
+constexpr int kFuseStatic = 4;        // static slots per thread held in registers
 static_assert(kSelThreads == 1024, "one thread per bin of the third digit");
 constexpr int kFselLoads = 16;  // score loads per lane: a wave's whole slice
 constexpr int kCtlWords = 16;   // control words per segment
@@ -149,10 +159,12 @@ STDK_DEV Cand load_agent(const Cand* p) {
 // (bits 9..0) over the candidates whose top 22 bits are `pre22`, and the
 // ordered compaction. `pre` holds the workgroups' candidate offsets [P + 1];
 // `h2` (1024 bins) is zero on entry.
-template <bool kLds>
-STDK_DEV void select_tail(const SelectArgs& a, int64_t seg, int P, int64_t span, uint32_t m, uint32_t pre22,
-                          uint32_t need, bool take_all, const uint32_t* pre, Cand* cl, uint32_t* h2,
-                          uint32_t* tmp, int* s_bin, uint32_t* s_beyond) {
+// With kSv the chosen rows and scores also go to crow / czs (LDS) for the
+// fused softmax . V. Returns the number of rows taken before the cap at K.
+template <bool kLds, bool kSv>
+STDK_DEV uint32_t select_tail(const SelectArgs& a, int64_t seg, int P, int64_t span, uint32_t m, uint32_t pre22,
+                              uint32_t need, bool take_all, const uint32_t* pre, Cand* cl, uint32_t* h2,
+                              uint32_t* tmp, int* s_bin, uint32_t* s_beyond, int32_t* crow, float* czs) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int K = a.K;
   const Cand* lst = a.list + seg * a.n_pad;
@@ -242,6 +254,10 @@ STDK_DEV void select_tail(const SelectArgs& a, int64_t seg, int P, int64_t span,
               srow[r] = row;
               sz[r] = key2f(cv[u].key);
               if (io) io[r] = row;
+              if (kSv) {
+                crow[r] = row;
+                czs[r] = key2f(cv[u].key);
+              }
             }
             ++r;
           }
@@ -308,6 +324,10 @@ STDK_DEV void select_tail(const SelectArgs& a, int64_t seg, int P, int64_t span,
           srow[pos] = row;
           sz[pos] = key2f(cv[u].key);
           if (io) io[pos] = row;
+          if (kSv) {
+            crow[pos] = row;
+            czs[pos] = key2f(cv[u].key);
+          }
         }
         out += (uint32_t)__popcll(tm);
         eq_seen += (uint32_t)__popcll(em);
@@ -319,6 +339,7 @@ STDK_DEV void select_tail(const SelectArgs& a, int64_t seg, int P, int64_t span,
     sz[i] = -INFINITY;
     if (io) io[i] = -1;
   }
+  return tot_all;
 }
 
 // Grid (P, S), kSelThreads threads: workgroup x of segment s filters the
@@ -327,7 +348,80 @@ STDK_DEV void select_tail(const SelectArgs& a, int64_t seg, int P, int64_t span,
 // Dynamic LDS (last workgroup): pre[P + 1] (the workgroups' candidate
 // offsets) then, if the candidates fit, their contiguous copy (position
 // order); else the copy goes to clist.
-__global__ __launch_bounds__(kSelThreads) void topk_filter_select(SelectArgs a) {
+// softmax . V over the T slots in crow / czs (LDS: rows, then scores, which
+// become the weights) by the whole workgroup; the finished o and lse of
+// segment seg. red (LDS, NG x 128) and wred (kSelectWaves) are scratch.
+// Same arithmetic as sparse_sv + combine up to the order of the sums: m is
+// the maximum over all slots, the weights e^{z - m} (a -inf score weighs 0,
+// a NaN propagates) are summed in a fixed order, and the value rows are
+// accumulated per row group, then over the groups in order.
+template <typename T>
+STDK_DEV void tail_softmax_v(const SelectArgs& a, int64_t seg, const int32_t* crow, float* czs, uint32_t Tn,
+                             float (*red)[kHeadDim], float* wred) {
+  constexpr int EPL = KvTraits<T>::EPL, LPR = KvTraits<T>::LPR, ROWB = KvTraits<T>::ROWB;
+  constexpr int NG = kSelThreads / LPR;  // row groups
+  constexpr int U = 16;                  // value rows per group in flight
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int gid = tid / LPR, c = tid % LPR;
+  const uint32_t g0 = (uint32_t)(wv * (64 / LPR));  // first row group of this wave
+  __syncthreads();  // every slot written; the candidate copy (under red) is dead
+  float zm = -INFINITY;
+  for (uint32_t i = tid; i < Tn; i += kSelThreads) zm = fmaxf(zm, czs[i]);
+  zm = wave_max(zm);
+  if (lane == 0) wred[wv] = zm;
+  __syncthreads();
+  float m = wred[0];
+#pragma unroll
+  for (int v = 1; v < kSelectWaves; ++v) m = fmaxf(m, wred[v]);
+  float ps = 0.f;
+  for (uint32_t i = tid; i < Tn; i += kSelThreads) {
+    const float z = czs[i];
+    const float wt = z == -INFINITY ? 0.f : __expf(z - m);
+    czs[i] = wt;
+    ps += wt;
+  }
+  ps = wave_sum(ps);
+  __syncthreads();  // the weights are visible, and every read of m is done
+  if (lane == 0) wred[wv] = ps;
+  const int b = (int)(seg / a.Hq), hq = (int)(seg % a.Hq), hkv = hq / a.G;
+  const char* vb = a.v + (int64_t)b * a.stride_b_bytes + (int64_t)hkv * a.stride_h_bytes + c * 16;
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  for (uint32_t base = 0; base < Tn; base += NG * U) {
+    u32x4 vw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) vw[u] = load16(vb + (int64_t)crow[min(base + gid + NG * u, Tn - 1)] * ROWB);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (base + g0 + NG * u < Tn) {  // wave-uniform
+        const uint32_t i = base + gid + NG * u;
+        const float wt = i < Tn ? czs[i] : 0.f;
+        float x[EPL];
+        unpack16<T>(vw[u], x);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] = fmaf(wt, x[e], acc[e]);
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) red[gid][c * EPL + e] = acc[e];
+  __syncthreads();
+  if (tid < kHeadDim) {
+    float o = 0.f;
+#pragma unroll 8
+    for (int g = 0; g < NG; ++g) o += red[g][tid];
+    float ssum = 0.f;
+#pragma unroll
+    for (int v = 0; v < kSelectWaves; ++v) ssum += wred[v];
+    // ssum == 0: no row (o = 0, lse = -inf); a NaN sum propagates
+    a.o_out[seg * kHeadDim + tid] = ssum == 0.f ? 0.f : o / ssum;
+    if (tid == 0) a.lse_out[seg] = ssum == 0.f ? -INFINITY : m + __logf(ssum);
+  }
+}
+
+template <typename T, bool kSv>
+STDK_DEV void fsel_body(const SelectArgs& a) {
   extern __shared__ uint32_t dyn[];
   __shared__ uint32_t h1[kHistBins];  // second digit, this workgroup's candidates in bin b*
   __shared__ uint32_t h2[1024];       // third digit
@@ -483,13 +577,61 @@ __global__ __launch_bounds__(kSelThreads) void topk_filter_select(SelectArgs a) 
   const uint32_t b1 = take_all ? 0u : s_b1;
   const uint32_t need = take_all ? (uint32_t)K : (uint32_t)K - s_beyond - s_beyond1;
   const uint32_t pre22 = (b0 << 11) | b1;
-  if (m <= (uint32_t)a.cache_cap) {
-    Cand* cl = reinterpret_cast<Cand*>(dyn + ((P + 2) & ~1));
-    select_tail<true>(a, seg, P, span, m, pre22, need, take_all, pre, cl, h2, tmp, &s_bin, &s_beyond);
-  } else {
-    select_tail<false>(a, seg, P, span, m, pre22, need, take_all, pre, a.clist + seg * a.n_pad, h2, tmp, &s_bin,
-                       &s_beyond);
+  // fused softmax . V: the static slots' scores and rows are requested now
+  // (clamped loads, kept in registers until the chosen rows are known);
+  // chosen and static slots go after the candidate copy, and the softmax's
+  // group sums overwrite the copy once it is read
+  const int pre_words = (P + 2) & ~1;
+  int32_t* crow = nullptr;
+  float* czs = nullptr;
+  float zst[kFuseStatic];
+  int32_t rst[kFuseStatic];
+  if (kSv) {
+    crow = reinterpret_cast<int32_t*>(dyn + pre_words + 2 * a.cache_cap);
+    czs = reinterpret_cast<float*>(crow + (K + a.n_extra));
+    if (a.n_extra > 0) {
+#pragma unroll
+      for (int u = 0; u < kFuseStatic; ++u) {
+        const int64_t p = a.n + min(tid + kSelThreads * u, a.n_extra - 1);
+        zst[u] = a.scores[seg * a.n_pad + p];
+        rst[u] = (int32_t)pos_to_row(a.tab, p);
+      }
+    }
   }
+  uint32_t tot;
+  if (m <= (uint32_t)a.cache_cap) {
+    Cand* cl = reinterpret_cast<Cand*>(dyn + pre_words);
+    tot = select_tail<true, kSv>(a, seg, P, span, m, pre22, need, take_all, pre, cl, h2, tmp, &s_bin, &s_beyond,
+                                 crow, czs);
+  } else {
+    tot = select_tail<false, kSv>(a, seg, P, span, m, pre22, need, take_all, pre, a.clist + seg * a.n_pad, h2, tmp,
+                                  &s_bin, &s_beyond, crow, czs);
+  }
+  if (kSv) {
+    const uint32_t nk = min(tot, (uint32_t)K);
+#pragma unroll
+    for (int u = 0; u < kFuseStatic; ++u) {
+      const int j = tid + kSelThreads * u;
+      if (j < a.n_extra) {
+        crow[nk + j] = rst[u];
+        czs[nk + j] = zst[u];
+      }
+    }
+    tail_softmax_v<T>(a, seg, crow, czs, nk + (uint32_t)a.n_extra,
+                      reinterpret_cast<float(*)[kHeadDim]>(dyn + pre_words), reinterpret_cast<float*>(tmp));
+  }
+}
+
+__global__ __launch_bounds__(kSelThreads) void topk_filter_select(SelectArgs a) { fsel_body<uint16_t, false>(a); }
+
+// topk_filter_select whose last workgroup per segment also forms softmax . V
+// over the chosen rows and the static slots (tail_softmax_v): one launch
+// instead of three (sparse_sv + combine after the select). Dynamic LDS: as
+// topk_filter_select with room for the copy of at least the group sums
+// (NG x 128 floats), then K + n_extra rows and as many scores.
+template <typename T>
+__global__ __launch_bounds__(kSelThreads) void topk_filter_select_sv(SelectArgs a) {
+  fsel_body<T, true>(a);
 }
 
 // ---------------------------------------------------------------------------
