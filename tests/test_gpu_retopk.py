@@ -250,6 +250,23 @@ def test_retopk_serving_variants(ops, B, tau, K, L):
     assert s["reuse"] + s["exact"] > 0
 
 
+@pytest.mark.parametrize("K", [3072, 4096])
+def test_retopk_rerank_path_lockstep(ops, K):
+    """Candidate sets too large for one workgroup's LDS (R*K + W = 12,320 and
+    16,416 slots): the reuse heads take retopk_select, retopk_rerank and the
+    rerank select (staged in LDS for the first size, from global memory for
+    the second), then the row-split softmax . V that pushes the cache; every
+    head against the oracle, refreshes included."""
+    log(f"case retopk rerank path K={K} L=32768")
+    w = make_workload(3, L=32768, steps=12, warm=8)
+    p = ref.RetopkParams(top_k=K, cache_cap=8, top_r=4, recent=32, tau=0.85, refresh=4)
+    heads = [(0, h) for h in range(28)]
+    s = run_lockstep(ops, w, p, 12, heads, n_warm=8)
+    log(f"retopk rerank path K={K}: reuse {s['reuse']} exact {s['exact']} flagged {s['flagged']} "
+        f"mean M {np.mean(s['cand']) if s['cand'] else 0:.0f} band swaps {s['swaps']}")
+    assert s["reuse"] > 0 and s["exact"] > 0
+
+
 @pytest.mark.slow
 def test_retopk_c3_full_lockstep(ops):
     """c3 at full size (L0 = 65536, K=512, C=32, R=4, W=32, tau=0.85,
