@@ -14,7 +14,12 @@
  *    thread) holds the text. No C++ exception crosses the ABI.
  *  - Ordering: all work is enqueued on `stream` (a hipStream_t; NULL = the
  *    legacy default stream) and nothing is synchronised inside the library.
- *  - Determinism: identical inputs give bit-identical outputs.
+ *  - Determinism: identical inputs give bit-identical outputs. The chosen
+ *    rows never depend on the batch; o and lse are summed in one of two
+ *    fixed orders, chosen by the head count (B * n_q_heads at least the
+ *    GPU's CU count folds softmax . V into the select launch), so the same
+ *    sequence in a batch on the other side of that count may differ in the
+ *    last bits of o and lse.
  *  - Concurrency: calls are reentrant; two calls that are in flight at the
  *    same time must not share a workspace buffer.
  *  - Workspace state: the first B * n_q_heads * 16448 bytes of a workspace
