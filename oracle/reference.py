@@ -25,7 +25,7 @@ Sources (cited by page title and section):
   candidate union with the recent window, exact rerank, similarity fallback
   and periodic refresh).
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
 
 * scale = 1/sqrt(d) with d the head dimension; passed explicitly.
 * Top-K ties go to the lowest row index. Index sets are returned ascending,

@@ -90,7 +90,7 @@ def oracle_head(w, b: int, h: int, ranges, K: int, q=None):
 
 
 # Oracle work over many heads runs in a thread pool (numpy releases the GIL
-# inside its array loops); the GPU machine gives one GPU 16 host threads.
+# inside its array loops), at most 16 host threads.
 ORACLE_THREADS = max(1, min(16, os.cpu_count() or 1))
 
 
