@@ -59,14 +59,15 @@ int32_t ok() {
 enum KernelId {
   KID_SCAN, KID_SELECT, KID_SV, KID_DENSE, KID_COMBINE, KID_MERGE, KID_FILL,
   KID_RT_SELECT, KID_RT_RERANK, KID_RT_RSEL, KID_RT_INIT, KID_MQ_BLOCKMAX, KID_MQ_THRESH,
-  KID_MQ_COLLECT, KID_MQ_SELECT, KID_MQ_FILL, KID_RT_VOTE, KID_Q8_QUANT, KID_READ, KID_RT_ATTEND, KID_RT_REUSE, KID_SELECT_SV, KID_COUNT
+  KID_MQ_COLLECT, KID_MQ_SELECT, KID_MQ_FILL, KID_RT_VOTE, KID_Q8_QUANT, KID_READ, KID_RT_ATTEND, KID_RT_REUSE, KID_SELECT_SV, KID_SELECT_LDS, KID_SELECT_LDS_SV, KID_COUNT
 };
 const char* const kKernelNames[KID_COUNT] = {
     "k_scan",        "topk_filter_select",             "sparse_sv",
     "dense_attn",  "combine",       "attn_merge",    "fill_empty",           "retopk_select",
     "retopk_rerank", "retopk_rerank_select", "retopk_init", "mq_blockmax",
     "mq_threshold",  "mq_collect",    "mq_select",     "mq_fill",       "retopk_vote",   "k_quantize",
-    "hbm_read",      "retopk_attend", "retopk_reuse", "topk_filter_select_sv"};
+    "hbm_read",      "retopk_attend", "retopk_reuse", "topk_filter_select_sv",
+    "topk_select_lds", "topk_select_lds_sv"};
 
 struct Profiler {
   std::mutex mu;
@@ -240,6 +241,11 @@ int32_t dev_info(DevInfo** out) {
     (void)hipFuncSetAttribute((const void*)topk_filter_select_sv<uint16_t>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               dyn_max);
     (void)hipFuncSetAttribute((const void*)topk_filter_select_sv<float>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              dyn_max);
+    (void)hipFuncSetAttribute((const void*)topk_select_lds, hipFuncAttributeMaxDynamicSharedMemorySize, dyn_max);
+    (void)hipFuncSetAttribute((const void*)topk_select_lds_sv<uint16_t>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              dyn_max);
+    (void)hipFuncSetAttribute((const void*)topk_select_lds_sv<float>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               dyn_max);
     (void)hipFuncSetAttribute((const void*)retopk_select<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               std::max(0, d.max_lds - 12 * 1024));
@@ -478,10 +484,11 @@ struct Q8Keys {
   int64_t max_len;
 };
 
-// Softmax . V fused into the select launch (topk_filter_select_sv): where
-// the caller wants o and lse of every head (no per-head mask, no cache
-// push), the chosen plus static slots fit the last workgroup's LDS, and
-// there are at least as many heads as CUs. One workgroup reads a head's
+// Softmax . V fused into the select launch, where the caller wants o and
+// lse of every head (no per-head mask, no cache push). Long segments
+// (topk_filter_select_sv): where the chosen plus static slots fit the last
+// workgroup's LDS and there are at least as many heads as CUs; short ones
+// (topk_select_lds_sv): fuse_lds_short below. One workgroup reads a head's
 // value rows at about one CU's share of HBM bandwidth (~40 GB/s measured),
 // so the fusion pays only when the heads' tails cover the whole chip
 // (batched decode: 3.47K against 3.42K steps/s on 16 x 32 heads); with 32
@@ -508,6 +515,31 @@ bool fuse_lds(const Geo& g, const TopkWs& w, const DevInfo* di, size_t* dyn, int
   *cache_cap = (int32_t)cap;
   *dyn = pre_bytes + (size_t)cap * sizeof(Cand) + slots;
   return true;
+}
+
+// LDS of the fused one-workgroup select of a short segment
+// (topk_select_lds_sv). Each head's softmax . V then runs in one workgroup
+// at about one CU's share of HBM bandwidth, which pays where the heads cover
+// the chip or where a head's value rows are few (K + n_extra rows of at most
+// kFuseShortBytes: the separate softmax . V launch costs more than reading
+// them); false otherwise or when it does not fit.
+constexpr size_t kFuseShortBytes = 64 * 1024;
+bool fuse_lds_short(const Geo& g, const TopkWs& w, const DevInfo* di, size_t* dyn) {
+  if (w.n > kSelLdsMax || w.n_extra > (int64_t)kFuseStatic * kSelThreads) return false;
+  const int rowb = g.bf16 ? KvTraits<uint16_t>::ROWB : KvTraits<float>::ROWB;
+  if (w.S < di->n_cu && (size_t)(w.K + w.n_extra) * rowb > kFuseShortBytes) return false;
+  const size_t head = g.bf16 ? sel_lds_sv_head<uint16_t>(w.n) : sel_lds_sv_head<float>(w.n);
+  const size_t bytes = head + (size_t)(w.K + w.n_extra) * 8;
+  if (bytes + kSelStaticLds > (size_t)di->max_lds) return false;
+  *dyn = bytes;
+  return true;
+}
+
+// Whether run_exact_select can fuse softmax . V into its select launch.
+bool can_fuse(const Geo& g, const TopkWs& w, const DevInfo* di) {
+  size_t dyn;
+  int32_t cap;
+  return w.n <= kSelLdsMax ? fuse_lds_short(g, w, di, &dyn) : fuse_lds(g, w, di, &dyn, &cap);
 }
 
 int32_t run_exact_select(const Geo& g, const TopkWs& w, char* ws, const float* q, const void* k_cache,
@@ -594,6 +626,29 @@ int32_t run_exact_select(const Geo& g, const TopkWs& w, char* ws, const float* q
     const int64_t want = std::min<int64_t>(w.n, std::max<int64_t>(8192, 2 * w.K));
     size_t dyn = std::min(avail, pre_bytes + (size_t)want * sizeof(Cand));
     a.cache_cap = (int32_t)((dyn - pre_bytes) / sizeof(Cand));
+    if (w.n <= kSelLdsMax) {
+      // a short segment: the whole select in one workgroup per head
+      if (fuse) {
+        size_t lds;
+        if (!fuse_lds_short(g, w, di, &lds)) return fail(STDK_EUNSUPPORTED, "fused softmax.V does not fit");
+        a.v = (const char*)fuse->v_cache;
+        a.stride_b_bytes = g.sb_bytes;
+        a.stride_h_bytes = g.sh_bytes;
+        a.o_out = fuse->o_out;
+        a.lse_out = fuse->lse_out;
+        a.n_extra = (int32_t)w.n_extra;
+        a.Hq = g.Hq;
+        a.G = g.G;
+        return launch(KID_SELECT_LDS_SV, s, [&](hipEvent_t e0, hipEvent_t e1) {
+          if (g.bf16) STDK_LAUNCH(topk_select_lds_sv<uint16_t>, dim3((unsigned)w.S), dim3(kSelThreads), lds, s, a);
+          else STDK_LAUNCH(topk_select_lds_sv<float>, dim3((unsigned)w.S), dim3(kSelThreads), lds, s, a);
+        });
+      }
+      const size_t lds = (size_t)2 * sel_lds_stride(w.n) * 4;
+      return launch(KID_SELECT_LDS, s, [&](hipEvent_t e0, hipEvent_t e1) {
+        STDK_LAUNCH(topk_select_lds, dim3((unsigned)w.S), dim3(kSelThreads), lds, s, a);
+      });
+    }
     if (w.wg > 65535) return fail(STDK_EUNSUPPORTED, "%lld select workgroups per head", (long long)w.wg);
     const dim3 grid((unsigned)w.wg, (unsigned)w.S);
     if (fuse) {
@@ -928,9 +983,7 @@ int32_t run_static(const Geo& g, const StaticSplit& sp, char* ws, const float* q
                      lse_out, s, sp.n_dyn);
   }
   const TopkWs w = topk_ws(g.S, sp.n_dyn, top_k, sp.n_st);
-  size_t dyn;
-  int32_t cap;
-  if (fuse_lds(g, w, di, &dyn, &cap)) {
+  if (can_fuse(g, w, di)) {
     const SvFuse fz{v_cache, o_out, lse_out};
     return run_exact_select(g, w, ws, q, k_cache, sp.all, scale, nullptr, idx_out, di, s, nullptr, nullptr, &fz);
   }
@@ -1132,10 +1185,8 @@ int32_t topk_attn_decode(const stdk_layout* lay, const float* q, const void* k_c
   if (top_k >= n) {
     rc = run_dense(g, dense_ws(g.S, n), ws, q, k_cache, v_cache, tab, scale, top_k, idx_out, o_out, lse_out, s);
   } else {
-    size_t dyn;
-    int32_t cap;
     const SvFuse fz{v_cache, o_out, lse_out};
-    if (fuse_lds(g, w, di, &dyn, &cap)) {
+    if (can_fuse(g, w, di)) {
       rc = run_exact_select(g, w, ws, q, k_cache, tab, scale, nullptr, idx_out, di, s, nullptr, nullptr, &fz);
     } else {
       rc = run_exact_select(g, w, ws, q, k_cache, tab, scale, nullptr, idx_out, di, s);

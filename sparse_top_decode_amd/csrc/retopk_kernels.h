@@ -710,196 +710,6 @@ __global__ __launch_bounds__(kRerankSelThreads) void retopk_rerank_select(RtRera
 // candidate segment and ranks with ballots.
 constexpr int kRselStageMax = 16384;
 
-// The exact top-K of the M candidate scores zs (rows rs) staged in LDS,
-// ties to the lower candidate index (the candidates ascend by row), in two
-// steps: the cut (lds_cut_radix or lds_cut_linear), then an ordered
-// compaction (lds_emit) in which wave w owns a contiguous candidate segment
-// and ballots rank the taken ones. emit(pos, row, z) receives the chosen
-// candidates in ascending order (pos < K); the count before the cap at K is
-// returned. NT threads; every thread must call them.
-//
-// The cut of a top-K selection: keys (f2key of the scores) above Tk are
-// taken and, of the keys equal to Tk, the first `need` in candidate order;
-// take_all: every candidate (M <= K).
-struct TopkCut {
-  uint32_t Tk, need;
-  bool take_all;
-};
-
-// Radix passes over a window of keys [lo, lo + width): the first spans the
-// candidates' own key range, each later one exactly the bin that holds the
-// K-th key (keys above it were counted in `beyond` already and must not be
-// counted again), in 2048 bins of 1 << sh keys; stop at single keys (sh = 0)
-// or once that bin is taken whole. The threshold Tk is then the bin's
-// smallest key and `need` the number of keys equal to it to take.
-template <int NT>
-STDK_DEV TopkCut lds_cut_radix(const float* zs, uint32_t M, int K, uint32_t* h, uint32_t (*wc)[NT / 64],
-                               int* s_bin_p, uint32_t* s_beyond_p) {
-  constexpr int NW = NT / 64;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  if (M <= (uint32_t)K) return TopkCut{0u, (uint32_t)K, true};
-  int& s_bin = *s_bin_p;
-  uint32_t& s_beyond = *s_beyond_p;
-  uint32_t need = (uint32_t)K;
-  uint32_t kmin = 0xffffffffu, kmax = 0u;
-  for (uint32_t j = tid; j < M; j += NT) {
-    const uint32_t kv = f2key(zs[j]);
-    kmin = min(kmin, kv);
-    kmax = max(kmax, kv);
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
-  }
-  if (lane == 0) {
-    wc[0][w] = kmin;
-    wc[1][w] = kmax;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int v = 0; v < NW; ++v) {
-    kmin = min(kmin, wc[0][v]);
-    kmax = max(kmax, wc[1][v]);
-  }
-  __syncthreads();
-  uint32_t lo = kmin;
-  const uint32_t span = kmax - kmin;
-  int sh = span < 2048u ? 0 : (32 - __clz((int)span)) - 11;
-  uint64_t width = 2048ull << sh;  // covers [kmin, kmax]
-  // at most three passes: sh <= 21 and drops by 11 (to 0) each time
-  for (;;) {
-    for (int i = tid; i < 2048; i += NT) h[i] = 0u;
-    __syncthreads();
-    for (uint32_t j = tid; j < M; j += NT) {
-      const uint32_t kv = f2key(zs[j]);
-      if (kv >= lo && (uint64_t)(kv - lo) < width) atomicAdd(&h[(kv - lo) >> sh], 1u);
-    }
-    __syncthreads();
-    if (w == 0) find_bin_wave<2048, true>(h, need, &s_bin, &s_beyond);
-    __syncthreads();
-    const int bin = s_bin < 0 ? 0 : s_bin;
-    need -= s_beyond;
-    lo += (uint32_t)bin << sh;
-    width = 1ull << sh;
-    if (sh == 0 || h[bin] == need) break;
-    sh = sh > 11 ? sh - 11 : 0;
-    __syncthreads();
-  }
-  return TopkCut{lo, need, false};
-}
-
-// One histogram pass instead of radix passes when the scores are finite
-// with lo < hi (their minimum and maximum): bin(z) = min(2047, (z - lo) *
-// 2048 / (hi - lo)) truncated is non-decreasing in z, so every score in a
-// higher bin is larger than every score in a lower one. The bin holding the
-// K-th largest score is then ranked exactly (its keys, at most kCutList of
-// them) to give Tk and the number of keys equal to it to take. h must be
-// zero and *s_cnt 0 on entry. Returns false (workgroup-uniform, nothing
-// decided) when that bin holds more than kCutList scores.
-constexpr int kCutList = 64;
-template <int NT>
-STDK_DEV bool lds_cut_linear(const float* zs, uint32_t M, int K, float lo, float hi, uint32_t* h,
-                             uint32_t* lst, uint32_t* s_cnt, uint32_t* s_cut, int* s_bin, uint32_t* s_beyond,
-                             TopkCut* out) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const float sc = 2048.f / (hi - lo);
-  auto bin_of = [&](float z) { return (int)fminf((z - lo) * sc, 2047.f); };
-  for (uint32_t j = tid; j < M; j += NT) atomicAdd(&h[bin_of(zs[j])], 1u);
-  __syncthreads();
-  if (w == 0) find_bin_wave<2048, true>(h, (uint32_t)K, s_bin, s_beyond);
-  __syncthreads();
-  const int b = *s_bin;
-  const uint32_t need = (uint32_t)K - *s_beyond, cb = h[b];
-  if (cb > (uint32_t)kCutList) return false;
-  for (uint32_t j = tid; j < M; j += NT) {
-    const float z = zs[j];
-    if (bin_of(z) == b) lst[atomicAdd(s_cnt, 1u)] = f2key(z);
-  }
-  __syncthreads();
-  if (w == 0) {
-    // Tk: the key with fewer than `need` keys above it and at least `need`
-    // at or above it
-    const uint32_t k = lane < (int)cb ? lst[lane] : 0u;
-    uint32_t gt = 0, ge = 0;
-    for (uint32_t f = 0; f < cb; ++f) {
-      const uint32_t kf = lst[f];
-      gt += kf > k;
-      ge += kf >= k;
-    }
-    if (lane < (int)cb && gt < need && need <= ge) {
-      s_cut[0] = k;
-      s_cut[1] = need - gt;
-    }
-  }
-  __syncthreads();
-  *out = TopkCut{s_cut[0], s_cut[1], false};
-  return true;
-}
-
-// Ordered compaction of the selection: wave w owns candidates [s0, s1);
-// emit(pos, row, score) for each taken candidate in candidate order, pos <
-// K. Returns the number taken.
-template <int NT, typename Emit>
-STDK_DEV uint32_t lds_emit(const float* zs, const int32_t* rs, uint32_t M, int K, const TopkCut& cut,
-                           uint32_t (*wc)[NT / 64], Emit emit) {
-  constexpr int NW = NT / 64;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const bool take_all = cut.take_all;
-  const uint32_t Tk = cut.Tk, need = cut.need;
-  const uint32_t SEG = ((M + NW - 1) / NW + 63u) & ~63u;
-  const uint32_t s0 = min(M, (uint32_t)w * SEG), s1 = min(M, s0 + SEG);
-  uint32_t cg = 0, ce = 0;
-  for (uint32_t j = s0 + lane; j < s1; j += 64) {
-    const uint32_t kv = f2key(zs[j]);
-    cg += take_all || kv > Tk;
-    ce += !take_all && kv == Tk;
-  }
-  cg = __shfl(wave_incl_scan(cg), 63, 64);
-  ce = __shfl(wave_incl_scan(ce), 63, 64);
-  if (lane == 0) {
-    wc[0][w] = cg;
-    wc[1][w] = ce;
-  }
-  __syncthreads();
-  uint32_t out = 0, eq_seen = 0, tot = 0, eq_all = 0;
-#pragma unroll
-  for (int v = 0; v < NW; ++v) {
-    const uint32_t e = wc[1][v];
-    const uint32_t te = min(e, need > eq_all ? need - eq_all : 0u);
-    if (v < w) {
-      out += wc[0][v] + te;
-      eq_seen += e;
-    }
-    tot += wc[0][v] + te;
-    eq_all += e;
-  }
-  for (uint32_t jb = s0; jb < s1; jb += 64) {
-    const uint32_t j = jb + lane;
-    const bool valid = j < s1;
-    const float z = valid ? zs[j] : 0.f;
-    const uint32_t kv = f2key(z);
-    const bool gt = valid && (take_all || kv > Tk);
-    const bool eq = valid && !take_all && kv == Tk;
-    const uint64_t em = __ballot(eq);
-    const bool take = gt || (eq && eq_seen + lane_rank(em) < need);
-    const uint64_t tm = __ballot(take);
-    const uint32_t pos = out + lane_rank(tm);
-    if (take && pos < (uint32_t)K) emit(pos, rs[j], z);
-    out += (uint32_t)__popcll(tm);
-    eq_seen += (uint32_t)__popcll(em);
-  }
-  return tot;
-}
-
-
-// lds_cut_radix, then lds_emit
-template <int NT, typename Emit>
-STDK_DEV uint32_t lds_topk(const float* zs, const int32_t* rs, uint32_t M, int K, uint32_t* h,
-                           uint32_t (*wc)[NT / 64], int* s_bin_p, uint32_t* s_beyond_p, Emit emit) {
-  const TopkCut cut = lds_cut_radix<NT>(zs, M, K, h, wc, s_bin_p, s_beyond_p);
-  return lds_emit<NT>(zs, rs, M, K, cut, wc, emit);
-}
 
 
 __global__ __launch_bounds__(kRerankSelThreads) void retopk_rerank_select_lds(RtRerankArgs a) {

@@ -360,7 +360,6 @@ STDK_DEV void tail_softmax_v(const SelectArgs& a, int64_t seg, const int32_t* cr
                              float (*red)[kHeadDim], float* wred) {
   constexpr int EPL = KvTraits<T>::EPL, LPR = KvTraits<T>::LPR, ROWB = KvTraits<T>::ROWB;
   constexpr int NG = kSelThreads / LPR;  // row groups
-  constexpr int U = 16;                  // value rows per group in flight
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int gid = tid / LPR, c = tid % LPR;
   const uint32_t g0 = (uint32_t)(wv * (64 / LPR));  // first row group of this wave
@@ -388,7 +387,13 @@ STDK_DEV void tail_softmax_v(const SelectArgs& a, int64_t seg, const int32_t* cr
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-  for (uint32_t base = 0; base < Tn; base += NG * U) {
+  // U value rows per group in flight, as few as the slot count needs: every
+  // load is issued (clamped to the last slot) so that they are all in flight
+  // at once, and loads past the slots would only repeat the last row. Each
+  // thread adds its rows in the same order whatever U is.
+  Tn = (uint32_t)__builtin_amdgcn_readfirstlane((int)Tn);
+  auto gather = [&](auto uc, uint32_t base) {
+    constexpr int U = decltype(uc)::value;
     u32x4 vw[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) vw[u] = load16(vb + (int64_t)crow[min(base + gid + NG * u, Tn - 1)] * ROWB);
@@ -403,6 +408,13 @@ STDK_DEV void tail_softmax_v(const SelectArgs& a, int64_t seg, const int32_t* cr
         for (int e = 0; e < EPL; ++e) acc[e] = fmaf(wt, x[e], acc[e]);
       }
     }
+  };
+  if (Tn <= 2 * NG) {
+    gather(std::integral_constant<int, 2>(), 0u);
+  } else if (Tn <= 4 * NG) {
+    gather(std::integral_constant<int, 4>(), 0u);
+  } else {
+    for (uint32_t base = 0; base < Tn; base += NG * 16) gather(std::integral_constant<int, 16>(), base);
   }
 #pragma unroll
   for (int e = 0; e < EPL; ++e) red[gid][c * EPL + e] = acc[e];
@@ -632,6 +644,349 @@ __global__ __launch_bounds__(kSelThreads) void topk_filter_select(SelectArgs a) 
 template <typename T>
 __global__ __launch_bounds__(kSelThreads) void topk_filter_select_sv(SelectArgs a) {
   fsel_body<T, true>(a);
+}
+
+// The exact top-K of the M candidate scores zs (rows rs) staged in LDS,
+// ties to the lower candidate index (the candidates ascend by row), in two
+// steps: the cut (lds_cut_radix or lds_cut_linear), then an ordered
+// compaction (lds_emit) in which wave w owns a contiguous candidate segment
+// and ballots rank the taken ones. emit(pos, row, z) receives the chosen
+// candidates in ascending order (pos < K); the count before the cap at K is
+// returned. NT threads; every thread must call them.
+//
+// The cut of a top-K selection: keys (f2key of the scores) above Tk are
+// taken and, of the keys equal to Tk, the first `need` in candidate order;
+// take_all: every candidate (M <= K).
+struct TopkCut {
+  uint32_t Tk, need;
+  bool take_all;
+};
+
+// Radix passes over a window of keys [lo, lo + width): the first spans the
+// candidates' own key range, each later one exactly the bin that holds the
+// K-th key (keys above it were counted in `beyond` already and must not be
+// counted again), in 2048 bins of 1 << sh keys; stop at single keys (sh = 0)
+// or once that bin is taken whole. The threshold Tk is then the bin's
+// smallest key and `need` the number of keys equal to it to take.
+template <int NT>
+STDK_DEV TopkCut lds_cut_radix(const float* zs, uint32_t M, int K, uint32_t* h, uint32_t (*wc)[NT / 64],
+                               int* s_bin_p, uint32_t* s_beyond_p) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (M <= (uint32_t)K) return TopkCut{0u, (uint32_t)K, true};
+  int& s_bin = *s_bin_p;
+  uint32_t& s_beyond = *s_beyond_p;
+  uint32_t need = (uint32_t)K;
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+  for (uint32_t j = tid; j < M; j += NT) {
+    const uint32_t kv = f2key(zs[j]);
+    kmin = min(kmin, kv);
+    kmax = max(kmax, kv);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+  }
+  if (lane == 0) {
+    wc[0][w] = kmin;
+    wc[1][w] = kmax;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int v = 0; v < NW; ++v) {
+    kmin = min(kmin, wc[0][v]);
+    kmax = max(kmax, wc[1][v]);
+  }
+  __syncthreads();
+  uint32_t lo = kmin;
+  const uint32_t span = kmax - kmin;
+  int sh = span < 2048u ? 0 : (32 - __clz((int)span)) - 11;
+  uint64_t width = 2048ull << sh;  // covers [kmin, kmax]
+  // at most three passes: sh <= 21 and drops by 11 (to 0) each time
+  for (;;) {
+    for (int i = tid; i < 2048; i += NT) h[i] = 0u;
+    __syncthreads();
+    for (uint32_t j = tid; j < M; j += NT) {
+      const uint32_t kv = f2key(zs[j]);
+      if (kv >= lo && (uint64_t)(kv - lo) < width) atomicAdd(&h[(kv - lo) >> sh], 1u);
+    }
+    __syncthreads();
+    if (w == 0) find_bin_wave<2048, true>(h, need, &s_bin, &s_beyond);
+    __syncthreads();
+    const int bin = s_bin < 0 ? 0 : s_bin;
+    need -= s_beyond;
+    lo += (uint32_t)bin << sh;
+    width = 1ull << sh;
+    if (sh == 0 || h[bin] == need) break;
+    sh = sh > 11 ? sh - 11 : 0;
+    __syncthreads();
+  }
+  return TopkCut{lo, need, false};
+}
+
+// One histogram pass instead of radix passes when the scores are finite
+// with lo < hi (their minimum and maximum): bin(z) = min(2047, (z - lo) *
+// 2048 / (hi - lo)) truncated is non-decreasing in z, so every score in a
+// higher bin is larger than every score in a lower one. The bin holding the
+// K-th largest score is then ranked exactly (its keys, at most kCutList of
+// them) to give Tk and the number of keys equal to it to take. h must be
+// zero and *s_cnt 0 on entry. Returns false (workgroup-uniform, nothing
+// decided) when that bin holds more than kCutList scores.
+constexpr int kCutList = 64;
+template <int NT>
+STDK_DEV bool lds_cut_linear(const float* zs, uint32_t M, int K, float lo, float hi, uint32_t* h,
+                             uint32_t* lst, uint32_t* s_cnt, uint32_t* s_cut, int* s_bin, uint32_t* s_beyond,
+                             TopkCut* out) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const float sc = 2048.f / (hi - lo);
+  auto bin_of = [&](float z) { return (int)fminf((z - lo) * sc, 2047.f); };
+  for (uint32_t j = tid; j < M; j += NT) atomicAdd(&h[bin_of(zs[j])], 1u);
+  __syncthreads();
+  if (w == 0) find_bin_wave<2048, true>(h, (uint32_t)K, s_bin, s_beyond);
+  __syncthreads();
+  const int b = *s_bin;
+  const uint32_t need = (uint32_t)K - *s_beyond, cb = h[b];
+  if (cb > (uint32_t)kCutList) return false;
+  for (uint32_t j = tid; j < M; j += NT) {
+    const float z = zs[j];
+    if (bin_of(z) == b) lst[atomicAdd(s_cnt, 1u)] = f2key(z);
+  }
+  __syncthreads();
+  if (w == 0) {
+    // Tk: the key with fewer than `need` keys above it and at least `need`
+    // at or above it
+    const uint32_t k = lane < (int)cb ? lst[lane] : 0u;
+    uint32_t gt = 0, ge = 0;
+    for (uint32_t f = 0; f < cb; ++f) {
+      const uint32_t kf = lst[f];
+      gt += kf > k;
+      ge += kf >= k;
+    }
+    if (lane < (int)cb && gt < need && need <= ge) {
+      s_cut[0] = k;
+      s_cut[1] = need - gt;
+    }
+  }
+  __syncthreads();
+  *out = TopkCut{s_cut[0], s_cut[1], false};
+  return true;
+}
+
+// Ordered compaction of the selection: wave w owns candidates [s0, s1);
+// emit(pos, row, score) for each taken candidate in candidate order, pos <
+// K. Returns the number taken.
+template <int NT, typename Emit>
+STDK_DEV uint32_t lds_emit(const float* zs, const int32_t* rs, uint32_t M, int K, const TopkCut& cut,
+                           uint32_t (*wc)[NT / 64], Emit emit) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const bool take_all = cut.take_all;
+  const uint32_t Tk = cut.Tk, need = cut.need;
+  const uint32_t SEG = ((M + NW - 1) / NW + 63u) & ~63u;
+  const uint32_t s0 = min(M, (uint32_t)w * SEG), s1 = min(M, s0 + SEG);
+  uint32_t cg = 0, ce = 0;
+  for (uint32_t j = s0 + lane; j < s1; j += 64) {
+    const uint32_t kv = f2key(zs[j]);
+    cg += take_all || kv > Tk;
+    ce += !take_all && kv == Tk;
+  }
+  cg = __shfl(wave_incl_scan(cg), 63, 64);
+  ce = __shfl(wave_incl_scan(ce), 63, 64);
+  if (lane == 0) {
+    wc[0][w] = cg;
+    wc[1][w] = ce;
+  }
+  __syncthreads();
+  uint32_t out = 0, eq_seen = 0, tot = 0, eq_all = 0;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) {
+    const uint32_t e = wc[1][v];
+    const uint32_t te = min(e, need > eq_all ? need - eq_all : 0u);
+    if (v < w) {
+      out += wc[0][v] + te;
+      eq_seen += e;
+    }
+    tot += wc[0][v] + te;
+    eq_all += e;
+  }
+  for (uint32_t jb = s0; jb < s1; jb += 64) {
+    const uint32_t j = jb + lane;
+    const bool valid = j < s1;
+    const float z = valid ? zs[j] : 0.f;
+    const uint32_t kv = f2key(z);
+    const bool gt = valid && (take_all || kv > Tk);
+    const bool eq = valid && !take_all && kv == Tk;
+    const uint64_t em = __ballot(eq);
+    const bool take = gt || (eq && eq_seen + lane_rank(em) < need);
+    const uint64_t tm = __ballot(take);
+    const uint32_t pos = out + lane_rank(tm);
+    if (take && pos < (uint32_t)K) emit(pos, rs[j], z);
+    out += (uint32_t)__popcll(tm);
+    eq_seen += (uint32_t)__popcll(em);
+  }
+  return tot;
+}
+
+
+// lds_cut_radix, then lds_emit
+template <int NT, typename Emit>
+STDK_DEV uint32_t lds_topk(const float* zs, const int32_t* rs, uint32_t M, int K, uint32_t* h,
+                           uint32_t (*wc)[NT / 64], int* s_bin_p, uint32_t* s_beyond_p, Emit emit) {
+  const TopkCut cut = lds_cut_radix<NT>(zs, M, K, h, wc, s_bin_p, s_beyond_p);
+  return lds_emit<NT>(zs, rs, M, K, cut, wc, emit);
+}
+
+
+// ---------------------------------------------------------------------------
+// topk_select_lds: the select of a short segment (n <= kSelLdsMax positions)
+// in one workgroup, without the filter's hand-over between workgroups: all
+// n scores to LDS, the exact top K there (the same key order and
+// lowest-position ties as topk_filter_select), the chosen rows in ascending
+// order. The segment's first-digit histogram (the scan's counts) is zeroed
+// for the next call. Dynamic LDS: n scores, then n positions (each array
+// rounded up to 64 entries).
+//
+// topk_select_lds_sv<T> goes on to softmax . V over the chosen rows and the
+// n_extra static slots (tail_softmax_v) in the same workgroup; the chosen
+// rows go to idx_out only (the workspace's chosen-row arrays are not
+// written). Dynamic LDS: the larger of the two arrays above and the
+// softmax's group sums, then K + n_extra rows and as many scores.
+// ---------------------------------------------------------------------------
+constexpr int kSelLdsMax = 8192;
+inline __host__ __device__ uint32_t sel_lds_stride(int64_t n) { return (uint32_t)((n + 63) & ~(int64_t)63); }
+// bytes in front of the slot arrays of topk_select_lds_sv
+template <typename T>
+inline __host__ __device__ size_t sel_lds_sv_head(int64_t n) {
+  const size_t arrays = (size_t)2 * sel_lds_stride(n) * 4;
+  const size_t red = (size_t)(kSelThreads / KvTraits<T>::LPR) * kHeadDim * 4;
+  return arrays > red ? arrays : red;
+}
+
+template <typename T, bool kSv>
+STDK_DEV void sel_lds_body(const SelectArgs& a) {
+  extern __shared__ uint32_t sl_dyn[];
+  __shared__ uint32_t h[kHistBins];
+  __shared__ uint32_t wc[2][kSelectWaves];
+  __shared__ float wlo[kSelectWaves], whi[kSelectWaves];
+  __shared__ uint32_t lst[kCutList], s_cut[2], s_cnt, s_bad;
+  __shared__ int s_bin;
+  __shared__ uint32_t s_beyond;
+  const int64_t seg = blockIdx.x;
+  if (a.seg_active && a.seg_active[seg] == 0) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int K = a.K;
+  const uint32_t n = (uint32_t)(a.n_dev ? min(a.n, max((int64_t)0, *a.n_dev)) : a.n);
+  float* zs = reinterpret_cast<float*>(sl_dyn);
+  int32_t* rs = reinterpret_cast<int32_t*>(sl_dyn + sel_lds_stride(a.n));
+  const float* sc = a.scores + seg * a.n_pad;
+  // the static slots' scores and rows, requested first
+  float zst[kFuseStatic];
+  int32_t rst[kFuseStatic];
+  if (kSv && a.n_extra > 0) {
+#pragma unroll
+    for (int u = 0; u < kFuseStatic; ++u) {
+      const int64_t p = a.n + min(tid + kSelThreads * u, a.n_extra - 1);
+      zst[u] = sc[p];
+      rst[u] = (int32_t)pos_to_row(a.tab, p);
+    }
+  }
+  // scores to LDS, with their range (lo, hi) and whether any is not finite
+  constexpr int U = 8;
+  float lo = INFINITY, hi = -INFINITY;
+  bool bad = false;
+  for (uint32_t j0 = 0; j0 < n; j0 += U * kSelThreads) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = sc[min(j0 + (uint32_t)(u * kSelThreads + tid), n - 1)];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t j = j0 + (uint32_t)(u * kSelThreads + tid);
+      if (j < n) {
+        zs[j] = v[u];
+        rs[j] = (int32_t)j;
+        lo = fminf(lo, v[u]);
+        hi = fmaxf(hi, v[u]);
+        bad |= !__builtin_isfinite(v[u]);
+      }
+    }
+  }
+  for (int i = tid; i < kHistBins; i += kSelThreads) h[i] = 0u;
+  if (tid == 0) {
+    s_cnt = 0u;
+    s_bad = 0u;
+  }
+  lo = wave_min(lo);
+  hi = wave_max(hi);
+  const bool wbad = __ballot(bad) != 0ull;
+  __syncthreads();
+  if (lane == 0) {
+    wlo[w] = lo;
+    whi[w] = hi;
+    if (wbad) s_bad = 1u;
+  }
+  uint32_t* hg = a.hist + seg * kHistBins;
+  for (int i = tid; i < kHistBins; i += kSelThreads) hg[i] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int v = 0; v < kSelectWaves; ++v) {
+    lo = fminf(lo, wlo[v]);
+    hi = fmaxf(hi, whi[v]);
+  }
+  // the cut: one histogram pass over [lo, hi] (lds_cut_linear) when the
+  // scores are finite and spread, else (or when the K-th score's bin is
+  // crowded) the radix passes; both give the same exact cut
+  TopkCut cut{0u, (uint32_t)K, true};
+  if (n > (uint32_t)K) {
+    const bool ok = s_bad == 0u && hi > lo && 2048.f / (hi - lo) <= __FLT_MAX__ &&
+                    lds_cut_linear<kSelThreads>(zs, n, K, lo, hi, h, lst, &s_cnt, s_cut, &s_bin, &s_beyond, &cut);
+    if (!ok) cut = lds_cut_radix<kSelThreads>(zs, n, K, h, wc, &s_bin, &s_beyond);
+  }
+  int32_t* srow = a.sel_row + seg * K;
+  float* sz = a.sel_z + seg * K;
+  int32_t* io = a.idx_out ? a.idx_out + seg * K : nullptr;
+  int32_t* crow = reinterpret_cast<int32_t*>(sl_dyn + (kSv ? sel_lds_sv_head<T>(a.n) / 4 : 0));
+  float* czs = reinterpret_cast<float*>(crow + (K + a.n_extra));
+  const uint32_t tot = lds_emit<kSelThreads>(zs, rs, n, K, cut, wc, [&](uint32_t pos, int32_t p, float z) {
+    const int32_t row = (int32_t)pos_to_row(a.tab, p);
+    if (kSv) {
+      crow[pos] = row;
+      czs[pos] = z;
+    } else {
+      srow[pos] = row;
+      sz[pos] = z;
+    }
+    if (io) io[pos] = row;
+  });
+  const uint32_t nk = min(tot, (uint32_t)K);
+  for (uint32_t i = nk + tid; i < (uint32_t)K; i += kSelThreads) {
+    if (!kSv) {
+      srow[i] = -1;
+      sz[i] = -INFINITY;
+    }
+    if (io) io[i] = -1;
+  }
+  if (kSv) {
+    // the slots' arrays lie beyond the scores read by lds_emit; the group
+    // sums that overwrite those are written after tail_softmax_v's barrier
+#pragma unroll
+    for (int u = 0; u < kFuseStatic; ++u) {
+      const int j = tid + kSelThreads * u;
+      if (j < a.n_extra) {
+        crow[nk + j] = rst[u];
+        czs[nk + j] = zst[u];
+      }
+    }
+    tail_softmax_v<T>(a, seg, crow, czs, nk + (uint32_t)a.n_extra, reinterpret_cast<float(*)[kHeadDim]>(sl_dyn),
+                      wlo);
+  }
+}
+
+__global__ __launch_bounds__(kSelThreads) void topk_select_lds(SelectArgs a) { sel_lds_body<uint16_t, false>(a); }
+
+template <typename T>
+__global__ __launch_bounds__(kSelThreads) void topk_select_lds_sv(SelectArgs a) {
+  sel_lds_body<T, true>(a);
 }
 
 // ---------------------------------------------------------------------------

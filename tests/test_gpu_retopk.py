@@ -218,7 +218,10 @@ def test_retopk_tiny_cache_all_paths(ops):
 
 
 def test_retopk_always_exact_equals_topk(ops):
-    """tau > 1: every step takes the exact path and equals topk_attn_decode."""
+    """tau > 1: every step takes the exact path: the same rows as
+    topk_attn_decode, and o and lse equal up to the order in which the fp32
+    softmax . V sums are formed (topk_attn_decode may fuse them into its
+    select launch; the ReTopK exact step keeps them separate)."""
     w = make_workload(3, L=2048, steps=6, warm=4)
     k, v = dev_kv(w)
     rt = ops.Retopk(k, 28, top_k=32, cache_cap=4, top_r=2, recent=8, tau=1.5, refresh=0, scale=w.scale)
@@ -231,7 +234,8 @@ def test_retopk_always_exact_equals_topk(ops):
         torch.cuda.synchronize()
         assert np.all(out["path"].cpu().numpy() == 1)
         assert torch.equal(out["support"], idx)
-        assert torch.equal(out["o"], o) and torch.equal(out["lse"], lse)
+        assert torch.max(torch.abs(out["o"] - o)).item() < 1e-5
+        assert torch.max(torch.abs(out["lse"] - lse)).item() < 1e-5
 
 
 @pytest.mark.parametrize("B,tau,K,L", [(3, 0.90, 128, 8192), (1, 0.85, 1024, 16384), (5, 0.85, 1100, 8192)])

@@ -151,6 +151,36 @@ def test_exact_ties_lowest_row_wins(ops):
     log(f"tie heads checked exactly: {n_exact}")
 
 
+@pytest.mark.parametrize("L", [8192, 8193])
+def test_short_segment_boundary(ops, L):
+    """Segments of up to 8192 positions are selected by one workgroup per
+    head (all scores in LDS), longer ones by the filter-select: both sides of
+    the boundary, every head checked."""
+    w = make_workload(2, L=L)
+    K = 100
+    log(f"case short-segment boundary L={L}")
+    idx, o, lse = run(ops, w, [(0, L)], K)
+    heads = [(0, h) for h in range(w.H_q)]
+    check_heads(w, heads, idx, o, lse, [(0, L)], K, label=f"boundary L={L}")
+
+
+def test_short_segment_codebook_ties(ops):
+    """A short segment whose scores take 6 values: the K-th score's bin holds
+    about a thousand scores, too many for the one-pass histogram cut, so the
+    radix cut decides; the set must equal the oracle's (lowest rows first)."""
+    from workloads import make_multi_query
+    w = make_multi_query(1, 4, 2, 1, 6000, "bf16", codebook=6, tag=44)
+    w.q = np.ascontiguousarray(w.q[:, :, 0])
+    ranges = [(0, 2500), (3000, 6000)]
+    for K in (1, 300, 5499):
+        log(f"case short codebook ties K={K}")
+        idx, o, lse = run(ops, w, ranges, K)
+        want = ref.topk_attn_decode(w.q, w.k, w.v, ranges, K, w.scale)
+        assert np.array_equal(idx, want["idx"])
+        for h in range(w.H_q):
+            check_out(o[0, h], lse[0, h], want["o"][0, h], want["lse"][0, h], False, f"short codebook K={K} head {h}")
+
+
 @pytest.mark.parametrize("K", [300, 9000])
 def test_codebook_ties_many_candidates(ops, K):
     """Keys from a 6-row codebook over 24,000 rows: every score ties with
@@ -294,7 +324,7 @@ def test_workspace_shared_with_multi_query(ops):
 @pytest.mark.parametrize("entry", ["topk", "static", "retopk"])
 def test_failed_call_leaves_workspace_usable(ops, entry):
     """A launch failure forced from the host right after the scan (the
-    filter-select is never enqueued) leaves the workspace's counters non-zero; the
+    select is never enqueued) leaves the workspace's counters non-zero; the
     call returns STDK_EHIP, and the next call on the same buffer repairs them
     first: its results equal those of a fresh buffer."""
     from sparse_top_decode_amd.native import STDK_EHIP, StdkError
