@@ -75,22 +75,46 @@ STDK_DEV float group_sum(float x) {
   return x;
 }
 
+// Value of lane l (the same l in every lane: a constant or a value derived
+// from a ballot) in every lane, through a scalar register.
+STDK_DEV uint32_t lane_read(uint32_t x, int l) { return (uint32_t)__builtin_amdgcn_readlane((int)x, l); }
+STDK_DEV float lane_read(float x, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l)); }
+
+// Wave reductions (every lane of the wave active): DPP rotations reduce each
+// 16-lane row (all lanes of a row end with the same bits), then the four
+// rows' values are read through scalar registers and combined in row order,
+// so every lane receives the same bits.
+template <typename F>
+STDK_DEV float wave_reduce(float x, F op) {
+  x = op(x, row_ror<8>(x));
+  x = op(x, row_ror<4>(x));
+  x = op(x, row_ror<2>(x));
+  x = op(x, row_ror<1>(x));
+  return op(op(lane_read(x, 0), lane_read(x, 16)), op(lane_read(x, 32), lane_read(x, 48)));
+}
+template <typename F>
+STDK_DEV uint32_t wave_reduce_u32(uint32_t x, F op) {
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xF, 0xF, false));  // row_ror:8
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x124, 0xF, 0xF, false));  // row_ror:4
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x122, 0xF, 0xF, false));  // row_ror:2
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x121, 0xF, 0xF, false));  // row_ror:1
+  return op(op(lane_read(x, 0), lane_read(x, 16)), op(lane_read(x, 32), lane_read(x, 48)));
+}
+
 STDK_DEV float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-  return x;
+  return wave_reduce(x, [](float a, float b) { return fmaxf(a, b); });
 }
-
 STDK_DEV float wave_min(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fminf(x, __shfl_xor(x, o, 64));
-  return x;
+  return wave_reduce(x, [](float a, float b) { return fminf(a, b); });
 }
-
 STDK_DEV float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-  return x;
+  return wave_reduce(x, [](float a, float b) { return a + b; });
+}
+STDK_DEV uint32_t wave_max_u32(uint32_t x) {
+  return wave_reduce_u32(x, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+STDK_DEV uint32_t wave_min_u32(uint32_t x) {
+  return wave_reduce_u32(x, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
 }
 
 // Number of set bits of `mask` below this lane.
@@ -232,7 +256,7 @@ STDK_DEV void find_bin_wave(const uint32_t* hist, uint32_t need, int* bin, uint3
     return;
   }
   const int L = __ffsll((unsigned long long)own) - 1;
-  const uint32_t before_L = __shfl(before, L, 64);
+  const uint32_t before_L = lane_read(before, L);
   const uint32_t x = lane < PER ? hist[bin_of(L * PER + lane)] : 0u;
   const uint32_t cum = before_L + wave_incl_scan(x);
   const uint64_t hit = __ballot(lane < PER && cum >= need);

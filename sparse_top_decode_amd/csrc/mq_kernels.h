@@ -468,7 +468,7 @@ __global__ __launch_bounds__(64 * kMqSelWaves) void mq_select(MqSelArgs a) {
       const int j = j0 + u * 64 + lane;
       const uint32_t incl = wave_incl_scan(cv[u]);
       if (j < ns) pre[j] = run + incl - cv[u];
-      run += __shfl(incl, 63, 64);
+      run += lane_read(incl, 63);
     }
   }
   const uint32_t m = run;
@@ -548,8 +548,7 @@ __global__ __launch_bounds__(64 * kMqSelWaves) void mq_select(MqSelArgs a) {
         src[v] = (int64_t)j * a.chunk;
         most = max(most, cnt[v]);
       }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) most = max(most, (uint32_t)__shfl_xor((int)most, o, 64));
+      most = wave_max_u32(most);
       for (uint32_t e0 = 0; e0 < most; e0 += kE) {
         Cand cv[kS][kE];
 #pragma unroll

@@ -72,7 +72,7 @@ STDK_DEV uint32_t first_digit_search(const u32x4 (&hv)[8], uint32_t need, uint32
     return 0u;
   }
   const int L = __ffsll((unsigned long long)own) - 1;
-  const uint32_t before_L = __shfl(before, L, 64);
+  const uint32_t before_L = lane_read(before, L);
   // lane k < 32 takes rank k of lane L: bin word 31 - k of L's block
   uint32_t x = 0;
 #pragma unroll
@@ -80,14 +80,14 @@ STDK_DEV uint32_t first_digit_search(const u32x4 (&hv)[8], uint32_t need, uint32
     const uint32_t w4[4] = {hv[i].x, hv[i].y, hv[i].z, hv[i].w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const uint32_t t = __shfl(w4[e], L, 64);
+      const uint32_t t = lane_read(w4[e], L);
       if (lane == 31 - (4 * i + e)) x = t;
     }
   }
   const uint32_t cum = before_L + wave_incl_scan(lane < 32 ? x : 0u);
   const uint64_t hit = __ballot(lane < 32 && cum >= need);
   const int k = __ffsll((unsigned long long)hit) - 1;
-  if (beyond) *beyond = __shfl(cum - x, k, 64);
+  if (beyond) *beyond = lane_read(cum - x, k);
   return (uint32_t)(kHistBins - 1 - (32 * L + k));
 }
 
@@ -287,8 +287,8 @@ STDK_DEV uint32_t select_tail(const SelectArgs& a, int64_t seg, int P, int64_t s
         ce += valid && !take_all && kv[u] == Tk;
       }
     }
-    cg = __shfl(wave_incl_scan(cg), 63, 64);
-    ce = __shfl(wave_incl_scan(ce), 63, 64);
+    cg = lane_read(wave_incl_scan(cg), 63);
+    ce = lane_read(wave_incl_scan(ce), 63);
     if (lane == 0) {
       tmp[wv] = cg;
       tmp[kSelectWaves + wv] = ce;
@@ -578,7 +578,7 @@ STDK_DEV void fsel_body(const SelectArgs& a) {
       const uint32_t c = j < P ? load_agent(a.wg_cnt + seg * P + j) : 0u;
       const uint32_t incl = wave_incl_scan(c);
       if (j < P) pre[j] = run + incl - c;
-      run += __shfl(incl, 63, 64);
+      run += lane_read(incl, 63);
     }
     if (lane == 0) pre[P] = run;
   }
@@ -683,11 +683,8 @@ STDK_DEV TopkCut lds_cut_radix(const float* zs, uint32_t M, int K, uint32_t* h, 
     kmin = min(kmin, kv);
     kmax = max(kmax, kv);
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
-  }
+  kmin = wave_min_u32(kmin);
+  kmax = wave_max_u32(kmax);
   if (lane == 0) {
     wc[0][w] = kmin;
     wc[1][w] = kmax;
@@ -791,8 +788,8 @@ STDK_DEV uint32_t lds_emit(const float* zs, const int32_t* rs, uint32_t M, int K
     cg += take_all || kv > Tk;
     ce += !take_all && kv == Tk;
   }
-  cg = __shfl(wave_incl_scan(cg), 63, 64);
-  ce = __shfl(wave_incl_scan(ce), 63, 64);
+  cg = lane_read(wave_incl_scan(cg), 63);
+  ce = lane_read(wave_incl_scan(ce), 63);
   if (lane == 0) {
     wc[0][w] = cg;
     wc[1][w] = ce;
