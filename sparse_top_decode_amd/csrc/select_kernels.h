@@ -462,16 +462,20 @@ STDK_DEV void fsel_body(const SelectArgs& a) {
   // segment's global histogram, after the candidate stores so that those are
   // not queued behind them. A batch's loads are issued after the previous
   // batch's stores: every workgroup of the grid streams at once, which keeps
-  // the memory system busy without deeper pipelining inside one.
+  // the memory system busy without deeper pipelining inside one (measured:
+  // requesting the next batch first changed nothing).
   {
     const float* sc = a.scores + seg * a.n_pad;
     Cand* out = a.list + seg * a.n_pad + (int64_t)blockIdx.x * span;
-    float v[kFselLoads];
+    // 16-byte loads: chunk u of a wave's slice is positions [256u, 256u +
+    // 256), lane l holding 4l .. 4l + 3 (rows start on 64-float boundaries;
+    // addresses past the slice stay inside the segment's row and are not used)
+    constexpr int NV = kFselLoads / 4;
+    float4 v[NV];
     auto load_batch = [&](int bt) {
       const int64_t p0 = (int64_t)blockIdx.x * span + ((int64_t)bt * kSelectWaves + wv) * a.slice;
-      const int64_t plast = max((int64_t)0, min(n, p0 + a.slice) - 1);  // clamped into the scores
 #pragma unroll
-      for (int u = 0; u < kFselLoads; ++u) v[u] = sc[min(p0 + 64 * u + lane, plast)];
+      for (int u = 0; u < NV; ++u) v[u] = *reinterpret_cast<const float4*>(sc + min(p0 + 256 * u + 4 * lane, a.n_pad - 4));
     };
     u32x4 hv[8];
     if (wv == 0 && !take_all) first_digit_load(hg, hv);
@@ -492,18 +496,28 @@ STDK_DEV void fsel_body(const SelectArgs& a) {
     for (int bt = 0;;) {
       const int64_t p0 = (int64_t)blockIdx.x * span + ((int64_t)bt * kSelectWaves + wv) * a.slice;
       const int64_t p1 = min(n, p0 + a.slice);
-      uint32_t key[kFselLoads];
-      uint64_t tm[kFselLoads];
+      // per chunk: each lane's taken positions as 4 bits, their count
+      // scanned over the wave (the order is lane, then element)
+      uint32_t key[NV][4], bits[NV], ex[NV], ct[NV];
       uint32_t cnt = 0;
 #pragma unroll
-      for (int u = 0; u < kFselLoads; ++u) {
-        const int64_t p = p0 + 64 * u + lane;
-        key[u] = f2key(v[u]);
-        const uint32_t d0 = key[u] >> (32 - kHistBits);
-        const bool take = p < p1 && (take_all || d0 >= b0);
-        tm[u] = __ballot(take);
-        cnt += (uint32_t)__popcll(tm[u]);
-        if (take && !take_all && d0 == b0) atomicAdd(&h1[(key[u] >> 10) & 0x7FFu], 1u);
+      for (int u = 0; u < NV; ++u) {
+        const float f[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+        bits[u] = 0u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t p = p0 + 256 * u + 4 * lane + e;
+          key[u][e] = f2key(f[e]);
+          const uint32_t d0 = key[u][e] >> (32 - kHistBits);
+          const bool take = p < p1 && (take_all || d0 >= b0);
+          bits[u] |= (take ? 1u : 0u) << e;
+          if (take && !take_all && d0 == b0) atomicAdd(&h1[(key[u][e] >> 10) & 0x7FFu], 1u);
+        }
+        const uint32_t c = (uint32_t)__popc(bits[u]);
+        const uint32_t incl = wave_incl_scan(c);
+        ex[u] = incl - c;
+        ct[u] = lane_read(incl, 63);
+        cnt += ct[u];
       }
       // the counts alternate between two arrays, so one barrier per batch
       // suffices: a batch's array is rewritten two batches later, after
@@ -518,9 +532,14 @@ STDK_DEV void fsel_body(const SelectArgs& a) {
         tot += c;
       }
 #pragma unroll
-      for (int u = 0; u < kFselLoads; ++u) {
-        if ((tm[u] >> lane) & 1ull) store_agent(out + off + lane_rank(tm[u]), Cand{key[u], (int32_t)(p0 + 64 * u + lane)});
-        off += (uint32_t)__popcll(tm[u]);
+      for (int u = 0; u < NV; ++u) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if ((bits[u] >> e) & 1u)
+            store_agent(out + off + ex[u] + (uint32_t)__popc(bits[u] & ((1u << e) - 1u)),
+                        Cand{key[u][e], (int32_t)(p0 + 256 * u + 4 * lane + e)});
+        }
+        off += ct[u];
       }
       written += tot;
       if (++bt == a.nb) break;
