@@ -58,8 +58,9 @@ STDK_DEV void first_digit_load(const uint32_t* hist, u32x4 (&hv)[8]) {
 }
 
 // Returns the bin (0 if the histogram holds fewer than `need` items) and, in
-// *beyond, the count in the bins above it.
-STDK_DEV uint32_t first_digit_search(const u32x4 (&hv)[8], uint32_t need, uint32_t* beyond = nullptr) {
+// *beyond, the count in the bins above it and in *bin_count the bin's own.
+STDK_DEV uint32_t first_digit_search(const u32x4 (&hv)[8], uint32_t need, uint32_t* beyond = nullptr,
+                                     uint32_t* bin_count = nullptr) {
   const int lane = threadIdx.x & 63;
   uint32_t local = 0;
 #pragma unroll
@@ -69,6 +70,7 @@ STDK_DEV uint32_t first_digit_search(const u32x4 (&hv)[8], uint32_t need, uint32
   const uint64_t own = __ballot(before < need && need <= incl);
   if (own == 0) {
     if (beyond) *beyond = 0u;
+    if (bin_count) *bin_count = 0u;
     return 0u;
   }
   const int L = __ffsll((unsigned long long)own) - 1;
@@ -88,6 +90,7 @@ STDK_DEV uint32_t first_digit_search(const u32x4 (&hv)[8], uint32_t need, uint32
   const uint64_t hit = __ballot(lane < 32 && cum >= need);
   const int k = __ffsll((unsigned long long)hit) - 1;
   if (beyond) *beyond = lane_read(cum - x, k);
+  if (bin_count) *bin_count = lane_read(x, k);
   return (uint32_t)(kHistBins - 1 - (32 * L + k));
 }
 
@@ -163,19 +166,27 @@ STDK_DEV Cand load_agent(const Cand* p) {
 // fused softmax . V. Returns the number of rows taken before the cap at K.
 template <bool kLds, bool kSv>
 STDK_DEV uint32_t select_tail(const SelectArgs& a, int64_t seg, int P, int64_t span, uint32_t m, uint32_t pre22,
-                              uint32_t need, bool take_all, const uint32_t* pre, Cand* cl, uint32_t* h2,
+                              uint32_t need, bool take_all, const uint32_t* pre, Cand* cl, uint32_t cap, uint32_t* h2,
                               uint32_t* tmp, int* s_bin, uint32_t* s_beyond, int32_t* crow, float* czs) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int K = a.K;
   const Cand* lst = a.list + seg * a.n_pad;
 
   // Copy in position order: candidate i lives in the region of the last
-  // workgroup r with pre[r] <= i. All loads of a round are issued before the
-  // first is used.
+  // workgroup r with pre[r] <= i. Candidates whose first two digits lie
+  // below the K-th key's (key >> 10 < pre22) cannot be chosen and are
+  // dropped. The kept ones keep their order: each wave publishes its ballot
+  // count per load slot, wave 0 turns the round's 4 x 16 counts (slot-major,
+  // as the positions run) into offsets with one scan, and each lane adds its
+  // rank in the ballot. At most `cap` are kept. The third digit is counted
+  // for the candidates in the K-th key's second-digit bin. The next round is
+  // requested before a round is placed.
   {
     constexpr int CU = 4;
-    for (uint32_t base = 0; base < m; base += kSelThreads * CU) {
-      Cand c[CU];
+    constexpr uint32_t RND = kSelThreads * CU;  // candidates per round
+    __shared__ uint32_t s_cc[CU * kSelectWaves], s_off[CU * kSelectWaves], s_tot;
+    uint32_t mk = 0;
+    auto load_round = [&](uint32_t base, Cand (&c)[CU]) {
 #pragma unroll
       for (int u = 0; u < CU; ++u) {
         const uint32_t i = min(base + (uint32_t)(u * kSelThreads + tid), m - 1u);
@@ -187,15 +198,47 @@ STDK_DEV uint32_t select_tail(const SelectArgs& a, int64_t seg, int P, int64_t s
         }
         c[u] = load_agent(lst + (int64_t)lo * span + (i - pre[lo]));
       }
+    };
+    auto place_round = [&](uint32_t base, const Cand (&c)[CU]) {
+      uint64_t km[CU];
 #pragma unroll
       for (int u = 0; u < CU; ++u) {
         const uint32_t i = base + (uint32_t)(u * kSelThreads + tid);
-        if (i < m) {
-          cl[i] = c[u];
-          if (!take_all && (c[u].key >> 10) == pre22) atomicAdd(&h2[c[u].key & 0x3FFu], 1u);
+        km[u] = __ballot(i < m && (take_all || (c[u].key >> 10) >= pre22));
+        if (lane == 0) s_cc[u * kSelectWaves + wv] = (uint32_t)__popcll(km[u]);
+      }
+      __syncthreads();
+      if (wv == 0) {
+        const uint32_t x = s_cc[lane];
+        const uint32_t incl = wave_incl_scan(x);
+        s_off[lane] = mk + incl - x;
+        if (lane == 63) s_tot = incl;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < CU; ++u) {
+        if ((km[u] >> lane) & 1ull) {
+          const uint32_t j = s_off[u * kSelectWaves + wv] + lane_rank(km[u]);
+          if (j < cap) {
+            cl[j] = c[u];
+            if (!take_all && (c[u].key >> 10) == pre22) atomicAdd(&h2[c[u].key & 0x3FFu], 1u);
+          }
         }
       }
+      mk += s_tot;
+    };
+    Cand ca[CU], cb[CU];
+    if (m > 0) load_round(0, ca);
+    for (uint32_t base = 0; base < m;) {
+      if (base + RND < m) load_round(base + RND, cb);
+      place_round(base, ca);
+      base += RND;
+      if (base >= m) break;
+      if (base + RND < m) load_round(base + RND, ca);
+      place_round(base, cb);
+      base += RND;
     }
+    m = min(mk, cap);
   }
   __syncthreads();
   uint32_t Tk = 0;
@@ -440,7 +483,7 @@ STDK_DEV void fsel_body(const SelectArgs& a) {
   __shared__ uint32_t tmp[2 * kSelectWaves + 2];
   __shared__ uint32_t s_wc[2][kSelectWaves];
   __shared__ int s_bin;
-  __shared__ uint32_t s_beyond, s_b1, s_beyond1, s_last;
+  __shared__ uint32_t s_beyond, s_b1, s_beyond1, s_cnt1, s_last;
   const int64_t seg = blockIdx.y;
   if (a.seg_active && a.seg_active[seg] == 0) return;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -577,11 +620,12 @@ STDK_DEV void fsel_body(const SelectArgs& a) {
         hv[i].z = load_agent(base + 4 * i + 2);
         hv[i].w = load_agent(base + 4 * i + 3);
       }
-      uint32_t beyond1 = 0;
-      const uint32_t b1 = first_digit_search(hv, (uint32_t)K - s_beyond, &beyond1);
+      uint32_t beyond1 = 0, cnt1 = 0;
+      const uint32_t b1 = first_digit_search(hv, (uint32_t)K - s_beyond, &beyond1, &cnt1);
       if (lane == 0) {
         s_b1 = b1;
         s_beyond1 = beyond1;
+        s_cnt1 = cnt1;
       }
     }
     const u32x4 z = {0u, 0u, 0u, 0u};
@@ -629,14 +673,18 @@ STDK_DEV void fsel_body(const SelectArgs& a) {
       }
     }
   }
+  // the candidates the copy keeps: those above the K-th key's first-digit
+  // bin, and in it those at or above its second-digit bin (both histograms
+  // count exactly the candidates); LDS holds them when they fit
+  const uint32_t kept = take_all ? m : min(m, s_beyond + s_beyond1 + s_cnt1);
   uint32_t tot;
-  if (m <= (uint32_t)a.cache_cap) {
+  if (kept <= (uint32_t)a.cache_cap) {
     Cand* cl = reinterpret_cast<Cand*>(dyn + pre_words);
-    tot = select_tail<true, kSv>(a, seg, P, span, m, pre22, need, take_all, pre, cl, h2, tmp, &s_bin, &s_beyond,
-                                 crow, czs);
+    tot = select_tail<true, kSv>(a, seg, P, span, m, pre22, need, take_all, pre, cl, (uint32_t)a.cache_cap, h2, tmp,
+                                 &s_bin, &s_beyond, crow, czs);
   } else {
-    tot = select_tail<false, kSv>(a, seg, P, span, m, pre22, need, take_all, pre, a.clist + seg * a.n_pad, h2, tmp,
-                                  &s_bin, &s_beyond, crow, czs);
+    tot = select_tail<false, kSv>(a, seg, P, span, m, pre22, need, take_all, pre, a.clist + seg * a.n_pad, m, h2,
+                                  tmp, &s_bin, &s_beyond, crow, czs);
   }
   if (kSv) {
     const uint32_t nk = min(tot, (uint32_t)K);
