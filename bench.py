@@ -309,7 +309,7 @@ def cpu_baseline_mq(w, K: int, budget_s: float = 10.0):
 # ---------------------------------------------------------------------------
 # timing
 # ---------------------------------------------------------------------------
-def timed_passes(step, steps, names, reset=None, graph=None):
+def timed_passes(step, steps, names, reset=None, graph=None, graph_steps=1):
     """Pass A: `steps` steps bracketed by stream events only (a timing event
     attached to a dispatch costs several microseconds of step time). Pass B:
     the same number of steps again with HIP start/stop events attached by the
@@ -317,21 +317,25 @@ def timed_passes(step, steps, names, reset=None, graph=None):
     average duration, and because every dispatch carries them each start
     stamp follows the previous kernel's end, so they agree with a rocprofv3
     kernel trace. `reset` (if given) restores the starting state before each
-    pass. Returns (ms per step, {kernel: (avg_us, launches)})."""
+    pass. A `graph` holds `graph_steps` consecutive steps; pass A replays it
+    until at least `steps` steps have run. Returns (ms per step, {kernel:
+    (avg_us, launches)})."""
     import torch
     from sparse_top_decode_amd import ops
     run = graph.replay if graph is not None else step
+    per_run = graph_steps if graph is not None else 1
+    runs = -(-steps // per_run)
     if reset:
         reset()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     ev0.record()
-    for _ in range(steps):
+    for _ in range(runs):
         run()
     ev1.record()
     torch.cuda.synchronize()
-    total_ms = ev0.elapsed_time(ev1)
+    total_ms = ev0.elapsed_time(ev1) * steps / (runs * per_run)
     kern = {}
     if names:
         if reset:
@@ -351,8 +355,10 @@ def timed_passes(step, steps, names, reset=None, graph=None):
     return total_ms / steps, kern
 
 
-def capture(step):
-    """The step captured once in a HIP graph (None if capture fails)."""
+def capture(step, n=1):
+    """n consecutive steps captured once in a HIP graph (None if capture
+    fails). With rotating layer caches n is their number, so that each
+    replay scans every cache once, as the direct launches do."""
     import torch
     try:
         side = torch.cuda.Stream()
@@ -362,7 +368,8 @@ def capture(step):
         torch.cuda.current_stream().wait_stream(side)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            step()
+            for _ in range(n):
+                step()
         torch.cuda.synchronize()
         for _ in range(3):
             g.replay()
@@ -521,11 +528,11 @@ def bench_topk(args, cfg):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    graph = capture(step) if args.graph == "on" else None
+    graph = capture(step, n_layers) if args.graph == "on" else None
     names = TOPK_KERNELS if args.kernel_events == "on" else ()
     if q8 is not None:
         names = names + ("retopk_rerank", "retopk_rerank_select") if names else ()
-    ms, kern = timed_passes(step, args.steps, names, graph=graph)
+    ms, kern = timed_passes(step, args.steps, names, graph=graph, graph_steps=n_layers)
     row_bytes = 128 * (4 if w.kv_dtype == "f32" else 2)
     if q8 is None:
         scan_bytes = B * w.H_kv * n_dyn * row_bytes  # every dynamic key row once, d=128
