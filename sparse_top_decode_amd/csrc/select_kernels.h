@@ -475,244 +475,6 @@ STDK_DEV void tail_softmax_v(const SelectArgs& a, int64_t seg, const int32_t* cr
   }
 }
 
-template <typename T, bool kSv>
-STDK_DEV void fsel_body(const SelectArgs& a) {
-  extern __shared__ uint32_t dyn[];
-  __shared__ uint32_t h1[kHistBins];  // second digit, this workgroup's candidates in bin b*
-  __shared__ uint32_t h2[1024];       // third digit
-  __shared__ uint32_t tmp[2 * kSelectWaves + 2];
-  __shared__ uint32_t s_wc[2][kSelectWaves];
-  __shared__ int s_bin;
-  __shared__ uint32_t s_beyond, s_b1, s_beyond1, s_cnt1, s_last;
-  const int64_t seg = blockIdx.y;
-  if (a.seg_active && a.seg_active[seg] == 0) return;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int P = (int)gridDim.x;
-  const int K = a.K;
-  const int64_t n = a.n_dev ? min(a.n, max((int64_t)0, *a.n_dev)) : a.n;
-  const bool take_all = n <= K;
-  uint32_t* hg = a.hist + seg * kHistBins;
-  uint32_t* h1g = a.hist1 + seg * kHistBins;
-  const int64_t span = (int64_t)a.nb * kSelectWaves * a.slice;
-
-  // 1. Filter, in nb batches of 16 wave slices. Wave 0 requests the
-  // histogram first, then every wave the scores of its first slice; wave 0
-  // finds b* (the first digit's bin of the K-th largest key) while they
-  // arrive. The candidates (first digit >= b*) go to this workgroup's region
-  // in position order: the waves' counts give each wave its offset, ballots
-  // rank the lanes. The candidates in bin b* are counted by their second
-  // digit (bits 20..10) in LDS; the non-zero bins are then added to the
-  // segment's global histogram, after the candidate stores so that those are
-  // not queued behind them. A batch's loads are issued after the previous
-  // batch's stores: every workgroup of the grid streams at once, which keeps
-  // the memory system busy without deeper pipelining inside one (measured:
-  // requesting the next batch first changed nothing).
-  {
-    const float* sc = a.scores + seg * a.n_pad;
-    Cand* out = a.list + seg * a.n_pad + (int64_t)blockIdx.x * span;
-    // 16-byte loads: chunk u of a wave's slice is positions [256u, 256u +
-    // 256), lane l holding 4l .. 4l + 3 (rows start on 64-float boundaries;
-    // addresses past the slice stay inside the segment's row and are not used)
-    constexpr int NV = kFselLoads / 4;
-    float4 v[NV];
-    auto load_batch = [&](int bt) {
-      const int64_t p0 = (int64_t)blockIdx.x * span + ((int64_t)bt * kSelectWaves + wv) * a.slice;
-#pragma unroll
-      for (int u = 0; u < NV; ++u) v[u] = *reinterpret_cast<const float4*>(sc + min(p0 + 256 * u + 4 * lane, a.n_pad - 4));
-    };
-    u32x4 hv[8];
-    if (wv == 0 && !take_all) first_digit_load(hg, hv);
-    load_batch(0);
-#pragma unroll
-    for (int u = 0; u < kHistBins / kSelThreads; ++u) h1[u * kSelThreads + tid] = 0u;
-    if (wv == 0) {
-      uint32_t beyond = 0;
-      const uint32_t bin = take_all ? 0u : first_digit_search(hv, (uint32_t)K, &beyond);
-      if (lane == 0) {
-        s_bin = (int)bin;
-        s_beyond = beyond;
-      }
-    }
-    __syncthreads();
-    const uint32_t b0 = (uint32_t)s_bin;
-    uint32_t written = 0;
-    for (int bt = 0;;) {
-      const int64_t p0 = (int64_t)blockIdx.x * span + ((int64_t)bt * kSelectWaves + wv) * a.slice;
-      const int64_t p1 = min(n, p0 + a.slice);
-      // per chunk: each lane's taken positions as 4 bits, their count
-      // scanned over the wave (the order is lane, then element)
-      uint32_t key[NV][4], bits[NV], ex[NV], ct[NV];
-      uint32_t cnt = 0;
-#pragma unroll
-      for (int u = 0; u < NV; ++u) {
-        const float f[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-        bits[u] = 0u;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int64_t p = p0 + 256 * u + 4 * lane + e;
-          key[u][e] = f2key(f[e]);
-          const uint32_t d0 = key[u][e] >> (32 - kHistBits);
-          const bool take = p < p1 && (take_all || d0 >= b0);
-          bits[u] |= (take ? 1u : 0u) << e;
-          if (take && !take_all && d0 == b0) atomicAdd(&h1[(key[u][e] >> 10) & 0x7FFu], 1u);
-        }
-        const uint32_t c = (uint32_t)__popc(bits[u]);
-        const uint32_t incl = wave_incl_scan(c);
-        ex[u] = incl - c;
-        ct[u] = lane_read(incl, 63);
-        cnt += ct[u];
-      }
-      // the counts alternate between two arrays, so one barrier per batch
-      // suffices: a batch's array is rewritten two batches later, after
-      // every wave has passed the barrier between
-      if (lane == 0) s_wc[bt & 1][wv] = cnt;
-      __syncthreads();
-      uint32_t off = written, tot = 0;
-#pragma unroll
-      for (int w = 0; w < kSelectWaves; ++w) {
-        const uint32_t c = s_wc[bt & 1][w];
-        off += w < wv ? c : 0u;
-        tot += c;
-      }
-#pragma unroll
-      for (int u = 0; u < NV; ++u) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if ((bits[u] >> e) & 1u)
-            store_agent(out + off + ex[u] + (uint32_t)__popc(bits[u] & ((1u << e) - 1u)),
-                        Cand{key[u][e], (int32_t)(p0 + 256 * u + 4 * lane + e)});
-        }
-        off += ct[u];
-      }
-      written += tot;
-      if (++bt == a.nb) break;
-      load_batch(bt);
-    }
-    if (tid == 0) store_agent(a.wg_cnt + seg * P + blockIdx.x, written);
-    if (!take_all) {
-#pragma unroll
-      for (int u = 0; u < kHistBins / kSelThreads; ++u) {
-        const uint32_t c = h1[u * kSelThreads + tid];
-        if (c != 0u) atomicAdd(&h1g[u * kSelThreads + tid], c);
-      }
-    }
-  }
-
-  // 2. Arrival: once every wave's writes and histogram adds are complete,
-  // thread 0 counts the workgroup in. The workgroup that takes the count to
-  // P finishes the segment (and resets the counter); the others are done.
-  if (!arrive_last(a.done + seg * kCtlWords, (uint32_t)P, &s_last)) return;
-
-  // 3. Select. Wave 0 finds the second digit's bin from the global
-  // histogram, then zeroes both histograms for the next call (every
-  // workgroup of the segment read the first before it arrived, and its adds
-  // to the second are complete); wave 1 builds the workgroups' candidate
-  // offsets; every thread clears the third digit's histogram.
-  uint32_t* pre = dyn;
-  if (wv == 0) {
-    if (!take_all) {
-      const uint32_t* base = h1g + (kHistBins - 32 - 32 * lane);
-      u32x4 hv[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        hv[i].x = load_agent(base + 4 * i);
-        hv[i].y = load_agent(base + 4 * i + 1);
-        hv[i].z = load_agent(base + 4 * i + 2);
-        hv[i].w = load_agent(base + 4 * i + 3);
-      }
-      uint32_t beyond1 = 0, cnt1 = 0;
-      const uint32_t b1 = first_digit_search(hv, (uint32_t)K - s_beyond, &beyond1, &cnt1);
-      if (lane == 0) {
-        s_b1 = b1;
-        s_beyond1 = beyond1;
-        s_cnt1 = cnt1;
-      }
-    }
-    const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      *reinterpret_cast<u32x4*>(hg + (kHistBins - 32 - 32 * lane) + 4 * i) = z;
-      *reinterpret_cast<u32x4*>(h1g + (kHistBins - 32 - 32 * lane) + 4 * i) = z;
-    }
-  } else if (wv == 1) {
-    uint32_t run = 0;
-    for (int j0 = 0; j0 < P; j0 += 64) {
-      const int j = j0 + lane;
-      const uint32_t c = j < P ? load_agent(a.wg_cnt + seg * P + j) : 0u;
-      const uint32_t incl = wave_incl_scan(c);
-      if (j < P) pre[j] = run + incl - c;
-      run += lane_read(incl, 63);
-    }
-    if (lane == 0) pre[P] = run;
-  }
-  h2[tid] = 0u;
-  __syncthreads();
-  const uint32_t m = pre[P];
-  const uint32_t b0 = take_all ? 0u : (uint32_t)s_bin;
-  const uint32_t b1 = take_all ? 0u : s_b1;
-  const uint32_t need = take_all ? (uint32_t)K : (uint32_t)K - s_beyond - s_beyond1;
-  const uint32_t pre22 = (b0 << 11) | b1;
-  // fused softmax . V: the static slots' scores and rows are requested now
-  // (clamped loads, kept in registers until the chosen rows are known);
-  // chosen and static slots go after the candidate copy, and the softmax's
-  // group sums overwrite the copy once it is read
-  const int pre_words = (P + 2) & ~1;
-  int32_t* crow = nullptr;
-  float* czs = nullptr;
-  float zst[kFuseStatic];
-  int32_t rst[kFuseStatic];
-  if (kSv) {
-    crow = reinterpret_cast<int32_t*>(dyn + pre_words + 2 * a.cache_cap);
-    czs = reinterpret_cast<float*>(crow + (K + a.n_extra));
-    if (a.n_extra > 0) {
-#pragma unroll
-      for (int u = 0; u < kFuseStatic; ++u) {
-        const int64_t p = a.n + min(tid + kSelThreads * u, a.n_extra - 1);
-        zst[u] = a.scores[seg * a.n_pad + p];
-        rst[u] = (int32_t)pos_to_row(a.tab, p);
-      }
-    }
-  }
-  // the candidates the copy keeps: those above the K-th key's first-digit
-  // bin, and in it those at or above its second-digit bin (both histograms
-  // count exactly the candidates); LDS holds them when they fit
-  const uint32_t kept = take_all ? m : min(m, s_beyond + s_beyond1 + s_cnt1);
-  uint32_t tot;
-  if (kept <= (uint32_t)a.cache_cap) {
-    Cand* cl = reinterpret_cast<Cand*>(dyn + pre_words);
-    tot = select_tail<true, kSv>(a, seg, P, span, m, pre22, need, take_all, pre, cl, (uint32_t)a.cache_cap, h2, tmp,
-                                 &s_bin, &s_beyond, crow, czs);
-  } else {
-    tot = select_tail<false, kSv>(a, seg, P, span, m, pre22, need, take_all, pre, a.clist + seg * a.n_pad, m, h2,
-                                  tmp, &s_bin, &s_beyond, crow, czs);
-  }
-  if (kSv) {
-    const uint32_t nk = min(tot, (uint32_t)K);
-#pragma unroll
-    for (int u = 0; u < kFuseStatic; ++u) {
-      const int j = tid + kSelThreads * u;
-      if (j < a.n_extra) {
-        crow[nk + j] = rst[u];
-        czs[nk + j] = zst[u];
-      }
-    }
-    tail_softmax_v<T>(a, seg, crow, czs, nk + (uint32_t)a.n_extra,
-                      reinterpret_cast<float(*)[kHeadDim]>(dyn + pre_words), reinterpret_cast<float*>(tmp));
-  }
-}
-
-__global__ __launch_bounds__(kSelThreads) void topk_filter_select(SelectArgs a) { fsel_body<uint16_t, false>(a); }
-
-// topk_filter_select whose last workgroup per segment also forms softmax . V
-// over the chosen rows and the static slots (tail_softmax_v): one launch
-// instead of three (sparse_sv + combine after the select). Dynamic LDS: as
-// topk_filter_select with room for the copy of at least the group sums
-// (NG x 128 floats), then K + n_extra rows and as many scores.
-template <typename T>
-__global__ __launch_bounds__(kSelThreads) void topk_filter_select_sv(SelectArgs a) {
-  fsel_body<T, true>(a);
-}
-
 // The exact top-K of the M candidate scores zs (rows rs) staged in LDS,
 // ties to the lower candidate index (the candidates ascend by row), in two
 // steps: the cut (lds_cut_radix or lds_cut_linear), then an ordered
@@ -900,6 +662,354 @@ STDK_DEV uint32_t lds_topk(const float* zs, const int32_t* rs, uint32_t M, int K
   const TopkCut cut = lds_cut_radix<NT>(zs, M, K, h, wc, s_bin_p, s_beyond_p);
   return lds_emit<NT>(zs, rs, M, K, cut, wc, emit);
 }
+
+// The last workgroup's select when the head's candidates fit its LDS: all
+// m of them (key and position, in position order) are copied there, the
+// exact top K taken by the one-pass linear-bin cut over their range
+// (lds_cut_linear; the radix passes when a score is not finite or the K-th
+// score's bin holds more than kCutList), and the chosen rows emitted in
+// order (lds_emit: the key order and lowest-position ties of select_tail).
+// Needs no second-digit histogram. `h` (kHistBins words) is zero on entry;
+// `scr` holds at least 128 words.
+template <bool kSv>
+STDK_DEV uint32_t select_tail_lds(const SelectArgs& a, int64_t seg, int P, int64_t span, uint32_t m,
+                                  const uint32_t* pre, float* zs, int32_t* rs, uint32_t* h,
+                                  uint32_t (*wc)[kSelectWaves], uint32_t* scr, uint32_t* tmp, int* s_bin,
+                                  uint32_t* s_beyond, int32_t* crow, float* czs) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int K = a.K;
+  const Cand* lst = a.list + seg * a.n_pad;
+  float lo = INFINITY, hi = -INFINITY;
+  bool bad = false;
+  {
+    constexpr int CU = 4;
+    for (uint32_t base = 0; base < m; base += kSelThreads * CU) {
+      Cand c[CU];
+#pragma unroll
+      for (int u = 0; u < CU; ++u) {
+        const uint32_t i = min(base + (uint32_t)(u * kSelThreads + tid), m - 1u);
+        int lo_r = 0, hi_r = P - 1;
+        while (lo_r < hi_r) {
+          const int mid = (lo_r + hi_r + 1) >> 1;
+          if (pre[mid] <= i) lo_r = mid;
+          else hi_r = mid - 1;
+        }
+        c[u] = load_agent(lst + (int64_t)lo_r * span + (i - pre[lo_r]));
+      }
+#pragma unroll
+      for (int u = 0; u < CU; ++u) {
+        const uint32_t i = base + (uint32_t)(u * kSelThreads + tid);
+        if (i < m) {
+          const float z = key2f(c[u].key);
+          zs[i] = z;
+          rs[i] = c[u].pos;
+          lo = fminf(lo, z);
+          hi = fmaxf(hi, z);
+          bad |= !__builtin_isfinite(z);
+        }
+      }
+    }
+  }
+  float* wlo = reinterpret_cast<float*>(scr + kCutList);
+  float* whi = wlo + kSelectWaves;
+  uint32_t* s_bad = scr + kCutList + 2 * kSelectWaves;
+  uint32_t* s_cnt = tmp + 2;
+  if (tid == 0) {
+    *s_bad = 0u;
+    *s_cnt = 0u;
+  }
+  lo = wave_min(lo);
+  hi = wave_max(hi);
+  const bool wbad = __ballot(bad) != 0ull;
+  __syncthreads();
+  if (lane == 0) {
+    wlo[wv] = lo;
+    whi[wv] = hi;
+    if (wbad) *s_bad = 1u;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int v = 0; v < kSelectWaves; ++v) {
+    lo = fminf(lo, wlo[v]);
+    hi = fmaxf(hi, whi[v]);
+  }
+  TopkCut cut{0u, (uint32_t)K, true};
+  if (m > (uint32_t)K) {
+    const bool ok = *s_bad == 0u && hi > lo && 2048.f / (hi - lo) <= __FLT_MAX__ &&
+                    lds_cut_linear<kSelThreads>(zs, m, K, lo, hi, h, scr, s_cnt, tmp, s_bin, s_beyond, &cut);
+    if (!ok) cut = lds_cut_radix<kSelThreads>(zs, m, K, h, wc, s_bin, s_beyond);
+  }
+  int32_t* srow = a.sel_row + seg * K;
+  float* sz = a.sel_z + seg * K;
+  int32_t* io = a.idx_out ? a.idx_out + seg * K : nullptr;
+  const uint32_t tot = lds_emit<kSelThreads>(zs, rs, m, K, cut, wc, [&](uint32_t pos, int32_t p, float z) {
+    const int32_t row = (int32_t)pos_to_row(a.tab, p);
+    srow[pos] = row;
+    sz[pos] = z;
+    if (io) io[pos] = row;
+    if (kSv) {
+      crow[pos] = row;
+      czs[pos] = z;
+    }
+  });
+  for (uint32_t i = min(tot, (uint32_t)K) + tid; i < (uint32_t)K; i += kSelThreads) {
+    srow[i] = -1;
+    sz[i] = -INFINITY;
+    if (io) io[i] = -1;
+  }
+  return tot;
+}
+
+template <typename T, bool kSv>
+STDK_DEV void fsel_body(const SelectArgs& a) {
+  extern __shared__ uint32_t dyn[];
+  __shared__ uint32_t h1[kHistBins];  // second digit, this workgroup's candidates in bin b*
+  __shared__ uint32_t h2[1024];       // third digit
+  __shared__ uint32_t tmp[2 * kSelectWaves + 2];
+  __shared__ uint32_t s_wc[2][kSelectWaves];
+  __shared__ int s_bin;
+  __shared__ uint32_t s_beyond, s_b1, s_beyond1, s_cnt1, s_last, s_ldsm;
+  const int64_t seg = blockIdx.y;
+  if (a.seg_active && a.seg_active[seg] == 0) return;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int P = (int)gridDim.x;
+  const int K = a.K;
+  const int64_t n = a.n_dev ? min(a.n, max((int64_t)0, *a.n_dev)) : a.n;
+  const bool take_all = n <= K;
+  uint32_t* hg = a.hist + seg * kHistBins;
+  uint32_t* h1g = a.hist1 + seg * kHistBins;
+  const int64_t span = (int64_t)a.nb * kSelectWaves * a.slice;
+
+  // 1. Filter, in nb batches of 16 wave slices. Wave 0 requests the
+  // histogram first, then every wave the scores of its first slice; wave 0
+  // finds b* (the first digit's bin of the K-th largest key) while they
+  // arrive. The candidates (first digit >= b*) go to this workgroup's region
+  // in position order: the waves' counts give each wave its offset, ballots
+  // rank the lanes. The candidates in bin b* are counted by their second
+  // digit (bits 20..10) in LDS; the non-zero bins are then added to the
+  // segment's global histogram, after the candidate stores so that those are
+  // not queued behind them. A batch's loads are issued after the previous
+  // batch's stores: every workgroup of the grid streams at once, which keeps
+  // the memory system busy without deeper pipelining inside one (measured:
+  // requesting the next batch first changed nothing).
+  {
+    const float* sc = a.scores + seg * a.n_pad;
+    Cand* out = a.list + seg * a.n_pad + (int64_t)blockIdx.x * span;
+    // 16-byte loads: chunk u of a wave's slice is positions [256u, 256u +
+    // 256), lane l holding 4l .. 4l + 3 (rows start on 64-float boundaries;
+    // addresses past the slice stay inside the segment's row and are not used)
+    constexpr int NV = kFselLoads / 4;
+    float4 v[NV];
+    auto load_batch = [&](int bt) {
+      const int64_t p0 = (int64_t)blockIdx.x * span + ((int64_t)bt * kSelectWaves + wv) * a.slice;
+#pragma unroll
+      for (int u = 0; u < NV; ++u) v[u] = *reinterpret_cast<const float4*>(sc + min(p0 + 256 * u + 4 * lane, a.n_pad - 4));
+    };
+    u32x4 hv[8];
+    if (wv == 0 && !take_all) first_digit_load(hg, hv);
+    load_batch(0);
+#pragma unroll
+    for (int u = 0; u < kHistBins / kSelThreads; ++u) h1[u * kSelThreads + tid] = 0u;
+    if (wv == 0) {
+      uint32_t beyond = 0, cnt0 = 0;
+      const uint32_t bin = take_all ? 0u : first_digit_search(hv, (uint32_t)K, &beyond, &cnt0);
+      if (lane == 0) {
+        s_bin = (int)bin;
+        s_beyond = beyond;
+        // one workgroup per head whose candidates all fit its LDS: it
+        // selects there directly and needs no second-digit histogram (with
+        // several, reading that histogram overlaps the read of their counts,
+        // and the one-pass cut over all candidates costs more than it saves)
+        s_ldsm = P == 1 && (take_all ? (uint32_t)n : beyond + cnt0) <= (uint32_t)a.cache_cap ? 1u : 0u;
+      }
+    }
+    __syncthreads();
+    const uint32_t b0 = (uint32_t)s_bin;
+    const bool lds_mode = s_ldsm != 0u;
+    uint32_t written = 0;
+    for (int bt = 0;;) {
+      const int64_t p0 = (int64_t)blockIdx.x * span + ((int64_t)bt * kSelectWaves + wv) * a.slice;
+      const int64_t p1 = min(n, p0 + a.slice);
+      // per chunk: each lane's taken positions as 4 bits, their count
+      // scanned over the wave (the order is lane, then element)
+      uint32_t key[NV][4], bits[NV], ex[NV], ct[NV];
+      uint32_t cnt = 0;
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        const float f[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+        bits[u] = 0u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t p = p0 + 256 * u + 4 * lane + e;
+          key[u][e] = f2key(f[e]);
+          const uint32_t d0 = key[u][e] >> (32 - kHistBits);
+          const bool take = p < p1 && (take_all || d0 >= b0);
+          bits[u] |= (take ? 1u : 0u) << e;
+          if (take && !lds_mode && d0 == b0) atomicAdd(&h1[(key[u][e] >> 10) & 0x7FFu], 1u);
+        }
+        const uint32_t c = (uint32_t)__popc(bits[u]);
+        const uint32_t incl = wave_incl_scan(c);
+        ex[u] = incl - c;
+        ct[u] = lane_read(incl, 63);
+        cnt += ct[u];
+      }
+      // the counts alternate between two arrays, so one barrier per batch
+      // suffices: a batch's array is rewritten two batches later, after
+      // every wave has passed the barrier between
+      if (lane == 0) s_wc[bt & 1][wv] = cnt;
+      __syncthreads();
+      uint32_t off = written, tot = 0;
+#pragma unroll
+      for (int w = 0; w < kSelectWaves; ++w) {
+        const uint32_t c = s_wc[bt & 1][w];
+        off += w < wv ? c : 0u;
+        tot += c;
+      }
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if ((bits[u] >> e) & 1u)
+            store_agent(out + off + ex[u] + (uint32_t)__popc(bits[u] & ((1u << e) - 1u)),
+                        Cand{key[u][e], (int32_t)(p0 + 256 * u + 4 * lane + e)});
+        }
+        off += ct[u];
+      }
+      written += tot;
+      if (++bt == a.nb) break;
+      load_batch(bt);
+    }
+    if (tid == 0) store_agent(a.wg_cnt + seg * P + blockIdx.x, written);
+    if (!lds_mode) {
+#pragma unroll
+      for (int u = 0; u < kHistBins / kSelThreads; ++u) {
+        const uint32_t c = h1[u * kSelThreads + tid];
+        if (c != 0u) atomicAdd(&h1g[u * kSelThreads + tid], c);
+      }
+    }
+  }
+
+  // 2. Arrival: once every wave's writes and histogram adds are complete,
+  // thread 0 counts the workgroup in. The workgroup that takes the count to
+  // P finishes the segment (and resets the counter); the others are done.
+  if (!arrive_last(a.done + seg * kCtlWords, (uint32_t)P, &s_last)) return;
+
+  // 3. Select. Wave 0 finds the second digit's bin from the global
+  // histogram, then zeroes both histograms for the next call (every
+  // workgroup of the segment read the first before it arrived, and its adds
+  // to the second are complete); wave 1 builds the workgroups' candidate
+  // offsets; every thread clears the third digit's histogram.
+  uint32_t* pre = dyn;
+  const bool lds_mode = s_ldsm != 0u;
+  if (wv == 0) {
+    if (!lds_mode) {
+      const uint32_t* base = h1g + (kHistBins - 32 - 32 * lane);
+      u32x4 hv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        hv[i].x = load_agent(base + 4 * i);
+        hv[i].y = load_agent(base + 4 * i + 1);
+        hv[i].z = load_agent(base + 4 * i + 2);
+        hv[i].w = load_agent(base + 4 * i + 3);
+      }
+      uint32_t beyond1 = 0, cnt1 = 0;
+      const uint32_t b1 = first_digit_search(hv, (uint32_t)K - s_beyond, &beyond1, &cnt1);
+      if (lane == 0) {
+        s_b1 = b1;
+        s_beyond1 = beyond1;
+        s_cnt1 = cnt1;
+      }
+    }
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      *reinterpret_cast<u32x4*>(hg + (kHistBins - 32 - 32 * lane) + 4 * i) = z;
+      if (!lds_mode) *reinterpret_cast<u32x4*>(h1g + (kHistBins - 32 - 32 * lane) + 4 * i) = z;
+    }
+  } else if (wv == 1) {
+    uint32_t run = 0;
+    for (int j0 = 0; j0 < P; j0 += 64) {
+      const int j = j0 + lane;
+      const uint32_t c = j < P ? load_agent(a.wg_cnt + seg * P + j) : 0u;
+      const uint32_t incl = wave_incl_scan(c);
+      if (j < P) pre[j] = run + incl - c;
+      run += lane_read(incl, 63);
+    }
+    if (lane == 0) pre[P] = run;
+  }
+  h2[tid] = 0u;
+  __syncthreads();
+  const uint32_t m = pre[P];
+  const uint32_t b0 = take_all || lds_mode ? 0u : (uint32_t)s_bin;
+  const uint32_t b1 = take_all || lds_mode ? 0u : s_b1;
+  const uint32_t need = take_all || lds_mode ? (uint32_t)K : (uint32_t)K - s_beyond - s_beyond1;
+  const uint32_t pre22 = (b0 << 11) | b1;
+  // fused softmax . V: the static slots' scores and rows are requested now
+  // (clamped loads, kept in registers until the chosen rows are known);
+  // chosen and static slots go after the candidate copy, and the softmax's
+  // group sums overwrite the copy once it is read
+  const int pre_words = (P + 2) & ~1;
+  int32_t* crow = nullptr;
+  float* czs = nullptr;
+  float zst[kFuseStatic];
+  int32_t rst[kFuseStatic];
+  if (kSv) {
+    crow = reinterpret_cast<int32_t*>(dyn + pre_words + 2 * a.cache_cap);
+    czs = reinterpret_cast<float*>(crow + (K + a.n_extra));
+    if (a.n_extra > 0) {
+#pragma unroll
+      for (int u = 0; u < kFuseStatic; ++u) {
+        const int64_t p = a.n + min(tid + kSelThreads * u, a.n_extra - 1);
+        zst[u] = a.scores[seg * a.n_pad + p];
+        rst[u] = (int32_t)pos_to_row(a.tab, p);
+      }
+    }
+  }
+  // the candidates the copy keeps: those above the K-th key's first-digit
+  // bin, and in it those at or above its second-digit bin (both histograms
+  // count exactly the candidates); LDS holds them when they fit
+  const uint32_t kept = take_all ? m : min(m, s_beyond + s_beyond1 + s_cnt1);
+  uint32_t tot;
+  if (lds_mode) {
+    tot = select_tail_lds<kSv>(a, seg, P, span, min(m, (uint32_t)a.cache_cap), pre,
+                               reinterpret_cast<float*>(dyn + pre_words),
+                               reinterpret_cast<int32_t*>(dyn + pre_words + a.cache_cap), h1, s_wc, h2, tmp,
+                               &s_bin, &s_beyond, crow, czs);
+  } else if (kept <= (uint32_t)a.cache_cap) {
+    Cand* cl = reinterpret_cast<Cand*>(dyn + pre_words);
+    tot = select_tail<true, kSv>(a, seg, P, span, m, pre22, need, take_all, pre, cl, (uint32_t)a.cache_cap, h2, tmp,
+                                 &s_bin, &s_beyond, crow, czs);
+  } else {
+    tot = select_tail<false, kSv>(a, seg, P, span, m, pre22, need, take_all, pre, a.clist + seg * a.n_pad, m, h2,
+                                  tmp, &s_bin, &s_beyond, crow, czs);
+  }
+  if (kSv) {
+    const uint32_t nk = min(tot, (uint32_t)K);
+#pragma unroll
+    for (int u = 0; u < kFuseStatic; ++u) {
+      const int j = tid + kSelThreads * u;
+      if (j < a.n_extra) {
+        crow[nk + j] = rst[u];
+        czs[nk + j] = zst[u];
+      }
+    }
+    tail_softmax_v<T>(a, seg, crow, czs, nk + (uint32_t)a.n_extra,
+                      reinterpret_cast<float(*)[kHeadDim]>(dyn + pre_words), reinterpret_cast<float*>(tmp));
+  }
+}
+
+__global__ __launch_bounds__(kSelThreads) void topk_filter_select(SelectArgs a) { fsel_body<uint16_t, false>(a); }
+
+// topk_filter_select whose last workgroup per segment also forms softmax . V
+// over the chosen rows and the static slots (tail_softmax_v): one launch
+// instead of three (sparse_sv + combine after the select). Dynamic LDS: as
+// topk_filter_select with room for the copy of at least the group sums
+// (NG x 128 floats), then K + n_extra rows and as many scores.
+template <typename T>
+__global__ __launch_bounds__(kSelThreads) void topk_filter_select_sv(SelectArgs a) {
+  fsel_body<T, true>(a);
+}
+
 
 
 // ---------------------------------------------------------------------------
