@@ -181,6 +181,41 @@ def test_short_segment_codebook_ties(ops):
             check_out(o[0, h], lse[0, h], want["o"][0, h], want["lse"][0, h], False, f"short codebook K={K} head {h}")
 
 
+@pytest.mark.parametrize("K", [300, 5000])
+def test_one_workgroup_per_head_ties_and_nan(ops, K):
+    """256 heads of 9,000 positions: one filter workgroup per head, which
+    selects in its own LDS (one-pass cut, radix passes when the K-th score's
+    bin is crowded or a score is NaN). Keys from a 6-row codebook, so every
+    score ties with about 1,500 others: the index sets must equal the
+    oracle's exactly (lowest rows first). A NaN in one head's query makes
+    that head's o and lse NaN and leaves every other head bit-identical."""
+    from workloads import make_multi_query
+    w = make_multi_query(8, 32, 4, 1, 9000, "bf16", codebook=6, tag=45)
+    w.q = np.ascontiguousarray(w.q[:, :, 0])
+    ranges = [(0, 9000)]
+    log(f"case one workgroup per head, codebook ties K={K}")
+    idx, o, lse = run(ops, w, ranges, K)
+    want = ref.topk_attn_decode(w.q, w.k, w.v, ranges, K, w.scale)
+    assert np.array_equal(idx, want["idx"])
+    for b in range(w.B):
+        for h in range(w.H_q):
+            check_out(o[b, h], lse[b, h], want["o"][b, h], want["lse"][b, h], False, f"ties K={K} ({b},{h})")
+    qn = w.q.copy()
+    qn[3, 5, 17] = np.nan
+    qt = torch.from_numpy(qn).cuda()
+    k, v = dev_kv(w)
+    idx2, o2, lse2 = ops.topk_attn_decode(qt, k, v, ranges, K, w.scale)
+    torch.cuda.synchronize()
+    idx2, o2, lse2 = idx2.cpu().numpy(), o2.cpu().numpy(), lse2.cpu().numpy()
+    assert np.all(np.isnan(o2[3, 5])) and np.isnan(lse2[3, 5])
+    sel = idx2[3, 5][idx2[3, 5] >= 0]
+    assert sel.shape[0] == K and np.all(np.diff(sel) > 0)
+    keep = np.ones((w.B, w.H_q), bool)
+    keep[3, 5] = False
+    for x, y in ((idx, idx2), (o, o2), (lse, lse2)):
+        assert np.array_equal(x[keep], y[keep])
+
+
 @pytest.mark.parametrize("K", [300, 9000])
 def test_codebook_ties_many_candidates(ops, K):
     """Keys from a 6-row codebook over 24,000 rows: every score ties with
