@@ -903,15 +903,16 @@ STDK_DEV void fsel_body(const SelectArgs& a) {
   const bool lds_mode = s_ldsm != 0u;
   if (wv == 0) {
     if (!lds_mode) {
+      // 16-byte loads from the device's coherence point (the bins were
+      // added there by every workgroup of the segment), all issued before
+      // one wait
       const uint32_t* base = h1g + (kHistBins - 32 - 32 * lane);
       u32x4 hv[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        hv[i].x = load_agent(base + 4 * i);
-        hv[i].y = load_agent(base + 4 * i + 1);
-        hv[i].z = load_agent(base + 4 * i + 2);
-        hv[i].w = load_agent(base + 4 * i + 3);
-      }
+      for (int i = 0; i < 8; ++i) __asm__ volatile("global_load_dwordx4 %0, %1, off sc1" : "=v"(hv[i]) : "v"(base + 4 * i));
+      wait_vm<0>();
+#pragma unroll
+      for (int i = 0; i < 8; ++i) arrived(hv[i]);
       uint32_t beyond1 = 0, cnt1 = 0;
       const uint32_t b1 = first_digit_search(hv, (uint32_t)K - s_beyond, &beyond1, &cnt1);
       if (lane == 0) {
