@@ -1265,8 +1265,11 @@ __global__ __launch_bounds__(kSvThreads) void sparse_sv(SvArgs a) {
       const int j = j0 + jj;
       if (jj < nr) {
         if (j < a.k_top) {
+          // row and score requested together; a padding slot (row -1)
+          // weighs nothing
           r[i] = a.sel_row[seg * a.k_top + j];
-          if (r[i] >= 0) z[i] = a.sel_z[seg * a.k_top + j];
+          const float zz = a.sel_z[seg * a.k_top + j];
+          z[i] = r[i] >= 0 ? zz : -INFINITY;
         } else {
           const int64_t p = a.n + (j - a.k_top);
           r[i] = (int32_t)pos_to_row(a.tab, p);
