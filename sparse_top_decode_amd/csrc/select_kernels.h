@@ -663,52 +663,27 @@ STDK_DEV uint32_t lds_topk(const float* zs, const int32_t* rs, uint32_t M, int K
   return lds_emit<NT>(zs, rs, M, K, cut, wc, emit);
 }
 
-// The last workgroup's select when the head's candidates fit its LDS: all
-// m of them (key and position, in position order) are copied there, the
-// exact top K taken by the one-pass linear-bin cut over their range
-// (lds_cut_linear; the radix passes when a score is not finite or the K-th
-// score's bin holds more than kCutList), and the chosen rows emitted in
-// order (lds_emit: the key order and lowest-position ties of select_tail).
-// Needs no second-digit histogram. `h` (kHistBins words) is zero on entry;
-// `scr` holds at least 128 words.
+// The select of a head with one filter workgroup whose candidates fit its
+// LDS: the filter left all m of them there (scores zs and positions rs, in
+// position order); the exact top K is taken by the one-pass linear-bin cut
+// over their range (lds_cut_linear; the radix passes when a score is not
+// finite or the K-th score's bin holds more than kCutList), and the chosen
+// rows are emitted in order (lds_emit: the key order and lowest-position
+// ties of select_tail). Needs no second-digit histogram. `h` (kHistBins
+// words) is zero on entry; `scr` holds at least 128 words.
 template <bool kSv>
-STDK_DEV uint32_t select_tail_lds(const SelectArgs& a, int64_t seg, int P, int64_t span, uint32_t m,
-                                  const uint32_t* pre, float* zs, int32_t* rs, uint32_t* h,
+STDK_DEV uint32_t select_tail_lds(const SelectArgs& a, int64_t seg, uint32_t m, float* zs, int32_t* rs, uint32_t* h,
                                   uint32_t (*wc)[kSelectWaves], uint32_t* scr, uint32_t* tmp, int* s_bin,
                                   uint32_t* s_beyond, int32_t* crow, float* czs) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int K = a.K;
-  const Cand* lst = a.list + seg * a.n_pad;
   float lo = INFINITY, hi = -INFINITY;
   bool bad = false;
-  {
-    constexpr int CU = 4;
-    for (uint32_t base = 0; base < m; base += kSelThreads * CU) {
-      Cand c[CU];
-#pragma unroll
-      for (int u = 0; u < CU; ++u) {
-        const uint32_t i = min(base + (uint32_t)(u * kSelThreads + tid), m - 1u);
-        int lo_r = 0, hi_r = P - 1;
-        while (lo_r < hi_r) {
-          const int mid = (lo_r + hi_r + 1) >> 1;
-          if (pre[mid] <= i) lo_r = mid;
-          else hi_r = mid - 1;
-        }
-        c[u] = load_agent(lst + (int64_t)lo_r * span + (i - pre[lo_r]));
-      }
-#pragma unroll
-      for (int u = 0; u < CU; ++u) {
-        const uint32_t i = base + (uint32_t)(u * kSelThreads + tid);
-        if (i < m) {
-          const float z = key2f(c[u].key);
-          zs[i] = z;
-          rs[i] = c[u].pos;
-          lo = fminf(lo, z);
-          hi = fmaxf(hi, z);
-          bad |= !__builtin_isfinite(z);
-        }
-      }
-    }
+  for (uint32_t i = tid; i < m; i += kSelThreads) {
+    const float z = zs[i];
+    lo = fminf(lo, z);
+    hi = fmaxf(hi, z);
+    bad |= !__builtin_isfinite(z);
   }
   float* wlo = reinterpret_cast<float*>(scr + kCutList);
   float* whi = wlo + kSelectWaves;
@@ -779,6 +754,12 @@ STDK_DEV void fsel_body(const SelectArgs& a) {
   uint32_t* hg = a.hist + seg * kHistBins;
   uint32_t* h1g = a.hist1 + seg * kHistBins;
   const int64_t span = (int64_t)a.nb * kSelectWaves * a.slice;
+  // one workgroup per head whose candidates fit its LDS (decided below from
+  // the first-digit histogram): they go straight to its LDS (scores, then
+  // positions, after the 2-word prefix slot), no hand-over
+  float* lzs = reinterpret_cast<float*>(dyn + 2);
+  int32_t* lrs = reinterpret_cast<int32_t*>(dyn + 2 + a.cache_cap);
+  uint32_t written = 0;
 
   // 1. Filter, in nb batches of 16 wave slices. Wave 0 requests the
   // histogram first, then every wave the scores of its first slice; wave 0
@@ -826,7 +807,6 @@ STDK_DEV void fsel_body(const SelectArgs& a) {
     __syncthreads();
     const uint32_t b0 = (uint32_t)s_bin;
     const bool lds_mode = s_ldsm != 0u;
-    uint32_t written = 0;
     for (int bt = 0;;) {
       const int64_t p0 = (int64_t)blockIdx.x * span + ((int64_t)bt * kSelectWaves + wv) * a.slice;
       const int64_t p1 = min(n, p0 + a.slice);
@@ -865,21 +845,36 @@ STDK_DEV void fsel_body(const SelectArgs& a) {
         off += w < wv ? c : 0u;
         tot += c;
       }
+      if (lds_mode) {
 #pragma unroll
-      for (int u = 0; u < NV; ++u) {
+        for (int u = 0; u < NV; ++u) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if ((bits[u] >> e) & 1u)
-            store_agent(out + off + ex[u] + (uint32_t)__popc(bits[u] & ((1u << e) - 1u)),
-                        Cand{key[u][e], (int32_t)(p0 + 256 * u + 4 * lane + e)});
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t idx = off + ex[u] + (uint32_t)__popc(bits[u] & ((1u << e) - 1u));
+            if (((bits[u] >> e) & 1u) && idx < (uint32_t)a.cache_cap) {
+              lzs[idx] = key2f(key[u][e]);
+              lrs[idx] = (int32_t)(p0 + 256 * u + 4 * lane + e);
+            }
+          }
+          off += ct[u];
         }
-        off += ct[u];
+      } else {
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if ((bits[u] >> e) & 1u)
+              store_agent(out + off + ex[u] + (uint32_t)__popc(bits[u] & ((1u << e) - 1u)),
+                          Cand{key[u][e], (int32_t)(p0 + 256 * u + 4 * lane + e)});
+          }
+          off += ct[u];
+        }
       }
       written += tot;
       if (++bt == a.nb) break;
       load_batch(bt);
     }
-    if (tid == 0) store_agent(a.wg_cnt + seg * P + blockIdx.x, written);
+    if (tid == 0 && !lds_mode) store_agent(a.wg_cnt + seg * P + blockIdx.x, written);
     if (!lds_mode) {
 #pragma unroll
       for (int u = 0; u < kHistBins / kSelThreads; ++u) {
@@ -892,7 +887,9 @@ STDK_DEV void fsel_body(const SelectArgs& a) {
   // 2. Arrival: once every wave's writes and histogram adds are complete,
   // thread 0 counts the workgroup in. The workgroup that takes the count to
   // P finishes the segment (and resets the counter); the others are done.
-  if (!arrive_last(a.done + seg * kCtlWords, (uint32_t)P, &s_last)) return;
+  // (a workgroup that is its head's only one is also its last)
+  const bool lds_mode = s_ldsm != 0u;
+  if (!lds_mode && !arrive_last(a.done + seg * kCtlWords, (uint32_t)P, &s_last)) return;
 
   // 3. Select. Wave 0 finds the second digit's bin from the global
   // histogram, then zeroes both histograms for the next call (every
@@ -900,7 +897,6 @@ STDK_DEV void fsel_body(const SelectArgs& a) {
   // to the second are complete); wave 1 builds the workgroups' candidate
   // offsets; every thread clears the third digit's histogram.
   uint32_t* pre = dyn;
-  const bool lds_mode = s_ldsm != 0u;
   if (wv == 0) {
     if (!lds_mode) {
       // 16-byte loads from the device's coherence point (the bins were
@@ -927,7 +923,7 @@ STDK_DEV void fsel_body(const SelectArgs& a) {
       *reinterpret_cast<u32x4*>(hg + (kHistBins - 32 - 32 * lane) + 4 * i) = z;
       if (!lds_mode) *reinterpret_cast<u32x4*>(h1g + (kHistBins - 32 - 32 * lane) + 4 * i) = z;
     }
-  } else if (wv == 1) {
+  } else if (wv == 1 && !lds_mode) {
     uint32_t run = 0;
     for (int j0 = 0; j0 < P; j0 += 64) {
       const int j = j0 + lane;
@@ -940,7 +936,7 @@ STDK_DEV void fsel_body(const SelectArgs& a) {
   }
   h2[tid] = 0u;
   __syncthreads();
-  const uint32_t m = pre[P];
+  const uint32_t m = lds_mode ? min(written, (uint32_t)a.cache_cap) : pre[P];
   const uint32_t b0 = take_all || lds_mode ? 0u : (uint32_t)s_bin;
   const uint32_t b1 = take_all || lds_mode ? 0u : s_b1;
   const uint32_t need = take_all || lds_mode ? (uint32_t)K : (uint32_t)K - s_beyond - s_beyond1;
@@ -972,10 +968,7 @@ STDK_DEV void fsel_body(const SelectArgs& a) {
   const uint32_t kept = take_all ? m : min(m, s_beyond + s_beyond1 + s_cnt1);
   uint32_t tot;
   if (lds_mode) {
-    tot = select_tail_lds<kSv>(a, seg, P, span, min(m, (uint32_t)a.cache_cap), pre,
-                               reinterpret_cast<float*>(dyn + pre_words),
-                               reinterpret_cast<int32_t*>(dyn + pre_words + a.cache_cap), h1, s_wc, h2, tmp,
-                               &s_bin, &s_beyond, crow, czs);
+    tot = select_tail_lds<kSv>(a, seg, m, lzs, lrs, h1, s_wc, h2, tmp, &s_bin, &s_beyond, crow, czs);
   } else if (kept <= (uint32_t)a.cache_cap) {
     Cand* cl = reinterpret_cast<Cand*>(dyn + pre_words);
     tot = select_tail<true, kSv>(a, seg, P, span, m, pre22, need, take_all, pre, cl, (uint32_t)a.cache_cap, h2, tmp,
