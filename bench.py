@@ -357,8 +357,9 @@ def timed_passes(step, steps, names, reset=None, graph=None, graph_steps=1):
 
 def capture(step, n=1):
     """n consecutive steps captured once in a HIP graph (None if capture
-    fails). With rotating layer caches n is their number, so that each
-    replay scans every cache once, as the direct launches do."""
+    fails). With rotating layer caches n is a multiple of their number, so
+    that each replay scans every cache equally often, as the direct
+    launches do."""
     import torch
     try:
         side = torch.cuda.Stream()
@@ -528,11 +529,14 @@ def bench_topk(args, cfg):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    graph = capture(step, n_layers) if args.graph == "on" else None
+    # a graph holds whole rounds of the layer caches, at least 8 steps, so
+    # that a replay's own launch cost is spread over them
+    graph_steps = n_layers * -(-8 // n_layers)
+    graph = capture(step, graph_steps) if args.graph == "on" else None
     names = TOPK_KERNELS if args.kernel_events == "on" else ()
     if q8 is not None:
         names = names + ("retopk_rerank", "retopk_rerank_select") if names else ()
-    ms, kern = timed_passes(step, args.steps, names, graph=graph, graph_steps=n_layers)
+    ms, kern = timed_passes(step, args.steps, names, graph=graph, graph_steps=graph_steps)
     row_bytes = 128 * (4 if w.kv_dtype == "f32" else 2)
     if q8 is None:
         scan_bytes = B * w.H_kv * n_dyn * row_bytes  # every dynamic key row once, d=128
