@@ -124,7 +124,6 @@ __global__ __launch_bounds__(kDenseThreads) void dense_attn(DenseArgs a) {
   constexpr int EPL = KvTraits<T>::EPL, LPR = KvTraits<T>::LPR, RPL = KvTraits<T>::RPL, ROWB = KvTraits<T>::ROWB;
   constexpr int NW = kDenseThreads / 64;
   constexpr int U = kDenseTile / (NW * RPL);  // tile rows per wave load group
-  constexpr int GROUPS = NW * RPL;
   __shared__ float zt[G][kDenseTile];
   __shared__ int64_t trow[kDenseTile];
   __shared__ float tmax[G], tsum[G];
