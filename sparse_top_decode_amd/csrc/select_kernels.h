@@ -452,7 +452,9 @@ STDK_DEV void tail_softmax_v(const SelectArgs& a, int64_t seg, const int32_t* cr
       }
     }
   };
-  if (Tn <= 2 * NG) {
+  if (Tn == 0) {
+    // no slot: nothing is read (o = 0, lse = -inf below)
+  } else if (Tn <= 2 * NG) {
     gather(std::integral_constant<int, 2>(), 0u);
   } else if (Tn <= 4 * NG) {
     gather(std::integral_constant<int, 4>(), 0u);
@@ -825,7 +827,7 @@ STDK_DEV void fsel_body(const SelectArgs& a) {
           const uint32_t d0 = key[u][e] >> (32 - kHistBits);
           const bool take = p < p1 && (take_all || d0 >= b0);
           bits[u] |= (take ? 1u : 0u) << e;
-          if (take && !lds_mode && d0 == b0) atomicAdd(&h1[(key[u][e] >> 10) & 0x7FFu], 1u);
+          if (take && !take_all && !lds_mode && d0 == b0) atomicAdd(&h1[(key[u][e] >> 10) & 0x7FFu], 1u);
         }
         const uint32_t c = (uint32_t)__popc(bits[u]);
         const uint32_t incl = wave_incl_scan(c);
@@ -875,7 +877,7 @@ STDK_DEV void fsel_body(const SelectArgs& a) {
       load_batch(bt);
     }
     if (tid == 0 && !lds_mode) store_agent(a.wg_cnt + seg * P + blockIdx.x, written);
-    if (!lds_mode) {
+    if (!take_all && !lds_mode) {
 #pragma unroll
       for (int u = 0; u < kHistBins / kSelThreads; ++u) {
         const uint32_t c = h1[u * kSelThreads + tid];
@@ -898,7 +900,7 @@ STDK_DEV void fsel_body(const SelectArgs& a) {
   // offsets; every thread clears the third digit's histogram.
   uint32_t* pre = dyn;
   if (wv == 0) {
-    if (!lds_mode) {
+    if (!take_all && !lds_mode) {
       // 16-byte loads from the device's coherence point (the bins were
       // added there by every workgroup of the segment), all issued before
       // one wait
