@@ -89,7 +89,7 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak of MI355X
 SCAN_SOURCES = ["sparse_top_decode_amd/csrc/scan_kernels.h", "sparse_top_decode_amd/csrc/device.h"]
 METRIC = "top-K decode-attention steps/sec at 128K ctx; K-scan HBM GB/s vs peak"
-TOPK_KERNELS = ("k_scan", "topk_filter_select", "topk_filter_select_sv", "topk_select_lds",
+TOPK_KERNELS = ("k_scan", "topk_filter_select", "topk_filter_select_sv", "topk_filter_lds_sv", "topk_select_lds",
                 "topk_select_lds_sv", "sparse_sv", "dense_attn", "combine", "attn_merge")
 MQ_KERNELS = ("mq_blockmax", "mq_threshold", "mq_collect", "mq_select")
 RETOPK_KERNELS = ("retopk_reuse", "retopk_select", "retopk_vote", "retopk_attend", "retopk_rerank", "retopk_rerank_select",

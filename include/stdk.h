@@ -463,7 +463,8 @@ int32_t stdk_hbm_read(const void* base, int64_t group_stride_bytes, int32_t n_gr
  * "retopk_rerank_select", "retopk_init", "retopk_vote",
  * "mq_blockmax", "mq_threshold", "mq_collect", "mq_select", "mq_fill",
  * "k_quantize", "hbm_read", "retopk_attend", "retopk_reuse",
- * "topk_filter_select_sv", "topk_select_lds", "topk_select_lds_sv".
+ * "topk_filter_select_sv", "topk_select_lds", "topk_select_lds_sv",
+ * "topk_filter_lds_sv".
  * Unknown names return STDK_EINVAL. */
 int32_t stdk_profile_enable(int32_t capacity, const char* only);
 int32_t stdk_profile_disable(void);

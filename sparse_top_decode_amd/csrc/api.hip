@@ -59,7 +59,7 @@ int32_t ok() {
 enum KernelId {
   KID_SCAN, KID_SELECT, KID_SV, KID_DENSE, KID_COMBINE, KID_MERGE, KID_FILL,
   KID_RT_SELECT, KID_RT_RERANK, KID_RT_RSEL, KID_RT_INIT, KID_MQ_BLOCKMAX, KID_MQ_THRESH,
-  KID_MQ_COLLECT, KID_MQ_SELECT, KID_MQ_FILL, KID_RT_VOTE, KID_Q8_QUANT, KID_READ, KID_RT_ATTEND, KID_RT_REUSE, KID_SELECT_SV, KID_SELECT_LDS, KID_SELECT_LDS_SV, KID_COUNT
+  KID_MQ_COLLECT, KID_MQ_SELECT, KID_MQ_FILL, KID_RT_VOTE, KID_Q8_QUANT, KID_READ, KID_RT_ATTEND, KID_RT_REUSE, KID_SELECT_SV, KID_SELECT_LDS, KID_SELECT_LDS_SV, KID_SELECT_HALF_SV, KID_COUNT
 };
 const char* const kKernelNames[KID_COUNT] = {
     "k_scan",        "topk_filter_select",             "sparse_sv",
@@ -67,7 +67,7 @@ const char* const kKernelNames[KID_COUNT] = {
     "retopk_rerank", "retopk_rerank_select", "retopk_init", "mq_blockmax",
     "mq_threshold",  "mq_collect",    "mq_select",     "mq_fill",       "retopk_vote",   "k_quantize",
     "hbm_read",      "retopk_attend", "retopk_reuse", "topk_filter_select_sv",
-    "topk_select_lds", "topk_select_lds_sv"};
+    "topk_select_lds", "topk_select_lds_sv", "topk_filter_lds_sv"};
 
 struct Profiler {
   std::mutex mu;
@@ -247,6 +247,11 @@ int32_t dev_info(DevInfo** out) {
                               dyn_max);
     (void)hipFuncSetAttribute((const void*)topk_select_lds_sv<float>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               dyn_max);
+    const int half_max = std::max(0, d.max_lds / 2 - (int)kHalfStaticLds);
+    (void)hipFuncSetAttribute((const void*)topk_filter_lds_sv<uint16_t>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              half_max);
+    (void)hipFuncSetAttribute((const void*)topk_filter_lds_sv<float>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              half_max);
     (void)hipFuncSetAttribute((const void*)retopk_select<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               std::max(0, d.max_lds - 12 * 1024));
     (void)hipFuncSetAttribute((const void*)mq_select, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -346,7 +351,7 @@ constexpr int64_t kFselTargetWg = 256;
 // scored by the same scan and appended whole to every chosen-row list.
 struct TopkWs {
   int64_t S, n, n_extra, n_pad, K, ksel, nsplit, slice, nb, wg;
-  size_t hist, hist1, done, counters, scores, list, clist, wg_cnt, sel_row, sel_z, part, total;
+  size_t hist, hist1, done, counters, scores, list, clist, wg_cnt, sel_row, sel_z, part, ovf, total;
 };
 
 TopkWs topk_ws(int64_t S, int64_t n, int64_t K, int64_t n_extra = 0) {
@@ -387,6 +392,8 @@ TopkWs topk_ws(int64_t S, int64_t n, int64_t K, int64_t n_extra = 0) {
   off = al256(off + (size_t)S * K * 4);
   w.part = off;
   off = al256(off + (size_t)S * std::max<int64_t>(w.nsplit, kDenseMaxWg) * kPartStride * 4);
+  w.ovf = off;
+  off = al256(off + (size_t)S * 4);
   w.total = off;
   return w;
 }
@@ -535,6 +542,26 @@ bool fuse_lds_short(const Geo& g, const TopkWs& w, const DevInfo* di, size_t* dy
   return true;
 }
 
+// LDS of topk_filter_lds_sv (two workgroups per CU, each with at most half
+// of its LDS): used where every head has one filter workgroup and the heads
+// are at least twice as many as the CUs; false otherwise or when the slots
+// and the group sums do not fit. The candidate capacity takes the rest, up
+// to n.
+bool fuse_half(const Geo& g, const TopkWs& w, const DevInfo* di, size_t* dyn, int32_t* cache_cap) {
+  if (w.wg != 1 || w.n <= kSelLdsMax || w.S < 2 * (int64_t)di->n_cu || w.ksel > kFuseMaxSlots ||
+      w.n_extra > (int64_t)kFuseStatic * kHalfThreads)
+    return false;
+  const size_t avail = (size_t)di->max_lds / 2 - kHalfStaticLds;
+  const size_t slots = (size_t)w.ksel * 8;
+  const size_t red = (size_t)(kHalfThreads / (g.bf16 ? KvTraits<uint16_t>::LPR : KvTraits<float>::LPR)) * kHeadDim * 4;
+  if (8 + slots + red > avail) return false;
+  const int64_t cap = std::min<int64_t>(w.n, (int64_t)((avail - 8 - slots) / sizeof(Cand)));
+  if ((size_t)cap * sizeof(Cand) < red) return false;
+  *cache_cap = (int32_t)cap;
+  *dyn = 8 + (size_t)cap * sizeof(Cand) + slots;
+  return true;
+}
+
 // Whether run_exact_select can fuse softmax . V into its select launch.
 bool can_fuse(const Geo& g, const TopkWs& w, const DevInfo* di) {
   size_t dyn;
@@ -661,6 +688,21 @@ int32_t run_exact_select(const Geo& g, const TopkWs& w, char* ws, const float* q
       a.n_extra = (int32_t)w.n_extra;
       a.Hq = g.Hq;
       a.G = g.G;
+      size_t dyn_h;
+      int32_t cap_h;
+      if (!active && fuse_half(g, w, di, &dyn_h, &cap_h)) {
+        // half-size workgroups, two per CU; the heads whose candidates do not
+        // fit their LDS are then taken by topk_filter_select_sv, masked by
+        // the flags (all its workgroups exit at once when no head is flagged)
+        SelectArgs ah = a;
+        ah.cache_cap = cap_h;
+        ah.ovf = (int32_t*)(ws + w.ovf);
+        STDK_TRY(launch(KID_SELECT_HALF_SV, s, [&](hipEvent_t e0, hipEvent_t e1) {
+          if (g.bf16) STDK_LAUNCH(topk_filter_lds_sv<uint16_t>, dim3((unsigned)w.S), dim3(kHalfThreads), dyn_h, s, ah);
+          else STDK_LAUNCH(topk_filter_lds_sv<float>, dim3((unsigned)w.S), dim3(kHalfThreads), dyn_h, s, ah);
+        }));
+        a.seg_active = ah.ovf;
+      }
       STDK_TRY(launch(KID_SELECT_SV, s, [&](hipEvent_t e0, hipEvent_t e1) {
         if (g.bf16) STDK_LAUNCH(topk_filter_select_sv<uint16_t>, grid, dim3(kSelThreads), dyn, s, a);
         else STDK_LAUNCH(topk_filter_select_sv<float>, grid, dim3(kSelThreads), dyn, s, a);

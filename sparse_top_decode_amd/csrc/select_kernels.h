@@ -136,6 +136,7 @@ struct SelectArgs {
   float* o_out;               // [S][128]
   float* lse_out;             // [S]
   int32_t n_extra, Hq, G, pad_;
+  int32_t* ovf;               // topk_filter_lds_sv only: [S] 1 where a head's candidates did not fit, else 0
 };
 
 constexpr int kSelectWaves = kSelThreads / 64;
@@ -398,25 +399,25 @@ STDK_DEV uint32_t select_tail(const SelectArgs& a, int64_t seg, int P, int64_t s
 // the maximum over all slots, the weights e^{z - m} (a -inf score weighs 0,
 // a NaN propagates) are summed in a fixed order, and the value rows are
 // accumulated per row group, then over the groups in order.
-template <typename T>
+template <typename T, int NT = kSelThreads>
 STDK_DEV void tail_softmax_v(const SelectArgs& a, int64_t seg, const int32_t* crow, float* czs, uint32_t Tn,
                              float (*red)[kHeadDim], float* wred) {
   constexpr int EPL = KvTraits<T>::EPL, LPR = KvTraits<T>::LPR, ROWB = KvTraits<T>::ROWB;
-  constexpr int NG = kSelThreads / LPR;  // row groups
+  constexpr int NG = NT / LPR;  // row groups
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int gid = tid / LPR, c = tid % LPR;
   const uint32_t g0 = (uint32_t)(wv * (64 / LPR));  // first row group of this wave
   __syncthreads();  // every slot written; the candidate copy (under red) is dead
   float zm = -INFINITY;
-  for (uint32_t i = tid; i < Tn; i += kSelThreads) zm = fmaxf(zm, czs[i]);
+  for (uint32_t i = tid; i < Tn; i += NT) zm = fmaxf(zm, czs[i]);
   zm = wave_max(zm);
   if (lane == 0) wred[wv] = zm;
   __syncthreads();
   float m = wred[0];
 #pragma unroll
-  for (int v = 1; v < kSelectWaves; ++v) m = fmaxf(m, wred[v]);
+  for (int v = 1; v < NT / 64; ++v) m = fmaxf(m, wred[v]);
   float ps = 0.f;
-  for (uint32_t i = tid; i < Tn; i += kSelThreads) {
+  for (uint32_t i = tid; i < Tn; i += NT) {
     const float z = czs[i];
     const float wt = z == -INFINITY ? 0.f : __expf(z - m);
     czs[i] = wt;
@@ -470,7 +471,7 @@ STDK_DEV void tail_softmax_v(const SelectArgs& a, int64_t seg, const int32_t* cr
     for (int g = 0; g < NG; ++g) o += red[g][tid];
     float ssum = 0.f;
 #pragma unroll
-    for (int v = 0; v < kSelectWaves; ++v) ssum += wred[v];
+    for (int v = 0; v < NT / 64; ++v) ssum += wred[v];
     // ssum == 0: no row (o = 0, lse = -inf); a NaN sum propagates
     a.o_out[seg * kHeadDim + tid] = ssum == 0.f ? 0.f : o / ssum;
     if (tid == 0) a.lse_out[seg] = ssum == 0.f ? -INFINITY : m + __logf(ssum);
@@ -673,23 +674,23 @@ STDK_DEV uint32_t lds_topk(const float* zs, const int32_t* rs, uint32_t M, int K
 // rows are emitted in order (lds_emit: the key order and lowest-position
 // ties of select_tail). Needs no second-digit histogram. `h` (kHistBins
 // words) is zero on entry; `scr` holds at least 128 words.
-template <bool kSv>
+template <bool kSv, int NT = kSelThreads>
 STDK_DEV uint32_t select_tail_lds(const SelectArgs& a, int64_t seg, uint32_t m, float* zs, int32_t* rs, uint32_t* h,
-                                  uint32_t (*wc)[kSelectWaves], uint32_t* scr, uint32_t* tmp, int* s_bin,
+                                  uint32_t (*wc)[NT / 64], uint32_t* scr, uint32_t* tmp, int* s_bin,
                                   uint32_t* s_beyond, int32_t* crow, float* czs) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int K = a.K;
   float lo = INFINITY, hi = -INFINITY;
   bool bad = false;
-  for (uint32_t i = tid; i < m; i += kSelThreads) {
+  for (uint32_t i = tid; i < m; i += NT) {
     const float z = zs[i];
     lo = fminf(lo, z);
     hi = fmaxf(hi, z);
     bad |= !__builtin_isfinite(z);
   }
   float* wlo = reinterpret_cast<float*>(scr + kCutList);
-  float* whi = wlo + kSelectWaves;
-  uint32_t* s_bad = scr + kCutList + 2 * kSelectWaves;
+  float* whi = wlo + NT / 64;
+  uint32_t* s_bad = scr + kCutList + 2 * NT / 64;
   uint32_t* s_cnt = tmp + 2;
   if (tid == 0) {
     *s_bad = 0u;
@@ -706,20 +707,20 @@ STDK_DEV uint32_t select_tail_lds(const SelectArgs& a, int64_t seg, uint32_t m, 
   }
   __syncthreads();
 #pragma unroll
-  for (int v = 0; v < kSelectWaves; ++v) {
+  for (int v = 0; v < NT / 64; ++v) {
     lo = fminf(lo, wlo[v]);
     hi = fmaxf(hi, whi[v]);
   }
   TopkCut cut{0u, (uint32_t)K, true};
   if (m > (uint32_t)K) {
     const bool ok = *s_bad == 0u && hi > lo && 2048.f / (hi - lo) <= __FLT_MAX__ &&
-                    lds_cut_linear<kSelThreads>(zs, m, K, lo, hi, h, scr, s_cnt, tmp, s_bin, s_beyond, &cut);
-    if (!ok) cut = lds_cut_radix<kSelThreads>(zs, m, K, h, wc, s_bin, s_beyond);
+                    lds_cut_linear<NT>(zs, m, K, lo, hi, h, scr, s_cnt, tmp, s_bin, s_beyond, &cut);
+    if (!ok) cut = lds_cut_radix<NT>(zs, m, K, h, wc, s_bin, s_beyond);
   }
   int32_t* srow = a.sel_row + seg * K;
   float* sz = a.sel_z + seg * K;
   int32_t* io = a.idx_out ? a.idx_out + seg * K : nullptr;
-  const uint32_t tot = lds_emit<kSelThreads>(zs, rs, m, K, cut, wc, [&](uint32_t pos, int32_t p, float z) {
+  const uint32_t tot = lds_emit<NT>(zs, rs, m, K, cut, wc, [&](uint32_t pos, int32_t p, float z) {
     const int32_t row = (int32_t)pos_to_row(a.tab, p);
     srow[pos] = row;
     sz[pos] = z;
@@ -729,7 +730,7 @@ STDK_DEV uint32_t select_tail_lds(const SelectArgs& a, int64_t seg, uint32_t m, 
       czs[pos] = z;
     }
   });
-  for (uint32_t i = min(tot, (uint32_t)K) + tid; i < (uint32_t)K; i += kSelThreads) {
+  for (uint32_t i = min(tot, (uint32_t)K) + tid; i < (uint32_t)K; i += NT) {
     srow[i] = -1;
     sz[i] = -INFINITY;
     if (io) io[i] = -1;
@@ -1004,6 +1005,165 @@ __global__ __launch_bounds__(kSelThreads) void topk_filter_select(SelectArgs a) 
 template <typename T>
 __global__ __launch_bounds__(kSelThreads) void topk_filter_select_sv(SelectArgs a) {
   fsel_body<T, true>(a);
+}
+
+// One head per half-size workgroup (kHalfThreads), for heads that each have
+// one filter workgroup and are at least twice as many as the CUs (batched
+// decode): the head's candidates (first digit >= b*, from the scan's
+// histogram) are filtered straight into LDS, cut there (lds_cut_linear, else
+// lds_cut_radix, then lds_emit) and followed by softmax . V, as the
+// one-workgroup path of topk_filter_select_sv does. Two of these run on a
+// CU where one full-size workgroup would, so one head's LDS phases (cut,
+// emit, weights) overlap another head's score and value reads, instead of
+// every CU taking its heads in two rounds whose phases run in lockstep.
+// A head whose candidates exceed cache_cap sets ovf[seg] = 1 and returns
+// before it writes anything else (its histogram stays for
+// topk_filter_select_sv, launched next with ovf as its head mask); the
+// others set ovf[seg] = 0. Dynamic LDS: 2 words, cache_cap scores and rows,
+// then K + n_extra rows and scores; the group sums of softmax . V overwrite
+// the candidates once they are read (cache_cap >= 64 * NT / LPR).
+constexpr int kHalfThreads = 512;
+constexpr size_t kHalfStaticLds = 9 * 1024;  // static LDS of topk_filter_lds_sv, rounded up
+template <typename T>
+__global__ __launch_bounds__(kHalfThreads) __attribute__((amdgpu_waves_per_eu(4))) void topk_filter_lds_sv(
+    SelectArgs a) {
+  constexpr int NT = kHalfThreads, NW = NT / 64;
+  constexpr int NV = kFselLoads / 4;  // a wave's slice of a batch: 4 x 256 positions
+  constexpr int SLICE = 64 * kFselLoads;
+  extern __shared__ uint32_t dyn[];
+  __shared__ uint32_t h[kHistBins];               // the cut's histogram
+  __shared__ uint32_t scr[kCutList + 2 * NW + 2];  // the cut's list, wave minima and maxima, flag
+  __shared__ uint32_t tmp[2 * NW + 2];
+  __shared__ uint32_t s_wc[2][NW];
+  __shared__ int s_bin;
+  __shared__ uint32_t s_beyond, s_fit;
+  const int64_t seg = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int K = a.K;
+  const uint32_t cap = (uint32_t)a.cache_cap;
+  const int64_t n = a.n_dev ? min(a.n, max((int64_t)0, *a.n_dev)) : a.n;
+  const bool take_all = n <= K;
+  uint32_t* hg = a.hist + seg * kHistBins;
+  const float* sc = a.scores + seg * a.n_pad;
+  float* lzs = reinterpret_cast<float*>(dyn + 2);
+  int32_t* lrs = reinterpret_cast<int32_t*>(dyn + 2 + cap);
+  int32_t* crow = reinterpret_cast<int32_t*>(dyn + 2 + 2 * cap);
+  float* czs = reinterpret_cast<float*>(crow + (K + a.n_extra));
+  const int64_t nbat = max((int64_t)1, (n + NW * SLICE - 1) / (NW * SLICE));
+
+  // 1. Filter. Wave 0 requests the histogram, every wave its first slice
+  // (loads clamped inside the segment's row; positions past n are not
+  // taken); wave 0 finds b* and whether the candidates fit.
+  float4 v[NV];
+  auto load_batch = [&](int64_t bt) {
+    const int64_t p0 = (bt * NW + wv) * SLICE;
+#pragma unroll
+    for (int u = 0; u < NV; ++u) v[u] = *reinterpret_cast<const float4*>(sc + min(p0 + 256 * u + 4 * lane, a.n_pad - 4));
+  };
+  u32x4 hv[8];
+  if (wv == 0 && !take_all) first_digit_load(hg, hv);
+  load_batch(0);
+  for (int i = tid; i < kHistBins; i += NT) h[i] = 0u;
+  if (wv == 0) {
+    uint32_t beyond = 0, cnt0 = 0;
+    const uint32_t bin = take_all ? 0u : first_digit_search(hv, (uint32_t)K, &beyond, &cnt0);
+    if (lane == 0) {
+      s_bin = (int)bin;
+      s_fit = (take_all ? (uint64_t)n : (uint64_t)beyond + cnt0) <= cap ? 1u : 0u;
+    }
+  }
+  __syncthreads();
+  if (s_fit == 0u) {
+    if (tid == 0) a.ovf[seg] = 1;
+    return;
+  }
+  if (tid == 0) a.ovf[seg] = 0;
+  if (wv == 0) {
+    // the histogram is read: zeroed for the next call
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(hg + (kHistBins - 32 - 32 * lane) + 4 * i) = z;
+  }
+  const uint32_t b0 = (uint32_t)s_bin;
+  uint32_t written = 0;
+  for (int64_t bt = 0;;) {
+    const int64_t p0 = (bt * NW + wv) * SLICE;
+    const int64_t p1 = min(n, p0 + SLICE);
+    // per chunk: each lane's taken positions as 4 bits, their count scanned
+    // over the wave (the order is lane, then element)
+    uint32_t key[NV][4], bits[NV], ex[NV], ct[NV];
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const float f[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      bits[u] = 0u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t p = p0 + 256 * u + 4 * lane + e;
+        key[u][e] = f2key(f[e]);
+        const bool take = p < p1 && (take_all || (key[u][e] >> (32 - kHistBits)) >= b0);
+        bits[u] |= (take ? 1u : 0u) << e;
+      }
+      const uint32_t c = (uint32_t)__popc(bits[u]);
+      const uint32_t incl = wave_incl_scan(c);
+      ex[u] = incl - c;
+      ct[u] = lane_read(incl, 63);
+      cnt += ct[u];
+    }
+    // the counts alternate between two arrays: one barrier per batch
+    if (lane == 0) s_wc[bt & 1][wv] = cnt;
+    __syncthreads();
+    uint32_t off = written, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const uint32_t c = s_wc[bt & 1][w];
+      off += w < wv ? c : 0u;
+      tot += c;
+    }
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t idx = off + ex[u] + (uint32_t)__popc(bits[u] & ((1u << e) - 1u));
+        if (((bits[u] >> e) & 1u) && idx < cap) {
+          lzs[idx] = key2f(key[u][e]);
+          lrs[idx] = (int32_t)(p0 + 256 * u + 4 * lane + e);
+        }
+      }
+      off += ct[u];
+    }
+    written += tot;
+    if (++bt == nbat) break;
+    load_batch(bt);
+  }
+
+  // 2. Select in LDS, with the static slots' scores and rows requested first
+  float zst[kFuseStatic];
+  int32_t rst[kFuseStatic];
+  if (a.n_extra > 0) {
+#pragma unroll
+    for (int u = 0; u < kFuseStatic; ++u) {
+      const int64_t p = a.n + min(tid + NT * u, a.n_extra - 1);
+      zst[u] = sc[p];
+      rst[u] = (int32_t)pos_to_row(a.tab, p);
+    }
+  }
+  __syncthreads();  // every candidate is in LDS
+  const uint32_t tot = select_tail_lds<true, NT>(a, seg, min(written, cap), lzs, lrs, h, s_wc, scr, tmp, &s_bin,
+                                                 &s_beyond, crow, czs);
+
+  // 3. Softmax . V over the chosen rows and the static slots
+  const uint32_t nk = min(tot, (uint32_t)K);
+#pragma unroll
+  for (int u = 0; u < kFuseStatic; ++u) {
+    const int j = tid + NT * u;
+    if (j < a.n_extra) {
+      crow[nk + j] = rst[u];
+      czs[nk + j] = zst[u];
+    }
+  }
+  tail_softmax_v<T, NT>(a, seg, crow, czs, nk + (uint32_t)a.n_extra, reinterpret_cast<float(*)[kHeadDim]>(dyn + 2),
+                        reinterpret_cast<float*>(tmp));
 }
 
 

@@ -137,6 +137,31 @@ def test_batch_and_ragged_static(ops):
     log(f"[ragged static] {w.q.shape[0] * w.H_q} heads ok")
 
 
+def test_batch_static_half_workgroups(ops):
+    """c4 layout over 12,288 rows with a 640-row static window: 512 heads of
+    11,648 dynamic positions, each filtered, selected and attended (its
+    static slots included) in a half-size workgroup, two per CU; every
+    (b, h) against the oracle."""
+    if 2 * torch.cuda.get_device_properties(0).multi_processor_count > 512:
+        pytest.skip("half-size workgroups need at least twice as many heads as CUs")
+    log("case static c4 layout B=16 L=12288 K=1024, half-size workgroups")
+    w = make_workload(4, L=12288)
+    ranges = [(128, 11776)]
+    static = [(0, 128), (11776, 12288)]
+    timer = ops.KernelTimer()
+    try:
+        idx, o, lse = run_static(ops, w, ranges, static, 1024)
+        assert timer.read("topk_filter_lds_sv")[1] == 1
+    finally:
+        timer.close()
+    for b in range(w.q.shape[0]):
+        for h in range(w.H_q):
+            r, rows, om, lm = oracle_step(w, b, h, ranges, static, 1024)
+            check_index_set(idx[b, h], rows, r["z"], r["zk"], 1024)
+            check_out(o[b, h], lse[b, h], om, lm, False, f"half static ({b},{h})")
+    log(f"[half static] {w.q.shape[0] * w.H_q} heads ok")
+
+
 def test_graph_replays_match_eager(ops):
     """The one-pass step captured in a HIP graph: several replays, with eager
     calls and synchronisations between them, each equal to the eager result

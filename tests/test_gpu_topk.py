@@ -19,8 +19,9 @@ def ops(stdk):
     return ops
 
 
-def run(ops, w, ranges, K, **kw):
-    q = torch.from_numpy(w.q if w.q.ndim == 3 else w.q[:, :, 0]).cuda()
+def run(ops, w, ranges, K, q=None, **kw):
+    qa = w.q if q is None else q
+    q = torch.from_numpy(np.ascontiguousarray(qa if qa.ndim == 3 else qa[:, :, 0])).cuda()
     k, v = dev_kv(w)
     idx, o, lse = ops.topk_attn_decode(q, k, v, ranges, K, w.scale, **kw)
     torch.cuda.synchronize()
@@ -212,6 +213,47 @@ def test_one_workgroup_per_head_ties_and_nan(ops, K):
     assert sel.shape[0] == K and np.all(np.diff(sel) > 0)
     keep = np.ones((w.B, w.H_q), bool)
     keep[3, 5] = False
+    for x, y in ((idx, idx2), (o, o2), (lse, lse2)):
+        assert np.array_equal(x[keep], y[keep])
+
+
+@pytest.mark.parametrize("K", [64, 3000])
+def test_half_workgroups_ties_nan_overflow(ops, K):
+    """512 heads of 9,000 positions, twice as many heads as CUs: each head
+    is filtered, selected and attended in a half-size workgroup (two per
+    CU) with its candidates in LDS. Keys from a 6-row codebook (every score
+    ties with about 1,500 others): the index sets must equal the oracle's
+    exactly. A NaN in one query makes all 9,000 positions its head's
+    candidates, more than that LDS holds: the head is flagged and taken by
+    the full-size kernel, its o and lse are NaN, and every other head is
+    bit-identical to the run without the NaN."""
+    from workloads import make_multi_query
+    if 2 * torch.cuda.get_device_properties(0).multi_processor_count > 512:
+        pytest.skip("half-size workgroups need at least twice as many heads as CUs")
+    w = make_multi_query(16, 32, 4, 1, 9000, "bf16", codebook=6, tag=46)
+    w.q = np.ascontiguousarray(w.q[:, :, 0])
+    ranges = [(0, 9000)]
+    log(f"case half-size workgroups, codebook ties K={K}")
+    qn = w.q.copy()
+    qn[11, 7, 40] = np.nan
+    timer = ops.KernelTimer()
+    try:
+        idx, o, lse = run(ops, w, ranges, K)
+        idx2, o2, lse2 = run(ops, w, ranges, K, q=qn)
+        assert timer.read("topk_filter_lds_sv")[1] == 2
+        assert timer.read("topk_filter_select_sv")[1] == 2
+    finally:
+        timer.close()
+    want = ref.topk_attn_decode(w.q, w.k, w.v, ranges, K, w.scale)
+    assert np.array_equal(idx, want["idx"])
+    for b in range(w.B):
+        for h in range(w.H_q):
+            check_out(o[b, h], lse[b, h], want["o"][b, h], want["lse"][b, h], False, f"half K={K} ({b},{h})")
+    assert np.all(np.isnan(o2[11, 7])) and np.isnan(lse2[11, 7])
+    sel = idx2[11, 7][idx2[11, 7] >= 0]
+    assert sel.shape[0] == K and np.all(np.diff(sel) > 0)
+    keep = np.ones((w.B, w.H_q), bool)
+    keep[11, 7] = False
     for x, y in ((idx, idx2), (o, o2), (lse, lse2)):
         assert np.array_equal(x[keep], y[keep])
 
