@@ -438,7 +438,8 @@ int32_t stdk_inject_launch_failure(int32_t after_launches);
 /* Measurement aid: the plain HBM read rate of the key scan's partition.
  * Reads every byte of n_groups regions once: region g is group_bytes bytes
  * from base + g * group_stride_bytes, streamed by wg_per_group workgroups
- * of 512 threads that each take an equal contiguous share (16-byte loads,
+ * of 512 threads that each take an equal contiguous share (16-byte
+ * non-temporal loads, as the scan issues its key loads,
  * two sets of four in flight), the way k_scan splits a KV head's rows over
  * its workgroups. Nothing is written except, in a case that does not occur
  * for real data (an XOR of all words equal to a fixed constant), one word

@@ -1613,18 +1613,19 @@ __global__ __launch_bounds__(512) void hbm_read(const char* base, int64_t stride
   u32x4 acc = {0u, 0u, 0u, 0u};
   u32x4 v[2][4];
   int64_t off = b0 + (int64_t)threadIdx.x * 16;
-  // loads past the share are clamped onto its last 16 bytes
+  // non-temporal loads, as the key scan issues; loads past the share are
+  // clamped onto its last 16 bytes
 #pragma unroll
-  for (int u = 0; u < 4; ++u) v[0][u] = load16(p + min(off + u * kStep, b1 - 16));
+  for (int u = 0; u < 4; ++u) v[0][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + min(off + u * kStep, b1 - 16)));
   for (; off < b1; off += 8 * kStep) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[1][u] = load16(p + min(off + (4 + u) * kStep, b1 - 16));
+    for (int u = 0; u < 4; ++u) v[1][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + min(off + (4 + u) * kStep, b1 - 16)));
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < 4; ++u) acc ^= v[0][u];
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[0][u] = load16(p + min(off + (8 + u) * kStep, b1 - 16));
+    for (int u = 0; u < 4; ++u) v[0][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + min(off + (8 + u) * kStep, b1 - 16)));
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < 4; ++u) acc ^= v[1][u];

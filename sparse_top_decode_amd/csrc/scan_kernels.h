@@ -196,35 +196,14 @@ STDK_DEV int lane_perm(int c, bool* out_lane) {
   return pi;
 }
 
-// Wait until at most N of this wave's key loads are in flight (vmcnt(N),
-// N < 16; expcnt and lgkmcnt left at their maximum).
-template <int N>
-STDK_DEV void wait_vm() {
-  static_assert(N >= 0 && N < 16, "vmcnt");
-  __builtin_amdgcn_s_waitcnt(N | 0x0F70);
-}
-
-// The key rows are requested with explicit load instructions that the
-// compiler's wait insertion does not track, and each register set is waited
-// for explicitly before it is used (wait_vm, then an empty asm that "writes"
-// the set's registers so that no use is scheduled above the wait). The
-// compiler, left to itself, merged the loop's entry and back edges into a
-// wait for every outstanding load at the top of each iteration, which left
-// one register set in flight instead of two.
-STDK_DEV void load16_async(u32x4& dst, const char* p, std::integral_constant<int, 0>) {
-  __asm__ volatile("global_load_dwordx4 %0, %1, off" : "=v"(dst) : "v"(p));
-}
+// Key rows are read with non-temporal 16-byte loads: each row is read once
+// per call, and on this part the non-temporal form streams measurably faster
+// than the default cache policy.
 template <int OFF>
-STDK_DEV void load16_async(u32x4& dst, const char* p, std::integral_constant<int, OFF>) {
-  __asm__ volatile("global_load_dwordx4 %0, %1, off offset:%2" : "=v"(dst) : "v"(p), "i"(OFF));
+STDK_DEV void load16_nt(u32x4& dst, const char* p, std::integral_constant<int, OFF>) {
+  dst = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + OFF));
 }
-STDK_DEV void load4_async(float& dst, const float* p) {
-  __asm__ volatile("global_load_dword %0, %1, off" : "=v"(dst) : "v"(p));
-}
-template <typename X>
-STDK_DEV void arrived(X& x) {
-  __asm__ volatile("" : "+v"(x));
-}
+STDK_DEV void load4_nt(float& dst, const float* p) { dst = __builtin_nontemporal_load(p); }
 
 template <typename T, int G>
 __global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
@@ -303,21 +282,11 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
     for (int s = 0; s < UR; ++s) {
       const int64_t p = min(it.base + (int64_t)(w * UR + (s ^ rowperm)) * RPW + rg, it.pe - 1);
       const char* rp = kb + (p + it.ro) * ROWB;
-      load16_async(kw[s][0], rp, std::integral_constant<int, 0>{});
-      if constexpr (NCH > 1) load16_async(kw[s][1], rp, std::integral_constant<int, LPR * 16>{});
-      if constexpr (NCH > 2) load16_async(kw[s][2], rp, std::integral_constant<int, 2 * LPR * 16>{});
-      if constexpr (NCH > 3) load16_async(kw[s][3], rp, std::integral_constant<int, 3 * LPR * 16>{});
-      if constexpr (kQ8) load4_async(sc[s], ksb + p + it.ro);
-    }
-  };
-  // the set's loads have arrived once at most NL newer loads are in flight
-  auto wait_set = [&](u32x4 (&kw)[UR][NCH], float (&sc)[UR]) {
-    wait_vm<NL>();
-#pragma unroll
-    for (int s = 0; s < UR; ++s) {
-#pragma unroll
-      for (int k = 0; k < NCH; ++k) arrived(kw[s][k]);
-      if constexpr (kQ8) arrived(sc[s]);
+      load16_nt(kw[s][0], rp, std::integral_constant<int, 0>{});
+      if constexpr (NCH > 1) load16_nt(kw[s][1], rp, std::integral_constant<int, LPR * 16>{});
+      if constexpr (NCH > 2) load16_nt(kw[s][2], rp, std::integral_constant<int, 2 * LPR * 16>{});
+      if constexpr (NCH > 3) load16_nt(kw[s][3], rp, std::integral_constant<int, 3 * LPR * 16>{});
+      if constexpr (kQ8) load4_nt(sc[s], ksb + p + it.ro);
     }
   };
   static_assert(NCH <= 4 && NL < 16, "load shape");
@@ -445,7 +414,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
   // would not fit beside it, or at the end (with the whole block staged,
   // that is once, after the last iteration)
   auto after = [&](const Iter& it, const Iter& nx) {
-    if (staged && (!nx.ok || nx.base + IT - cstart > a.stage_rows)) {
+    if (staged && it.ok && (!nx.ok || nx.base + IT - cstart > a.stage_rows)) {
       flush(cstart, min(it.base + IT, it.pe));
       cstart = nx.base;
     }
@@ -453,28 +422,22 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
   // Two register sets: each is requested again as soon as it has been
   // consumed, so while one is consumed the other is in flight, and while a
   // wave waits both are. An iteration past the end is issued clamped and
-  // scores nothing.
+  // scores nothing. Both sets are requested before the exit test, so every
+  // path into the loop head has them in the same order and the compiler's
+  // wait for one set leaves the other in flight.
   for (;;) {
-    wait_set(kw[0], ksc[0]);
     consume(d0, cstart, kw[0], ksc[0]);
-    __builtin_amdgcn_sched_barrier(0);
     after(d0, d1);
-    if (!d1.ok) break;
-    d0 = advance(d1);
-    issue(d0, kw[0], ksc[0]);
-    __builtin_amdgcn_sched_barrier(0);
-    wait_set(kw[1], ksc[1]);
+    const Iter d2 = advance(d1);
+    issue(d2, kw[0], ksc[0]);
     consume(d1, cstart, kw[1], ksc[1]);
-    __builtin_amdgcn_sched_barrier(0);
-    after(d1, d0);
-    if (!d0.ok) break;
-    d1 = advance(d0);
-    issue(d1, kw[1], ksc[1]);
-    __builtin_amdgcn_sched_barrier(0);
+    after(d1, d2);
+    const Iter d3 = advance(d2);
+    issue(d3, kw[1], ksc[1]);
+    if (!d2.ok) break;
+    d0 = d2;
+    d1 = d3;
   }
-  // the clamped loads past the end are still in flight: drain them before
-  // their registers are reused
-  wait_vm<0>();
   __syncthreads();
   // Add the block histogram to the global one: all LDS reads of a thread are
   // issued before the first wait, then one atomic per non-empty bin. Heads

@@ -904,14 +904,24 @@ STDK_DEV void fsel_body(const SelectArgs& a) {
     if (!take_all && !lds_mode) {
       // 16-byte loads from the device's coherence point (the bins were
       // added there by every workgroup of the segment), all issued before
-      // one wait
+      // one wait in the same asm statement, so no output register is read
+      // or reused while its load is in flight
       const uint32_t* base = h1g + (kHistBins - 32 - 32 * lane);
       u32x4 hv[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) __asm__ volatile("global_load_dwordx4 %0, %1, off sc1" : "=v"(hv[i]) : "v"(base + 4 * i));
-      wait_vm<0>();
-#pragma unroll
-      for (int i = 0; i < 8; ++i) arrived(hv[i]);
+      __asm__ volatile(
+          "global_load_dwordx4 %0, %8, off sc1\n"
+          "global_load_dwordx4 %1, %8, off offset:16 sc1\n"
+          "global_load_dwordx4 %2, %8, off offset:32 sc1\n"
+          "global_load_dwordx4 %3, %8, off offset:48 sc1\n"
+          "global_load_dwordx4 %4, %8, off offset:64 sc1\n"
+          "global_load_dwordx4 %5, %8, off offset:80 sc1\n"
+          "global_load_dwordx4 %6, %8, off offset:96 sc1\n"
+          "global_load_dwordx4 %7, %8, off offset:112 sc1\n"
+          "s_waitcnt vmcnt(0)"
+          : "=&v"(hv[0]), "=&v"(hv[1]), "=&v"(hv[2]), "=&v"(hv[3]), "=&v"(hv[4]), "=&v"(hv[5]), "=&v"(hv[6]),
+            "=&v"(hv[7])
+          : "v"(base)
+          : "memory");
       uint32_t beyond1 = 0, cnt1 = 0;
       const uint32_t b1 = first_digit_search(hv, (uint32_t)K - s_beyond, &beyond1, &cnt1);
       if (lane == 0) {
