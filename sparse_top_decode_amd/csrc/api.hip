@@ -199,23 +199,33 @@ struct DevInfo {
   bool init = false;
   int max_lds = 65536;
   int n_cu = 256;
-  int scan_occ[3][STDK_MAX_GROUP + 1] = {};  // resident k_scan workgroups per CU, by (fp32 / bf16 / int8, G)
+  int scan_occ[3][STDK_MAX_GROUP + 1] = {};     // resident k_scan workgroups per CU, by (fp32 / bf16 / int8, G)
+  int scan_static[3][STDK_MAX_GROUP + 1] = {};  // static LDS bytes of k_scan, same index
 };
 std::mutex g_dev_mu;
 DevInfo g_dev[64];
 
+// Resident workgroups per CU of k_scan<T, G>, and its static LDS bytes; the
+// staged scores may use the rest of the CU's LDS (up to kScanStageMax).
 template <typename T, int G>
-int occ_of() {
-  (void)hipFuncSetAttribute((const void*)k_scan<T, G>, hipFuncAttributeMaxDynamicSharedMemorySize, kScanStageMax);
+void occ_of(int max_lds, int* occ, int* stat) {
+  hipFuncAttributes fa{};
+  int st = G * kHistBins * 4;
+  if (hipFuncGetAttributes(&fa, (const void*)k_scan<T, G>) == hipSuccess) st = (int)fa.sharedSizeBytes;
+  (void)hipFuncSetAttribute((const void*)k_scan<T, G>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            std::max(0, std::min(kScanStageMax, max_lds - st)));
   int nb = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_scan<T, G>, kScanThreads, 0) != hipSuccess || nb < 1) nb = 1;
-  return nb;
+  *occ = nb;
+  *stat = st;
 }
 
 template <typename T>
-void occ_row(int* o) {
-  o[1] = occ_of<T, 1>(); o[2] = occ_of<T, 2>(); o[3] = occ_of<T, 3>(); o[4] = occ_of<T, 4>();
-  o[5] = occ_of<T, 5>(); o[6] = occ_of<T, 6>(); o[7] = occ_of<T, 7>(); o[8] = occ_of<T, 8>();
+void occ_row(int max_lds, int* o, int* st) {
+  occ_of<T, 1>(max_lds, o + 1, st + 1); occ_of<T, 2>(max_lds, o + 2, st + 2);
+  occ_of<T, 3>(max_lds, o + 3, st + 3); occ_of<T, 4>(max_lds, o + 4, st + 4);
+  occ_of<T, 5>(max_lds, o + 5, st + 5); occ_of<T, 6>(max_lds, o + 6, st + 6);
+  occ_of<T, 7>(max_lds, o + 7, st + 7); occ_of<T, 8>(max_lds, o + 8, st + 8);
 }
 
 int32_t dev_info(DevInfo** out) {
@@ -233,9 +243,9 @@ int32_t dev_info(DevInfo** out) {
     e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return fail(STDK_EHIP, "hipDeviceGetAttribute: %s", hipGetErrorString(e));
     d.n_cu = v;
-    occ_row<float>(d.scan_occ[0]);
-    occ_row<uint16_t>(d.scan_occ[1]);
-    occ_row<int8_t>(d.scan_occ[2]);
+    occ_row<float>(d.max_lds, d.scan_occ[0], d.scan_static[0]);
+    occ_row<uint16_t>(d.max_lds, d.scan_occ[1], d.scan_static[1]);
+    occ_row<int8_t>(d.max_lds, d.scan_occ[2], d.scan_static[2]);
     const int dyn_max = std::max(0, d.max_lds - (int)kSelStaticLds);
     (void)hipFuncSetAttribute((const void*)topk_filter_select, hipFuncAttributeMaxDynamicSharedMemorySize, dyn_max);
     (void)hipFuncSetAttribute((const void*)topk_filter_select_sv<uint16_t>, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -438,14 +448,14 @@ RangeTab make_tab(const int64_t* ranges, int n_ranges, int64_t* n_total) {
 template <typename T>
 int scan_rows_iter(int G) {
   switch (G) {
-    case 1: return ScanShape<T, 1>::ROWS_ITER;
-    case 2: return ScanShape<T, 2>::ROWS_ITER;
-    case 3: return ScanShape<T, 3>::ROWS_ITER;
-    case 4: return ScanShape<T, 4>::ROWS_ITER;
-    case 5: return ScanShape<T, 5>::ROWS_ITER;
-    case 6: return ScanShape<T, 6>::ROWS_ITER;
-    case 7: return ScanShape<T, 7>::ROWS_ITER;
-    default: return ScanShape<T, 8>::ROWS_ITER;
+    case 1: return scan_iter_rows<T, 1>();
+    case 2: return scan_iter_rows<T, 2>();
+    case 3: return scan_iter_rows<T, 3>();
+    case 4: return scan_iter_rows<T, 4>();
+    case 5: return scan_iter_rows<T, 5>();
+    case 6: return scan_iter_rows<T, 6>();
+    case 7: return scan_iter_rows<T, 7>();
+    default: return scan_iter_rows<T, 8>();
   }
 }
 
@@ -613,7 +623,7 @@ int32_t run_exact_select(const Geo& g, const TopkWs& w, char* ws, const float* q
     // beside the histogram (row stride padded so that the G rows start on
     // different banks)
     const int occ = di->scan_occ[ti][g.G];
-    const int64_t lds_free = std::min<int64_t>(kScanStageMax, (int64_t)di->max_lds / occ - (int64_t)g.G * kHistBins * 4 - 1024);
+    const int64_t lds_free = std::min<int64_t>(kScanStageMax, (int64_t)di->max_lds / occ - di->scan_static[ti][g.G] - 1024);
     const int64_t chunk = std::min<int64_t>(rpb, (lds_free / (4 * g.G) - 16) / ri * ri);
     if (chunk >= ri) {
       a.stage_rows = (int32_t)chunk;

@@ -297,4 +297,51 @@ STDK_DEV bool arrive_last(uint32_t* counter, uint32_t total, uint32_t* s_flag) {
 
 STDK_DEV u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+STDK_DEV bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Splits 8 fp32 values into bf16 values (rounded to nearest even by the
+// hardware conversion) and bf16 remainders, packed two per word in element
+// order (element 2i in the low half of word i). The remainder x - hi is exact
+// in fp32, so x = hi + lo + r with |r| <= 2^-17 |x|.
+STDK_DEV void split_bf16x8(const float (&x)[8], u32x4& hi, u32x4& lo) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  uint32_t hw[4], lw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x[2 * i], x[2 * i + 1]}, bf16x2));
+    const float r0 = x[2 * i] - __uint_as_float(hb << 16);
+    const float r1 = x[2 * i + 1] - __uint_as_float(hb & 0xFFFF0000u);
+    hw[i] = hb;
+    lw[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{r0, r1}, bf16x2));
+  }
+  hi = u32x4{hw[0], hw[1], hw[2], hw[3]};
+  lo = u32x4{lw[0], lw[1], lw[2], lw[3]};
+}
+
+// Splits 8 fp32 values into three bf16 parts, x = hi + mid + lo + r: each
+// part is the bf16 rounding of what the earlier parts leave (an exact fp32
+// difference), so the three carry all 24 bits of an fp32 significand and
+// |r| <= 2^-27 |x|.
+STDK_DEV void split3_bf16x8(const float (&x)[8], u32x4& hi, u32x4& mid, u32x4& lo) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  uint32_t w[3][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float r0 = x[2 * i], r1 = x[2 * i + 1];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{r0, r1}, bf16x2));
+      w[k][i] = hb;
+      r0 -= __uint_as_float(hb << 16);
+      r1 -= __uint_as_float(hb & 0xFFFF0000u);
+    }
+  }
+  hi = u32x4{w[0][0], w[0][1], w[0][2], w[0][3]};
+  mid = u32x4{w[1][0], w[1][1], w[1][2], w[1][3]};
+  lo = u32x4{w[2][0], w[2][1], w[2][2], w[2][3]};
+}
+
 }  // namespace stdk

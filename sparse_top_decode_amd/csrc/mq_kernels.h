@@ -38,7 +38,6 @@
 
 namespace stdk {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float mq_f32x4 __attribute__((ext_vector_type(4)));
 
@@ -82,28 +81,11 @@ struct MqArgs {
   RangeTab tab;
 };
 
-// Splits 8 fp32 values into bf16 values (rounded to nearest even by the
-// hardware conversion) and bf16 remainders, packed two per word in element
-// order (element 2i in the low half of word i). The remainder x - hi is exact
-// in fp32.
+// Splits 8 fp32 values into bf16 high parts and bf16 remainders (split_bf16x8).
 STDK_DEV void split8(const mq_f32x4& x0, const mq_f32x4& x1, u32x4& hi, u32x4& lo) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
   const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-  uint32_t hw[4], lw[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x[2 * i], x[2 * i + 1]}, bf16x2));
-    const float r0 = x[2 * i] - __uint_as_float(hb << 16);
-    const float r1 = x[2 * i + 1] - __uint_as_float(hb & 0xFFFF0000u);
-    hw[i] = hb;
-    lw[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{r0, r1}, bf16x2));
-  }
-  hi = u32x4{hw[0], hw[1], hw[2], hw[3]};
-  lo = u32x4{lw[0], lw[1], lw[2], lw[3]};
+  split_bf16x8(x, hi, lo);
 }
-
-STDK_DEV bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
 
 STDK_DEV int64_t min64(int64_t x, int64_t y) { return x < y ? x : y; }
 

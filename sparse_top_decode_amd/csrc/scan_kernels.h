@@ -110,6 +110,7 @@ struct ScanArgs {
 };
 
 constexpr int kScanThreads = 512;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Work shape of the scan for row type T and G query heads per KV head.
 //  - LPR lanes read one key row (8, or 16 when G > 4 to halve the query
@@ -205,8 +206,9 @@ STDK_DEV void load16_nt(u32x4& dst, const char* p, std::integral_constant<int, O
 }
 STDK_DEV void load4_nt(float& dst, const float* p) { dst = __builtin_nontemporal_load(p); }
 
+// The scan on the vector ALUs (fp32 rows and int8 codes).
 template <typename T, int G>
-__global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
+STDK_DEV void scan_valu_body(const ScanArgs& a) {
   using Sh = ScanShape<T, G>;
   constexpr bool kQ8 = sizeof(T) == 1;  // int8 codes: score = scale * row scale * (q . code)
   constexpr int GP = Sh::GP, LPR = Sh::LPR, NCH = Sh::NCH, EPC = Sh::EPC, E = Sh::E, UR = Sh::UR, V = Sh::V;
@@ -456,6 +458,252 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
       if (vals[e] != 0u && ((act >> hh) & 1u)) atomicAdd(&a.hist[(seg0 + hh) * kHistBins + (i % kHistBins)], vals[e]);
     }
   }
+}
+
+
+// bf16 rows on the matrix cores. The G dot products of a key row are a
+// 16-row x 128 x 16-column product tile (v_mfma_f32_16x16x32_bf16, four
+// steps of 32 along the head dimension): the A operand is 16 key rows, the B
+// operand the group's queries (columns past G are zero). Lane l of a wave
+// supplies A row l%16 and B column l%16 with k = 8*(l/16) + i of each step;
+// result register r of lane l is key row 4*(l/16) + r, query head l%16.
+// Step s, lane group g uses head-dimension elements 32*s + 8*g + i (any
+// fixed order of the elements gives the same dot product).
+//
+// Each query is split into three bf16 parts that together hold its fp32
+// significand (|q - hi - mid - lo| <= 2^-27 |q|) and every part is
+// multiplied (three products per step). Products of bf16 values are exact in
+// fp32 and the matrix core accumulates in fp32, so a score matches the fp32
+// dot product to fp32 rounding. (Two parts, |q - hi - lo| <= 2^-17 |q|, were
+// measured to reorder rows whose scores differ by about 1e-6.)
+//
+// The key rows are loaded the way a plain read streams them: each load
+// instruction of a wave takes 1 KB of consecutive bytes (4 rows, 16 lanes
+// per row), which reads HBM faster than handing each lane its own row. The
+// wave then transposes its 16-row tile through its own LDS region (rows 272
+// bytes apart, so that both the row-wise stores and the column-wise reads
+// fall on distinct banks) into the product's operand layout.
+constexpr int kMfTiles = 2;                                       // 16-row tiles per wave and register set
+constexpr int kMfRowsIter = (kScanThreads / 64) * 16 * kMfTiles;  // rows per workgroup iteration
+constexpr int kMfRowStride = 272;                                 // LDS bytes per transposed key row
+constexpr int kMfTileLds = (kScanThreads / 64) * 16 * kMfRowStride;
+
+template <int G>
+STDK_DEV void scan_mf_body(const ScanArgs& a) {
+  static_assert(G >= 1 && G <= 16, "one product tile holds the group's query heads");
+  constexpr int IT = kMfRowsIter, ROWB = 256;
+  __shared__ __attribute__((aligned(16))) uint32_t lh[G * kHistBins];
+  __shared__ __attribute__((aligned(16))) char tl[kMfTileLds];
+  extern __shared__ __attribute__((aligned(16))) float sst[];  // staged scores, when a.stage_stride > 0
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lo = lane & 15, hi = lane >> 4;
+  const int group = blockIdx.x / a.blocks_per_group;
+  const int blk = blockIdx.x % a.blocks_per_group;
+  const int b = group / a.Hkv, hkv = group % a.Hkv;
+  const int64_t seg0 = (int64_t)b * a.Hq + (int64_t)hkv * G;
+  uint32_t act = (1u << G) - 1u;  // heads of this group that take part
+  if (a.head_active) {
+    act = 0u;
+#pragma unroll
+    for (int h = 0; h < G; ++h) act |= (a.head_active[seg0 + h] != 0 ? 1u : 0u) << h;
+    if (act == 0u) return;
+  }
+  const char* kb = a.k + (int64_t)b * a.stride_b_bytes + (int64_t)hkv * a.stride_h_bytes + lo * 16;
+  int64_t n_all = a.n, n_hist = a.n_hist;
+  if (a.n_dev) {
+    const int64_t nd = max((int64_t)0, *a.n_dev);
+    n_all = min(n_all, nd);
+    n_hist = min(n_hist, nd);
+  }
+  const int64_t p_beg = (int64_t)blk * a.rows_per_block;
+  const int64_t p_end = min(n_all, p_beg + a.rows_per_block);
+  if (p_beg >= p_end) return;  // no row of this workgroup's block is in use
+  // An iteration covers positions [base, base + IT) of the piece [.., pe) of
+  // one range, whose rows are position + ro; wave w takes the tiles at
+  // base + 16 * (w * kMfTiles + t). Past the block's end `ok` is false: the
+  // iteration keeps the last piece (its loads stay clamped to a valid row)
+  // and scores nothing.
+  struct Iter {
+    int64_t base, pe, ro;
+    bool ok;
+  };
+  auto piece_at = [&](int64_t p) -> Iter {
+    Iter it{p, a.tab.pos0[1], a.tab.row0[0] - a.tab.pos0[0], true};
+#pragma unroll
+    for (int i = 1; i < kMaxRanges; ++i) {
+      if (i >= a.tab.n) break;
+      if (p >= a.tab.pos0[i]) {
+        it.pe = a.tab.pos0[i + 1];
+        it.ro = a.tab.row0[i] - a.tab.pos0[i];
+      }
+    }
+    it.pe = min(it.pe, p_end);
+    return it;
+  };
+  auto advance = [&](const Iter& it) -> Iter {
+    const int64_t nb = it.base + IT;
+    if (nb < it.pe) return Iter{nb, it.pe, it.ro, it.ok};
+    if (it.ok && it.pe < p_end) return piece_at(it.pe);
+    return Iter{p_end + IT, it.pe, it.ro, false};
+  };
+  // load s of tile t: rows 4s .. 4s + 3 of the tile, lane l taking bytes
+  // 16*(l%16) .. + 16 of row 4s + l/16 (loads past the piece are clamped to
+  // its last row and their results dropped)
+  auto issue = [&](const Iter& it, u32x4 (&kw)[kMfTiles][4]) {
+#pragma unroll
+    for (int t = 0; t < kMfTiles; ++t)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int64_t p = min(it.base + (int64_t)(w * kMfTiles + t) * 16 + 4 * s + hi, it.pe - 1);
+        kw[t][s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + (p + it.ro) * ROWB));
+      }
+  };
+  u32x4 kw[2][kMfTiles][4];
+
+  // B operand: query head lo (zero past G), elements 32*s + 8*hi + i
+  u32x4 qh[4], qm[4], ql[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    float x[8];
+    if (lo < G) {
+      const float4* qp = reinterpret_cast<const float4*>(a.q + (seg0 + lo) * kHeadDim + 32 * s + 8 * hi);
+      const float4 v0 = qp[0], v1 = qp[1];
+      x[0] = v0.x; x[1] = v0.y; x[2] = v0.z; x[3] = v0.w;
+      x[4] = v1.x; x[5] = v1.y; x[6] = v1.z; x[7] = v1.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = 0.f;
+    }
+    split3_bf16x8(x, qh[s], qm[s], ql[s]);
+  }
+  // both register sets of key rows are requested right after the query
+  Iter d0 = piece_at(p_beg);
+  Iter d1 = advance(d0);
+  issue(d0, kw[0]);
+  issue(d1, kw[1]);
+  for (int i = tid; i < G * kHistBins; i += kScanThreads) lh[i] = 0u;
+  // LDS-only barrier: the key loads stay in flight
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+
+  char* my = tl + w * 16 * kMfRowStride;
+  auto consume = [&](const Iter& it, int64_t cstart, const u32x4 (&kv)[kMfTiles][4]) {
+#pragma unroll
+    for (int t = 0; t < kMfTiles; ++t) {
+      // The wave's own region: its LDS operations complete in issue order,
+      // so only the compiler has to be kept from moving them across each
+      // other (the empty asm statements).
+      __asm__ volatile("" ::: "memory");
+#pragma unroll
+      for (int s = 0; s < 4; ++s) *reinterpret_cast<u32x4*>(my + (4 * s + hi) * kMfRowStride + 16 * lo) = kv[t][s];
+      __asm__ volatile("" ::: "memory");
+      u32x4 e[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) e[s] = *reinterpret_cast<const u32x4*>(my + lo * kMfRowStride + (4 * s + hi) * 16);
+      __asm__ volatile("" ::: "memory");
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(e[s]), as_bf16x8(ql[s]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(e[s]), as_bf16x8(qm[s]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(e[s]), as_bf16x8(qh[s]), acc, 0, 0, 0);
+      }
+      if (lo < G) {
+        const int64_t p0 = it.base + (int64_t)(w * kMfTiles + t) * 16 + 4 * hi;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t p = p0 + r;
+          if (p < it.pe) {
+            const float val = acc[r] * a.scale;
+            if (a.stage_stride > 0) sst[lo * a.stage_stride + (p - cstart)] = val;
+            else __builtin_nontemporal_store(val, &a.scores[(seg0 + lo) * a.n_pad + p]);
+            if (p < n_hist) atomicAdd(&lh[lo * kHistBins + (f2key(val) >> (32 - kHistBits))], 1u);
+          }
+        }
+      }
+    }
+  };
+  // Staged scores: a chunk of consecutive positions [c0, c1) goes out once
+  // every wave has scored it, as coalesced non-temporal stores; LDS-only
+  // barriers around it keep the key loads in flight.
+  auto flush = [&](int64_t c0, int64_t c1) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    const int len = (int)(c1 - c0);
+    const int nvec = (c0 & 3) == 0 ? len / 4 : 0;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      if (!((act >> h) & 1u)) continue;
+      float* dst = a.scores + (seg0 + h) * a.n_pad + c0;
+      const float* srcp = sst + h * a.stage_stride;
+      for (int i = tid; i < nvec; i += kScanThreads)
+        __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(srcp + 4 * i), reinterpret_cast<f32x4*>(dst + 4 * i));
+      for (int i = 4 * nvec + tid; i < len; i += kScanThreads) __builtin_nontemporal_store(srcp[i], dst + i);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  };
+  const bool staged = a.stage_stride > 0;
+  int64_t cstart = d0.base;
+  auto after = [&](const Iter& it, const Iter& nx) {
+    if (staged && it.ok && (!nx.ok || nx.base + IT - cstart > a.stage_rows)) {
+      flush(cstart, min(it.base + IT, it.pe));
+      cstart = nx.base;
+    }
+  };
+  // Two register sets, each requested again as soon as it has been consumed;
+  // both are requested before the exit test, so that the compiler's wait for
+  // one set leaves the other in flight.
+  for (;;) {
+    consume(d0, cstart, kw[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    after(d0, d1);
+    const Iter d2 = advance(d1);
+    issue(d2, kw[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    consume(d1, cstart, kw[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    after(d1, d2);
+    const Iter d3 = advance(d2);
+    issue(d3, kw[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (!d2.ok) break;
+    d0 = d2;
+    d1 = d3;
+  }
+  __syncthreads();
+  // Add the block histogram to the global one (one atomic per non-empty bin
+  // of a head that takes part).
+  constexpr int NV = G * kHistBins / 4 / kScanThreads;
+  u32x4 hv[NV];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) hv[k] = *reinterpret_cast<const u32x4*>(&lh[4 * (k * kScanThreads + tid)]);
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const uint32_t vals[4] = {hv[k].x, hv[k].y, hv[k].z, hv[k].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 4 * (k * kScanThreads + tid) + e;
+      const int hh = i / kHistBins;
+      if (vals[e] != 0u && ((act >> hh) & 1u)) atomicAdd(&a.hist[(seg0 + hh) * kHistBins + (i % kHistBins)], vals[e]);
+    }
+  }
+}
+
+// Rows per workgroup iteration of the scan for row type T and group size G.
+template <typename T, int G>
+constexpr int scan_iter_rows() {
+  return std::is_same<T, uint16_t>::value ? kMfRowsIter : ScanShape<T, G>::ROWS_ITER;
+}
+
+template <typename T, int G>
+__global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
+  if constexpr (std::is_same<T, uint16_t>::value) scan_mf_body<G>(a);
+  else scan_valu_body<T, G>(a);
 }
 
 }  // namespace stdk

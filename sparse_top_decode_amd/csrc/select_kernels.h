@@ -787,7 +787,10 @@ STDK_DEV void fsel_body(const SelectArgs& a) {
     auto load_batch = [&](int bt) {
       const int64_t p0 = (int64_t)blockIdx.x * span + ((int64_t)bt * kSelectWaves + wv) * a.slice;
 #pragma unroll
-      for (int u = 0; u < NV; ++u) v[u] = *reinterpret_cast<const float4*>(sc + min(p0 + 256 * u + 4 * lane, a.n_pad - 4));
+      for (int u = 0; u < NV; ++u) {
+      const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sc + min(p0 + 256 * u + 4 * lane, a.n_pad - 4)));
+      v[u] = make_float4(x[0], x[1], x[2], x[3]);
+    }
     };
     u32x4 hv[8];
     if (wv == 0 && !take_all) first_digit_load(hg, hv);
@@ -1068,7 +1071,10 @@ __global__ __launch_bounds__(kHalfThreads) __attribute__((amdgpu_waves_per_eu(4)
   auto load_batch = [&](int64_t bt) {
     const int64_t p0 = (bt * NW + wv) * SLICE;
 #pragma unroll
-    for (int u = 0; u < NV; ++u) v[u] = *reinterpret_cast<const float4*>(sc + min(p0 + 256 * u + 4 * lane, a.n_pad - 4));
+    for (int u = 0; u < NV; ++u) {
+      const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sc + min(p0 + 256 * u + 4 * lane, a.n_pad - 4)));
+      v[u] = make_float4(x[0], x[1], x[2], x[3]);
+    }
   };
   u32x4 hv[8];
   if (wv == 0 && !take_all) first_digit_load(hg, hv);
